@@ -1,0 +1,21 @@
+"""CPU oracle of the batched multi-session decode step (plain fp64 numpy).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package; the product path
+(``session_decode_step_amd`` and its HIP library) never does, and this package
+imports nothing from it.  The two share no code: only the seeded input generator
+(``workload``), which holds no arithmetic of the method, serves both.
+
+What it computes is the plain definition of one decode step for B sessions
+(memra-engine 0.72.0, src/decode_batch.rs: module header and the Full-attention arm
+of ``decode_batch_layers``; hf2q ADR-040 §0.7 task blocks F2-F5), in fp64, with
+fp32 only at the rounding points the method defines: the activation quantiser and
+the fp16 KV store.  Each function cites the passage it follows.
+
+Pins (tests marked ``not gpu``) check it against hand-worked blocks, closed forms,
+brute force and library routines; the end-to-end values of whole configurations
+have no external pin beyond that chain (parity unpinned beyond the op-level pins).
+"""
+from .ops import (QK, attention, block_dots, dequantize, dequantize_act, mmvq, mmvq_blocks,  # noqa: F401
+                  quantize_act, rmsnorm, rope_neox, router_topk, silu, swiglu, weight_codes)
+from .step import DenseWeights, OracleCaches, decode_step, moe_ffn  # noqa: F401

@@ -1,0 +1,212 @@
+"""Per-operation definitions of the batched decode step, in plain fp64 numpy.
+
+TEST INFRASTRUCTURE ONLY: nothing in the product path imports this module.
+
+Each function restates the operation from its definition; the pages it follows
+are cited by title and section.  fp32 appears only at the rounding points the
+method defines as part of its result: the activation quantiser (its integers
+are part of the output of the quantise step) and the fp16 KV store.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+
+QK = 32  # elements per quantisation block
+
+
+# ---------------------------------------------------------------------------------------
+# Weight codecs
+# ---------------------------------------------------------------------------------------
+def weight_codes(w: Dict, r0: int = 0, r1: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Integer codes ``q[n, nb, 32]`` (int64) and fp64 block scales ``d[n, nb]`` of rows [r0, r1).
+
+    Q8_0 (memra-engine decode_batch.rs, the exact-16 admission list names QT_Q8_0 as a
+    per-block int8 class): each 32-element block stores int8 codes q in [-127, 127] and one
+    fp16 scale; the value is ``d * q``.
+
+    Q4_0 (same list, QT_Q4_0; hf2q ADR-040 names Q4_0 among GGUF weight types): each block
+    stores 16 bytes; byte j holds the code of element j in its low nibble and of element
+    j + 16 in its high nibble; the signed value is ``nibble - 8`` (range [-8, 7]).
+    """
+    r1 = w["n"] if r1 is None else r1
+    nb = w["k"] // QK
+    d = w["d"][r0:r1].astype(np.float64)
+    if w["fmt"] == "q8_0":
+        q = w["qs"][r0:r1].astype(np.int64).reshape(r1 - r0, nb, QK)
+    elif w["fmt"] == "q4_0":
+        by = w["qs"][r0:r1].reshape(r1 - r0, nb, QK // 2).astype(np.int64)
+        lo = by & 0x0F          # elements 0..15 of the block
+        hi = by >> 4            # elements 16..31 of the block
+        q = np.concatenate([lo, hi], axis=2) - 8
+    else:
+        raise ValueError(w["fmt"])
+    return q, d
+
+
+def dequantize(w: Dict, r0: int = 0, r1: Optional[int] = None) -> np.ndarray:
+    """Dense fp64 values ``[r1 - r0, k]`` of a quantised matrix: ``w = d * q`` per block."""
+    q, d = weight_codes(w, r0, r1)
+    return (q.astype(np.float64) * d[:, :, None]).reshape(q.shape[0], -1)
+
+
+# ---------------------------------------------------------------------------------------
+# Activation quantiser Q(.)
+# ---------------------------------------------------------------------------------------
+def quantize_act(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Symmetric per-32-block int8 quantisation of fp32 rows ``x[B, K]``.
+
+    The pages name the step (memra-engine decode_batch.rs, ``decode_batch_layers``: one
+    ``quantize_q8_1`` of the normed rows feeds the q/k/v products, one feeds gate/up, one
+    the down product) and its consumer (int8 dot products, the dp4a / batched-mmvq classes
+    in the exact-16 admission notes), but not its arithmetic.  The reading used here:
+    per block, ``a = max |x_i|``; if ``a == 0`` the scale and codes are 0; otherwise
+    ``d = fp32(a / 127)`` (IEEE fp32 division) and ``q_i = clamp(round_half_away(fp32(x_i / d)),
+    -127, 127)``.  Returns int8 codes ``[B, K]`` and fp32 scales ``[B, K/32]``.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    B, K = x.shape
+    assert K % QK == 0
+    blk = x.reshape(B, K // QK, QK)
+    a = np.max(np.abs(blk), axis=2)                                 # exact in fp32
+    d = (a / np.float32(127.0)).astype(np.float32)                  # IEEE fp32 division
+    safe = np.where(d == 0, np.float32(1.0), d).astype(np.float32)
+    ratio = (blk / safe[:, :, None]).astype(np.float32)             # IEEE fp32 division
+    r64 = ratio.astype(np.float64)                                  # exact widening
+    rounded = np.sign(r64) * np.floor(np.abs(r64) + 0.5)            # half away from zero, exact in fp64
+    q = np.clip(rounded, -127, 127).astype(np.int64)
+    q[d == 0] = 0
+    return q.reshape(B, K).astype(np.int8), d
+
+
+# ---------------------------------------------------------------------------------------
+# mmvq: block-quantised matrix times B quantised rows
+# ---------------------------------------------------------------------------------------
+def block_dots(w: Dict, xq: np.ndarray, r0: int = 0, r1: Optional[int] = None) -> np.ndarray:
+    """Exact per-block integer dot products ``S[b, n, blk] = sum_i q_w[n, blk, i] * q_x[b, blk, i]``."""
+    qw, _ = weight_codes(w, r0, r1)
+    B = xq.shape[0]
+    qx = xq.astype(np.int64).reshape(B, -1, QK)
+    return np.einsum("nki,bki->bnk", qw, qx, optimize=True)
+
+
+def mmvq_blocks(w: Dict, xq: np.ndarray, xd: np.ndarray) -> np.ndarray:
+    """Block formula ``y[b, n] = sum_blk d_w[n, blk] * d_x[b, blk] * S[b, n, blk]`` in fp64.
+
+    One weight read serves all B rows (memra-engine decode_batch.rs module header: every
+    projection at m = B rows amortises one weight read; hf2q ADR-040 §0.7 F3, small-m
+    quantised decode GEMM).
+    """
+    S = block_dots(w, xq).astype(np.float64)
+    _, dw = weight_codes(w)
+    return np.einsum("nk,bk,bnk->bn", dw, xd.astype(np.float64), S, optimize=True)
+
+
+def dequantize_act(xq: np.ndarray, xd: np.ndarray) -> np.ndarray:
+    B, K = xq.shape
+    return (xq.astype(np.float64).reshape(B, K // QK, QK) * xd.astype(np.float64)[:, :, None]).reshape(B, K)
+
+
+def mmvq(w: Dict, xq: np.ndarray, xd: np.ndarray, dense: Optional[np.ndarray] = None,
+         r0: int = 0, r1: Optional[int] = None, chunk: int = 4096) -> np.ndarray:
+    """Same value as :func:`mmvq_blocks` via a dense fp64 product (dequantise, then matmul).
+
+    ``sum_k (d_w q_w)(d_x q_x)`` regroups the block formula's terms, so the two agree to
+    fp64 rounding; the dense form lets BLAS do the work on large shapes.  Rows [r0, r1) of
+    the matrix only; ``dense`` may hold a cached dequantised copy of those rows.
+    """
+    r1 = w["n"] if r1 is None else r1
+    xv = dequantize_act(xq, xd)
+    if dense is not None:
+        return xv @ dense.T
+    out = np.empty((xq.shape[0], r1 - r0), dtype=np.float64)
+    for c0 in range(r0, r1, chunk):
+        c1 = min(r1, c0 + chunk)
+        out[:, c0 - r0:c1 - r0] = xv @ dequantize(w, c0, c1).T
+    return out
+
+
+# ---------------------------------------------------------------------------------------
+# Row operations
+# ---------------------------------------------------------------------------------------
+def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """``y = x / sqrt(mean(x^2) + eps) * g`` per row (memra-engine decode_batch.rs, the
+    attn_norm / post_attn_norm / output-norm calls of the batched layer walk)."""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * np.asarray(g, dtype=np.float64)
+
+
+def rope_neox(x: np.ndarray, pos: int, base: float) -> np.ndarray:
+    """NEOX rotary embedding of heads ``x[n_heads, hd]`` at position ``pos``.
+
+    Element i < hd/2 pairs with element i + hd/2 and both rotate by
+    ``theta_i = pos * base^(-2i/hd)``; every dim is rotated (memra-engine decode_batch.rs,
+    ``rope_neox`` on q and k with the per-row position buffer).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    hd = x.shape[-1]
+    half = hd // 2
+    i = np.arange(half, dtype=np.float64)
+    theta = float(pos) * np.power(float(base), -2.0 * i / hd)
+    c, s = np.cos(theta), np.sin(theta)
+    a, b = x[..., :half], x[..., half:]
+    return np.concatenate([a * c - b * s, a * s + b * c], axis=-1)
+
+
+def silu(g: np.ndarray) -> np.ndarray:
+    g = np.asarray(g, dtype=np.float64)
+    return g / (1.0 + np.exp(-g))
+
+
+def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """``silu(g) * u`` (memra-engine decode_batch.rs, ``silu_mul`` between gate/up and down)."""
+    return silu(g) * np.asarray(u, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------------------
+# Attention over one row's own cache
+# ---------------------------------------------------------------------------------------
+def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, t: int) -> np.ndarray:
+    """Decode attention of one row: ``q[H, hd]`` over keys ``[0, t)`` of ``K, V[G, >=t, hd]``.
+
+    Query head h reads KV head ``h // (H / G)`` (consecutive query heads share a KV head);
+    ``score_j = q_h . K_j / sqrt(hd)``; ``p = softmax(score)``; ``out_h = sum_j p_j V_j``.
+    No split: the split-K partition is an evaluation order, not part of the definition.
+    (memra-engine decode_batch.rs: scale ``1/sqrt(head_dim)``, ``t_kv = pos + 1``.)
+    """
+    q = np.asarray(q, dtype=np.float64)
+    H, hd = q.shape
+    G = K.shape[0]
+    grp = H // G
+    out = np.empty((H, hd), dtype=np.float64)
+    scale = 1.0 / np.sqrt(hd)
+    for h in range(H):
+        g = h // grp
+        k = K[g, :t].astype(np.float64)
+        v = V[g, :t].astype(np.float64)
+        s = (k @ q[h]) * scale
+        p = np.exp(s - np.max(s))
+        p /= np.sum(p)
+        out[h] = p @ v
+    return out
+
+
+# ---------------------------------------------------------------------------------------
+# Router
+# ---------------------------------------------------------------------------------------
+def router_topk(r: np.ndarray, k: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Top-k experts of router logits ``r[E]`` and their softmax weights.
+
+    Ranked by descending logit, ties to the lower expert id; weights are the softmax over
+    the k selected logits (hf2q ADR-040 §0.7 F4 per-token top-k routing; the reading of the
+    top-8 softmax router in the MoE workload).
+    """
+    r = np.asarray(r, dtype=np.float64)
+    order = np.lexsort((np.arange(r.shape[0]), -r))   # primary: -r ascending; ties: id ascending
+    ids = order[:k]
+    z = r[ids] - np.max(r[ids])
+    p = np.exp(z)
+    p /= np.sum(p)
+    return ids, p

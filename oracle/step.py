@@ -1,0 +1,172 @@
+"""One batched decode step over a layer stack, composed from :mod:`oracle.ops` in fp64.
+
+TEST INFRASTRUCTURE ONLY: nothing in the product path imports this module.
+
+The op order is the Full-attention arm of the batched layer walk on the memra-engine
+page (src/decode_batch.rs, ``decode_batch_layers``): attn_norm -> quantise -> q/k/v
+products at m = B -> RoPE with per-row positions -> phase A, append every row's K/V ->
+phase B, every row attends over its own cache -> o product -> residual add +
+post-attention norm -> quantise -> gate/up -> silu_mul -> quantise -> down -> residual
+add; then the output norm and lm_head (``decode_step_batch_lean_masked``).  The block
+variants that page also carries (QK-norm, output gate) are not part of this model.  The
+MoE FFN follows hf2q ADR-040 §0.7 F4 (per-token top-k routing, each active expert's
+matrices applied to the rows routed to it, weighted sum) and the shared expert of the
+Strata pull request #1524 ("What changes").
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+from . import ops
+
+
+class DenseWeights:
+    """Optional cache of dequantised fp64 matrices (speed only; values equal ops.dequantize)."""
+
+    def __init__(self, budget_bytes: int = 0):
+        self.budget = budget_bytes
+        self.used = 0
+        self.mem: Dict[int, np.ndarray] = {}
+
+    def get(self, w: Dict) -> Optional[np.ndarray]:
+        key = id(w)
+        if key in self.mem:
+            return self.mem[key]
+        need = w["n"] * w["k"] * 8
+        if self.used + need > self.budget:
+            return None
+        dense = ops.dequantize(w)
+        self.mem[key] = dense
+        self.used += need
+        return dense
+
+
+class OracleCaches:
+    """fp16 K/V of the sessions the oracle follows: ``K[s][il]`` is ``[G, capacity, hd]``."""
+
+    def __init__(self, wl, sessions: Optional[Sequence[int]] = None):
+        from workload import kv_prefill  # seeded inputs only
+        sp = wl.spec
+        self.sessions = list(range(len(wl.prefill))) if sessions is None else list(sessions)
+        self.K: Dict[int, List[np.ndarray]] = {}
+        self.V: Dict[int, List[np.ndarray]] = {}
+        for s in self.sessions:
+            self.K[s], self.V[s] = [], []
+            for il in range(sp.n_layers):
+                k0, v0 = kv_prefill(wl, s, il)
+                K = np.zeros((sp.n_head_kv, wl.capacity, sp.head_dim), dtype=np.float16)
+                V = np.zeros_like(K)
+                K[:, : k0.shape[1]] = k0
+                V[:, : v0.shape[1]] = v0
+                self.K[s].append(K)
+                self.V[s].append(V)
+
+
+def _mm(w: Dict, xq, xd, dense: Optional[DenseWeights], blocks: bool) -> np.ndarray:
+    if blocks:
+        return ops.mmvq_blocks(w, xq, xd)
+    return ops.mmvq(w, xq, xd, dense.get(w) if dense is not None else None)
+
+
+def _q(x: np.ndarray):
+    """Q(.) of the fp64 value rounded to fp32 (the quantiser's input precision)."""
+    return ops.quantize_act(np.asarray(x, dtype=np.float64).astype(np.float32))
+
+
+def moe_ffn(spec, L: Dict, z: np.ndarray, zq, zd, dense: Optional[DenseWeights], blocks: bool,
+            route_override: Optional[Dict[int, np.ndarray]] = None, info: Optional[Dict] = None):
+    """Routed experts + shared expert for rows ``z[B, d]`` (reading: rank-ordered sum, then + shared)."""
+    B, d = z.shape
+    E, k, Fe = spec.n_experts, spec.n_expert_used, spec.expert_ffn
+    r = z @ L["router"].astype(np.float64).T            # fp32 router weights, unquantised input
+    out = np.zeros((B, d), dtype=np.float64)
+    for b in range(B):
+        ids, p = ops.router_topk(r[b], k)
+        if route_override is not None and b in route_override:
+            ids = np.asarray(route_override[b])
+            zz = r[b][ids] - np.max(r[b][ids])
+            p = np.exp(zz) / np.sum(np.exp(zz))
+        if info is not None:
+            srt = np.sort(r[b])[::-1]
+            info.setdefault("gap", []).append(float(srt[k - 1] - srt[k]))
+            info.setdefault("ids", []).append(ids.copy())
+        acc = np.zeros(d, dtype=np.float64)
+        for rank in range(k):
+            e = int(ids[rank])
+            if blocks:
+                sub = lambda w, r0, r1: {**w, "n": r1 - r0, "qs": w["qs"][r0:r1], "d": w["d"][r0:r1]}
+                g = ops.mmvq_blocks(sub(L["e_gate"], e * Fe, (e + 1) * Fe), zq[b:b + 1], zd[b:b + 1])
+                u = ops.mmvq_blocks(sub(L["e_up"], e * Fe, (e + 1) * Fe), zq[b:b + 1], zd[b:b + 1])
+                hq, hd = _q(ops.swiglu(g, u))
+                y = ops.mmvq_blocks(sub(L["e_down"], e * d, (e + 1) * d), hq, hd)
+            else:
+                g = ops.mmvq(L["e_gate"], zq[b:b + 1], zd[b:b + 1], r0=e * Fe, r1=(e + 1) * Fe)
+                u = ops.mmvq(L["e_up"], zq[b:b + 1], zd[b:b + 1], r0=e * Fe, r1=(e + 1) * Fe)
+                hq, hd = _q(ops.swiglu(g, u))
+                y = ops.mmvq(L["e_down"], hq, hd, r0=e * d, r1=(e + 1) * d)
+            acc += p[rank] * y[0]
+        out[b] = acc
+    # Shared expert: always on, weight 1, added after the routed sum.
+    g = _mm(L["s_gate"], zq, zd, dense, blocks)
+    u = _mm(L["s_up"], zq, zd, dense, blocks)
+    hq, hd = _q(ops.swiglu(g, u))
+    return out + _mm(L["s_down"], hq, hd, dense, blocks)
+
+
+def decode_step(model: Dict, caches: OracleCaches, x_in: np.ndarray, sessions: Sequence[int],
+                pos: Sequence[int], dense: Optional[DenseWeights] = None, blocks: bool = False,
+                route_override: Optional[Dict] = None, info: Optional[Dict] = None,
+                trace: Optional[List] = None) -> np.ndarray:
+    """One decode step for rows ``x_in[B, d]``; row b writes and reads cache ``sessions[b]``.
+
+    Row b appends its K/V at ``pos[b]`` and attends the first ``pos[b] + 1`` keys; every
+    append of the layer precedes every attention (phase A / phase B of the batched walk),
+    so rows sharing a cache at consecutive positions attend causally.  Returns logits
+    ``[B, vocab]`` if the model has an lm_head, the output-normed rows if it has an output
+    norm, else the residual stream.  Caches are updated in place.
+    """
+    sp = model["spec"]
+    H, G, hd, eps = sp.n_head, sp.n_head_kv, sp.head_dim, sp.rms_eps
+    x = np.asarray(x_in, dtype=np.float32).astype(np.float64)
+    B = x.shape[0]
+    for il, L in enumerate(model["layers"]):
+        xn = ops.rmsnorm(x, L["attn_norm"], eps)
+        xq, xd = _q(xn)
+        qkv = _mm(L["wqkv"], xq, xd, dense, blocks)
+        q = qkv[:, : H * hd].reshape(B, H, hd)
+        k = qkv[:, H * hd: (H + G) * hd].reshape(B, G, hd)
+        v = qkv[:, (H + G) * hd:].reshape(B, G, hd)
+        q = np.stack([ops.rope_neox(q[b], pos[b], sp.rope_base) for b in range(B)])
+        k = np.stack([ops.rope_neox(k[b], pos[b], sp.rope_base) for b in range(B)])
+        for b in range(B):                                   # phase A: append all rows
+            s = sessions[b]
+            caches.K[s][il][:, pos[b]] = k[b].astype(np.float16)
+            caches.V[s][il][:, pos[b]] = v[b].astype(np.float16)
+        attn = np.stack([ops.attention(q[b], caches.K[sessions[b]][il], caches.V[sessions[b]][il],
+                                       pos[b] + 1) for b in range(B)])   # phase B: attend
+        aq, ad = _q(attn.reshape(B, H * hd))
+        x1 = x + _mm(L["wo"], aq, ad, dense, blocks)
+        if trace is not None:
+            trace.append({"layer": il, "q": q, "k": k, "v": v, "attn": attn, "x1": x1})
+        if not sp.has_ffn:
+            x = x1
+            continue
+        z = ops.rmsnorm(x1, L["ffn_norm"], eps)
+        zq, zd = _q(z)
+        if sp.n_experts:
+            f = moe_ffn(sp, L, z, zq, zd, dense, blocks, route_override.get(il) if route_override else None,
+                        info.setdefault(il, {}) if info is not None else None)
+        else:
+            g = _mm(L["w_gate"], zq, zd, dense, blocks)
+            u = _mm(L["w_up"], zq, zd, dense, blocks)
+            hq, hdd = _q(ops.swiglu(g, u))
+            f = _mm(L["w_down"], hq, hdd, dense, blocks)
+        x = x1 + f
+    if model["final_norm"] is not None:
+        x = ops.rmsnorm(x, model["final_norm"], eps)
+    if model["lm_head"] is not None:
+        oq, od = _q(x)
+        x = _mm(model["lm_head"], oq, od, dense, blocks)
+    return x

@@ -1,0 +1,350 @@
+"""Pins of the CPU oracle against things other than itself (no GPU).
+
+Hand-worked blocks (tests/golden), closed forms, brute force on tiny inputs and library
+routines (torch CPU in fp64).  Each pin is chosen so a plausible slip in the oracle (a
+dropped term, a swapped nibble, a transposed operand, a wrong sign or index) fails it.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import ops
+import workload as wlmod
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------------- codecs (O1, O2)
+def test_q4_0_golden_block():
+    g = _gold("q4_0_block.json")
+    w = {"fmt": "q4_0", "n": 1, "k": 32, "qs": np.frombuffer(bytes.fromhex(g["bytes_hex"]), np.uint8).reshape(1, 16),
+         "d": np.array([[g["d"]]], dtype=np.float16)}
+    assert ops.dequantize(w)[0].tolist() == g["values"]
+
+
+def test_q8_0_golden_block():
+    g = _gold("q8_0_block.json")
+    w = {"fmt": "q8_0", "n": 1, "k": 32, "qs": np.array([g["codes"]], dtype=np.int8),
+         "d": np.array([[g["d"]]], dtype=np.float16)}
+    assert ops.dequantize(w)[0].tolist() == g["values"]
+
+
+def test_q4_0_codes_cover_range_and_rows():
+    # Two rows x two blocks, every nibble value present: decoded codes span [-8, 7] and row /
+    # block indexing keeps each block's own scale.
+    qs = np.array([[(j | ((15 - j) << 4)) for j in range(16)] * 2,
+                   [((j * 5) % 16) | (((j * 3) % 16) << 4) for j in range(16)] * 2], dtype=np.uint8)
+    d = np.array([[1.0, 2.0], [0.5, 4.0]], dtype=np.float16)
+    w = {"fmt": "q4_0", "n": 2, "k": 64, "qs": qs, "d": d}
+    q, dd = ops.weight_codes(w)
+    assert q.min() == -8 and q.max() == 7
+    assert q[1, 0, 3] == ((3 * 5) % 16) - 8 and q[1, 0, 19] == ((3 * 3) % 16) - 8
+    v = ops.dequantize(w)
+    assert v[0, 32 + 5] == 2.0 * (5 - 8) and v[1, 32 + 16 + 2] == 4.0 * (((2 * 3) % 16) - 8)
+
+
+# --------------------------------------------------------------------------- quantiser (O3)
+def test_act_quant_golden_blocks():
+    g = _gold("act_quant_blocks.json")
+    x = np.array([np.concatenate([b["x"] for b in g["blocks"]])], dtype=np.float32)
+    q, d = ops.quantize_act(x)
+    assert d[0].tolist() == [b["d"] for b in g["blocks"]]
+    assert q[0].tolist() == sum((b["q"] for b in g["blocks"]), [])
+
+
+def test_act_quant_invariants_random():
+    r = np.random.default_rng(1)
+    x = (r.standard_normal((7, 32 * 40)) * np.exp(r.uniform(-6, 6, (7, 1)))).astype(np.float32)
+    x[3, 64:96] = 0.0
+    q, d = ops.quantize_act(x)
+    blk = x.reshape(7, 40, 32).astype(np.float64)
+    qb = q.reshape(7, 40, 32).astype(np.float64)
+    dd = d.astype(np.float64)[:, :, None]
+    # reconstruction error at most half a step (plus fp32 rounding of x/d)
+    assert np.all(np.abs(blk - dd * qb) <= dd * (0.5 + 1e-6))
+    # the amax element maps to +-127, codes within range
+    amax_idx = np.argmax(np.abs(blk), axis=2)
+    picked = np.take_along_axis(qb, amax_idx[:, :, None], 2)[:, :, 0]
+    nz = d > 0
+    assert np.all(np.abs(picked[nz]) == 127)
+    assert np.all(np.abs(qb) <= 127)
+    # zero block: zero scale and codes
+    assert d[3, 2] == 0 and np.all(q[3, 64:96] == 0)
+    # scale is the IEEE fp32 quotient amax/127
+    assert np.array_equal(d, (np.max(np.abs(x.reshape(7, 40, 32)), 2) / np.float32(127)).astype(np.float32))
+
+
+def test_act_quant_ties_round_away_from_zero():
+    # d = 1 (amax 127): x/d = k + 0.5 must round away from zero, for both signs.
+    x = np.zeros((1, 32), np.float32)
+    x[0, 0] = 127.0
+    x[0, 1:9] = [0.5, 1.5, 2.5, 3.5, -0.5, -1.5, -2.5, -3.5]
+    q, _ = ops.quantize_act(x)
+    assert q[0, 1:9].tolist() == [1, 2, 3, 4, -1, -2, -3, -4]
+    # the largest fp32 below 0.5 rounds to 0 (an fp32 "+0.5 then floor" would give 1)
+    x[0, 9] = np.nextafter(np.float32(0.5), np.float32(0))
+    q, _ = ops.quantize_act(x)
+    assert q[0, 9] == 0
+
+
+# --------------------------------------------------------------------------- mmvq (O4)
+def test_mmvq_golden_block():
+    g = _gold("mmvq_block.json")
+    w = {"fmt": "q8_0", "n": 1, "k": 32, "qs": np.array([g["w_codes"]], np.int8), "d": np.array([[g["w_d"]]], np.float16)}
+    xq, xd = ops.quantize_act(np.array([g["x"]], np.float32))
+    assert xq[0].tolist() == g["x_codes"] and xd[0, 0] == g["x_d"]
+    assert ops.block_dots(w, xq)[0, 0, 0] == g["S"]
+    assert ops.mmvq_blocks(w, xq, xd)[0, 0] == g["y"]
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_0"])
+def test_block_dots_bruteforce(fmt):
+    r = np.random.default_rng(2)
+    w = (wlmod.draw_q8_0 if fmt == "q8_0" else wlmod.draw_q4_0)(r, r, 3, 64)
+    xq = r.integers(-127, 128, (2, 64)).astype(np.int8)
+    S = ops.block_dots(w, xq)
+    # brute force via an independent decode of each element from the raw bytes
+    for n in range(3):
+        for blk in range(2):
+            for b in range(2):
+                s = 0
+                for i in range(32):
+                    if fmt == "q8_0":
+                        c = int(w["qs"][n, 32 * blk + i])
+                    else:
+                        byte = int(w["qs"][n, 16 * blk + (i % 16)])
+                        c = ((byte >> 4) if i >= 16 else (byte & 15)) - 8
+                    s += c * int(xq[b, 32 * blk + i])
+                assert S[b, n, blk] == s
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_0"])
+def test_mmvq_block_formula_equals_dense(fmt):
+    r = np.random.default_rng(3)
+    w = (wlmod.draw_q8_0 if fmt == "q8_0" else wlmod.draw_q4_0)(r, r, 40, 256)
+    x = r.standard_normal((5, 256)).astype(np.float32)
+    xq, xd = ops.quantize_act(x)
+    yb = ops.mmvq_blocks(w, xq, xd)
+    yd = ops.mmvq(w, xq, xd, chunk=16)
+    np.testing.assert_allclose(yb, yd, rtol=1e-12, atol=1e-12 * np.abs(yd).max())
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_0"])
+def test_mmvq_vs_unquantised_closed_form_bound(fmt):
+    r = np.random.default_rng(4)
+    w = (wlmod.draw_q8_0 if fmt == "q8_0" else wlmod.draw_q4_0)(r, r, 64, 512)
+    x = r.standard_normal((4, 512)).astype(np.float32)
+    xq, xd = ops.quantize_act(x)
+    y = ops.mmvq_blocks(w, xq, xd)
+    exact = x.astype(np.float64) @ ops.dequantize(w).T
+    qw, dw = ops.weight_codes(w)
+    bound = np.einsum("nk,bk->bn", np.abs(dw) * np.abs(qw).sum(2), xd.astype(np.float64) / 2)
+    assert np.all(np.abs(y - exact) <= bound * (1 + 1e-6) + 1e-12)
+    assert np.any(np.abs(y - exact) > 0.05 * bound)  # the bound is not vacuous
+
+
+# --------------------------------------------------------------------------- row ops (O5, O6, O9)
+def test_rmsnorm_constant_and_torch():
+    g = np.array([1.5, -2.0, 0.25, 3.0])
+    y = ops.rmsnorm(np.full(4, -3.0), g, 1e-5)
+    np.testing.assert_allclose(y, -g * 3.0 / math.sqrt(9.0 + 1e-5), rtol=1e-15)
+    r = np.random.default_rng(5)
+    x = r.standard_normal((3, 64))
+    gg = r.standard_normal(64)
+    ref = torch.nn.functional.rms_norm(torch.tensor(x), (64,), torch.tensor(gg), eps=1e-5).numpy()
+    np.testing.assert_allclose(ops.rmsnorm(x, gg, 1e-5), ref, rtol=1e-13, atol=1e-14)
+
+
+def test_rope_closed_forms():
+    r = np.random.default_rng(6)
+    x = r.standard_normal((3, 128))
+    np.testing.assert_array_equal(ops.rope_neox(x, 0, 10000.0), x)            # pos 0: identity
+    y = ops.rope_neox(x, 1234, 10000.0)
+    pn = lambda a: a[:, :64] ** 2 + a[:, 64:] ** 2
+    np.testing.assert_allclose(pn(y), pn(x), rtol=1e-12)                       # pair norms kept
+    np.testing.assert_allclose(ops.rope_neox(ops.rope_neox(x, 17, 1e4), 40, 1e4),
+                               ops.rope_neox(x, 57, 1e4), rtol=1e-9, atol=1e-12)  # R(a)R(b)=R(a+b)
+    q, k = r.standard_normal(128), r.standard_normal(128)
+    d1 = ops.rope_neox(q[None], 100, 1e4)[0] @ ops.rope_neox(k[None], 90, 1e4)[0]
+    d2 = ops.rope_neox(q[None], 5010, 1e4)[0] @ ops.rope_neox(k[None], 5000, 1e4)[0]
+    assert abs(d1 - d2) < 1e-9 * (1 + abs(d1))                                   # relative position
+    # the pairing is (i, i + hd/2): a vector with only element 0 set rotates into element 64
+    e0 = np.zeros(128); e0[0] = 1.0
+    y0 = ops.rope_neox(e0[None], 1, 1e4)[0]
+    assert abs(y0[0] - math.cos(1.0)) < 1e-15 and abs(y0[64] - math.sin(1.0)) < 1e-15
+    # element 1 rotates with theta = base^(-2/hd)
+    e1 = np.zeros(128); e1[1] = 1.0
+    y1 = ops.rope_neox(e1[None], 3, 1e4)[0]
+    th = 3 * 1e4 ** (-2.0 / 128)
+    assert abs(y1[1] - math.cos(th)) < 1e-15 and abs(y1[65] - math.sin(th)) < 1e-15
+
+
+def test_swiglu_special_cases_and_torch():
+    assert ops.silu(np.array([0.0]))[0] == 0.0
+    assert abs(ops.swiglu(np.array([40.0]), np.array([3.0]))[0] - 120.0) < 1e-12
+    r = np.random.default_rng(7)
+    g, u = r.standard_normal(100), r.standard_normal(100)
+    ref = (torch.nn.functional.silu(torch.tensor(g)) * torch.tensor(u)).numpy()
+    np.testing.assert_allclose(ops.swiglu(g, u), ref, rtol=1e-14, atol=1e-15)
+
+
+# --------------------------------------------------------------------------- attention (O8)
+def test_attention_special_cases():
+    r = np.random.default_rng(8)
+    H, G, hd = 4, 2, 64
+    K = r.standard_normal((G, 10, hd)).astype(np.float16)
+    V = r.standard_normal((G, 10, hd)).astype(np.float16)
+    q = r.standard_normal((H, hd))
+    out = ops.attention(q, K, V, 1)                       # t = 1: out = V[0]
+    for h in range(H):
+        np.testing.assert_array_equal(out[h], V[h // 2, 0].astype(np.float64))
+    out0 = ops.attention(np.zeros((H, hd)), K, V, 7)       # q = 0: uniform weights
+    for h in range(H):
+        np.testing.assert_allclose(out0[h], V[h // 2, :7].astype(np.float64).mean(0), rtol=1e-12, atol=1e-14)
+    K2 = K.copy(); K2[:, :] = K[:, :1]                     # identical keys: mean of V
+    out2 = ops.attention(q, K2, V, 9)
+    np.testing.assert_allclose(out2[3], V[1, :9].astype(np.float64).mean(0), rtol=1e-12, atol=1e-14)
+    K3 = np.zeros_like(K); K3[1, 4] = 1.0                  # one dominant key for heads of group 1
+    q3 = np.zeros((H, hd)); q3[2:, :] = 60.0
+    out3 = ops.attention(q3, K3, V, 10)
+    np.testing.assert_allclose(out3[2], V[1, 4].astype(np.float64), rtol=1e-9, atol=1e-9)
+
+
+def test_attention_vs_torch_sdpa_gqa():
+    r = np.random.default_rng(9)
+    H, G, hd, t = 8, 2, 64, 37
+    K = r.standard_normal((G, 50, hd)).astype(np.float16)
+    V = r.standard_normal((G, 50, hd)).astype(np.float16)
+    q = r.standard_normal((H, hd))
+    ours = ops.attention(q, K, V, t)
+    kk = torch.tensor(K[:, :t].astype(np.float64)).repeat_interleave(H // G, 0)   # head h -> group h // (H/G)
+    vv = torch.tensor(V[:, :t].astype(np.float64)).repeat_interleave(H // G, 0)
+    ref = torch.nn.functional.scaled_dot_product_attention(torch.tensor(q)[:, None, :], kk, vv)[:, 0].numpy()
+    np.testing.assert_allclose(ours, ref, rtol=1e-12, atol=1e-13)
+
+
+# --------------------------------------------------------------------------- router
+def test_router_topk_ties_and_torch():
+    r = np.array([0.5, 2.0, 2.0, -1.0, 3.0, 2.0, 0.1, 3.0])
+    ids, p = ops.router_topk(r, 4)
+    assert ids.tolist() == [4, 7, 1, 2]               # ties to the lower id
+    np.testing.assert_allclose(p.sum(), 1.0, rtol=1e-15)
+    np.testing.assert_allclose(p, torch.softmax(torch.tensor(r[ids]), 0).numpy(), rtol=1e-14)
+    rr = np.random.default_rng(10).standard_normal(128)
+    ids2, _ = ops.router_topk(rr, 8)
+    assert ids2.tolist() == torch.topk(torch.tensor(rr), 8).indices.tolist()
+
+
+# --------------------------------------------------------------------------- composition
+TINY = wlmod.ModelSpec("tiny", 2, 128, 4, 2, 64, 256, "q8_0", vocab=96, final_norm=True)
+TINY_MOE = wlmod.ModelSpec("tiny_moe", 2, 128, 4, 2, 64, 0, "q4_0", final_norm=True,
+                           n_experts=8, n_expert_used=3, expert_ffn=64, shared_ffn=96)
+
+
+def _tiny_wl(spec, code, rows, prefill, cap=48):
+    return wlmod.Workload(code, spec, prefill, rows, 1, cap, 0)
+
+
+@pytest.mark.parametrize("spec", [TINY, TINY_MOE], ids=["dense", "moe"])
+def test_step_block_formula_equals_dense_formulation(spec):
+    wl = _tiny_wl(spec, 91, [(0, 0), (1, 0), (1, 1)], [5, 20])
+    model = wlmod.make_model(spec, 91)
+    x = wlmod.step_inputs(wl, 0)
+    ys = []
+    for blocks in (True, False):
+        c = oracle.OracleCaches(wl)
+        ys.append(oracle.decode_step(model, c, x, [0, 1, 1], wl.positions(0), blocks=blocks))
+    np.testing.assert_allclose(ys[0], ys[1], rtol=1e-10, atol=1e-10 * np.abs(ys[1]).max())
+
+
+def test_moe_routed_sum_equals_dense_masked_sum():
+    spec = TINY_MOE
+    model = wlmod.make_model(spec, 92)
+    L = model["layers"][0]
+    r = np.random.default_rng(11)
+    z = r.standard_normal((3, spec.d))
+    zq, zd = ops.quantize_act(z.astype(np.float32))
+    routed = oracle.moe_ffn(spec, L, z, zq, zd, None, blocks=False)
+    # dense evaluation of every expert, weighted by p masked to the top-k
+    logits = z @ L["router"].astype(np.float64).T
+    dense = np.zeros_like(routed)
+    Fe, d = spec.expert_ffn, spec.d
+    for b in range(3):
+        order = sorted(range(spec.n_experts), key=lambda e: (-logits[b, e], e))[: spec.n_expert_used]
+        w = np.zeros(spec.n_experts)
+        ex = np.exp(logits[b, order] - logits[b, order].max())
+        w[order] = ex / ex.sum()
+        for e in range(spec.n_experts):
+            Wg = ops.dequantize(L["e_gate"], e * Fe, (e + 1) * Fe)
+            Wu = ops.dequantize(L["e_up"], e * Fe, (e + 1) * Fe)
+            Wd = ops.dequantize(L["e_down"], e * d, (e + 1) * d)
+            xv = ops.dequantize_act(zq[b:b + 1], zd[b:b + 1])
+            hq, hd = ops.quantize_act(ops.swiglu(xv @ Wg.T, xv @ Wu.T).astype(np.float32))
+            dense[b] += w[e] * (ops.dequantize_act(hq, hd) @ Wd.T)[0]
+        xv = ops.dequantize_act(zq[b:b + 1], zd[b:b + 1])
+        hq, hd = ops.quantize_act(ops.swiglu(xv @ ops.dequantize(L["s_gate"]).T,
+                                             xv @ ops.dequantize(L["s_up"]).T).astype(np.float32))
+        dense[b] += (ops.dequantize_act(hq, hd) @ ops.dequantize(L["s_down"]).T)[0]
+    np.testing.assert_allclose(routed, dense, rtol=1e-10, atol=1e-12)
+
+
+def test_verify_rows_equal_sequential_steps():
+    # A stream's 4 draft rows in one step (append all, then attend) equal 4 sequential
+    # single-row steps at positions L..L+3 (Strata #1524 "Fresh validation": solo and batch
+    # tokens matched; memra-engine decode_batch.rs: phase A then phase B).
+    spec = TINY
+    wl = _tiny_wl(spec, 93, [(0, j) for j in range(4)], [11])
+    model = wlmod.make_model(spec, 93)
+    x = wlmod.step_inputs(wl, 0)
+    cb = oracle.OracleCaches(wl)
+    yb = oracle.decode_step(model, cb, x, [0] * 4, wl.positions(0), blocks=True)
+    cs = oracle.OracleCaches(wl)
+    ys = np.concatenate([oracle.decode_step(model, cs, x[j:j + 1], [0], [11 + j], blocks=True) for j in range(4)])
+    np.testing.assert_allclose(yb, ys, rtol=1e-12, atol=1e-12 * np.abs(ys).max())
+    for il in range(spec.n_layers):
+        np.testing.assert_array_equal(cb.K[0][il], cs.K[0][il])
+        np.testing.assert_array_equal(cb.V[0][il], cs.V[0][il])
+
+
+def test_rows_are_isolated_in_the_oracle():
+    spec = TINY
+    wl = _tiny_wl(spec, 94, [(0, 0), (1, 0)], [9, 30])
+    model = wlmod.make_model(spec, 94)
+    x = wlmod.step_inputs(wl, 0)
+    y2 = oracle.decode_step(model, oracle.OracleCaches(wl), x, [0, 1], wl.positions(0), blocks=True)
+    y1 = oracle.decode_step(model, oracle.OracleCaches(wl), x[1:], [1], [30], blocks=True)
+    np.testing.assert_allclose(y2[1], y1[0], rtol=1e-12, atol=1e-12 * np.abs(y1).max())
+
+
+def test_append_writes_exactly_one_slot_per_row():
+    spec = TINY
+    wl = _tiny_wl(spec, 95, [(0, 0), (1, 0)], [9, 30])
+    model = wlmod.make_model(spec, 95)
+    c = oracle.OracleCaches(wl)
+    before = [[k.copy() for k in c.K[s]] for s in (0, 1)]
+    oracle.decode_step(model, c, wlmod.step_inputs(wl, 0), [0, 1], wl.positions(0))
+    for s, p in ((0, 9), (1, 30)):
+        for il in range(spec.n_layers):
+            diff = np.any(c.K[s][il] != before[s][il], axis=(0, 2))
+            assert diff.nonzero()[0].tolist() == [p]
+
+
+def test_workload_determinism():
+    a = wlmod.make_model(TINY, 7)
+    b = wlmod.make_model(TINY, 7)
+    assert np.array_equal(a["layers"][1]["w_down"]["qs"], b["layers"][1]["w_down"]["qs"])
+    wl = wlmod.workload("c1")
+    assert np.array_equal(wlmod.step_inputs(wl, 0), wlmod.step_inputs(wl, 0))
+    assert wl.positions(0) == [17, 40]
+    lens = wlmod.c3_lengths(0)
+    assert all(512 <= t <= 32768 for t in lens) and len(set(lens)) > 8

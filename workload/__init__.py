@@ -1,0 +1,256 @@
+"""Seeded synthetic inputs for the batched multi-session decode step.
+
+This module is shared by the CPU oracle and the GPU harness, so it holds *only*
+shapes and random draws: no arithmetic of the decode step (no quantisation, no
+nibble decoding, no norm, no attention) lives here.  Every array is produced by
+an independent numpy stream keyed by (seed, config, tensor, layer, index), so a
+single tensor can be regenerated without drawing the others.
+
+Distributions follow the workload descriptions of the batched-decode pages:
+
+* Q8_0 weights: 32-element blocks of int8 drawn uniformly from the closed range
+  [-127, 127] plus one fp16 scale ``|N(0, 0.02)| / 127`` per block.
+* Q4_0 weights: 32-element blocks of 4-bit codes drawn uniformly (a uniformly
+  random byte holds two uniformly random 4-bit codes), plus one fp16 scale
+  ``|N(0, 0.02)| / 8`` per block (same max-|w| scale as Q8_0).
+* Norm gains ``1 + 0.1 N(0, 1)`` (fp32), router weights ``N(0, 0.02)`` (fp32),
+  step inputs ``N(0, 1)`` fp32 rows, KV prefill ``fp16(N(0, 1))``.
+
+Storage conventions of the arrays produced here (both sides read them):
+
+* Q8_0 ``qs``: int8 ``[n_out, k]`` row-major; ``d``: fp16 ``[n_out, k/32]``.
+* Q4_0 ``qs``: uint8 ``[n_out, k/2]`` (16 bytes per 32-element block, the
+  block's bytes contiguous); ``d``: fp16 ``[n_out, k/32]``.
+* KV prefill for one (session, layer): fp16 ``[G, L, hd]`` for K and for V.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Tuple
+
+import numpy as np
+
+# Tensor codes for the per-tensor seed key (stable across versions).
+T_ATTN_NORM, T_WQKV_Q, T_WQKV_D, T_WO_Q, T_WO_D, T_FFN_NORM = 1, 2, 3, 4, 5, 6
+T_GATE_Q, T_GATE_D, T_UP_Q, T_UP_D, T_DOWN_Q, T_DOWN_D = 7, 8, 9, 10, 11, 12
+T_ROUTER = 13
+T_EGATE_Q, T_EGATE_D, T_EUP_Q, T_EUP_D, T_EDOWN_Q, T_EDOWN_D = 14, 15, 16, 17, 18, 19
+T_SGATE_Q, T_SGATE_D, T_SUP_Q, T_SUP_D, T_SDOWN_Q, T_SDOWN_D = 20, 21, 22, 23, 24, 25
+T_FINAL_NORM, T_LM_Q, T_LM_D = 26, 27, 28
+T_X_IN, T_K_PRE, T_V_PRE, T_LENGTHS = 29, 30, 31, 32
+
+
+def rng_for(seed: int, cfg_code: int, tensor: int, layer: int = 0, index: int = 0) -> np.random.Generator:
+    """An independent numpy Generator for one tensor (SeedSequence keyed by the tuple)."""
+    return np.random.default_rng([int(seed), int(cfg_code), int(tensor), int(layer), int(index)])
+
+
+@dataclass(frozen=True)
+class ModelSpec:
+    """Shape of a decoder stack (plain pre-norm block; no biases, no QK-norm, no gate)."""
+    name: str
+    n_layers: int
+    d: int
+    n_head: int
+    n_head_kv: int
+    head_dim: int
+    ffn: int                 # dense SwiGLU width; 0 = none (attention-only or MoE)
+    fmt: str                 # "q8_0" or "q4_0" for every quantised matrix
+    vocab: int = 0           # lm_head rows; 0 = no lm_head
+    final_norm: bool = False
+    n_experts: int = 0       # 0 = dense FFN
+    n_expert_used: int = 0
+    expert_ffn: int = 0
+    shared_ffn: int = 0
+    rope_base: float = 10000.0
+    rms_eps: float = 1e-5
+
+    @property
+    def qkv_rows(self) -> int:
+        return (self.n_head + 2 * self.n_head_kv) * self.head_dim
+
+    @property
+    def has_ffn(self) -> bool:
+        return self.ffn > 0 or self.n_experts > 0
+
+    @property
+    def out_dim(self) -> int:
+        return self.vocab if self.vocab else self.d
+
+
+@dataclass
+class Workload:
+    """Sessions, rows and steps of one synthetic decode workload.
+
+    ``rows[b] = (session, j)``: row b decodes in cache ``session`` at position
+    ``prefill[session] + j + step``.  Several rows may share a session only at
+    distinct positions (speculative-verify rows, causal within the stream).
+    """
+    code: int
+    spec: ModelSpec
+    prefill: List[int]                   # cache length of each session before step 0
+    rows: List[Tuple[int, int]]          # (session, draft offset) per row
+    steps: int
+    capacity: int
+    seed: int = 0
+    note: str = ""
+
+    @property
+    def B(self) -> int:
+        return len(self.rows)
+
+    def positions(self, step: int) -> List[int]:
+        """pos of each row at this step: the session's cache length before the row is written."""
+        return [self.prefill[s] + j + step for (s, j) in self.rows]
+
+
+# --------------------------------------------------------------------------------------
+# The five workloads (shapes and session mixes) and their reduced variants for CPU tests.
+# --------------------------------------------------------------------------------------
+SPEC_C1 = ModelSpec("c1_1layer_d256_q8_0", 1, 256, 4, 2, 64, 1024, "q8_0")
+SPEC_C2 = ModelSpec("c2_8layer_d2048_q8_0_lm32000", 8, 2048, 16, 4, 128, 5632, "q8_0",
+                    vocab=32000, final_norm=True)
+SPEC_C3 = ModelSpec("c3_attn_d4096_q8_0", 1, 4096, 32, 8, 128, 0, "q8_0")
+SPEC_C4 = ModelSpec("c4_32layer_d4096_q4_0", 32, 4096, 32, 8, 128, 14336, "q4_0", final_norm=True)
+SPEC_C5 = ModelSpec("c5_moe8layer_d2816_q4_0", 8, 2816, 16, 8, 128, 0, "q4_0", final_norm=True,
+                    n_experts=128, n_expert_used=8, expert_ffn=704, shared_ffn=2816)
+
+
+def c3_lengths(seed: int = 0, B: int = 16) -> List[int]:
+    """Per-session KV lengths drawn log-uniform in [512, 32768] (floor, clamped)."""
+    r = rng_for(seed, 3, T_LENGTHS)
+    u = r.uniform(math.log(512.0), math.log(32768.0), size=B)
+    return [int(min(32768, max(512, math.floor(math.exp(v))))) for v in u]
+
+
+def workload(name: str, B: Optional[int] = None, seed: int = 0, steps: Optional[int] = None) -> Workload:
+    """Build one of the five workloads ("c1".."c5"); ``B``/``steps`` override the defaults."""
+    if name == "c1":
+        assert B in (None, 2, 1)
+        prefill = [17, 40]
+        rows = [(0, 0), (1, 0)] if B in (None, 2) else [(0, 0)]
+        return Workload(1, SPEC_C1, prefill[: len(rows)], rows, steps or 1, 64, seed)
+    if name == "c2":
+        B = B or 8
+        return Workload(2, SPEC_C2, [1238] * B, [(b, 0) for b in range(B)], steps or 64,
+                        1238 + 64, seed)
+    if name == "c3":
+        B = B or 16
+        lens = c3_lengths(seed, 16)[:B]
+        return Workload(3, SPEC_C3, lens, [(b, 0) for b in range(B)], steps or 1, 32768 + 1, seed)
+    if name == "c4":
+        B = B or 8
+        return Workload(4, SPEC_C4, [4096] * B, [(b, 0) for b in range(B)], steps or 32,
+                        4096 + 32, seed)
+    if name == "c5":
+        n_streams = (B or 16) // 4
+        assert n_streams * 4 == (B or 16)
+        rows = [(s, j) for s in range(n_streams) for j in range(4)]
+        return Workload(5, SPEC_C5, [8192] * n_streams, rows, steps or 1, 8192 + 4, seed)
+    raise ValueError(name)
+
+
+# --------------------------------------------------------------------------------------
+# Random draws
+# --------------------------------------------------------------------------------------
+def draw_q8_0(rq: np.random.Generator, rd: np.random.Generator, n: int, k: int) -> Dict:
+    qs = rq.integers(-127, 128, size=(n, k), dtype=np.int8)
+    d = (np.abs(rd.standard_normal((n, k // 32), dtype=np.float32)) * np.float32(0.02)
+         / np.float32(127.0)).astype(np.float16)
+    return {"fmt": "q8_0", "n": n, "k": k, "qs": qs, "d": d}
+
+
+def draw_q4_0(rq: np.random.Generator, rd: np.random.Generator, n: int, k: int) -> Dict:
+    qs = rq.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    d = (np.abs(rd.standard_normal((n, k // 32), dtype=np.float32)) * np.float32(0.02)
+         / np.float32(8.0)).astype(np.float16)
+    return {"fmt": "q4_0", "n": n, "k": k, "qs": qs, "d": d}
+
+
+def draw_weight(fmt: str, seed: int, code: int, tq: int, td: int, layer: int, n: int, k: int) -> Dict:
+    rq, rd = rng_for(seed, code, tq, layer), rng_for(seed, code, td, layer)
+    return (draw_q8_0 if fmt == "q8_0" else draw_q4_0)(rq, rd, n, k)
+
+
+def draw_gain(seed: int, code: int, tensor: int, layer: int, n: int) -> np.ndarray:
+    r = rng_for(seed, code, tensor, layer)
+    return (np.float32(1.0) + np.float32(0.1) * r.standard_normal(n, dtype=np.float32)).astype(np.float32)
+
+
+def make_layer(spec: ModelSpec, code: int, seed: int, il: int) -> Dict:
+    d, fmt = spec.d, spec.fmt
+    L: Dict = {
+        "attn_norm": draw_gain(seed, code, T_ATTN_NORM, il, d),
+        "wqkv": draw_weight(fmt, seed, code, T_WQKV_Q, T_WQKV_D, il, spec.qkv_rows, d),
+        "wo": draw_weight(fmt, seed, code, T_WO_Q, T_WO_D, il, d, spec.n_head * spec.head_dim),
+    }
+    if spec.has_ffn:
+        L["ffn_norm"] = draw_gain(seed, code, T_FFN_NORM, il, d)
+    if spec.ffn:
+        F = spec.ffn
+        L["w_gate"] = draw_weight(fmt, seed, code, T_GATE_Q, T_GATE_D, il, F, d)
+        L["w_up"] = draw_weight(fmt, seed, code, T_UP_Q, T_UP_D, il, F, d)
+        L["w_down"] = draw_weight(fmt, seed, code, T_DOWN_Q, T_DOWN_D, il, d, F)
+    if spec.n_experts:
+        E, Fe, Fs = spec.n_experts, spec.expert_ffn, spec.shared_ffn
+        r = rng_for(seed, code, T_ROUTER, il)
+        L["router"] = (r.standard_normal((E, d), dtype=np.float32) * np.float32(0.02)).astype(np.float32)
+        # Experts stacked along the output rows: expert e = rows [e*Fe, (e+1)*Fe) of
+        # e_gate/e_up and rows [e*d, (e+1)*d) of e_down.
+        L["e_gate"] = draw_weight(fmt, seed, code, T_EGATE_Q, T_EGATE_D, il, E * Fe, d)
+        L["e_up"] = draw_weight(fmt, seed, code, T_EUP_Q, T_EUP_D, il, E * Fe, d)
+        L["e_down"] = draw_weight(fmt, seed, code, T_EDOWN_Q, T_EDOWN_D, il, E * d, Fe)
+        L["s_gate"] = draw_weight(fmt, seed, code, T_SGATE_Q, T_SGATE_D, il, Fs, d)
+        L["s_up"] = draw_weight(fmt, seed, code, T_SUP_Q, T_SUP_D, il, Fs, d)
+        L["s_down"] = draw_weight(fmt, seed, code, T_SDOWN_Q, T_SDOWN_D, il, d, Fs)
+    return L
+
+
+def make_model(spec: ModelSpec, code: int, seed: int = 0) -> Dict:
+    """All weights of a model: {"spec", "layers": [...], "final_norm", "lm_head"}."""
+    m: Dict = {"spec": spec, "layers": [make_layer(spec, code, seed, il) for il in range(spec.n_layers)]}
+    m["final_norm"] = draw_gain(seed, code, T_FINAL_NORM, 0, spec.d) if spec.final_norm else None
+    m["lm_head"] = (draw_weight(spec.fmt, seed, code, T_LM_Q, T_LM_D, 0, spec.vocab, spec.d)
+                    if spec.vocab else None)
+    return m
+
+
+def step_inputs(wl: Workload, step: int) -> np.ndarray:
+    """Fresh N(0,1) fp32 input rows ``[B, d]`` for one step (one stream per (step, row))."""
+    d = wl.spec.d
+    out = np.empty((wl.B, d), dtype=np.float32)
+    for b, (s, j) in enumerate(wl.rows):
+        out[b] = rng_for(wl.seed, wl.code, T_X_IN, step, 1000 * s + j).standard_normal(d, dtype=np.float32)
+    return out
+
+
+def kv_prefill(wl: Workload, session: int, layer: int) -> Tuple[np.ndarray, np.ndarray]:
+    """fp16 K and V ``[G, L, hd]`` already in the cache before step 0 (treated as post-RoPE)."""
+    sp = wl.spec
+    shape = (sp.n_head_kv, wl.prefill[session], sp.head_dim)
+    rk = rng_for(wl.seed, wl.code, T_K_PRE, layer, session)
+    rv = rng_for(wl.seed, wl.code, T_V_PRE, layer, session)
+    k = rk.standard_normal(shape, dtype=np.float32).astype(np.float16)
+    v = rv.standard_normal(shape, dtype=np.float32).astype(np.float16)
+    return k, v
+
+
+def algorithmic_bytes_weights(spec: ModelSpec) -> int:
+    """Bytes of every quantised matrix and fp32 router the step streams once (dense view)."""
+    bpw = 34 if spec.fmt == "q8_0" else 18     # bytes per 32-element block
+
+    def mat(n, k):
+        return n * (k // 32) * bpw
+
+    tot = 0
+    for _ in range(spec.n_layers):
+        tot += mat(spec.qkv_rows, spec.d) + mat(spec.d, spec.n_head * spec.head_dim)
+        if spec.ffn:
+            tot += 2 * mat(spec.ffn, spec.d) + mat(spec.d, spec.ffn)
+        if spec.n_experts:
+            tot += spec.n_experts * spec.d * 4
+            tot += 2 * mat(spec.shared_ffn, spec.d) + mat(spec.d, spec.shared_ffn)
+    if spec.vocab:
+        tot += mat(spec.vocab, spec.d)
+    return tot
