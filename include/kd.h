@@ -1,0 +1,225 @@
+/*
+ * kd.h — C ABI of the batched multi-session decode step on MI355X (gfx950).
+ *
+ * One decode step for B in [1, 16] concurrent sessions: every block-quantised weight
+ * matrix is streamed from HBM once and applied to all B rows (mmvq at m = B), and each row
+ * attends over its own ragged-length fp16 KV cache with a split-K flash-decode.  The
+ * operation is the batched decode step of memra-engine 0.72.0 (src/decode_batch.rs:
+ * module header "bandwidth thesis" and "exactness contract", ``decode_batch_layers``) and
+ * the fused batch=N decode of hf2q ADR-040 (§0.4 corrected mental model, §0.7 F2-F5).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All pointers named as device pointers point to GPU memory owned by the caller (for
+ *    example allocated through torch); the library allocates no memory on any call.
+ *    Host arrays (positions, cache base-address tables, descriptors) are read during the
+ *    call only and may be freed when it returns.
+ *  - ``stream`` is a ``hipStream_t`` (NULL = the null stream).  Work is enqueued
+ *    asynchronously; no entry point synchronises the stream.
+ *  - Arguments are validated on the host before anything is enqueued.  On any error
+ *    nothing is enqueued and the status says why; ``kd_last_error()`` returns a
+ *    thread-local message.  KD_ERR_HIP means a launch failed; the stream's contents for
+ *    that call are then undefined.
+ *  - Row invariance: for every entry point, output row b depends only on input row b (and
+ *    on row b's own cache), never on B or on the other rows: the B-row result equals, bit
+ *    for bit, the 1-row call on row b alone (memra-engine decode_batch.rs exactness
+ *    contract; hf2q ADR-040 §0.12 execution log: the row-parity proof of the
+ *    batched lm_head and the dense-matmul row-identity fix).
+ *  - Calls that share a workspace must not overlap (use one workspace per stream).
+ *
+ * Native layouts (MI355X-first; produced by the pack / quantise entry points)
+ * --------------------------------------------------------------------------
+ *  A quantised matrix has n_out rows and k columns, k % 32 == 0, 32-element blocks.
+ *  NR = ceil(n_out / 16) row groups, NQ = ceil(k / 128) block quads.  Tile t = r * NQ + q
+ *  holds rows [16r, 16r + 16) x blocks [4q, 4q + 4); rows/blocks past the matrix are zero.
+ *  Inside a tile, "lane" l = 16 g + n (g in 0..3, n in 0..15) owns row 16r + n and the
+ *  eight block elements P_g = {4g..4g+3, 4g+16..4g+19} of each of the four blocks, so a
+ *  64-lane wave reads a tile with fully coalesced 16-byte loads and feeds it straight to
+ *  v_mfma_i32_16x16x32_i8 (K = 32 = one block).
+ *   - KD_FMT_Q8_0 qs: 2048 bytes per tile.  Bytes [h*1024 + 16 l, +16) = int8 codes P_g of
+ *     block 4q+2h (first 8 bytes) and of block 4q+2h+1 (last 8 bytes), h in {0,1}.
+ *   - KD_FMT_Q4_0 qs: 1024 bytes per tile.  Bytes [16 l + 4 j, +4) = bytes [4g, 4g+4) of
+ *     block 4q+j in GGUF order (low nibble = element i, high nibble = element i+16,
+ *     value = nibble - 8).
+ *   - d (both formats): fp16, 64 per tile: d[t * 64 + 4 n + j] = scale of row 16r+n,
+ *     block 4q+j.
+ *  Quantised activations (kd_act_q8) for B rows of length k: int8 codes
+ *  qs[(b * NQ + q) * 128 + 32 g + 8 j + e] = code of element P_g[e] of block 4q+j of row b,
+ *  and fp32 scales d[b * 4 NQ + blk]; padded blocks have code 0 and scale 0.
+ *  KV caches: per (session, layer) one K and one V array, fp16 [G][capacity][hd]
+ *  (head-major: each KV head's keys are one contiguous stream).
+ */
+#ifndef KD_H
+#define KD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KD_OK = 0,
+  KD_ERR_INVALID = -1,      /* null pointer, bad shape, mismatched counts */
+  KD_ERR_UNSUPPORTED = -2,  /* B outside [1,16], k % 32 != 0, head_dim not 64/128, H % G != 0, format */
+  KD_ERR_CAPACITY = -3,     /* a row's pos + 1 exceeds the cache capacity */
+  KD_ERR_WORKSPACE = -4,    /* workspace too small or null */
+  KD_ERR_HIP = -5           /* a HIP launch failed */
+} kd_status;
+
+typedef enum { KD_FMT_Q8_0 = 1, KD_FMT_Q4_0 = 2, KD_FMT_F32 = 3 } kd_format;
+
+#define KD_MAX_B 16
+
+/* A quantised matrix in the native tiled layout (device pointers, 16-byte aligned).
+ * For KD_FMT_F32 (router only): qs is float [n_out][k] row-major and d is NULL. */
+typedef struct {
+  int32_t fmt;
+  int32_t n_out;
+  int32_t k;
+  const void* qs;
+  const void* d;
+} kd_weight;
+
+/* Quantised activations in the native layout (device pointers). */
+typedef struct {
+  int8_t* qs;
+  float* d;
+} kd_act_q8;
+
+const char* kd_version(void);
+const char* kd_last_error(void);
+
+/* ---- layouts ------------------------------------------------------------------------ */
+/* Bytes of the tiled qs and d arrays of an n_out x k matrix (0 on bad arguments). */
+size_t kd_weight_qs_bytes(int32_t fmt, int32_t n_out, int32_t k);
+size_t kd_weight_d_bytes(int32_t fmt, int32_t n_out, int32_t k);
+/* Bytes of the qs and d arrays of B quantised activation rows of length k. */
+size_t kd_act_qs_bytes(int32_t B, int32_t k);
+size_t kd_act_d_bytes(int32_t B, int32_t k);
+
+/* Repack a matrix from the row-major block layout (Q8_0: int8 [n_out][k]; Q4_0: uint8
+ * [n_out][k/2], 16 bytes per block; d: fp16 [n_out][k/32]; device pointers) into the tiled
+ * layout above (dst_qs / dst_d sized by kd_weight_*_bytes).  Once per matrix, at load. */
+kd_status kd_pack_weight(int32_t fmt, int32_t n_out, int32_t k, const void* src_qs, const void* src_d,
+                         void* dst_qs, void* dst_d, void* stream);
+
+/* ---- activation quantiser ----------------------------------------------------------- */
+/* Q(x) of fp32 rows x[B][k] (row stride ldx floats): per 32-element block a = max|x_i|,
+ * d = a / 127 (IEEE fp32 division; 0 if a == 0), q_i = round-half-away(x_i / d) clamped
+ * to [-127, 127].  The activation operand of every m = B product (memra-engine
+ * decode_batch.rs, ``quantize_q8_1`` in ``decode_batch_layers``). */
+kd_status kd_quantize_act_q8(const float* x, int32_t B, int32_t k, int32_t ldx, kd_act_q8 out, void* stream);
+
+/* ---- mmvq at m = B -------------------------------------------------------------------- */
+/* y[b][n] = sum_blk d_w[n][blk] * d_x[b][blk] * S[b][n][blk], S = exact int32 block dot of
+ * the codes, for n < W->n_out, b < B; y row stride ldy floats (>= n_out).  One pass over
+ * the weights serves all B rows (memra-engine decode_batch.rs ``matmul_pre`` at m = B;
+ * hf2q ADR-040 §0.7 F3).  The fp32 accumulation order of each output depends only on k.
+ * W->fmt must match the entry point. */
+kd_status kd_mmvq_q8_0(const kd_weight* W, kd_act_q8 x, int32_t B, float* y, int32_t ldy, void* stream);
+kd_status kd_mmvq_q4_0(const kd_weight* W, kd_act_q8 x, int32_t B, float* y, int32_t ldy, void* stream);
+
+/* ---- row operations (fp32, rows of length n, row stride n) ------------------------- */
+/* y = x / sqrt(mean(x^2) + eps) * g  (memra-engine decode_batch.rs attn_norm / output norm). */
+kd_status kd_rmsnorm_rows(const float* x, const float* g, float* y, int32_t B, int32_t n, float eps, void* stream);
+/* x1 = x + r; y = rmsnorm(x1, g)  (memra-engine decode_batch.rs ``add_rms_norm``). */
+kd_status kd_add_rmsnorm_rows(const float* x, const float* r, const float* g, float* x1, float* y,
+                              int32_t B, int32_t n, float eps, void* stream);
+/* In-place NEOX RoPE of x[B][n_heads][hd]: element i < hd/2 pairs with i + hd/2 and both
+ * rotate by pos[b] * base^(-2i/hd); angles and their cos/sin are evaluated in fp64 and
+ * rounded to fp32 (memra-engine decode_batch.rs ``rope_neox`` with the per-row position
+ * buffer).  pos is a host array [B]. */
+kd_status kd_rope_neox_rows(float* x, int32_t B, int32_t n_heads, int32_t hd, const int32_t* pos,
+                            float base, void* stream);
+/* a = silu(g) * u  (memra-engine decode_batch.rs ``silu_mul``). */
+kd_status kd_swiglu_rows(const float* g, const float* u, float* a, int32_t B, int32_t n, void* stream);
+/* z = x + y  (memra-engine decode_batch.rs residual ``add``). */
+kd_status kd_add_rows(const float* x, const float* y, float* z, int32_t B, int32_t n, void* stream);
+
+/* ---- KV append and ragged split-K decode attention --------------------------------- */
+/* Store row b's k[b][G][hd] and v[b][G][hd] (fp32, rounded to fp16 nearest-even) at
+ * position pos[b] of its own cache: K_b[g][pos[b]][:] (memra-engine decode_batch.rs phase A,
+ * one launch for all B rows through the per-row cache pointer table).  k_base / v_base /
+ * pos are host arrays [B]; several rows may share a cache only at distinct positions. */
+kd_status kd_kv_append(const float* k, const float* v, int32_t B, int32_t G, int32_t hd,
+                       void* const* k_base, void* const* v_base, const int32_t* pos,
+                       int32_t capacity, void* stream);
+/* Workspace bytes of kd_fa_decode_ragged for these per-row key counts (host t_kv[B]). */
+size_t kd_fa_decode_workspace(int32_t B, int32_t H, int32_t hd, const int32_t* t_kv);
+/* out[b][h][:] = sum_j softmax_j(q[b][h] . K_b[g][j] * scale) V_b[g][j], j < t_kv[b],
+ * g = h / (H/G) (memra-engine decode_batch.rs phase B, ``fa_decode_batch_seqs_v4``: one
+ * launch over all rows plus one combine).  Keys are split into chunks of
+ * c_b = max(128, ceil(t_b / 128)) — a function of the row's own t_kv only — and the chunk
+ * partials are merged in chunk order.  q, out: fp32 [B][H][hd]; caches fp16 [G][capacity][hd];
+ * H/G must be 1, 2, 4 or 8, hd 64 or 128, 1 <= t_kv[b] <= min(capacity, 131072). */
+kd_status kd_fa_decode_ragged(const float* q, int32_t B, int32_t H, int32_t G, int32_t hd,
+                              const void* const* k_base, const void* const* v_base,
+                              const int32_t* t_kv, int32_t capacity, float scale, float* out,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* ---- whole step ---------------------------------------------------------------------- */
+typedef struct {
+  const float* attn_norm;   /* [d] */
+  kd_weight wqkv;           /* [(H + 2G) hd, d]: rows q (H hd), then k (G hd), then v (G hd) */
+  kd_weight wo;             /* [d, H hd] */
+  const float* ffn_norm;    /* [d]; NULL for an attention-only layer */
+  kd_weight w_gate, w_up;   /* dense SwiGLU [F, d] (qs NULL if MoE or attention-only) */
+  kd_weight w_down;         /* [d, F] */
+  const float* router;      /* MoE: fp32 [E][d] */
+  kd_weight e_gate, e_up;   /* MoE: experts stacked by rows, expert e = rows [e Fe, (e+1) Fe) of [E Fe, d] */
+  kd_weight e_down;         /* MoE: expert e = rows [e d, (e+1) d) of [E d, Fe] */
+  kd_weight s_gate, s_up;   /* MoE shared expert [Fs, d] */
+  kd_weight s_down;         /* [d, Fs] */
+} kd_layer_desc;
+
+typedef struct {
+  int32_t n_layers, d, n_head, n_head_kv, head_dim;
+  int32_t ffn;                           /* dense SwiGLU width, 0 if none */
+  int32_t n_experts, n_expert_used;      /* 0 = dense */
+  int32_t expert_ffn, shared_ffn;
+  int32_t vocab;                         /* lm_head rows, 0 = none */
+  float rope_base, rms_eps;
+  const kd_layer_desc* layers;           /* host array [n_layers] (copied by kd_model_create) */
+  const float* final_norm;               /* [d] or NULL */
+  kd_weight lm_head;                     /* [vocab, d] or qs NULL */
+} kd_model_desc;
+
+typedef struct kd_model kd_model;
+
+/* Validate a descriptor and keep a host copy of it (device pointers are borrowed, not
+ * owned).  The model is immutable and may be shared across threads and streams. */
+kd_status kd_model_create(const kd_model_desc* desc, kd_model** out);
+void kd_model_destroy(kd_model* m);
+
+/* Workspace bytes of kd_decode_step for B rows with these positions (host pos[B]). */
+size_t kd_decode_step_workspace(const kd_model* m, int32_t B, const int32_t* pos);
+
+/* One decode step for B rows: x_in fp32 [B][d]; row b writes K/V at pos[b] of its caches
+ * and attends pos[b] + 1 keys; all appends of a layer precede its attention, so rows that
+ * share a cache at consecutive positions (speculative-verify rows) attend causally.
+ * k_base / v_base: host arrays [n_layers][B] of cache base addresses.  out: fp32
+ * [B][vocab] logits if the model has an lm_head, else [B][d] (output-normed if final_norm).
+ * Positions are not advanced: the caller owns session state (memra-engine
+ * decode_batch.rs ``decode_batch_epilogue`` advances pos after the step). */
+kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x_in, const int32_t* pos,
+                         void* const* k_base, void* const* v_base, int32_t capacity, float* out,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* ---- test exports ---------------------------------------------------------------------- */
+/* The exact int32 block dot products S[b][n][blk] (b < B, n < n_out, blk < k/32) that the
+ * mmvq kernel computes for this matrix and activation (same kernel, epilogue replaced). */
+kd_status kd_debug_block_dots(const kd_weight* W, kd_act_q8 x, int32_t B, int32_t* S, void* stream);
+/* kd_fa_decode_ragged with a forced chunk size (keys per split, >= 1) for split-invariance
+ * tests; the workspace must hold ceil(t_b / chunk) splits per row. */
+size_t kd_debug_fa_workspace(int32_t B, int32_t H, int32_t hd, const int32_t* t_kv, int32_t chunk);
+kd_status kd_debug_fa_decode_chunked(const float* q, int32_t B, int32_t H, int32_t G, int32_t hd,
+                                     const void* const* k_base, const void* const* v_base,
+                                     const int32_t* t_kv, int32_t capacity, float scale, float* out,
+                                     int32_t chunk, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KD_H */

@@ -1,0 +1,380 @@
+"""Python binding of libkd.so — the batched multi-session decode step on MI355X.
+
+Argument marshalling only: every step of the decode path runs in the HIP kernels behind
+the C ABI declared in ``include/kd.h``.  PyTorch provides device memory and the current
+stream.  There is no fallback: if the library is not built, importing the binding's
+entry points raises.
+
+The wrappers keep the C names (``kd_mmvq_q8_0`` ...) and take torch tensors.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkd.so")
+
+KD_OK, KD_ERR_INVALID, KD_ERR_UNSUPPORTED, KD_ERR_CAPACITY, KD_ERR_WORKSPACE, KD_ERR_HIP = 0, -1, -2, -3, -4, -5
+KD_FMT_Q8_0, KD_FMT_Q4_0, KD_FMT_F32 = 1, 2, 3
+FMT_CODE = {"q8_0": KD_FMT_Q8_0, "q4_0": KD_FMT_Q4_0}
+KD_MAX_B = 16
+
+
+class KdError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"[{status}] {msg}")
+        self.status = status
+
+
+class KdWeight(C.Structure):
+    _fields_ = [("fmt", C.c_int32), ("n_out", C.c_int32), ("k", C.c_int32), ("qs", C.c_void_p), ("d", C.c_void_p)]
+
+
+class KdAct(C.Structure):
+    _fields_ = [("qs", C.c_void_p), ("d", C.c_void_p)]
+
+
+class KdLayerDesc(C.Structure):
+    _fields_ = [("attn_norm", C.c_void_p), ("wqkv", KdWeight), ("wo", KdWeight), ("ffn_norm", C.c_void_p),
+                ("w_gate", KdWeight), ("w_up", KdWeight), ("w_down", KdWeight), ("router", C.c_void_p),
+                ("e_gate", KdWeight), ("e_up", KdWeight), ("e_down", KdWeight),
+                ("s_gate", KdWeight), ("s_up", KdWeight), ("s_down", KdWeight)]
+
+
+class KdModelDesc(C.Structure):
+    _fields_ = [("n_layers", C.c_int32), ("d", C.c_int32), ("n_head", C.c_int32), ("n_head_kv", C.c_int32),
+                ("head_dim", C.c_int32), ("ffn", C.c_int32), ("n_experts", C.c_int32), ("n_expert_used", C.c_int32),
+                ("expert_ffn", C.c_int32), ("shared_ffn", C.c_int32), ("vocab", C.c_int32),
+                ("rope_base", C.c_float), ("rms_eps", C.c_float), ("layers", C.POINTER(KdLayerDesc)),
+                ("final_norm", C.c_void_p), ("lm_head", KdWeight)]
+
+
+_P, _I, _F, _S = C.c_void_p, C.c_int32, C.c_float, C.c_size_t
+_PW = C.POINTER(KdWeight)
+_PP = C.POINTER(C.c_void_p)
+_PI = C.POINTER(C.c_int32)
+
+# name -> (restype, argtypes); the ABI surface of include/kd.h
+SIGNATURES = {
+    "kd_version": (C.c_char_p, []),
+    "kd_last_error": (C.c_char_p, []),
+    "kd_weight_qs_bytes": (_S, [_I, _I, _I]),
+    "kd_weight_d_bytes": (_S, [_I, _I, _I]),
+    "kd_act_qs_bytes": (_S, [_I, _I]),
+    "kd_act_d_bytes": (_S, [_I, _I]),
+    "kd_pack_weight": (_I, [_I, _I, _I, _P, _P, _P, _P, _P]),
+    "kd_quantize_act_q8": (_I, [_P, _I, _I, _I, KdAct, _P]),
+    "kd_mmvq_q8_0": (_I, [_PW, KdAct, _I, _P, _I, _P]),
+    "kd_mmvq_q4_0": (_I, [_PW, KdAct, _I, _P, _I, _P]),
+    "kd_rmsnorm_rows": (_I, [_P, _P, _P, _I, _I, _F, _P]),
+    "kd_add_rmsnorm_rows": (_I, [_P, _P, _P, _P, _P, _I, _I, _F, _P]),
+    "kd_rope_neox_rows": (_I, [_P, _I, _I, _I, _PI, _F, _P]),
+    "kd_swiglu_rows": (_I, [_P, _P, _P, _I, _I, _P]),
+    "kd_add_rows": (_I, [_P, _P, _P, _I, _I, _P]),
+    "kd_kv_append": (_I, [_P, _P, _I, _I, _I, _PP, _PP, _PI, _I, _P]),
+    "kd_fa_decode_workspace": (_S, [_I, _I, _I, _PI]),
+    "kd_fa_decode_ragged": (_I, [_P, _I, _I, _I, _I, _PP, _PP, _PI, _I, _F, _P, _P, _S, _P]),
+    "kd_model_create": (_I, [C.POINTER(KdModelDesc), C.POINTER(_P)]),
+    "kd_model_destroy": (None, [_P]),
+    "kd_decode_step_workspace": (_S, [_P, _I, _PI]),
+    "kd_decode_step": (_I, [_P, _I, _P, _PI, _PP, _PP, _I, _P, _P, _S, _P]),
+    "kd_debug_block_dots": (_I, [_PW, KdAct, _I, _P, _P]),
+    "kd_debug_fa_workspace": (_S, [_I, _I, _I, _PI, _I]),
+    "kd_debug_fa_decode_chunked": (_I, [_P, _I, _I, _I, _I, _PP, _PP, _PI, _I, _F, _P, _I, _P, _S, _P]),
+}
+
+_lib: Optional[C.CDLL] = None
+
+
+def lib() -> C.CDLL:
+    """The loaded libkd.so (raises if it has not been built: there is no fallback path)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run `python -m session_decode_step_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int, name: str) -> None:
+    if status != KD_OK:
+        raise KdError(status, f"{name}: {lib().kd_last_error().decode()}")
+
+
+def _stream(stream=None) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _i32(seq: Sequence[int]):
+    arr = (C.c_int32 * len(seq))(*[int(v) for v in seq])
+    return arr
+
+
+def _ptrs(seq: Sequence[int]):
+    return (C.c_void_p * len(seq))(*[int(v) for v in seq])
+
+
+def kd_version() -> str:
+    return lib().kd_version().decode()
+
+
+# ------------------------------------------------------------------------------ weights
+@dataclass
+class PackedWeight:
+    fmt: int
+    n_out: int
+    k: int
+    qs: torch.Tensor
+    d: Optional[torch.Tensor]
+
+    def c(self) -> KdWeight:
+        return KdWeight(self.fmt, self.n_out, self.k, self.qs.data_ptr(), self.d.data_ptr() if self.d is not None else None)
+
+    @property
+    def nbytes(self) -> int:
+        return self.qs.numel() * self.qs.element_size() + (0 if self.d is None else self.d.numel() * 2)
+
+
+def kd_pack_weight(w: Dict, device="cuda", stream=None) -> PackedWeight:
+    """Upload a row-major block matrix (``{"fmt","n","k","qs","d"}`` numpy) and repack it on the GPU."""
+    fmt, n, k = FMT_CODE[w["fmt"]], int(w["n"]), int(w["k"])
+    src_qs = torch.from_numpy(np.ascontiguousarray(w["qs"]).view(np.uint8)).to(device)
+    src_d = torch.from_numpy(np.ascontiguousarray(w["d"]).view(np.int16)).to(device)
+    qs = torch.empty(lib().kd_weight_qs_bytes(fmt, n, k), dtype=torch.uint8, device=device)
+    dd = torch.empty(lib().kd_weight_d_bytes(fmt, n, k) // 2, dtype=torch.int16, device=device)
+    _check(lib().kd_pack_weight(fmt, n, k, src_qs.data_ptr(), src_d.data_ptr(), qs.data_ptr(), dd.data_ptr(),
+                                _stream(stream)), "kd_pack_weight")
+    torch.cuda.current_stream().synchronize()   # the sources are freed on return
+    return PackedWeight(fmt, n, k, qs, dd)
+
+
+def expert_view(w: PackedWeight, n_out: int) -> PackedWeight:
+    return PackedWeight(w.fmt, n_out, w.k, w.qs, w.d)
+
+
+# ------------------------------------------------------------------------------ activations
+@dataclass
+class Act:
+    qs: torch.Tensor
+    d: torch.Tensor
+    B: int
+    k: int
+
+    def c(self) -> KdAct:
+        return KdAct(self.qs.data_ptr(), self.d.data_ptr())
+
+
+def alloc_act(B: int, k: int, device="cuda") -> Act:
+    qs = torch.empty(lib().kd_act_qs_bytes(B, k), dtype=torch.int8, device=device)
+    d = torch.empty(lib().kd_act_d_bytes(B, k) // 4, dtype=torch.float32, device=device)
+    return Act(qs, d, B, k)
+
+
+def kd_quantize_act_q8(x: torch.Tensor, out: Optional[Act] = None, stream=None) -> Act:
+    B, k = x.shape
+    out = out or alloc_act(B, k, x.device)
+    _check(lib().kd_quantize_act_q8(x.data_ptr(), B, k, x.stride(0), out.c(), _stream(stream)), "kd_quantize_act_q8")
+    return out
+
+
+def _mmvq(name: str, W: PackedWeight, x: Act, B: int, y: Optional[torch.Tensor], stream) -> torch.Tensor:
+    if y is None:
+        y = torch.empty((B, W.n_out), dtype=torch.float32, device=x.qs.device)
+    wc = W.c()
+    _check(getattr(lib(), name)(C.byref(wc), x.c(), B, y.data_ptr(), y.stride(0), _stream(stream)), name)
+    return y
+
+
+def kd_mmvq_q8_0(W: PackedWeight, x: Act, B: int, y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    return _mmvq("kd_mmvq_q8_0", W, x, B, y, stream)
+
+
+def kd_mmvq_q4_0(W: PackedWeight, x: Act, B: int, y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    return _mmvq("kd_mmvq_q4_0", W, x, B, y, stream)
+
+
+def kd_debug_block_dots(W: PackedWeight, x: Act, B: int, stream=None) -> torch.Tensor:
+    S = torch.empty((B, W.n_out, W.k // 32), dtype=torch.int32, device=x.qs.device)
+    wc = W.c()
+    _check(lib().kd_debug_block_dots(C.byref(wc), x.c(), B, S.data_ptr(), _stream(stream)), "kd_debug_block_dots")
+    return S
+
+
+# ------------------------------------------------------------------------------ row ops
+def kd_rmsnorm_rows(x: torch.Tensor, g: torch.Tensor, eps: float, stream=None) -> torch.Tensor:
+    y = torch.empty_like(x)
+    _check(lib().kd_rmsnorm_rows(x.data_ptr(), g.data_ptr(), y.data_ptr(), x.shape[0], x.shape[1], eps,
+                                 _stream(stream)), "kd_rmsnorm_rows")
+    return y
+
+
+def kd_add_rmsnorm_rows(x: torch.Tensor, r: torch.Tensor, g: torch.Tensor, eps: float, stream=None):
+    x1, y = torch.empty_like(x), torch.empty_like(x)
+    _check(lib().kd_add_rmsnorm_rows(x.data_ptr(), r.data_ptr(), g.data_ptr(), x1.data_ptr(), y.data_ptr(),
+                                     x.shape[0], x.shape[1], eps, _stream(stream)), "kd_add_rmsnorm_rows")
+    return x1, y
+
+
+def kd_rope_neox_rows(x: torch.Tensor, pos: Sequence[int], base: float, stream=None) -> torch.Tensor:
+    B, nh, hd = x.shape
+    _check(lib().kd_rope_neox_rows(x.data_ptr(), B, nh, hd, _i32(pos), base, _stream(stream)), "kd_rope_neox_rows")
+    return x
+
+
+def kd_swiglu_rows(g: torch.Tensor, u: torch.Tensor, stream=None) -> torch.Tensor:
+    a = torch.empty_like(g)
+    _check(lib().kd_swiglu_rows(g.data_ptr(), u.data_ptr(), a.data_ptr(), g.shape[0], g.shape[1], _stream(stream)),
+           "kd_swiglu_rows")
+    return a
+
+
+def kd_add_rows(x: torch.Tensor, y: torch.Tensor, stream=None) -> torch.Tensor:
+    z = torch.empty_like(x)
+    _check(lib().kd_add_rows(x.data_ptr(), y.data_ptr(), z.data_ptr(), x.shape[0], x.shape[1], _stream(stream)),
+           "kd_add_rows")
+    return z
+
+
+# ------------------------------------------------------------------------------ KV + attention
+def kd_kv_append(k: torch.Tensor, v: torch.Tensor, k_base: Sequence[int], v_base: Sequence[int], pos: Sequence[int],
+                 capacity: int, stream=None) -> None:
+    B, G, hd = k.shape
+    _check(lib().kd_kv_append(k.data_ptr(), v.data_ptr(), B, G, hd, _ptrs(k_base), _ptrs(v_base), _i32(pos), capacity,
+                              _stream(stream)), "kd_kv_append")
+
+
+def kd_fa_decode_workspace(B: int, H: int, hd: int, t_kv: Sequence[int]) -> int:
+    return lib().kd_fa_decode_workspace(B, H, hd, _i32(t_kv))
+
+
+def kd_fa_decode_ragged(q: torch.Tensor, G: int, k_base, v_base, t_kv, capacity: int, scale: float,
+                        ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None, chunk: int = 0,
+                        stream=None) -> torch.Tensor:
+    B, H, hd = q.shape
+    out = torch.empty_like(q) if out is None else out
+    if chunk:
+        need = lib().kd_debug_fa_workspace(B, H, hd, _i32(t_kv), chunk)
+    else:
+        need = kd_fa_decode_workspace(B, H, hd, t_kv)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if chunk:
+        st = lib().kd_debug_fa_decode_chunked(q.data_ptr(), B, H, G, hd, _ptrs(k_base), _ptrs(v_base), _i32(t_kv),
+                                              capacity, scale, out.data_ptr(), chunk, ws.data_ptr(), ws.numel(),
+                                              _stream(stream))
+        _check(st, "kd_debug_fa_decode_chunked")
+    else:
+        st = lib().kd_fa_decode_ragged(q.data_ptr(), B, H, G, hd, _ptrs(k_base), _ptrs(v_base), _i32(t_kv), capacity,
+                                       scale, out.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream))
+        _check(st, "kd_fa_decode_ragged")
+    return out
+
+
+# ------------------------------------------------------------------------------ model + step
+class KdModel:
+    """Packs a model's weights (row-major block arrays, numpy) into device tiles and creates
+    the kd_model.  The tensors it holds back the borrowed device pointers."""
+
+    def __init__(self, model: Dict, device="cuda"):
+        sp = model["spec"]
+        self.spec = sp
+        self.keep: List[torch.Tensor] = []
+        self.layers = (KdLayerDesc * sp.n_layers)()
+        self.weight_bytes = 0
+        empty = KdWeight(0, 0, 0, None, None)
+
+        def W(w):
+            pw = kd_pack_weight(w, device)
+            self.keep += [pw.qs, pw.d]
+            self.weight_bytes += pw.nbytes
+            return pw.c()
+
+        def F(a):
+            t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+            self.keep.append(t)
+            return t.data_ptr()
+
+        for il, L in enumerate(model["layers"]):
+            D = self.layers[il]
+            D.attn_norm = F(L["attn_norm"])
+            D.wqkv = W(L["wqkv"])
+            D.wo = W(L["wo"])
+            D.ffn_norm = F(L["ffn_norm"]) if "ffn_norm" in L else None
+            D.w_gate, D.w_up, D.w_down = ((W(L["w_gate"]), W(L["w_up"]), W(L["w_down"])) if "w_gate" in L
+                                          else (empty, empty, empty))
+            if "router" in L:
+                D.router = F(L["router"])
+                D.e_gate, D.e_up, D.e_down = W(L["e_gate"]), W(L["e_up"]), W(L["e_down"])
+                D.s_gate, D.s_up, D.s_down = W(L["s_gate"]), W(L["s_up"]), W(L["s_down"])
+            else:
+                D.router = None
+                D.e_gate = D.e_up = D.e_down = D.s_gate = D.s_up = D.s_down = empty
+        self.desc = KdModelDesc(sp.n_layers, sp.d, sp.n_head, sp.n_head_kv, sp.head_dim, sp.ffn, sp.n_experts,
+                                sp.n_expert_used, sp.expert_ffn, sp.shared_ffn, sp.vocab, sp.rope_base, sp.rms_eps,
+                                self.layers, F(model["final_norm"]) if model["final_norm"] is not None else None,
+                                W(model["lm_head"]) if model["lm_head"] is not None else empty)
+        h = C.c_void_p()
+        _check(lib().kd_model_create(C.byref(self.desc), C.byref(h)), "kd_model_create")
+        self.handle = h
+
+    def __del__(self):
+        try:
+            if getattr(self, "handle", None):
+                lib().kd_model_destroy(self.handle)
+                self.handle = None
+        except Exception:
+            pass
+
+    def workspace_bytes(self, B: int, pos: Sequence[int]) -> int:
+        return lib().kd_decode_step_workspace(self.handle, B, _i32(pos))
+
+    def kd_decode_step(self, x_in: torch.Tensor, pos: Sequence[int], k_base: Sequence[int], v_base: Sequence[int],
+                       capacity: int, out: torch.Tensor, ws: torch.Tensor, stream=None) -> torch.Tensor:
+        B = x_in.shape[0]
+        st = lib().kd_decode_step(self.handle, B, x_in.data_ptr(), _i32(pos), _ptrs(k_base), _ptrs(v_base), capacity,
+                                  out.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream))
+        _check(st, "kd_decode_step")
+        return out
+
+
+class SessionCaches:
+    """fp16 K/V caches of several sessions: one tensor [n_layers, 2, G, capacity, hd] per session."""
+
+    def __init__(self, n_sessions: int, n_layers: int, G: int, capacity: int, hd: int, device="cuda"):
+        self.n_layers, self.G, self.capacity, self.hd = n_layers, G, capacity, hd
+        self.t = [torch.zeros((n_layers, 2, G, capacity, hd), dtype=torch.float16, device=device)
+                  for _ in range(n_sessions)]
+
+    def k_ptr(self, s: int, il: int) -> int:
+        return self.t[s][il, 0].data_ptr()
+
+    def v_ptr(self, s: int, il: int) -> int:
+        return self.t[s][il, 1].data_ptr()
+
+    def tables(self, sessions: Sequence[int]):
+        """Host tables [n_layers][B] of K and V base addresses for rows reading these sessions."""
+        kb = [self.k_ptr(s, il) for il in range(self.n_layers) for s in sessions]
+        vb = [self.v_ptr(s, il) for il in range(self.n_layers) for s in sessions]
+        return kb, vb
+
+    def fill_prefill(self, s: int, il: int, k: np.ndarray, v: np.ndarray) -> None:
+        L = k.shape[1]
+        self.t[s][il, 0, :, :L] = torch.from_numpy(k).to(self.t[s].device)
+        self.t[s][il, 1, :, :L] = torch.from_numpy(v).to(self.t[s].device)

@@ -1,0 +1,150 @@
+// Internal declarations shared by the kd HIP sources (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/kd.h"
+
+namespace kd {
+
+void set_error(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
+// Checks hipGetLastError after a launch; sets the message and returns KD_ERR_HIP on failure.
+kd_status check_launch(const char* what);
+
+#define KD_REQUIRE(cond, code, ...)  \
+  do {                               \
+    if (!(cond)) {                   \
+      ::kd::set_error(__VA_ARGS__);  \
+      return (code);                 \
+    }                                \
+  } while (0)
+
+__host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Quads of 4 blocks (128 elements) along k.
+__host__ __device__ inline int n_quads(int k) { return ceil_div(k, 128); }
+__host__ __device__ inline int n_rowgroups(int n_out) { return ceil_div(n_out, 16); }
+
+// ---- device helpers -------------------------------------------------------------------
+__device__ inline uint32_t pack4b(int a, int b, int c, int d) {
+  return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) | ((uint32_t)(c & 0xFF) << 16) |
+         ((uint32_t)(d & 0xFF) << 24);
+}
+
+// Activation quantiser on one 32-element block v[0..31]: a = max|v_i|; d = a / 127 (IEEE fp32
+// division; 0 if a == 0); q_i = round-half-away(v_i / d) clamped to [-127, 127].  Codes are
+// stored in the tiled activation layout (dst_block = row base + q*128 + j*8; group g's eight
+// codes P_g = {4g..4g+3, 4g+16..4g+19} at dst_block + 32 g) and the scale at *d_out.
+__device__ inline void quant32(const float* v, int8_t* dst_block, float* d_out) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const float dd = amax / 127.0f;
+  int c[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    int qv = 0;
+    if (amax != 0.0f) {
+      qv = (int)roundf(v[i] / dd);
+      qv = qv > 127 ? 127 : (qv < -127 ? -127 : qv);
+    }
+    c[i] = qv;
+  }
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    uint2 w;
+    w.x = pack4b(c[4 * g], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]);
+    w.y = pack4b(c[4 * g + 16], c[4 * g + 17], c[4 * g + 18], c[4 * g + 19]);
+    *reinterpret_cast<uint2*>(dst_block + g * 32) = w;
+  }
+  *d_out = dd;
+}
+
+__device__ inline float wave_sum(float v) {
+  // xor butterfly: every lane ends with the same value (fp add is commutative).
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+// ---- launchers used by the step driver (arguments already validated) -------------------
+void launch_act_quant(const float* x, int B, int k, int ldx, int8_t* qs, float* d, hipStream_t st);
+// Fused RMSNorm (optionally with a residual add) + activation quantiser.  If r != nullptr:
+// x1 = x + r is written to x1_out.  y = rmsnorm(x or x1) is written to y_out if non-null.
+// The quantised y goes to (qs, d) if qs != nullptr.
+void launch_norm_quant(const float* x, const float* r, const float* g, int B, int n, float eps,
+                       float* x1_out, float* y_out, int8_t* qs, float* d, hipStream_t st);
+
+// Row maps for grouped (MoE) products: output row j of group e reads activation row
+// act_row[e*16 + j] and writes output row out_row[e*16 + j], j < count[e].
+struct RowMap {
+  const int32_t* count;    // [n_groups]
+  const int32_t* act_row;  // [n_groups * 16]
+  const int32_t* out_row;  // [n_groups * 16]
+  int n_groups;
+  long long w_group_tiles;  // tiles between consecutive groups' weights
+};
+
+void launch_mmvq(const kd_weight& W, const int8_t* xq, const float* xd, int B, float* y, int ldy,
+                 hipStream_t st, const RowMap* map = nullptr, int32_t* debug_S = nullptr);
+
+// Per-row cache addresses and positions of one layer, passed by value as a kernel argument
+// (B <= 16 rows: no host-to-device copy and no synchronisation per step).
+struct RowCaches {
+  void* k[KD_MAX_B];
+  void* v[KD_MAX_B];
+  int32_t pos[KD_MAX_B];
+};
+
+// cos/sin table [B][hd/2][2] fp32 from per-row positions (angles in fp64).
+void launch_rope_table(const RowCaches& rc, int B, int hd, float base, float* cs, hipStream_t st);
+// Rotates q (in place, rows of qkv with stride ldqkv) and k, rounds k and v to fp16 and
+// stores them at each row's position (append) or only rotates (q and k heads).  cs is the
+// per-step table, or null to evaluate cos/sin inline with the same fp64 expression.
+void launch_rope_append(float* qkv, int ldqkv, int B, int H, int G, int hd, const float* cs,
+                        const RowCaches& rc, int capacity, bool append, hipStream_t st, float base);
+void launch_kv_append(const float* k, const float* v, int B, int G, int hd, const RowCaches& rc, int capacity,
+                      hipStream_t st);
+
+struct FaPlan {
+  int B, H, G, hd;
+  int n_items;                        // total (row, split) items
+  int32_t split_off[KD_MAX_B + 1];    // prefix sums of splits per row
+  int32_t chunk[KD_MAX_B];            // keys per split of each row
+  int32_t t_kv[KD_MAX_B];             // keys attended by each row
+};
+int fa_chunk_for(int t_kv);
+bool fa_make_plan(FaPlan& p, int B, int H, int G, int hd, const int32_t* t_kv, int forced_chunk);
+size_t fa_workspace_bytes(const FaPlan& p);
+// q/out fp32 [B][H][hd] (row stride ldq / H*hd); if out_qs != nullptr the combine also
+// writes the quantised output rows.
+void launch_fa(const FaPlan& p, const float* q, int ldq, const RowCaches& rc, int capacity, float scale,
+               float* out, int8_t* out_qs, float* out_d, void* ws, hipStream_t st);
+bool fa_shape_supported(int H, int G, int hd);
+int fa_max_keys();
+
+void launch_swiglu_quant(const float* g, const float* u, int rows, int n, int ld, float* a_out, int8_t* qs,
+                         float* d, hipStream_t st);
+void launch_add(const float* x, const float* y, float* z, size_t n, hipStream_t st);
+
+void launch_router(const float* z, const float* Wr, int B, int d, int E, int K, int32_t* ids, float* p, float* logits,
+                   hipStream_t st);
+void launch_bucket(const int32_t* ids, int B, int K, int E, int32_t* count, int32_t* rows, int32_t* pairs,
+                   hipStream_t st);
+void launch_moe_combine(const float* y, const float* p, const float* sh, int B, int K, int d, float* f, hipStream_t st);
+int moe_max_experts();
+int moe_max_topk();
+
+}  // namespace kd

@@ -1,0 +1,241 @@
+// Row-parallel operations of the batched decode step: RMSNorm (optionally fused with the
+// residual add and with the activation quantiser), NEOX RoPE with per-row positions fused
+// with the fp16 KV append, SwiGLU fused with the quantiser, and the residual add.
+//
+// These are the row ops that "batch trivially" on the memra-engine page (src/decode_batch.rs
+// module header) and that hf2q ADR-040 batches as single dispatches over N rows (§0.12,
+// batched norm / RoPE / KV-encode).  Every kernel processes each row independently with a
+// reduction order fixed by the row length, so row b's result never depends on B.
+#include "kd_internal.h"
+
+namespace kd {
+
+// ---------------------------------------------------------------------------------------
+// RMSNorm (+ residual add) (+ quantise).  One 256-thread workgroup per row.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void norm_quant_kernel(const float* __restrict__ x, const float* __restrict__ r,
+                                                         const float* __restrict__ g, int n, float eps,
+                                                         float* __restrict__ x1_out, float* __restrict__ y_out,
+                                                         int8_t* __restrict__ qs, float* __restrict__ qd) {
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float* xr = x + (size_t)b * n;
+  const float* rr = r ? r + (size_t)b * n : nullptr;
+  float ss = 0.0f;
+  for (int i = tid; i < n; i += 256) {
+    const float v = rr ? xr[i] + rr[i] : xr[i];
+    ss = fmaf(v, v, ss);
+  }
+  ss = wave_sum(ss);
+  __shared__ float part[4];
+  if ((tid & 63) == 0) part[tid >> 6] = ss;
+  __syncthreads();
+  const float tot = ((part[0] + part[1]) + part[2]) + part[3];
+  const float inv = 1.0f / sqrtf(tot / (float)n + eps);
+  const int nb = n / 32;
+  const int NQ = n_quads(n);
+  for (int blk = tid; blk < NQ * 4; blk += 256) {
+    float v[32];
+    if (blk < nb) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int c = blk * 32 + i;
+        const float xv = rr ? xr[c] + rr[c] : xr[c];
+        if (x1_out) x1_out[(size_t)b * n + c] = xv;
+        v[i] = (xv * inv) * g[c];
+        if (y_out) y_out[(size_t)b * n + c] = v[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = 0.0f;
+    }
+    if (qs) quant32(v, qs + ((size_t)b * NQ + (blk >> 2)) * 128 + (blk & 3) * 8, qd + (size_t)b * NQ * 4 + blk);
+  }
+}
+
+void launch_norm_quant(const float* x, const float* r, const float* g, int B, int n, float eps, float* x1_out,
+                       float* y_out, int8_t* qs, float* d, hipStream_t st) {
+  norm_quant_kernel<<<B, 256, 0, st>>>(x, r, g, n, eps, x1_out, y_out, qs, d);
+}
+
+// ---------------------------------------------------------------------------------------
+// RoPE tables and RoPE + KV append
+// ---------------------------------------------------------------------------------------
+// cos/sin of pos * base^(-2i/hd), evaluated in fp64 and rounded to fp32.
+__device__ inline float2 rope_cs(int pos, int i, int hd, double base) {
+  const double theta = (double)pos * pow(base, -2.0 * (double)i / (double)hd);
+  double s, c;
+  sincos(theta, &s, &c);
+  return make_float2((float)c, (float)s);
+}
+
+__global__ void rope_table_kernel(RowCaches rc, int B, int hd, double base, float* __restrict__ cs) {
+  const int half = hd / 2;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= B * half) return;
+  const int b = idx / half, i = idx % half;
+  const float2 v = rope_cs(rc.pos[b], i, hd, base);
+  cs[2 * idx] = v.x;
+  cs[2 * idx + 1] = v.y;
+}
+
+void launch_rope_table(const RowCaches& rc, int B, int hd, float base, float* cs, hipStream_t st) {
+  const int total = B * hd / 2;
+  rope_table_kernel<<<ceil_div(total, 256), 256, 0, st>>>(rc, B, hd, (double)base, cs);
+}
+
+// grid (H + 2G, B); block hd/2 threads.  Head index h < H: query (rotate in place);
+// H <= h < H+G: key (rotate, store fp16); h >= H+G: value (store fp16).  cs is the per-step
+// table, or null to evaluate the same fp64 expression inline.
+__global__ void rope_append_kernel(float* __restrict__ qkv, int ldqkv, int H, int G, int hd,
+                                   const float* __restrict__ cs, double base, RowCaches rc, int capacity,
+                                   int append) {
+  const int h = blockIdx.x, b = blockIdx.y, i = threadIdx.x;
+  const int half = hd / 2;
+  float* row = qkv + (size_t)b * ldqkv + (size_t)h * hd;
+  const int pos = rc.pos[b];
+  if (h < H + G) {
+    const float2 t = cs ? make_float2(cs[2 * (b * half + i)], cs[2 * (b * half + i) + 1]) : rope_cs(pos, i, hd, base);
+    const float c = t.x, s = t.y;
+    const float x0 = row[i], x1 = row[i + half];
+    const float y0 = fmaf(x0, c, -(x1 * s));
+    const float y1 = fmaf(x0, s, x1 * c);
+    row[i] = y0;
+    row[i + half] = y1;
+    if (h >= H && append) {
+      __half* K = static_cast<__half*>(rc.k[b]) + ((size_t)(h - H) * capacity + pos) * hd;
+      K[i] = __float2half_rn(y0);
+      K[i + half] = __float2half_rn(y1);
+    }
+  } else if (append) {
+    __half* V = static_cast<__half*>(rc.v[b]) + ((size_t)(h - H - G) * capacity + pos) * hd;
+    V[i] = __float2half_rn(row[i]);
+    V[i + half] = __float2half_rn(row[i + half]);
+  }
+}
+
+void launch_rope_append(float* qkv, int ldqkv, int B, int H, int G, int hd, const float* cs, const RowCaches& rc,
+                        int capacity, bool append, hipStream_t st, float base) {
+  dim3 grid(append ? H + 2 * G : H + G, B);
+  rope_append_kernel<<<grid, hd / 2, 0, st>>>(qkv, ldqkv, H, G, hd, cs, (double)base, rc, capacity, append ? 1 : 0);
+}
+
+// Plain KV append (no rotation): k and v rows [B][G][hd] fp32 -> fp16 at pos.
+__global__ void kv_append_kernel(const float* __restrict__ k, const float* __restrict__ v, int G, int hd,
+                                 RowCaches rc, int capacity) {
+  const int g = blockIdx.x, b = blockIdx.y;
+  const size_t src = ((size_t)b * G + g) * hd;
+  __half* K = static_cast<__half*>(rc.k[b]) + ((size_t)g * capacity + rc.pos[b]) * hd;
+  __half* V = static_cast<__half*>(rc.v[b]) + ((size_t)g * capacity + rc.pos[b]) * hd;
+  for (int i = threadIdx.x; i < hd; i += blockDim.x) {
+    K[i] = __float2half_rn(k[src + i]);
+    V[i] = __float2half_rn(v[src + i]);
+  }
+}
+
+void launch_kv_append(const float* k, const float* v, int B, int G, int hd, const RowCaches& rc, int capacity,
+                      hipStream_t st) {
+  kv_append_kernel<<<dim3(G, B), 64, 0, st>>>(k, v, G, hd, rc, capacity);
+}
+
+// ---------------------------------------------------------------------------------------
+// SwiGLU (+ quantise): one thread per 32-element block.
+// ---------------------------------------------------------------------------------------
+__global__ void swiglu_quant_kernel(const float* __restrict__ g, const float* __restrict__ u, int rows, int n,
+                                    int ld, float* __restrict__ a_out, int8_t* __restrict__ qs,
+                                    float* __restrict__ qd) {
+  const int NQ = n_quads(n);
+  const int nbp = NQ * 4;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= rows * nbp) return;
+  const int b = idx / nbp, blk = idx % nbp;
+  float v[32];
+  if (blk * 32 < n) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int c = blk * 32 + i;
+      const float gv = g[(size_t)b * ld + c];
+      const float sv = gv / (1.0f + expf(-gv));
+      v[i] = sv * u[(size_t)b * ld + c];
+      if (a_out) a_out[(size_t)b * n + c] = v[i];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = 0.0f;
+  }
+  if (qs) quant32(v, qs + ((size_t)b * NQ + (blk >> 2)) * 128 + (blk & 3) * 8, qd + (size_t)b * nbp + blk);
+}
+
+void launch_swiglu_quant(const float* g, const float* u, int rows, int n, int ld, float* a_out, int8_t* qs, float* d,
+                         hipStream_t st) {
+  const int total = rows * n_quads(n) * 4;
+  swiglu_quant_kernel<<<ceil_div(total, 128), 128, 0, st>>>(g, u, rows, n, ld, a_out, qs, d);
+}
+
+__global__ void add_kernel(const float* __restrict__ x, const float* __restrict__ y, float* __restrict__ z, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) z[i] = x[i] + y[i];
+}
+
+void launch_add(const float* x, const float* y, float* z, size_t n, hipStream_t st) {
+  add_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(x, y, z, n);
+}
+
+}  // namespace kd
+
+using namespace kd;
+
+// ---------------------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------------------
+#define ROWS_OK(who, B, n)                                                                       \
+  KD_REQUIRE((B) >= 1 && (B) <= KD_MAX_B, KD_ERR_UNSUPPORTED, "%s: B=%d outside [1,16]", who, (int)(B)); \
+  KD_REQUIRE((n) > 0, KD_ERR_INVALID, "%s: n=%d", who, (int)(n))
+
+extern "C" kd_status kd_rmsnorm_rows(const float* x, const float* g, float* y, int32_t B, int32_t n, float eps,
+                                     void* stream) {
+  ROWS_OK("kd_rmsnorm_rows", B, n);
+  KD_REQUIRE(n % 32 == 0, KD_ERR_UNSUPPORTED, "kd_rmsnorm_rows: n=%d is not a multiple of 32", n);
+  KD_REQUIRE(x && g && y, KD_ERR_INVALID, "kd_rmsnorm_rows: null pointer");
+  launch_norm_quant(x, nullptr, g, B, n, eps, nullptr, y, nullptr, nullptr, as_stream(stream));
+  return check_launch("kd_rmsnorm_rows");
+}
+
+extern "C" kd_status kd_add_rmsnorm_rows(const float* x, const float* r, const float* g, float* x1, float* y,
+                                         int32_t B, int32_t n, float eps, void* stream) {
+  ROWS_OK("kd_add_rmsnorm_rows", B, n);
+  KD_REQUIRE(n % 32 == 0, KD_ERR_UNSUPPORTED, "kd_add_rmsnorm_rows: n=%d is not a multiple of 32", n);
+  KD_REQUIRE(x && r && g && x1 && y, KD_ERR_INVALID, "kd_add_rmsnorm_rows: null pointer");
+  launch_norm_quant(x, r, g, B, n, eps, x1, y, nullptr, nullptr, as_stream(stream));
+  return check_launch("kd_add_rmsnorm_rows");
+}
+
+extern "C" kd_status kd_rope_neox_rows(float* x, int32_t B, int32_t n_heads, int32_t hd, const int32_t* pos,
+                                       float base, void* stream) {
+  ROWS_OK("kd_rope_neox_rows", B, n_heads);
+  KD_REQUIRE(hd == 64 || hd == 128, KD_ERR_UNSUPPORTED, "kd_rope_neox_rows: hd=%d not 64 or 128", hd);
+  KD_REQUIRE(x && pos, KD_ERR_INVALID, "kd_rope_neox_rows: null pointer");
+  RowCaches rc = {};
+  for (int b = 0; b < B; ++b) {
+    KD_REQUIRE(pos[b] >= 0, KD_ERR_INVALID, "kd_rope_neox_rows: pos[%d]=%d < 0", b, pos[b]);
+    rc.pos[b] = pos[b];
+  }
+  // Rotate all n_heads heads of each row in place; cos/sin evaluated inline (no table).
+  launch_rope_append(x, n_heads * hd, B, n_heads, 0, hd, nullptr, rc, 0, false, as_stream(stream), base);
+  return check_launch("kd_rope_neox_rows");
+}
+
+extern "C" kd_status kd_swiglu_rows(const float* g, const float* u, float* a, int32_t B, int32_t n, void* stream) {
+  ROWS_OK("kd_swiglu_rows", B, n);
+  KD_REQUIRE(n % 32 == 0, KD_ERR_UNSUPPORTED, "kd_swiglu_rows: n=%d is not a multiple of 32", n);
+  KD_REQUIRE(g && u && a, KD_ERR_INVALID, "kd_swiglu_rows: null pointer");
+  launch_swiglu_quant(g, u, B, n, n, a, nullptr, nullptr, as_stream(stream));
+  return check_launch("kd_swiglu_rows");
+}
+
+extern "C" kd_status kd_add_rows(const float* x, const float* y, float* z, int32_t B, int32_t n, void* stream) {
+  ROWS_OK("kd_add_rows", B, n);
+  KD_REQUIRE(x && y && z, KD_ERR_INVALID, "kd_add_rows: null pointer");
+  launch_add(x, y, z, (size_t)B * n, as_stream(stream));
+  return check_launch("kd_add_rows");
+}

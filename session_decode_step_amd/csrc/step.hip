@@ -1,0 +1,345 @@
+// One batched decode step over a layer stack (kd_decode_step) and the library plumbing.
+//
+// Launch sequence per layer (memra-engine 0.72.0, src/decode_batch.rs, ``decode_batch_layers``
+// Full-attention arm, without the QK-norm and output-gate variants; hf2q ADR-040 §0.4 and
+// §0.7 F2: one [N, hidden] forward per tick with every projection at m = N):
+//   [residual add +] attn_norm + quantise        (norm_quant)
+//   q/k/v product at m = B                         (mmvq)
+//   RoPE with per-row positions + fp16 KV append  (rope_append: phase A, all rows)
+//   split-K attention + combine + quantise        (fa: phase B, all rows)
+//   o product                                      (mmvq)
+//   residual add + post-attention norm + quantise (norm_quant)
+//   gate, up products -> silu_mul + quantise -> down product   (dense FFN)
+//   or router -> expert buckets -> grouped gate/up -> silu_mul -> grouped down,
+//      shared expert, rank-ordered combine                       (MoE FFN)
+// The residual add that closes a layer is fused into the next layer's norm.  The number of
+// launches is independent of B (B is a grid dimension, never a host loop: hf2q ADR-040
+// §0.12, the "N as a grid dimension, constant dispatch" plan).  Nothing here synchronises
+// the stream or copies host data to the device: per-row positions and cache addresses
+// travel as kernel arguments.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "kd_internal.h"
+
+namespace kd {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+}
+
+kd_status check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("%s: HIP launch failed: %s", what, hipGetErrorString(e));
+    return KD_ERR_HIP;
+  }
+  return KD_OK;
+}
+
+}  // namespace kd
+
+using namespace kd;
+
+struct kd_model {
+  kd_model_desc desc;
+  std::vector<kd_layer_desc> layers;
+  int max_k;  // longest activation row any product reads
+};
+
+extern "C" const char* kd_last_error(void) { return g_err; }
+extern "C" const char* kd_version(void) { return "kd 0.1.0 gfx950 (mfma_i32_16x16x32_i8 mmvq, split-K fa_decode)"; }
+
+// ---------------------------------------------------------------------------------------
+// Model
+// ---------------------------------------------------------------------------------------
+static kd_status check_weight(const char* name, int il, const kd_weight& w, int n_out, int k, bool quant_only = true) {
+  KD_REQUIRE(w.qs, KD_ERR_INVALID, "kd_model_create: layer %d %s: null qs", il, name);
+  KD_REQUIRE(w.n_out == n_out && w.k == k, KD_ERR_INVALID, "kd_model_create: layer %d %s: shape %d x %d, expected %d x %d",
+             il, name, w.n_out, w.k, n_out, k);
+  if (quant_only) {
+    KD_REQUIRE(w.fmt == KD_FMT_Q8_0 || w.fmt == KD_FMT_Q4_0, KD_ERR_UNSUPPORTED,
+               "kd_model_create: layer %d %s: format %d is not Q8_0/Q4_0", il, name, w.fmt);
+    KD_REQUIRE(w.d, KD_ERR_INVALID, "kd_model_create: layer %d %s: null scales", il, name);
+    KD_REQUIRE(k % 32 == 0, KD_ERR_UNSUPPORTED, "kd_model_create: layer %d %s: k=%d not a multiple of 32", il, name, k);
+    KD_REQUIRE(aligned16(w.qs) && aligned16(w.d), KD_ERR_INVALID, "kd_model_create: layer %d %s: unaligned", il, name);
+  }
+  return KD_OK;
+}
+
+#define KD_TRY(expr)                 \
+  do {                               \
+    const kd_status s_ = (expr);     \
+    if (s_ != KD_OK) return s_;      \
+  } while (0)
+
+extern "C" kd_status kd_model_create(const kd_model_desc* desc, kd_model** out) {
+  KD_REQUIRE(desc && out, KD_ERR_INVALID, "kd_model_create: null argument");
+  const kd_model_desc& m = *desc;
+  KD_REQUIRE(m.n_layers >= 1 && m.layers, KD_ERR_INVALID, "kd_model_create: n_layers=%d", m.n_layers);
+  KD_REQUIRE(m.d > 0 && m.d % 32 == 0, KD_ERR_UNSUPPORTED, "kd_model_create: d=%d not a positive multiple of 32", m.d);
+  KD_REQUIRE(fa_shape_supported(m.n_head, m.n_head_kv, m.head_dim), KD_ERR_UNSUPPORTED,
+             "kd_model_create: H=%d G=%d hd=%d unsupported (H/G in {1,2,4,8}, hd in {64,128})", m.n_head, m.n_head_kv,
+             m.head_dim);
+  KD_REQUIRE(m.rms_eps > 0 && m.rope_base > 0, KD_ERR_INVALID, "kd_model_create: eps / rope base");
+  const int H = m.n_head, G = m.n_head_kv, hd = m.head_dim, d = m.d;
+  const bool moe = m.n_experts > 0;
+  if (moe) {
+    KD_REQUIRE(m.n_experts <= moe_max_experts() && m.n_expert_used >= 1 && m.n_expert_used <= moe_max_topk() &&
+                   m.n_expert_used <= m.n_experts,
+               KD_ERR_UNSUPPORTED, "kd_model_create: experts %d / used %d", m.n_experts, m.n_expert_used);
+    KD_REQUIRE(m.expert_ffn > 0 && m.expert_ffn % 32 == 0 && m.shared_ffn > 0 && m.shared_ffn % 32 == 0 && d % 16 == 0,
+               KD_ERR_UNSUPPORTED, "kd_model_create: expert widths must be multiples of 32 (Fe=%d Fs=%d)", m.expert_ffn,
+               m.shared_ffn);
+    KD_REQUIRE(m.ffn == 0, KD_ERR_INVALID, "kd_model_create: dense ffn and experts both set");
+  }
+  KD_REQUIRE(m.ffn >= 0 && m.ffn % 32 == 0, KD_ERR_UNSUPPORTED, "kd_model_create: ffn=%d", m.ffn);
+  for (int il = 0; il < m.n_layers; ++il) {
+    const kd_layer_desc& L = m.layers[il];
+    KD_REQUIRE(L.attn_norm, KD_ERR_INVALID, "kd_model_create: layer %d: null attn_norm", il);
+    KD_TRY(check_weight("wqkv", il, L.wqkv, (H + 2 * G) * hd, d));
+    KD_TRY(check_weight("wo", il, L.wo, d, H * hd));
+    if (m.ffn > 0 || moe) KD_REQUIRE(L.ffn_norm, KD_ERR_INVALID, "kd_model_create: layer %d: null ffn_norm", il);
+    if (m.ffn > 0) {
+      KD_TRY(check_weight("w_gate", il, L.w_gate, m.ffn, d));
+      KD_TRY(check_weight("w_up", il, L.w_up, m.ffn, d));
+      KD_TRY(check_weight("w_down", il, L.w_down, d, m.ffn));
+    }
+    if (moe) {
+      KD_REQUIRE(L.router, KD_ERR_INVALID, "kd_model_create: layer %d: null router", il);
+      KD_TRY(check_weight("e_gate", il, L.e_gate, m.n_experts * m.expert_ffn, d));
+      KD_TRY(check_weight("e_up", il, L.e_up, m.n_experts * m.expert_ffn, d));
+      KD_TRY(check_weight("e_down", il, L.e_down, m.n_experts * d, m.expert_ffn));
+      KD_REQUIRE(m.expert_ffn % 16 == 0, KD_ERR_UNSUPPORTED, "kd_model_create: expert_ffn %% 16");
+      KD_TRY(check_weight("s_gate", il, L.s_gate, m.shared_ffn, d));
+      KD_TRY(check_weight("s_up", il, L.s_up, m.shared_ffn, d));
+      KD_TRY(check_weight("s_down", il, L.s_down, d, m.shared_ffn));
+    }
+  }
+  if (m.vocab > 0) {
+    KD_TRY(check_weight("lm_head", -1, m.lm_head, m.vocab, d));
+  }
+  kd_model* mm = new (std::nothrow) kd_model;
+  KD_REQUIRE(mm, KD_ERR_INVALID, "kd_model_create: out of host memory");
+  mm->desc = m;
+  mm->layers.assign(m.layers, m.layers + m.n_layers);
+  mm->desc.layers = mm->layers.data();
+  int mk = d;
+  mk = H * hd > mk ? H * hd : mk;
+  mk = m.ffn > mk ? m.ffn : mk;
+  mk = m.shared_ffn > mk ? m.shared_ffn : mk;
+  mm->max_k = mk;
+  *out = mm;
+  return KD_OK;
+}
+
+extern "C" void kd_model_destroy(kd_model* m) { delete m; }
+
+// ---------------------------------------------------------------------------------------
+// Workspace
+// ---------------------------------------------------------------------------------------
+namespace {
+struct Carve {
+  char* base;
+  size_t off = 0;
+  explicit Carve(void* b) : base(static_cast<char*>(b)) {}
+  template <class T>
+  T* take(size_t n) {
+    off = (off + 255) & ~(size_t)255;
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += n * sizeof(T);
+    return p;
+  }
+};
+
+struct StepBufs {
+  float *xa, *xb, *f, *qkv, *attn, *o, *gu, *z, *cs, *sh, *sgu;
+  int8_t *act_qs, *hq_qs;
+  float *act_d, *hq_d;
+  void* fa_ws;
+  int32_t *ids, *count, *rows, *pairs;
+  float *p, *gup, *yp;
+  int8_t* lm_qs;
+  float* lm_d;
+};
+
+size_t carve_step(const kd_model* m, int B, const FaPlan& plan, void* ws, StepBufs& s) {
+  const kd_model_desc& d = m->desc;
+  const int H = d.n_head, G = d.n_head_kv, hd = d.head_dim, D = d.d;
+  Carve c(ws);
+  s.xa = c.take<float>((size_t)B * D);
+  s.xb = c.take<float>((size_t)B * D);
+  s.f = c.take<float>((size_t)B * D);
+  s.o = c.take<float>((size_t)B * D);
+  s.z = c.take<float>((size_t)B * D);
+  s.qkv = c.take<float>((size_t)B * (H + 2 * G) * hd);
+  s.attn = c.take<float>((size_t)B * H * hd);
+  s.cs = c.take<float>((size_t)B * hd);
+  s.act_qs = c.take<int8_t>((size_t)B * n_quads(m->max_k) * 128);
+  s.act_d = c.take<float>((size_t)B * n_quads(m->max_k) * 4);
+  s.fa_ws = c.take<char>(fa_workspace_bytes(plan));
+  s.gu = d.ffn ? c.take<float>((size_t)B * 2 * d.ffn) : nullptr;
+  if (d.n_experts) {
+    const int K = d.n_expert_used, E = d.n_experts, Fe = d.expert_ffn, Fs = d.shared_ffn;
+    s.ids = c.take<int32_t>((size_t)B * K);
+    s.p = c.take<float>((size_t)B * K);
+    s.count = c.take<int32_t>(E);
+    s.rows = c.take<int32_t>((size_t)E * 16);
+    s.pairs = c.take<int32_t>((size_t)E * 16);
+    s.gup = c.take<float>((size_t)B * K * 2 * Fe);
+    s.hq_qs = c.take<int8_t>((size_t)B * K * n_quads(Fe) * 128);
+    s.hq_d = c.take<float>((size_t)B * K * n_quads(Fe) * 4);
+    s.yp = c.take<float>((size_t)B * K * D);
+    s.sh = c.take<float>((size_t)B * D);
+    s.sgu = c.take<float>((size_t)B * 2 * Fs);
+  }
+  return c.off + 256;
+}
+
+bool plan_for(const kd_model* m, int B, const int32_t* pos, FaPlan& plan) {
+  int32_t t[KD_MAX_B];
+  for (int b = 0; b < B; ++b) t[b] = pos[b] + 1;
+  return fa_make_plan(plan, B, m->desc.n_head, m->desc.n_head_kv, m->desc.head_dim, t, 0);
+}
+}  // namespace
+
+extern "C" size_t kd_decode_step_workspace(const kd_model* m, int32_t B, const int32_t* pos) {
+  if (!m || B < 1 || B > KD_MAX_B || !pos) return 0;
+  for (int b = 0; b < B; ++b)
+    if (pos[b] < 0) return 0;
+  FaPlan plan;
+  plan_for(m, B, pos, plan);
+  StepBufs s;
+  return carve_step(m, B, plan, nullptr, s);
+}
+
+// ---------------------------------------------------------------------------------------
+// The step
+// ---------------------------------------------------------------------------------------
+extern "C" kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x_in, const int32_t* pos,
+                                    void* const* k_base, void* const* v_base, int32_t capacity, float* out, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  KD_REQUIRE(m, KD_ERR_INVALID, "kd_decode_step: null model");
+  KD_REQUIRE(B >= 1 && B <= KD_MAX_B, KD_ERR_UNSUPPORTED, "kd_decode_step: B=%d outside [1,16]", B);
+  KD_REQUIRE(x_in && pos && k_base && v_base && out, KD_ERR_INVALID, "kd_decode_step: null pointer");
+  const kd_model_desc& d = m->desc;
+  const int L = d.n_layers, H = d.n_head, G = d.n_head_kv, hd = d.head_dim, D = d.d;
+  for (int b = 0; b < B; ++b) {
+    KD_REQUIRE(pos[b] >= 0, KD_ERR_INVALID, "kd_decode_step: pos[%d]=%d < 0", b, pos[b]);
+    KD_REQUIRE(pos[b] + 1 <= capacity, KD_ERR_CAPACITY, "kd_decode_step: pos[%d]=%d does not fit capacity %d", b,
+               pos[b], capacity);
+    KD_REQUIRE(pos[b] + 1 <= fa_max_keys(), KD_ERR_UNSUPPORTED, "kd_decode_step: pos[%d]=%d beyond %d keys", b, pos[b],
+               fa_max_keys());
+  }
+  for (int il = 0; il < L; ++il)
+    for (int b = 0; b < B; ++b) {
+      void* kb = k_base[(size_t)il * B + b];
+      void* vb = v_base[(size_t)il * B + b];
+      KD_REQUIRE(kb && vb, KD_ERR_INVALID, "kd_decode_step: null cache pointer (layer %d row %d)", il, b);
+      KD_REQUIRE(aligned16(kb) && aligned16(vb), KD_ERR_INVALID, "kd_decode_step: cache (layer %d row %d) unaligned", il,
+                 b);
+      for (int a = 0; a < b; ++a)
+        KD_REQUIRE(!(k_base[(size_t)il * B + a] == kb && pos[a] == pos[b]), KD_ERR_INVALID,
+                   "kd_decode_step: rows %d and %d write the same cache slot (layer %d)", a, b, il);
+    }
+  FaPlan plan;
+  plan_for(m, B, pos, plan);
+  StepBufs s;
+  const size_t need = carve_step(m, B, plan, nullptr, s);
+  KD_REQUIRE(ws && ws_bytes >= need, KD_ERR_WORKSPACE, "kd_decode_step: workspace %zu < %zu bytes", ws_bytes, need);
+  void* ws_al = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~(uintptr_t)255);
+  KD_REQUIRE(ws_bytes - ((char*)ws_al - (char*)ws) >= need - 256, KD_ERR_WORKSPACE, "kd_decode_step: workspace alignment");
+  carve_step(m, B, plan, ws_al, s);
+
+  hipStream_t st = as_stream(stream);
+  const bool moe = d.n_experts > 0;
+  const bool has_ffn = d.ffn > 0 || moe;
+  const float scale = 1.0f / sqrtf((float)hd);
+  const int ldqkv = (H + 2 * G) * hd;
+
+  RowCaches rc = {};
+  for (int b = 0; b < B; ++b) rc.pos[b] = pos[b];
+  launch_rope_table(rc, B, hd, d.rope_base, s.cs, st);
+
+  // Residual stream = base (+ add, pending); the pending add is fused into the next norm.
+  const float* base = x_in;
+  const float* add = nullptr;
+  for (int il = 0; il < L; ++il) {
+    const kd_layer_desc& Ly = m->layers[il];
+    for (int b = 0; b < B; ++b) {
+      rc.k[b] = k_base[(size_t)il * B + b];
+      rc.v[b] = v_base[(size_t)il * B + b];
+    }
+    // attn_norm (+ pending residual add) + quantise
+    float* res = const_cast<float*>(base);
+    if (add) {
+      res = (base == s.xa) ? s.xb : s.xa;
+      launch_norm_quant(base, add, Ly.attn_norm, B, D, d.rms_eps, res, nullptr, s.act_qs, s.act_d, st);
+    } else {
+      launch_norm_quant(base, nullptr, Ly.attn_norm, B, D, d.rms_eps, nullptr, nullptr, s.act_qs, s.act_d, st);
+    }
+    launch_mmvq(Ly.wqkv, s.act_qs, s.act_d, B, s.qkv, ldqkv, st);
+    launch_rope_append(s.qkv, ldqkv, B, H, G, hd, s.cs, rc, capacity, true, st, d.rope_base);
+    launch_fa(plan, s.qkv, ldqkv, rc, capacity, scale, s.attn, s.act_qs, s.act_d, s.fa_ws, st);
+    launch_mmvq(Ly.wo, s.act_qs, s.act_d, B, s.o, D, st);
+    if (!has_ffn) {
+      base = res;
+      add = s.o;
+      continue;
+    }
+    float* x1 = (res == s.xa) ? s.xb : s.xa;
+    launch_norm_quant(res, s.o, Ly.ffn_norm, B, D, d.rms_eps, x1, moe ? s.z : nullptr, s.act_qs, s.act_d, st);
+    if (!moe) {
+      const int F = d.ffn;
+      launch_mmvq(Ly.w_gate, s.act_qs, s.act_d, B, s.gu, 2 * F, st);
+      launch_mmvq(Ly.w_up, s.act_qs, s.act_d, B, s.gu + F, 2 * F, st);
+      launch_swiglu_quant(s.gu, s.gu + F, B, F, 2 * F, nullptr, s.act_qs, s.act_d, st);
+      launch_mmvq(Ly.w_down, s.act_qs, s.act_d, B, s.f, D, st);
+    } else {
+      const int E = d.n_experts, K = d.n_expert_used, Fe = d.expert_ffn, Fs = d.shared_ffn;
+      launch_router(s.z, Ly.router, B, D, E, K, s.ids, s.p, nullptr, st);
+      launch_bucket(s.ids, B, K, E, s.count, s.rows, s.pairs, st);
+      RowMap gu_map{s.count, s.rows, s.pairs, E, (long long)n_rowgroups(Fe) * n_quads(D)};
+      kd_weight eg = Ly.e_gate, eu = Ly.e_up, ed = Ly.e_down;
+      eg.n_out = Fe;
+      eu.n_out = Fe;
+      ed.n_out = D;
+      launch_mmvq(eg, s.act_qs, s.act_d, 0, s.gup, 2 * Fe, st, &gu_map);
+      launch_mmvq(eu, s.act_qs, s.act_d, 0, s.gup + Fe, 2 * Fe, st, &gu_map);
+      // shared expert gate/up (reads the same Q(z) before it is overwritten)
+      launch_mmvq(Ly.s_gate, s.act_qs, s.act_d, B, s.sgu, 2 * Fs, st);
+      launch_mmvq(Ly.s_up, s.act_qs, s.act_d, B, s.sgu + Fs, 2 * Fs, st);
+      launch_swiglu_quant(s.gup, s.gup + Fe, B * K, Fe, 2 * Fe, nullptr, s.hq_qs, s.hq_d, st);
+      RowMap dn_map{s.count, s.pairs, s.pairs, E, (long long)n_rowgroups(D) * n_quads(Fe)};
+      launch_mmvq(ed, s.hq_qs, s.hq_d, 0, s.yp, D, st, &dn_map);
+      launch_swiglu_quant(s.sgu, s.sgu + Fs, B, Fs, 2 * Fs, nullptr, s.act_qs, s.act_d, st);
+      launch_mmvq(Ly.s_down, s.act_qs, s.act_d, B, s.sh, D, st);
+      launch_moe_combine(s.yp, s.p, s.sh, B, K, D, s.f, st);
+    }
+    base = x1;
+    add = s.f;
+  }
+  // output: [residual add +] final norm [+ quantise + lm_head]
+  if (d.vocab > 0) {
+    launch_norm_quant(base, add, d.final_norm, B, D, d.rms_eps, nullptr, nullptr, s.act_qs, s.act_d, st);
+    launch_mmvq(d.lm_head, s.act_qs, s.act_d, B, out, d.vocab, st);
+  } else if (d.final_norm) {
+    launch_norm_quant(base, add, d.final_norm, B, D, d.rms_eps, nullptr, out, nullptr, nullptr, st);
+  } else if (add) {
+    launch_add(base, add, out, (size_t)B * D, st);
+  } else {
+    if (hipMemcpyAsync(out, base, sizeof(float) * B * D, hipMemcpyDeviceToDevice, st) != hipSuccess) {
+      set_error("kd_decode_step: copy failed");
+      return KD_ERR_HIP;
+    }
+  }
+  return check_launch("kd_decode_step");
+}

@@ -1,0 +1,70 @@
+"""Device-side set-up of a synthetic decode workload: packed weights, per-session fp16 KV
+caches holding the seeded prefill, and a ``step()`` that calls ``kd_decode_step``.
+
+Marshalling only (uploads, pointer tables, buffer sizes); the step itself runs in libkd.
+The seeded inputs come from the ``workload`` module, which holds no arithmetic of the step.
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+import torch
+
+import workload as W
+
+from . import KdModel, SessionCaches
+
+
+class GpuWorkload:
+    def __init__(self, wl: W.Workload, model: Optional[Dict] = None, device: str = "cuda",
+                 fill: str = "seeded", sessions: Optional[Sequence[int]] = None):
+        """``fill="seeded"``: KV prefill from the workload generator; ``fill="device"``: a
+        seeded torch device generator (for GPU-only comparisons at large shapes)."""
+        self.wl = wl
+        sp = wl.spec
+        self.model = model if model is not None else W.make_model(sp, wl.code, wl.seed)
+        self.km = KdModel(self.model, device)
+        n_sess = len(wl.prefill)
+        self.caches = SessionCaches(n_sess, sp.n_layers, sp.n_head_kv, wl.capacity, sp.head_dim, device)
+        fill_sessions = range(n_sess) if sessions is None else sessions
+        if fill == "seeded":
+            for s in fill_sessions:
+                for il in range(sp.n_layers):
+                    k, v = W.kv_prefill(wl, s, il)
+                    self.caches.fill_prefill(s, il, k, v)
+        else:
+            gen = torch.Generator(device=device)
+            for s in fill_sessions:
+                gen.manual_seed(1000003 * (wl.seed + 1) + s)
+                L = wl.prefill[s]
+                t = self.caches.t[s]
+                t[:, :, :, :L].normal_(generator=gen)
+        self.device = device
+        last = max(0, wl.steps - 1)
+        self.ws = torch.empty(self.km.workspace_bytes(wl.B, wl.positions(last)) + 4096, dtype=torch.uint8,
+                              device=device)
+        self.out = torch.empty((wl.B, sp.out_dim), dtype=torch.float32, device=device)
+        self._x_cache: Dict[int, torch.Tensor] = {}
+
+    def inputs(self, step: int) -> torch.Tensor:
+        if step not in self._x_cache:
+            self._x_cache[step] = torch.from_numpy(W.step_inputs(self.wl, step)).to(self.device)
+        return self._x_cache[step]
+
+    def step(self, s: int, rows: Optional[Sequence[int]] = None, out: Optional[torch.Tensor] = None,
+             stream=None) -> torch.Tensor:
+        """Run decode step ``s`` for the given row indices (default: all rows)."""
+        wl = self.wl
+        rows = list(range(wl.B)) if rows is None else list(rows)
+        x = self.inputs(s)
+        if len(rows) != wl.B:
+            x = x[rows].contiguous()
+        pos_all = wl.positions(s)
+        pos = [pos_all[b] for b in rows]
+        sess = [wl.rows[b][0] for b in rows]
+        kb, vb = self.caches.tables(sess)
+        if out is None:
+            out = self.out if len(rows) == wl.B else torch.empty((len(rows), wl.spec.out_dim), dtype=torch.float32,
+                                                                 device=self.device)
+        return self.km.kd_decode_step(x, pos, kb, vb, wl.capacity, out, self.ws, stream)

@@ -1,0 +1,142 @@
+"""C ABI checks that need no GPU: libkd.so loads, exports every symbol kd.h declares, the
+layout size queries are right, and argument errors are reported before anything is
+enqueued (so these calls never reach the HIP runtime)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import session_decode_step_amd as kd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "kd.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(kd.LIB_PATH), reason="libkd.so not built")
+
+
+def declared_functions():
+    src = open(HDR).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(kd_[a-z0-9_]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    names = declared_functions()
+    assert len(names) >= 25
+    L = kd.lib()
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in kd.SIGNATURES, f"{n} has no binding signature"
+    assert set(kd.SIGNATURES) == set(names)
+
+
+def test_version_and_error_strings():
+    assert "gfx950" in kd.kd_version()
+    assert isinstance(kd.lib().kd_last_error(), bytes)
+
+
+def test_layout_sizes():
+    L = kd.lib()
+    # 4096 x 4096 Q4_0: 256 row groups x 32 quads, 1024 B + 128 B of scales per tile
+    assert L.kd_weight_qs_bytes(kd.KD_FMT_Q4_0, 4096, 4096) == 256 * 32 * 1024
+    assert L.kd_weight_d_bytes(kd.KD_FMT_Q4_0, 4096, 4096) == 256 * 32 * 128
+    assert L.kd_weight_qs_bytes(kd.KD_FMT_Q8_0, 4096, 4096) == 256 * 32 * 2048
+    # ragged shapes pad to whole tiles: 704 rows -> 44 groups; k = 704 -> 6 quads
+    assert L.kd_weight_qs_bytes(kd.KD_FMT_Q4_0, 700, 704) == 44 * 6 * 1024
+    assert L.kd_weight_qs_bytes(kd.KD_FMT_Q8_0, 16, 48) == 0           # k % 32 != 0
+    assert L.kd_act_qs_bytes(3, 704) == 3 * 6 * 128
+    assert L.kd_act_d_bytes(3, 704) == 3 * 24 * 4
+    t = (C.c_int32 * 3)(1, 129, 40000)
+    # splits: 1 -> 1 (chunk 128), 129 -> 2, 40000 -> chunk 313, 128 splits
+    assert L.kd_fa_decode_workspace(3, 8, 128, t) == (1 + 2 + 128) * 8 * (128 + 2) * 4
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def test_mmvq_validation_before_launch():
+    L = kd.lib()
+    w = kd.KdWeight(kd.KD_FMT_Q8_0, 64, 256, 0x1000, 0x2000)
+    act = kd.KdAct(0x3000, 0x4000)
+    assert L.kd_mmvq_q8_0(C.byref(w), act, 17, 0x5000, 64, None) == kd.KD_ERR_UNSUPPORTED
+    assert L.kd_mmvq_q8_0(C.byref(w), act, 0, 0x5000, 64, None) == kd.KD_ERR_UNSUPPORTED
+    assert b"B=0" in L.kd_last_error()
+    assert L.kd_mmvq_q4_0(C.byref(w), act, 2, 0x5000, 64, None) == kd.KD_ERR_UNSUPPORTED  # format mismatch
+    assert L.kd_mmvq_q8_0(C.byref(w), act, 2, None, 64, None) == kd.KD_ERR_INVALID
+    assert L.kd_mmvq_q8_0(C.byref(w), act, 2, 0x5000, 32, None) == kd.KD_ERR_INVALID       # ldy < n_out
+    w2 = kd.KdWeight(kd.KD_FMT_Q8_0, 64, 250, 0x1000, 0x2000)
+    assert L.kd_mmvq_q8_0(C.byref(w2), act, 2, 0x5000, 64, None) == kd.KD_ERR_UNSUPPORTED  # k % 32
+    w3 = kd.KdWeight(kd.KD_FMT_Q8_0, 64, 256, 0x1001, 0x2000)
+    assert L.kd_mmvq_q8_0(C.byref(w3), act, 2, 0x5000, 64, None) == kd.KD_ERR_INVALID      # unaligned
+    assert L.kd_quantize_act_q8(0x1000, 2, 100, 100, act, None) == kd.KD_ERR_UNSUPPORTED
+    assert L.kd_pack_weight(7, 16, 32, 0x10, 0x20, 0x30, 0x40, None) == kd.KD_ERR_UNSUPPORTED
+
+
+def test_attention_and_append_validation_before_launch():
+    L = kd.lib()
+    kb = (C.c_void_p * 2)(0x1000, 0x2000)
+    vb = (C.c_void_p * 2)(0x3000, 0x4000)
+    t = (C.c_int32 * 2)(10, 20)
+    st = L.kd_fa_decode_ragged(0x100, 2, 8, 3, 128, kb, vb, t, 64, 0.1, 0x200, 0x300, 1 << 20, None)
+    assert st == kd.KD_ERR_UNSUPPORTED                       # H % G != 0
+    st = L.kd_fa_decode_ragged(0x100, 2, 8, 2, 96, kb, vb, t, 64, 0.1, 0x200, 0x300, 1 << 20, None)
+    assert st == kd.KD_ERR_UNSUPPORTED                       # hd 96
+    st = L.kd_fa_decode_ragged(0x100, 2, 8, 2, 128, kb, vb, t, 15, 0.1, 0x200, 0x300, 1 << 20, None)
+    assert st == kd.KD_ERR_CAPACITY                          # t_kv > capacity
+    st = L.kd_fa_decode_ragged(0x100, 2, 8, 2, 128, kb, vb, t, 64, 0.1, 0x200, 0x300, 16, None)
+    assert st == kd.KD_ERR_WORKSPACE
+    pos = (C.c_int32 * 2)(63, 5)
+    assert L.kd_kv_append(0x10, 0x20, 2, 2, 128, kb, vb, pos, 63, None) == kd.KD_ERR_CAPACITY
+    pos2 = (C.c_int32 * 2)(5, 5)
+    same = (C.c_void_p * 2)(0x1000, 0x1000)
+    assert L.kd_kv_append(0x10, 0x20, 2, 2, 128, same, vb, pos2, 64, None) == kd.KD_ERR_INVALID  # same slot twice
+    assert L.kd_kv_append(0x10, 0x20, 17, 2, 128, kb, vb, pos, 64, None) == kd.KD_ERR_UNSUPPORTED
+
+
+def _fake_weight(fmt, n, k, base):
+    return kd.KdWeight(fmt, n, k, base, base + (1 << 24))
+
+
+def _fake_model(n_layers=2, d=256, H=4, G=2, hd=64, F=512):
+    layers = (kd.KdLayerDesc * n_layers)()
+    for il in range(n_layers):
+        b = 0x10000000 * (il + 1)
+        D = layers[il]
+        D.attn_norm = b
+        D.wqkv = _fake_weight(kd.KD_FMT_Q8_0, (H + 2 * G) * hd, d, b + 0x100000)
+        D.wo = _fake_weight(kd.KD_FMT_Q8_0, d, H * hd, b + 0x200000)
+        D.ffn_norm = b + 0x300000
+        D.w_gate = _fake_weight(kd.KD_FMT_Q8_0, F, d, b + 0x400000)
+        D.w_up = _fake_weight(kd.KD_FMT_Q8_0, F, d, b + 0x500000)
+        D.w_down = _fake_weight(kd.KD_FMT_Q8_0, d, F, b + 0x600000)
+    desc = kd.KdModelDesc(n_layers, d, H, G, hd, F, 0, 0, 0, 0, 0, 10000.0, 1e-5, layers, 0, kd.KdWeight())
+    return desc, layers
+
+
+def test_model_create_validation_and_step_errors():
+    L = kd.lib()
+    desc, layers = _fake_model()
+    h = C.c_void_p()
+    assert L.kd_model_create(C.byref(desc), C.byref(h)) == kd.KD_OK
+    try:
+        pos = (C.c_int32 * 2)(10, 63)
+        kb = (C.c_void_p * 4)(0x1000, 0x2000, 0x3000, 0x4000)
+        vb = (C.c_void_p * 4)(0x5000, 0x6000, 0x7000, 0x8000)
+        need = L.kd_decode_step_workspace(h, 2, pos)
+        assert need > 0
+        assert L.kd_decode_step(h, 2, 0x100, pos, kb, vb, 63, 0x200, 0x300, need, None) == kd.KD_ERR_CAPACITY
+        assert L.kd_decode_step(h, 2, 0x100, pos, kb, vb, 64, 0x200, 0x300, need - 300, None) == kd.KD_ERR_WORKSPACE
+        assert L.kd_decode_step(h, 17, 0x100, pos, kb, vb, 64, 0x200, 0x300, need, None) == kd.KD_ERR_UNSUPPORTED
+        kb_same = (C.c_void_p * 4)(0x1000, 0x1000, 0x3000, 0x4000)
+        pos_same = (C.c_int32 * 2)(10, 10)
+        assert L.kd_decode_step(h, 2, 0x100, pos_same, kb_same, vb, 64, 0x200, 0x300, 1 << 30, None) == kd.KD_ERR_INVALID
+    finally:
+        L.kd_model_destroy(h)
+    bad = kd.KdModelDesc(desc.n_layers, 256, 4, 3, 64, 512, 0, 0, 0, 0, 0, 10000.0, 1e-5, layers, 0, kd.KdWeight())
+    assert L.kd_model_create(C.byref(bad), C.byref(h)) == kd.KD_ERR_UNSUPPORTED        # H % G
+    layers[1].wo = _fake_weight(kd.KD_FMT_Q8_0, 255, 256, 0x900000)
+    assert L.kd_model_create(C.byref(desc), C.byref(h)) == kd.KD_ERR_INVALID          # wrong shape
+    assert b"wo" in L.kd_last_error()

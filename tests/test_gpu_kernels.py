@@ -1,0 +1,204 @@
+"""Per-kernel parity of the HIP path against the CPU oracle (MI355X only).
+
+Integers (quantised codes, per-block int32 dot products) and fp16 KV bytes must match
+exactly; fp32 results within 2e-3 of the oracle's fp64 value (per-row scaled); every
+row of a B-row call must equal, bit for bit, the 1-row call on that row.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import ops
+import workload as W
+from gpu_util import assert_close_rows, requires_gpu, say, untile_act
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+kd = pytest.importorskip("session_decode_step_amd")
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ activation quantiser
+@pytest.mark.parametrize("B,k", [(1, 256), (5, 704), (16, 2048), (3, 14336)])
+def test_act_quant_codes_and_scales_exact(B, k):
+    say(f"act_quant B={B} k={k}")
+    r = np.random.default_rng(100 + k)
+    x = (r.standard_normal((B, k)) * np.exp(r.uniform(-4, 4, (B, 1)))).astype(np.float32)
+    x[0, 32:64] = 0.0                                           # a zero block
+    x[0, 64] = 127.0
+    x[0, 65:69] = [0.5, -0.5, 2.5, -2.5]                         # exact ties (scale 1)
+    act = kd.kd_quantize_act_q8(dev(x))
+    sync()
+    codes, sc, pad_codes, pad_sc = untile_act(act.qs, act.d, B, k)
+    q_ref, d_ref = ops.quantize_act(x)
+    np.testing.assert_array_equal(sc, d_ref)
+    np.testing.assert_array_equal(codes, q_ref)
+    assert np.all(pad_codes == 0) and np.all(pad_sc == 0)
+
+
+# ------------------------------------------------------------------ mmvq
+SHAPES = [("q8_0", 100, 704), ("q8_0", 512, 2048), ("q4_0", 100, 704), ("q4_0", 4096, 4096), ("q8_0", 48, 256)]
+
+
+@pytest.mark.parametrize("fmt,n,k", SHAPES)
+def test_block_dots_exact(fmt, n, k):
+    say(f"block_dots {fmt} n={n} k={k}")
+    r = np.random.default_rng(7 + n)
+    w = (W.draw_q8_0 if fmt == "q8_0" else W.draw_q4_0)(r, r, n, k)
+    x = r.standard_normal((16, k)).astype(np.float32)
+    pw = kd.kd_pack_weight(w)
+    act = kd.kd_quantize_act_q8(dev(x))
+    S = kd.kd_debug_block_dots(pw, act, 16)
+    sync()
+    xq, _ = ops.quantize_act(x)
+    np.testing.assert_array_equal(S.cpu().numpy(), ops.block_dots(w, xq))
+
+
+@pytest.mark.parametrize("fmt,n,k", SHAPES)
+def test_mmvq_matches_oracle_and_rows_are_b_invariant(fmt, n, k):
+    say(f"mmvq {fmt} n={n} k={k}")
+    r = np.random.default_rng(11 + n + k)
+    w = (W.draw_q8_0 if fmt == "q8_0" else W.draw_q4_0)(r, r, n, k)
+    x = r.standard_normal((16, k)).astype(np.float32)
+    pw = kd.kd_pack_weight(w)
+    act = kd.kd_quantize_act_q8(dev(x))
+    fn = kd.kd_mmvq_q8_0 if fmt == "q8_0" else kd.kd_mmvq_q4_0
+    y16 = fn(pw, act, 16)
+    sync()
+    xq, xd = ops.quantize_act(x)
+    ref = ops.mmvq(w, xq, xd)
+    assert_close_rows(y16.cpu().numpy(), ref, 2e-3, "mmvq")
+    # fp32 epilogue error is far below the budget: one rounding per block
+    assert_close_rows(y16.cpu().numpy(), ref, 1e-4, "mmvq tight")
+    y16h = y16.cpu().numpy()
+    for B in range(1, 16):
+        yB = fn(pw, act, B).cpu().numpy()
+        np.testing.assert_array_equal(yB, y16h[:B])
+    # a row alone (its activation moved to row 0) gives the same bytes
+    for b in (5, 15):
+        act1 = kd.kd_quantize_act_q8(dev(x[b:b + 1]))
+        y1 = fn(pw, act1, 1).cpu().numpy()
+        np.testing.assert_array_equal(y1[0], y16h[b])
+
+
+def test_mmvq_rejects_wrong_format():
+    r = np.random.default_rng(3)
+    w = W.draw_q8_0(r, r, 16, 64)
+    pw = kd.kd_pack_weight(w)
+    act = kd.kd_quantize_act_q8(dev(np.ones((1, 64), np.float32)))
+    with pytest.raises(kd.KdError):
+        kd.kd_mmvq_q4_0(pw, act, 1)
+
+
+# ------------------------------------------------------------------ row ops
+def test_rmsnorm_and_add_rmsnorm():
+    say("rmsnorm")
+    r = np.random.default_rng(5)
+    x = r.standard_normal((7, 2816)).astype(np.float32)
+    res = r.standard_normal((7, 2816)).astype(np.float32)
+    g = (1 + 0.1 * r.standard_normal(2816)).astype(np.float32)
+    y = kd.kd_rmsnorm_rows(dev(x), dev(g), 1e-5).cpu().numpy()
+    assert_close_rows(y, ops.rmsnorm(x, g, 1e-5), 1e-5, "rmsnorm")
+    x1, y2 = kd.kd_add_rmsnorm_rows(dev(x), dev(res), dev(g), 1e-5)
+    np.testing.assert_array_equal(x1.cpu().numpy(), x + res)
+    assert_close_rows(y2.cpu().numpy(), ops.rmsnorm((x + res).astype(np.float64), g, 1e-5), 1e-5, "add_rmsnorm")
+    # row invariance
+    y1 = kd.kd_rmsnorm_rows(dev(x[3:4]), dev(g), 1e-5).cpu().numpy()
+    np.testing.assert_array_equal(y1[0], y[3])
+
+
+def test_rope_per_row_positions():
+    say("rope")
+    r = np.random.default_rng(6)
+    for hd in (64, 128):
+        x = r.standard_normal((4, 6, hd)).astype(np.float32)
+        pos = [0, 17, 4096, 32768]
+        t = dev(x)
+        kd.kd_rope_neox_rows(t, pos, 10000.0)
+        got = t.cpu().numpy()
+        ref = np.stack([ops.rope_neox(x[b], pos[b], 10000.0) for b in range(4)])
+        np.testing.assert_array_equal(got[0], x[0])  # pos 0 is the identity
+        assert_close_rows(got, ref, 1e-5, f"rope hd={hd}")
+
+
+def test_swiglu_and_add():
+    say("swiglu")
+    r = np.random.default_rng(8)
+    g = (3 * r.standard_normal((5, 704))).astype(np.float32)
+    u = r.standard_normal((5, 704)).astype(np.float32)
+    a = kd.kd_swiglu_rows(dev(g), dev(u)).cpu().numpy()
+    assert_close_rows(a, ops.swiglu(g, u), 1e-5, "swiglu")
+    z = kd.kd_add_rows(dev(g), dev(u)).cpu().numpy()
+    np.testing.assert_array_equal(z, g + u)
+
+
+# ------------------------------------------------------------------ KV append + attention
+def _caches(n, G, cap, hd):
+    return [(torch.zeros((G, cap, hd), dtype=torch.float16, device="cuda"),
+             torch.zeros((G, cap, hd), dtype=torch.float16, device="cuda")) for _ in range(n)]
+
+
+def test_kv_append_bytes_exact():
+    say("kv_append")
+    r = np.random.default_rng(9)
+    B, G, hd, cap = 5, 8, 128, 40
+    caches = _caches(B, G, cap, hd)
+    k = (r.standard_normal((B, G, hd)) * 10).astype(np.float32)
+    v = r.standard_normal((B, G, hd)).astype(np.float32)
+    pos = [0, 39, 7, 8, 20]
+    kd.kd_kv_append(dev(k), dev(v), [c[0].data_ptr() for c in caches], [c[1].data_ptr() for c in caches], pos, cap)
+    sync()
+    for b in range(B):
+        K = caches[b][0].cpu().numpy()
+        V = caches[b][1].cpu().numpy()
+        np.testing.assert_array_equal(K[:, pos[b]].view(np.uint16), k[b].astype(np.float16).view(np.uint16))
+        np.testing.assert_array_equal(V[:, pos[b]].view(np.uint16), v[b].astype(np.float16).view(np.uint16))
+        mask = np.ones(cap, bool)
+        mask[pos[b]] = False
+        assert not K[:, mask].any() and not V[:, mask].any()
+
+
+@pytest.mark.parametrize("H,G,hd", [(32, 8, 128), (16, 4, 128), (4, 2, 64), (16, 8, 128), (8, 8, 64)])
+def test_fa_decode_ragged_vs_oracle(H, G, hd):
+    say(f"fa H={H} G={G} hd={hd}")
+    r = np.random.default_rng(H * 100 + G)
+    t_kv = [1, 2, 127, 128, 129, 300, 1238, 5000]
+    B, cap = len(t_kv), 5008
+    caches = _caches(B, G, cap, hd)
+    Ks, Vs = [], []
+    for b in range(B):
+        Kb = r.standard_normal((G, cap, hd)).astype(np.float16)
+        Vb = r.standard_normal((G, cap, hd)).astype(np.float16)
+        caches[b][0].copy_(torch.from_numpy(Kb))
+        caches[b][1].copy_(torch.from_numpy(Vb))
+        Ks.append(Kb)
+        Vs.append(Vb)
+    q = (r.standard_normal((B, H, hd)) * 0.5).astype(np.float32)
+    kb = [c[0].data_ptr() for c in caches]
+    vb = [c[1].data_ptr() for c in caches]
+    scale = 1.0 / math.sqrt(hd)
+    out = kd.kd_fa_decode_ragged(dev(q), G, kb, vb, t_kv, cap, scale).cpu().numpy()
+    ref = np.stack([ops.attention(q[b], Ks[b], Vs[b], t_kv[b]) for b in range(B)])
+    assert_close_rows(out.reshape(B, -1), ref.reshape(B, -1), 2e-3, "fa")
+    assert_close_rows(out.reshape(B, -1), ref.reshape(B, -1), 1e-4, "fa tight")
+    # t = 1: exactly V[0] (one key: p = 1)
+    np.testing.assert_array_equal(out[0], np.stack([Vs[0][h // (H // G), 0].astype(np.float32) for h in range(H)]))
+    # rows are B-invariant
+    for b in (3, 7):
+        o1 = kd.kd_fa_decode_ragged(dev(q[b:b + 1]), G, kb[b:b + 1], vb[b:b + 1], t_kv[b:b + 1], cap, scale)
+        np.testing.assert_array_equal(o1.cpu().numpy()[0], out[b])
+    # other split sizes agree within fp32 rounding; the merge adds one rounding per split,
+    # so the bound grows with the split count (5000 single-key splits at chunk = 1)
+    for chunk, tol in ((1, 2e-5), (37, 2e-6), (1000, 2e-6)):
+        oc = kd.kd_fa_decode_ragged(dev(q), G, kb, vb, t_kv, cap, scale, chunk=chunk).cpu().numpy()
+        assert_close_rows(oc.reshape(B, -1), out.reshape(B, -1), tol, f"fa chunk={chunk}")
