@@ -91,6 +91,7 @@ def moe_ffn(spec, L: Dict, z: np.ndarray, zq, zd, dense: Optional[DenseWeights],
         if info is not None:
             srt = np.sort(r[b])[::-1]
             info.setdefault("gap", []).append(float(srt[k - 1] - srt[k]))
+            info.setdefault("kth", []).append(float(abs(srt[k - 1])))
             info.setdefault("ids", []).append(ids.copy())
         acc = np.zeros(d, dtype=np.float64)
         for rank in range(k):

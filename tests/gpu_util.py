@@ -33,17 +33,35 @@ def untile_act(qs: torch.Tensor, d: torch.Tensor, B: int, k: int):
     return codes.reshape(B, NQ * 128)[:, :k], sc[:, : k // 32], codes[:, k // 32:], sc[:, k // 32:]
 
 
-def assert_close_rows(gpu, ref, rel=2e-3, what=""):
-    """Per output row: |gpu - ref| <= rel * max(|ref_i|, rms(ref_row)) for every element."""
+def row_errors(gpu, ref):
+    """(normwise, elementwise) relative errors per row: ||g - r||_2 / ||r||_2 and
+    max_i |g_i - r_i| / max(|r_i|, rms(r))."""
+    g2 = np.asarray(gpu, dtype=np.float64).reshape(-1, np.shape(gpu)[-1])
+    r2 = np.asarray(ref, dtype=np.float64).reshape(-1, np.shape(ref)[-1])
+    d = g2 - r2
+    nrm = np.sqrt(np.sum(r2 * r2, axis=1))
+    normwise = np.sqrt(np.sum(d * d, axis=1)) / np.where(nrm == 0, 1.0, nrm)
+    rms = np.sqrt(np.mean(r2 * r2, axis=1, keepdims=True))
+    scale = np.maximum(np.abs(r2), rms)
+    elem = np.max(np.abs(d) / np.where(scale == 0, 1.0, scale), axis=1)
+    return normwise, elem
+
+
+def assert_close_rows(gpu, ref, rel=2e-3, what="", elem_rel=None):
+    """Kernel-level bar: every element |g_i - r_i| <= rel * max(|r_i|, rms(row)).
+
+    With ``elem_rel`` given (whole-step bar): per row ||g - r|| / ||r|| <= rel and every
+    element within elem_rel * max(|r_i|, rms(row)).  Returns the worst normwise error."""
     gpu = np.asarray(gpu, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
-    g2 = gpu.reshape(-1, gpu.shape[-1])
-    r2 = ref.reshape(-1, ref.shape[-1])
-    rms = np.sqrt(np.mean(r2 * r2, axis=1, keepdims=True))
-    scale = np.maximum(np.abs(r2), rms)
-    err = np.abs(g2 - r2) / np.where(scale == 0, 1.0, scale)
-    worst = float(err.max()) if err.size else 0.0
-    assert np.all(np.isfinite(g2)), f"{what}: non-finite GPU values"
-    assert worst <= rel, f"{what}: worst scaled error {worst:.3e} > {rel:.1e}"
-    return worst
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite GPU values"
+    normwise, elem = row_errors(gpu, ref)
+    if elem_rel is None:
+        worst = float(elem.max()) if elem.size else 0.0
+        assert worst <= rel, f"{what}: worst scaled error {worst:.3e} > {rel:.1e}"
+        return worst
+    say(f"  {what}: normwise max {normwise.max():.3e}, elementwise max {elem.max():.3e}")
+    assert normwise.max() <= rel, f"{what}: normwise relative error {normwise.max():.3e} > {rel:.1e}"
+    assert elem.max() <= elem_rel, f"{what}: elementwise scaled error {elem.max():.3e} > {elem_rel:.1e}"
+    return float(normwise.max())

@@ -348,3 +348,24 @@ def test_workload_determinism():
     assert wl.positions(0) == [17, 40]
     lens = wlmod.c3_lengths(0)
     assert all(512 <= t <= 32768 for t in lens) and len(set(lens)) > 8
+
+
+def test_deep_step_is_discontinuous_at_rounding_level():
+    """The step is discontinuous (int8 activation codes): a 3e-7 relative perturbation of the
+    input rows -- the size of fp32 evaluation error -- changes some rows of a deep stack's
+    output by over 1e-4 (a >300x amplification no continuous evaluation of this stack shows)
+    once a code flips and later codes follow, and the spread stays at the quantisation-noise
+    level.  This is the evidence behind the whole-step tolerance for deep stacks (fp32 GPU
+    path vs fp64 oracle)."""
+    spec = wlmod.ModelSpec("deep", 8, 256, 4, 2, 64, 512, "q8_0", vocab=512, final_norm=True)
+    rows = 32
+    wl = _tiny_wl(spec, 96, [(b, 0) for b in range(rows)], [40] * rows, cap=48)
+    model = wlmod.make_model(spec, 96)
+    x = wlmod.step_inputs(wl, 0).astype(np.float64)
+    ya = oracle.decode_step(model, oracle.OracleCaches(wl), x, list(range(rows)), wl.positions(0))
+    xp = (x * (1 + 3e-7 * np.random.default_rng(0).standard_normal(x.shape))).astype(np.float32)
+    yb = oracle.decode_step(model, oracle.OracleCaches(wl), xp, list(range(rows)), wl.positions(0))
+    nw = np.sqrt(((ya - yb) ** 2).sum(1) / (ya ** 2).sum(1))
+    assert nw.max() > 1e-4          # some rows cascade far beyond the input perturbation
+    assert np.median(nw) < 1e-5     # most rows see no flip at all
+    assert nw.max() < 2e-2          # and the spread saturates at the quantisation-noise level
