@@ -165,7 +165,9 @@ typedef struct {
   kd_weight wqkv;           /* [(H + 2G) hd, d]: rows q (H hd), then k (G hd), then v (G hd) */
   kd_weight wo;             /* [d, H hd] */
   const float* ffn_norm;    /* [d]; NULL for an attention-only layer */
-  kd_weight w_gate, w_up;   /* dense SwiGLU [F, d] (qs NULL if MoE or attention-only) */
+  kd_weight w_gate, w_up;   /* dense SwiGLU [F, d] (qs NULL if MoE or attention-only); or w_gate
+                               holding [2F, d] (gate rows, then up rows) with w_up.qs NULL:
+                               one product streams both (kd_stack_rows builds it) */
   kd_weight w_down;         /* [d, F] */
   const float* router;      /* MoE: fp32 [E][d] */
   kd_weight e_gate, e_up;   /* MoE: experts stacked by rows, expert e = rows [e Fe, (e+1) Fe) of [E Fe, d] */

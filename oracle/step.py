@@ -47,15 +47,17 @@ class OracleCaches:
     """fp16 K/V of the sessions the oracle follows: ``K[s][il]`` is ``[G, capacity, hd]``."""
 
     def __init__(self, wl, sessions: Optional[Sequence[int]] = None):
-        from workload import kv_prefill  # seeded inputs only
+        from workload import kv_prefill_many  # seeded inputs only
         sp = wl.spec
         self.sessions = list(range(len(wl.prefill))) if sessions is None else list(sessions)
         self.K: Dict[int, List[np.ndarray]] = {}
         self.V: Dict[int, List[np.ndarray]] = {}
+        pairs = [(s, il) for s in self.sessions for il in range(sp.n_layers)]
+        pre = dict(zip(pairs, kv_prefill_many(wl, pairs)))
         for s in self.sessions:
             self.K[s], self.V[s] = [], []
             for il in range(sp.n_layers):
-                k0, v0 = kv_prefill(wl, s, il)
+                k0, v0 = pre[(s, il)]
                 K = np.zeros((sp.n_head_kv, wl.capacity, sp.head_dim), dtype=np.float16)
                 V = np.zeros_like(K)
                 K[:, : k0.shape[1]] = k0

@@ -165,6 +165,13 @@ def kd_pack_weight(w: Dict, device="cuda", stream=None) -> PackedWeight:
     return PackedWeight(fmt, n, k, qs, dd)
 
 
+def stack_rows(a: Dict, b: Dict) -> Dict:
+    """Row-major block matrices a [n_a, k] and b [n_b, k] stacked into one [n_a + n_b, k]."""
+    assert a["fmt"] == b["fmt"] and a["k"] == b["k"]
+    return {"fmt": a["fmt"], "n": a["n"] + b["n"], "k": a["k"], "qs": np.concatenate([a["qs"], b["qs"]]),
+            "d": np.concatenate([a["d"], b["d"]])}
+
+
 def expert_view(w: PackedWeight, n_out: int) -> PackedWeight:
     return PackedWeight(w.fmt, n_out, w.k, w.qs, w.d)
 
@@ -317,8 +324,10 @@ class KdModel:
             D.wqkv = W(L["wqkv"])
             D.wo = W(L["wo"])
             D.ffn_norm = F(L["ffn_norm"]) if "ffn_norm" in L else None
-            D.w_gate, D.w_up, D.w_down = ((W(L["w_gate"]), W(L["w_up"]), W(L["w_down"])) if "w_gate" in L
-                                          else (empty, empty, empty))
+            if "w_gate" in L:   # gate and up stacked into one [2F, d] matrix: one product streams both
+                D.w_gate, D.w_up, D.w_down = W(stack_rows(L["w_gate"], L["w_up"])), empty, W(L["w_down"])
+            else:
+                D.w_gate, D.w_up, D.w_down = empty, empty, empty
             if "router" in L:
                 D.router = F(L["router"])
                 D.e_gate, D.e_up, D.e_down = W(L["e_gate"]), W(L["e_up"]), W(L["e_down"])

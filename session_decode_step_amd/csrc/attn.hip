@@ -205,6 +205,9 @@ __global__ __launch_bounds__(kFaThreads) void fa_split_kernel(FaPlan p, const fl
 }
 
 // grid (H, B); HD threads.  Merge the row's chunks in chunk order; optionally quantise.
+// The chunk maxima and their weights e^(m_s - M) are staged in LDS once; each thread then
+// reads its dimension of every chunk's partial with 8 loads in flight at a time.
+constexpr int kCombineStage = 1024;
 template <int HD>
 __global__ __launch_bounds__(HD) void fa_combine_kernel(FaPlan p, const float* __restrict__ ws, float* __restrict__ out,
                                                         int8_t* __restrict__ oq, float* __restrict__ od) {
@@ -213,33 +216,64 @@ __global__ __launch_bounds__(HD) void fa_combine_kernel(FaPlan p, const float* _
   const float* po = ws;
   const float* pm = ws + (size_t)p.n_items * H * HD;
   const float* pl = pm + (size_t)p.n_items * H;
-  const int s0 = p.split_off[b], s1 = p.split_off[b + 1];
+  const int s0 = p.split_off[b], S = p.split_off[b + 1] - s0;
+  __shared__ float wm[kCombineStage];
+  __shared__ float wl[kCombineStage];
+  __shared__ float red[HD / 64];
   float M = -INFINITY;
-  for (int s = s0; s < s1; ++s) M = fmaxf(M, pm[(size_t)s * H + h]);
+  for (int s = d; s < S; s += HD) M = fmaxf(M, pm[(size_t)(s0 + s) * H + h]);
+  M = wave_max(M);
+  if ((d & 63) == 0) red[d >> 6] = M;
+  __syncthreads();
+  M = red[0];
+  for (int i = 1; i < HD / 64; ++i) M = fmaxf(M, red[i]);
   float num = 0.0f, den = 0.0f;
-  for (int s = s0; s < s1; ++s) {
-    const float wgt = expf(pm[(size_t)s * H + h] - M);
-    num = fmaf(wgt, po[((size_t)s * H + h) * HD + d], num);
-    den = fmaf(wgt, pl[(size_t)s * H + h], den);
+  for (int base = 0; base < S; base += kCombineStage) {
+    const int n = min(kCombineStage, S - base);
+    __syncthreads();
+    for (int s = d; s < n; s += HD) {
+      const size_t it = (size_t)(s0 + base + s) * H + h;
+      const float w = expf(pm[it] - M);
+      wm[s] = w;
+      wl[s] = w * pl[it];
+    }
+    __syncthreads();
+    int s = 0;
+    for (; s + 8 <= n; s += 8) {
+      float o[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = po[((size_t)(s0 + base + s + i) * H + h) * HD + d];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        num = fmaf(wm[s + i], o[i], num);
+        den += wl[s + i];
+      }
+    }
+    for (; s < n; ++s) {
+      num = fmaf(wm[s], po[((size_t)(s0 + base + s) * H + h) * HD + d], num);
+      den += wl[s];
+    }
   }
   const float v = num / den;
   out[((size_t)b * H + h) * HD + d] = v;
   if (oq) {
+    // 8 lanes per 32-element block: lane d holds dims (d/8)*32 + 4(d%8) .. +3 after a shuffle
+    // through LDS; HD/32 blocks per head.
     __shared__ float row[HD];
     row[d] = v;
     __syncthreads();
-    const int n = H * HD;
-    const int NQ = n_quads(n);
-    if (d < HD / 32) {
-      const int blk = (h * HD) / 32 + d;
-      quant32(row + 32 * d, oq + ((size_t)b * NQ + (blk >> 2)) * 128 + (blk & 3) * 8, od + (size_t)b * NQ * 4 + blk);
+    const int n = H * HD, NQ = n_quads(n), nbp = NQ * 4;
+    if (d < (HD / 32) * 8) {
+      const int lb = d >> 3, sub = d & 7;
+      const float4 x4 = *reinterpret_cast<const float4*>(row + lb * 32 + 4 * sub);
+      const int blk = (h * HD) / 32 + lb;
+      quant4_lane8(x4, sub, true, oq + ((size_t)b * NQ + (blk >> 2)) * 128 + (blk & 3) * 8, od + (size_t)b * nbp + blk);
     }
     // padded blocks past H*HD (only when H*HD is not a multiple of 128)
-    if (h == H - 1 && d == 0) {
-      float z[32];
-      for (int i = 0; i < 32; ++i) z[i] = 0.0f;
-      for (int blk = n / 32; blk < NQ * 4; ++blk)
-        quant32(z, oq + ((size_t)b * NQ + (blk >> 2)) * 128 + (blk & 3) * 8, od + (size_t)b * NQ * 4 + blk);
+    if (h == H - 1 && d < 8) {
+      for (int blk = n / 32; blk < nbp; ++blk)
+        quant4_lane8(make_float4(0.0f, 0.0f, 0.0f, 0.0f), d, true,
+                     oq + ((size_t)b * NQ + (blk >> 2)) * 128 + (blk & 3) * 8, od + (size_t)b * nbp + blk);
     }
   }
 }

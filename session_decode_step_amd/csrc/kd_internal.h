@@ -7,7 +7,7 @@
 #include <cstddef>
 #include <cstdint>
 
-#include "../../include/kd.h"
+#include "kd.h"
 
 namespace kd {
 
@@ -66,6 +66,34 @@ __device__ inline void quant32(const float* v, int8_t* dst_block, float* d_out) 
   *d_out = dd;
 }
 
+// The same quantiser with a block spread over 8 consecutive lanes (lane sub = tid % 8 holds
+// elements [4 sub, 4 sub + 4) in v).  Every lane of the group must execute it (shuffles);
+// stores happen only if `store`.  Codes and scale equal quant32's for the same 32 values
+// (max is exact and order-free; each code is computed alone).
+__device__ inline void quant4_lane8(float4 v, int sub, bool store, int8_t* dst_block, float* d_out) {
+  float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
+  const float dd = amax / 127.0f;
+  int c[4] = {0, 0, 0, 0};
+  if (amax != 0.0f) {
+    const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int qv = (int)roundf(e[i] / dd);
+      c[i] = qv > 127 ? 127 : (qv < -127 ? -127 : qv);
+    }
+  }
+  if (store) {
+    // elements 4 sub .. 4 sub + 3: group (sub & 3), first half if sub < 4 else second half
+    *reinterpret_cast<uint32_t*>(dst_block + 32 * (sub & 3) + (sub >> 2) * 4) = pack4b(c[0], c[1], c[2], c[3]);
+    if (sub == 0) *d_out = dd;
+  }
+}
+
+__device__ inline float4 f4_add(float4 a, float4 b) { return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w); }
+
 __device__ inline float wave_sum(float v) {
   // xor butterfly: every lane ends with the same value (fp add is commutative).
 #pragma unroll
@@ -80,6 +108,7 @@ __device__ inline float wave_max(float v) {
 }
 
 // ---- launchers used by the step driver (arguments already validated) -------------------
+int norm_max_len();
 void launch_act_quant(const float* x, int B, int k, int ldx, int8_t* qs, float* d, hipStream_t st);
 // Fused RMSNorm (optionally with a residual add) + activation quantiser.  If r != nullptr:
 // x1 = x + r is written to x1_out.  y = rmsnorm(x or x1) is written to y_out if non-null.
@@ -95,6 +124,7 @@ struct RowMap {
   const int32_t* out_row;  // [n_groups * 16]
   int n_groups;
   long long w_group_tiles;  // tiles between consecutive groups' weights
+  int act_rows;             // rows of the activation buffer the act_row entries index
 };
 
 void launch_mmvq(const kd_weight& W, const int8_t* xq, const float* xd, int B, float* y, int ldy,

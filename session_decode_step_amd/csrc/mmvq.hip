@@ -24,6 +24,20 @@ namespace kd {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
+#ifndef KD_MMVQ_NT
+#define KD_MMVQ_NT 1
+#endif
+#ifndef KD_MMVQ_DEPTH_Q4
+#define KD_MMVQ_DEPTH_Q4 2
+#endif
+#ifndef KD_MMVQ_DEPTH_Q8
+#define KD_MMVQ_DEPTH_Q8 2
+#endif
+#ifndef KD_MMVQ_WAVE_QUADS
+#define KD_MMVQ_WAVE_QUADS 4
+#endif
+
+
 constexpr int kTileQ8 = 2048;
 constexpr int kTileQ4 = 1024;
 
@@ -73,47 +87,29 @@ __global__ void pack_weight_kernel(const uint8_t* __restrict__ src_qs, const __h
 // ---------------------------------------------------------------------------------------
 // Activation quantiser: one thread per (row, block).
 // ---------------------------------------------------------------------------------------
-__global__ void act_quant_kernel(const float* __restrict__ x, int B, int k, int ldx, int NQ,
-                                 int8_t* __restrict__ qs, float* __restrict__ d) {
-  const int nb_pad = NQ * 4;
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= B * nb_pad) return;
-  const int b = idx / nb_pad, blk = idx % nb_pad;
-  float v[32];
-  if (blk * 32 < k) {
-    const float4* s = reinterpret_cast<const float4*>(x + (size_t)b * ldx + blk * 32);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float4 t = s[i];
-      v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = 0.0f;
-  }
-  quant32(v, qs + ((size_t)b * NQ + (blk >> 2)) * 128 + (blk & 3) * 8, d + (size_t)b * nb_pad + blk);
+// grid (ceil(blocks / 32), rows); 8 lanes per 32-element block.
+__global__ __launch_bounds__(256) void act_quant_kernel(const float* __restrict__ x, int k, int ldx, int NQ,
+                                                        int8_t* __restrict__ qs, float* __restrict__ d) {
+  const int b = blockIdx.y;
+  const int sub = threadIdx.x & 7;
+  const int blk = blockIdx.x * 32 + (threadIdx.x >> 3);
+  const int nbp = NQ * 4;
+  float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if (blk * 32 < k) v = *reinterpret_cast<const float4*>(x + (size_t)b * ldx + blk * 32 + 4 * sub);
+  quant4_lane8(v, sub, blk < nbp, qs + ((size_t)b * NQ + (blk >> 2)) * 128 + (blk & 3) * 8, d + (size_t)b * nbp + blk);
 }
 
 // ---------------------------------------------------------------------------------------
 // mmvq
 // ---------------------------------------------------------------------------------------
-__device__ inline long q4_operand(uint32_t w) {
-  // Four bytes of a Q4_0 block: low nibbles = elements 4g..4g+3, high nibbles = 4g+16..4g+19.
-  // Nibble n -> signed code n - 8 per byte: (n + 0x78) ^ 0x80 (no carry leaves a byte).
-  uint32_t lo = w & 0x0F0F0F0Fu;
-  uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
-  lo = (lo + 0x78787878u) ^ 0x80808080u;
-  hi = (hi + 0x78787878u) ^ 0x80808080u;
-  return (long)(((uint64_t)hi << 32) | (uint64_t)lo);
-}
-
 __device__ inline long lo64(int4 v) { return (long)(((uint64_t)(uint32_t)v.y << 32) | (uint32_t)v.x); }
 __device__ inline long hi64(int4 v) { return (long)(((uint64_t)(uint32_t)v.w << 32) | (uint32_t)v.z); }
 
 struct MmvqArgs {
   const uint8_t* wq;
   const __half* wd;
-  int n_out, NQ, kblocks;
+  uint32_t w_bytes, d_bytes, x_bytes, xd_bytes;  // buffer extents (reads past them return 0)
+  int n_out, NR, NQ, QW, kblocks;
   const int8_t* xq;
   const float* xd;
   int B;
@@ -127,11 +123,120 @@ struct MmvqArgs {
   int32_t* debug_S;  // [B][n_out][kblocks] when non-null (epilogue replaced)
 };
 
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+// Streaming (non-temporal) loads for weights: read once per step, kept out of the way of
+// the activations that every workgroup re-reads.
+__device__ __forceinline__ int4 ld_nt16(const void* p) {
+#if KD_MMVQ_NT
+  const v4i v = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
+  return make_int4(v.x, v.y, v.z, v.w);
+#else
+  return *reinterpret_cast<const int4*>(p);
+#endif
+}
+__device__ __forceinline__ uint2 ld_nt8(const void* p) {
+#if KD_MMVQ_NT
+  const v2u v = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(p));
+  return make_uint2(v.x, v.y);
+#else
+  return *reinterpret_cast<const uint2*>(p);
+#endif
+}
+
+__device__ __forceinline__ float f4_get(const float4& v, int j) {
+  return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
+}
+
+// The A operand of lane n for the 4 blocks of one quad: 32 bytes (2 x 16-byte loads).
+__device__ __forceinline__ long act_op(const int4& a0, const int4& a1, int j) {
+  return (j == 0) ? lo64(a0) : (j == 1) ? hi64(a0) : (j == 2) ? lo64(a1) : hi64(a1);
+}
+
+// B operand of a weight tile for block j of the quad.  Q8_0: the 8 codes.  Q4_0: the 8
+// nibbles as unsigned bytes 0..15 (low nibbles = elements 4g..4g+3, high = 4g+16..4g+19);
+// the -8 offset of every code is added by a second MFMA against a constant -8 operand.
 template <int FMT>
-__global__ __launch_bounds__(512) void mmvq_kernel(MmvqArgs a) {
+__device__ __forceinline__ long w_op(const int4& w0, const int4& w1, int j) {
+  if (FMT == KD_FMT_Q8_0) return (j == 0) ? lo64(w0) : (j == 1) ? hi64(w0) : (j == 2) ? lo64(w1) : hi64(w1);
+  const uint32_t word = (j == 0) ? (uint32_t)w0.x : (j == 1) ? (uint32_t)w0.y : (j == 2) ? (uint32_t)w0.z : (uint32_t)w0.w;
+  const uint32_t lo = word & 0x0F0F0F0Fu;
+  const uint32_t hi = (word >> 4) & 0x0F0F0F0Fu;
+  return (long)(((uint64_t)hi << 32) | (uint64_t)lo);
+}
+
+// Exact int32 block dots for block j: S = sum_k x_k * q_k.  For Q4_0, q_k = nibble_k - 8, so
+// S = sum_k x_k * nibble_k + sum_k x_k * (-8): the second term is one more MFMA against the
+// constant operand -8 (all bytes 0xF8), accumulated into the first (integers: exact).
+template <int FMT>
+__device__ __forceinline__ v4i block_dots(long A, long Bw) {
+  const v4i zero = {0, 0, 0, 0};
+  v4i S = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, Bw, zero, 0, 0, 0);
+  if (FMT == KD_FMT_Q4_0) S = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, (long)0xF8F8F8F8F8F8F8F8ull, S, 0, 0, 0);
+  return S;
+}
+
+__device__ __forceinline__ float half_bits(uint32_t hw, int hi) {
+  return __half2float(__ushort_as_half((unsigned short)(hi ? (hw >> 16) : (hw & 0xFFFF))));
+}
+
+// Buffer resources: raw (stride 0) descriptors whose offsets past num_records read as zero
+// without touching memory -- used to mask the activation rows that hold no live row.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+// AUX = 2: non-temporal (streamed once) on gfx950.
+template <int AUX>
+__device__ __forceinline__ int4 buf16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
+  return make_int4(v.x, v.y, v.z, v.w);
+}
+template <int AUX>
+__device__ __forceinline__ uint2 buf8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef int v2i __attribute__((ext_vector_type(2)));
+  const v2i v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX);
+  return make_uint2((uint32_t)v.x, (uint32_t)v.y);
+}
+constexpr int kWeightAux = KD_MMVQ_NT ? 2 : 0;
+__device__ __forceinline__ float buf4f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+constexpr uint32_t kOOB = 0x80000000u;  // an offset past every buffer this kernel reads
+
+// One quad of a wave's stream: the weight tile (16 B per lane, two for Q8_0), its scales and
+// the lane's activation operand (2 x 16 B).
+template <int FMT>
+struct QStage {
+  int4 w0, w1, a0, a1;
+  uint2 dw;
+};
+
+// Issue the loads of quad q (offsets past the wave's range read zeros with no traffic).
+template <int FMT>
+__device__ __forceinline__ void qstage_load(QStage<FMT>& st, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rd,
+                                            __amdgpu_buffer_rsrc_t rx, uint32_t w_off, uint32_t d_off, uint32_t a_off,
+                                            int q, bool valid) {
   constexpr int TILE = FMT == KD_FMT_Q8_0 ? kTileQ8 : kTileQ4;
-  const int r = blockIdx.x;  // 16-row group
-  const int e = blockIdx.y;  // group (expert) for grouped products
+  const uint32_t wo = valid ? w_off + (uint32_t)q * TILE : kOOB;
+  st.w0 = buf16<kWeightAux>(rw, wo);
+  st.w1 = (FMT == KD_FMT_Q8_0) ? buf16<kWeightAux>(rw, valid ? wo + 1024 : kOOB) : st.w0;
+  st.dw = buf8<kWeightAux>(rd, valid ? d_off + (uint32_t)q * 128 : kOOB);
+  const uint32_t ao = (valid && a_off != kOOB) ? a_off + (uint32_t)q * 128 : kOOB;
+  st.a0 = buf16<0>(rx, ao);
+  st.a1 = buf16<0>(rx, ao == kOOB ? kOOB : ao + 16);
+}
+
+// grid (NR, n_groups); block = nw waves.  Wave w streams quads [q0, q1) = [w*QW, min(NQ,
+// w*QW + QW)) of the row group (a partition that depends on NQ only) through a depth-D
+// register ring: quad q is computed while quads q+1 .. q+D-1 are in flight.  Loads are
+// branch-free (out-of-range quads read zeros and add exactly zero).  The wave stages its
+// own activation scales in its own LDS slice; the waves' partial sums are added in wave
+// order through LDS.
+// Dynamic LDS: per-wave activation scales [nw][16][QW][4] floats, then [nw][4][64] floats.
+template <int FMT, int QW, int NS, bool DEBUG>
+__global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
+  constexpr int D0 = FMT == KD_FMT_Q8_0 ? KD_MMVQ_DEPTH_Q8 : KD_MMVQ_DEPTH_Q4;
+  constexpr int D = D0 < QW ? D0 : QW;
+  const int e = blockIdx.y;
   int nrows = a.B;
   const int32_t* act_row = nullptr;
   const int32_t* out_row = nullptr;
@@ -141,112 +246,149 @@ __global__ __launch_bounds__(512) void mmvq_kernel(MmvqArgs a) {
     act_row = a.act_row + e * 16;
     out_row = a.out_row + e * 16;
   }
+  constexpr int TILE = FMT == KD_FMT_Q8_0 ? kTileQ8 : kTileQ4;
+  extern __shared__ float smem[];
   const int nw = blockDim.x >> 6;
   const int w = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, n = lane & 15;
   const int NQ = a.NQ;
-  // K-slice of this wave: a function of NQ (hence of k) only.
-  const int q0 = (w * NQ) / nw, q1 = ((w + 1) * NQ) / nw;
-  const int ns = nrows < 4 ? nrows : 4;  // epilogue slots that can hold a live row
+  const int q0 = w * QW;
+  const int q1 = min(NQ, q0 + QW);
+  const int rg = blockIdx.x;
 
-  const size_t tile0 = (size_t)e * (size_t)a.w_group_tiles + (size_t)r * NQ;
-  const uint8_t* wt = a.wq + tile0 * TILE + lane * 16;
-  const __half* dt = a.wd + tile0 * 64 + n * 4;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.wq, a.w_bytes);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.wd, a.d_bytes);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.xq, a.x_bytes);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.xd, a.xd_bytes);
+  const uint32_t tile0 = (uint32_t)((size_t)e * (size_t)a.w_group_tiles + (size_t)rg * NQ);
+  const uint32_t w_off = tile0 * TILE + lane * 16;
+  const uint32_t d_off = tile0 * 128 + n * 8;
+  // A operand row of lane n (rows past the live rows read zeros)
+  const uint32_t a_off = (n < nrows) ? (uint32_t)(act_row ? act_row[n] : n) * (uint32_t)NQ * 128u + g * 32 : kOOB;
 
-  // A operand: activation row of lane's i = n
-  const bool a_live = n < nrows;
-  const int a_row = a_live ? (act_row ? act_row[n] : n) : 0;
-  const int8_t* ap = a.xq + (size_t)a_row * NQ * 128 + g * 32;
-  // epilogue rows of lane's slots: i = 4g + s
-  int s_row[4];
-  bool s_live[4];
+  // ---- this wave's activation scales: rows 0..15 x quads [q0, q0 + QW), float4 per
+  // (row, quad); lane l stages (row l/4, quads (l%4) + 4i).
+  float* dxw = smem + w * (16 * QW * 4);  // this wave's [16][QW][4]
+  if (!DEBUG) {
+    const int r = lane >> 2, p = lane & 3;
+    const uint32_t row_base = (r < nrows) ? (uint32_t)(act_row ? act_row[r] : r) * (uint32_t)NQ * 16u : kOOB;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int i = 4 * g + s;
-    s_live[s] = (s < ns) && (i < nrows);
-    s_row[s] = s_live[s] ? (act_row ? act_row[i] : i) : 0;
+    for (int qq = p; qq < QW; qq += 4) {
+      const int q = q0 + qq;
+      const uint32_t off = (q < q1 && row_base != kOOB) ? row_base + (uint32_t)q * 16u : kOOB;
+      const int4 v = buf16<0>(rs, off);
+      *reinterpret_cast<int4*>(dxw + (r * QW + qq) * 4) = v;
+    }
   }
-  const int nbp = NQ * 4;
 
+  // ---- prologue: D quads in flight
+  QStage<FMT> st[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) qstage_load<FMT>(st[i], rw, rd, rx, w_off, d_off, a_off, q0 + i, q0 + i < q1);
+
+  // ---- the stream, fully unrolled (no loop back-edge, so every wait is exact): quad
+  // q0 + j is computed from stage j % D, which is then refilled with quad q0 + j + D.
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  const v4i zero = {0, 0, 0, 0};
-
-  for (int q = q0; q < q1; ++q) {
-    int4 w0 = *reinterpret_cast<const int4*>(wt + (size_t)q * TILE);
-    int4 w1 = w0;
-    if (FMT == KD_FMT_Q8_0) w1 = *reinterpret_cast<const int4*>(wt + (size_t)q * TILE + 1024);
-    const uint2 dwr = *reinterpret_cast<const uint2*>(dt + (size_t)q * 64);
-    int4 a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
-    if (a_live) {
-      a0 = *reinterpret_cast<const int4*>(ap + (size_t)q * 128);
-      a1 = *reinterpret_cast<const int4*>(ap + (size_t)q * 128 + 16);
-    }
+#pragma unroll
+  for (int j = 0; j < QW; ++j) {
+    QStage<FMT>& cur = st[j % D];
+    const int q = q0 + j;
+    const bool live = q < q1;
+    const float zsc = live ? 1.0f : 0.0f;
     float4 dx[4];
+    if (!DEBUG) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      dx[s] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      if (s < ns && s_live[s]) dx[s] = *reinterpret_cast<const float4*>(a.xd + (size_t)s_row[s] * nbp + q * 4);
+      for (int s = 0; s < NS; ++s) dx[s] = *reinterpret_cast<const float4*>(dxw + ((4 * g + s) * QW + j) * 4);
     }
-    float dw[4];
-    dw[0] = __half2float(__ushort_as_half((unsigned short)(dwr.x & 0xFFFF)));
-    dw[1] = __half2float(__ushort_as_half((unsigned short)(dwr.x >> 16)));
-    dw[2] = __half2float(__ushort_as_half((unsigned short)(dwr.y & 0xFFFF)));
-    dw[3] = __half2float(__ushort_as_half((unsigned short)(dwr.y >> 16)));
-
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const long A = (j == 0) ? lo64(a0) : (j == 1) ? hi64(a0) : (j == 2) ? lo64(a1) : hi64(a1);
-      long Bw;
-      if (FMT == KD_FMT_Q8_0) {
-        Bw = (j == 0) ? lo64(w0) : (j == 1) ? hi64(w0) : (j == 2) ? lo64(w1) : hi64(w1);
-      } else {
-        const uint32_t word = (j == 0) ? (uint32_t)w0.x : (j == 1) ? (uint32_t)w0.y : (j == 2) ? (uint32_t)w0.z : (uint32_t)w0.w;
-        Bw = q4_operand(word);
-      }
-      const v4i S = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, Bw, zero, 0, 0, 0);
-      if (a.debug_S) {
-        const int blk = 4 * q + j;
-        const int row = r * 16 + n;
+    for (int jb = 0; jb < 4; ++jb) {
+      const v4i S = block_dots<FMT>(act_op(cur.a0, cur.a1, jb), w_op<FMT>(cur.w0, cur.w1, jb));
+      if (DEBUG) {
+        const int blk = 4 * q + jb;
+        const int row = rg * 16 + n;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const int i = 4 * g + s;
-          if (i < nrows && row < a.n_out && blk < a.kblocks)
-            a.debug_S[((size_t)i * a.n_out + row) * a.kblocks + blk] = S[s];
+          const int r = 4 * g + s;
+          if (live && r < nrows && row < a.n_out && blk < a.kblocks)
+            a.debug_S[((size_t)r * a.n_out + row) * a.kblocks + blk] = S[s];
         }
-        continue;
-      }
-      const float dxs[4] = {j == 0 ? dx[0].x : j == 1 ? dx[0].y : j == 2 ? dx[0].z : dx[0].w,
-                            j == 0 ? dx[1].x : j == 1 ? dx[1].y : j == 2 ? dx[1].z : dx[1].w,
-                            j == 0 ? dx[2].x : j == 1 ? dx[2].y : j == 2 ? dx[2].z : dx[2].w,
-                            j == 0 ? dx[3].x : j == 1 ? dx[3].y : j == 2 ? dx[3].z : dx[3].w};
+      } else {
+        const float dwj = zsc * half_bits(jb < 2 ? cur.dw.x : cur.dw.y, jb & 1);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        if (s < ns) acc[s] = fmaf(dw[j] * dxs[s], (float)S[s], acc[s]);
+        for (int s = 0; s < NS; ++s) acc[s] = fmaf(dwj * f4_get(dx[s], jb), (float)S[s], acc[s]);
       }
     }
+    if (j + D < QW) qstage_load<FMT>(cur, rw, rd, rx, w_off, d_off, a_off, q + D, q + D < q1);
   }
-  if (a.debug_S) return;
+  if (DEBUG) return;
 
-  __shared__ float red[8][4][64];
+  float* red = smem + nw * (16 * QW * 4);  // [nw][4][64]
 #pragma unroll
-  for (int s = 0; s < 4; ++s) red[w][s][lane] = acc[s];
+  for (int s = 0; s < 4; ++s) red[(w * 4 + s) * 64 + lane] = acc[s];
   __syncthreads();
-  for (int t = threadIdx.x; t < 256; t += blockDim.x) {  // 256 (slot, lane) outputs, any wave count
+  for (int t = threadIdx.x; t < 256; t += blockDim.x) {
     const int s = t >> 6, l = t & 63;
-    float v = red[0][s][l];
-    for (int ww = 1; ww < nw; ++ww) v += red[ww][s][l];  // fixed wave order
-    const int i = 4 * (l >> 4) + s;
-    const int row = r * 16 + (l & 15);
-    if (i < nrows && row < a.n_out) {
-      const int orow = out_row ? out_row[i] : i;
+    float v = red[s * 64 + l];
+    for (int ww = 1; ww < nw; ++ww) v += red[(ww * 4 + s) * 64 + l];  // fixed wave order
+    const int r = 4 * (l >> 4) + s;
+    const int row = rg * 16 + (l & 15);
+    if (r < nrows && row < a.n_out) {
+      const int orow = out_row ? out_row[r] : r;
       a.y[(size_t)orow * a.ldy + row] = v;
     }
   }
 }
 
-// Waves per workgroup: a function of the quad count only (never of B).
-static int mmvq_waves(int NQ) { return NQ >= 8 ? 8 : NQ; }
+// Quads per wave: about KD_MMVQ_WAVE_QUADS, and enough that at most 16 waves cover NQ;
+// then balanced (the smallest QW giving the same wave count).  Waves per workgroup:
+// ceil(NQ / QW).  Both depend on the matrix's k only.
+static int mmvq_qw(int NQ) {
+  int qw = ceil_div(NQ, 16);  // at most 16 waves; QW <= 8 covers k <= 16384
+  const int want = NQ < KD_MMVQ_WAVE_QUADS ? NQ : KD_MMVQ_WAVE_QUADS;
+  qw = qw > want ? qw : want;
+  const int nw = ceil_div(NQ, qw);
+  return ceil_div(NQ, nw);
+}
+
+template <int FMT, int QW, int NS>
+static void launch_mmvq_qn(const MmvqArgs& a, int n_groups, hipStream_t st) {
+  const int nw = ceil_div(a.NQ, QW);
+  dim3 grid(a.NR, n_groups);
+  const size_t dx_shm = (size_t)nw * 16 * QW * 4 * sizeof(float);
+  if (a.debug_S) {
+    mmvq_kernel<FMT, QW, 4, true><<<grid, 64 * nw, dx_shm, st>>>(a);
+  } else {
+    mmvq_kernel<FMT, QW, NS, false><<<grid, 64 * nw, dx_shm + (size_t)nw * 256 * sizeof(float), st>>>(a);
+  }
+}
+
+template <int FMT, int QW>
+static void launch_mmvq_q(const MmvqArgs& a, int n_groups, hipStream_t st) {
+  // epilogue slots: a function of B (rows past B are never written, so dropping their
+  // slots leaves every live output's operation sequence unchanged)
+  const int ns = a.count ? 4 : (a.B < 4 ? a.B : 4);
+  switch (ns) {
+    case 1: return launch_mmvq_qn<FMT, QW, 1>(a, n_groups, st);
+    case 2: return launch_mmvq_qn<FMT, QW, 2>(a, n_groups, st);
+    case 3: return launch_mmvq_qn<FMT, QW, 3>(a, n_groups, st);
+    default: return launch_mmvq_qn<FMT, QW, 4>(a, n_groups, st);
+  }
+}
+
+template <int FMT>
+static void launch_mmvq_t(const MmvqArgs& a, int n_groups, hipStream_t st) {
+  switch (a.QW) {
+    case 1: return launch_mmvq_q<FMT, 1>(a, n_groups, st);
+    case 2: return launch_mmvq_q<FMT, 2>(a, n_groups, st);
+    case 3: return launch_mmvq_q<FMT, 3>(a, n_groups, st);
+    case 4: return launch_mmvq_q<FMT, 4>(a, n_groups, st);
+    case 5: return launch_mmvq_q<FMT, 5>(a, n_groups, st);
+    case 6: return launch_mmvq_q<FMT, 6>(a, n_groups, st);
+    case 7: return launch_mmvq_q<FMT, 7>(a, n_groups, st);
+    default: return launch_mmvq_q<FMT, 8>(a, n_groups, st);
+  }
+}
 
 void launch_mmvq(const kd_weight& W, const int8_t* xq, const float* xd, int B, float* y, int ldy,
                  hipStream_t st, const RowMap* map, int32_t* debug_S) {
@@ -254,7 +396,9 @@ void launch_mmvq(const kd_weight& W, const int8_t* xq, const float* xd, int B, f
   a.wq = static_cast<const uint8_t*>(W.qs);
   a.wd = static_cast<const __half*>(W.d);
   a.n_out = W.n_out;
+  a.NR = n_rowgroups(W.n_out);
   a.NQ = n_quads(W.k);
+  a.QW = mmvq_qw(a.NQ);
   a.kblocks = W.k / 32;
   a.xq = xq;
   a.xd = xd;
@@ -266,19 +410,24 @@ void launch_mmvq(const kd_weight& W, const int8_t* xq, const float* xd, int B, f
   a.out_row = map ? map->out_row : nullptr;
   a.w_group_tiles = map ? map->w_group_tiles : 0;
   a.debug_S = debug_S;
-  const int NR = n_rowgroups(W.n_out);
-  dim3 grid(NR, map ? map->n_groups : 1);
-  dim3 block(64 * mmvq_waves(a.NQ));
+  const int ng = map ? map->n_groups : 1;
+  {
+    const size_t tiles = (size_t)(map ? map->n_groups : 1) * (map ? (size_t)map->w_group_tiles : (size_t)a.NR * a.NQ);
+    a.w_bytes = (uint32_t)(tiles * (W.fmt == KD_FMT_Q8_0 ? kTileQ8 : kTileQ4));
+    a.d_bytes = (uint32_t)(tiles * 128);
+    const size_t rows = map ? (size_t)map->act_rows : (size_t)B;
+    a.x_bytes = (uint32_t)(rows * a.NQ * 128);
+    a.xd_bytes = (uint32_t)(rows * a.NQ * 16);
+  }
   if (W.fmt == KD_FMT_Q8_0)
-    mmvq_kernel<KD_FMT_Q8_0><<<grid, block, 0, st>>>(a);
+    launch_mmvq_t<KD_FMT_Q8_0>(a, ng, st);
   else
-    mmvq_kernel<KD_FMT_Q4_0><<<grid, block, 0, st>>>(a);
+    launch_mmvq_t<KD_FMT_Q4_0>(a, ng, st);
 }
 
 void launch_act_quant(const float* x, int B, int k, int ldx, int8_t* qs, float* d, hipStream_t st) {
   const int NQ = n_quads(k);
-  const int total = B * NQ * 4;
-  act_quant_kernel<<<ceil_div(total, 256), 256, 0, st>>>(x, B, k, ldx, NQ, qs, d);
+  act_quant_kernel<<<dim3(ceil_div(NQ * 4, 32), B), 256, 0, st>>>(x, k, ldx, NQ, qs, d);
 }
 
 }  // namespace kd

@@ -13,18 +13,36 @@ namespace kd {
 // ---------------------------------------------------------------------------------------
 // RMSNorm (+ residual add) (+ quantise).  One 256-thread workgroup per row.
 // ---------------------------------------------------------------------------------------
+// Thread layout: 8 lanes per 32-element block (lane sub holds 4 consecutive elements as a
+// float4), 32 blocks per pass of the 256 threads; the row stays in registers between the
+// sum of squares and the normalise + quantise pass.  Sum of squares: per thread in pass
+// order, then a fixed xor tree per wave, then the 4 wave sums in wave order.
+template <int MAXP>
 __global__ __launch_bounds__(256) void norm_quant_kernel(const float* __restrict__ x, const float* __restrict__ r,
                                                          const float* __restrict__ g, int n, float eps,
                                                          float* __restrict__ x1_out, float* __restrict__ y_out,
                                                          int8_t* __restrict__ qs, float* __restrict__ qd) {
   const int b = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, sub = tid & 7, lb = tid >> 3;
+  const int nb = n / 32, NQ = n_quads(n), nbp = NQ * 4;
+  const int P = ceil_div(nbp, 32);
   const float* xr = x + (size_t)b * n;
   const float* rr = r ? r + (size_t)b * n : nullptr;
+  float4 v[MAXP];
   float ss = 0.0f;
-  for (int i = tid; i < n; i += 256) {
-    const float v = rr ? xr[i] + rr[i] : xr[i];
-    ss = fmaf(v, v, ss);
+#pragma unroll
+  for (int p = 0; p < MAXP; ++p) {
+    v[p] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    const int blk = p * 32 + lb;
+    if (p < P && blk < nb) {
+      const int c = blk * 32 + 4 * sub;
+      v[p] = *reinterpret_cast<const float4*>(xr + c);
+      if (rr) v[p] = f4_add(v[p], *reinterpret_cast<const float4*>(rr + c));
+    }
+    ss = fmaf(v[p].x, v[p].x, ss);
+    ss = fmaf(v[p].y, v[p].y, ss);
+    ss = fmaf(v[p].z, v[p].z, ss);
+    ss = fmaf(v[p].w, v[p].w, ss);
   }
   ss = wave_sum(ss);
   __shared__ float part[4];
@@ -32,30 +50,34 @@ __global__ __launch_bounds__(256) void norm_quant_kernel(const float* __restrict
   __syncthreads();
   const float tot = ((part[0] + part[1]) + part[2]) + part[3];
   const float inv = 1.0f / sqrtf(tot / (float)n + eps);
-  const int nb = n / 32;
-  const int NQ = n_quads(n);
-  for (int blk = tid; blk < NQ * 4; blk += 256) {
-    float v[32];
-    if (blk < nb) {
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const int c = blk * 32 + i;
-        const float xv = rr ? xr[c] + rr[c] : xr[c];
-        if (x1_out) x1_out[(size_t)b * n + c] = xv;
-        v[i] = (xv * inv) * g[c];
-        if (y_out) y_out[(size_t)b * n + c] = v[i];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) v[i] = 0.0f;
+  for (int p = 0; p < MAXP; ++p) {
+    const int blk = p * 32 + lb;
+    float4 y = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (p < P && blk < nb) {
+      const int c = blk * 32 + 4 * sub;
+      const float4 gg = *reinterpret_cast<const float4*>(g + c);
+      y = make_float4((v[p].x * inv) * gg.x, (v[p].y * inv) * gg.y, (v[p].z * inv) * gg.z, (v[p].w * inv) * gg.w);
+      if (x1_out) *reinterpret_cast<float4*>(x1_out + (size_t)b * n + c) = v[p];
+      if (y_out) *reinterpret_cast<float4*>(y_out + (size_t)b * n + c) = y;
     }
-    if (qs) quant32(v, qs + ((size_t)b * NQ + (blk >> 2)) * 128 + (blk & 3) * 8, qd + (size_t)b * NQ * 4 + blk);
+    if (qs && p < P)
+      quant4_lane8(y, sub, blk < nbp, qs + ((size_t)b * NQ + (blk >> 2)) * 128 + (blk & 3) * 8,
+                   qd + (size_t)b * nbp + blk);
   }
 }
 
+int norm_max_len() { return 16 * 1024; }
+
 void launch_norm_quant(const float* x, const float* r, const float* g, int B, int n, float eps, float* x1_out,
                        float* y_out, int8_t* qs, float* d, hipStream_t st) {
-  norm_quant_kernel<<<B, 256, 0, st>>>(x, r, g, n, eps, x1_out, y_out, qs, d);
+  const int P = ceil_div(n_quads(n) * 4, 32);
+  if (P <= 4)
+    norm_quant_kernel<4><<<B, 256, 0, st>>>(x, r, g, n, eps, x1_out, y_out, qs, d);
+  else if (P <= 8)
+    norm_quant_kernel<8><<<B, 256, 0, st>>>(x, r, g, n, eps, x1_out, y_out, qs, d);
+  else
+    norm_quant_kernel<16><<<B, 256, 0, st>>>(x, r, g, n, eps, x1_out, y_out, qs, d);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -139,37 +161,34 @@ void launch_kv_append(const float* k, const float* v, int B, int G, int hd, cons
 }
 
 // ---------------------------------------------------------------------------------------
-// SwiGLU (+ quantise): one thread per 32-element block.
+// SwiGLU (+ quantise): grid (ceil(blocks / 32), rows), 8 lanes per 32-element block.
 // ---------------------------------------------------------------------------------------
-__global__ void swiglu_quant_kernel(const float* __restrict__ g, const float* __restrict__ u, int rows, int n,
-                                    int ld, float* __restrict__ a_out, int8_t* __restrict__ qs,
-                                    float* __restrict__ qd) {
-  const int NQ = n_quads(n);
-  const int nbp = NQ * 4;
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= rows * nbp) return;
-  const int b = idx / nbp, blk = idx % nbp;
-  float v[32];
-  if (blk * 32 < n) {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const int c = blk * 32 + i;
-      const float gv = g[(size_t)b * ld + c];
-      const float sv = gv / (1.0f + expf(-gv));
-      v[i] = sv * u[(size_t)b * ld + c];
-      if (a_out) a_out[(size_t)b * n + c] = v[i];
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = 0.0f;
+__global__ __launch_bounds__(256) void swiglu_quant_kernel(const float* __restrict__ g, const float* __restrict__ u,
+                                                           int n, int ld, float* __restrict__ a_out,
+                                                           int8_t* __restrict__ qs, float* __restrict__ qd) {
+  const int b = blockIdx.y;
+  const int sub = threadIdx.x & 7;
+  const int blk = blockIdx.x * 32 + (threadIdx.x >> 3);
+  const int nb = n / 32, NQ = n_quads(n), nbp = NQ * 4;
+  float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if (blk < nb) {
+    const int c = blk * 32 + 4 * sub;
+    const float4 gv = *reinterpret_cast<const float4*>(g + (size_t)b * ld + c);
+    const float4 uv = *reinterpret_cast<const float4*>(u + (size_t)b * ld + c);
+    a.x = (gv.x / (1.0f + expf(-gv.x))) * uv.x;
+    a.y = (gv.y / (1.0f + expf(-gv.y))) * uv.y;
+    a.z = (gv.z / (1.0f + expf(-gv.z))) * uv.z;
+    a.w = (gv.w / (1.0f + expf(-gv.w))) * uv.w;
+    if (a_out) *reinterpret_cast<float4*>(a_out + (size_t)b * n + c) = a;
   }
-  if (qs) quant32(v, qs + ((size_t)b * NQ + (blk >> 2)) * 128 + (blk & 3) * 8, qd + (size_t)b * nbp + blk);
+  if (qs)
+    quant4_lane8(a, sub, blk < nbp, qs + ((size_t)b * NQ + (blk >> 2)) * 128 + (blk & 3) * 8, qd + (size_t)b * nbp + blk);
 }
 
 void launch_swiglu_quant(const float* g, const float* u, int rows, int n, int ld, float* a_out, int8_t* qs, float* d,
                          hipStream_t st) {
-  const int total = rows * n_quads(n) * 4;
-  swiglu_quant_kernel<<<ceil_div(total, 128), 128, 0, st>>>(g, u, rows, n, ld, a_out, qs, d);
+  dim3 grid(ceil_div(n_quads(n) * 4, 32), rows);
+  swiglu_quant_kernel<<<grid, 256, 0, st>>>(g, u, n, ld, a_out, qs, d);
 }
 
 __global__ void add_kernel(const float* __restrict__ x, const float* __restrict__ y, float* __restrict__ z, size_t n) {
@@ -195,8 +214,10 @@ using namespace kd;
 extern "C" kd_status kd_rmsnorm_rows(const float* x, const float* g, float* y, int32_t B, int32_t n, float eps,
                                      void* stream) {
   ROWS_OK("kd_rmsnorm_rows", B, n);
-  KD_REQUIRE(n % 32 == 0, KD_ERR_UNSUPPORTED, "kd_rmsnorm_rows: n=%d is not a multiple of 32", n);
+  KD_REQUIRE(n % 32 == 0 && n <= norm_max_len(), KD_ERR_UNSUPPORTED,
+             "kd_rmsnorm_rows: n=%d is not a multiple of 32 in [32, %d]", n, norm_max_len());
   KD_REQUIRE(x && g && y, KD_ERR_INVALID, "kd_rmsnorm_rows: null pointer");
+  KD_REQUIRE(aligned16(x) && aligned16(g) && aligned16(y), KD_ERR_INVALID, "kd_rmsnorm_rows: unaligned");
   launch_norm_quant(x, nullptr, g, B, n, eps, nullptr, y, nullptr, nullptr, as_stream(stream));
   return check_launch("kd_rmsnorm_rows");
 }
@@ -204,8 +225,11 @@ extern "C" kd_status kd_rmsnorm_rows(const float* x, const float* g, float* y, i
 extern "C" kd_status kd_add_rmsnorm_rows(const float* x, const float* r, const float* g, float* x1, float* y,
                                          int32_t B, int32_t n, float eps, void* stream) {
   ROWS_OK("kd_add_rmsnorm_rows", B, n);
-  KD_REQUIRE(n % 32 == 0, KD_ERR_UNSUPPORTED, "kd_add_rmsnorm_rows: n=%d is not a multiple of 32", n);
+  KD_REQUIRE(n % 32 == 0 && n <= norm_max_len(), KD_ERR_UNSUPPORTED,
+             "kd_add_rmsnorm_rows: n=%d is not a multiple of 32 in [32, %d]", n, norm_max_len());
   KD_REQUIRE(x && r && g && x1 && y, KD_ERR_INVALID, "kd_add_rmsnorm_rows: null pointer");
+  KD_REQUIRE(aligned16(x) && aligned16(r) && aligned16(g) && aligned16(x1) && aligned16(y), KD_ERR_INVALID,
+             "kd_add_rmsnorm_rows: unaligned");
   launch_norm_quant(x, r, g, B, n, eps, x1, y, nullptr, nullptr, as_stream(stream));
   return check_launch("kd_add_rmsnorm_rows");
 }
@@ -229,6 +253,7 @@ extern "C" kd_status kd_swiglu_rows(const float* g, const float* u, float* a, in
   ROWS_OK("kd_swiglu_rows", B, n);
   KD_REQUIRE(n % 32 == 0, KD_ERR_UNSUPPORTED, "kd_swiglu_rows: n=%d is not a multiple of 32", n);
   KD_REQUIRE(g && u && a, KD_ERR_INVALID, "kd_swiglu_rows: null pointer");
+  KD_REQUIRE(aligned16(g) && aligned16(u) && aligned16(a), KD_ERR_INVALID, "kd_swiglu_rows: unaligned");
   launch_swiglu_quant(g, u, B, n, n, a, nullptr, nullptr, as_stream(stream));
   return check_launch("kd_swiglu_rows");
 }

@@ -85,7 +85,8 @@ extern "C" kd_status kd_model_create(const kd_model_desc* desc, kd_model** out) 
   KD_REQUIRE(desc && out, KD_ERR_INVALID, "kd_model_create: null argument");
   const kd_model_desc& m = *desc;
   KD_REQUIRE(m.n_layers >= 1 && m.layers, KD_ERR_INVALID, "kd_model_create: n_layers=%d", m.n_layers);
-  KD_REQUIRE(m.d > 0 && m.d % 32 == 0, KD_ERR_UNSUPPORTED, "kd_model_create: d=%d not a positive multiple of 32", m.d);
+  KD_REQUIRE(m.d > 0 && m.d % 32 == 0 && m.d <= norm_max_len(), KD_ERR_UNSUPPORTED,
+             "kd_model_create: d=%d not a multiple of 32 in [32, %d]", m.d, norm_max_len());
   KD_REQUIRE(fa_shape_supported(m.n_head, m.n_head_kv, m.head_dim), KD_ERR_UNSUPPORTED,
              "kd_model_create: H=%d G=%d hd=%d unsupported (H/G in {1,2,4,8}, hd in {64,128})", m.n_head, m.n_head_kv,
              m.head_dim);
@@ -109,8 +110,12 @@ extern "C" kd_status kd_model_create(const kd_model_desc* desc, kd_model** out) 
     KD_TRY(check_weight("wo", il, L.wo, d, H * hd));
     if (m.ffn > 0 || moe) KD_REQUIRE(L.ffn_norm, KD_ERR_INVALID, "kd_model_create: layer %d: null ffn_norm", il);
     if (m.ffn > 0) {
-      KD_TRY(check_weight("w_gate", il, L.w_gate, m.ffn, d));
-      KD_TRY(check_weight("w_up", il, L.w_up, m.ffn, d));
+      if (L.w_up.qs) {
+        KD_TRY(check_weight("w_gate", il, L.w_gate, m.ffn, d));
+        KD_TRY(check_weight("w_up", il, L.w_up, m.ffn, d));
+      } else {
+        KD_TRY(check_weight("w_gate (stacked gate+up)", il, L.w_gate, 2 * m.ffn, d));
+      }
       KD_TRY(check_weight("w_down", il, L.w_down, d, m.ffn));
     }
     if (moe) {
@@ -299,15 +304,19 @@ extern "C" kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x
     launch_norm_quant(res, s.o, Ly.ffn_norm, B, D, d.rms_eps, x1, moe ? s.z : nullptr, s.act_qs, s.act_d, st);
     if (!moe) {
       const int F = d.ffn;
-      launch_mmvq(Ly.w_gate, s.act_qs, s.act_d, B, s.gu, 2 * F, st);
-      launch_mmvq(Ly.w_up, s.act_qs, s.act_d, B, s.gu + F, 2 * F, st);
+      if (Ly.w_up.qs) {
+        launch_mmvq(Ly.w_gate, s.act_qs, s.act_d, B, s.gu, 2 * F, st);
+        launch_mmvq(Ly.w_up, s.act_qs, s.act_d, B, s.gu + F, 2 * F, st);
+      } else {  // stacked [gate; up]: one pass writes gate to columns [0, F) and up to [F, 2F)
+        launch_mmvq(Ly.w_gate, s.act_qs, s.act_d, B, s.gu, 2 * F, st);
+      }
       launch_swiglu_quant(s.gu, s.gu + F, B, F, 2 * F, nullptr, s.act_qs, s.act_d, st);
       launch_mmvq(Ly.w_down, s.act_qs, s.act_d, B, s.f, D, st);
     } else {
       const int E = d.n_experts, K = d.n_expert_used, Fe = d.expert_ffn, Fs = d.shared_ffn;
       launch_router(s.z, Ly.router, B, D, E, K, s.ids, s.p, nullptr, st);
       launch_bucket(s.ids, B, K, E, s.count, s.rows, s.pairs, st);
-      RowMap gu_map{s.count, s.rows, s.pairs, E, (long long)n_rowgroups(Fe) * n_quads(D)};
+      RowMap gu_map{s.count, s.rows, s.pairs, E, (long long)n_rowgroups(Fe) * n_quads(D), B};
       kd_weight eg = Ly.e_gate, eu = Ly.e_up, ed = Ly.e_down;
       eg.n_out = Fe;
       eu.n_out = Fe;
@@ -318,7 +327,7 @@ extern "C" kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x
       launch_mmvq(Ly.s_gate, s.act_qs, s.act_d, B, s.sgu, 2 * Fs, st);
       launch_mmvq(Ly.s_up, s.act_qs, s.act_d, B, s.sgu + Fs, 2 * Fs, st);
       launch_swiglu_quant(s.gup, s.gup + Fe, B * K, Fe, 2 * Fe, nullptr, s.hq_qs, s.hq_d, st);
-      RowMap dn_map{s.count, s.pairs, s.pairs, E, (long long)n_rowgroups(D) * n_quads(Fe)};
+      RowMap dn_map{s.count, s.pairs, s.pairs, E, (long long)n_rowgroups(D) * n_quads(Fe), B * K};
       launch_mmvq(ed, s.hq_qs, s.hq_d, 0, s.yp, D, st, &dn_map);
       launch_swiglu_quant(s.sgu, s.sgu + Fs, B, Fs, 2 * Fs, nullptr, s.act_qs, s.act_d, st);
       launch_mmvq(Ly.s_down, s.act_qs, s.act_d, B, s.sh, D, st);

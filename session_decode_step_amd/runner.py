@@ -30,9 +30,9 @@ class GpuWorkload:
         fill_sessions = range(n_sess) if sessions is None else sessions
         if fill == "seeded":
             for s in fill_sessions:
-                for il in range(sp.n_layers):
-                    k, v = W.kv_prefill(wl, s, il)
-                    self.caches.fill_prefill(s, il, k, v)
+                pairs = [(s, il) for il in range(sp.n_layers)]
+                for (ss, il), (k, v) in zip(pairs, W.kv_prefill_many(wl, pairs)):
+                    self.caches.fill_prefill(ss, il, k, v)
         else:
             gen = torch.Generator(device=device)
             for s in fill_sessions:

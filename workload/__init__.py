@@ -207,9 +207,15 @@ def make_layer(spec: ModelSpec, code: int, seed: int, il: int) -> Dict:
     return L
 
 
-def make_model(spec: ModelSpec, code: int, seed: int = 0) -> Dict:
-    """All weights of a model: {"spec", "layers": [...], "final_norm", "lm_head"}."""
-    m: Dict = {"spec": spec, "layers": [make_layer(spec, code, seed, il) for il in range(spec.n_layers)]}
+def make_model(spec: ModelSpec, code: int, seed: int = 0, threads: int = 8) -> Dict:
+    """All weights of a model: {"spec", "layers": [...], "final_norm", "lm_head"}.
+
+    Layers are drawn on a thread pool; every tensor has its own seed key, so the arrays do
+    not depend on the thread count or order."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max(1, threads)) as ex:
+        layers = list(ex.map(lambda il: make_layer(spec, code, seed, il), range(spec.n_layers)))
+    m: Dict = {"spec": spec, "layers": layers}
     m["final_norm"] = draw_gain(seed, code, T_FINAL_NORM, 0, spec.d) if spec.final_norm else None
     m["lm_head"] = (draw_weight(spec.fmt, seed, code, T_LM_Q, T_LM_D, 0, spec.vocab, spec.d)
                     if spec.vocab else None)
@@ -234,6 +240,13 @@ def kv_prefill(wl: Workload, session: int, layer: int) -> Tuple[np.ndarray, np.n
     k = rk.standard_normal(shape, dtype=np.float32).astype(np.float16)
     v = rv.standard_normal(shape, dtype=np.float32).astype(np.float16)
     return k, v
+
+
+def kv_prefill_many(wl: Workload, pairs, threads: int = 8):
+    """kv_prefill for many (session, layer) pairs on a thread pool; same arrays as one by one."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max(1, threads)) as ex:
+        return list(ex.map(lambda p: kv_prefill(wl, p[0], p[1]), pairs))
 
 
 def algorithmic_bytes_weights(spec: ModelSpec) -> int:
