@@ -31,23 +31,183 @@ HBM_PEAK_GBS = 8000.0
 
 
 def summarize_trace(path: str) -> None:
+    """Per-(kernel, grid) call counts and average durations from a rocprofv3 kernel-trace
+    CSV, then the longest run of back-to-back dispatches of one (kernel, grid): the bench's
+    own timing loop of the dominant kernel, whose average the bench reports."""
     import csv
     from collections import defaultdict
-    acc = defaultdict(lambda: [0, 0.0])
+    acc = defaultdict(lambda: [0, 0.0, 0])
+    seq = []
     with open(path) as f:
         for row in csv.DictReader(f):
             name = row.get("Kernel_Name") or row.get("KernelName") or "?"
             grid = "x".join(row.get(k, "") for k in ("Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z") if k in row)
-            if not grid:
-                grid = row.get("Grid_Size", "")
             dur = float(row["End_Timestamp"]) - float(row["Start_Timestamp"])
-            a = acc[(name[:90], grid)]
+            key = (name[:90], grid)
+            a = acc[key]
             a[0] += 1
             a[1] += dur
+            a[2] = int(row.get("VGPR_Count") or 0) + int(row.get("Accum_VGPR_Count") or 0)
+            seq.append((int(row.get("Dispatch_Id") or len(seq)), key, dur))
+    seq.sort()
     tot = sum(v[1] for v in acc.values())
-    print(f"{'calls':>7} {'avg_us':>10} {'total_ms':>10} {'share':>6}  grid  kernel")
-    for (name, grid), (n, t) in sorted(acc.items(), key=lambda kv: -kv[1][1]):
-        print(f"{n:7d} {t / n / 1e3:10.2f} {t / 1e6:10.3f} {100 * t / tot:5.1f}%  {grid}  {name}")
+    print(f"{'calls':>7} {'avg_us':>10} {'total_ms':>10} {'share':>6} {'vgpr':>4}  grid  kernel")
+    for (name, grid), (n, t, vg) in sorted(acc.items(), key=lambda kv: -kv[1][1]):
+        print(f"{n:7d} {t / n / 1e3:10.2f} {t / 1e6:10.3f} {100 * t / tot:5.1f}% {vg:4d}  {grid}  {name}")
+    best, i = (0, 0, 0), 0
+    while i < len(seq):
+        j = i
+        while j + 1 < len(seq) and seq[j + 1][1] == seq[i][1]:
+            j += 1
+        if j - i + 1 > best[0]:
+            best = (j - i + 1, i, j)
+        i = j + 1
+    n, i, j = best
+    if n > 1:
+        durs = [d for _, _, d in seq[i:j + 1]]
+        print(f"\nlongest back-to-back run: {n} dispatches of {seq[i][1][0]} grid {seq[i][1][1]}: "
+              f"avg {sum(durs) / n / 1e3:.2f} us (min {min(durs) / 1e3:.2f}, max {max(durs) / 1e3:.2f})")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def mmvq_algorithmic_bytes(n: int, k: int, B: int) -> int:
+    """Q4_0 weights once (18 B per 32), B int8 activation rows with fp32 block scales, fp32 out."""
+    return n * k * 18 // 32 + B * k + B * (k // 32) * 4 + B * n * 4
+
+
+def time_rotating(launch, iters: int, stream) -> float:
+    """Average launch duration (us) of ``launch(i)`` over ``iters`` launches, HIP events on
+    ``stream`` (the stream the launches go to), after a few untimed ones."""
+    import torch
+    for i in range(4):
+        launch(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(iters):
+        launch(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / iters
+
+
+# ---------------------------------------------------------------------- HBM traffic (PMC)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mmvq_q4_0_28672x4096_b8.txt")
+TRAFFIC_SOURCES = ("session_decode_step_amd/csrc/mmvq.hip", "session_decode_step_amd/csrc/kd_internal.h")
+CALIB_BYTES = 512 << 20
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_probe() -> None:
+    """Launches for the two ``rocprofv3 --pmc`` passes: a plain fp32 elementwise copy of
+    512 MiB (the calibration kernel: reads and writes 512 MiB), then the stacked gate+up
+    mmvq at B=8 on four distinct matrices."""
+    import torch
+    import workload as W
+    import session_decode_step_amd as kd
+    torch.cuda.set_device(0)
+    src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    n, k, B = 28672, 4096, 8
+    mats = [kd.kd_pack_weight(W.draw_weight("q4_0", 0, 4, 90, 91, i, n, k)) for i in range(4)]
+    act = kd.kd_quantize_act_q8(torch.randn((B, k), device="cuda"))
+    y = torch.empty((B, n), dtype=torch.float32, device="cuda")
+    for i in range(8):
+        kd.kd_mmvq_q4_0(mats[i % 4], act, B, y)
+    torch.cuda.synchronize()
+    log("traffic probe done")
+
+
+def _read_counters(path: str):
+    """{dispatch: (kernel_name, counter_value)} from a rocprofv3 counter_collection CSV (or
+    the directory holding it)."""
+    import csv
+    import glob
+    if os.path.isdir(path):
+        hits = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+        if len(hits) != 1:
+            raise SystemExit(f"expected one counter_collection.csv under {path}, found {hits}")
+        path = hits[0]
+    out = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            key = row.get("Dispatch_Id") or row.get("Correlation_Id")
+            name = row.get("Kernel_Name", "?")
+            val = float(row["Counter_Value"])
+            prev = out.get(key, (name, 0.0))
+            out[key] = (name, prev[1] + val)
+    return out
+
+
+def traffic_summarize(fetch: str, write: str, fetch_cmd: str, write_cmd: str) -> None:
+    """Per-dispatch HBM bytes of the mmvq launches from the FETCH_SIZE and WRITE_SIZE passes
+    (KiB per dispatch), each scaled by what the counter reads for the 512 MiB calibration
+    copy; writes the profile summary that the bench reads back."""
+    res = {}
+    for tag, path in (("fetch", fetch), ("write", write)):
+        rows = _read_counters(path)
+        calib = max((v for nm, v in rows.values() if "mmvq" not in nm), default=0.0)
+        mm = [v for nm, v in rows.values() if "mmvq_kernel" in nm]
+        if not calib or not mm:
+            raise SystemExit(f"{tag}: calibration or mmvq dispatches missing in {path}")
+        factor = CALIB_BYTES / (calib * 1024.0)
+        res[tag] = {"calib_kib": calib, "factor": factor, "mmvq_kib": mm,
+                    "bytes": sum(mm) / len(mm) * 1024.0 * factor}
+    n, k, B = 28672, 4096, 8
+    alg = mmvq_algorithmic_bytes(n, k, B)
+    total = res["fetch"]["bytes"] + res["write"]["bytes"]
+    rec = {"kernel": "mmvq_kernel<Q4_0> 28672x4096 B=8", "source_hash": kernel_source_hash(),
+           "fetch_bytes": round(res["fetch"]["bytes"]), "write_bytes": round(res["write"]["bytes"]),
+           "traffic_bytes": round(total), "algorithmic_bytes": alg, "traffic_over_algorithmic": round(total / alg, 4),
+           "fetch_factor": round(res["fetch"]["factor"], 5), "write_factor": round(res["write"]["factor"], 5)}
+    lines = [
+        "HBM traffic of mmvq_kernel<Q4_0>, stacked gate+up 28672 x 4096, B=8 (rocprofv3 PMC, MI355X)",
+        "",
+        f"FETCH_SIZE pass: {fetch_cmd}",
+        f"WRITE_SIZE pass: {write_cmd}",
+        f"summary: python bench.py --traffic-summarize <fetch dir> <write dir>",
+        "",
+        f"calibration: torch.mul(x, 1.0, out=y) over {CALIB_BYTES >> 20} MiB fp32 (reads and writes {CALIB_BYTES} B)",
+        f"  FETCH_SIZE {res['fetch']['calib_kib']:.0f} KiB -> factor {res['fetch']['factor']:.5f} B per counted B",
+        f"  WRITE_SIZE {res['write']['calib_kib']:.0f} KiB -> factor {res['write']['factor']:.5f}",
+        f"mmvq dispatches FETCH_SIZE KiB: {', '.join(f'{v:.0f}' for v in res['fetch']['mmvq_kib'])}",
+        f"mmvq dispatches WRITE_SIZE KiB: {', '.join(f'{v:.0f}' for v in res['write']['mmvq_kib'])}",
+        f"per launch: fetch {rec['fetch_bytes']} B + write {rec['write_bytes']} B = {rec['traffic_bytes']} B; "
+        f"algorithmic {alg} B; ratio {rec['traffic_over_algorithmic']}",
+        "",
+        "TRAFFIC_JSON " + json.dumps(rec),
+    ]
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def load_traffic(n: int, k: int, B: int):
+    """Measured HBM bytes per launch of the dominant kernel, or None when no measurement
+    exists for this shape or the kernel source has changed since it was taken."""
+    if (n, k, B) != (28672, 4096, 8) or not os.path.exists(TRAFFIC_FILE):
+        return None
+    for line in open(TRAFFIC_FILE):
+        if line.startswith("TRAFFIC_JSON "):
+            rec = json.loads(line[len("TRAFFIC_JSON "):])
+            if rec.get("source_hash") == kernel_source_hash():
+                return rec["traffic_bytes"]
+    return None
 
 
 def main() -> None:
@@ -61,9 +221,18 @@ def main() -> None:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=16, help="layers of one step the oracle is timed on")
     ap.add_argument("--summarize-trace", default=None)
+    ap.add_argument("--traffic-probe", action="store_true", help="launches for the PMC traffic passes only")
+    ap.add_argument("--traffic-summarize", nargs=2, metavar=("FETCH", "WRITE"), default=None)
+    ap.add_argument("--traffic-cmds", nargs=2, metavar=("FETCH_CMD", "WRITE_CMD"), default=("?", "?"))
     args = ap.parse_args()
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
+        return
+    if args.traffic_summarize:
+        traffic_summarize(*args.traffic_summarize, *args.traffic_cmds)
+        return
+    if args.traffic_probe:
+        traffic_probe()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; the step shards by session across GPUs with no "
@@ -86,6 +255,7 @@ def main() -> None:
     wl = W.workload("c4", B=Bmax, steps=max(K, Wu, 1))
     sp = wl.spec
     t0 = time.time()
+    log("packing weights and filling caches")
     gw = GpuWorkload(wl, fill="device")   # seeded N(0,1) fp16 KV drawn on the device (speed)
     setup_s = time.time() - t0
     stream = torch.cuda.current_stream()
@@ -93,16 +263,17 @@ def main() -> None:
     # ---------------------------------------------------------------- whole steps
     sweep = {}
     for B in widths:
+        log(f"whole steps at B={B}")
         rows = list(range(B))
         out = torch.empty((B, sp.out_dim), dtype=torch.float32, device="cuda")
         for s in range(Wu):
-            gw.step(s, rows=rows, out=out)
+            gw.step(s, rows=rows, out=out, stream=stream)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t_host = time.perf_counter()
         e0.record(stream)
         for s in range(K):
-            gw.step(s, rows=rows, out=out)
+            gw.step(s, rows=rows, out=out, stream=stream)
         e1.record(stream)
         torch.cuda.synchronize()
         host_s = time.perf_counter() - t_host
@@ -122,44 +293,32 @@ def main() -> None:
         sweep[B]["step_GBs"] = step_bytes(B, mid) / (sweep[B]["ms_per_step"] / 1e3) / 1e9
 
     # ---------------------------------------------------------------- dominant kernel: mmvq
-    # gate/up shape of the FFN (14336 x 4096 Q4_0) at the headline width: 64 of the step's
-    # launches and 54% of its weight bytes.
+    # the stacked gate+up product of the FFN (28672 x 4096 Q4_0) at the headline width: 32 of
+    # the step's launches and 54% of its weight bytes.  Launches rotate over the 32 layers'
+    # own matrices (2.1 GB, well above the 256 MB Infinity Cache), as inside a step.
     B = Bh
-    lay = gw.model["layers"][0]
-    pw = kd.kd_pack_weight(lay["w_gate"])
+    log(f"dominant kernel: stacked gate+up mmvq at B={B}")
+    mats = [gw.km.packed[il]["w_gateup"] for il in range(L)]
     xin = torch.randn((B, sp.d), device="cuda", generator=torch.Generator(device="cuda").manual_seed(0))
     act = kd.kd_quantize_act_q8(xin)
-    y = torch.empty((B, pw.n_out), dtype=torch.float32, device="cuda")
-    for _ in range(5):
-        kd.kd_mmvq_q4_0(pw, act, B, y)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.kernel_iters):
-        kd.kd_mmvq_q4_0(pw, act, B, y)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    mm_us = e0.elapsed_time(e1) * 1e3 / args.kernel_iters
-    n, k = pw.n_out, pw.k
-    mm_bytes = n * k * 18 // 32 + B * k * (1 + 4 / 32) + B * n * 4
+    y = torch.empty((B, mats[0].n_out), dtype=torch.float32, device="cuda")
+    mm_us = time_rotating(lambda i: kd.kd_mmvq_q4_0(mats[i % L], act, B, y, stream=stream), args.kernel_iters, stream)
+    n, k = mats[0].n_out, mats[0].k
+    mm_bytes = mmvq_algorithmic_bytes(n, k, B)
     mm_gbs = mm_bytes / (mm_us * 1e-6) / 1e9
+    traffic = load_traffic(n, k, B)
 
     # ---------------------------------------------------------------- fa_decode at B = 8
+    log(f"fa_decode at B={B}")
     t_kv = [p + 1 for p in wl.positions(mid)[:B]]
     q = torch.randn((B, sp.n_head, hd), device="cuda", generator=torch.Generator(device="cuda").manual_seed(1))
-    kb = [gw.caches.k_ptr(s, 0) for s in range(B)]
-    vb = [gw.caches.v_ptr(s, 0) for s in range(B)]
+    kbl = [[gw.caches.k_ptr(s, il) for s in range(B)] for il in range(L)]
+    vbl = [[gw.caches.v_ptr(s, il) for s in range(B)] for il in range(L)]
     fa_ws = torch.empty(kd.kd_fa_decode_workspace(B, sp.n_head, hd, t_kv), dtype=torch.uint8, device="cuda")
     fa_out = torch.empty_like(q)
-    for _ in range(5):
-        kd.kd_fa_decode_ragged(q, G, kb, vb, t_kv, wl.capacity, hd ** -0.5, ws=fa_ws, out=fa_out)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.kernel_iters):
-        kd.kd_fa_decode_ragged(q, G, kb, vb, t_kv, wl.capacity, hd ** -0.5, ws=fa_ws, out=fa_out)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    fa_us = e0.elapsed_time(e1) * 1e3 / args.kernel_iters
+    fa_us = time_rotating(lambda i: kd.kd_fa_decode_ragged(q, G, kbl[i % L], vbl[i % L], t_kv, wl.capacity,
+                                                           hd ** -0.5, ws=fa_ws, out=fa_out, stream=stream),
+                          args.kernel_iters, stream)
     fa_bytes = sum(t_kv) * G * hd * 2 * 2 + 2 * B * sp.n_head * hd * 4
     fa_gbs = fa_bytes / (fa_us * 1e-6) / 1e9
 
@@ -180,6 +339,7 @@ def main() -> None:
         sub_model = {"spec": sub_spec, "layers": gw.model["layers"][:nl], "final_norm": gw.model["final_norm"],
                      "lm_head": None}
         sub_wl = dataclasses.replace(wl, spec=sub_spec)
+        log(f"cpu baseline: oracle over {nl} layers")
         oc = oracle.OracleCaches(sub_wl, sessions=list(range(Bh)))
         t0 = time.perf_counter()
         oracle.decode_step(sub_model, oc, W.step_inputs(wl, 0)[:Bh], list(range(Bh)), wl.positions(0)[:Bh])
@@ -209,9 +369,9 @@ def main() -> None:
         "sweep": {str(b): {kk: round(v, 3) for kk, v in sweep[b].items()} for b in widths},
         "step_GBs": round(top["step_GBs"], 1),
         "step_frac_of_peak": round(top["step_GBs"] / HBM_PEAK_GBS, 4),
-        "roofline": {"bound": "hbm", "kernel": "mmvq_kernel<Q4_0> 14336x4096 (gate/up) at B=%d" % Bh,
+        "roofline": {"bound": "hbm", "kernel": "mmvq_kernel<Q4_0> 28672x4096 (stacked gate+up) at B=%d" % Bh,
                      "achieved": round(mm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(mm_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(mm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "avg_launch_us": round(mm_us, 3), "algorithmic_bytes": int(mm_bytes)},
         "fa_roofline": {"bound": "hbm", "kernel": "fa_split_kernel + fa_combine_kernel, B=%d, t_kv=%d" % (B, t_kv[0]),
                         "achieved": round(fa_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

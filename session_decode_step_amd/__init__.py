@@ -305,12 +305,16 @@ class KdModel:
         self.keep: List[torch.Tensor] = []
         self.layers = (KdLayerDesc * sp.n_layers)()
         self.weight_bytes = 0
+        self.packed: List[Dict[str, PackedWeight]] = [dict() for _ in range(sp.n_layers + 1)]
         empty = KdWeight(0, 0, 0, None, None)
+        slot = [0]
 
-        def W(w):
+        def W(w, name=None):
             pw = kd_pack_weight(w, device)
             self.keep += [pw.qs, pw.d]
             self.weight_bytes += pw.nbytes
+            if name:
+                self.packed[slot[0]][name] = pw
             return pw.c()
 
         def F(a):
@@ -319,13 +323,15 @@ class KdModel:
             return t.data_ptr()
 
         for il, L in enumerate(model["layers"]):
+            slot[0] = il
             D = self.layers[il]
             D.attn_norm = F(L["attn_norm"])
-            D.wqkv = W(L["wqkv"])
-            D.wo = W(L["wo"])
+            D.wqkv = W(L["wqkv"], "wqkv")
+            D.wo = W(L["wo"], "wo")
             D.ffn_norm = F(L["ffn_norm"]) if "ffn_norm" in L else None
             if "w_gate" in L:   # gate and up stacked into one [2F, d] matrix: one product streams both
-                D.w_gate, D.w_up, D.w_down = W(stack_rows(L["w_gate"], L["w_up"])), empty, W(L["w_down"])
+                D.w_gate, D.w_up, D.w_down = (W(stack_rows(L["w_gate"], L["w_up"]), "w_gateup"), empty,
+                                              W(L["w_down"], "w_down"))
             else:
                 D.w_gate, D.w_up, D.w_down = empty, empty, empty
             if "router" in L:
@@ -338,7 +344,10 @@ class KdModel:
         self.desc = KdModelDesc(sp.n_layers, sp.d, sp.n_head, sp.n_head_kv, sp.head_dim, sp.ffn, sp.n_experts,
                                 sp.n_expert_used, sp.expert_ffn, sp.shared_ffn, sp.vocab, sp.rope_base, sp.rms_eps,
                                 self.layers, F(model["final_norm"]) if model["final_norm"] is not None else None,
-                                W(model["lm_head"]) if model["lm_head"] is not None else empty)
+                                empty)
+        slot[0] = sp.n_layers   # packed[n_layers] holds the output head
+        if model["lm_head"] is not None:
+            self.desc.lm_head = W(model["lm_head"], "lm_head")
         h = C.c_void_p()
         _check(lib().kd_model_create(C.byref(self.desc), C.byref(h)), "kd_model_create")
         self.handle = h
