@@ -17,6 +17,16 @@
 
 namespace kd {
 
+#ifndef KD_FA_TK
+#define KD_FA_TK 128      // keys per tile when R <= 4
+#endif
+#ifndef KD_FA_AUX
+#define KD_FA_AUX 2       // cache policy of the K/V loads (2: non-temporal)
+#endif
+#ifndef KD_FA_MIN_WAVES
+#define KD_FA_MIN_WAVES 1  // occupancy floor handed to the register allocator (waves per SIMD)
+#endif
+
 constexpr int kFaThreads = 256;
 constexpr int kFaMinChunk = 128;
 constexpr int kFaMaxSplits = 128;
@@ -49,12 +59,12 @@ bool fa_make_plan(FaPlan& p, int B, int H, int G, int hd, const int32_t* t_kv, i
   return true;
 }
 
-// Partials: o [items][H][hd] fp32, then m and l [items][H] fp32.
+// Partials: o [items][H][hd] fp32, then m (base-2 scaled) and l [items][H] fp32.
 size_t fa_workspace_bytes(const FaPlan& p) {
   return (size_t)p.n_items * p.H * (p.hd + 2) * sizeof(float);
 }
 
-__device__ inline void half8_to_float(const uint4 u, float* f) {
+__device__ inline void half8_to_float(const int4 u, float* f) {
   const __half2* h = reinterpret_cast<const __half2*>(&u);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -64,144 +74,196 @@ __device__ inline void half8_to_float(const uint4 u, float* f) {
   }
 }
 
-// grid (n_items, G); 256 threads.  R = query heads per KV head; HD = head dim.
+// 2^x by the hardware instruction (about 1 ulp; results below 2^-126 flush to zero, which
+// only drops probabilities that cannot change an fp32 sum holding a term of 1).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each aligned group of N = 8 or 16 lanes; every lane of the group ends with the
+// same bits (each step adds two equal partial sums, in one order or the other).
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);  // row_half_mirror: lane i of 8 takes lane 7-i
+  if (N == 16) v += dpp_f<0x140>(v);  // row_mirror: lane i of 16 takes lane 15-i
+  return v;
+}
+
+// Lane geometry of one workgroup (4 waves) over a tile of keys: a key's HD fp16 values are
+// read by LPK lanes, 16 bytes (8 dims) each, so one wave load covers KPW whole keys and the
+// workgroup SLOTS keys; a tile of TK keys is NL loads per lane for K and NL for V, all
+// issued before the first score is computed.
 template <int R, int HD>
-__global__ __launch_bounds__(kFaThreads) void fa_split_kernel(FaPlan p, const float* __restrict__ q, int ldq,
+struct FaShape {
+  static constexpr int LPK = HD / 8;
+  static constexpr int KPW = 64 / LPK;
+  static constexpr int SLOTS = 4 * KPW;
+  static constexpr int TK = R <= 4 ? KD_FA_TK : KD_FA_TK / 2;
+  static constexpr int NL = TK / SLOTS;
+};
+
+// grid (n_items, G); 256 threads.  One workgroup per (row b, split s, KV head g): it reads
+// keys [s*c_b, min((s+1)*c_b, t_b)) of head g once for the R query heads of the group, tile
+// by tile with a running max (the tile order and every reduction tree are fixed by c_b and
+// t_b), and writes the split's partials (m, l, o) for those R heads.
+template <int R, int HD>
+__global__ __launch_bounds__(kFaThreads, KD_FA_MIN_WAVES) void fa_split_kernel(FaPlan p, const float* __restrict__ q, int ldq,
                                                               RowCaches rc, int capacity, float scale,
                                                               float* __restrict__ ws) {
-  constexpr int DPL = HD / 8;   // dims per lane in the score phase (8 lanes per key)
-  constexpr int DV = HD / 16;   // dims per lane in the PV phase (16 lanes per key row)
-  extern __shared__ float smem[];
+  using S = FaShape<R, HD>;
+  constexpr int LPK = S::LPK, SLOTS = S::SLOTS, TK = S::TK, NL = S::NL;
+  constexpr int NOUT = R * HD;  // outputs of one (row, KV head)
   const int item = blockIdx.x, g = blockIdx.y;
-  // row of this item
   int b = 0;
 #pragma unroll
   for (int i = 1; i < KD_MAX_B; ++i)
     if (item >= p.split_off[i]) b = i;
-  const int s = item - p.split_off[b];
+  const int s0 = p.split_off[b];
   const int c = p.chunk[b];
-  const int k0 = s * c;
+  const int k0 = (item - s0) * c;
   const int k1 = min(k0 + c, p.t_kv[b]);
   const int nk = k1 - k0;
   const int H = p.H;
-  float* sc = smem;                      // [R][c] scores, then probabilities
-  float* red = smem + R * c;             // [4][R][HD]
-  __shared__ float ml[R][2];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // scores are carried in base 2: s2 = (q . k) * scale * log2(e), so e^(s - m) = 2^(s2 - m2)
+  const float scale2 = scale * 1.44269504088896341f;
+  const int dl = lane % LPK;                     // this lane's dims [8 dl, 8 dl + 8)
+  const int slot = w * S::KPW + lane / LPK;      // this lane's key slot
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  __shared__ float tmax[2][4][R];
+  __shared__ float red_l[4][R];
+  __shared__ float red_o[4][R][HD];
+
+  float qv[R][8];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float4* qr = reinterpret_cast<const float4*>(q + (size_t)b * ldq + (size_t)(g * R + r) * HD + dl * 8);
+    const float4 a = qr[0], e = qr[1];
+    qv[r][0] = a.x; qv[r][1] = a.y; qv[r][2] = a.z; qv[r][3] = a.w;
+    qv[r][4] = e.x; qv[r][5] = e.y; qv[r][6] = e.z; qv[r][7] = e.w;
+  }
+  // descriptors over keys [0, k1) of head g: loads past the chunk read zeros
   const __half* Kg = static_cast<const __half*>(rc.k[b]) + (size_t)g * capacity * HD;
   const __half* Vg = static_cast<const __half*>(rc.v[b]) + (size_t)g * capacity * HD;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg, (uint32_t)k1 * HD * 2);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg, (uint32_t)k1 * HD * 2);
 
-  // ---- phase 1: scores.  32 groups of 8 lanes; a group owns one key at a time.
-  {
-    const int grp = tid >> 3, sub = tid & 7;
-    float qv[R][DPL];
+  float m_run[R], l_acc[R], o_acc[R][8];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float* qr = q + (size_t)b * ldq + (size_t)(g * R + r) * HD + sub * DPL;
+  for (int r = 0; r < R; ++r) {
+    m_run[r] = -INFINITY;
+    l_acc[r] = 0.0f;
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) qv[r][i] = qr[i];
+    for (int e = 0; e < 8; ++e) o_acc[r][e] = 0.0f;
+  }
+
+  for (int t0 = 0, par = 0; t0 < nk; t0 += TK, par ^= 1) {
+    const int nt = min(TK, nk - t0);
+    int4 kr[NL], vr[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int j = i * SLOTS + slot;
+      const uint32_t off = j < nt ? ((uint32_t)(k0 + t0 + j) * HD + dl * 8) * 2 : kOOB;
+      kr[i] = buf16<KD_FA_AUX>(rk, off);
     }
-    for (int j = grp; j < nk; j += 32) {
-      const __half* kp = Kg + (size_t)(k0 + j) * HD + sub * DPL;
-      float kf[DPL];
 #pragma unroll
-      for (int i = 0; i < DPL; i += 8) half8_to_float(*reinterpret_cast<const uint4*>(kp + i), kf + i);
+    for (int i = 0; i < NL; ++i) {
+      const int j = i * SLOTS + slot;
+      const uint32_t off = j < nt ? ((uint32_t)(k0 + t0 + j) * HD + dl * 8) * 2 : kOOB;
+      vr[i] = buf16<KD_FA_AUX>(rv, off);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep every K and V load of the tile ahead of the math
+    // scores of this lane's NL keys for the R heads (identical in the LPK lanes of a key)
+    float sc[R][NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      float kf[8];
+      half8_to_float(kr[i], kf);
+      const bool live = i * SLOTS + slot < nt;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         float part = 0.0f;
 #pragma unroll
-        for (int i = 0; i < DPL; ++i) part = fmaf(qv[r][i], kf[i], part);
-        part += __shfl_xor(part, 1, 64);
-        part += __shfl_xor(part, 2, 64);
-        part += __shfl_xor(part, 4, 64);
-        if (sub == 0) sc[r * c + j] = part * scale;
+        for (int e = 0; e < 8; ++e) part = fmaf(qv[r][e], kf[e], part);
+        part = group_sum<LPK>(part);
+        sc[r][i] = live ? part * scale2 : -INFINITY;
       }
     }
-  }
-  __syncthreads();
-
-  // ---- phase 2: per-head max and exp-sum over the chunk (wave r % 4 owns head r).
-  for (int r = w; r < R; r += 4) {
-    float m = -INFINITY;
-    for (int j = lane; j < nk; j += 64) m = fmaxf(m, sc[r * c + j]);
-    m = wave_max(m);
-    float l = 0.0f;
-    for (int j = lane; j < nk; j += 64) {
-      const float e = expf(sc[r * c + j] - m);
-      sc[r * c + j] = e;
-      l += e;
+    // tile max per head: lane keys, then the key groups of the wave, then the 4 waves
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float mx = sc[r][0];
+#pragma unroll
+      for (int i = 1; i < NL; ++i) mx = fmaxf(mx, sc[r][i]);
+#pragma unroll
+      for (int m = LPK; m < 64; m <<= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+      if (lane == 0) tmax[par][w][r] = mx;
     }
-    l = wave_sum(l);
-    if (lane == 0) {
-      ml[r][0] = m;
-      ml[r][1] = l;
+    __syncthreads();
+    float alpha[R], mnew[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float M = fmaxf(fmaxf(tmax[par][0][r], tmax[par][1][r]), fmaxf(tmax[par][2][r], tmax[par][3][r]));
+      mnew[r] = fmaxf(m_run[r], M);
+      alpha[r] = fast_exp2(m_run[r] - mnew[r]);  // 0 on the first tile
+      m_run[r] = mnew[r];
+      l_acc[r] *= alpha[r];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o_acc[r][e] *= alpha[r];
     }
-  }
-  __syncthreads();
-
-  // ---- phase 3: o[r][:] = sum_j p[r][j] V[j][:].  16 key slots (4 per wave), 16 lanes per row.
-  {
-    const int kg = lane >> 4, dl = lane & 15;
-    const int slot = w * 4 + kg;
-    float o[R][DV];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int i = 0; i < DV; ++i) o[r][i] = 0.0f;
-    for (int j = slot; j < nk; j += 16) {
-      const __half* vp = Vg + (size_t)(k0 + j) * HD + dl * DV;
-      float vf[DV];
-      if (DV == 8) {
-        half8_to_float(*reinterpret_cast<const uint4*>(vp), vf);
-      } else {
-        const uint2 u = *reinterpret_cast<const uint2*>(vp);
-        const __half2* h2 = reinterpret_cast<const __half2*>(&u);
-#pragma unroll
-        for (int i = 0; i < DV / 2; ++i) {
-          const float2 t = __half22float2(h2[i]);
-          vf[2 * i] = t.x;
-          vf[2 * i + 1] = t.y;
-        }
-      }
+    for (int i = 0; i < NL; ++i) {
+      float vf[8];
+      half8_to_float(vr[i], vf);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const float pj = sc[r * c + j];
+        const float pj = fast_exp2(sc[r][i] - mnew[r]);
+        l_acc[r] += pj;
 #pragma unroll
-        for (int i = 0; i < DV; ++i) o[r][i] = fmaf(pj, vf[i], o[r][i]);
+        for (int e = 0; e < 8; ++e) o_acc[r][e] = fmaf(pj, vf[e], o_acc[r][e]);
       }
     }
+  }
+
+  // key groups of the wave (butterfly), then the 4 waves through LDS in wave order
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+  for (int r = 0; r < R; ++r) {
 #pragma unroll
-      for (int i = 0; i < DV; ++i) {
-        float v = o[r][i];
-        v += __shfl_xor(v, 16, 64);
-        v += __shfl_xor(v, 32, 64);
-        o[r][i] = v;
-      }
-    if (kg == 0) {
+    for (int m = LPK; m < 64; m <<= 1) {
+      l_acc[r] += __shfl_xor(l_acc[r], m, 64);
 #pragma unroll
-      for (int r = 0; r < R; ++r)
+      for (int e = 0; e < 8; ++e) o_acc[r][e] += __shfl_xor(o_acc[r][e], m, 64);
+    }
+  }
+  if (lane < LPK) {
 #pragma unroll
-        for (int i = 0; i < DV; ++i) red[(w * R + r) * HD + dl * DV + i] = o[r][i];
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red_o[w][r][dl * 8 + e] = o_acc[r][e];
+      if (dl == 0) red_l[w][r] = l_acc[r];
     }
   }
   __syncthreads();
-  float* po = ws;                                    // [items][H][HD]
-  float* pm = ws + (size_t)p.n_items * H * HD;       // [items][H]
-  float* pl = pm + (size_t)p.n_items * H;            // [items][H]
-  for (int t = tid; t < R * HD; t += kFaThreads) {
-    const int r = t / HD, d = t % HD;
-    const float v = ((red[(0 * R + r) * HD + d] + red[(1 * R + r) * HD + d]) + red[(2 * R + r) * HD + d]) +
-                    red[(3 * R + r) * HD + d];
-    po[((size_t)item * H + g * R + r) * HD + d] = v;
+
+  float* po = ws;                                  // [items][H][HD]
+  float* pm = ws + (size_t)p.n_items * H * HD;     // [items][H]
+  float* pl = pm + (size_t)p.n_items * H;          // [items][H]
+  for (int idx = tid; idx < NOUT; idx += kFaThreads) {
+    const int r = idx / HD, d = idx % HD;
+    po[((size_t)item * H + g * R) * HD + idx] =
+        ((red_o[0][r][d] + red_o[1][r][d]) + red_o[2][r][d]) + red_o[3][r][d];
   }
-  if (tid < R) {
-    pm[(size_t)item * H + g * R + tid] = ml[tid][0];
-    pl[(size_t)item * H + g * R + tid] = ml[tid][1];
-  }
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    if (tid == r) {
+      pm[(size_t)item * H + g * R + r] = m_run[r];
+      pl[(size_t)item * H + g * R + r] = ((red_l[0][r] + red_l[1][r]) + red_l[2][r]) + red_l[3][r];
+    }
 }
 
 // grid (H, B); HD threads.  Merge the row's chunks in chunk order; optionally quantise.
@@ -233,7 +295,7 @@ __global__ __launch_bounds__(HD) void fa_combine_kernel(FaPlan p, const float* _
     __syncthreads();
     for (int s = d; s < n; s += HD) {
       const size_t it = (size_t)(s0 + base + s) * H + h;
-      const float w = expf(pm[it] - M);
+      const float w = fast_exp2(pm[it] - M);
       wm[s] = w;
       wl[s] = w * pl[it];
     }
@@ -281,11 +343,8 @@ __global__ __launch_bounds__(HD) void fa_combine_kernel(FaPlan p, const float* _
 template <int R, int HD>
 static void launch_fa_t(const FaPlan& p, const float* q, int ldq, const RowCaches& rc, int capacity, float scale,
                         float* out, int8_t* oq, float* od, void* ws, hipStream_t st) {
-  int cmax = 1;
-  for (int b = 0; b < p.B; ++b) cmax = p.chunk[b] > cmax ? p.chunk[b] : cmax;
-  const size_t shm = (size_t)(R * cmax + 4 * R * HD) * sizeof(float);
-  fa_split_kernel<R, HD><<<dim3(p.n_items, p.G), kFaThreads, shm, st>>>(p, q, ldq, rc, capacity, scale,
-                                                                         static_cast<float*>(ws));
+  fa_split_kernel<R, HD><<<dim3(p.n_items, p.G), kFaThreads, 0, st>>>(p, q, ldq, rc, capacity, scale,
+                                                                      static_cast<float*>(ws));
   fa_combine_kernel<HD><<<dim3(p.H, p.B), HD, 0, st>>>(p, static_cast<const float*>(ws), out, oq, od);
 }
 

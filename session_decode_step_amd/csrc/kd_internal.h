@@ -107,6 +107,31 @@ __device__ inline float wave_max(float v) {
   return v;
 }
 
+// ---- buffer loads ----------------------------------------------------------------------
+// Raw (stride 0) buffer descriptors: an offset at or past num_records reads as zero without
+// touching memory, which masks out-of-range lanes without a branch.
+typedef int v4i __attribute__((ext_vector_type(4)));
+constexpr uint32_t kOOB = 0x80000000u;  // an offset past every buffer the kernels read
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+// AUX = 2: non-temporal (data streamed once) on gfx950.
+template <int AUX>
+__device__ __forceinline__ int4 buf16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
+  return make_int4(v.x, v.y, v.z, v.w);
+}
+template <int AUX>
+__device__ __forceinline__ uint2 buf8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef int v2i __attribute__((ext_vector_type(2)));
+  const v2i v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX);
+  return make_uint2((uint32_t)v.x, (uint32_t)v.y);
+}
+__device__ __forceinline__ float buf4f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
 // ---- launchers used by the step driver (arguments already validated) -------------------
 int norm_max_len();
 void launch_act_quant(const float* x, int B, int k, int ldx, int8_t* qs, float* d, hipStream_t st);

@@ -22,8 +22,6 @@
 
 namespace kd {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
-
 #ifndef KD_MMVQ_NT
 #define KD_MMVQ_NT 1
 #endif
@@ -35,6 +33,9 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 #endif
 #ifndef KD_MMVQ_WAVE_QUADS
 #define KD_MMVQ_WAVE_QUADS 4
+#endif
+#ifndef KD_MMVQ_RG
+#define KD_MMVQ_RG 1  // row groups per workgroup (they share the activation operands)
 #endif
 
 
@@ -123,26 +124,6 @@ struct MmvqArgs {
   int32_t* debug_S;  // [B][n_out][kblocks] when non-null (epilogue replaced)
 };
 
-typedef unsigned int v2u __attribute__((ext_vector_type(2)));
-// Streaming (non-temporal) loads for weights: read once per step, kept out of the way of
-// the activations that every workgroup re-reads.
-__device__ __forceinline__ int4 ld_nt16(const void* p) {
-#if KD_MMVQ_NT
-  const v4i v = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p));
-  return make_int4(v.x, v.y, v.z, v.w);
-#else
-  return *reinterpret_cast<const int4*>(p);
-#endif
-}
-__device__ __forceinline__ uint2 ld_nt8(const void* p) {
-#if KD_MMVQ_NT
-  const v2u v = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(p));
-  return make_uint2(v.x, v.y);
-#else
-  return *reinterpret_cast<const uint2*>(p);
-#endif
-}
-
 __device__ __forceinline__ float f4_get(const float4& v, int j) {
   return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
 }
@@ -179,63 +160,43 @@ __device__ __forceinline__ float half_bits(uint32_t hw, int hi) {
   return __half2float(__ushort_as_half((unsigned short)(hi ? (hw >> 16) : (hw & 0xFFFF))));
 }
 
-// Buffer resources: raw (stride 0) descriptors whose offsets past num_records read as zero
-// without touching memory -- used to mask the activation rows that hold no live row.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
-// AUX = 2: non-temporal (streamed once) on gfx950.
-template <int AUX>
-__device__ __forceinline__ int4 buf16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
-  return make_int4(v.x, v.y, v.z, v.w);
-}
-template <int AUX>
-__device__ __forceinline__ uint2 buf8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  typedef int v2i __attribute__((ext_vector_type(2)));
-  const v2i v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX);
-  return make_uint2((uint32_t)v.x, (uint32_t)v.y);
-}
 constexpr int kWeightAux = KD_MMVQ_NT ? 2 : 0;
-__device__ __forceinline__ float buf4f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
-}
-constexpr uint32_t kOOB = 0x80000000u;  // an offset past every buffer this kernel reads
 
-// One quad of a wave's stream: the weight tile (16 B per lane, two for Q8_0), its scales and
-// the lane's activation operand (2 x 16 B).
+// One weight tile of a wave's stream: 16 bytes per lane (two for Q8_0) and its 4 scales.
 template <int FMT>
-struct QStage {
-  int4 w0, w1, a0, a1;
+struct WStage {
+  int4 w0, w1;
   uint2 dw;
 };
 
-// Issue the loads of quad q (offsets past the wave's range read zeros with no traffic).
+// Issue the loads of one tile (an invalid tile reads zeros with no traffic).
 template <int FMT>
-__device__ __forceinline__ void qstage_load(QStage<FMT>& st, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rd,
-                                            __amdgpu_buffer_rsrc_t rx, uint32_t w_off, uint32_t d_off, uint32_t a_off,
-                                            int q, bool valid) {
+__device__ __forceinline__ void wstage_load(WStage<FMT>& st, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rd,
+                                            uint32_t tile, bool valid, int lane, int n) {
   constexpr int TILE = FMT == KD_FMT_Q8_0 ? kTileQ8 : kTileQ4;
-  const uint32_t wo = valid ? w_off + (uint32_t)q * TILE : kOOB;
+  const uint32_t wo = valid ? tile * TILE + lane * 16 : kOOB;
   st.w0 = buf16<kWeightAux>(rw, wo);
   st.w1 = (FMT == KD_FMT_Q8_0) ? buf16<kWeightAux>(rw, valid ? wo + 1024 : kOOB) : st.w0;
-  st.dw = buf8<kWeightAux>(rd, valid ? d_off + (uint32_t)q * 128 : kOOB);
-  const uint32_t ao = (valid && a_off != kOOB) ? a_off + (uint32_t)q * 128 : kOOB;
-  st.a0 = buf16<0>(rx, ao);
-  st.a1 = buf16<0>(rx, ao == kOOB ? kOOB : ao + 16);
+  st.dw = buf8<kWeightAux>(rd, valid ? tile * 128 + n * 8 : kOOB);
 }
 
-// grid (NR, n_groups); block = nw waves.  Wave w streams quads [q0, q1) = [w*QW, min(NQ,
-// w*QW + QW)) of the row group (a partition that depends on NQ only) through a depth-D
-// register ring: quad q is computed while quads q+1 .. q+D-1 are in flight.  Loads are
-// branch-free (out-of-range quads read zeros and add exactly zero).  The wave stages its
-// own activation scales in its own LDS slice; the waves' partial sums are added in wave
-// order through LDS.
-// Dynamic LDS: per-wave activation scales [nw][16][QW][4] floats, then [nw][4][64] floats.
+// grid (ceil(NR / RG), n_groups); block = nw waves.  A workgroup owns RG consecutive row
+// groups.  Wave w owns quads [q0, q1) = [w*QW, min(NQ, w*QW + QW)) of every one of them (a
+// partition that depends on NQ only).  It streams its QW x RG weight tiles quad by quad
+// (the RG tiles of one quad share that quad's activation operands, loaded once, one quad
+// ahead) through a depth-D register ring, so tile t is computed while tiles t+1 .. t+D-1
+// are in flight.  Loads are branch-free (out-of-range tiles read zeros and add exactly
+// zero).  The wave stages its own activation scales in its own LDS slice; the waves'
+// partial sums are added in wave order through LDS.  Per output, the fp32 sequence is: the
+// blocks of the wave's quads in ascending order, then the waves in ascending order -- a
+// function of k alone.
+// Dynamic LDS: per-wave activation scales [nw][16][QW][4] floats, then [nw][RG][4][64].
 template <int FMT, int QW, int NS, bool DEBUG>
 __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
+  constexpr int RG = KD_MMVQ_RG;
+  constexpr int NT = RG * QW;
   constexpr int D0 = FMT == KD_FMT_Q8_0 ? KD_MMVQ_DEPTH_Q8 : KD_MMVQ_DEPTH_Q4;
-  constexpr int D = D0 < QW ? D0 : QW;
+  constexpr int D = D0 < NT ? D0 : NT;
   const int e = blockIdx.y;
   int nrows = a.B;
   const int32_t* act_row = nullptr;
@@ -246,7 +207,6 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
     act_row = a.act_row + e * 16;
     out_row = a.out_row + e * 16;
   }
-  constexpr int TILE = FMT == KD_FMT_Q8_0 ? kTileQ8 : kTileQ4;
   extern __shared__ float smem[];
   const int nw = blockDim.x >> 6;
   const int w = threadIdx.x >> 6;
@@ -255,86 +215,121 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
   const int NQ = a.NQ;
   const int q0 = w * QW;
   const int q1 = min(NQ, q0 + QW);
-  const int rg = blockIdx.x;
+  const int rg0 = blockIdx.x * RG;
 
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.wq, a.w_bytes);
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.wd, a.d_bytes);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.xq, a.x_bytes);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.xd, a.xd_bytes);
-  const uint32_t tile0 = (uint32_t)((size_t)e * (size_t)a.w_group_tiles + (size_t)rg * NQ);
-  const uint32_t w_off = tile0 * TILE + lane * 16;
-  const uint32_t d_off = tile0 * 128 + n * 8;
-  // A operand row of lane n (rows past the live rows read zeros)
+  const uint32_t gtile = (uint32_t)((size_t)e * (size_t)a.w_group_tiles);
+  // A operand of lane n: activation row n (rows past the live rows read zeros)
   const uint32_t a_off = (n < nrows) ? (uint32_t)(act_row ? act_row[n] : n) * (uint32_t)NQ * 128u + g * 32 : kOOB;
 
-  // ---- this wave's activation scales: rows 0..15 x quads [q0, q0 + QW), float4 per
-  // (row, quad); lane l stages (row l/4, quads (l%4) + 4i).
+  // ---- this wave's activation scales: rows 0..15 x quads [q0, q0 + QW), float4 per (row,
+  // quad); lane l fetches (row l/4, quads (l%4) + 4i).  Loaded first (L2 hits), stored to
+  // this wave's LDS slice after the weight loads are issued, so no wait holds the stream.
+  constexpr int NDX = (QW + 3) / 4;
   float* dxw = smem + w * (16 * QW * 4);  // this wave's [16][QW][4]
+  int4 dxv[NDX];
   if (!DEBUG) {
     const int r = lane >> 2, p = lane & 3;
     const uint32_t row_base = (r < nrows) ? (uint32_t)(act_row ? act_row[r] : r) * (uint32_t)NQ * 16u : kOOB;
 #pragma unroll
-    for (int qq = p; qq < QW; qq += 4) {
-      const int q = q0 + qq;
-      const uint32_t off = (q < q1 && row_base != kOOB) ? row_base + (uint32_t)q * 16u : kOOB;
-      const int4 v = buf16<0>(rs, off);
-      *reinterpret_cast<int4*>(dxw + (r * QW + qq) * 4) = v;
+    for (int i = 0; i < NDX; ++i) {
+      const int q = q0 + 4 * i + p;
+      const uint32_t off = (4 * i + p < QW && q < q1 && row_base != kOOB) ? row_base + (uint32_t)q * 16u : kOOB;
+      dxv[i] = buf16<0>(rs, off);
     }
   }
 
-  // ---- prologue: D quads in flight
-  QStage<FMT> st[D];
+  // ---- prologue: D weight tiles in flight, then the first two quads' activation operands
+  WStage<FMT> st[D];
 #pragma unroll
-  for (int i = 0; i < D; ++i) qstage_load<FMT>(st[i], rw, rd, rx, w_off, d_off, a_off, q0 + i, q0 + i < q1);
+  for (int i = 0; i < D; ++i) {
+    const int j = i / RG, r = i % RG;
+    wstage_load<FMT>(st[i], rw, rd, gtile + (uint32_t)(rg0 + r) * NQ + q0 + j, q0 + j < q1 && rg0 + r < a.NR, lane,
+                     n);
+  }
+  int4 ax0[2], ax1[2];
+#pragma unroll
+  for (int j = 0; j < 2 && j < QW; ++j) {
+    const uint32_t ao = (q0 + j < q1 && a_off != kOOB) ? a_off + (uint32_t)(q0 + j) * 128u : kOOB;
+    ax0[j] = buf16<0>(rx, ao);
+    ax1[j] = buf16<0>(rx, ao == kOOB ? kOOB : ao + 16);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // every prologue load is issued before anything waits
+  if (!DEBUG) {
+    const int r = lane >> 2, p = lane & 3;
+#pragma unroll
+    for (int i = 0; i < NDX; ++i)
+      if (4 * i + p < QW) *reinterpret_cast<int4*>(dxw + (r * QW + 4 * i + p) * 4) = dxv[i];
+  }
 
-  // ---- the stream, fully unrolled (no loop back-edge, so every wait is exact): quad
-  // q0 + j is computed from stage j % D, which is then refilled with quad q0 + j + D.
-  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  // ---- the stream, fully unrolled (no loop back-edge, so every wait is exact): tile t =
+  // (quad j = t / RG, row group r = t % RG) is computed from stage t % D, which is then
+  // refilled with tile t + D.
+  float acc[RG][4];
 #pragma unroll
-  for (int j = 0; j < QW; ++j) {
-    QStage<FMT>& cur = st[j % D];
+  for (int r = 0; r < RG; ++r)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc[r][s] = 0.0f;
+  float4 dx[4];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int j = t / RG, r = t % RG;
+    WStage<FMT>& cur = st[t % D];
     const int q = q0 + j;
     const bool live = q < q1;
     const float zsc = live ? 1.0f : 0.0f;
-    float4 dx[4];
-    if (!DEBUG) {
+    if (!DEBUG && r == 0) {
 #pragma unroll
       for (int s = 0; s < NS; ++s) dx[s] = *reinterpret_cast<const float4*>(dxw + ((4 * g + s) * QW + j) * 4);
     }
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb) {
-      const v4i S = block_dots<FMT>(act_op(cur.a0, cur.a1, jb), w_op<FMT>(cur.w0, cur.w1, jb));
+      const v4i S = block_dots<FMT>(act_op(ax0[j & 1], ax1[j & 1], jb), w_op<FMT>(cur.w0, cur.w1, jb));
       if (DEBUG) {
         const int blk = 4 * q + jb;
-        const int row = rg * 16 + n;
+        const int row = (rg0 + r) * 16 + n;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const int r = 4 * g + s;
-          if (live && r < nrows && row < a.n_out && blk < a.kblocks)
-            a.debug_S[((size_t)r * a.n_out + row) * a.kblocks + blk] = S[s];
+          const int b = 4 * g + s;
+          if (live && b < nrows && row < a.n_out && blk < a.kblocks)
+            a.debug_S[((size_t)b * a.n_out + row) * a.kblocks + blk] = S[s];
         }
       } else {
         const float dwj = zsc * half_bits(jb < 2 ? cur.dw.x : cur.dw.y, jb & 1);
 #pragma unroll
-        for (int s = 0; s < NS; ++s) acc[s] = fmaf(dwj * f4_get(dx[s], jb), (float)S[s], acc[s]);
+        for (int s = 0; s < NS; ++s) acc[r][s] = fmaf(dwj * f4_get(dx[s], jb), (float)S[s], acc[r][s]);
       }
     }
-    if (j + D < QW) qstage_load<FMT>(cur, rw, rd, rx, w_off, d_off, a_off, q + D, q + D < q1);
+    if (r == RG - 1 && j + 2 < QW) {  // this quad's operand slot now takes quad j + 2
+      const uint32_t ao = (q0 + j + 2 < q1 && a_off != kOOB) ? a_off + (uint32_t)(q0 + j + 2) * 128u : kOOB;
+      ax0[j & 1] = buf16<0>(rx, ao);
+      ax1[j & 1] = buf16<0>(rx, ao == kOOB ? kOOB : ao + 16);
+    }
+    if (t + D < NT) {
+      const int j2 = (t + D) / RG, r2 = (t + D) % RG;
+      wstage_load<FMT>(cur, rw, rd, gtile + (uint32_t)(rg0 + r2) * NQ + q0 + j2, q0 + j2 < q1 && rg0 + r2 < a.NR,
+                       lane, n);
+    }
   }
   if (DEBUG) return;
 
-  float* red = smem + nw * (16 * QW * 4);  // [nw][4][64]
+  float* red = smem + nw * (16 * QW * 4);  // [nw][RG][4][64]
 #pragma unroll
-  for (int s = 0; s < 4; ++s) red[(w * 4 + s) * 64 + lane] = acc[s];
+  for (int r = 0; r < RG; ++r)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) red[((w * RG + r) * 4 + s) * 64 + lane] = acc[r][s];
   __syncthreads();
-  for (int t = threadIdx.x; t < 256; t += blockDim.x) {
-    const int s = t >> 6, l = t & 63;
-    float v = red[s * 64 + l];
-    for (int ww = 1; ww < nw; ++ww) v += red[(ww * 4 + s) * 64 + l];  // fixed wave order
-    const int r = 4 * (l >> 4) + s;
-    const int row = rg * 16 + (l & 15);
-    if (r < nrows && row < a.n_out) {
-      const int orow = out_row ? out_row[r] : r;
+  for (int t = threadIdx.x; t < RG * 256; t += blockDim.x) {
+    const int r = t >> 8, s = (t >> 6) & 3, l = t & 63;
+    float v = red[(r * 4 + s) * 64 + l];
+    for (int ww = 1; ww < nw; ++ww) v += red[((ww * RG + r) * 4 + s) * 64 + l];  // fixed wave order
+    const int b = 4 * (l >> 4) + s;
+    const int row = (rg0 + r) * 16 + (l & 15);
+    if (b < nrows && row < a.n_out) {
+      const int orow = out_row ? out_row[b] : b;
       a.y[(size_t)orow * a.ldy + row] = v;
     }
   }
@@ -354,12 +349,13 @@ static int mmvq_qw(int NQ) {
 template <int FMT, int QW, int NS>
 static void launch_mmvq_qn(const MmvqArgs& a, int n_groups, hipStream_t st) {
   const int nw = ceil_div(a.NQ, QW);
-  dim3 grid(a.NR, n_groups);
+  dim3 grid(ceil_div(a.NR, KD_MMVQ_RG), n_groups);
   const size_t dx_shm = (size_t)nw * 16 * QW * 4 * sizeof(float);
   if (a.debug_S) {
     mmvq_kernel<FMT, QW, 4, true><<<grid, 64 * nw, dx_shm, st>>>(a);
   } else {
-    mmvq_kernel<FMT, QW, NS, false><<<grid, 64 * nw, dx_shm + (size_t)nw * 256 * sizeof(float), st>>>(a);
+    mmvq_kernel<FMT, QW, NS, false>
+        <<<grid, 64 * nw, dx_shm + (size_t)nw * KD_MMVQ_RG * 256 * sizeof(float), st>>>(a);
   }
 }
 

@@ -45,21 +45,39 @@ class GpuWorkload:
         self.ws = torch.empty(self.km.workspace_bytes(wl.B, wl.positions(last)) + 4096, dtype=torch.uint8,
                               device=device)
         self.out = torch.empty((wl.B, sp.out_dim), dtype=torch.float32, device=device)
-        self._x_cache: Dict[int, torch.Tensor] = {}
+        self._x_cache: Dict = {}
 
     def inputs(self, step: int) -> torch.Tensor:
+        """Device input rows of one step (uploaded on first use: call ``prefetch`` before a
+        timed loop, so that no host-to-device copy stalls the stream inside it)."""
         if step not in self._x_cache:
             self._x_cache[step] = torch.from_numpy(W.step_inputs(self.wl, step)).to(self.device)
         return self._x_cache[step]
+
+    def prefetch(self, steps: Sequence[int], rows: Optional[Sequence[int]] = None) -> None:
+        """Upload the inputs of these steps (and gather the row subset) ahead of time."""
+        for s in steps:
+            self._rows_input(s, rows)
+        torch.cuda.synchronize()
+
+    def _rows_input(self, s: int, rows: Optional[Sequence[int]]) -> torch.Tensor:
+        x = self.inputs(s)
+        if rows is None or list(rows) == list(range(self.wl.B)):
+            return x
+        rows = list(rows)
+        if rows == list(range(rows[0], rows[0] + len(rows))):
+            return x[rows[0]:rows[0] + len(rows)]           # a contiguous view: no copy
+        key = (s, tuple(rows))
+        if key not in self._x_cache:
+            self._x_cache[key] = x[rows].contiguous()
+        return self._x_cache[key]
 
     def step(self, s: int, rows: Optional[Sequence[int]] = None, out: Optional[torch.Tensor] = None,
              stream=None) -> torch.Tensor:
         """Run decode step ``s`` for the given row indices (default: all rows)."""
         wl = self.wl
         rows = list(range(wl.B)) if rows is None else list(rows)
-        x = self.inputs(s)
-        if len(rows) != wl.B:
-            x = x[rows].contiguous()
+        x = self._rows_input(s, rows)
         pos_all = wl.positions(s)
         pos = [pos_all[b] for b in rows]
         sess = [wl.rows[b][0] for b in rows]

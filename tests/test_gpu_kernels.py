@@ -168,7 +168,7 @@ def test_kv_append_bytes_exact():
         assert not K[:, mask].any() and not V[:, mask].any()
 
 
-@pytest.mark.parametrize("H,G,hd", [(32, 8, 128), (16, 4, 128), (4, 2, 64), (16, 8, 128), (8, 8, 64)])
+@pytest.mark.parametrize("H,G,hd", [(32, 8, 128), (16, 4, 128), (4, 2, 64), (16, 8, 128), (8, 8, 64), (8, 1, 128), (16, 2, 64)])
 def test_fa_decode_ragged_vs_oracle(H, G, hd):
     say(f"fa H={H} G={G} hd={hd}")
     r = np.random.default_rng(H * 100 + G)
