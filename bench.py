@@ -74,8 +74,11 @@ def log(msg: str) -> None:
 
 
 def mmvq_algorithmic_bytes(n: int, k: int, B: int) -> int:
-    """Q4_0 weights once (18 B per 32), B int8 activation rows with fp32 block scales, fp32 out."""
-    return n * k * 18 // 32 + B * k + B * (k // 32) * 4 + B * n * 4
+    """The interleaved gate/up product with its SwiGLU epilogue: Q4_0 weights once (18 B per
+    32), B int8 activation rows of k with fp32 block scales in, B quantised rows of F = n/2
+    (int8 codes + fp32 block scales) out."""
+    F = n // 2
+    return n * k * 18 // 32 + B * k + B * (k // 32) * 4 + B * F + B * (F // 32) * 4
 
 
 def time_rotating(launch, iters: int, stream) -> float:
@@ -111,8 +114,8 @@ def kernel_source_hash() -> str:
 
 def traffic_probe() -> None:
     """Launches for the two ``rocprofv3 --pmc`` passes: a plain fp32 elementwise copy of
-    512 MiB (the calibration kernel: reads and writes 512 MiB), then the stacked gate+up
-    mmvq at B=8 on four distinct matrices."""
+    512 MiB (the calibration kernel: reads and writes 512 MiB), then the gate/up mmvq with
+    its SwiGLU epilogue at B=8 on four distinct matrices."""
     import torch
     import workload as W
     import session_decode_step_amd as kd
@@ -125,9 +128,9 @@ def traffic_probe() -> None:
     n, k, B = 28672, 4096, 8
     mats = [kd.kd_pack_weight(W.draw_weight("q4_0", 0, 4, 90, 91, i, n, k)) for i in range(4)]
     act = kd.kd_quantize_act_q8(torch.randn((B, k), device="cuda"))
-    y = torch.empty((B, n), dtype=torch.float32, device="cuda")
+    h_act = kd.alloc_act(B, n // 2)
     for i in range(8):
-        kd.kd_mmvq_q4_0(mats[i % 4], act, B, y)
+        kd.kd_mmvq_swiglu(mats[i % 4], act, B, h_act)
     torch.cuda.synchronize()
     log("traffic probe done")
 
@@ -170,12 +173,12 @@ def traffic_summarize(fetch: str, write: str, fetch_cmd: str, write_cmd: str) ->
     n, k, B = 28672, 4096, 8
     alg = mmvq_algorithmic_bytes(n, k, B)
     total = res["fetch"]["bytes"] + res["write"]["bytes"]
-    rec = {"kernel": "mmvq_kernel<Q4_0> 28672x4096 B=8", "source_hash": kernel_source_hash(),
+    rec = {"kernel": "mmvq_kernel<Q4_0, SwiGLU epilogue> 28672x4096 B=8", "source_hash": kernel_source_hash(),
            "fetch_bytes": round(res["fetch"]["bytes"]), "write_bytes": round(res["write"]["bytes"]),
            "traffic_bytes": round(total), "algorithmic_bytes": alg, "traffic_over_algorithmic": round(total / alg, 4),
            "fetch_factor": round(res["fetch"]["factor"], 5), "write_factor": round(res["write"]["factor"], 5)}
     lines = [
-        "HBM traffic of mmvq_kernel<Q4_0>, stacked gate+up 28672 x 4096, B=8 (rocprofv3 PMC, MI355X)",
+        "HBM traffic of mmvq_kernel<Q4_0> with the SwiGLU epilogue, gate/up 28672 x 4096, B=8 (rocprofv3 PMC, MI355X)",
         "",
         f"FETCH_SIZE pass: {fetch_cmd}",
         f"WRITE_SIZE pass: {write_cmd}",
@@ -298,16 +301,18 @@ def main() -> None:
         sweep[B]["step_GBs"] = step_bytes(B, mid) / (sweep[B]["ms_per_step"] / 1e3) / 1e9
 
     # ---------------------------------------------------------------- dominant kernel: mmvq
-    # the stacked gate+up product of the FFN (28672 x 4096 Q4_0) at the headline width: 32 of
-    # the step's launches and 54% of its weight bytes.  Launches rotate over the 32 layers'
-    # own matrices (2.1 GB, well above the 256 MB Infinity Cache), as inside a step.
+    # the FFN's interleaved gate/up product (28672 x 4096 Q4_0) with its SwiGLU + quantiser
+    # epilogue, at the headline width: 32 of the step's launches and 54% of its weight bytes.
+    # Launches rotate over the 32 layers' own matrices (2.1 GB, well above the 256 MB
+    # Infinity Cache), as inside a step.
     B = Bh
-    log(f"dominant kernel: stacked gate+up mmvq at B={B}")
+    log(f"dominant kernel: gate/up mmvq with SwiGLU epilogue at B={B}")
     mats = [gw.km.packed[il]["w_gateup"] for il in range(L)]
     xin = torch.randn((B, sp.d), device="cuda", generator=torch.Generator(device="cuda").manual_seed(0))
     act = kd.kd_quantize_act_q8(xin)
-    y = torch.empty((B, mats[0].n_out), dtype=torch.float32, device="cuda")
-    mm_us = time_rotating(lambda i: kd.kd_mmvq_q4_0(mats[i % L], act, B, y, stream=stream), args.kernel_iters, stream)
+    h_act = kd.alloc_act(B, mats[0].n_out // 2)
+    mm_us = time_rotating(lambda i: kd.kd_mmvq_swiglu(mats[i % L], act, B, h_act, stream=stream), args.kernel_iters,
+                          stream)
     n, k = mats[0].n_out, mats[0].k
     mm_bytes = mmvq_algorithmic_bytes(n, k, B)
     mm_gbs = mm_bytes / (mm_us * 1e-6) / 1e9
@@ -374,7 +379,7 @@ def main() -> None:
         "sweep": {str(b): {kk: round(v, 3) for kk, v in sweep[b].items()} for b in widths},
         "step_GBs": round(top["step_GBs"], 1),
         "step_frac_of_peak": round(top["step_GBs"] / HBM_PEAK_GBS, 4),
-        "roofline": {"bound": "hbm", "kernel": "mmvq_kernel<Q4_0> 28672x4096 (stacked gate+up) at B=%d" % Bh,
+        "roofline": {"bound": "hbm", "kernel": "mmvq_kernel<Q4_0, SwiGLU epilogue> 28672x4096 (gate/up) at B=%d" % Bh,
                      "achieved": round(mm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(mm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "avg_launch_us": round(mm_us, 3), "algorithmic_bytes": int(mm_bytes)},

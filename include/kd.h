@@ -138,6 +138,22 @@ kd_status kd_swiglu_rows(const float* g, const float* u, float* a, int32_t B, in
 /* z = x + y  (memra-engine decode_batch.rs residual ``add``). */
 kd_status kd_add_rows(const float* x, const float* y, float* z, int32_t B, int32_t n, void* stream);
 
+/* ---- products with fused epilogues ----------------------------------------------------- */
+/* The dense FFN's first product with SwiGLU in its epilogue: W is [2F, k] with the gate and
+ * up rows interleaved in blocks of 32 (the kd_layer_desc stacked layout, F % 32 == 0); the
+ * output is Q(silu(gate) * up) for the B rows, in the activation layout for k = F
+ * (kd_act_qs_bytes(B, F) / kd_act_d_bytes(B, F)).  silu(g) * u = g / (1 + e^-g) * u, as
+ * kd_swiglu_rows (memra-engine decode_batch.rs FFN arm: gate, up, activation, quantise). */
+kd_status kd_mmvq_swiglu(const kd_weight* W, kd_act_q8 x, int32_t B, kd_act_q8 out, void* stream);
+/* The attention input product with NEOX RoPE and the fp16 KV append in its epilogue: W is
+ * wqkv ([(H + 2G) hd, k]) with each head's rows in pair order (kd_layer_desc wqkv_pair_rows);
+ * q_out fp32 [B][ldq] receives the rotated q (H hd columns); the rotated k and the v rows go
+ * to position pos[b] of row b's caches as kd_kv_append stores them; angles as
+ * kd_rope_neox_rows (fp64 from pos and rope_base) (memra-engine decode_batch.rs phase A). */
+kd_status kd_mmvq_rope(const kd_weight* W, kd_act_q8 x, int32_t B, int32_t H, int32_t G, int32_t hd,
+                       float* q_out, int32_t ldq, void* const* k_base, void* const* v_base,
+                       const int32_t* pos, int32_t capacity, float rope_base, void* stream);
+
 /* ---- KV append and ragged split-K decode attention --------------------------------- */
 /* Store row b's k[b][G][hd] and v[b][G][hd] (fp32, rounded to fp16 nearest-even) at
  * position pos[b] of its own cache: K_b[g][pos[b]][:] (memra-engine decode_batch.rs phase A,
@@ -163,11 +179,19 @@ kd_status kd_fa_decode_ragged(const float* q, int32_t B, int32_t H, int32_t G, i
 typedef struct {
   const float* attn_norm;   /* [d] */
   kd_weight wqkv;           /* [(H + 2G) hd, d]: rows q (H hd), then k (G hd), then v (G hd) */
+  int32_t wqkv_pair_rows;   /* 1: within each head the packed rows are in RoPE pair order --
+                               packed row 2i is row i, packed row 2i + 1 is row i + hd/2
+                               (i < hd/2) -- so every 16-row tile holds 8 whole pairs and the
+                               product itself rotates q and k and stores k and v in the caches;
+                               0: canonical order (a separate RoPE + append launch) */
   kd_weight wo;             /* [d, H hd] */
   const float* ffn_norm;    /* [d]; NULL for an attention-only layer */
   kd_weight w_gate, w_up;   /* dense SwiGLU [F, d] (qs NULL if MoE or attention-only); or w_gate
-                               holding [2F, d] (gate rows, then up rows) with w_up.qs NULL:
-                               one product streams both (kd_stack_rows builds it) */
+                               holding [2F, d] with w_up.qs NULL, rows interleaved in blocks of
+                               32 -- packed rows 64m .. 64m+31 are gate rows 32m .. 32m+31 and
+                               packed rows 64m+32 .. 64m+63 the same up rows (F % 32 == 0) --
+                               so one product streams both and applies SwiGLU and the
+                               activation quantiser to its own output */
   kd_weight w_down;         /* [d, F] */
   const float* router;      /* MoE: fp32 [E][d] */
   kd_weight e_gate, e_up;   /* MoE: experts stacked by rows, expert e = rows [e Fe, (e+1) Fe) of [E Fe, d] */

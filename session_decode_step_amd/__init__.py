@@ -41,7 +41,8 @@ class KdAct(C.Structure):
 
 
 class KdLayerDesc(C.Structure):
-    _fields_ = [("attn_norm", C.c_void_p), ("wqkv", KdWeight), ("wo", KdWeight), ("ffn_norm", C.c_void_p),
+    _fields_ = [("attn_norm", C.c_void_p), ("wqkv", KdWeight), ("wqkv_pair_rows", C.c_int32), ("wo", KdWeight),
+                ("ffn_norm", C.c_void_p),
                 ("w_gate", KdWeight), ("w_up", KdWeight), ("w_down", KdWeight), ("router", C.c_void_p),
                 ("e_gate", KdWeight), ("e_up", KdWeight), ("e_down", KdWeight),
                 ("s_gate", KdWeight), ("s_up", KdWeight), ("s_down", KdWeight)]
@@ -84,6 +85,8 @@ SIGNATURES = {
     "kd_model_destroy": (None, [_P]),
     "kd_decode_step_workspace": (_S, [_P, _I, _PI]),
     "kd_decode_step": (_I, [_P, _I, _P, _PI, _PP, _PP, _I, _P, _P, _S, _P]),
+    "kd_mmvq_swiglu": (_I, [_PW, KdAct, _I, KdAct, _P]),
+    "kd_mmvq_rope": (_I, [_PW, KdAct, _I, _I, _I, _I, _P, _I, _PP, _PP, _PI, _I, _F, _P]),
     "kd_debug_block_dots": (_I, [_PW, KdAct, _I, _P, _P]),
     "kd_debug_fa_workspace": (_S, [_I, _I, _I, _PI, _I]),
     "kd_debug_fa_decode_chunked": (_I, [_P, _I, _I, _I, _I, _PP, _PP, _PI, _I, _F, _P, _I, _P, _S, _P]),
@@ -165,11 +168,30 @@ def kd_pack_weight(w: Dict, device="cuda", stream=None) -> PackedWeight:
     return PackedWeight(fmt, n, k, qs, dd)
 
 
-def stack_rows(a: Dict, b: Dict) -> Dict:
-    """Row-major block matrices a [n_a, k] and b [n_b, k] stacked into one [n_a + n_b, k]."""
-    assert a["fmt"] == b["fmt"] and a["k"] == b["k"]
-    return {"fmt": a["fmt"], "n": a["n"] + b["n"], "k": a["k"], "qs": np.concatenate([a["qs"], b["qs"]]),
-            "d": np.concatenate([a["d"], b["d"]])}
+def _take_rows(w: Dict, order: np.ndarray) -> Dict:
+    return {"fmt": w["fmt"], "n": len(order), "k": w["k"], "qs": np.ascontiguousarray(w["qs"][order]),
+            "d": np.ascontiguousarray(w["d"][order])}
+
+
+def interleave_gate_up(gate: Dict, up: Dict) -> Dict:
+    """gate and up [F, k] as one [2F, k] matrix in blocks of 32 rows (gate rows 32m..32m+31,
+    then up rows 32m..32m+31): the layout of the stacked gate/up product in ``kd.h``."""
+    assert gate["fmt"] == up["fmt"] and gate["k"] == up["k"] and gate["n"] == up["n"] and gate["n"] % 32 == 0
+    F = gate["n"]
+    both = {"fmt": gate["fmt"], "n": 2 * F, "k": gate["k"], "qs": np.concatenate([gate["qs"], up["qs"]]),
+            "d": np.concatenate([gate["d"], up["d"]])}
+    blk = np.arange(F // 32)[:, None]
+    order = np.concatenate([blk * 32 + np.arange(32)[None, :], F + blk * 32 + np.arange(32)[None, :]], axis=1)
+    return _take_rows(both, order.reshape(-1))
+
+
+def rope_pair_rows(wqkv: Dict, n_heads: int, hd: int) -> Dict:
+    """wqkv with each head's rows in RoPE pair order: packed row 2i = row i, 2i+1 = row i + hd/2."""
+    half = hd // 2
+    within = np.stack([np.arange(half), np.arange(half) + half], axis=1).reshape(-1)
+    order = (np.arange(n_heads)[:, None] * hd + within[None, :]).reshape(-1)
+    assert wqkv["n"] == n_heads * hd
+    return _take_rows(wqkv, order)
 
 
 def expert_view(w: PackedWeight, n_out: int) -> PackedWeight:
@@ -215,6 +237,24 @@ def kd_mmvq_q8_0(W: PackedWeight, x: Act, B: int, y: Optional[torch.Tensor] = No
 
 def kd_mmvq_q4_0(W: PackedWeight, x: Act, B: int, y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     return _mmvq("kd_mmvq_q4_0", W, x, B, y, stream)
+
+
+def kd_mmvq_swiglu(W: PackedWeight, x: Act, B: int, out: Optional[Act] = None, stream=None) -> Act:
+    """Interleaved gate/up product with SwiGLU and the quantiser in its epilogue."""
+    F = W.n_out // 2
+    out = out or alloc_act(B, F, x.qs.device)
+    wc = W.c()
+    _check(lib().kd_mmvq_swiglu(C.byref(wc), x.c(), B, out.c(), _stream(stream)), "kd_mmvq_swiglu")
+    return out
+
+
+def kd_mmvq_rope(W: PackedWeight, x: Act, B: int, H: int, G: int, hd: int, q_out: torch.Tensor, k_base, v_base,
+                 pos: Sequence[int], capacity: int, rope_base: float, stream=None) -> torch.Tensor:
+    """Pair-ordered wqkv product with RoPE and the fp16 KV append in its epilogue."""
+    wc = W.c()
+    _check(lib().kd_mmvq_rope(C.byref(wc), x.c(), B, H, G, hd, q_out.data_ptr(), q_out.stride(0), _ptrs(k_base),
+                              _ptrs(v_base), _i32(pos), capacity, rope_base, _stream(stream)), "kd_mmvq_rope")
+    return q_out
 
 
 def kd_debug_block_dots(W: PackedWeight, x: Act, B: int, stream=None) -> torch.Tensor:
@@ -299,7 +339,10 @@ class KdModel:
     """Packs a model's weights (row-major block arrays, numpy) into device tiles and creates
     the kd_model.  The tensors it holds back the borrowed device pointers."""
 
-    def __init__(self, model: Dict, device="cuda"):
+    def __init__(self, model: Dict, device="cuda", fused: bool = True):
+        """``fused``: pack wqkv in RoPE pair order and gate/up interleaved, so the step runs
+        the RoPE/append and SwiGLU/quantise work in the products' epilogues; False keeps the
+        canonical layouts (separate launches; the same results bit for bit)."""
         sp = model["spec"]
         self.spec = sp
         self.keep: List[torch.Tensor] = []
@@ -326,12 +369,19 @@ class KdModel:
             slot[0] = il
             D = self.layers[il]
             D.attn_norm = F(L["attn_norm"])
-            D.wqkv = W(L["wqkv"], "wqkv")
+            if fused:
+                D.wqkv = W(rope_pair_rows(L["wqkv"], sp.n_head + 2 * sp.n_head_kv, sp.head_dim), "wqkv")
+                D.wqkv_pair_rows = 1
+            else:
+                D.wqkv = W(L["wqkv"], "wqkv")
+                D.wqkv_pair_rows = 0
             D.wo = W(L["wo"], "wo")
             D.ffn_norm = F(L["ffn_norm"]) if "ffn_norm" in L else None
-            if "w_gate" in L:   # gate and up stacked into one [2F, d] matrix: one product streams both
-                D.w_gate, D.w_up, D.w_down = (W(stack_rows(L["w_gate"], L["w_up"]), "w_gateup"), empty,
+            if "w_gate" in L and fused:   # gate and up interleaved: one product streams both
+                D.w_gate, D.w_up, D.w_down = (W(interleave_gate_up(L["w_gate"], L["w_up"]), "w_gateup"), empty,
                                               W(L["w_down"], "w_down"))
+            elif "w_gate" in L:
+                D.w_gate, D.w_up, D.w_down = W(L["w_gate"], "w_gate"), W(L["w_up"], "w_up"), W(L["w_down"], "w_down")
             else:
                 D.w_gate, D.w_up, D.w_down = empty, empty, empty
             if "router" in L:

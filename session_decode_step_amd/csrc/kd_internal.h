@@ -107,6 +107,14 @@ __device__ inline float wave_max(float v) {
   return v;
 }
 
+// cos/sin of the NEOX RoPE angle pos * base^(-2i/hd), evaluated in fp64, rounded to fp32.
+__device__ inline float2 rope_cs(int pos, int i, int hd, double base) {
+  const double theta = (double)pos * pow(base, -2.0 * (double)i / (double)hd);
+  double s, c;
+  sincos(theta, &s, &c);
+  return make_float2((float)c, (float)s);
+}
+
 // ---- buffer loads ----------------------------------------------------------------------
 // Raw (stride 0) buffer descriptors: an offset at or past num_records reads as zero without
 // touching memory, which masks out-of-range lanes without a branch.
@@ -162,6 +170,17 @@ struct RowCaches {
   void* v[KD_MAX_B];
   int32_t pos[KD_MAX_B];
 };
+
+// Fused products.  SwiGLU: W is the [2F, d] gate/up matrix interleaved in blocks of 32 rows
+// (gate rows 32m.., then up rows 32m..); writes the quantised silu(gate) * up rows [B][F].
+void launch_mmvq_swiglu(const kd_weight& W, const int8_t* xq, const float* xd, int B, int8_t* out_qs, float* out_d,
+                        hipStream_t st);
+// RoPE: W is wqkv with each head's rows in pair order (i, i + hd/2 adjacent); writes the
+// rotated q rows to q (stride ldq) and the rotated k and the v rows (fp16) at each row's
+// position in its caches; cs is the step's cos/sin table.
+// cs == nullptr: the angles are evaluated in the epilogue (rope_base), same values.
+void launch_mmvq_rope(const kd_weight& W, const int8_t* xq, const float* xd, int B, float* q, int ldq, int H, int G,
+                      int hd, const float* cs, float rope_base, const RowCaches& rc, int capacity, hipStream_t st);
 
 // cos/sin table [B][hd/2][2] fp32 from per-row positions (angles in fp64).
 void launch_rope_table(const RowCaches& rc, int B, int hd, float base, float* cs, hipStream_t st);

@@ -122,7 +122,19 @@ struct MmvqArgs {
   const int32_t* out_row;
   long long w_group_tiles;
   int32_t* debug_S;  // [B][n_out][kblocks] when non-null (epilogue replaced)
+  // fused epilogues (plain products leave these unused)
+  int8_t* epi_qs;     // SwiGLU: quantised silu(gate) * up rows, F = n_out / 2 columns
+  float* epi_qd;
+  float* epi_q;       // RoPE: rotated q rows (stride epi_ldq); k and v go to the caches
+  const float* epi_cs;  // cos/sin table [B][hd/2][2], or null: evaluated here from epi_base
+  double epi_base;
+  int epi_ldq, epi_H, epi_G, epi_hd, epi_capacity;
+  RowCaches epi_rc;
 };
+
+// Epilogue of a product: write y (plain); apply SwiGLU to the interleaved gate/up rows and
+// quantise the result (swiglu); rotate q/k pairs and store q, and k and v in the caches (rope).
+enum { EPI_PLAIN = 0, EPI_SWIGLU = 1, EPI_ROPE = 2 };
 
 __device__ __forceinline__ float f4_get(const float4& v, int j) {
   return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
@@ -190,10 +202,10 @@ __device__ __forceinline__ void wstage_load(WStage<FMT>& st, __amdgpu_buffer_rsr
 // partial sums are added in wave order through LDS.  Per output, the fp32 sequence is: the
 // blocks of the wave's quads in ascending order, then the waves in ascending order -- a
 // function of k alone.
-// Dynamic LDS: per-wave activation scales [nw][16][QW][4] floats, then [nw][RG][4][64].
-template <int FMT, int QW, int NS, bool DEBUG>
+// Dynamic LDS: per-wave activation scales [nw][16][QW][4] floats, then [nw][RG][4][64],
+// then (fused epilogues) the workgroup's outputs [RG * 16][16].
+template <int FMT, int QW, int NS, int RG, int EPI, bool DEBUG>
 __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
-  constexpr int RG = KD_MMVQ_RG;
   constexpr int NT = RG * QW;
   constexpr int D0 = FMT == KD_FMT_Q8_0 ? KD_MMVQ_DEPTH_Q8 : KD_MMVQ_DEPTH_Q4;
   constexpr int D = D0 < NT ? D0 : NT;
@@ -322,15 +334,76 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) red[((w * RG + r) * 4 + s) * 64 + lane] = acc[r][s];
   __syncthreads();
+  if (EPI == EPI_PLAIN) {
+    for (int t = threadIdx.x; t < RG * 256; t += blockDim.x) {
+      const int r = t >> 8, s = (t >> 6) & 3, l = t & 63;
+      float v = red[(r * 4 + s) * 64 + l];
+      for (int ww = 1; ww < nw; ++ww) v += red[((ww * RG + r) * 4 + s) * 64 + l];  // fixed wave order
+      const int b = 4 * (l >> 4) + s;
+      const int row = (rg0 + r) * 16 + (l & 15);
+      if (b < nrows && row < a.n_out) {
+        const int orow = out_row ? out_row[b] : b;
+        a.y[(size_t)orow * a.ldy + row] = v;
+      }
+    }
+    return;
+  }
+  // fused epilogues: the workgroup's outputs outv[row in workgroup][activation row]
+  float* outv = red + nw * RG * 256;
   for (int t = threadIdx.x; t < RG * 256; t += blockDim.x) {
     const int r = t >> 8, s = (t >> 6) & 3, l = t & 63;
     float v = red[(r * 4 + s) * 64 + l];
     for (int ww = 1; ww < nw; ++ww) v += red[((ww * RG + r) * 4 + s) * 64 + l];  // fixed wave order
-    const int b = 4 * (l >> 4) + s;
-    const int row = (rg0 + r) * 16 + (l & 15);
-    if (b < nrows && row < a.n_out) {
-      const int orow = out_row ? out_row[b] : b;
-      a.y[(size_t)orow * a.ldy + row] = v;
+    outv[(r * 16 + (l & 15)) * 16 + 4 * (l >> 4) + s] = v;
+  }
+  __syncthreads();
+  // 8 lanes per (activation row, 32-element block); the loop steps by whole waves, so the 8
+  // lanes of a group stay together (small-k launches have a single wave)
+  for (int t = threadIdx.x; t < 8 * nrows; t += blockDim.x) {
+    const int bq = t >> 3, sub = t & 7;
+    if (EPI == EPI_SWIGLU) {
+      // rows 0..31 of the workgroup: gate rows 32m..32m+31; rows 32..63: the same up rows
+      const int m = blockIdx.x, F = a.n_out / 2;
+      const int NQo = n_quads(F), nbpo = NQo * 4;
+      float av[4];
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const int i = 4 * sub + e2;
+        const float gv = outv[i * 16 + bq], uv = outv[(32 + i) * 16 + bq];
+        av[e2] = (gv / (1.0f + expf(-gv))) * uv;
+      }
+      quant4_lane8(make_float4(av[0], av[1], av[2], av[3]), sub, true,
+                   a.epi_qs + ((size_t)bq * NQo + (m >> 2)) * 128 + (m & 3) * 8, a.epi_qd + (size_t)bq * nbpo + m);
+      if (m == F / 32 - 1)  // zero blocks past F (only when F is not a multiple of 128)
+        for (int blk = F / 32; blk < nbpo; ++blk)
+          quant4_lane8(make_float4(0.0f, 0.0f, 0.0f, 0.0f), sub, true,
+                       a.epi_qs + ((size_t)bq * NQo + (blk >> 2)) * 128 + (blk & 3) * 8,
+                       a.epi_qd + (size_t)bq * nbpo + blk);
+    } else {
+      // 16 rows = 8 RoPE pairs (i, i + hd/2) of one head, packed adjacently
+      const int hd = a.epi_hd, half = hd / 2, H = a.epi_H, G = a.epi_G;
+      const int row0 = rg0 * 16, hh = row0 / hd, i = (row0 % hd) / 2 + sub;
+      const float x0 = outv[(2 * sub) * 16 + bq], x1 = outv[(2 * sub + 1) * 16 + bq];
+      const int pos = a.epi_rc.pos[bq];
+      if (hh < H + G) {
+        const float2 cs = a.epi_cs ? make_float2(a.epi_cs[2 * (bq * half + i)], a.epi_cs[2 * (bq * half + i) + 1])
+                                   : rope_cs(pos, i, hd, a.epi_base);
+        const float y0 = fmaf(x0, cs.x, -(x1 * cs.y));
+        const float y1 = fmaf(x0, cs.y, x1 * cs.x);
+        if (hh < H) {
+          float* qr = a.epi_q + (size_t)bq * a.epi_ldq + (size_t)hh * hd;
+          qr[i] = y0;
+          qr[i + half] = y1;
+        } else {
+          __half* K = static_cast<__half*>(a.epi_rc.k[bq]) + ((size_t)(hh - H) * a.epi_capacity + pos) * hd;
+          K[i] = __float2half_rn(y0);
+          K[i + half] = __float2half_rn(y1);
+        }
+      } else {
+        __half* V = static_cast<__half*>(a.epi_rc.v[bq]) + ((size_t)(hh - H - G) * a.epi_capacity + pos) * hd;
+        V[i] = __float2half_rn(x0);
+        V[i + half] = __float2half_rn(x1);
+      }
     }
   }
 }
@@ -346,49 +419,52 @@ static int mmvq_qw(int NQ) {
   return ceil_div(NQ, nw);
 }
 
-template <int FMT, int QW, int NS>
+template <int FMT, int QW, int NS, int RG, int EPI>
 static void launch_mmvq_qn(const MmvqArgs& a, int n_groups, hipStream_t st) {
   const int nw = ceil_div(a.NQ, QW);
-  dim3 grid(ceil_div(a.NR, KD_MMVQ_RG), n_groups);
+  dim3 grid(ceil_div(a.NR, RG), n_groups);
   const size_t dx_shm = (size_t)nw * 16 * QW * 4 * sizeof(float);
-  if (a.debug_S) {
-    mmvq_kernel<FMT, QW, 4, true><<<grid, 64 * nw, dx_shm, st>>>(a);
-  } else {
-    mmvq_kernel<FMT, QW, NS, false>
-        <<<grid, 64 * nw, dx_shm + (size_t)nw * KD_MMVQ_RG * 256 * sizeof(float), st>>>(a);
+  const size_t red_shm = (size_t)nw * RG * 256 * sizeof(float);
+  const size_t out_shm = EPI == EPI_PLAIN ? 0 : (size_t)RG * 256 * sizeof(float);
+  if constexpr (EPI == EPI_PLAIN) {
+    if (a.debug_S) {
+      mmvq_kernel<FMT, QW, 4, RG, EPI_PLAIN, true><<<grid, 64 * nw, dx_shm, st>>>(a);
+      return;
+    }
   }
+  mmvq_kernel<FMT, QW, NS, RG, EPI, false><<<grid, 64 * nw, dx_shm + red_shm + out_shm, st>>>(a);
 }
 
-template <int FMT, int QW>
+template <int FMT, int QW, int RG, int EPI>
 static void launch_mmvq_q(const MmvqArgs& a, int n_groups, hipStream_t st) {
   // epilogue slots: a function of B (rows past B are never written, so dropping their
   // slots leaves every live output's operation sequence unchanged)
   const int ns = a.count ? 4 : (a.B < 4 ? a.B : 4);
   switch (ns) {
-    case 1: return launch_mmvq_qn<FMT, QW, 1>(a, n_groups, st);
-    case 2: return launch_mmvq_qn<FMT, QW, 2>(a, n_groups, st);
-    case 3: return launch_mmvq_qn<FMT, QW, 3>(a, n_groups, st);
-    default: return launch_mmvq_qn<FMT, QW, 4>(a, n_groups, st);
+    case 1: return launch_mmvq_qn<FMT, QW, 1, RG, EPI>(a, n_groups, st);
+    case 2: return launch_mmvq_qn<FMT, QW, 2, RG, EPI>(a, n_groups, st);
+    case 3: return launch_mmvq_qn<FMT, QW, 3, RG, EPI>(a, n_groups, st);
+    default: return launch_mmvq_qn<FMT, QW, 4, RG, EPI>(a, n_groups, st);
   }
 }
 
-template <int FMT>
+template <int FMT, int RG, int EPI>
 static void launch_mmvq_t(const MmvqArgs& a, int n_groups, hipStream_t st) {
   switch (a.QW) {
-    case 1: return launch_mmvq_q<FMT, 1>(a, n_groups, st);
-    case 2: return launch_mmvq_q<FMT, 2>(a, n_groups, st);
-    case 3: return launch_mmvq_q<FMT, 3>(a, n_groups, st);
-    case 4: return launch_mmvq_q<FMT, 4>(a, n_groups, st);
-    case 5: return launch_mmvq_q<FMT, 5>(a, n_groups, st);
-    case 6: return launch_mmvq_q<FMT, 6>(a, n_groups, st);
-    case 7: return launch_mmvq_q<FMT, 7>(a, n_groups, st);
-    default: return launch_mmvq_q<FMT, 8>(a, n_groups, st);
+    case 1: return launch_mmvq_q<FMT, 1, RG, EPI>(a, n_groups, st);
+    case 2: return launch_mmvq_q<FMT, 2, RG, EPI>(a, n_groups, st);
+    case 3: return launch_mmvq_q<FMT, 3, RG, EPI>(a, n_groups, st);
+    case 4: return launch_mmvq_q<FMT, 4, RG, EPI>(a, n_groups, st);
+    case 5: return launch_mmvq_q<FMT, 5, RG, EPI>(a, n_groups, st);
+    case 6: return launch_mmvq_q<FMT, 6, RG, EPI>(a, n_groups, st);
+    case 7: return launch_mmvq_q<FMT, 7, RG, EPI>(a, n_groups, st);
+    default: return launch_mmvq_q<FMT, 8, RG, EPI>(a, n_groups, st);
   }
 }
 
-void launch_mmvq(const kd_weight& W, const int8_t* xq, const float* xd, int B, float* y, int ldy,
-                 hipStream_t st, const RowMap* map, int32_t* debug_S) {
-  MmvqArgs a;
+static MmvqArgs mmvq_args(const kd_weight& W, const int8_t* xq, const float* xd, int B, float* y, int ldy,
+                          const RowMap* map, int32_t* debug_S) {
+  MmvqArgs a = {};
   a.wq = static_cast<const uint8_t*>(W.qs);
   a.wd = static_cast<const __half*>(W.d);
   a.n_out = W.n_out;
@@ -406,19 +482,50 @@ void launch_mmvq(const kd_weight& W, const int8_t* xq, const float* xd, int B, f
   a.out_row = map ? map->out_row : nullptr;
   a.w_group_tiles = map ? map->w_group_tiles : 0;
   a.debug_S = debug_S;
-  const int ng = map ? map->n_groups : 1;
-  {
-    const size_t tiles = (size_t)(map ? map->n_groups : 1) * (map ? (size_t)map->w_group_tiles : (size_t)a.NR * a.NQ);
-    a.w_bytes = (uint32_t)(tiles * (W.fmt == KD_FMT_Q8_0 ? kTileQ8 : kTileQ4));
-    a.d_bytes = (uint32_t)(tiles * 128);
-    const size_t rows = map ? (size_t)map->act_rows : (size_t)B;
-    a.x_bytes = (uint32_t)(rows * a.NQ * 128);
-    a.xd_bytes = (uint32_t)(rows * a.NQ * 16);
-  }
+  const size_t tiles = (size_t)(map ? map->n_groups : 1) * (map ? (size_t)map->w_group_tiles : (size_t)a.NR * a.NQ);
+  a.w_bytes = (uint32_t)(tiles * (W.fmt == KD_FMT_Q8_0 ? kTileQ8 : kTileQ4));
+  a.d_bytes = (uint32_t)(tiles * 128);
+  const size_t rows = map ? (size_t)map->act_rows : (size_t)B;
+  a.x_bytes = (uint32_t)(rows * a.NQ * 128);
+  a.xd_bytes = (uint32_t)(rows * a.NQ * 16);
+  return a;
+}
+
+template <int RG, int EPI>
+static void launch_mmvq_fmt(const kd_weight& W, const MmvqArgs& a, int ng, hipStream_t st) {
   if (W.fmt == KD_FMT_Q8_0)
-    launch_mmvq_t<KD_FMT_Q8_0>(a, ng, st);
+    launch_mmvq_t<KD_FMT_Q8_0, RG, EPI>(a, ng, st);
   else
-    launch_mmvq_t<KD_FMT_Q4_0>(a, ng, st);
+    launch_mmvq_t<KD_FMT_Q4_0, RG, EPI>(a, ng, st);
+}
+
+void launch_mmvq(const kd_weight& W, const int8_t* xq, const float* xd, int B, float* y, int ldy,
+                 hipStream_t st, const RowMap* map, int32_t* debug_S) {
+  const MmvqArgs a = mmvq_args(W, xq, xd, B, y, ldy, map, debug_S);
+  launch_mmvq_fmt<KD_MMVQ_RG, EPI_PLAIN>(W, a, map ? map->n_groups : 1, st);
+}
+
+void launch_mmvq_swiglu(const kd_weight& W, const int8_t* xq, const float* xd, int B, int8_t* out_qs, float* out_d,
+                        hipStream_t st) {
+  MmvqArgs a = mmvq_args(W, xq, xd, B, nullptr, 0, nullptr, nullptr);
+  a.epi_qs = out_qs;
+  a.epi_qd = out_d;
+  launch_mmvq_fmt<4, EPI_SWIGLU>(W, a, 1, st);
+}
+
+void launch_mmvq_rope(const kd_weight& W, const int8_t* xq, const float* xd, int B, float* q, int ldq, int H, int G,
+                      int hd, const float* cs, float rope_base, const RowCaches& rc, int capacity, hipStream_t st) {
+  MmvqArgs a = mmvq_args(W, xq, xd, B, nullptr, 0, nullptr, nullptr);
+  a.epi_base = (double)rope_base;
+  a.epi_q = q;
+  a.epi_ldq = ldq;
+  a.epi_H = H;
+  a.epi_G = G;
+  a.epi_hd = hd;
+  a.epi_cs = cs;
+  a.epi_rc = rc;
+  a.epi_capacity = capacity;
+  launch_mmvq_fmt<1, EPI_ROPE>(W, a, 1, st);
 }
 
 void launch_act_quant(const float* x, int B, int k, int ldx, int8_t* qs, float* d, hipStream_t st) {
@@ -519,6 +626,50 @@ extern "C" kd_status kd_mmvq_q8_0(const kd_weight* W, kd_act_q8 x, int32_t B, fl
 
 extern "C" kd_status kd_mmvq_q4_0(const kd_weight* W, kd_act_q8 x, int32_t B, float* y, int32_t ldy, void* stream) {
   return mmvq_entry("kd_mmvq_q4_0", KD_FMT_Q4_0, W, x, B, y, ldy, stream);
+}
+
+extern "C" kd_status kd_mmvq_swiglu(const kd_weight* W, kd_act_q8 x, int32_t B, kd_act_q8 out, void* stream) {
+  const char* who = "kd_mmvq_swiglu";
+  KD_REQUIRE(W, KD_ERR_INVALID, "%s: null weight", who);
+  kd_status s = check_mmvq_args(who, W, W->fmt, x, B);
+  if (s != KD_OK) return s;
+  KD_REQUIRE(fmt_quant(W->fmt), KD_ERR_UNSUPPORTED, "%s: format %d", who, W->fmt);
+  KD_REQUIRE(W->n_out % 64 == 0, KD_ERR_UNSUPPORTED, "%s: n_out=%d is not 2F with F a multiple of 32", who,
+             W->n_out);
+  KD_REQUIRE(out.qs && out.d && aligned16(out.qs) && aligned16(out.d), KD_ERR_INVALID,
+             "%s: output buffers null or not 16-byte aligned", who);
+  launch_mmvq_swiglu(*W, x.qs, x.d, B, out.qs, out.d, as_stream(stream));
+  return check_launch(who);
+}
+
+extern "C" kd_status kd_mmvq_rope(const kd_weight* W, kd_act_q8 x, int32_t B, int32_t H, int32_t G, int32_t hd,
+                                  float* q_out, int32_t ldq, void* const* k_base, void* const* v_base,
+                                  const int32_t* pos, int32_t capacity, float rope_base, void* stream) {
+  const char* who = "kd_mmvq_rope";
+  KD_REQUIRE(W, KD_ERR_INVALID, "%s: null weight", who);
+  kd_status s = check_mmvq_args(who, W, W->fmt, x, B);
+  if (s != KD_OK) return s;
+  KD_REQUIRE(fmt_quant(W->fmt), KD_ERR_UNSUPPORTED, "%s: format %d", who, W->fmt);
+  KD_REQUIRE(H > 0 && G > 0 && H % G == 0, KD_ERR_INVALID, "%s: H=%d G=%d", who, H, G);
+  KD_REQUIRE(hd == 64 || hd == 128, KD_ERR_UNSUPPORTED, "%s: hd=%d not 64 or 128", who, hd);
+  KD_REQUIRE(W->n_out == (H + 2 * G) * hd, KD_ERR_INVALID, "%s: n_out=%d is not (H + 2G) hd = %d", who, W->n_out,
+             (H + 2 * G) * hd);
+  KD_REQUIRE(q_out && ldq >= H * hd, KD_ERR_INVALID, "%s: q_out null or ldq=%d < H hd", who, ldq);
+  KD_REQUIRE(k_base && v_base && pos, KD_ERR_INVALID, "%s: null cache table", who);
+  RowCaches rc = {};
+  for (int b = 0; b < B; ++b) {
+    KD_REQUIRE(k_base[b] && v_base[b], KD_ERR_INVALID, "%s: null cache pointer for row %d", who, b);
+    KD_REQUIRE(pos[b] >= 0 && pos[b] + 1 <= capacity, KD_ERR_CAPACITY, "%s: pos[%d]=%d does not fit capacity %d", who,
+               b, pos[b], capacity);
+    for (int a = 0; a < b; ++a)
+      KD_REQUIRE(!(k_base[a] == k_base[b] && pos[a] == pos[b]), KD_ERR_INVALID,
+                 "%s: rows %d and %d write the same cache slot", who, a, b);
+    rc.k[b] = k_base[b];
+    rc.v[b] = v_base[b];
+    rc.pos[b] = pos[b];
+  }
+  launch_mmvq_rope(*W, x.qs, x.d, B, q_out, ldq, H, G, hd, nullptr, rope_base, rc, capacity, as_stream(stream));
+  return check_launch(who);
 }
 
 extern "C" kd_status kd_debug_block_dots(const kd_weight* W, kd_act_q8 x, int32_t B, int32_t* S, void* stream) {

@@ -28,15 +28,17 @@ __global__ __launch_bounds__(256) void norm_quant_kernel(const float* __restrict
   const int P = ceil_div(nbp, 32);
   const float* xr = x + (size_t)b * n;
   const float* rr = r ? r + (size_t)b * n : nullptr;
-  float4 v[MAXP];
+  float4 v[MAXP], gg[MAXP];
   float ss = 0.0f;
 #pragma unroll
-  for (int p = 0; p < MAXP; ++p) {
+  for (int p = 0; p < MAXP; ++p) {  // x, r and the gains are all fetched before the reduction
     v[p] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    gg[p] = v[p];
     const int blk = p * 32 + lb;
     if (p < P && blk < nb) {
       const int c = blk * 32 + 4 * sub;
       v[p] = *reinterpret_cast<const float4*>(xr + c);
+      gg[p] = *reinterpret_cast<const float4*>(g + c);
       if (rr) v[p] = f4_add(v[p], *reinterpret_cast<const float4*>(rr + c));
     }
     ss = fmaf(v[p].x, v[p].x, ss);
@@ -56,8 +58,8 @@ __global__ __launch_bounds__(256) void norm_quant_kernel(const float* __restrict
     float4 y = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     if (p < P && blk < nb) {
       const int c = blk * 32 + 4 * sub;
-      const float4 gg = *reinterpret_cast<const float4*>(g + c);
-      y = make_float4((v[p].x * inv) * gg.x, (v[p].y * inv) * gg.y, (v[p].z * inv) * gg.z, (v[p].w * inv) * gg.w);
+      y = make_float4((v[p].x * inv) * gg[p].x, (v[p].y * inv) * gg[p].y, (v[p].z * inv) * gg[p].z,
+                      (v[p].w * inv) * gg[p].w);
       if (x1_out) *reinterpret_cast<float4*>(x1_out + (size_t)b * n + c) = v[p];
       if (y_out) *reinterpret_cast<float4*>(y_out + (size_t)b * n + c) = y;
     }
@@ -83,14 +85,6 @@ void launch_norm_quant(const float* x, const float* r, const float* g, int B, in
 // ---------------------------------------------------------------------------------------
 // RoPE tables and RoPE + KV append
 // ---------------------------------------------------------------------------------------
-// cos/sin of pos * base^(-2i/hd), evaluated in fp64 and rounded to fp32.
-__device__ inline float2 rope_cs(int pos, int i, int hd, double base) {
-  const double theta = (double)pos * pow(base, -2.0 * (double)i / (double)hd);
-  double s, c;
-  sincos(theta, &s, &c);
-  return make_float2((float)c, (float)s);
-}
-
 __global__ void rope_table_kernel(RowCaches rc, int B, int hd, double base, float* __restrict__ cs) {
   const int half = hd / 2;
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;

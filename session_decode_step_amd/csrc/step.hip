@@ -107,6 +107,8 @@ extern "C" kd_status kd_model_create(const kd_model_desc* desc, kd_model** out) 
     const kd_layer_desc& L = m.layers[il];
     KD_REQUIRE(L.attn_norm, KD_ERR_INVALID, "kd_model_create: layer %d: null attn_norm", il);
     KD_TRY(check_weight("wqkv", il, L.wqkv, (H + 2 * G) * hd, d));
+    KD_REQUIRE(L.wqkv_pair_rows == 0 || L.wqkv_pair_rows == 1, KD_ERR_INVALID,
+               "kd_model_create: layer %d: wqkv_pair_rows=%d", il, L.wqkv_pair_rows);
     KD_TRY(check_weight("wo", il, L.wo, d, H * hd));
     if (m.ffn > 0 || moe) KD_REQUIRE(L.ffn_norm, KD_ERR_INVALID, "kd_model_create: layer %d: null ffn_norm", il);
     if (m.ffn > 0) {
@@ -114,7 +116,9 @@ extern "C" kd_status kd_model_create(const kd_model_desc* desc, kd_model** out) 
         KD_TRY(check_weight("w_gate", il, L.w_gate, m.ffn, d));
         KD_TRY(check_weight("w_up", il, L.w_up, m.ffn, d));
       } else {
-        KD_TRY(check_weight("w_gate (stacked gate+up)", il, L.w_gate, 2 * m.ffn, d));
+        KD_TRY(check_weight("w_gate (interleaved gate+up)", il, L.w_gate, 2 * m.ffn, d));
+        KD_REQUIRE(m.ffn % 32 == 0, KD_ERR_UNSUPPORTED,
+                   "kd_model_create: interleaved gate/up needs ffn %% 32 == 0 (ffn=%d)", m.ffn);
       }
       KD_TRY(check_weight("w_down", il, L.w_down, d, m.ffn));
     }
@@ -167,8 +171,8 @@ struct Carve {
 
 struct StepBufs {
   float *xa, *xb, *f, *qkv, *attn, *o, *gu, *z, *cs, *sh, *sgu;
-  int8_t *act_qs, *hq_qs;
-  float *act_d, *hq_d;
+  int8_t *act_qs, *act2_qs, *hq_qs;
+  float *act_d, *act2_d, *hq_d;
   void* fa_ws;
   int32_t *ids, *count, *rows, *pairs;
   float *p, *gup, *yp;
@@ -192,6 +196,8 @@ size_t carve_step(const kd_model* m, int B, const FaPlan& plan, void* ws, StepBu
   s.act_d = c.take<float>((size_t)B * n_quads(m->max_k) * 4);
   s.fa_ws = c.take<char>(fa_workspace_bytes(plan));
   s.gu = d.ffn ? c.take<float>((size_t)B * 2 * d.ffn) : nullptr;
+  s.act2_qs = d.ffn ? c.take<int8_t>((size_t)B * n_quads(d.ffn) * 128) : nullptr;  // SwiGLU output rows
+  s.act2_d = d.ffn ? c.take<float>((size_t)B * n_quads(d.ffn) * 4) : nullptr;
   if (d.n_experts) {
     const int K = d.n_expert_used, E = d.n_experts, Fe = d.expert_ffn, Fs = d.shared_ffn;
     s.ids = c.take<int32_t>((size_t)B * K);
@@ -291,8 +297,12 @@ extern "C" kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x
     } else {
       launch_norm_quant(base, nullptr, Ly.attn_norm, B, D, d.rms_eps, nullptr, nullptr, s.act_qs, s.act_d, st);
     }
-    launch_mmvq(Ly.wqkv, s.act_qs, s.act_d, B, s.qkv, ldqkv, st);
-    launch_rope_append(s.qkv, ldqkv, B, H, G, hd, s.cs, rc, capacity, true, st, d.rope_base);
+    if (Ly.wqkv_pair_rows) {  // the product rotates q/k and appends k/v itself
+      launch_mmvq_rope(Ly.wqkv, s.act_qs, s.act_d, B, s.qkv, ldqkv, H, G, hd, s.cs, d.rope_base, rc, capacity, st);
+    } else {
+      launch_mmvq(Ly.wqkv, s.act_qs, s.act_d, B, s.qkv, ldqkv, st);
+      launch_rope_append(s.qkv, ldqkv, B, H, G, hd, s.cs, rc, capacity, true, st, d.rope_base);
+    }
     launch_fa(plan, s.qkv, ldqkv, rc, capacity, scale, s.attn, s.act_qs, s.act_d, s.fa_ws, st);
     launch_mmvq(Ly.wo, s.act_qs, s.act_d, B, s.o, D, st);
     if (!has_ffn) {
@@ -307,11 +317,11 @@ extern "C" kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x
       if (Ly.w_up.qs) {
         launch_mmvq(Ly.w_gate, s.act_qs, s.act_d, B, s.gu, 2 * F, st);
         launch_mmvq(Ly.w_up, s.act_qs, s.act_d, B, s.gu + F, 2 * F, st);
-      } else {  // stacked [gate; up]: one pass writes gate to columns [0, F) and up to [F, 2F)
-        launch_mmvq(Ly.w_gate, s.act_qs, s.act_d, B, s.gu, 2 * F, st);
+        launch_swiglu_quant(s.gu, s.gu + F, B, F, 2 * F, nullptr, s.act2_qs, s.act2_d, st);
+      } else {  // interleaved gate/up: one product, SwiGLU and quantiser in its epilogue
+        launch_mmvq_swiglu(Ly.w_gate, s.act_qs, s.act_d, B, s.act2_qs, s.act2_d, st);
       }
-      launch_swiglu_quant(s.gu, s.gu + F, B, F, 2 * F, nullptr, s.act_qs, s.act_d, st);
-      launch_mmvq(Ly.w_down, s.act_qs, s.act_d, B, s.f, D, st);
+      launch_mmvq(Ly.w_down, s.act2_qs, s.act2_d, B, s.f, D, st);
     } else {
       const int E = d.n_experts, K = d.n_expert_used, Fe = d.expert_ffn, Fs = d.shared_ffn;
       launch_router(s.z, Ly.router, B, D, E, K, s.ids, s.p, nullptr, st);

@@ -18,13 +18,13 @@ from . import KdModel, SessionCaches
 
 class GpuWorkload:
     def __init__(self, wl: W.Workload, model: Optional[Dict] = None, device: str = "cuda",
-                 fill: str = "seeded", sessions: Optional[Sequence[int]] = None):
+                 fill: str = "seeded", sessions: Optional[Sequence[int]] = None, fused: bool = True):
         """``fill="seeded"``: KV prefill from the workload generator; ``fill="device"``: a
         seeded torch device generator (for GPU-only comparisons at large shapes)."""
         self.wl = wl
         sp = wl.spec
         self.model = model if model is not None else W.make_model(sp, wl.code, wl.seed)
-        self.km = KdModel(self.model, device)
+        self.km = KdModel(self.model, device, fused=fused)
         n_sess = len(wl.prefill)
         self.caches = SessionCaches(n_sess, sp.n_layers, sp.n_head_kv, wl.capacity, sp.head_dim, device)
         fill_sessions = range(n_sess) if sessions is None else sessions

@@ -71,6 +71,25 @@ def test_mmvq_validation_before_launch():
     assert L.kd_mmvq_q8_0(C.byref(w2), act, 2, 0x5000, 64, None) == kd.KD_ERR_UNSUPPORTED  # k % 32
     w3 = kd.KdWeight(kd.KD_FMT_Q8_0, 64, 256, 0x1001, 0x2000)
     assert L.kd_mmvq_q8_0(C.byref(w3), act, 2, 0x5000, 64, None) == kd.KD_ERR_INVALID      # unaligned
+    # fused-epilogue products
+    out = kd.KdAct(0x6000, 0x7000)
+    wg = kd.KdWeight(kd.KD_FMT_Q4_0, 96, 256, 0x1000, 0x2000)                               # 2F = 96: F % 32 != 0
+    assert L.kd_mmvq_swiglu(C.byref(wg), act, 2, out, None) == kd.KD_ERR_UNSUPPORTED
+    wg = kd.KdWeight(kd.KD_FMT_Q4_0, 128, 256, 0x1000, 0x2000)
+    assert L.kd_mmvq_swiglu(C.byref(wg), act, 2, kd.KdAct(0x6001, 0x7000), None) == kd.KD_ERR_INVALID
+    assert L.kd_mmvq_swiglu(C.byref(wg), act, 17, out, None) == kd.KD_ERR_UNSUPPORTED
+    kb = (C.c_void_p * 2)(0x10000, 0x20000)
+    vb = (C.c_void_p * 2)(0x30000, 0x40000)
+    pos = (C.c_int32 * 2)(3, 4)
+    wq = kd.KdWeight(kd.KD_FMT_Q8_0, (4 + 2 * 2) * 64, 256, 0x1000, 0x2000)
+    assert L.kd_mmvq_rope(C.byref(wq), act, 2, 4, 2, 128, 0x8000, 512, kb, vb, pos, 8, 1e4, None) == kd.KD_ERR_INVALID
+    assert L.kd_mmvq_rope(C.byref(wq), act, 2, 4, 2, 96, 0x8000, 512, kb, vb, pos, 8, 1e4, None) == kd.KD_ERR_UNSUPPORTED
+    assert L.kd_mmvq_rope(C.byref(wq), act, 2, 4, 2, 64, 0x8000, 128, kb, vb, pos, 8, 1e4, None) == kd.KD_ERR_INVALID
+    assert L.kd_mmvq_rope(C.byref(wq), act, 2, 4, 2, 64, 0x8000, 256, kb, vb, pos, 4, 1e4, None) == kd.KD_ERR_CAPACITY
+    kb_same = (C.c_void_p * 2)(0x10000, 0x10000)
+    pos_same = (C.c_int32 * 2)(3, 3)
+    assert L.kd_mmvq_rope(C.byref(wq), act, 2, 4, 2, 64, 0x8000, 256, kb_same, vb, pos_same, 8, 1e4, None) \
+        == kd.KD_ERR_INVALID
     assert L.kd_quantize_act_q8(0x1000, 2, 100, 100, act, None) == kd.KD_ERR_UNSUPPORTED
     assert L.kd_pack_weight(7, 16, 32, 0x10, 0x20, 0x30, 0x40, None) == kd.KD_ERR_UNSUPPORTED
 

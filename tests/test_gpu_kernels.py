@@ -202,3 +202,73 @@ def test_fa_decode_ragged_vs_oracle(H, G, hd):
     for chunk, tol in ((1, 2e-5), (37, 2e-6), (1000, 2e-6)):
         oc = kd.kd_fa_decode_ragged(dev(q), G, kb, vb, t_kv, cap, scale, chunk=chunk).cpu().numpy()
         assert_close_rows(oc.reshape(B, -1), out.reshape(B, -1), tol, f"fa chunk={chunk}")
+
+
+# ------------------------------------------------------------------ products with fused epilogues
+@pytest.mark.parametrize("fmt,F,k,B", [("q4_0", 1024, 512, 8), ("q8_0", 704, 256, 5), ("q4_0", 2048, 4096, 16),
+                                       ("q4_0", 352, 704, 1)])
+def test_mmvq_swiglu_equals_unfused_path(fmt, F, k, B):
+    """The SwiGLU epilogue gives the bytes of product -> kd_swiglu_rows -> quantiser, and the
+    dequantised rows match the oracle's silu(gate) * up."""
+    say(f"mmvq_swiglu {fmt} F={F} k={k} B={B}")
+    r = np.random.default_rng(F + k + B)
+    draw = W.draw_q8_0 if fmt == "q8_0" else W.draw_q4_0
+    gate, up = draw(r, r, F, k), draw(r, r, F, k)
+    x = r.standard_normal((B, k)).astype(np.float32)
+    act = kd.kd_quantize_act_q8(dev(x))
+    fused = kd.kd_mmvq_swiglu(kd.kd_pack_weight(kd.interleave_gate_up(gate, up)), act, B)
+    fn = kd.kd_mmvq_q8_0 if fmt == "q8_0" else kd.kd_mmvq_q4_0
+    g = fn(kd.kd_pack_weight(gate), act, B)
+    u = fn(kd.kd_pack_weight(up), act, B)
+    ref_act = kd.kd_quantize_act_q8(kd.kd_swiglu_rows(g, u))
+    sync()
+    c1, s1, pc1, ps1 = untile_act(fused.qs, fused.d, B, F)
+    c2, s2, _, _ = untile_act(ref_act.qs, ref_act.d, B, F)
+    np.testing.assert_array_equal(c1, c2)
+    np.testing.assert_array_equal(s1, s2)
+    assert np.all(pc1 == 0) and np.all(ps1 == 0)            # padding blocks past F
+    # against the oracle (fp64 products of the same quantised input)
+    q, d = ops.quantize_act(x)
+    a_ref = ops.swiglu(ops.mmvq(gate, q, d), ops.mmvq(up, q, d))
+    deq = (c1.reshape(B, -1, 32).astype(np.float64) * s1.reshape(B, -1, 1)).reshape(B, F)
+    # one quantisation step (d/2 per element) is the only error beyond fp32 rounding
+    assert np.all(np.abs(deq - a_ref) <= 0.5 * np.repeat(s1.reshape(B, -1), 32, axis=1) + 2e-3 * np.abs(a_ref) + 1e-6)
+
+
+@pytest.mark.parametrize("fmt,H,G,hd,B", [("q8_0", 4, 2, 64, 2), ("q4_0", 32, 8, 128, 8), ("q4_0", 16, 8, 128, 16)])
+def test_mmvq_rope_equals_unfused_path(fmt, H, G, hd, B):
+    """The RoPE/append epilogue writes the q bits and the fp16 K/V bytes of product ->
+    kd_rope_neox_rows -> kd_kv_append; rows are B-invariant."""
+    say(f"mmvq_rope {fmt} H={H} G={G} hd={hd} B={B}")
+    r = np.random.default_rng(H * hd + B)
+    k = 512
+    n = (H + 2 * G) * hd
+    w = (W.draw_q8_0 if fmt == "q8_0" else W.draw_q4_0)(r, r, n, k)
+    x = r.standard_normal((B, k)).astype(np.float32)
+    act = kd.kd_quantize_act_q8(dev(x))
+    cap = 64
+    pos = [int(p) for p in r.integers(0, cap, B)]
+    fused_c = _caches(B, G, cap, hd)
+    plain_c = _caches(B, G, cap, hd)
+    q_f = torch.zeros((B, H * hd), dtype=torch.float32, device="cuda")
+    kd.kd_mmvq_rope(kd.kd_pack_weight(kd.rope_pair_rows(w, H + 2 * G, hd)), act, B, H, G, hd, q_f,
+                    [c[0].data_ptr() for c in fused_c], [c[1].data_ptr() for c in fused_c], pos, cap, 10000.0)
+    fn = kd.kd_mmvq_q8_0 if fmt == "q8_0" else kd.kd_mmvq_q4_0
+    y = fn(kd.kd_pack_weight(w), act, B)
+    qk = y[:, :(H + G) * hd].contiguous().view(B, H + G, hd)
+    kd.kd_rope_neox_rows(qk, pos, 10000.0)
+    kv_k = qk[:, H:].contiguous()
+    kv_v = y[:, (H + G) * hd:].contiguous().view(B, G, hd)
+    kd.kd_kv_append(kv_k, kv_v, [c[0].data_ptr() for c in plain_c], [c[1].data_ptr() for c in plain_c], pos, cap)
+    sync()
+    np.testing.assert_array_equal(q_f.cpu().numpy().view(np.uint32),
+                                  qk[:, :H].reshape(B, H * hd).cpu().numpy().view(np.uint32))
+    for b in range(B):
+        for j in (0, 1):
+            np.testing.assert_array_equal(fused_c[b][j].cpu().numpy().view(np.uint16),
+                                          plain_c[b][j].cpu().numpy().view(np.uint16))
+    # against the oracle: RoPE of the fp64 product
+    q, d = ops.quantize_act(x)
+    ref = ops.mmvq(w, q, d)
+    qref = np.stack([ops.rope_neox(ref[b, :H * hd].reshape(H, hd), pos[b], 10000.0) for b in range(B)])
+    assert_close_rows(q_f.cpu().numpy(), qref.reshape(B, -1), 2e-3, "mmvq_rope q")

@@ -117,6 +117,25 @@ def test_c2_full_64_steps_bit_identity():
     # sampled oracle check on the final step's logits chain is covered by test_c2_dense_q8_lm_head
 
 
+@pytest.mark.parametrize("name,B,steps", [("c1", 2, 1), ("c2", 4, 3), ("c4", 8, 2)])
+def test_fused_epilogues_equal_separate_launches(name, B, steps):
+    """wqkv in pair order and interleaved gate/up (RoPE/append and SwiGLU/quantise in the
+    products' epilogues) give the outputs and K/V bytes of the canonical layouts (separate
+    launches), bit for bit."""
+    say(f"fused vs separate {name} B={B}")
+    wl = W.workload(name, B=B, steps=steps)
+    fill = "device" if name == "c4" else "seeded"
+    gf = GpuWorkload(wl, fill=fill)
+    gs = GpuWorkload(wl, model=gf.model, fill=fill, fused=False)
+    for s in range(steps):
+        yf = gf.step(s).cpu().numpy()
+        ys = gs.step(s).cpu().numpy()
+        np.testing.assert_array_equal(yf.view(np.uint32), ys.view(np.uint32))
+    for sess in range(len(wl.prefill)):
+        np.testing.assert_array_equal(gf.caches.t[sess].cpu().numpy().view(np.uint16),
+                                      gs.caches.t[sess].cpu().numpy().view(np.uint16))
+
+
 def test_c3_ragged_attention_b16():
     say("c3")
     wl = W.workload("c3")
