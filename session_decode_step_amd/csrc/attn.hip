@@ -17,17 +17,10 @@
 
 namespace kd {
 
-#ifndef KD_FA_TK
-#define KD_FA_TK 128      // keys per tile when R <= 4
-#endif
 #ifndef KD_FA_AUX
 #define KD_FA_AUX 2       // cache policy of the K/V loads (2: non-temporal)
 #endif
-#ifndef KD_FA_MIN_WAVES
-#define KD_FA_MIN_WAVES 1  // occupancy floor handed to the register allocator (waves per SIMD)
-#endif
 
-constexpr int kFaThreads = 256;
 constexpr int kFaMinChunk = 128;
 constexpr int kFaMaxSplits = 128;
 constexpr int kFaMaxKeys = 128 * 1024;  // t_kv limit: chunk <= 1024 keys
@@ -64,60 +57,44 @@ size_t fa_workspace_bytes(const FaPlan& p) {
   return (size_t)p.n_items * p.H * (p.hd + 2) * sizeof(float);
 }
 
-__device__ inline void half8_to_float(const int4 u, float* f) {
-  const __half2* h = reinterpret_cast<const __half2*>(&u);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float2 t = __half22float2(h[i]);
-    f[2 * i] = t.x;
-    f[2 * i + 1] = t.y;
-  }
-}
 
 // 2^x by the hardware instruction (about 1 ulp; results below 2^-126 flush to zero, which
 // only drops probabilities that cannot change an fp32 sum holding a term of 1).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+// ---------------------------------------------------------------------------------------
+// Split kernel on the matrix cores: 8 waves, each taking 16 keys of every 128-key tile.
+//   scores  S^T[key][head] = K[key][:] . q'[head][:] with v_mfma_f32_16x16x32_f16: the A
+//           operand is 16 keys x 32 dims of K (lane: key l%16, 8 dims), B is q' (lane: head
+//           l%16, the same 8 dims); q' = q * scale * log2(e) * 2^e_h is split into two fp16
+//           halves hi + lo (two products), so the scores keep ~22 bits (K is fp16 already).
+//           The power of two 2^e_h brings head h's largest |q'| just under 2^14, so the low
+//           half stays a normal fp16 number; the products are scaled back by 2^-e_h (exact).
+//   output  O[head][dim] += P[head][key] V[key][dim] with v_mfma_f32_16x16x16_f16: A is P
+//           (lane: head l%16, keys 4(l/16) .. +3 -- the lane's own score tile entries), B is V
+//           (lane: dim 8(l%16) + m of the same 4 keys; one product per m = 0..7); P' = 2^14 p
+//           (p <= 1) is split into fp16 hi + lo the same way and the sum scaled back by 2^-14.
+// Head slots past R are zero rows of q' and their outputs are dropped.
+// ---------------------------------------------------------------------------------------
+typedef _Float16 fa_v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 fa_v4h __attribute__((ext_vector_type(4)));
+typedef float fa_v4f __attribute__((ext_vector_type(4)));
+constexpr int kFaWaves = 8;
+
+__device__ __forceinline__ void split_f16(float x, _Float16& hi, _Float16& lo) {
+  hi = (_Float16)x;
+  lo = (_Float16)(x - (float)hi);
 }
 
-// Sum over each aligned group of N = 8 or 16 lanes; every lane of the group ends with the
-// same bits (each step adds two equal partial sums, in one order or the other).
-template <int N>
-__device__ __forceinline__ float group_sum(float v) {
-  v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
-  v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
-  v += dpp_f<0x141>(v);  // row_half_mirror: lane i of 8 takes lane 7-i
-  if (N == 16) v += dpp_f<0x140>(v);  // row_mirror: lane i of 16 takes lane 15-i
-  return v;
-}
-
-// Lane geometry of one workgroup (4 waves) over a tile of keys: a key's HD fp16 values are
-// read by LPK lanes, 16 bytes (8 dims) each, so one wave load covers KPW whole keys and the
-// workgroup SLOTS keys; a tile of TK keys is NL loads per lane for K and NL for V, all
-// issued before the first score is computed.
 template <int R, int HD>
-struct FaShape {
-  static constexpr int LPK = HD / 8;
-  static constexpr int KPW = 64 / LPK;
-  static constexpr int SLOTS = 4 * KPW;
-  static constexpr int TK = R <= 4 ? KD_FA_TK : KD_FA_TK / 2;
-  static constexpr int NL = TK / SLOTS;
-};
-
-// grid (n_items, G); 256 threads.  One workgroup per (row b, split s, KV head g): it reads
-// keys [s*c_b, min((s+1)*c_b, t_b)) of head g once for the R query heads of the group, tile
-// by tile with a running max (the tile order and every reduction tree are fixed by c_b and
-// t_b), and writes the split's partials (m, l, o) for those R heads.
-template <int R, int HD>
-__global__ __launch_bounds__(kFaThreads, KD_FA_MIN_WAVES) void fa_split_kernel(FaPlan p, const float* __restrict__ q, int ldq,
-                                                              RowCaches rc, int capacity, float scale,
-                                                              float* __restrict__ ws) {
-  using S = FaShape<R, HD>;
-  constexpr int LPK = S::LPK, SLOTS = S::SLOTS, TK = S::TK, NL = S::NL;
-  constexpr int NOUT = R * HD;  // outputs of one (row, KV head)
+__global__ __launch_bounds__(64 * kFaWaves) void fa_split_kernel(FaPlan p, const float* __restrict__ q,
+                                                                          int ldq, RowCaches rc, int capacity,
+                                                                          float scale, float* __restrict__ ws) {
+  constexpr int NW = kFaWaves;
+  constexpr int NC = HD / 32;      // 32-dim slices of the score product
+  constexpr int TK = 16 * NW;      // keys per tile
+  constexpr float kPScale = 16384.0f, kPInv = 1.0f / 16384.0f;
+  static_assert(R <= 16, "heads per KV head");
   const int item = blockIdx.x, g = blockIdx.y;
   int b = 0;
 #pragma unroll
@@ -130,140 +107,164 @@ __global__ __launch_bounds__(kFaThreads, KD_FA_MIN_WAVES) void fa_split_kernel(F
   const int nk = k1 - k0;
   const int H = p.H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  // scores are carried in base 2: s2 = (q . k) * scale * log2(e), so e^(s - m) = 2^(s2 - m2)
+  const int n = lane & 15, gq = lane >> 4;
   const float scale2 = scale * 1.44269504088896341f;
-  const int dl = lane % LPK;                     // this lane's dims [8 dl, 8 dl + 8)
-  const int slot = w * S::KPW + lane / LPK;      // this lane's key slot
 
-  __shared__ float tmax[2][4][R];
-  __shared__ float red_l[4][R];
-  __shared__ float red_o[4][R][HD];
+  __shared__ float tmax[2][NW][16];
+  __shared__ float red_l[NW][16];
+  __shared__ float red_o[NW][R][HD];
+  __shared__ __attribute__((aligned(16))) _Float16 qlds[2][NC][16][32];
+  __shared__ float qun[16];
+  __shared__ float alpha_s[2][16];
 
-  float qv[R][8];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const float4* qr = reinterpret_cast<const float4*>(q + (size_t)b * ldq + (size_t)(g * R + r) * HD + dl * 8);
-    const float4 a = qr[0], e = qr[1];
-    qv[r][0] = a.x; qv[r][1] = a.y; qv[r][2] = a.z; qv[r][3] = a.w;
-    qv[r][4] = e.x; qv[r][5] = e.y; qv[r][6] = e.z; qv[r][7] = e.w;
-  }
-  // descriptors over keys [0, k1) of head g: loads past the chunk read zeros
   const __half* Kg = static_cast<const __half*>(rc.k[b]) + (size_t)g * capacity * HD;
   const __half* Vg = static_cast<const __half*>(rc.v[b]) + (size_t)g * capacity * HD;
+  // descriptors end at key k1: keys past the chunk read zeros, so offsets are base + constants
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg, (uint32_t)k1 * HD * 2);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg, (uint32_t)k1 * HD * 2);
 
-  float m_run[R], l_acc[R], o_acc[R][8];
+  float m_run = -INFINITY;  // running max of head n (every lane of column n holds it)
+  float l_run = 0.0f;       // this lane's share of head n's exp-sum
+  fa_v4f o[8];              // o[m][s]: head 4gq + s, dim 8n + m (scaled by 2^14)
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    m_run[r] = -INFINITY;
-    l_acc[r] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o_acc[r][e] = 0.0f;
-  }
+  for (int m = 0; m < 8; ++m) o[m] = fa_v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   for (int t0 = 0, par = 0; t0 < nk; t0 += TK, par ^= 1) {
-    const int nt = min(TK, nk - t0);
-    int4 kr[NL], vr[NL];
+    const int wk = t0 + 16 * w;  // this wave's first key within the chunk
+    // K: slice j -> key wk + n, dims 32j + 8gq (16 bytes)
+    const uint32_t kb = ((uint32_t)(k0 + wk + n) * HD + 8 * gq) * 2;
+    int4 kr[NC];
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int j = i * SLOTS + slot;
-      const uint32_t off = j < nt ? ((uint32_t)(k0 + t0 + j) * HD + dl * 8) * 2 : kOOB;
-      kr[i] = buf16<KD_FA_AUX>(rk, off);
-    }
+    for (int j = 0; j < NC; ++j) kr[j] = buf16<KD_FA_AUX>(rk, kb + j * 64);
+    // V: key wk + 4gq + t, dims 8n .. 8n+7 (lanes with 8n >= HD read bytes whose outputs are dropped)
+    const uint32_t vb0 = ((uint32_t)(k0 + wk + 4 * gq) * HD + 8 * n) * 2;
+    int4 vr[4];
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int j = i * SLOTS + slot;
-      const uint32_t off = j < nt ? ((uint32_t)(k0 + t0 + j) * HD + dl * 8) * 2 : kOOB;
-      vr[i] = buf16<KD_FA_AUX>(rv, off);
-    }
-    __builtin_amdgcn_sched_barrier(0);  // keep every K and V load of the tile ahead of the math
-    // scores of this lane's NL keys for the R heads (identical in the LPK lanes of a key)
-    float sc[R][NL];
+    for (int t = 0; t < 4; ++t) vr[t] = buf16<KD_FA_AUX>(rv, vb0 + t * HD * 2);
+    __builtin_amdgcn_sched_barrier(0);  // every K and V load of the tile ahead of the math
+    if (t0 == 0) {
+      // q' = q * scale * log2(e) * 2^e_h for the 16 head slots (zero past R), as fp16 hi + lo
+      // in LDS in the operand layout [hi/lo][slice][head][32 dims]; wave w stages heads w, w + 8
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      float kf[8];
-      half8_to_float(kr[i], kf);
-      const bool live = i * SLOTS + slot < nt;
+      for (int hs = 0; hs < 16 / NW; ++hs) {
+        const int h = w + NW * hs;
+        float xs[HD / 64];
+        float am = 0.0f;
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        float part = 0.0f;
+        for (int i = 0; i < HD / 64; ++i) {
+          xs[i] = h < R ? q[(size_t)b * ldq + (size_t)(g * R + h) * HD + lane + 64 * i] * scale2 : 0.0f;
+          am = fmaxf(am, fabsf(xs[i]));
+        }
+        am = wave_max(am);
+        int ex = 0;
+        if (am > 0.0f) frexpf(am, &ex);  // am < 2^ex
+        ex = 14 - max(ex, -100);           // |q' 2^ex| < 2^14
 #pragma unroll
-        for (int e = 0; e < 8; ++e) part = fmaf(qv[r][e], kf[e], part);
-        part = group_sum<LPK>(part);
-        sc[r][i] = live ? part * scale2 : -INFINITY;
+        for (int i = 0; i < HD / 64; ++i) {
+          const int d = lane + 64 * i;
+          _Float16 hi, lo;
+          split_f16(ldexpf(xs[i], ex), hi, lo);
+          qlds[0][d / 32][h][d % 32] = hi;
+          qlds[1][d / 32][h][d % 32] = lo;
+        }
+        if (lane == 0) qun[h] = ldexpf(1.0f, -ex);
       }
+      __syncthreads();
     }
-    // tile max per head: lane keys, then the key groups of the wave, then the 4 waves
+
+    // scores of keys wk + 4gq + s, head n (base 2)
+    fa_v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      float mx = sc[r][0];
-#pragma unroll
-      for (int i = 1; i < NL; ++i) mx = fmaxf(mx, sc[r][i]);
-#pragma unroll
-      for (int m = LPK; m < 64; m <<= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));
-      if (lane == 0) tmax[par][w][r] = mx;
+    for (int j = 0; j < NC; ++j) {
+      const fa_v8h kv = __builtin_bit_cast(fa_v8h, kr[j]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, *reinterpret_cast<const fa_v8h*>(&qlds[0][j][n][8 * gq]), acc,
+                                                   0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, *reinterpret_cast<const fa_v8h*>(&qlds[1][j][n][8 * gq]), acc,
+                                                   0, 0, 0);
     }
+    const float qunscale = qun[n];
+    float pv[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      pv[s] = wk + 4 * gq + s < nk ? acc[s] * qunscale : -INFINITY;
+      mx = fmaxf(mx, pv[s]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (gq == 0) tmax[par][w][n] = mx;
     __syncthreads();
-    float alpha[R], mnew[R];
+    float M = tmax[par][0][n];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float M = fmaxf(fmaxf(tmax[par][0][r], tmax[par][1][r]), fmaxf(tmax[par][2][r], tmax[par][3][r]));
-      mnew[r] = fmaxf(m_run[r], M);
-      alpha[r] = fast_exp2(m_run[r] - mnew[r]);  // 0 on the first tile
-      m_run[r] = mnew[r];
-      l_acc[r] *= alpha[r];
+    for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, tmax[par][ww][n]);
+    const float mnew = fmaxf(m_run, M);
+    const float alpha = fast_exp2(m_run - mnew);  // 0 on the first tile
+    m_run = mnew;
+    l_run *= alpha;
+    if (w == 0 && gq == 0) alpha_s[par][n] = alpha;
+    fa_v4h ph, pl;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o_acc[r][e] *= alpha[r];
+    for (int s = 0; s < 4; ++s) {
+      const float pe = fast_exp2(pv[s] - mnew);
+      l_run += pe;
+      _Float16 hi, lo;
+      split_f16(pe * kPScale, hi, lo);
+      ph[s] = hi;
+      pl[s] = lo;
     }
+    if (t0 > 0) {  // rescale the running output rows (head 4gq + s) by their heads' alpha
+      __syncthreads();
+      float al[4];
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      float vf[8];
-      half8_to_float(vr[i], vf);
+      for (int s = 0; s < 4; ++s) al[s] = alpha_s[par][4 * gq + s];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const float pj = fast_exp2(sc[r][i] - mnew[r]);
-        l_acc[r] += pj;
+      for (int m = 0; m < 8; ++m)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o_acc[r][e] = fmaf(pj, vf[e], o_acc[r][e]);
-      }
+        for (int s = 0; s < 4; ++s) o[m][s] *= al[s];
+    }
+    // O += P V, one product per dim offset m of the lane's 8 dims
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      fa_v4h vb;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) vb[t] = __builtin_bit_cast(fa_v8h, vr[t])[m];
+      o[m] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, vb, o[m], 0, 0, 0);
+      o[m] = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, vb, o[m], 0, 0, 0);
     }
   }
 
-  // key groups of the wave (butterfly), then the 4 waves through LDS in wave order
+  // exp-sums: the 4 key groups of the wave, then the waves in order
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (gq == 0) red_l[w][n] = l_run;
+  // outputs: this lane holds heads 4gq + s, dims 8n + m
+  if (8 * n < HD) {
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
+    for (int s = 0; s < 4; ++s) {
+      const int h = 4 * gq + s;
+      if (h < R)
 #pragma unroll
-    for (int m = LPK; m < 64; m <<= 1) {
-      l_acc[r] += __shfl_xor(l_acc[r], m, 64);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o_acc[r][e] += __shfl_xor(o_acc[r][e], m, 64);
-    }
-  }
-  if (lane < LPK) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) red_o[w][r][dl * 8 + e] = o_acc[r][e];
-      if (dl == 0) red_l[w][r] = l_acc[r];
+        for (int m = 0; m < 8; ++m) red_o[w][h][8 * n + m] = o[m][s];
     }
   }
   __syncthreads();
-
   float* po = ws;                                  // [items][H][HD]
   float* pm = ws + (size_t)p.n_items * H * HD;     // [items][H]
-  float* pl = pm + (size_t)p.n_items * H;          // [items][H]
-  for (int idx = tid; idx < NOUT; idx += kFaThreads) {
-    const int r = idx / HD, d = idx % HD;
-    po[((size_t)item * H + g * R) * HD + idx] =
-        ((red_o[0][r][d] + red_o[1][r][d]) + red_o[2][r][d]) + red_o[3][r][d];
-  }
+  float* pl2 = pm + (size_t)p.n_items * H;         // [items][H]
+  for (int idx = tid; idx < R * HD; idx += 64 * NW) {
+    const int h = idx / HD, d = idx % HD;
+    float v = red_o[0][h][d];
 #pragma unroll
-  for (int r = 0; r < R; ++r)
-    if (tid == r) {
-      pm[(size_t)item * H + g * R + r] = m_run[r];
-      pl[(size_t)item * H + g * R + r] = ((red_l[0][r] + red_l[1][r]) + red_l[2][r]) + red_l[3][r];
-    }
+    for (int ww = 1; ww < NW; ++ww) v += red_o[ww][h][d];
+    po[((size_t)item * H + g * R) * HD + idx] = v * kPInv;
+  }
+  if (tid < R) {
+    float l = red_l[0][tid];
+#pragma unroll
+    for (int ww = 1; ww < NW; ++ww) l += red_l[ww][tid];
+    pm[(size_t)item * H + g * R + tid] = m_run;  // lane tid holds head tid's running max
+    pl2[(size_t)item * H + g * R + tid] = l;
+  }
 }
 
 // grid (H, B); HD threads.  Merge the row's chunks in chunk order; optionally quantise.
@@ -343,8 +344,8 @@ __global__ __launch_bounds__(HD) void fa_combine_kernel(FaPlan p, const float* _
 template <int R, int HD>
 static void launch_fa_t(const FaPlan& p, const float* q, int ldq, const RowCaches& rc, int capacity, float scale,
                         float* out, int8_t* oq, float* od, void* ws, hipStream_t st) {
-  fa_split_kernel<R, HD><<<dim3(p.n_items, p.G), kFaThreads, 0, st>>>(p, q, ldq, rc, capacity, scale,
-                                                                      static_cast<float*>(ws));
+  fa_split_kernel<R, HD><<<dim3(p.n_items, p.G), 64 * kFaWaves, 0, st>>>(p, q, ldq, rc, capacity, scale,
+                                                                        static_cast<float*>(ws));
   fa_combine_kernel<HD><<<dim3(p.H, p.B), HD, 0, st>>>(p, static_cast<const float*>(ws), out, oq, od);
 }
 
