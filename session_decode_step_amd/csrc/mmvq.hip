@@ -34,6 +34,12 @@ namespace kd {
 #ifndef KD_MMVQ_WAVE_QUADS
 #define KD_MMVQ_WAVE_QUADS 4
 #endif
+#ifndef KD_MMVQ_DEPTH_RG
+#define KD_MMVQ_DEPTH_RG 2  // ring depth when a workgroup streams several row groups
+#endif
+#ifndef KD_MMVQ_TILE_FENCE
+#define KD_MMVQ_TILE_FENCE 1
+#endif
 #ifndef KD_MMVQ_RG
 #define KD_MMVQ_RG 1  // row groups per workgroup (they share the activation operands)
 #endif
@@ -174,40 +180,43 @@ __device__ __forceinline__ float half_bits(uint32_t hw, int hi) {
 
 constexpr int kWeightAux = KD_MMVQ_NT ? 2 : 0;
 
-// One weight tile of a wave's stream: 16 bytes per lane (two for Q8_0) and its 4 scales.
+// One weight tile of a wave's stream: 16 bytes per lane (two for Q8_0).
 template <int FMT>
 struct WStage {
   int4 w0, w1;
-  uint2 dw;
 };
 
 // Issue the loads of one tile (an invalid tile reads zeros with no traffic).
 template <int FMT>
-__device__ __forceinline__ void wstage_load(WStage<FMT>& st, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rd,
-                                            uint32_t tile, bool valid, int lane, int n) {
+__device__ __forceinline__ void wstage_load(WStage<FMT>& st, __amdgpu_buffer_rsrc_t rw, uint32_t tile, bool valid,
+                                            int lane) {
   constexpr int TILE = FMT == KD_FMT_Q8_0 ? kTileQ8 : kTileQ4;
   const uint32_t wo = valid ? tile * TILE + lane * 16 : kOOB;
   st.w0 = buf16<kWeightAux>(rw, wo);
   st.w1 = (FMT == KD_FMT_Q8_0) ? buf16<kWeightAux>(rw, valid ? wo + 1024 : kOOB) : st.w0;
-  st.dw = buf8<kWeightAux>(rd, valid ? tile * 128 + n * 8 : kOOB);
 }
+
+// LDS slice of one wave (bytes): activation scales [16][QW] float4 and weight scales
+// [RG][QW] x 128 B.
+__host__ __device__ constexpr int mmvq_wave_lds(int QW, int RG) { return 16 * QW * 16 + RG * QW * 128; }
 
 // grid (ceil(NR / RG), n_groups); block = nw waves.  A workgroup owns RG consecutive row
 // groups.  Wave w owns quads [q0, q1) = [w*QW, min(NQ, w*QW + QW)) of every one of them (a
-// partition that depends on NQ only).  It streams its QW x RG weight tiles quad by quad
-// (the RG tiles of one quad share that quad's activation operands, loaded once, one quad
-// ahead) through a depth-D register ring, so tile t is computed while tiles t+1 .. t+D-1
-// are in flight.  Loads are branch-free (out-of-range tiles read zeros and add exactly
-// zero).  The wave stages its own activation scales in its own LDS slice; the waves'
-// partial sums are added in wave order through LDS.  Per output, the fp32 sequence is: the
-// blocks of the wave's quads in ascending order, then the waves in ascending order -- a
-// function of k alone.
-// Dynamic LDS: per-wave activation scales [nw][16][QW][4] floats, then [nw][RG][4][64],
-// then (fused epilogues) the workgroup's outputs [RG * 16][16].
+// partition that depends on NQ only).  It first fetches, with few wide loads, the scales
+// its tiles share -- the weight scales of its RG x QW tiles (8 bytes per lane covering four
+// tiles) and the activation scales of its quads -- into its own LDS slice, and then streams
+// the weight tiles quad by quad through a depth-D register ring, so tile t is computed while
+// tiles t+1 .. t+D-1 are in flight; the activation operands of a quad are loaded once for
+// its RG tiles, one quad ahead.  Loads are branch-free (out-of-range tiles read zeros and
+// add exactly zero).  The waves' partial sums are added in wave order through LDS.  Per output, the fp32
+// sequence is: the blocks of the wave's quads in ascending order, then the waves in
+// ascending order -- a function of k alone.
+// Dynamic LDS: nw wave slices, then [nw][RG][4][64] floats, then (fused epilogues) the
+// workgroup's outputs [RG * 16][16].
 template <int FMT, int QW, int NS, int RG, int EPI, bool DEBUG>
 __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
   constexpr int NT = RG * QW;
-  constexpr int D0 = FMT == KD_FMT_Q8_0 ? KD_MMVQ_DEPTH_Q8 : KD_MMVQ_DEPTH_Q4;
+  constexpr int D0 = RG > 1 ? KD_MMVQ_DEPTH_RG : FMT == KD_FMT_Q8_0 ? KD_MMVQ_DEPTH_Q8 : KD_MMVQ_DEPTH_Q4;
   constexpr int D = D0 < NT ? D0 : NT;
   const int e = blockIdx.y;
   int nrows = a.B;
@@ -237,11 +246,15 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
   // A operand of lane n: activation row n (rows past the live rows read zeros)
   const uint32_t a_off = (n < nrows) ? (uint32_t)(act_row ? act_row[n] : n) * (uint32_t)NQ * 128u + g * 32 : kOOB;
 
-  // ---- this wave's activation scales: rows 0..15 x quads [q0, q0 + QW), float4 per (row,
-  // quad); lane l fetches (row l/4, quads (l%4) + 4i).  Loaded first (L2 hits), stored to
-  // this wave's LDS slice after the weight loads are issued, so no wait holds the stream.
+  char* slice = reinterpret_cast<char*>(smem) + (size_t)w * mmvq_wave_lds(QW, RG);
+  float* dxw = reinterpret_cast<float*>(slice);  // [16][QW] float4
+  char* dww = slice + 16 * QW * 16;              // [RG][QW] x 128 B
+
+  // ---- fetches shared by the wave's tiles, in the order they are consumed (loads complete in
+  // issue order): activation scales, weight scales
+  // activation scales: rows 0..15 x quads [q0, q0 + QW), float4 per (row, quad); lane l
+  // fetches (row l/4, quads (l%4) + 4i)
   constexpr int NDX = (QW + 3) / 4;
-  float* dxw = smem + w * (16 * QW * 4);  // this wave's [16][QW][4]
   int4 dxv[NDX];
   if (!DEBUG) {
     const int r = lane >> 2, p = lane & 3;
@@ -253,15 +266,28 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
       dxv[i] = buf16<0>(rs, off);
     }
   }
+  // weight scales: for row group r, the wave's QW tiles are consecutive (128 B each); lane l
+  // fetches 8 bytes at 8l + 512i
+  constexpr int NDW = (QW + 3) / 4;
+  uint2 dwv[RG][NDW];
+#pragma unroll
+  for (int r = 0; r < RG; ++r)
+#pragma unroll
+    for (int i = 0; i < NDW; ++i) {
+      const int j = 4 * i + (lane >> 4);  // the tile these 8 bytes belong to
+      const bool valid = j < QW && q0 + j < q1 && rg0 + r < a.NR;
+      const uint32_t tile = gtile + (uint32_t)(rg0 + r) * NQ + q0 + j;
+      dwv[r][i] = buf8<kWeightAux>(rd, valid ? tile * 128 + (lane & 15) * 8 : kOOB);
+    }
 
-  // ---- prologue: D weight tiles in flight, then the first two quads' activation operands
+  // ---- D weight tiles in flight (quad j = t / RG, row group r = t % RG)
   WStage<FMT> st[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) {
     const int j = i / RG, r = i % RG;
-    wstage_load<FMT>(st[i], rw, rd, gtile + (uint32_t)(rg0 + r) * NQ + q0 + j, q0 + j < q1 && rg0 + r < a.NR, lane,
-                     n);
+    wstage_load<FMT>(st[i], rw, gtile + (uint32_t)(rg0 + r) * NQ + q0 + j, q0 + j < q1 && rg0 + r < a.NR, lane);
   }
+  // the first two quads' activation operands (one quad ahead afterwards)
   int4 ax0[2], ax1[2];
 #pragma unroll
   for (int j = 0; j < 2 && j < QW; ++j) {
@@ -270,12 +296,21 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
     ax1[j] = buf16<0>(rx, ao == kOOB ? kOOB : ao + 16);
   }
   __builtin_amdgcn_sched_barrier(0);  // every prologue load is issued before anything waits
+
+  // ---- the shared fetches into this wave's LDS slice (each waits on its own loads only)
   if (!DEBUG) {
     const int r = lane >> 2, p = lane & 3;
 #pragma unroll
     for (int i = 0; i < NDX; ++i)
       if (4 * i + p < QW) *reinterpret_cast<int4*>(dxw + (r * QW + 4 * i + p) * 4) = dxv[i];
   }
+#pragma unroll
+  for (int r = 0; r < RG; ++r)
+#pragma unroll
+    for (int i = 0; i < NDW; ++i) {
+      const int j = 4 * i + (lane >> 4);
+      if (j < QW) *reinterpret_cast<uint2*>(dww + (r * QW + j) * 128 + (lane & 15) * 8) = dwv[r][i];
+    }
 
   // ---- the stream, fully unrolled (no loop back-edge, so every wait is exact): tile t =
   // (quad j = t / RG, row group r = t % RG) is computed from stage t % D, which is then
@@ -297,9 +332,11 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
 #pragma unroll
       for (int s = 0; s < NS; ++s) dx[s] = *reinterpret_cast<const float4*>(dxw + ((4 * g + s) * QW + j) * 4);
     }
+    const int4 A0 = ax0[j & 1], A1 = ax1[j & 1];
+    const uint2 dw = *reinterpret_cast<const uint2*>(dww + (r * QW + j) * 128 + n * 8);
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb) {
-      const v4i S = block_dots<FMT>(act_op(ax0[j & 1], ax1[j & 1], jb), w_op<FMT>(cur.w0, cur.w1, jb));
+      const v4i S = block_dots<FMT>(act_op(A0, A1, jb), w_op<FMT>(cur.w0, cur.w1, jb));
       if (DEBUG) {
         const int blk = 4 * q + jb;
         const int row = (rg0 + r) * 16 + n;
@@ -310,7 +347,7 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
             a.debug_S[((size_t)b * a.n_out + row) * a.kblocks + blk] = S[s];
         }
       } else {
-        const float dwj = zsc * half_bits(jb < 2 ? cur.dw.x : cur.dw.y, jb & 1);
+        const float dwj = zsc * half_bits(jb < 2 ? dw.x : dw.y, jb & 1);
 #pragma unroll
         for (int s = 0; s < NS; ++s) acc[r][s] = fmaf(dwj * f4_get(dx[s], jb), (float)S[s], acc[r][s]);
       }
@@ -322,13 +359,13 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
     }
     if (t + D < NT) {
       const int j2 = (t + D) / RG, r2 = (t + D) % RG;
-      wstage_load<FMT>(cur, rw, rd, gtile + (uint32_t)(rg0 + r2) * NQ + q0 + j2, q0 + j2 < q1 && rg0 + r2 < a.NR,
-                       lane, n);
+      wstage_load<FMT>(cur, rw, gtile + (uint32_t)(rg0 + r2) * NQ + q0 + j2, q0 + j2 < q1 && rg0 + r2 < a.NR, lane);
     }
+    if (RG > 1 && KD_MMVQ_TILE_FENCE) __builtin_amdgcn_sched_barrier(0);  // tiles do not interleave (registers)
   }
   if (DEBUG) return;
 
-  float* red = smem + nw * (16 * QW * 4);  // [nw][RG][4][64]
+  float* red = reinterpret_cast<float*>(reinterpret_cast<char*>(smem) + (size_t)nw * mmvq_wave_lds(QW, RG));
 #pragma unroll
   for (int r = 0; r < RG; ++r)
 #pragma unroll
@@ -423,16 +460,16 @@ template <int FMT, int QW, int NS, int RG, int EPI>
 static void launch_mmvq_qn(const MmvqArgs& a, int n_groups, hipStream_t st) {
   const int nw = ceil_div(a.NQ, QW);
   dim3 grid(ceil_div(a.NR, RG), n_groups);
-  const size_t dx_shm = (size_t)nw * 16 * QW * 4 * sizeof(float);
+  const size_t slices = (size_t)nw * mmvq_wave_lds(QW, RG);
   const size_t red_shm = (size_t)nw * RG * 256 * sizeof(float);
   const size_t out_shm = EPI == EPI_PLAIN ? 0 : (size_t)RG * 256 * sizeof(float);
   if constexpr (EPI == EPI_PLAIN) {
     if (a.debug_S) {
-      mmvq_kernel<FMT, QW, 4, RG, EPI_PLAIN, true><<<grid, 64 * nw, dx_shm, st>>>(a);
+      mmvq_kernel<FMT, QW, 4, RG, EPI_PLAIN, true><<<grid, 64 * nw, slices, st>>>(a);
       return;
     }
   }
-  mmvq_kernel<FMT, QW, NS, RG, EPI, false><<<grid, 64 * nw, dx_shm + red_shm + out_shm, st>>>(a);
+  mmvq_kernel<FMT, QW, NS, RG, EPI, false><<<grid, 64 * nw, slices + red_shm + out_shm, st>>>(a);
 }
 
 template <int FMT, int QW, int RG, int EPI>
