@@ -268,8 +268,10 @@ __global__ __launch_bounds__(64 * kFaWaves) void fa_split_kernel(FaPlan p, const
 }
 
 // grid (H, B); HD threads.  Merge the row's chunks in chunk order; optionally quantise.
-// The chunk maxima and their weights e^(m_s - M) are staged in LDS once; each thread then
-// reads its dimension of every chunk's partial with 8 loads in flight at a time.
+// Every load of the first kCombineFast chunks -- their m and l, and this thread's dimension
+// of their partial outputs -- is issued at once, so a row with up to kCombineFast chunks
+// costs one memory round trip; further chunks are merged in LDS-staged batches.
+constexpr int kCombineFast = 64;
 constexpr int kCombineStage = 1024;
 template <int HD>
 __global__ __launch_bounds__(HD) void fa_combine_kernel(FaPlan p, const float* __restrict__ ws, float* __restrict__ out,
@@ -280,18 +282,42 @@ __global__ __launch_bounds__(HD) void fa_combine_kernel(FaPlan p, const float* _
   const float* pm = ws + (size_t)p.n_items * H * HD;
   const float* pl = pm + (size_t)p.n_items * H;
   const int s0 = p.split_off[b], S = p.split_off[b + 1] - s0;
+  // descriptors over this row's chunks only: chunk s >= S reads zeros
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(po + (size_t)s0 * H * HD, (uint32_t)S * H * HD * 4);
+  const __amdgpu_buffer_rsrc_t rm = make_rsrc(pm + (size_t)s0 * H, (uint32_t)S * H * 4);
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(pl + (size_t)s0 * H, (uint32_t)S * H * 4);
+  const float mv = buf4f(rm, d < S ? (uint32_t)(d * H + h) * 4 : kOOB);  // thread d: chunk d
+  const float lv = buf4f(rl, d < S ? (uint32_t)(d * H + h) * 4 : kOOB);
+  float ov[kCombineFast];
+#pragma unroll
+  for (int i = 0; i < kCombineFast; ++i) ov[i] = buf4f(ro, (uint32_t)((i * H + h) * HD + d) * 4);
+  __builtin_amdgcn_sched_barrier(0);
+
   __shared__ float wm[kCombineStage];
   __shared__ float wl[kCombineStage];
   __shared__ float red[HD / 64];
-  float M = -INFINITY;
-  for (int s = d; s < S; s += HD) M = fmaxf(M, pm[(size_t)(s0 + s) * H + h]);
+  float M = d < S ? mv : -INFINITY;
+  for (int s = d + HD; s < S; s += HD) M = fmaxf(M, pm[(size_t)(s0 + s) * H + h]);
   M = wave_max(M);
   if ((d & 63) == 0) red[d >> 6] = M;
   __syncthreads();
   M = red[0];
   for (int i = 1; i < HD / 64; ++i) M = fmaxf(M, red[i]);
+  if (d < S && d < kCombineFast) {
+    const float w = fast_exp2(mv - M);
+    wm[d] = w;
+    wl[d] = w * lv;
+  }
+  __syncthreads();
   float num = 0.0f, den = 0.0f;
-  for (int base = 0; base < S; base += kCombineStage) {
+  const int nf = S < kCombineFast ? S : kCombineFast;
+#pragma unroll
+  for (int i = 0; i < kCombineFast; ++i)
+    if (i < nf) {
+      num = fmaf(wm[i], ov[i], num);
+      den += wl[i];
+    }
+  for (int base = kCombineFast; base < S; base += kCombineStage) {
     const int n = min(kCombineStage, S - base);
     __syncthreads();
     for (int s = d; s < n; s += HD) {
