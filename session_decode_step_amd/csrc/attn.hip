@@ -123,6 +123,17 @@ __global__ __launch_bounds__(64 * kFaWaves) void fa_split_kernel(FaPlan p, const
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg, (uint32_t)k1 * HD * 2);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg, (uint32_t)k1 * HD * 2);
 
+  // q of the heads this wave stages (w, w + 8), fetched before any K/V load so that waiting
+  // for it never waits for the tile's K/V bytes (loads complete in issue order)
+  float xs[16 / NW][HD / 64];
+#pragma unroll
+  for (int hs = 0; hs < 16 / NW; ++hs) {
+    const int h = w + NW * hs;
+#pragma unroll
+    for (int i = 0; i < HD / 64; ++i)
+      xs[hs][i] = h < R ? q[(size_t)b * ldq + (size_t)(g * R + h) * HD + lane + 64 * i] : 0.0f;
+  }
+
   float m_run = -INFINITY;  // running max of head n (every lane of column n holds it)
   float l_run = 0.0f;       // this lane's share of head n's exp-sum
   fa_v4f o[8];              // o[m][s]: head 4gq + s, dim 8n + m (scaled by 2^14)
@@ -148,12 +159,11 @@ __global__ __launch_bounds__(64 * kFaWaves) void fa_split_kernel(FaPlan p, const
 #pragma unroll
       for (int hs = 0; hs < 16 / NW; ++hs) {
         const int h = w + NW * hs;
-        float xs[HD / 64];
         float am = 0.0f;
 #pragma unroll
         for (int i = 0; i < HD / 64; ++i) {
-          xs[i] = h < R ? q[(size_t)b * ldq + (size_t)(g * R + h) * HD + lane + 64 * i] * scale2 : 0.0f;
-          am = fmaxf(am, fabsf(xs[i]));
+          xs[hs][i] *= scale2;
+          am = fmaxf(am, fabsf(xs[hs][i]));
         }
         am = wave_max(am);
         int ex = 0;
@@ -163,7 +173,7 @@ __global__ __launch_bounds__(64 * kFaWaves) void fa_split_kernel(FaPlan p, const
         for (int i = 0; i < HD / 64; ++i) {
           const int d = lane + 64 * i;
           _Float16 hi, lo;
-          split_f16(ldexpf(xs[i], ex), hi, lo);
+          split_f16(ldexpf(xs[hs][i], ex), hi, lo);
           qlds[0][d / 32][h][d % 32] = hi;
           qlds[1][d / 32][h][d % 32] = lo;
         }
