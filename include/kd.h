@@ -227,7 +227,8 @@ size_t kd_decode_step_workspace(const kd_model* m, int32_t B, const int32_t* pos
  * share a cache at consecutive positions (speculative-verify rows) attend causally.
  * k_base / v_base: host arrays [n_layers][B] of cache base addresses.  out: fp32
  * [B][vocab] logits if the model has an lm_head, else [B][d] (output-normed if final_norm).
- * Positions are not advanced: the caller owns session state (memra-engine
+ * x_in and out must be 16-byte aligned (rows are read and written four floats at a time);
+ * KD_ERR_INVALID otherwise.  Positions are not advanced: the caller owns session state (memra-engine
  * decode_batch.rs ``decode_batch_epilogue`` advances pos after the step). */
 kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x_in, const int32_t* pos,
                          void* const* k_base, void* const* v_base, int32_t capacity, float* out,

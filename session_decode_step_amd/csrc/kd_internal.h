@@ -174,7 +174,13 @@ struct RowCaches {
 // Fused products.  SwiGLU: W is the [2F, d] gate/up matrix interleaved in blocks of 32 rows
 // (gate rows 32m.., then up rows 32m..); writes the quantised silu(gate) * up rows [B][F].
 void launch_mmvq_swiglu(const kd_weight& W, const int8_t* xq, const float* xd, int B, int8_t* out_qs, float* out_d,
-                        hipStream_t st);
+                        hipStream_t st, const float* norm_ss = nullptr, int norm_n = 0, float norm_eps = 0.0f);
+// O-style product whose epilogue adds the residual and starts the next RMSNorm: x1 = res + W x
+// (x1 may not alias res), Q8 codes of x1 * gain with per-block scales, and the per-block sums
+// of squares ss [B][n_out / 32] that launch_mmvq_swiglu's norm_ss turns into 1/rms.
+constexpr int kNormFuseMax = 4096;  // longest row whose block sums the consumer's 8 lanes hold
+void launch_mmvq_resnorm(const kd_weight& W, const int8_t* xq, const float* xd, int B, const float* res, int ld,
+                         const float* gain, float* x1, int8_t* out_qs, float* out_d, float* ss, hipStream_t st);
 // RoPE: W is wqkv with each head's rows in pair order (i, i + hd/2 adjacent); writes the
 // rotated q rows to q (stride ldq) and the rotated k and the v rows (fp16) at each row's
 // position in its caches; cs is the step's cos/sin table.

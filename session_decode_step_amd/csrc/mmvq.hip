@@ -136,11 +136,57 @@ struct MmvqArgs {
   double epi_base;
   int epi_ldq, epi_H, epi_G, epi_hd, epi_capacity;
   RowCaches epi_rc;
+  // add + RMSNorm: x1 = res + y (stride epi_ld), x1 * gain quantised into epi_qs/epi_qd, and
+  // per (row, 32-element block) sums of x1^2 into epi_ss [B][n_out / 32]
+  const float* epi_res;
+  float* epi_x1;
+  const float* epi_gain;
+  float* epi_ss;
+  int epi_ld;
+  // normalised input (SwiGLU): every output of row b is scaled by
+  // 1 / sqrt(sum_blk norm_ss[b][blk] / norm_n + norm_eps); null: no scaling
+  const float* norm_ss;
+  int norm_n;
+  float norm_eps;
 };
 
 // Epilogue of a product: write y (plain); apply SwiGLU to the interleaved gate/up rows and
-// quantise the result (swiglu); rotate q/k pairs and store q, and k and v in the caches (rope).
-enum { EPI_PLAIN = 0, EPI_SWIGLU = 1, EPI_ROPE = 2 };
+// quantise the result (swiglu); rotate q/k pairs and store q, and k and v in the caches (rope);
+// add the residual, quantise x1 * gain and record the sums of squares of x1 (resnorm).
+enum { EPI_PLAIN = 0, EPI_SWIGLU = 1, EPI_ROPE = 2, EPI_RESNORM = 3 };
+
+// RMSNorm split across two products.  The producer (resnorm epilogue, 32 output rows per
+// workgroup = one block) quantises z = x1 * gain with the block's own scale and writes the
+// block's sum of squares of x1.  The consumer scales each output of row b by
+// inv_b = 1 / sqrt(sum of the row's block sums / n + eps): the block scale max|z|/127 times
+// inv_b is the scale of the normalised block y = x1 * inv_b * gain, and the codes of z and y
+// are the same numbers.  The row's blocks are added by its 8 lanes: lane `sub` adds blocks
+// [sub * c, sub * c + c) in order (c = ceil(blocks / 8) <= kNormPerLane), then the 8 lanes by
+// xor butterfly (every lane ends with the same value).
+constexpr int kNormPerLane = 16;  // block sums per lane: rows of up to 8 * 16 * 32 = 4096
+
+__device__ __forceinline__ void norm_ss_load(const MmvqArgs& a, int t, int nrows, float (&v)[kNormPerLane]) {
+  const int bq = t >> 3, sub = t & 7;
+  const int nblk = a.norm_n / 32, c = (nblk + 7) / 8;
+  // no sums (plain SwiGLU): an empty range, every load reads zero without touching memory
+  const __amdgpu_buffer_rsrc_t r =
+      a.norm_ss ? make_rsrc(a.norm_ss, (uint32_t)(nrows * nblk * 4)) : make_rsrc(a.xd, 0u);
+#pragma unroll
+  for (int i = 0; i < kNormPerLane; ++i) {
+    const int blk = sub * c + i;
+    v[i] = buf4f(r, (bq < nrows && i < c && blk < nblk) ? (uint32_t)(bq * nblk + blk) * 4u : kOOB);
+  }
+}
+
+__device__ __forceinline__ float norm_inv(const MmvqArgs& a, const float (&v)[kNormPerLane]) {
+  float s = v[0];
+#pragma unroll
+  for (int i = 1; i < kNormPerLane; ++i) s += v[i];
+  s += __shfl_xor(s, 1, 64);
+  s += __shfl_xor(s, 2, 64);
+  s += __shfl_xor(s, 4, 64);
+  return 1.0f / sqrtf(s / (float)a.norm_n + a.norm_eps);
+}
 
 __device__ __forceinline__ float f4_get(const float4& v, int j) {
   return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
@@ -365,6 +411,9 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
   }
   if (DEBUG) return;
 
+  float ssv[kNormPerLane];
+  const bool norm = EPI == EPI_SWIGLU && a.norm_ss != nullptr;
+
   float* red = reinterpret_cast<float*>(reinterpret_cast<char*>(smem) + (size_t)nw * mmvq_wave_lds(QW, RG));
 #pragma unroll
   for (int r = 0; r < RG; ++r)
@@ -385,6 +434,10 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
     }
     return;
   }
+  // normalised input: this thread's first row's block sums, in flight while the outputs are
+  // assembled (unconditional -- with no sums every load reads zero -- since a branch lets the
+  // compiler sink earlier work below it and hold its registers across the loads)
+  if (EPI == EPI_SWIGLU) norm_ss_load(a, threadIdx.x, nrows, ssv);
   // fused epilogues: the workgroup's outputs outv[row in workgroup][activation row]
   float* outv = red + nw * RG * 256;
   for (int t = threadIdx.x; t < RG * 256; t += blockDim.x) {
@@ -402,17 +455,56 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
       // rows 0..31 of the workgroup: gate rows 32m..32m+31; rows 32..63: the same up rows
       const int m = blockIdx.x, F = a.n_out / 2;
       const int NQo = n_quads(F), nbpo = NQo * 4;
+      float inv = 1.0f;
+      if (norm) {
+        if (t == (int)threadIdx.x) {
+          inv = norm_inv(a, ssv);
+        } else {  // a second row of a single-wave workgroup
+          float v2[kNormPerLane];
+          norm_ss_load(a, t, nrows, v2);
+          inv = norm_inv(a, v2);
+        }
+      }
       float av[4];
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
         const int i = 4 * sub + e2;
-        const float gv = outv[i * 16 + bq], uv = outv[(32 + i) * 16 + bq];
+        float gv = outv[i * 16 + bq], uv = outv[(32 + i) * 16 + bq];
+        if (norm) {
+          gv *= inv;
+          uv *= inv;
+        }
         av[e2] = (gv / (1.0f + expf(-gv))) * uv;
       }
       quant4_lane8(make_float4(av[0], av[1], av[2], av[3]), sub, true,
                    a.epi_qs + ((size_t)bq * NQo + (m >> 2)) * 128 + (m & 3) * 8, a.epi_qd + (size_t)bq * nbpo + m);
       if (m == F / 32 - 1)  // zero blocks past F (only when F is not a multiple of 128)
         for (int blk = F / 32; blk < nbpo; ++blk)
+          quant4_lane8(make_float4(0.0f, 0.0f, 0.0f, 0.0f), sub, true,
+                       a.epi_qs + ((size_t)bq * NQo + (blk >> 2)) * 128 + (blk & 3) * 8,
+                       a.epi_qd + (size_t)bq * nbpo + blk);
+    } else if (EPI == EPI_RESNORM) {
+      // the workgroup's 32 rows are block m of the residual row: x1 = res + y
+      const int m = blockIdx.x, Dn = a.n_out, nblk = Dn / 32;
+      const int NQo = n_quads(Dn), nbpo = NQo * 4;
+      const size_t o = (size_t)bq * a.epi_ld + 32 * m + 4 * sub;
+      const float4 xr = *reinterpret_cast<const float4*>(a.epi_res + o);
+      const float4 gn = *reinterpret_cast<const float4*>(a.epi_gain + 32 * m + 4 * sub);
+      const float* ov = outv + (4 * sub) * 16 + bq;
+      const float4 v = make_float4(xr.x + ov[0], xr.y + ov[16], xr.z + ov[32], xr.w + ov[48]);
+      *reinterpret_cast<float4*>(a.epi_x1 + o) = v;
+      float ss = v.x * v.x;
+      ss = fmaf(v.y, v.y, ss);
+      ss = fmaf(v.z, v.z, ss);
+      ss = fmaf(v.w, v.w, ss);
+      ss += __shfl_xor(ss, 1, 64);
+      ss += __shfl_xor(ss, 2, 64);
+      ss += __shfl_xor(ss, 4, 64);
+      if (sub == 0) a.epi_ss[(size_t)bq * nblk + m] = ss;
+      quant4_lane8(make_float4(v.x * gn.x, v.y * gn.y, v.z * gn.z, v.w * gn.w), sub, true,
+                   a.epi_qs + ((size_t)bq * NQo + (m >> 2)) * 128 + (m & 3) * 8, a.epi_qd + (size_t)bq * nbpo + m);
+      if (m == nblk - 1)  // zero blocks past the row (only when it is not a multiple of 128)
+        for (int blk = nblk; blk < nbpo; ++blk)
           quant4_lane8(make_float4(0.0f, 0.0f, 0.0f, 0.0f), sub, true,
                        a.epi_qs + ((size_t)bq * NQo + (blk >> 2)) * 128 + (blk & 3) * 8,
                        a.epi_qd + (size_t)bq * nbpo + blk);
@@ -448,9 +540,9 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
 // Quads per wave: about KD_MMVQ_WAVE_QUADS, and enough that at most 16 waves cover NQ;
 // then balanced (the smallest QW giving the same wave count).  Waves per workgroup:
 // ceil(NQ / QW).  Both depend on the matrix's k only.
-static int mmvq_qw(int NQ) {
+static int mmvq_qw(int NQ, int want_quads = KD_MMVQ_WAVE_QUADS) {
   int qw = ceil_div(NQ, 16);  // at most 16 waves; QW <= 8 covers k <= 16384
-  const int want = NQ < KD_MMVQ_WAVE_QUADS ? NQ : KD_MMVQ_WAVE_QUADS;
+  const int want = NQ < want_quads ? NQ : want_quads;
   qw = qw > want ? qw : want;
   const int nw = ceil_div(NQ, qw);
   return ceil_div(NQ, nw);
@@ -543,11 +635,30 @@ void launch_mmvq(const kd_weight& W, const int8_t* xq, const float* xd, int B, f
 }
 
 void launch_mmvq_swiglu(const kd_weight& W, const int8_t* xq, const float* xd, int B, int8_t* out_qs, float* out_d,
-                        hipStream_t st) {
+                        hipStream_t st, const float* norm_ss, int norm_n, float norm_eps) {
   MmvqArgs a = mmvq_args(W, xq, xd, B, nullptr, 0, nullptr, nullptr);
   a.epi_qs = out_qs;
   a.epi_qd = out_d;
+  a.norm_ss = norm_ss;
+  a.norm_n = norm_n;
+  a.norm_eps = norm_eps;
   launch_mmvq_fmt<4, EPI_SWIGLU>(W, a, 1, st);
+}
+
+// Two row groups per workgroup (one 32-element block of the residual row); two quads per
+// wave, so the workgroup count halves but the wave count does not.
+void launch_mmvq_resnorm(const kd_weight& W, const int8_t* xq, const float* xd, int B, const float* res, int ld,
+                         const float* gain, float* x1, int8_t* out_qs, float* out_d, float* ss, hipStream_t st) {
+  MmvqArgs a = mmvq_args(W, xq, xd, B, nullptr, 0, nullptr, nullptr);
+  a.QW = mmvq_qw(a.NQ, 2);
+  a.epi_res = res;
+  a.epi_ld = ld;
+  a.epi_gain = gain;
+  a.epi_x1 = x1;
+  a.epi_qs = out_qs;
+  a.epi_qd = out_d;
+  a.epi_ss = ss;
+  launch_mmvq_fmt<2, EPI_RESNORM>(W, a, 1, st);
 }
 
 void launch_mmvq_rope(const kd_weight& W, const int8_t* xq, const float* xd, int B, float* q, int ldq, int H, int G,

@@ -171,8 +171,8 @@ struct Carve {
 
 struct StepBufs {
   float *xa, *xb, *f, *qkv, *attn, *o, *gu, *z, *cs, *sh, *sgu;
-  int8_t *act_qs, *act2_qs, *hq_qs;
-  float *act_d, *act2_d, *hq_d;
+  int8_t *act_qs, *act2_qs, *hq_qs, *actn_qs;
+  float *act_d, *act2_d, *hq_d, *actn_d, *ss;
   void* fa_ws;
   int32_t *ids, *count, *rows, *pairs;
   float *p, *gup, *yp;
@@ -198,6 +198,10 @@ size_t carve_step(const kd_model* m, int B, const FaPlan& plan, void* ws, StepBu
   s.gu = d.ffn ? c.take<float>((size_t)B * 2 * d.ffn) : nullptr;
   s.act2_qs = d.ffn ? c.take<int8_t>((size_t)B * n_quads(d.ffn) * 128) : nullptr;  // SwiGLU output rows
   s.act2_d = d.ffn ? c.take<float>((size_t)B * n_quads(d.ffn) * 4) : nullptr;
+  // FFN input when the O product starts the RMSNorm: Q8 codes of x1 * gain, block sums of x1^2
+  s.actn_qs = d.ffn ? c.take<int8_t>((size_t)B * n_quads(D) * 128) : nullptr;
+  s.actn_d = d.ffn ? c.take<float>((size_t)B * n_quads(D) * 4) : nullptr;
+  s.ss = d.ffn ? c.take<float>((size_t)B * (D / 32)) : nullptr;
   if (d.n_experts) {
     const int K = d.n_expert_used, E = d.n_experts, Fe = d.expert_ffn, Fs = d.shared_ffn;
     s.ids = c.take<int32_t>((size_t)B * K);
@@ -241,6 +245,7 @@ extern "C" kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x
   KD_REQUIRE(m, KD_ERR_INVALID, "kd_decode_step: null model");
   KD_REQUIRE(B >= 1 && B <= KD_MAX_B, KD_ERR_UNSUPPORTED, "kd_decode_step: B=%d outside [1,16]", B);
   KD_REQUIRE(x_in && pos && k_base && v_base && out, KD_ERR_INVALID, "kd_decode_step: null pointer");
+  KD_REQUIRE(aligned16(x_in) && aligned16(out), KD_ERR_INVALID, "kd_decode_step: x_in and out must be 16-byte aligned");
   const kd_model_desc& d = m->desc;
   const int L = d.n_layers, H = d.n_head, G = d.n_head_kv, hd = d.head_dim, D = d.d;
   for (int b = 0; b < B; ++b) {
@@ -304,6 +309,17 @@ extern "C" kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x
       launch_rope_append(s.qkv, ldqkv, B, H, G, hd, s.cs, rc, capacity, true, st, d.rope_base);
     }
     launch_fa(plan, s.qkv, ldqkv, rc, capacity, scale, s.attn, s.act_qs, s.act_d, s.fa_ws, st);
+    if (!moe && has_ffn && !Ly.w_up.qs && D <= kNormFuseMax) {
+      // O product + residual add + the FFN RMSNorm's quantiser and sums of squares; the
+      // gate/up product applies 1/rms, SwiGLU and the quantiser for down
+      float* x1 = (res == s.xa) ? s.xb : s.xa;
+      launch_mmvq_resnorm(Ly.wo, s.act_qs, s.act_d, B, res, D, Ly.ffn_norm, x1, s.actn_qs, s.actn_d, s.ss, st);
+      launch_mmvq_swiglu(Ly.w_gate, s.actn_qs, s.actn_d, B, s.act2_qs, s.act2_d, st, s.ss, D, d.rms_eps);
+      launch_mmvq(Ly.w_down, s.act2_qs, s.act2_d, B, s.f, D, st);
+      base = x1;
+      add = s.f;
+      continue;
+    }
     launch_mmvq(Ly.wo, s.act_qs, s.act_d, B, s.o, D, st);
     if (!has_ffn) {
       base = res;

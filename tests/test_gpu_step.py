@@ -118,22 +118,27 @@ def test_c2_full_64_steps_bit_identity():
 
 
 @pytest.mark.parametrize("name,B,steps", [("c1", 2, 1), ("c2", 4, 3), ("c4", 8, 2)])
-def test_fused_epilogues_equal_separate_launches(name, B, steps):
-    """wqkv in pair order and interleaved gate/up (RoPE/append and SwiGLU/quantise in the
-    products' epilogues) give the outputs and K/V bytes of the canonical layouts (separate
-    launches), bit for bit."""
+def test_fused_epilogues_against_separate_launches(name, B, steps):
+    """The fused layouts against the canonical ones (separate launches).
+
+    * wqkv in pair order (RoPE and the K/V append in the QKV product's epilogue) changes no
+      bit: layer 0's K/V bytes, appended slots included, are identical.
+    * The O product's epilogue that adds the residual and starts the FFN RMSNorm (the
+      gate/up product applies 1/rms) rounds differently from the separate norm kernel, so
+      outputs agree within the oracle bars, not bit for bit."""
     say(f"fused vs separate {name} B={B}")
     wl = W.workload(name, B=B, steps=steps)
     fill = "device" if name == "c4" else "seeded"
     gf = GpuWorkload(wl, fill=fill)
     gs = GpuWorkload(wl, model=gf.model, fill=fill, fused=False)
+    nb, eb = SHALLOW if wl.spec.n_layers == 1 else DEEP
     for s in range(steps):
         yf = gf.step(s).cpu().numpy()
         ys = gs.step(s).cpu().numpy()
-        np.testing.assert_array_equal(yf.view(np.uint32), ys.view(np.uint32))
+        assert_close_rows(yf, ys.astype(np.float64), nb, f"{name} step {s} fused vs separate", elem_rel=eb)
     for sess in range(len(wl.prefill)):
-        np.testing.assert_array_equal(gf.caches.t[sess].cpu().numpy().view(np.uint16),
-                                      gs.caches.t[sess].cpu().numpy().view(np.uint16))
+        np.testing.assert_array_equal(gf.caches.t[sess][0].cpu().numpy().view(np.uint16),
+                                      gs.caches.t[sess][0].cpu().numpy().view(np.uint16))
 
 
 def test_c3_ragged_attention_b16():
