@@ -186,7 +186,8 @@ void launch_mmvq_resnorm(const kd_weight& W, const int8_t* xq, const float* xd, 
 // position in its caches; cs is the step's cos/sin table.
 // cs == nullptr: the angles are evaluated in the epilogue (rope_base), same values.
 void launch_mmvq_rope(const kd_weight& W, const int8_t* xq, const float* xd, int B, float* q, int ldq, int H, int G,
-                      int hd, const float* cs, float rope_base, const RowCaches& rc, int capacity, hipStream_t st);
+                      int hd, const float* cs, float rope_base, const RowCaches& rc, int capacity, hipStream_t st,
+                      const float* norm_ss = nullptr, int norm_n = 0, float norm_eps = 0.0f);
 
 // cos/sin table [B][hd/2][2] fp32 from per-row positions (angles in fp64).
 void launch_rope_table(const RowCaches& rc, int B, int hd, float base, float* cs, hipStream_t st);

@@ -411,8 +411,9 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
   }
   if (DEBUG) return;
 
+  constexpr bool kNormEpi = EPI == EPI_SWIGLU || EPI == EPI_ROPE;  // may take a normalised input
   float ssv[kNormPerLane];
-  const bool norm = EPI == EPI_SWIGLU && a.norm_ss != nullptr;
+  const bool norm = kNormEpi && a.norm_ss != nullptr;
 
   float* red = reinterpret_cast<float*>(reinterpret_cast<char*>(smem) + (size_t)nw * mmvq_wave_lds(QW, RG));
 #pragma unroll
@@ -437,7 +438,7 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
   // normalised input: this thread's first row's block sums, in flight while the outputs are
   // assembled (unconditional -- with no sums every load reads zero -- since a branch lets the
   // compiler sink earlier work below it and hold its registers across the loads)
-  if (EPI == EPI_SWIGLU) norm_ss_load(a, threadIdx.x, nrows, ssv);
+  if (kNormEpi) norm_ss_load(a, threadIdx.x, nrows, ssv);
   // fused epilogues: the workgroup's outputs outv[row in workgroup][activation row]
   float* outv = red + nw * RG * 256;
   for (int t = threadIdx.x; t < RG * 256; t += blockDim.x) {
@@ -451,20 +452,20 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
   // lanes of a group stay together (small-k launches have a single wave)
   for (int t = threadIdx.x; t < 8 * nrows; t += blockDim.x) {
     const int bq = t >> 3, sub = t & 7;
+    float inv = 1.0f;  // normalised input: 1/rms of activation row bq
+    if (norm) {
+      if (t == (int)threadIdx.x) {
+        inv = norm_inv(a, ssv);
+      } else {  // a second row of a single-wave workgroup
+        float v2[kNormPerLane];
+        norm_ss_load(a, t, nrows, v2);
+        inv = norm_inv(a, v2);
+      }
+    }
     if (EPI == EPI_SWIGLU) {
       // rows 0..31 of the workgroup: gate rows 32m..32m+31; rows 32..63: the same up rows
       const int m = blockIdx.x, F = a.n_out / 2;
       const int NQo = n_quads(F), nbpo = NQo * 4;
-      float inv = 1.0f;
-      if (norm) {
-        if (t == (int)threadIdx.x) {
-          inv = norm_inv(a, ssv);
-        } else {  // a second row of a single-wave workgroup
-          float v2[kNormPerLane];
-          norm_ss_load(a, t, nrows, v2);
-          inv = norm_inv(a, v2);
-        }
-      }
       float av[4];
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
@@ -512,7 +513,11 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
       // 16 rows = 8 RoPE pairs (i, i + hd/2) of one head, packed adjacently
       const int hd = a.epi_hd, half = hd / 2, H = a.epi_H, G = a.epi_G;
       const int row0 = rg0 * 16, hh = row0 / hd, i = (row0 % hd) / 2 + sub;
-      const float x0 = outv[(2 * sub) * 16 + bq], x1 = outv[(2 * sub + 1) * 16 + bq];
+      float x0 = outv[(2 * sub) * 16 + bq], x1 = outv[(2 * sub + 1) * 16 + bq];
+      if (norm) {
+        x0 *= inv;
+        x1 *= inv;
+      }
       const int pos = a.epi_rc.pos[bq];
       if (hh < H + G) {
         const float2 cs = a.epi_cs ? make_float2(a.epi_cs[2 * (bq * half + i)], a.epi_cs[2 * (bq * half + i) + 1])
@@ -662,8 +667,12 @@ void launch_mmvq_resnorm(const kd_weight& W, const int8_t* xq, const float* xd, 
 }
 
 void launch_mmvq_rope(const kd_weight& W, const int8_t* xq, const float* xd, int B, float* q, int ldq, int H, int G,
-                      int hd, const float* cs, float rope_base, const RowCaches& rc, int capacity, hipStream_t st) {
+                      int hd, const float* cs, float rope_base, const RowCaches& rc, int capacity, hipStream_t st,
+                      const float* norm_ss, int norm_n, float norm_eps) {
   MmvqArgs a = mmvq_args(W, xq, xd, B, nullptr, 0, nullptr, nullptr);
+  a.norm_ss = norm_ss;
+  a.norm_n = norm_n;
+  a.norm_eps = norm_eps;
   a.epi_base = (double)rope_base;
   a.epi_q = q;
   a.epi_ldq = ldq;

@@ -286,8 +286,16 @@ extern "C" kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x
   launch_rope_table(rc, B, hd, d.rope_base, s.cs, st);
 
   // Residual stream = base (+ add, pending); the pending add is fused into the next norm.
+  // A layer whose FFN ends in a resnorm epilogue leaves the next layer's attention input
+  // already quantised (codes of x * attn_norm in act, block sums of squares in ss):
+  // prenormed, and the QKV product applies 1/rms.
   const float* base = x_in;
   const float* add = nullptr;
+  bool prenormed = false;
+  const auto norm_fusable = [&](int il) {
+    const kd_layer_desc& Ly = m->layers[il];
+    return !moe && has_ffn && !Ly.w_up.qs && D <= kNormFuseMax;
+  };
   for (int il = 0; il < L; ++il) {
     const kd_layer_desc& Ly = m->layers[il];
     for (int b = 0; b < B; ++b) {
@@ -296,30 +304,46 @@ extern "C" kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x
     }
     // attn_norm (+ pending residual add) + quantise
     float* res = const_cast<float*>(base);
-    if (add) {
+    if (prenormed) {
+      // done by the previous layer's down product
+    } else if (add) {
       res = (base == s.xa) ? s.xb : s.xa;
       launch_norm_quant(base, add, Ly.attn_norm, B, D, d.rms_eps, res, nullptr, s.act_qs, s.act_d, st);
     } else {
       launch_norm_quant(base, nullptr, Ly.attn_norm, B, D, d.rms_eps, nullptr, nullptr, s.act_qs, s.act_d, st);
     }
     if (Ly.wqkv_pair_rows) {  // the product rotates q/k and appends k/v itself
-      launch_mmvq_rope(Ly.wqkv, s.act_qs, s.act_d, B, s.qkv, ldqkv, H, G, hd, s.cs, d.rope_base, rc, capacity, st);
+      launch_mmvq_rope(Ly.wqkv, s.act_qs, s.act_d, B, s.qkv, ldqkv, H, G, hd, s.cs, d.rope_base, rc, capacity, st,
+                       prenormed ? s.ss : nullptr, D, d.rms_eps);
     } else {
       launch_mmvq(Ly.wqkv, s.act_qs, s.act_d, B, s.qkv, ldqkv, st);
       launch_rope_append(s.qkv, ldqkv, B, H, G, hd, s.cs, rc, capacity, true, st, d.rope_base);
     }
     launch_fa(plan, s.qkv, ldqkv, rc, capacity, scale, s.attn, s.act_qs, s.act_d, s.fa_ws, st);
-    if (!moe && has_ffn && !Ly.w_up.qs && D <= kNormFuseMax) {
+    if (norm_fusable(il)) {
       // O product + residual add + the FFN RMSNorm's quantiser and sums of squares; the
       // gate/up product applies 1/rms, SwiGLU and the quantiser for down
       float* x1 = (res == s.xa) ? s.xb : s.xa;
       launch_mmvq_resnorm(Ly.wo, s.act_qs, s.act_d, B, res, D, Ly.ffn_norm, x1, s.actn_qs, s.actn_d, s.ss, st);
       launch_mmvq_swiglu(Ly.w_gate, s.actn_qs, s.actn_d, B, s.act2_qs, s.act2_d, st, s.ss, D, d.rms_eps);
-      launch_mmvq(Ly.w_down, s.act2_qs, s.act2_d, B, s.f, D, st);
-      base = x1;
-      add = s.f;
+      if (il + 1 < L && norm_fusable(il + 1) && m->layers[il + 1].wqkv_pair_rows) {
+        // down product + residual add + the next layer's attention RMSNorm (its QKV input
+        // goes to act, free once the O product has run)
+        float* x2 = (x1 == s.xa) ? s.xb : s.xa;
+        launch_mmvq_resnorm(Ly.w_down, s.act2_qs, s.act2_d, B, x1, D, m->layers[il + 1].attn_norm, x2, s.act_qs,
+                            s.act_d, s.ss, st);
+        base = x2;
+        add = nullptr;
+        prenormed = true;
+      } else {
+        launch_mmvq(Ly.w_down, s.act2_qs, s.act2_d, B, s.f, D, st);
+        base = x1;
+        add = s.f;
+        prenormed = false;
+      }
       continue;
     }
+    prenormed = false;
     launch_mmvq(Ly.wo, s.act_qs, s.act_d, B, s.o, D, st);
     if (!has_ffn) {
       base = res;
