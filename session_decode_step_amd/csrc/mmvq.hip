@@ -37,6 +37,9 @@ namespace kd {
 #ifndef KD_MMVQ_DEPTH_RG
 #define KD_MMVQ_DEPTH_RG 2  // ring depth when a workgroup streams several row groups
 #endif
+#ifndef KD_MMVQ_DEPTH_RN
+#define KD_MMVQ_DEPTH_RN 2  // ring depth of the add + RMSNorm products (two row groups)
+#endif
 #ifndef KD_MMVQ_TILE_FENCE
 #define KD_MMVQ_TILE_FENCE 1
 #endif
@@ -188,6 +191,11 @@ __device__ __forceinline__ float norm_inv(const MmvqArgs& a, const float (&v)[kN
   return 1.0f / sqrtf(s / (float)a.norm_n + a.norm_eps);
 }
 
+// Batch rows on the MFMA operand: operand row i (accumulator slot s = i % 4 of lane group
+// i / 4) holds activation row (i / 4) + 4 (i % 4), so B rows fill slots 0 .. ceil(B/4) - 1 of
+// every lane group and the fp32 epilogue runs ceil(B/4) slots instead of min(B, 4).
+__device__ __forceinline__ int mfma_row_b(int i) { return (i >> 2) + 4 * (i & 3); }
+
 __device__ __forceinline__ float f4_get(const float4& v, int j) {
   return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
 }
@@ -262,7 +270,10 @@ __host__ __device__ constexpr int mmvq_wave_lds(int QW, int RG) { return 16 * QW
 template <int FMT, int QW, int NS, int RG, int EPI, bool DEBUG>
 __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
   constexpr int NT = RG * QW;
-  constexpr int D0 = RG > 1 ? KD_MMVQ_DEPTH_RG : FMT == KD_FMT_Q8_0 ? KD_MMVQ_DEPTH_Q8 : KD_MMVQ_DEPTH_Q4;
+  constexpr int D0 = EPI == EPI_RESNORM ? KD_MMVQ_DEPTH_RN
+                     : RG > 1             ? KD_MMVQ_DEPTH_RG
+                     : FMT == KD_FMT_Q8_0 ? KD_MMVQ_DEPTH_Q8
+                                          : KD_MMVQ_DEPTH_Q4;
   constexpr int D = D0 < NT ? D0 : NT;
   const int e = blockIdx.y;
   int nrows = a.B;
@@ -289,8 +300,10 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.xq, a.x_bytes);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.xd, a.xd_bytes);
   const uint32_t gtile = (uint32_t)((size_t)e * (size_t)a.w_group_tiles);
-  // A operand of lane n: activation row n (rows past the live rows read zeros)
-  const uint32_t a_off = (n < nrows) ? (uint32_t)(act_row ? act_row[n] : n) * (uint32_t)NQ * 128u + g * 32 : kOOB;
+  // A operand of lane n: operand row n = activation row mfma_row_b(n) (rows past the live
+  // rows read zeros)
+  const int bn = mfma_row_b(n);
+  const uint32_t a_off = (bn < nrows) ? (uint32_t)(act_row ? act_row[bn] : bn) * (uint32_t)NQ * 128u + g * 32 : kOOB;
 
   char* slice = reinterpret_cast<char*>(smem) + (size_t)w * mmvq_wave_lds(QW, RG);
   float* dxw = reinterpret_cast<float*>(slice);  // [16][QW] float4
@@ -298,13 +311,13 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
 
   // ---- fetches shared by the wave's tiles, in the order they are consumed (loads complete in
   // issue order): activation scales, weight scales
-  // activation scales: rows 0..15 x quads [q0, q0 + QW), float4 per (row, quad); lane l
-  // fetches (row l/4, quads (l%4) + 4i)
+  // activation scales: operand rows 0..15 x quads [q0, q0 + QW), float4 per (row, quad);
+  // lane l fetches (operand row l/4, quads (l%4) + 4i)
   constexpr int NDX = (QW + 3) / 4;
   int4 dxv[NDX];
   if (!DEBUG) {
-    const int r = lane >> 2, p = lane & 3;
-    const uint32_t row_base = (r < nrows) ? (uint32_t)(act_row ? act_row[r] : r) * (uint32_t)NQ * 16u : kOOB;
+    const int r = lane >> 2, p = lane & 3, br = mfma_row_b(r);
+    const uint32_t row_base = (br < nrows) ? (uint32_t)(act_row ? act_row[br] : br) * (uint32_t)NQ * 16u : kOOB;
 #pragma unroll
     for (int i = 0; i < NDX; ++i) {
       const int q = q0 + 4 * i + p;
@@ -388,7 +401,7 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
         const int row = (rg0 + r) * 16 + n;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const int b = 4 * g + s;
+          const int b = g + 4 * s;
           if (live && b < nrows && row < a.n_out && blk < a.kblocks)
             a.debug_S[((size_t)b * a.n_out + row) * a.kblocks + blk] = S[s];
         }
@@ -426,7 +439,7 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
       const int r = t >> 8, s = (t >> 6) & 3, l = t & 63;
       float v = red[(r * 4 + s) * 64 + l];
       for (int ww = 1; ww < nw; ++ww) v += red[((ww * RG + r) * 4 + s) * 64 + l];  // fixed wave order
-      const int b = 4 * (l >> 4) + s;
+      const int b = (l >> 4) + 4 * s;
       const int row = (rg0 + r) * 16 + (l & 15);
       if (b < nrows && row < a.n_out) {
         const int orow = out_row ? out_row[b] : b;
@@ -445,7 +458,7 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
     const int r = t >> 8, s = (t >> 6) & 3, l = t & 63;
     float v = red[(r * 4 + s) * 64 + l];
     for (int ww = 1; ww < nw; ++ww) v += red[((ww * RG + r) * 4 + s) * 64 + l];  // fixed wave order
-    outv[(r * 16 + (l & 15)) * 16 + 4 * (l >> 4) + s] = v;
+    outv[(r * 16 + (l & 15)) * 16 + (l >> 4) + 4 * s] = v;
   }
   __syncthreads();
   // 8 lanes per (activation row, 32-element block); the loop steps by whole waves, so the 8
@@ -571,9 +584,9 @@ static void launch_mmvq_qn(const MmvqArgs& a, int n_groups, hipStream_t st) {
 
 template <int FMT, int QW, int RG, int EPI>
 static void launch_mmvq_q(const MmvqArgs& a, int n_groups, hipStream_t st) {
-  // epilogue slots: a function of B (rows past B are never written, so dropping their
-  // slots leaves every live output's operation sequence unchanged)
-  const int ns = a.count ? 4 : (a.B < 4 ? a.B : 4);
+  // epilogue slots: ceil(B / 4), a function of B (rows past B are never written, so
+  // dropping their slots leaves every live output's operation sequence unchanged)
+  const int ns = a.count ? 4 : (a.B + 3) / 4;
   switch (ns) {
     case 1: return launch_mmvq_qn<FMT, QW, 1, RG, EPI>(a, n_groups, st);
     case 2: return launch_mmvq_qn<FMT, QW, 2, RG, EPI>(a, n_groups, st);
