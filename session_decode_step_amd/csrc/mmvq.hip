@@ -251,8 +251,8 @@ __device__ __forceinline__ void wstage_load(WStage<FMT>& st, __amdgpu_buffer_rsr
 }
 
 // LDS slice of one wave (bytes): activation scales [16][QW] float4 and weight scales
-// [RG][QW] x 128 B.
-__host__ __device__ constexpr int mmvq_wave_lds(int QW, int RG) { return 16 * QW * 16 + RG * QW * 128; }
+// [RG][QW][16 columns] float4, converted to fp32 once when staged.
+__host__ __device__ constexpr int mmvq_wave_lds(int QW, int RG) { return 16 * QW * 16 + RG * QW * 256; }
 
 // grid (ceil(NR / RG), n_groups); block = nw waves.  A workgroup owns RG consecutive row
 // groups.  Wave w owns quads [q0, q1) = [w*QW, min(NQ, w*QW + QW)) of every one of them (a
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
 
   char* slice = reinterpret_cast<char*>(smem) + (size_t)w * mmvq_wave_lds(QW, RG);
   float* dxw = reinterpret_cast<float*>(slice);  // [16][QW] float4
-  char* dww = slice + 16 * QW * 16;              // [RG][QW] x 128 B
+  char* dww = slice + 16 * QW * 16;              // [RG][QW][16 columns] float4 (fp32 scales)
 
   // ---- fetches shared by the wave's tiles, in the order they are consumed (loads complete in
   // issue order): activation scales, weight scales
@@ -368,7 +368,10 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
 #pragma unroll
     for (int i = 0; i < NDW; ++i) {
       const int j = 4 * i + (lane >> 4);
-      if (j < QW) *reinterpret_cast<uint2*>(dww + (r * QW + j) * 128 + (lane & 15) * 8) = dwv[r][i];
+      if (j < QW)
+        *reinterpret_cast<float4*>(dww + ((r * QW + j) * 16 + (lane & 15)) * 16) =
+            make_float4(half_bits(dwv[r][i].x, 0), half_bits(dwv[r][i].x, 1), half_bits(dwv[r][i].y, 0),
+                        half_bits(dwv[r][i].y, 1));
     }
 
   // ---- the stream, fully unrolled (no loop back-edge, so every wait is exact): tile t =
@@ -386,13 +389,13 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
     WStage<FMT>& cur = st[t % D];
     const int q = q0 + j;
     const bool live = q < q1;
-    const float zsc = live ? 1.0f : 0.0f;
     if (!DEBUG && r == 0) {
 #pragma unroll
       for (int s = 0; s < NS; ++s) dx[s] = *reinterpret_cast<const float4*>(dxw + ((4 * g + s) * QW + j) * 4);
     }
     const int4 A0 = ax0[j & 1], A1 = ax1[j & 1];
-    const uint2 dw = *reinterpret_cast<const uint2*>(dww + (r * QW + j) * 128 + n * 8);
+    // tiles past the wave's quads have zero weight and activation scales: they add exact zeros
+    const float4 dw = *reinterpret_cast<const float4*>(dww + ((r * QW + j) * 16 + n) * 16);
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb) {
       const v4i S = block_dots<FMT>(act_op(A0, A1, jb), w_op<FMT>(cur.w0, cur.w1, jb));
@@ -406,7 +409,7 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
             a.debug_S[((size_t)b * a.n_out + row) * a.kblocks + blk] = S[s];
         }
       } else {
-        const float dwj = zsc * half_bits(jb < 2 ? dw.x : dw.y, jb & 1);
+        const float dwj = f4_get(dw, jb);
 #pragma unroll
         for (int s = 0; s < NS; ++s) acc[r][s] = fmaf(dwj * f4_get(dx[s], jb), (float)S[s], acc[r][s]);
       }
