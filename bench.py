@@ -67,6 +67,27 @@ def summarize_trace(path: str) -> None:
         durs = [d for _, _, d in seq[i:j + 1]]
         print(f"\nlongest back-to-back run: {n} dispatches of {seq[i][1][0]} grid {seq[i][1][1]}: "
               f"avg {sum(durs) / n / 1e3:.2f} us (min {min(durs) / 1e3:.2f}, max {max(durs) / 1e3:.2f})")
+    # the fa_decode timing loop: back-to-back (split, combine) pairs of one shape
+    best, i = (0, 0), 0
+    while i + 1 < len(seq):
+        a, b = seq[i][1], seq[i + 1][1]
+        if "fa_split_kernel" in a[0] and "fa_combine_kernel" in b[0]:
+            j = i
+            while j + 3 < len(seq) and seq[j + 2][1] == a and seq[j + 3][1] == b:
+                j += 2
+            if (j - i) // 2 + 1 > best[0]:
+                best = ((j - i) // 2 + 1, i)
+            i = j + 2
+        else:
+            i += 1
+    n, i = best
+    if n > 1:
+        sp = [seq[i + 2 * m][2] for m in range(n)]
+        cb = [seq[i + 2 * m + 1][2] for m in range(n)]
+        pr = [x + y for x, y in zip(sp, cb)]
+        print(f"longest back-to-back fa_decode run: {n} (split, combine) pairs, split grid {seq[i][1][1]}: "
+              f"split avg {sum(sp) / n / 1e3:.2f} us + combine avg {sum(cb) / n / 1e3:.2f} us = "
+              f"{sum(pr) / n / 1e3:.2f} us per call (min {min(pr) / 1e3:.2f}, max {max(pr) / 1e3:.2f})")
 
 
 def log(msg: str) -> None:
@@ -98,15 +119,34 @@ def time_rotating(launch, iters: int, stream) -> float:
 
 
 # ---------------------------------------------------------------------- HBM traffic (PMC)
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mmvq_q4_0_28672x4096_b8.txt")
-TRAFFIC_SOURCES = ("session_decode_step_amd/csrc/mmvq.hip", "session_decode_step_amd/csrc/kd_internal.h")
 CALIB_BYTES = 512 << 20
+FA_B, FA_T, FA_CAP = 8, 4113, 4128          # fa_decode traffic case: B rows of t keys
+MM_N, MM_K, MM_B = 28672, 4096, 8           # gate/up product traffic case
 
 
-def kernel_source_hash() -> str:
+def fa_algorithmic_bytes(t_kv, G: int, H: int, hd: int) -> int:
+    """fa_decode: each row's K and V (fp16) once, q in and the output out (fp32)."""
+    return sum(t_kv) * G * hd * 2 * 2 + 2 * len(t_kv) * H * hd * 4
+
+
+TRAFFIC = {
+    "fa": {"file": os.path.join(ROOT, "profiles", "traffic_fa_decode_b8_t4113.txt"),
+           "sources": ("session_decode_step_amd/csrc/attn.hip", "session_decode_step_amd/csrc/kd_internal.h"),
+           "kernels": ("fa_split_kernel", "fa_combine_kernel"),
+           "title": "fa_decode (fa_split_kernel + fa_combine_kernel), B=8 rows of t=4113 keys, H=32, G=8, hd=128",
+           "algorithmic": lambda: fa_algorithmic_bytes([FA_T] * FA_B, 8, 32, 128)},
+    "mmvq": {"file": os.path.join(ROOT, "profiles", "traffic_mmvq_q4_0_28672x4096_b8.txt"),
+             "sources": ("session_decode_step_amd/csrc/mmvq.hip", "session_decode_step_amd/csrc/kd_internal.h"),
+             "kernels": ("mmvq_kernel",),
+             "title": "mmvq_kernel<Q4_0> with the SwiGLU epilogue, gate/up 28672 x 4096, B=8",
+             "algorithmic": lambda: mmvq_algorithmic_bytes(MM_N, MM_K, MM_B)},
+}
+
+
+def kernel_source_hash(kind: str) -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in TRAFFIC_SOURCES:
+    for f in TRAFFIC[kind]["sources"]:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -114,8 +154,9 @@ def kernel_source_hash() -> str:
 
 def traffic_probe() -> None:
     """Launches for the two ``rocprofv3 --pmc`` passes: a plain fp32 elementwise copy of
-    512 MiB (the calibration kernel: reads and writes 512 MiB), then the gate/up mmvq with
-    its SwiGLU epilogue at B=8 on four distinct matrices."""
+    512 MiB (the calibration kernel: reads and writes 512 MiB), then 8 launches of the gate/up
+    mmvq with its SwiGLU epilogue at B=8 over four distinct matrices, then 8 fa_decode calls
+    at B=8 over two distinct sets of caches."""
     import torch
     import workload as W
     import session_decode_step_amd as kd
@@ -125,19 +166,30 @@ def traffic_probe() -> None:
     for _ in range(2):
         torch.mul(src, 1.0, out=dst)
     torch.cuda.synchronize()
-    n, k, B = 28672, 4096, 8
-    mats = [kd.kd_pack_weight(W.draw_weight("q4_0", 0, 4, 90, 91, i, n, k)) for i in range(4)]
-    act = kd.kd_quantize_act_q8(torch.randn((B, k), device="cuda"))
-    h_act = kd.alloc_act(B, n // 2)
+    del src, dst
+    mats = [kd.kd_pack_weight(W.draw_weight("q4_0", 0, 4, 90, 91, i, MM_N, MM_K)) for i in range(4)]
+    act = kd.kd_quantize_act_q8(torch.randn((MM_B, MM_K), device="cuda"))
+    h_act = kd.alloc_act(MM_B, MM_N // 2)
     for i in range(8):
-        kd.kd_mmvq_swiglu(mats[i % 4], act, B, h_act)
+        kd.kd_mmvq_swiglu(mats[i % 4], act, MM_B, h_act)
+    torch.cuda.synchronize()
+    H, G, hd = 32, 8, 128
+    sets = [torch.empty((FA_B, 2, G, FA_CAP, hd), dtype=torch.float16, device="cuda").fill_(0.01) for _ in range(2)]
+    t_kv = [FA_T] * FA_B
+    q = torch.randn((FA_B, H, hd), device="cuda")
+    ws = torch.empty(kd.kd_fa_decode_workspace(FA_B, H, hd, t_kv), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    for i in range(8):
+        c = sets[i % 2]
+        kd.kd_fa_decode_ragged(q, G, [c[b, 0].data_ptr() for b in range(FA_B)], [c[b, 1].data_ptr() for b in range(FA_B)],
+                               t_kv, FA_CAP, hd ** -0.5, ws=ws, out=out)
     torch.cuda.synchronize()
     log("traffic probe done")
 
 
 def _read_counters(path: str):
-    """{dispatch: (kernel_name, counter_value)} from a rocprofv3 counter_collection CSV (or
-    the directory holding it)."""
+    """[(dispatch, kernel_name, counter_value)] in dispatch order from a rocprofv3
+    counter_collection CSV (or the directory holding it)."""
     import csv
     import glob
     if os.path.isdir(path):
@@ -148,67 +200,76 @@ def _read_counters(path: str):
     out = {}
     with open(path) as f:
         for row in csv.DictReader(f):
-            key = row.get("Dispatch_Id") or row.get("Correlation_Id")
+            key = int(row.get("Dispatch_Id") or row.get("Correlation_Id"))
             name = row.get("Kernel_Name", "?")
             val = float(row["Counter_Value"])
             prev = out.get(key, (name, 0.0))
             out[key] = (name, prev[1] + val)
-    return out
+    return [(k, nm, v) for k, (nm, v) in sorted(out.items())]
 
 
 def traffic_summarize(fetch: str, write: str, fetch_cmd: str, write_cmd: str) -> None:
-    """Per-dispatch HBM bytes of the mmvq launches from the FETCH_SIZE and WRITE_SIZE passes
+    """HBM bytes per launch of the measured kernels from the FETCH_SIZE and WRITE_SIZE passes
     (KiB per dispatch), each scaled by what the counter reads for the 512 MiB calibration
-    copy; writes the profile summary that the bench reads back."""
-    res = {}
-    for tag, path in (("fetch", fetch), ("write", write)):
-        rows = _read_counters(path)
-        calib = max((v for nm, v in rows.values() if "mmvq" not in nm), default=0.0)
-        mm = [v for nm, v in rows.values() if "mmvq_kernel" in nm]
-        if not calib or not mm:
-            raise SystemExit(f"{tag}: calibration or mmvq dispatches missing in {path}")
-        factor = CALIB_BYTES / (calib * 1024.0)
-        res[tag] = {"calib_kib": calib, "factor": factor, "mmvq_kib": mm,
-                    "bytes": sum(mm) / len(mm) * 1024.0 * factor}
-    n, k, B = 28672, 4096, 8
-    alg = mmvq_algorithmic_bytes(n, k, B)
-    total = res["fetch"]["bytes"] + res["write"]["bytes"]
-    rec = {"kernel": "mmvq_kernel<Q4_0, SwiGLU epilogue> 28672x4096 B=8", "source_hash": kernel_source_hash(),
-           "fetch_bytes": round(res["fetch"]["bytes"]), "write_bytes": round(res["write"]["bytes"]),
-           "traffic_bytes": round(total), "algorithmic_bytes": alg, "traffic_over_algorithmic": round(total / alg, 4),
-           "fetch_factor": round(res["fetch"]["factor"], 5), "write_factor": round(res["write"]["factor"], 5)}
-    lines = [
-        "HBM traffic of mmvq_kernel<Q4_0> with the SwiGLU epilogue, gate/up 28672 x 4096, B=8 (rocprofv3 PMC, MI355X)",
-        "",
-        f"FETCH_SIZE pass: {fetch_cmd}",
-        f"WRITE_SIZE pass: {write_cmd}",
-        f"summary: python bench.py --traffic-summarize <fetch dir> <write dir>",
-        "",
-        f"calibration: torch.mul(x, 1.0, out=y) over {CALIB_BYTES >> 20} MiB fp32 (reads and writes {CALIB_BYTES} B)",
-        f"  FETCH_SIZE {res['fetch']['calib_kib']:.0f} KiB -> factor {res['fetch']['factor']:.5f} B per counted B",
-        f"  WRITE_SIZE {res['write']['calib_kib']:.0f} KiB -> factor {res['write']['factor']:.5f}",
-        f"mmvq dispatches FETCH_SIZE KiB: {', '.join(f'{v:.0f}' for v in res['fetch']['mmvq_kib'])}",
-        f"mmvq dispatches WRITE_SIZE KiB: {', '.join(f'{v:.0f}' for v in res['write']['mmvq_kib'])}",
-        f"per launch: fetch {rec['fetch_bytes']} B + write {rec['write_bytes']} B = {rec['traffic_bytes']} B; "
-        f"algorithmic {alg} B; ratio {rec['traffic_over_algorithmic']}",
-        "",
-        "TRAFFIC_JSON " + json.dumps(rec),
-    ]
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    with open(TRAFFIC_FILE, "w") as f:
-        f.write("\n".join(lines) + "\n")
-    print("\n".join(lines))
+    copy; writes one profile summary per kernel, which the bench reads back.  A call of
+    several kernels (fa_decode: split + combine) counts the mean of each kernel once."""
+    rows = {tag: _read_counters(path) for tag, path in (("fetch", fetch), ("write", write))}
+    factor, calib_kib = {}, {}
+    for tag, rr in rows.items():
+        calib = max((v for _, nm, v in rr if "MulFunctor" in nm), default=0.0)
+        if not calib:
+            raise SystemExit(f"{tag}: calibration dispatch missing")
+        calib_kib[tag], factor[tag] = calib, CALIB_BYTES / (calib * 1024.0)
+    for kind, spec in TRAFFIC.items():
+        per = {}
+        for tag, rr in rows.items():
+            per[tag] = {kn: [v for _, nm, v in rr if kn in nm] for kn in spec["kernels"]}
+            if not all(per[tag].values()):
+                raise SystemExit(f"{tag}: {kind} dispatches missing")
+        byts = {tag: sum(sum(v) / len(v) for v in per[tag].values()) * 1024.0 * factor[tag] for tag in per}
+        alg = spec["algorithmic"]()
+        total = byts["fetch"] + byts["write"]
+        rec = {"kernel": spec["title"], "source_hash": kernel_source_hash(kind),
+               "fetch_bytes": round(byts["fetch"]), "write_bytes": round(byts["write"]),
+               "traffic_bytes": round(total), "algorithmic_bytes": alg,
+               "traffic_over_algorithmic": round(total / alg, 4),
+               "fetch_factor": round(factor["fetch"], 5), "write_factor": round(factor["write"], 5)}
+        lines = [
+            f"HBM traffic of {spec['title']} (rocprofv3 PMC, MI355X)",
+            "",
+            f"FETCH_SIZE pass: {fetch_cmd}",
+            f"WRITE_SIZE pass: {write_cmd}",
+            "summary: python bench.py --traffic-summarize <fetch dir> <write dir>",
+            "",
+            f"calibration: torch.mul(x, 1.0, out=y) over {CALIB_BYTES >> 20} MiB fp32 (reads and writes {CALIB_BYTES} B)",
+            f"  FETCH_SIZE {calib_kib['fetch']:.0f} KiB -> factor {factor['fetch']:.5f} B per counted B",
+            f"  WRITE_SIZE {calib_kib['write']:.0f} KiB -> factor {factor['write']:.5f}",
+        ]
+        for tag in ("fetch", "write"):
+            for kn, vals in per[tag].items():
+                lines.append(f"{kn} dispatches {tag.upper()}_SIZE KiB: {', '.join(f'{v:.0f}' for v in vals)}")
+        lines += [
+            f"per launch: fetch {rec['fetch_bytes']} B + write {rec['write_bytes']} B = {rec['traffic_bytes']} B; "
+            f"algorithmic {alg} B; ratio {rec['traffic_over_algorithmic']}",
+            "",
+            "TRAFFIC_JSON " + json.dumps(rec),
+        ]
+        os.makedirs(os.path.dirname(spec["file"]), exist_ok=True)
+        with open(spec["file"], "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print("\n".join(lines) + "\n")
 
 
-def load_traffic(n: int, k: int, B: int):
-    """Measured HBM bytes per launch of the dominant kernel, or None when no measurement
-    exists for this shape or the kernel source has changed since it was taken."""
-    if (n, k, B) != (28672, 4096, 8) or not os.path.exists(TRAFFIC_FILE):
+def load_traffic(kind: str):
+    """Measured HBM bytes per launch of a kernel, or None when no measurement exists or the
+    kernel source has changed since it was taken."""
+    path = TRAFFIC[kind]["file"]
+    if not os.path.exists(path):
         return None
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if line.startswith("TRAFFIC_JSON "):
             rec = json.loads(line[len("TRAFFIC_JSON "):])
-            if rec.get("source_hash") == kernel_source_hash():
+            if rec.get("source_hash") == kernel_source_hash(kind):
                 return rec["traffic_bytes"]
     return None
 
@@ -300,13 +361,13 @@ def main() -> None:
     for B in widths:
         sweep[B]["step_GBs"] = step_bytes(B, mid) / (sweep[B]["ms_per_step"] / 1e3) / 1e9
 
-    # ---------------------------------------------------------------- dominant kernel: mmvq
+    # ---------------------------------------------------------------- the largest product
     # the FFN's interleaved gate/up product (28672 x 4096 Q4_0) with its SwiGLU + quantiser
-    # epilogue, at the headline width: 32 of the step's launches and 54% of its weight bytes.
-    # Launches rotate over the 32 layers' own matrices (2.1 GB, well above the 256 MB
-    # Infinity Cache), as inside a step.
+    # epilogue, at the headline width: 54% of the step's weight bytes.  Launches rotate over
+    # the 32 layers' own matrices (2.1 GB, well above the 256 MB Infinity Cache), as inside
+    # a step.
     B = Bh
-    log(f"dominant kernel: gate/up mmvq with SwiGLU epilogue at B={B}")
+    log(f"gate/up mmvq with SwiGLU epilogue at B={B}")
     mats = [gw.km.packed[il]["w_gateup"] for il in range(L)]
     xin = torch.randn((B, sp.d), device="cuda", generator=torch.Generator(device="cuda").manual_seed(0))
     act = kd.kd_quantize_act_q8(xin)
@@ -316,9 +377,11 @@ def main() -> None:
     n, k = mats[0].n_out, mats[0].k
     mm_bytes = mmvq_algorithmic_bytes(n, k, B)
     mm_gbs = mm_bytes / (mm_us * 1e-6) / 1e9
-    traffic = load_traffic(n, k, B)
+    mm_traffic = load_traffic("mmvq") if (n, k, B) == (MM_N, MM_K, MM_B) else None
 
-    # ---------------------------------------------------------------- fa_decode at B = 8
+    # ---------------------------------------------------------------- dominant kernel: fa_decode
+    # the split kernel and its combine: the largest share of the step's time (~40% at B = 8).
+    # Calls rotate over the 32 layers' caches (135 MB of KV per call), as inside a step.
     log(f"fa_decode at B={B}")
     t_kv = [p + 1 for p in wl.positions(mid)[:B]]
     q = torch.randn((B, sp.n_head, hd), device="cuda", generator=torch.Generator(device="cuda").manual_seed(1))
@@ -329,8 +392,9 @@ def main() -> None:
     fa_us = time_rotating(lambda i: kd.kd_fa_decode_ragged(q, G, kbl[i % L], vbl[i % L], t_kv, wl.capacity,
                                                            hd ** -0.5, ws=fa_ws, out=fa_out, stream=stream),
                           args.kernel_iters, stream)
-    fa_bytes = sum(t_kv) * G * hd * 2 * 2 + 2 * B * sp.n_head * hd * 4
+    fa_bytes = fa_algorithmic_bytes(t_kv, G, sp.n_head, hd)
     fa_gbs = fa_bytes / (fa_us * 1e-6) / 1e9
+    fa_traffic = load_traffic("fa") if t_kv == [FA_T] * FA_B else None
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
@@ -379,14 +443,14 @@ def main() -> None:
         "sweep": {str(b): {kk: round(v, 3) for kk, v in sweep[b].items()} for b in widths},
         "step_GBs": round(top["step_GBs"], 1),
         "step_frac_of_peak": round(top["step_GBs"] / HBM_PEAK_GBS, 4),
-        "roofline": {"bound": "hbm", "kernel": "mmvq_kernel<Q4_0, SwiGLU epilogue> 28672x4096 (gate/up) at B=%d" % Bh,
-                     "achieved": round(mm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(mm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "avg_launch_us": round(mm_us, 3), "algorithmic_bytes": int(mm_bytes)},
-        "fa_roofline": {"bound": "hbm", "kernel": "fa_split_kernel + fa_combine_kernel, B=%d, t_kv=%d" % (B, t_kv[0]),
-                        "achieved": round(fa_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": round(fa_gbs / HBM_PEAK_GBS, 4), "avg_launch_us": round(fa_us, 3),
-                        "algorithmic_bytes": int(fa_bytes)},
+        "roofline": {"bound": "hbm", "achieved": round(fa_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(fa_gbs / HBM_PEAK_GBS, 4), "traffic": fa_traffic,
+                     "kernel": "fa_decode: fa_split_kernel + fa_combine_kernel, B=%d, t_kv=%d" % (B, t_kv[0]),
+                     "avg_launch_us": round(fa_us, 3), "algorithmic_bytes": int(fa_bytes)},
+        "mmvq_roofline": {"bound": "hbm", "achieved": round(mm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(mm_gbs / HBM_PEAK_GBS, 4), "traffic": mm_traffic,
+                          "kernel": "mmvq_kernel<Q4_0, SwiGLU epilogue> 28672x4096 (gate/up) at B=%d" % Bh,
+                          "avg_launch_us": round(mm_us, 3), "algorithmic_bytes": int(mm_bytes)},
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),
     }
