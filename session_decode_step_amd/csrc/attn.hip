@@ -86,7 +86,10 @@ __device__ __forceinline__ void split_f16(float x, _Float16& hi, _Float16& lo) {
   lo = (_Float16)(x - (float)hi);
 }
 
-template <int R, int HD>
+// MULTI: chunks may span several 128-key tiles (rows longer than 128 x 128 keys).  Without
+// it the tile loop runs once, so the running output is not live across a tile's loads and
+// the kernel needs fewer registers (more workgroups per CU); the operations are the same.
+template <int R, int HD, bool MULTI>
 __global__ __launch_bounds__(64 * kFaWaves) void fa_split_kernel(FaPlan p, const float* __restrict__ q,
                                                                           int ldq, RowCaches rc, int capacity,
                                                                           float scale, float* __restrict__ ws) {
@@ -140,7 +143,7 @@ __global__ __launch_bounds__(64 * kFaWaves) void fa_split_kernel(FaPlan p, const
 #pragma unroll
   for (int m = 0; m < 8; ++m) o[m] = fa_v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  for (int t0 = 0, par = 0; t0 < nk; t0 += TK, par ^= 1) {
+  for (int t0 = 0, par = 0; t0 < (MULTI ? nk : 1); t0 += TK, par ^= 1) {
     const int wk = t0 + 16 * w;  // this wave's first key within the chunk
     // K: slice j -> key wk + n, dims 32j + 8gq (16 bytes)
     const uint32_t kb = ((uint32_t)(k0 + wk + n) * HD + 8 * gq) * 2;
@@ -380,8 +383,14 @@ __global__ __launch_bounds__(HD) void fa_combine_kernel(FaPlan p, const float* _
 template <int R, int HD>
 static void launch_fa_t(const FaPlan& p, const float* q, int ldq, const RowCaches& rc, int capacity, float scale,
                         float* out, int8_t* oq, float* od, void* ws, hipStream_t st) {
-  fa_split_kernel<R, HD><<<dim3(p.n_items, p.G), 64 * kFaWaves, 0, st>>>(p, q, ldq, rc, capacity, scale,
-                                                                        static_cast<float*>(ws));
+  int cmax = 0;
+  for (int b = 0; b < p.B; ++b) cmax = p.chunk[b] > cmax ? p.chunk[b] : cmax;
+  if (cmax > 16 * kFaWaves)
+    fa_split_kernel<R, HD, true><<<dim3(p.n_items, p.G), 64 * kFaWaves, 0, st>>>(p, q, ldq, rc, capacity, scale,
+                                                                                static_cast<float*>(ws));
+  else
+    fa_split_kernel<R, HD, false><<<dim3(p.n_items, p.G), 64 * kFaWaves, 0, st>>>(p, q, ldq, rc, capacity, scale,
+                                                                                 static_cast<float*>(ws));
   fa_combine_kernel<HD><<<dim3(p.H, p.B), HD, 0, st>>>(p, static_cast<const float*>(ws), out, oq, od);
 }
 

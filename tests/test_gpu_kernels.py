@@ -204,6 +204,28 @@ def test_fa_decode_ragged_vs_oracle(H, G, hd):
         assert_close_rows(oc.reshape(B, -1), out.reshape(B, -1), tol, f"fa chunk={chunk}")
 
 
+def test_fa_row_bits_independent_of_the_split_kernel_variant():
+    """A batch holding a row longer than 128 x 128 keys runs the multi-tile split kernel for
+    every row; a short row stepped alone runs the single-tile one.  Its output bits agree."""
+    say("fa single/multi-tile variants")
+    H, G, hd = 32, 8, 128
+    t_kv = [4113, 20000, 129]
+    B, cap = len(t_kv), 20008
+    r = np.random.default_rng(7)
+    caches = _caches(B, G, cap, hd)
+    for b in range(B):
+        caches[b][0].copy_(torch.from_numpy(r.standard_normal((G, cap, hd)).astype(np.float16)))
+        caches[b][1].copy_(torch.from_numpy(r.standard_normal((G, cap, hd)).astype(np.float16)))
+    q = (r.standard_normal((B, H, hd)) * 0.5).astype(np.float32)
+    kb = [c[0].data_ptr() for c in caches]
+    vb = [c[1].data_ptr() for c in caches]
+    scale = 1.0 / math.sqrt(hd)
+    out = kd.kd_fa_decode_ragged(dev(q), G, kb, vb, t_kv, cap, scale).cpu().numpy()
+    for b in (0, 2):
+        o1 = kd.kd_fa_decode_ragged(dev(q[b:b + 1]), G, kb[b:b + 1], vb[b:b + 1], t_kv[b:b + 1], cap, scale)
+        np.testing.assert_array_equal(o1.cpu().numpy()[0].view(np.uint32), out[b].view(np.uint32))
+
+
 # ------------------------------------------------------------------ products with fused epilogues
 @pytest.mark.parametrize("fmt,F,k,B", [("q4_0", 1024, 512, 8), ("q8_0", 704, 256, 5), ("q4_0", 2048, 4096, 16),
                                        ("q4_0", 352, 704, 1)])
