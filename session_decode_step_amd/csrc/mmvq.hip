@@ -32,19 +32,28 @@ namespace kd {
 #define KD_MMVQ_DEPTH_Q8 2
 #endif
 #ifndef KD_MMVQ_WAVE_QUADS
-#define KD_MMVQ_WAVE_QUADS 4
+#define KD_MMVQ_WAVE_QUADS 8
 #endif
 #ifndef KD_MMVQ_DEPTH_RG
-#define KD_MMVQ_DEPTH_RG 2  // ring depth when a workgroup streams several row groups
+#define KD_MMVQ_DEPTH_RG 4  // ring depth when a workgroup streams several row groups
 #endif
 #ifndef KD_MMVQ_DEPTH_RN
-#define KD_MMVQ_DEPTH_RN 2  // ring depth of the add + RMSNorm products (two row groups)
+#define KD_MMVQ_DEPTH_RN 4  // ring depth of the add + RMSNorm products (two row groups)
 #endif
 #ifndef KD_MMVQ_TILE_FENCE
 #define KD_MMVQ_TILE_FENCE 1
 #endif
 #ifndef KD_MMVQ_RG
 #define KD_MMVQ_RG 1  // row groups per workgroup (they share the activation operands)
+#endif
+#ifndef KD_MMVQ_QW_SWIGLU
+#define KD_MMVQ_QW_SWIGLU KD_MMVQ_WAVE_QUADS  // quads per wave of the gate/up product
+#endif
+#ifndef KD_MMVQ_QW_ROPE
+#define KD_MMVQ_QW_ROPE KD_MMVQ_WAVE_QUADS  // quads per wave of the QKV product
+#endif
+#ifndef KD_MMVQ_QW_RN
+#define KD_MMVQ_QW_RN 2  // quads per wave of the add + RMSNorm products
 #endif
 
 
@@ -663,6 +672,7 @@ void launch_mmvq_swiglu(const kd_weight& W, const int8_t* xq, const float* xd, i
   a.norm_ss = norm_ss;
   a.norm_n = norm_n;
   a.norm_eps = norm_eps;
+  a.QW = mmvq_qw(a.NQ, KD_MMVQ_QW_SWIGLU);
   launch_mmvq_fmt<4, EPI_SWIGLU>(W, a, 1, st);
 }
 
@@ -671,7 +681,7 @@ void launch_mmvq_swiglu(const kd_weight& W, const int8_t* xq, const float* xd, i
 void launch_mmvq_resnorm(const kd_weight& W, const int8_t* xq, const float* xd, int B, const float* res, int ld,
                          const float* gain, float* x1, int8_t* out_qs, float* out_d, float* ss, hipStream_t st) {
   MmvqArgs a = mmvq_args(W, xq, xd, B, nullptr, 0, nullptr, nullptr);
-  a.QW = mmvq_qw(a.NQ, 2);
+  a.QW = mmvq_qw(a.NQ, KD_MMVQ_QW_RN);
   a.epi_res = res;
   a.epi_ld = ld;
   a.epi_gain = gain;
@@ -698,6 +708,7 @@ void launch_mmvq_rope(const kd_weight& W, const int8_t* xq, const float* xd, int
   a.epi_cs = cs;
   a.epi_rc = rc;
   a.epi_capacity = capacity;
+  a.QW = mmvq_qw(a.NQ, KD_MMVQ_QW_ROPE);
   launch_mmvq_fmt<1, EPI_ROPE>(W, a, 1, st);
 }
 
