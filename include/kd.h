@@ -234,6 +234,24 @@ kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x_in, const 
                          void* const* k_base, void* const* v_base, int32_t capacity, float* out,
                          void* ws, size_t ws_bytes, void* stream);
 
+/* ---- next token: greedy argmax and embedding gather ----------------------------------- */
+/* Greedy token of each row (memra-engine decode_batch.rs, ``decode_step_batch_sampled``:
+ * the device argmax of each greedy row's logits, equal to the host argmax).  x: device fp32
+ * [B][ldx], the first n entries of each row are its logits.  idx[b] (device int32) = the
+ * lowest j < n with x[b][j] = max_j x[b][j] (ties go to the lower index); val[b] (device fp32,
+ * may be NULL) = that maximum.  NaN entries never win; a row of NaN only gives index 0 and
+ * value NaN.  The result is exact (comparisons only) and each row is independent of the
+ * others.  1 <= B <= 65535, n >= 1, ldx >= n. */
+kd_status kd_argmax_rows(const float* x, int32_t B, int32_t n, int32_t ldx, int32_t* idx, float* val,
+                         void* stream);
+/* The next step's input rows from tokens (memra-engine decode_batch.rs, phase 0 of
+ * ``decode_step_batch``: each row starts from its token's embedding row):
+ * out[b][0:d] = table[tokens[b]][0:d].  table: device fp32 [vocab][d]; tokens: device int32
+ * [B] (e.g. kd_argmax_rows' idx, so the token never visits the host); out: device fp32 [B][ldo].
+ * A token outside [0, vocab) gives a zero row and reads nothing.  1 <= B <= 65535, ldo >= d. */
+kd_status kd_embed_rows(const float* table, int32_t vocab, int32_t d, const int32_t* tokens, int32_t B,
+                        float* out, int32_t ldo, void* stream);
+
 /* ---- test exports ---------------------------------------------------------------------- */
 /* The exact int32 block dot products S[b][n][blk] (b < B, n < n_out, blk < k/32) that the
  * mmvq kernel computes for this matrix and activation (same kernel, epilogue replaced). */

@@ -210,3 +210,32 @@ def router_topk(r: np.ndarray, k: int) -> Tuple[np.ndarray, np.ndarray]:
     p = np.exp(z)
     p /= np.sum(p)
     return ids, p
+
+
+# ---------------------------------------------------------------------------------------
+# Next token
+# ---------------------------------------------------------------------------------------
+def greedy_token(logits: np.ndarray) -> np.ndarray:
+    """Greedy token of each row of ``logits[B, n]``: the lowest index among the row's maxima.
+
+    memra-engine 0.72.0, src/decode_batch.rs, ``decode_step_batch_sampled``: a greedy row
+    takes the argmax of its logits, and the device result equals a host argmax.  The pages
+    give no tie rule; the reading here is the first maximum, which a left-to-right scan that
+    replaces its candidate only on a strictly larger value finds.  Rows are finite.
+    """
+    x = np.asarray(logits)
+    out = np.empty(x.shape[0], dtype=np.int64)
+    for b in range(x.shape[0]):
+        m = np.max(x[b])
+        out[b] = np.flatnonzero(x[b] == m)[0]
+    return out
+
+
+def embed_rows(table: np.ndarray, tokens: np.ndarray) -> np.ndarray:
+    """The next step's input rows: row ``tokens[b]`` of the embedding table ``[vocab, d]``.
+
+    memra-engine 0.72.0, src/decode_batch.rs, phase 0 of ``decode_step_batch``: each row
+    enters the stack as its token's embedding row.
+    """
+    return np.asarray(table)[np.asarray(tokens, dtype=np.int64)].copy()
+

@@ -78,6 +78,8 @@ SIGNATURES = {
     "kd_rope_neox_rows": (_I, [_P, _I, _I, _I, _PI, _F, _P]),
     "kd_swiglu_rows": (_I, [_P, _P, _P, _I, _I, _P]),
     "kd_add_rows": (_I, [_P, _P, _P, _I, _I, _P]),
+    "kd_argmax_rows": (_I, [_P, _I, _I, _I, _P, _P, _P]),
+    "kd_embed_rows": (_I, [_P, _I, _I, _P, _I, _P, _I, _P]),
     "kd_kv_append": (_I, [_P, _P, _I, _I, _I, _PP, _PP, _PI, _I, _P]),
     "kd_fa_decode_workspace": (_S, [_I, _I, _I, _PI]),
     "kd_fa_decode_ragged": (_I, [_P, _I, _I, _I, _I, _PP, _PP, _PI, _I, _F, _P, _P, _S, _P]),
@@ -297,6 +299,30 @@ def kd_add_rows(x: torch.Tensor, y: torch.Tensor, stream=None) -> torch.Tensor:
     _check(lib().kd_add_rows(x.data_ptr(), y.data_ptr(), z.data_ptr(), x.shape[0], x.shape[1], _stream(stream)),
            "kd_add_rows")
     return z
+
+
+# ------------------------------------------------------------------------------ next token
+def kd_argmax_rows(x: torch.Tensor, n: Optional[int] = None, stream=None):
+    """Greedy token of each row of x [B, ldx] over its first n entries: (idx int32 [B],
+    val fp32 [B]) on x's device."""
+    B, ldx = x.shape
+    n = ldx if n is None else n
+    idx = torch.empty(B, dtype=torch.int32, device=x.device)
+    val = torch.empty(B, dtype=torch.float32, device=x.device)
+    _check(lib().kd_argmax_rows(x.data_ptr(), B, n, ldx, idx.data_ptr(), val.data_ptr(), _stream(stream)),
+           "kd_argmax_rows")
+    return idx, val
+
+
+def kd_embed_rows(table: torch.Tensor, tokens: torch.Tensor, out: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """Rows table[tokens[b]] of the fp32 embedding table [vocab, d] (tokens: device int32 [B])."""
+    vocab, d = table.shape
+    B = tokens.shape[0]
+    out = torch.empty((B, d), dtype=torch.float32, device=table.device) if out is None else out
+    _check(lib().kd_embed_rows(table.data_ptr(), vocab, d, tokens.data_ptr(), B, out.data_ptr(), out.stride(0),
+                               _stream(stream)), "kd_embed_rows")
+    return out
 
 
 # ------------------------------------------------------------------------------ KV + attention

@@ -73,11 +73,12 @@ class GpuWorkload:
         return self._x_cache[key]
 
     def step(self, s: int, rows: Optional[Sequence[int]] = None, out: Optional[torch.Tensor] = None,
-             stream=None) -> torch.Tensor:
-        """Run decode step ``s`` for the given row indices (default: all rows)."""
+             stream=None, x: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """Run decode step ``s`` for the given row indices (default: all rows).  ``x``: device
+        input rows [len(rows), d] to use instead of the workload's (e.g. embedded tokens)."""
         wl = self.wl
         rows = list(range(wl.B)) if rows is None else list(rows)
-        x = self._rows_input(s, rows)
+        x = self._rows_input(s, rows) if x is None else x
         pos_all = wl.positions(s)
         pos = [pos_all[b] for b in rows]
         sess = [wl.rows[b][0] for b in rows]

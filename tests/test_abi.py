@@ -135,6 +135,20 @@ def _fake_model(n_layers=2, d=256, H=4, G=2, hd=64, F=512):
     return desc, layers
 
 
+def test_token_validation_before_launch():
+    L = kd.lib()
+    assert L.kd_argmax_rows(0x100, 0, 10, 10, 0x200, None, None) == kd.KD_ERR_UNSUPPORTED
+    assert L.kd_argmax_rows(0x100, 2, 0, 10, 0x200, None, None) == kd.KD_ERR_INVALID
+    assert L.kd_argmax_rows(0x100, 2, 11, 10, 0x200, None, None) == kd.KD_ERR_INVALID    # ldx < n
+    assert b"ldx" in L.kd_last_error()
+    assert L.kd_argmax_rows(None, 2, 10, 10, 0x200, None, None) == kd.KD_ERR_INVALID
+    assert L.kd_argmax_rows(0x100, 2, 10, 10, None, None, None) == kd.KD_ERR_INVALID
+    assert L.kd_embed_rows(0x100, 0, 8, 0x200, 2, 0x300, 8, None) == kd.KD_ERR_INVALID    # vocab
+    assert L.kd_embed_rows(0x100, 4, 8, 0x200, 2, 0x300, 7, None) == kd.KD_ERR_INVALID    # ldo < d
+    assert L.kd_embed_rows(0x100, 4, 8, None, 2, 0x300, 8, None) == kd.KD_ERR_INVALID
+    assert L.kd_embed_rows(0x100, 4, 8, 0x200, 70000, 0x300, 8, None) == kd.KD_ERR_UNSUPPORTED
+
+
 def test_model_create_validation_and_step_errors():
     L = kd.lib()
     desc, layers = _fake_model()

@@ -294,3 +294,46 @@ def test_mmvq_rope_equals_unfused_path(fmt, H, G, hd, B):
     ref = ops.mmvq(w, q, d)
     qref = np.stack([ops.rope_neox(ref[b, :H * hd].reshape(H, hd), pos[b], 10000.0) for b in range(B)])
     assert_close_rows(q_f.cpu().numpy(), qref.reshape(B, -1), 2e-3, "mmvq_rope q")
+
+
+# ------------------------------------------------------------------ next token
+@pytest.mark.parametrize("B,n,ldx", [(1, 1, 1), (5, 33, 40), (16, 32000, 32000), (3, 100003, 100008)])
+def test_argmax_rows_exact(B, n, ldx):
+    """Greedy tokens equal the oracle's (first maximum) on rows with planted ties, -inf rows,
+    denormals and larger values past n in the row stride (ignored); values are the maxima."""
+    say(f"argmax B={B} n={n} ldx={ldx}")
+    r = np.random.default_rng(n + B)
+    x = r.standard_normal((B, ldx)).astype(np.float32)
+    x[:, n:] = 1e30                                              # past the row: never read as logits
+    for b in range(B):
+        if n > 8 and b % 2 == 0:                                 # the maximum planted several times
+            m = np.float32(x[b, :n].max() + 1.0)
+            for j in sorted(r.choice(n, size=min(4, n), replace=False)):
+                x[b, j] = m
+    if B > 1 and n > 3:
+        x[1, :n] = -np.inf
+        x[1, n - 1] = -np.inf
+    if B > 2 and n > 3:
+        x[2, :n] = 0.0
+        x[2, n - 2] = 1e-45                                      # a denormal maximum
+    idx, val = kd.kd_argmax_rows(dev(x), n)
+    ref = ops.greedy_token(x[:, :n])
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref)
+    np.testing.assert_array_equal(val.cpu().numpy().view(np.uint32), x[np.arange(B), ref].view(np.uint32))
+    # every row equals its 1-row call
+    for b in range(B):
+        i1, _ = kd.kd_argmax_rows(dev(x[b:b + 1]), n)
+        assert int(i1.cpu()[0]) == int(ref[b])
+
+
+def test_embed_rows_exact():
+    """Rows of the table, bit for bit; tokens outside [0, vocab) give zero rows."""
+    say("embed rows")
+    r = np.random.default_rng(5)
+    vocab, d = 1000, 2048
+    table = r.standard_normal((vocab, d)).astype(np.float32)
+    tok = np.array([0, 999, 17, 17, -1, 1000, 523], dtype=np.int32)
+    out = kd.kd_embed_rows(dev(table), dev(tok)).cpu().numpy()
+    ok = (tok >= 0) & (tok < vocab)
+    np.testing.assert_array_equal(out[ok].view(np.uint32), ops.embed_rows(table, tok[ok]).view(np.uint32))
+    assert not out[~ok].any()

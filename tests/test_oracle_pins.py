@@ -245,6 +245,42 @@ def test_router_topk_ties_and_torch():
     assert ids2.tolist() == torch.topk(torch.tensor(rr), 8).indices.tolist()
 
 
+# --------------------------------------------------------------------------- next token
+def test_greedy_token_hand_cases():
+    # first maximum wins on ties; a lone entry; all-equal and all -inf rows give index 0
+    x = np.array([[1.0, 3.0, 3.0, 2.0],
+                  [-5.0, -1.0, -2.0, -1.0],
+                  [7.0, 7.0, 7.0, 7.0],
+                  [-np.inf, -np.inf, -np.inf, -np.inf],
+                  [0.0, -0.0, 0.0, 1e-45]], dtype=np.float32)
+    assert ops.greedy_token(x).tolist() == [1, 1, 0, 0, 3]
+    assert ops.greedy_token(np.array([[4.5]], dtype=np.float32)).tolist() == [0]
+
+
+def test_greedy_token_scan_and_numpy():
+    # many ties (small integers): a strict-greater left-to-right scan, and numpy's argmax
+    # (documented to return the first occurrence of the maximum)
+    r = np.random.default_rng(11)
+    x = r.integers(-3, 4, size=(64, 257)).astype(np.float32)
+    scan = []
+    for row in x:
+        best, bi = row[0], 0
+        for j in range(1, row.shape[0]):
+            if row[j] > best:
+                best, bi = row[j], j
+        scan.append(bi)
+    assert ops.greedy_token(x).tolist() == scan
+    y = r.standard_normal((16, 32000)).astype(np.float32)
+    assert ops.greedy_token(y).tolist() == np.argmax(y, axis=1).tolist()
+
+
+def test_embed_rows_picks_rows():
+    table = np.arange(7 * 5, dtype=np.float32).reshape(7, 5)
+    out = ops.embed_rows(table, np.array([6, 0, 6, 3]))
+    assert out[:, 0].tolist() == [30.0, 0.0, 30.0, 15.0]
+    assert (out - out[:, :1] == np.arange(5, dtype=np.float32)).all()
+
+
 # --------------------------------------------------------------------------- composition
 TINY = wlmod.ModelSpec("tiny", 2, 128, 4, 2, 64, 256, "q8_0", vocab=96, final_norm=True)
 TINY_MOE = wlmod.ModelSpec("tiny_moe", 2, 128, 4, 2, 64, 0, "q4_0", final_norm=True,

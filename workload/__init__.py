@@ -14,7 +14,8 @@ Distributions follow the workload descriptions of the batched-decode pages:
   random byte holds two uniformly random 4-bit codes), plus one fp16 scale
   ``|N(0, 0.02)| / 8`` per block (same max-|w| scale as Q8_0).
 * Norm gains ``1 + 0.1 N(0, 1)`` (fp32), router weights ``N(0, 0.02)`` (fp32),
-  step inputs ``N(0, 1)`` fp32 rows, KV prefill ``fp16(N(0, 1))``.
+  step inputs ``N(0, 1)`` fp32 rows, token embedding rows ``N(0, 1)`` fp32, KV prefill
+  ``fp16(N(0, 1))``.
 
 Storage conventions of the arrays produced here (both sides read them):
 
@@ -39,6 +40,7 @@ T_EGATE_Q, T_EGATE_D, T_EUP_Q, T_EUP_D, T_EDOWN_Q, T_EDOWN_D = 14, 15, 16, 17, 1
 T_SGATE_Q, T_SGATE_D, T_SUP_Q, T_SUP_D, T_SDOWN_Q, T_SDOWN_D = 20, 21, 22, 23, 24, 25
 T_FINAL_NORM, T_LM_Q, T_LM_D = 26, 27, 28
 T_X_IN, T_K_PRE, T_V_PRE, T_LENGTHS = 29, 30, 31, 32
+T_EMBED = 33
 
 
 def rng_for(seed: int, cfg_code: int, tensor: int, layer: int = 0, index: int = 0) -> np.random.Generator:
@@ -228,6 +230,16 @@ def step_inputs(wl: Workload, step: int) -> np.ndarray:
     out = np.empty((wl.B, d), dtype=np.float32)
     for b, (s, j) in enumerate(wl.rows):
         out[b] = rng_for(wl.seed, wl.code, T_X_IN, step, 1000 * s + j).standard_normal(d, dtype=np.float32)
+    return out
+
+
+def embedding_table(wl: Workload) -> np.ndarray:
+    """Token embedding rows ``[vocab, d]`` fp32, N(0, 1) like the step inputs (one stream per
+    row), for decoding with the greedy token fed back as the next step's input."""
+    sp = wl.spec
+    out = np.empty((sp.vocab, sp.d), dtype=np.float32)
+    for t in range(sp.vocab):
+        out[t] = rng_for(wl.seed, wl.code, T_EMBED, 0, t).standard_normal(sp.d, dtype=np.float32)
     return out
 
 
