@@ -252,6 +252,19 @@ kd_status kd_argmax_rows(const float* x, int32_t B, int32_t n, int32_t ldx, int3
 kd_status kd_embed_rows(const float* table, int32_t vocab, int32_t d, const int32_t* tokens, int32_t B,
                         float* out, int32_t ldo, void* stream);
 
+/* Accepted prefix of speculative-verify rows (Strata PR #1524, "What changes": target
+ * verification of several streams' drafts in one step, with accepted-prefix state commits).
+ * Rows are stream-major, k per stream: fed[s k + j] is the token that row j of stream s took
+ * as input (j = 0: the stream's last committed token; j >= 1: its draft j), at position
+ * pos_s + j, and greedy[s k + j] is that row's greedy token (kd_argmax_rows).  Writes
+ * n_accept[s] = the largest a <= k - 1 with greedy[s k + j - 1] == fed[s k + j] for every
+ * 1 <= j <= a, and next_token[s] = greedy[s k + a] (the target's token after the kept
+ * prefix).  All arrays are device int32.  Commit: the caller sets pos_s += a + 1 and feeds
+ * next_token[s]; cache slots past the new pos_s hold rejected rows' K/V and are rewritten by
+ * later steps before any row attends them.  1 <= n_streams, n_streams k <= 16. */
+kd_status kd_verify_accept(const int32_t* greedy, const int32_t* fed, int32_t n_streams, int32_t k,
+                           int32_t* n_accept, int32_t* next_token, void* stream);
+
 /* ---- test exports ---------------------------------------------------------------------- */
 /* The exact int32 block dot products S[b][n][blk] (b < B, n < n_out, blk < k/32) that the
  * mmvq kernel computes for this matrix and activation (same kernel, epilogue replaced). */

@@ -239,3 +239,27 @@ def embed_rows(table: np.ndarray, tokens: np.ndarray) -> np.ndarray:
     """
     return np.asarray(table)[np.asarray(tokens, dtype=np.int64)].copy()
 
+
+def accept_drafts(greedy: np.ndarray, fed: np.ndarray, k: int):
+    """Accepted prefix of speculative-verify rows, per stream (rows stream-major, k each).
+
+    Strata PR #1524, "What changes" (target verification of concurrent streams' drafts with
+    accepted-prefix state commits).  Row j of a stream took token ``fed[j]`` as input (j = 0:
+    the last committed token, j >= 1: draft j) and its greedy token ``greedy[j]`` is the
+    target's choice after it.  Reading (greedy verification): walk the drafts in order and keep
+    draft j while the previous row's greedy token equals it; the token after the kept prefix is
+    the greedy token of the last kept row.  Returns (n_accept, next_token) per stream.
+    """
+    g = np.asarray(greedy).reshape(-1, k)
+    f = np.asarray(fed).reshape(-1, k)
+    n_acc, nxt = [], []
+    for s in range(g.shape[0]):
+        a = 0
+        for j in range(1, k):
+            if g[s, j - 1] != f[s, j]:
+                break
+            a = j
+        n_acc.append(a)
+        nxt.append(int(g[s, a]))
+    return np.array(n_acc, dtype=np.int64), np.array(nxt, dtype=np.int64)
+

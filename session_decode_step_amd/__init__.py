@@ -80,6 +80,7 @@ SIGNATURES = {
     "kd_add_rows": (_I, [_P, _P, _P, _I, _I, _P]),
     "kd_argmax_rows": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "kd_embed_rows": (_I, [_P, _I, _I, _P, _I, _P, _I, _P]),
+    "kd_verify_accept": (_I, [_P, _P, _I, _I, _P, _P, _P]),
     "kd_kv_append": (_I, [_P, _P, _I, _I, _I, _PP, _PP, _PI, _I, _P]),
     "kd_fa_decode_workspace": (_S, [_I, _I, _I, _PI]),
     "kd_fa_decode_ragged": (_I, [_P, _I, _I, _I, _I, _PP, _PP, _PI, _I, _F, _P, _P, _S, _P]),
@@ -323,6 +324,17 @@ def kd_embed_rows(table: torch.Tensor, tokens: torch.Tensor, out: Optional[torch
     _check(lib().kd_embed_rows(table.data_ptr(), vocab, d, tokens.data_ptr(), B, out.data_ptr(), out.stride(0),
                                _stream(stream)), "kd_embed_rows")
     return out
+
+
+def kd_verify_accept(greedy: torch.Tensor, fed: torch.Tensor, k: int, stream=None):
+    """Accepted draft count and next token per stream of stream-major verify rows (device int32
+    [n_streams * k] each): (n_accept, next_token), device int32 [n_streams]."""
+    n = greedy.shape[0] // k
+    n_accept = torch.empty(n, dtype=torch.int32, device=greedy.device)
+    nxt = torch.empty(n, dtype=torch.int32, device=greedy.device)
+    _check(lib().kd_verify_accept(greedy.data_ptr(), fed.data_ptr(), n, k, n_accept.data_ptr(), nxt.data_ptr(),
+                                  _stream(stream)), "kd_verify_accept")
+    return n_accept, nxt
 
 
 # ------------------------------------------------------------------------------ KV + attention

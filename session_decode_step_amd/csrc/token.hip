@@ -1,5 +1,5 @@
-// Greedy next token of each row and the embedding gather that turns tokens into the next
-// step's input rows.
+// Greedy next token of each row, the embedding gather that turns tokens into the next
+// step's input rows, and the accepted prefix of speculative-verify rows.
 //
 // What is computed (memra-engine 0.72.0, src/decode_batch.rs): ``decode_step_batch_sampled``
 // picks, for each greedy row, the device argmax of its logits row between the lm_head product
@@ -12,6 +12,13 @@
 // maximum; lanes, then waves, are merged with "larger value wins, equal values keep the lower
 // index" -- a total order, so the result does not depend on the merge tree.  NaN entries never
 // win.  No arithmetic touches the values: the result is exact.
+//
+// Verify rows (Strata PR #1524, "What changes": wider target verification across concurrent
+// streams with accepted-prefix state commits): a stream's k rows hold, in order, its last
+// committed token and k - 1 draft tokens at consecutive positions; row j's greedy token is the
+// target's choice after row j's input.  Reading (greedy verification; the page does not spell
+// out the rule): draft j + 1 is kept while it equals row j's greedy token, the first mismatch
+// ends the prefix, and the token after the kept prefix is the greedy token of its last row.
 #include <climits>
 
 #include "kd_internal.h"
@@ -82,9 +89,34 @@ __global__ __launch_bounds__(256) void embed_rows_kernel(const float* __restrict
   out[(size_t)b * ldo + c] = valid ? table[(size_t)tok * d + c] : 0.0f;
 }
 
+// One thread per stream: the accepted prefix of its drafts and the token that follows it.
+__global__ void verify_accept_kernel(const int32_t* __restrict__ greedy, const int32_t* __restrict__ fed,
+                                     int n_streams, int k, int32_t* __restrict__ n_accept,
+                                     int32_t* __restrict__ next_token) {
+  const int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= n_streams) return;
+  const int32_t* g = greedy + (size_t)s * k;
+  const int32_t* f = fed + (size_t)s * k;
+  int a = 0;
+  while (a + 1 < k && g[a] == f[a + 1]) ++a;
+  n_accept[s] = a;
+  next_token[s] = g[a];
+}
+
 }  // namespace kd
 
 using namespace kd;
+
+extern "C" kd_status kd_verify_accept(const int32_t* greedy, const int32_t* fed, int32_t n_streams, int32_t k,
+                                      int32_t* n_accept, int32_t* next_token, void* stream) {
+  KD_REQUIRE(n_streams >= 1 && n_streams <= KD_MAX_B, KD_ERR_UNSUPPORTED, "kd_verify_accept: n_streams=%d outside [1,16]",
+             n_streams);
+  KD_REQUIRE(k >= 1 && n_streams * k <= KD_MAX_B, KD_ERR_UNSUPPORTED,
+             "kd_verify_accept: %d streams x %d rows outside one step's 16 rows", n_streams, k);
+  KD_REQUIRE(greedy && fed && n_accept && next_token, KD_ERR_INVALID, "kd_verify_accept: null pointer");
+  verify_accept_kernel<<<1, 64, 0, as_stream(stream)>>>(greedy, fed, n_streams, k, n_accept, next_token);
+  return check_launch("kd_verify_accept");
+}
 
 extern "C" kd_status kd_argmax_rows(const float* x, int32_t B, int32_t n, int32_t ldx, int32_t* idx, float* val,
                                     void* stream) {

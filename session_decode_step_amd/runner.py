@@ -73,14 +73,16 @@ class GpuWorkload:
         return self._x_cache[key]
 
     def step(self, s: int, rows: Optional[Sequence[int]] = None, out: Optional[torch.Tensor] = None,
-             stream=None, x: Optional[torch.Tensor] = None) -> torch.Tensor:
+             stream=None, x: Optional[torch.Tensor] = None, pos: Optional[Sequence[int]] = None) -> torch.Tensor:
         """Run decode step ``s`` for the given row indices (default: all rows).  ``x``: device
-        input rows [len(rows), d] to use instead of the workload's (e.g. embedded tokens)."""
+        input rows [len(rows), d] to use instead of the workload's (e.g. embedded tokens);
+        ``pos``: the rows' positions instead of the workload's (e.g. after a verify commit)."""
         wl = self.wl
         rows = list(range(wl.B)) if rows is None else list(rows)
         x = self._rows_input(s, rows) if x is None else x
-        pos_all = wl.positions(s)
-        pos = [pos_all[b] for b in rows]
+        if pos is None:
+            pos_all = wl.positions(s)
+            pos = [pos_all[b] for b in rows]
         sess = [wl.rows[b][0] for b in rows]
         kb, vb = self.caches.tables(sess)
         if out is None:

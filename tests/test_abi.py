@@ -147,6 +147,10 @@ def test_token_validation_before_launch():
     assert L.kd_embed_rows(0x100, 4, 8, 0x200, 2, 0x300, 7, None) == kd.KD_ERR_INVALID    # ldo < d
     assert L.kd_embed_rows(0x100, 4, 8, None, 2, 0x300, 8, None) == kd.KD_ERR_INVALID
     assert L.kd_embed_rows(0x100, 4, 8, 0x200, 70000, 0x300, 8, None) == kd.KD_ERR_UNSUPPORTED
+    assert L.kd_verify_accept(0x100, 0x200, 0, 4, 0x300, 0x400, None) == kd.KD_ERR_UNSUPPORTED
+    assert L.kd_verify_accept(0x100, 0x200, 5, 4, 0x300, 0x400, None) == kd.KD_ERR_UNSUPPORTED   # 20 rows
+    assert L.kd_verify_accept(0x100, 0x200, 4, 0, 0x300, 0x400, None) == kd.KD_ERR_UNSUPPORTED
+    assert L.kd_verify_accept(0x100, None, 4, 4, 0x300, 0x400, None) == kd.KD_ERR_INVALID
 
 
 def test_model_create_validation_and_step_errors():

@@ -337,3 +337,20 @@ def test_embed_rows_exact():
     ok = (tok >= 0) & (tok < vocab)
     np.testing.assert_array_equal(out[ok].view(np.uint32), ops.embed_rows(table, tok[ok]).view(np.uint32))
     assert not out[~ok].any()
+
+
+def test_verify_accept_exact():
+    """Accepted prefixes and next tokens equal the oracle's on random stream-major rows."""
+    say("verify accept")
+    r = np.random.default_rng(13)
+    for n_streams, k in ((4, 4), (2, 8), (16, 1), (3, 5), (1, 16)):
+        for _ in range(20):
+            fed = r.integers(0, 4, size=n_streams * k).astype(np.int32)
+            greedy = np.roll(fed, -1).astype(np.int32)              # agrees unless perturbed
+            flip = r.random(n_streams * k) < 0.25
+            greedy[flip] = r.integers(0, 4, size=int(flip.sum()))
+            n_acc, nxt = kd.kd_verify_accept(dev(greedy), dev(fed), k)
+            ra, rn = ops.accept_drafts(greedy, fed, k)
+            np.testing.assert_array_equal(n_acc.cpu().numpy(), ra)
+            np.testing.assert_array_equal(nxt.cpu().numpy(), rn)
+

@@ -151,6 +151,67 @@ def test_c2_greedy_decode_feeds_tokens_back():
     say(f"  oracle's own greedy token equals the GPU's on {agree} of {steps * len(rows)} (row, step)")
 
 
+def test_c2_speculative_verify_commit_and_rollback():
+    """Two streams x k = 4 verify rows on the 8-layer Q8_0 stack with lm_head 32000, ctx 1238.
+    Stream 0's drafts are the stack's own greedy continuation; stream 1's second draft is
+    wrong.  Verify rows fed the right tokens equal the sequential greedy decode (logits bit for
+    bit); kd_verify_accept keeps 3 and 1 drafts; after the commit (pos += kept + 1) both streams
+    continue from the next token and equal the sequential decode bit for bit, the rejected
+    rows' cache slots rewritten with the sequential decode's bytes."""
+    say("c2 verify, commit, rollback")
+    k, L, n_seq = 4, 1238, 6
+    wl = W.workload("c2", B=2, steps=n_seq)
+    table_np = W.embedding_table(wl)
+    table = torch.from_numpy(table_np).cuda()
+    vocab = wl.spec.vocab
+    # the sequential greedy decode of both streams
+    gw_ref = GpuWorkload(wl)
+    x = torch.from_numpy(W.step_inputs(wl, 0)).cuda()
+    T, Y = [], []
+    for s in range(n_seq):
+        y = gw_ref.step(s, x=x)
+        idx, _ = kd.kd_argmax_rows(y)
+        x = kd.kd_embed_rows(table, idx)
+        T.append(idx.cpu().numpy().copy())
+        Y.append(y.cpu().numpy().copy())
+    T, Y = np.stack(T), np.stack(Y)                          # [step, stream], [step, stream, vocab]
+    say(f"  sequential tokens {T.T.tolist()}")
+    # one verify step: k rows per stream at positions L .. L + k - 1
+    wv = W.Workload(wl.code, wl.spec, [L, L], [(s, j) for s in range(2) for j in range(k)], 1, wl.capacity,
+                    wl.seed)
+    gw = GpuWorkload(wv, model=gw_ref.model)
+    drafts = [[int(T[0, 0]), int(T[1, 0]), int(T[2, 0])],
+              [int(T[0, 1]), int((T[1, 1] + 1) % vocab), int(T[2, 1])]]
+    x0 = W.step_inputs(wl, 0)
+    xv = np.concatenate([np.concatenate([x0[s:s + 1], table_np[drafts[s]]]) for s in range(2)])
+    yv = gw.step(0, x=torch.from_numpy(xv).cuda()).cpu().numpy()
+    for j in range(k):
+        np.testing.assert_array_equal(yv[j].view(np.uint32), Y[j, 0].view(np.uint32))
+    for j in range(2):
+        np.testing.assert_array_equal(yv[k + j].view(np.uint32), Y[j, 1].view(np.uint32))
+    g, _ = kd.kd_argmax_rows(torch.from_numpy(yv).cuda())
+    fed = np.array([-1] + drafts[0] + [-1] + drafts[1], dtype=np.int32)  # row 0: no token (input row)
+    n_acc, nxt = kd.kd_verify_accept(g, torch.from_numpy(fed).cuda(), k)
+    n_acc, nxt = n_acc.cpu().numpy(), nxt.cpu().numpy()
+    ra, rn = oracle.accept_drafts(g.cpu().numpy(), fed, k)
+    np.testing.assert_array_equal(n_acc, ra)
+    np.testing.assert_array_equal(nxt, rn)
+    assert n_acc.tolist() == [3, 1] and nxt.tolist() == [int(T[3, 0]), int(T[1, 1])]
+    # commit: pos += kept + 1, feed the next token; continue two steps on rows (0, 0), (1, 0)
+    pos = [L + int(n_acc[0]) + 1, L + int(n_acc[1]) + 1]
+    xc = kd.kd_embed_rows(table, torch.from_numpy(nxt.astype(np.int32)).cuda())
+    for c in range(2):
+        y = gw.step(0, rows=[0, k], x=xc, pos=pos)
+        np.testing.assert_array_equal(y[0].cpu().numpy().view(np.uint32), Y[4 + c, 0].view(np.uint32))
+        np.testing.assert_array_equal(y[1].cpu().numpy().view(np.uint32), Y[2 + c, 1].view(np.uint32))
+        idx, _ = kd.kd_argmax_rows(y)
+        xc = kd.kd_embed_rows(table, idx)
+        pos = [p + 1 for p in pos]
+    for sess, hi in ((0, L + 6), (1, L + 4)):
+        np.testing.assert_array_equal(gw.caches.t[sess][:, :, :, :hi].cpu().numpy().view(np.uint16),
+                                      gw_ref.caches.t[sess][:, :, :, :hi].cpu().numpy().view(np.uint16))
+
+
 def test_c2_full_64_steps_bit_identity():
     """The benchmarked shape (B = 8, 64 steps): rows 0 and 7 stepped alone over all 64 steps
     reproduce the batched run bit for bit, outputs and caches."""

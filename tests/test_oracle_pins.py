@@ -281,6 +281,42 @@ def test_embed_rows_picks_rows():
     assert (out - out[:, :1] == np.arange(5, dtype=np.float32)).all()
 
 
+def test_accept_drafts_hand_cases():
+    # two streams of k = 4 rows: (fed = last token + 3 drafts, greedy of each row)
+    fed = np.array([5, 10, 11, 12,    5, 10, 99, 12])
+    greedy = np.array([10, 11, 12, 13,   10, 11, 12, 13])
+    n_acc, nxt = ops.accept_drafts(greedy, fed, 4)
+    assert n_acc.tolist() == [3, 1]          # all drafts kept; the second draft rejected
+    assert nxt.tolist() == [13, 11]          # the token after the kept prefix
+    # a mismatch at the first draft keeps none, and later agreement does not count
+    n_acc, nxt = ops.accept_drafts(np.array([7, 11, 12, 13]), np.array([5, 10, 11, 12]), 4)
+    assert (n_acc.tolist(), nxt.tolist()) == ([0], [7])
+    # one row per stream: plain greedy decoding
+    n_acc, nxt = ops.accept_drafts(np.array([3, 4]), np.array([1, 2]), 1)
+    assert (n_acc.tolist(), nxt.tolist()) == ([0, 0], [3, 4])
+
+
+def test_accept_drafts_matches_sequential_greedy():
+    # a toy deterministic target (next = f(token)): drafts that follow it are all kept, and
+    # the result equals running the target one token at a time
+    f = lambda t: (7 * t + 3) % 50                                     # noqa: E731
+    r = np.random.default_rng(12)
+    for _ in range(200):
+        k = int(r.integers(1, 6))
+        t0 = int(r.integers(0, 50))
+        seq = [t0]
+        for _j in range(k):
+            seq.append(f(seq[-1]))
+        drafts = [seq[j] if r.random() < 0.8 else int(r.integers(0, 50)) for j in range(1, k)]
+        fed = np.array([t0] + drafts)
+        greedy = np.array([f(int(t)) for t in fed])
+        n_acc, nxt = ops.accept_drafts(greedy, fed, k)
+        a = 0
+        while a < k - 1 and drafts[a] == seq[a + 1]:
+            a += 1
+        assert n_acc[0] == a and nxt[0] == seq[a + 1]
+
+
 # --------------------------------------------------------------------------- composition
 TINY = wlmod.ModelSpec("tiny", 2, 128, 4, 2, 64, 256, "q8_0", vocab=96, final_norm=True)
 TINY_MOE = wlmod.ModelSpec("tiny_moe", 2, 128, 4, 2, 64, 0, "q4_0", final_norm=True,
