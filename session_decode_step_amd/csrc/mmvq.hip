@@ -237,6 +237,13 @@ __device__ __forceinline__ v4i block_dots(long A, long Bw) {
   return S;
 }
 
+// Q4_0 offset term of one block, sum_k x_k * (-8) for every activation row: it depends on the
+// activations only, so a quad's four offsets serve all the workgroup's row groups.
+__device__ __forceinline__ v4i block_offset(long A) {
+  const v4i zero = {0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_i32_16x16x32_i8(A, (long)0xF8F8F8F8F8F8F8F8ull, zero, 0, 0, 0);
+}
+
 __device__ __forceinline__ float half_bits(uint32_t hw, int hi) {
   return __half2float(__ushort_as_half((unsigned short)(hi ? (hw >> 16) : (hw & 0xFFFF))));
 }
@@ -392,6 +399,7 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) acc[r][s] = 0.0f;
   float4 dx[4];
+  v4i qoff[4];  // Q4_0, RG > 1: the current quad's offset terms
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int j = t / RG, r = t % RG;
@@ -403,11 +411,20 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
       for (int s = 0; s < NS; ++s) dx[s] = *reinterpret_cast<const float4*>(dxw + ((4 * g + s) * QW + j) * 4);
     }
     const int4 A0 = ax0[j & 1], A1 = ax1[j & 1];
+    if (FMT == KD_FMT_Q4_0 && RG > 1 && r == 0) {
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb) qoff[jb] = block_offset(act_op(A0, A1, jb));
+    }
     // tiles past the wave's quads have zero weight and activation scales: they add exact zeros
     const float4 dw = *reinterpret_cast<const float4*>(dww + ((r * QW + j) * 16 + n) * 16);
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb) {
-      const v4i S = block_dots<FMT>(act_op(A0, A1, jb), w_op<FMT>(cur.w0, cur.w1, jb));
+      // Q4_0 with several row groups: nibble dots accumulated onto the quad's cached offsets
+      // (the same exact integers as block_dots)
+      const v4i S = (FMT == KD_FMT_Q4_0 && RG > 1)
+                        ? __builtin_amdgcn_mfma_i32_16x16x32_i8(act_op(A0, A1, jb), w_op<FMT>(cur.w0, cur.w1, jb),
+                                                                qoff[jb], 0, 0, 0)
+                        : block_dots<FMT>(act_op(A0, A1, jb), w_op<FMT>(cur.w0, cur.w1, jb));
       if (DEBUG) {
         const int blk = 4 * q + jb;
         const int row = (rg0 + r) * 16 + n;
