@@ -8,9 +8,11 @@ B rows (all 32 layers + final norm).  K timed steps run at positions 4096..4096+
 warm-up steps (the same positions are re-written, so caches hold the same bytes each pass).
 
 Prints ONE JSON line: aggregate decode tok/s at B=8 (``value``), the B=1..16 sweep, step HBM
-GB/s, the roofline of the dominant kernel (mmvq on the gate/up shape 14336 x 4096 Q4_0 at
-B=8, timed with HIP events on the launch stream) and of fa_decode at B=8, and the CPU oracle
-timed on a bounded sample beside it.
+GB/s, the roofline of the dominant kernel (fa_decode at B=8) and of the largest product (the
+gate/up mmvq, 28672 x 4096 Q4_0 at B=8), both timed with HIP events on the launch stream, the
+other workloads of the path (``other_workloads``: the 8-layer Q8_0 stack with lm_head at
+B=1..8, the ragged B=16 attention sublayer and its fa_decode, the MoE verify step), and the
+CPU oracle timed on a bounded sample beside it.
 
 ``--summarize-trace CSV`` instead prints per-(kernel, grid) average durations from a
 rocprofv3 kernel-trace CSV (the profiles/ summaries are made with it).
@@ -274,6 +276,82 @@ def load_traffic(kind: str):
     return None
 
 
+def _time_steps(gw, stream, K: int, Wu: int, rows=None, repeat_first: bool = False) -> float:
+    """Average ms per kd_decode_step of ``gw`` over K steps after Wu warm-up steps (HIP
+    events on ``stream``); ``repeat_first``: re-run step 0 (its appends rewrite the same
+    slots, so the caches hold the same bytes each time)."""
+    import torch
+    rows = list(range(gw.wl.B)) if rows is None else list(rows)
+    out = torch.empty((len(rows), gw.wl.spec.out_dim), dtype=torch.float32, device="cuda")
+    steps = [0] * max(K, Wu) if repeat_first else list(range(max(K, Wu)))
+    gw.prefetch(sorted(set(steps)), rows)
+    for s in steps[:Wu]:
+        gw.step(s, rows=rows, out=out, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for s in steps[:K]:
+        gw.step(s, rows=rows, out=out, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / K
+
+
+def other_workloads(stream, iters: int) -> dict:
+    """The other measured workloads of the path, beside the headline (same stream, inputs
+    resident): the 8-layer Q8_0 stack with its 32000-row lm_head at B = 1, 2, 4, 8 (ctx 1238);
+    the attention sublayer with B = 16 ragged rows (log-uniform lengths in [512, 32768]), its
+    step and its fa_decode; the 8-layer MoE stack's verify step (4 streams x 4 draft rows,
+    ctx 8192)."""
+    import torch
+    import workload as W
+    import session_decode_step_amd as kd
+    from session_decode_step_amd.runner import GpuWorkload
+    res = {}
+    # dense Q8_0 stack with lm_head
+    log("8-layer Q8_0 stack with lm_head")
+    wl = W.workload("c2", B=8, steps=64)
+    gw = GpuWorkload(wl, fill="device")
+    dense = {}
+    for B in (1, 2, 4, 8):
+        ms = _time_steps(gw, stream, 16, 3, rows=list(range(B)))
+        dense[str(B)] = {"tok_s": round(B / ms * 1e3, 1), "ms_per_step": round(ms, 4)}
+    res["8-layer d=2048 Q8_0 decoder + lm_head 32000, ctx 1238"] = dense
+    del gw
+    # attention sublayer, ragged B = 16
+    log("attention sublayer, ragged B=16")
+    wl = W.workload("c3")
+    gw = GpuWorkload(wl, fill="device")
+    ms = _time_steps(gw, stream, iters, 3, repeat_first=True)
+    sp = wl.spec
+    t_kv = [p + 1 for p in wl.positions(0)]
+    q = torch.randn((wl.B, sp.n_head, sp.head_dim), device="cuda",
+                    generator=torch.Generator(device="cuda").manual_seed(2))
+    kb = [gw.caches.k_ptr(s, 0) for s in range(wl.B)]
+    vb = [gw.caches.v_ptr(s, 0) for s in range(wl.B)]
+    ws = torch.zeros(kd.kd_fa_decode_workspace(wl.B, sp.n_head, sp.head_dim, t_kv), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    us = time_rotating(lambda i: kd.kd_fa_decode_ragged(q, sp.n_head_kv, kb, vb, t_kv, wl.capacity,
+                                                       sp.head_dim ** -0.5, ws=ws, out=out, stream=stream),
+                       iters, stream)
+    fb = fa_algorithmic_bytes(t_kv, sp.n_head_kv, sp.n_head, sp.head_dim)
+    res["attention sublayer d=4096 32Q/8KV hd=128 Q8_0, B=16 ragged ctx 512..32768"] = {
+        "ms_per_step": round(ms, 4), "rows_s": round(wl.B / ms * 1e3, 1), "t_kv": t_kv,
+        "fa_us": round(us, 3), "fa_algorithmic_bytes": int(fb), "fa_GBs": round(fb / (us * 1e-6) / 1e9, 1),
+        "fa_frac": round(fb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    del gw
+    # MoE verify step
+    log("8-layer MoE stack, verify rows")
+    wl = W.workload("c5")
+    gw = GpuWorkload(wl, fill="device")
+    ms = _time_steps(gw, stream, iters, 3, repeat_first=True)
+    res["8-layer MoE d=2816 128 experts top-8 + shared, Q4_0; 4 streams x 4 verify rows, ctx 8192"] = {
+        "ms_per_step": round(ms, 4), "rows_s": round(wl.B / ms * 1e3, 1)}
+    del gw
+    torch.cuda.synchronize()
+    return res
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -283,6 +361,7 @@ def main() -> None:
     ap.add_argument("--headline-b", type=int, default=8, help="width whose aggregate tok/s is `value`")
     ap.add_argument("--kernel-iters", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other", action="store_true", help="skip the other workloads (headline only)")
     ap.add_argument("--cpu-layers", type=int, default=16, help="layers of one step the oracle is timed on")
     ap.add_argument("--summarize-trace", default=None)
     ap.add_argument("--traffic-probe", action="store_true", help="launches for the PMC traffic passes only")
@@ -396,6 +475,8 @@ def main() -> None:
     fa_gbs = fa_bytes / (fa_us * 1e-6) / 1e9
     fa_traffic = load_traffic("fa") if t_kv == [FA_T] * FA_B else None
 
+    other = None if args.no_other else other_workloads(stream, 20)
+
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -452,6 +533,7 @@ def main() -> None:
                           "kernel": "mmvq_kernel<Q4_0, SwiGLU epilogue> 28672x4096 (gate/up) at B=%d" % Bh,
                           "avg_launch_us": round(mm_us, 3), "algorithmic_bytes": int(mm_bytes)},
         "cpu_baseline": cpu,
+        "other_workloads": other,
         "setup_s": round(setup_s, 1),
     }
     print(json.dumps(res))

@@ -220,6 +220,8 @@ void launch_swiglu_quant(const float* g, const float* u, int rows, int n, int ld
                          float* d, hipStream_t st);
 void launch_add(const float* x, const float* y, float* z, size_t n, hipStream_t st);
 
+// Router: logits [B][E] (written; d % 4 == 0, 16-byte aligned rows), then top-K ids and
+// softmax weights per row.
 void launch_router(const float* z, const float* Wr, int B, int d, int E, int K, int32_t* ids, float* p, float* logits,
                    hipStream_t st);
 void launch_bucket(const int32_t* ids, int B, int K, int E, int32_t* count, int32_t* rows, int32_t* pairs,

@@ -584,11 +584,12 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
   }
 }
 
-// Quads per wave: about KD_MMVQ_WAVE_QUADS, and enough that at most 16 waves cover NQ;
-// then balanced (the smallest QW giving the same wave count).  Waves per workgroup:
-// ceil(NQ / QW).  Both depend on the matrix's k only.
+// Quads per wave: about NQ / 4 (four waves per workgroup), between 2 and KD_MMVQ_WAVE_QUADS,
+// and enough that at most 16 waves cover NQ; then balanced (the smallest QW giving the same
+// wave count).  Waves per workgroup: ceil(NQ / QW).  Both depend on the matrix's k only.
 static int mmvq_qw(int NQ, int want_quads = KD_MMVQ_WAVE_QUADS) {
   int qw = ceil_div(NQ, 16);  // at most 16 waves; QW <= 8 covers k <= 16384
+  want_quads = NQ / 4 < want_quads ? (NQ / 4 > 2 ? NQ / 4 : 2) : want_quads;
   const int want = NQ < want_quads ? NQ : want_quads;
   qw = qw > want ? qw : want;
   const int nw = ceil_div(NQ, qw);

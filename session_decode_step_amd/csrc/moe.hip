@@ -13,6 +13,8 @@
 // and treats its rows as the MFMA's activation rows, whose results never depend on which
 // other rows share the expert; the combine adds the k expert outputs of a row in rank
 // order.  So a row's result is the same at any B.
+#include <climits>
+
 #include "kd_internal.h"
 
 namespace kd {
@@ -20,40 +22,80 @@ namespace kd {
 constexpr int kMaxExperts = 256;
 constexpr int kMaxTopK = 16;
 
-// grid B; 256 threads.  z fp32 [B][d]; Wr fp32 [E][d].
-__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ z, const float* __restrict__ Wr,
-                                                          int d, int E, int K, int32_t* __restrict__ ids,
-                                                          float* __restrict__ p, float* __restrict__ logits) {
-  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  __shared__ float r[kMaxExperts];
-  const float* zr = z + (size_t)b * d;
-  for (int e = w; e < E; e += 4) {
-    const float* wr = Wr + (size_t)e * d;
-    float acc = 0.0f;
-    for (int i = lane; i < d; i += 64) acc = fmaf(wr[i], zr[i], acc);
-    acc = wave_sum(acc);
-    if (lane == 0) r[e] = acc;
+// Router logits r[b][e] = W_r[e] . z[b] (fp32): one wave per (expert, row), grid (E, B).  Lane
+// l adds float4 elements l, l + 64, ... of the row in order (kRouterVec of them in flight per
+// pass), then the wave adds its lanes by a fixed butterfly: the order depends on d only.
+constexpr int kRouterVec = 12;  // float4 per lane per pass: rows of up to 3072 in one pass
+__global__ __launch_bounds__(64) void router_logits_kernel(const float* __restrict__ z, const float* __restrict__ Wr,
+                                                           int d, int E, float* __restrict__ logits) {
+  const int e = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const float4* w4 = reinterpret_cast<const float4*>(Wr + (size_t)e * d);
+  const float4* z4 = reinterpret_cast<const float4*>(z + (size_t)b * d);
+  const int d4 = d / 4;
+  float acc = 0.0f;
+  for (int base = 0; base < d4; base += 64 * kRouterVec) {
+    float4 wv[kRouterVec], zv[kRouterVec];
+#pragma unroll
+    for (int i = 0; i < kRouterVec; ++i) {
+      const int idx = base + lane + 64 * i;
+      const bool ok = idx < d4;
+      wv[i] = ok ? w4[idx] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      zv[i] = ok ? z4[idx] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+#pragma unroll
+    for (int i = 0; i < kRouterVec; ++i) {
+      acc = fmaf(wv[i].x, zv[i].x, acc);
+      acc = fmaf(wv[i].y, zv[i].y, acc);
+      acc = fmaf(wv[i].z, zv[i].z, acc);
+      acc = fmaf(wv[i].w, zv[i].w, acc);
+    }
   }
-  __syncthreads();
-  if (logits)
-    for (int e = tid; e < E; e += 256) logits[(size_t)b * E + e] = r[e];
-  if (tid == 0) {
-    bool taken[kMaxExperts];
-    for (int e = 0; e < E; ++e) taken[e] = false;
-    int sel[kMaxTopK];
-    float val[kMaxTopK];
-    for (int k = 0; k < K; ++k) {
-      int best = -1;
-      float bv = -INFINITY;
-      for (int e = 0; e < E; ++e)
-        if (!taken[e] && (best < 0 || r[e] > bv)) {  // strict: ties keep the lower id
-          best = e;
-          bv = r[e];
+  acc = wave_sum(acc);
+  if (lane == 0) logits[(size_t)b * E + e] = acc;
+}
+
+// Top-K of each row's logits, grid B, 256 threads (thread e holds expert e): K rounds, each
+// taking the largest untaken logit with ties to the lower id (a total order: the reduction
+// tree does not matter); then the softmax over the K selected logits in rank order.
+__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits, int E, int K,
+                                                          int32_t* __restrict__ ids, float* __restrict__ p) {
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  __shared__ float wv[4];
+  __shared__ int wi[4];
+  __shared__ float val[kMaxTopK];
+  __shared__ int sel[kMaxTopK];
+  float r = tid < E ? logits[(size_t)b * E + tid] : -INFINITY;
+  bool live = tid < E;
+  for (int k = 0; k < K; ++k) {
+    float bv = live ? r : -INFINITY;
+    int bi = live ? tid : INT_MAX;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      const float v2 = __shfl_xor(bv, m, 64);
+      const int i2 = __shfl_xor(bi, m, 64);
+      if (i2 != INT_MAX && (bi == INT_MAX || v2 > bv || (v2 == bv && i2 < bi))) {
+        bv = v2;
+        bi = i2;
+      }
+    }
+    if (lane == 0) {
+      wv[w] = bv;
+      wi[w] = bi;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      for (int ww = 1; ww < 4; ++ww)
+        if (wi[ww] != INT_MAX && (bi == INT_MAX || wv[ww] > bv || (wv[ww] == bv && wi[ww] < bi))) {
+          bv = wv[ww];
+          bi = wi[ww];
         }
-      taken[best] = true;
-      sel[k] = best;
+      sel[k] = bi;
       val[k] = bv;
     }
+    __syncthreads();
+    if (tid == sel[k]) live = false;
+  }
+  if (tid == 0) {
     const float mx = val[0];
     float ex[kMaxTopK];
     float sum = 0.0f;
@@ -97,7 +139,8 @@ __global__ void moe_combine_kernel(const float* __restrict__ y, const float* __r
 
 void launch_router(const float* z, const float* Wr, int B, int d, int E, int K, int32_t* ids, float* p, float* logits,
                    hipStream_t st) {
-  router_topk_kernel<<<B, 256, 0, st>>>(z, Wr, d, E, K, ids, p, logits);
+  router_logits_kernel<<<dim3(E, B), 64, 0, st>>>(z, Wr, d, E, logits);
+  router_topk_kernel<<<B, 256, 0, st>>>(logits, E, K, ids, p);
 }
 
 void launch_bucket(const int32_t* ids, int B, int K, int E, int32_t* count, int32_t* rows, int32_t* pairs,

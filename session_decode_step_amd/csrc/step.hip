@@ -175,7 +175,7 @@ struct StepBufs {
   float *act_d, *act2_d, *hq_d, *actn_d, *ss;
   void* fa_ws;
   int32_t *ids, *count, *rows, *pairs;
-  float *p, *gup, *yp;
+  float *p, *gup, *yp, *rlog;
   int8_t* lm_qs;
   float* lm_d;
 };
@@ -206,6 +206,7 @@ size_t carve_step(const kd_model* m, int B, const FaPlan& plan, void* ws, StepBu
     const int K = d.n_expert_used, E = d.n_experts, Fe = d.expert_ffn, Fs = d.shared_ffn;
     s.ids = c.take<int32_t>((size_t)B * K);
     s.p = c.take<float>((size_t)B * K);
+    s.rlog = c.take<float>((size_t)B * E);
     s.count = c.take<int32_t>(E);
     s.rows = c.take<int32_t>((size_t)E * 16);
     s.pairs = c.take<int32_t>((size_t)E * 16);
@@ -364,7 +365,7 @@ extern "C" kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x
       launch_mmvq(Ly.w_down, s.act2_qs, s.act2_d, B, s.f, D, st);
     } else {
       const int E = d.n_experts, K = d.n_expert_used, Fe = d.expert_ffn, Fs = d.shared_ffn;
-      launch_router(s.z, Ly.router, B, D, E, K, s.ids, s.p, nullptr, st);
+      launch_router(s.z, Ly.router, B, D, E, K, s.ids, s.p, s.rlog, st);
       launch_bucket(s.ids, B, K, E, s.count, s.rows, s.pairs, st);
       RowMap gu_map{s.count, s.rows, s.pairs, E, (long long)n_rowgroups(Fe) * n_quads(D), B};
       kd_weight eg = Ly.e_gate, eu = Ly.e_up, ed = Ly.e_down;
