@@ -80,6 +80,7 @@ typedef _Float16 fa_v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 fa_v4h __attribute__((ext_vector_type(4)));
 typedef float fa_v4f __attribute__((ext_vector_type(4)));
 constexpr int kFaWaves = 8;
+constexpr int kFaGroupCols = 8;  // query columns of a workgroup whose rows share a cache pass
 
 __device__ __forceinline__ void split_f16(float x, _Float16& hi, _Float16& lo) {
   hi = (_Float16)x;
@@ -89,7 +90,11 @@ __device__ __forceinline__ void split_f16(float x, _Float16& hi, _Float16& lo) {
 // MULTI: chunks may span several 128-key tiles (rows longer than 128 x 128 keys).  Without
 // it the tile loop runs once, so the running output is not live across a tile's loads and
 // the kernel needs fewer registers (more workgroups per CU); the operations are the same.
-template <int R, int HD, bool MULTI>
+// C: query columns of the workgroup (R heads of each of the group's rows), C <= 16 -- the
+// MFMA's 16 columns.  Column h is head g R + h % R of the group's row h / R; each column
+// masks the keys at or past its own row's t_kv, so a row's partials are those of its own
+// pass (the keys it does not attend score -inf and weigh exactly 0).
+template <int R, int HD, bool MULTI, int C>
 __global__ __launch_bounds__(64 * kFaWaves) void fa_split_kernel(FaPlan p, const float* __restrict__ q,
                                                                           int ldq, RowCaches rc, int capacity,
                                                                           float scale, float* __restrict__ ws) {
@@ -97,31 +102,67 @@ __global__ __launch_bounds__(64 * kFaWaves) void fa_split_kernel(FaPlan p, const
   constexpr int NC = HD / 32;      // 32-dim slices of the score product
   constexpr int TK = 16 * NW;      // keys per tile
   constexpr float kPScale = 16384.0f, kPInv = 1.0f / 16384.0f;
-  static_assert(R <= 16, "heads per KV head");
+  static_assert(R <= C && C <= 16, "query columns");
+  constexpr bool GROUPED = C > R;  // rows sharing a cache pass; otherwise one row per workgroup
   const int item = blockIdx.x, g = blockIdx.y;
-  int b = 0;
-#pragma unroll
-  for (int i = 1; i < KD_MAX_B; ++i)
-    if (item >= p.split_off[i]) b = i;
-  const int s0 = p.split_off[b];
-  const int c = p.chunk[b];
-  const int k0 = (item - s0) * c;
-  const int k1 = min(k0 + c, p.t_kv[b]);
-  const int nk = k1 - k0;
   const int H = p.H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = lane & 15, gq = lane >> 4;
   const float scale2 = scale * 1.44269504088896341f;
+  int b = 0, nrow = 1, sc = 0, k0 = 0, k1 = 0;
+  const void* kbase;
+  const void* vbase;
+  if constexpr (GROUPED) {
+    int gi = 0;
+#pragma unroll
+    for (int i = 1; i < KD_MAX_B; ++i)
+      if (item >= p.grp_off[i]) gi = i;
+    b = p.grp_row[gi];
+    nrow = p.grp_n[gi];
+    sc = item - p.grp_off[gi];  // chunk index, the same for every row of the group
+    k0 = sc * p.grp_chunk[gi];
+    k1 = min(k0 + p.grp_chunk[gi], p.grp_t[gi]);
+    kbase = p.grp_k[gi];
+    vbase = p.grp_v[gi];
+  } else {
+#pragma unroll
+    for (int i = 1; i < KD_MAX_B; ++i)
+      if (item >= p.split_off[i]) b = i;
+    sc = item - p.split_off[b];
+    k0 = sc * p.chunk[b];
+    k1 = min(k0 + p.chunk[b], p.t_kv[b]);
+    kbase = rc.k[b];
+    vbase = rc.v[b];
+  }
+  const int ncol = GROUPED ? nrow * R : R;
+  const int nk = k1 - k0;
+  // Grouped: per-column facts, fetched before the K/V loads (loads complete in issue order):
+  // the row of column n and, for the columns this thread writes out, their row's t_kv and
+  // first split item.
+  constexpr int KO = (C * HD + 64 * NW - 1) / (64 * NW);
+  int tn = 0, t_out[KO], so_out[KO], t_ml = 0, so_ml = 0;
+  if constexpr (GROUPED) {
+    tn = p.t_kv[b + (n < ncol ? n / R : 0)];
+#pragma unroll
+    for (int k = 0; k < KO; ++k) {
+      const int h = min((tid + 64 * NW * k) / HD, ncol - 1);
+      t_out[k] = p.t_kv[b + h / R];
+      so_out[k] = p.split_off[b + h / R];
+    }
+    const int hm = tid < ncol ? tid : 0;
+    t_ml = p.t_kv[b + hm / R];
+    so_ml = p.split_off[b + hm / R];
+  }
 
   __shared__ float tmax[2][NW][16];
   __shared__ float red_l[NW][16];
-  __shared__ float red_o[NW][R][HD];
+  __shared__ float red_o[NW][C][HD];
   __shared__ __attribute__((aligned(16))) _Float16 qlds[2][NC][16][32];
   __shared__ float qun[16];
   __shared__ float alpha_s[2][16];
 
-  const __half* Kg = static_cast<const __half*>(rc.k[b]) + (size_t)g * capacity * HD;
-  const __half* Vg = static_cast<const __half*>(rc.v[b]) + (size_t)g * capacity * HD;
+  const __half* Kg = static_cast<const __half*>(kbase) + (size_t)g * capacity * HD;
+  const __half* Vg = static_cast<const __half*>(vbase) + (size_t)g * capacity * HD;
   // descriptors end at key k1: keys past the chunk read zeros, so offsets are base + constants
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg, (uint32_t)k1 * HD * 2);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg, (uint32_t)k1 * HD * 2);
@@ -134,9 +175,16 @@ __global__ __launch_bounds__(64 * kFaWaves) void fa_split_kernel(FaPlan p, const
     const int h = w + NW * hs;
 #pragma unroll
     for (int i = 0; i < HD / 64; ++i)
-      xs[hs][i] = h < R ? q[(size_t)b * ldq + (size_t)(g * R + h) * HD + lane + 64 * i] : 0.0f;
+      xs[hs][i] = h < ncol ? q[(size_t)(b + h / R) * ldq + (size_t)(g * R + h % R) * HD + lane + 64 * i] : 0.0f;
   }
 
+  // keys of this chunk that column n's row attends (grouped: columns past the group's, and
+  // rows that end before this chunk, whose partials are dropped, keep the chunk's count)
+  int nkc = nk;
+  if constexpr (GROUPED) {
+    const int kc = n < ncol ? min(k1, tn) : k1;
+    nkc = kc > k0 ? kc - k0 : nk;
+  }
   float m_run = -INFINITY;  // running max of head n (every lane of column n holds it)
   float l_run = 0.0f;       // this lane's share of head n's exp-sum
   fa_v4f o[8];              // o[m][s]: head 4gq + s, dim 8n + m (scaled by 2^14)
@@ -200,7 +248,7 @@ __global__ __launch_bounds__(64 * kFaWaves) void fa_split_kernel(FaPlan p, const
     float mx = -INFINITY;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      pv[s] = wk + 4 * gq + s < nk ? acc[s] * qunscale : -INFINITY;
+      pv[s] = wk + 4 * gq + s < nkc ? acc[s] * qunscale : -INFINITY;
       mx = fmaxf(mx, pv[s]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
@@ -255,7 +303,7 @@ __global__ __launch_bounds__(64 * kFaWaves) void fa_split_kernel(FaPlan p, const
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int h = 4 * gq + s;
-      if (h < R)
+      if (h < C)
 #pragma unroll
         for (int m = 0; m < 8; ++m) red_o[w][h][8 * n + m] = o[m][s];
     }
@@ -264,19 +312,43 @@ __global__ __launch_bounds__(64 * kFaWaves) void fa_split_kernel(FaPlan p, const
   float* po = ws;                                  // [items][H][HD]
   float* pm = ws + (size_t)p.n_items * H * HD;     // [items][H]
   float* pl2 = pm + (size_t)p.n_items * H;         // [items][H]
-  for (int idx = tid; idx < R * HD; idx += 64 * NW) {
-    const int h = idx / HD, d = idx % HD;
-    float v = red_o[0][h][d];
+  // column h's partials go to its row's own split item (rows whose keys end before this chunk
+  // have no such item: their columns are dropped)
+  if constexpr (GROUPED) {
 #pragma unroll
-    for (int ww = 1; ww < NW; ++ww) v += red_o[ww][h][d];
-    po[((size_t)item * H + g * R) * HD + idx] = v * kPInv;
-  }
-  if (tid < R) {
-    float l = red_l[0][tid];
+    for (int k = 0; k < KO; ++k) {
+      const int idx = tid + 64 * NW * k;
+      const int h = idx / HD, d = idx % HD;
+      if (idx < ncol * HD && k0 < t_out[k]) {
+        float v = red_o[0][h][d];
 #pragma unroll
-    for (int ww = 1; ww < NW; ++ww) l += red_l[ww][tid];
-    pm[(size_t)item * H + g * R + tid] = m_run;  // lane tid holds head tid's running max
-    pl2[(size_t)item * H + g * R + tid] = l;
+        for (int ww = 1; ww < NW; ++ww) v += red_o[ww][h][d];
+        po[((size_t)(so_out[k] + sc) * H + g * R + h % R) * HD + d] = v * kPInv;
+      }
+    }
+    if (tid < ncol && k0 < t_ml) {
+      float l = red_l[0][tid];
+#pragma unroll
+      for (int ww = 1; ww < NW; ++ww) l += red_l[ww][tid];
+      const size_t it = (size_t)(so_ml + sc) * H + g * R + tid % R;
+      pm[it] = m_run;  // lane tid holds column tid's running max
+      pl2[it] = l;
+    }
+  } else {
+    for (int idx = tid; idx < R * HD; idx += 64 * NW) {
+      const int h = idx / HD, d = idx % HD;
+      float v = red_o[0][h][d];
+#pragma unroll
+      for (int ww = 1; ww < NW; ++ww) v += red_o[ww][h][d];
+      po[((size_t)item * H + g * R) * HD + idx] = v * kPInv;
+    }
+    if (tid < R) {
+      float l = red_l[0][tid];
+#pragma unroll
+      for (int ww = 1; ww < NW; ++ww) l += red_l[ww][tid];
+      pm[(size_t)item * H + g * R + tid] = m_run;  // lane tid holds head tid's running max
+      pl2[(size_t)item * H + g * R + tid] = l;
+    }
   }
 }
 
@@ -380,22 +452,66 @@ __global__ __launch_bounds__(HD) void fa_combine_kernel(FaPlan p, const float* _
   }
 }
 
+template <int R, int HD, int C>
+static void launch_fa_c(const FaPlan& p, const float* q, int ldq, const RowCaches& rc, int capacity, float scale,
+                        void* ws, hipStream_t st) {
+  int cmax = 0;
+  for (int b = 0; b < p.B; ++b) cmax = p.chunk[b] > cmax ? p.chunk[b] : cmax;
+  const dim3 grid(C > R ? p.grp_off[p.n_grp] : p.n_items, p.G);
+  if (cmax > 16 * kFaWaves)
+    fa_split_kernel<R, HD, true, C><<<grid, 64 * kFaWaves, 0, st>>>(p, q, ldq, rc, capacity, scale,
+                                                                   static_cast<float*>(ws));
+  else
+    fa_split_kernel<R, HD, false, C><<<grid, 64 * kFaWaves, 0, st>>>(p, q, ldq, rc, capacity, scale,
+                                                                    static_cast<float*>(ws));
+}
+
 template <int R, int HD>
 static void launch_fa_t(const FaPlan& p, const float* q, int ldq, const RowCaches& rc, int capacity, float scale,
                         float* out, int8_t* oq, float* od, void* ws, hipStream_t st) {
-  int cmax = 0;
-  for (int b = 0; b < p.B; ++b) cmax = p.chunk[b] > cmax ? p.chunk[b] : cmax;
-  if (cmax > 16 * kFaWaves)
-    fa_split_kernel<R, HD, true><<<dim3(p.n_items, p.G), 64 * kFaWaves, 0, st>>>(p, q, ldq, rc, capacity, scale,
-                                                                                static_cast<float*>(ws));
+  if (p.max_grp > 1)
+    launch_fa_c<R, HD, kFaGroupCols>(p, q, ldq, rc, capacity, scale, ws, st);
   else
-    fa_split_kernel<R, HD, false><<<dim3(p.n_items, p.G), 64 * kFaWaves, 0, st>>>(p, q, ldq, rc, capacity, scale,
-                                                                                 static_cast<float*>(ws));
+    launch_fa_c<R, HD, R>(p, q, ldq, rc, capacity, scale, ws, st);
   fa_combine_kernel<HD><<<dim3(p.H, p.B), HD, 0, st>>>(p, static_cast<const float*>(ws), out, oq, od);
 }
 
-void launch_fa(const FaPlan& p, const float* q, int ldq, const RowCaches& rc, int capacity, float scale, float* out,
+// Rows that can share one pass over their keys: consecutive rows of one cache (same K and V
+// base) with the same chunk size, non-decreasing t_kv, and at most kFaGroupCols query columns.
+static void fa_group_rows(FaPlan& p, const RowCaches& rc) {
+  const int R = p.H / p.G;
+  const int cap = R < kFaGroupCols ? kFaGroupCols / R : 1;
+  p.n_grp = 0;
+  p.max_grp = 0;
+  p.grp_off[0] = 0;
+  for (int b = 0; b < p.B; ++b) {
+    const int i = p.n_grp - 1;
+    const bool join = i >= 0 && p.grp_n[i] < cap && rc.k[b] == rc.k[b - 1] && rc.v[b] == rc.v[b - 1] &&
+                      p.chunk[b] == p.chunk[b - 1] && p.t_kv[b] >= p.t_kv[b - 1];
+    if (join) {
+      ++p.grp_n[i];
+    } else {
+      p.grp_row[p.n_grp] = b;
+      p.grp_n[p.n_grp] = 1;
+      ++p.n_grp;
+    }
+  }
+  for (int i = 0; i < p.n_grp; ++i) {
+    const int first = p.grp_row[i], last = first + p.grp_n[i] - 1;  // the longest row: its chunks cover the group's
+    p.grp_off[i + 1] = p.grp_off[i] + (p.split_off[last + 1] - p.split_off[last]);
+    p.max_grp = p.grp_n[i] > p.max_grp ? p.grp_n[i] : p.max_grp;
+    p.grp_chunk[i] = p.chunk[first];
+    p.grp_t[i] = p.t_kv[last];
+    p.grp_k[i] = rc.k[first];
+    p.grp_v[i] = rc.v[first];
+  }
+  for (int i = p.n_grp; i < KD_MAX_B; ++i) p.grp_off[i + 1] = p.grp_off[p.n_grp];
+}
+
+void launch_fa(const FaPlan& plan, const float* q, int ldq, const RowCaches& rc, int capacity, float scale, float* out,
                int8_t* out_qs, float* out_d, void* ws, hipStream_t st) {
+  FaPlan p = plan;
+  fa_group_rows(p, rc);
   const int R = p.H / p.G;
 #define KD_FA_CASE(RR, HH) \
   if (R == RR && p.hd == HH) return launch_fa_t<RR, HH>(p, q, ldq, rc, capacity, scale, out, out_qs, out_d, ws, st);

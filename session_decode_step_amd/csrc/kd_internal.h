@@ -205,6 +205,19 @@ struct FaPlan {
   int32_t split_off[KD_MAX_B + 1];    // prefix sums of splits per row
   int32_t chunk[KD_MAX_B];            // keys per split of each row
   int32_t t_kv[KD_MAX_B];             // keys attended by each row
+  // Row groups that share one pass over a cache (set by launch_fa from the cache pointers):
+  // consecutive rows of one cache with the same chunk size and non-decreasing t_kv, e.g. a
+  // stream's speculative-verify rows.  Group i holds rows grp_row[i] .. + grp_n[i] - 1 and
+  // runs the chunks of its longest row; the group chunk prefix sums are grp_off.
+  int n_grp;
+  int max_grp;
+  int32_t grp_off[KD_MAX_B + 1];
+  int32_t grp_row[KD_MAX_B];
+  int32_t grp_n[KD_MAX_B];
+  int32_t grp_chunk[KD_MAX_B];        // the rows' common chunk size
+  int32_t grp_t[KD_MAX_B];            // t_kv of the group's longest (last) row
+  const void* grp_k[KD_MAX_B];        // the group's K and V cache bases
+  const void* grp_v[KD_MAX_B];
 };
 int fa_chunk_for(int t_kv);
 bool fa_make_plan(FaPlan& p, int B, int H, int G, int hd, const int32_t* t_kv, int forced_chunk);
@@ -221,11 +234,10 @@ void launch_swiglu_quant(const float* g, const float* u, int rows, int n, int ld
 void launch_add(const float* x, const float* y, float* z, size_t n, hipStream_t st);
 
 // Router: logits [B][E] (written; d % 4 == 0, 16-byte aligned rows), then top-K ids and
-// softmax weights per row.
+// softmax weights per row, and per expert the (row, pair) lists routed to it (count[E],
+// rows/pairs [E][16], ascending row order).
 void launch_router(const float* z, const float* Wr, int B, int d, int E, int K, int32_t* ids, float* p, float* logits,
-                   hipStream_t st);
-void launch_bucket(const int32_t* ids, int B, int K, int E, int32_t* count, int32_t* rows, int32_t* pairs,
-                   hipStream_t st);
+                   int32_t* count, int32_t* rows, int32_t* pairs, hipStream_t st);
 void launch_moe_combine(const float* y, const float* p, const float* sh, int B, int K, int d, float* f, hipStream_t st);
 int moe_max_experts();
 int moe_max_topk();

@@ -7,8 +7,8 @@
 // (ties to the lower id), p = softmax over the k selected logits, moe_b = sum_k p_k
 // Expert_{e_k}(z_b) in rank order, plus the shared expert's output.
 //
-// How: routing and grouping run on the device (no host round trip).  The bucketing kernel
-// lists, for each expert, the (row, rank) pairs routed to it in ascending row order; the
+// How: routing and grouping run on the device (no host round trip).  The routing kernel
+// also lists, for each expert, the (row, rank) pairs routed to it in ascending row order; the
 // grouped mmvq reads each active expert's tiles once (empty experts exit before reading)
 // and treats its rows as the MFMA's activation rows, whose results never depend on which
 // other rows share the expert; the combine adds the k expert outputs of a row in rank
@@ -54,74 +54,76 @@ __global__ __launch_bounds__(64) void router_logits_kernel(const float* __restri
   if (lane == 0) logits[(size_t)b * E + e] = acc;
 }
 
-// Top-K of each row's logits, grid B, 256 threads (thread e holds expert e): K rounds, each
-// taking the largest untaken logit with ties to the lower id (a total order: the reduction
-// tree does not matter); then the softmax over the K selected logits in rank order.
-__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits, int E, int K,
-                                                          int32_t* __restrict__ ids, float* __restrict__ p) {
-  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  __shared__ float wv[4];
-  __shared__ int wi[4];
-  __shared__ float val[kMaxTopK];
-  __shared__ int sel[kMaxTopK];
-  float r = tid < E ? logits[(size_t)b * E + tid] : -INFINITY;
-  bool live = tid < E;
-  for (int k = 0; k < K; ++k) {
-    float bv = live ? r : -INFINITY;
-    int bi = live ? tid : INT_MAX;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      const float v2 = __shfl_xor(bv, m, 64);
-      const int i2 = __shfl_xor(bi, m, 64);
-      if (i2 != INT_MAX && (bi == INT_MAX || v2 > bv || (v2 == bv && i2 < bi))) {
-        bv = v2;
-        bi = i2;
-      }
-    }
-    if (lane == 0) {
-      wv[w] = bv;
-      wi[w] = bi;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      for (int ww = 1; ww < 4; ++ww)
-        if (wi[ww] != INT_MAX && (bi == INT_MAX || wv[ww] > bv || (wv[ww] == bv && wi[ww] < bi))) {
-          bv = wv[ww];
-          bi = wi[ww];
-        }
-      sel[k] = bi;
-      val[k] = bv;
-    }
-    __syncthreads();
-    if (tid == sel[k]) live = false;
-  }
-  if (tid == 0) {
-    const float mx = val[0];
-    float ex[kMaxTopK];
-    float sum = 0.0f;
-    for (int k = 0; k < K; ++k) {
-      ex[k] = expf(val[k] - mx);
-      sum += ex[k];
-    }
-    for (int k = 0; k < K; ++k) {
-      ids[b * K + k] = sel[k];
-      p[b * K + k] = ex[k] / sum;
-    }
+// Top-K of every row and the expert buckets, in one workgroup of 16 waves.  Wave b takes row b:
+// its lanes hold experts l, l + 64, l + 128, l + 192, and each of K rounds takes the largest
+// untaken logit with ties to the lower id (a total order, so the butterfly's shape does not
+// matter); then the softmax over the K selected logits in rank order.  Then thread e lists the
+// (row, rank) pairs routed to expert e in ascending row order.
+__device__ __forceinline__ void topk_merge(float& v, int& i, float v2, int i2) {
+  if (i2 != INT_MAX && (i == INT_MAX || v2 > v || (v2 == v && i2 < i))) {
+    v = v2;
+    i = i2;
   }
 }
 
-// 1 workgroup, one thread per expert: rows routed to expert e, ascending row order.
-__global__ void moe_bucket_kernel(const int32_t* __restrict__ ids, int B, int K, int E, int32_t* __restrict__ count,
-                                  int32_t* __restrict__ rows, int32_t* __restrict__ pairs) {
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+__global__ __launch_bounds__(1024) void route_bucket_kernel(const float* __restrict__ logits, int B, int E, int K,
+                                                            int32_t* __restrict__ ids, float* __restrict__ p,
+                                                            int32_t* __restrict__ count, int32_t* __restrict__ rows,
+                                                            int32_t* __restrict__ pairs) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  __shared__ int32_t sids[KD_MAX_B * kMaxTopK];
+  if (w < B) {
+    float v[kMaxExperts / 64];
+    bool live[kMaxExperts / 64];
+#pragma unroll
+    for (int i = 0; i < kMaxExperts / 64; ++i) {
+      const int e = lane + 64 * i;
+      live[i] = e < E;
+      v[i] = live[i] ? logits[(size_t)w * E + e] : 0.0f;
+    }
+    int sel[kMaxTopK];
+    float val[kMaxTopK];
+    for (int k = 0; k < K; ++k) {
+      float bv = 0.0f;
+      int bi = INT_MAX;
+#pragma unroll
+      for (int i = 0; i < kMaxExperts / 64; ++i) topk_merge(bv, bi, v[i], live[i] ? lane + 64 * i : INT_MAX);
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) {
+        const float v2 = __shfl_xor(bv, m, 64);
+        const int i2 = __shfl_xor(bi, m, 64);
+        topk_merge(bv, bi, v2, i2);
+      }
+      sel[k] = bi;
+      val[k] = bv;
+#pragma unroll
+      for (int i = 0; i < kMaxExperts / 64; ++i)
+        if (lane + 64 * i == bi) live[i] = false;
+    }
+    if (lane == 0) {
+      const float mx = val[0];
+      float ex[kMaxTopK];
+      float sum = 0.0f;
+      for (int k = 0; k < K; ++k) {
+        ex[k] = expf(val[k] - mx);
+        sum += ex[k];
+      }
+      for (int k = 0; k < K; ++k) {
+        ids[w * K + k] = sel[k];
+        p[w * K + k] = ex[k] / sum;
+        sids[w * K + k] = sel[k];
+      }
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += blockDim.x) {
     int c = 0;
-    for (int b = 0; b < B; ++b)
-      for (int k = 0; k < K; ++k)
-        if (ids[b * K + k] == e) {
-          rows[e * 16 + c] = b;
-          pairs[e * 16 + c] = b * K + k;
-          ++c;
-        }
+    for (int j = 0; j < B * K; ++j)
+      if (sids[j] == e) {
+        rows[e * 16 + c] = j / K;
+        pairs[e * 16 + c] = j;
+        ++c;
+      }
     count[e] = c;
   }
 }
@@ -138,14 +140,9 @@ __global__ void moe_combine_kernel(const float* __restrict__ y, const float* __r
 }
 
 void launch_router(const float* z, const float* Wr, int B, int d, int E, int K, int32_t* ids, float* p, float* logits,
-                   hipStream_t st) {
+                   int32_t* count, int32_t* rows, int32_t* pairs, hipStream_t st) {
   router_logits_kernel<<<dim3(E, B), 64, 0, st>>>(z, Wr, d, E, logits);
-  router_topk_kernel<<<B, 256, 0, st>>>(logits, E, K, ids, p);
-}
-
-void launch_bucket(const int32_t* ids, int B, int K, int E, int32_t* count, int32_t* rows, int32_t* pairs,
-                   hipStream_t st) {
-  moe_bucket_kernel<<<1, 256, 0, st>>>(ids, B, K, E, count, rows, pairs);
+  route_bucket_kernel<<<1, 1024, 0, st>>>(logits, B, E, K, ids, p, count, rows, pairs);
 }
 
 void launch_moe_combine(const float* y, const float* p, const float* sh, int B, int K, int d, float* f, hipStream_t st) {

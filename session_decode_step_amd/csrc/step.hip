@@ -10,7 +10,7 @@
 //   o product                                      (mmvq)
 //   residual add + post-attention norm + quantise (norm_quant)
 //   gate, up products -> silu_mul + quantise -> down product   (dense FFN)
-//   or router -> expert buckets -> grouped gate/up -> silu_mul -> grouped down,
+//   or router + expert buckets -> grouped gate/up -> silu_mul -> grouped down,
 //      shared expert, rank-ordered combine                       (MoE FFN)
 // The residual add that closes a layer is fused into the next layer's norm.  The number of
 // launches is independent of B (B is a grid dimension, never a host loop: hf2q ADR-040
@@ -365,8 +365,7 @@ extern "C" kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x
       launch_mmvq(Ly.w_down, s.act2_qs, s.act2_d, B, s.f, D, st);
     } else {
       const int E = d.n_experts, K = d.n_expert_used, Fe = d.expert_ffn, Fs = d.shared_ffn;
-      launch_router(s.z, Ly.router, B, D, E, K, s.ids, s.p, s.rlog, st);
-      launch_bucket(s.ids, B, K, E, s.count, s.rows, s.pairs, st);
+      launch_router(s.z, Ly.router, B, D, E, K, s.ids, s.p, s.rlog, s.count, s.rows, s.pairs, st);
       RowMap gu_map{s.count, s.rows, s.pairs, E, (long long)n_rowgroups(Fe) * n_quads(D), B};
       kd_weight eg = Ly.e_gate, eu = Ly.e_up, ed = Ly.e_down;
       eg.n_out = Fe;
