@@ -354,3 +354,36 @@ def test_verify_accept_exact():
             np.testing.assert_array_equal(n_acc.cpu().numpy(), ra)
             np.testing.assert_array_equal(nxt.cpu().numpy(), rn)
 
+
+
+@pytest.mark.parametrize("H,G,hd,tails", [(16, 8, 128, (8193, 4)), (32, 8, 128, (4113, 2)), (8, 8, 64, (129, 8)),
+                                          (16, 8, 128, (20000, 4))])
+def test_fa_rows_sharing_a_cache_match_their_solo_pass(H, G, hd, tails):
+    """Rows of one cache at consecutive lengths (speculative-verify rows) take one pass over
+    the keys together; every row equals its own 1-row call bit for bit, next to a row of
+    another cache, also with a forced small chunk (many splits, some rows ending early)."""
+    t0, n = tails
+    say(f"fa shared cache H={H} G={G} hd={hd} t0={t0} rows={n}")
+    r = np.random.default_rng(t0 + n)
+    cap = t0 + n + 8
+    shared, other = _caches(2, G, cap, hd)
+    for c in (shared, other):
+        c[0].copy_(torch.from_numpy(r.standard_normal((G, cap, hd)).astype(np.float16)))
+        c[1].copy_(torch.from_numpy(r.standard_normal((G, cap, hd)).astype(np.float16)))
+    t_kv = [t0 + j for j in range(n)] + [t0 // 2 + 3]
+    kb = [shared[0].data_ptr()] * n + [other[0].data_ptr()]
+    vb = [shared[1].data_ptr()] * n + [other[1].data_ptr()]
+    B = len(t_kv)
+    q = (r.standard_normal((B, H, hd)) * 0.5).astype(np.float32)
+    scale = 1.0 / math.sqrt(hd)
+    for chunk in (0, 96):
+        out = kd.kd_fa_decode_ragged(dev(q), G, kb, vb, t_kv, cap, scale, chunk=chunk).cpu().numpy()
+        for b in range(B):
+            o1 = kd.kd_fa_decode_ragged(dev(q[b:b + 1]), G, kb[b:b + 1], vb[b:b + 1], t_kv[b:b + 1], cap, scale,
+                                        chunk=chunk).cpu().numpy()
+            np.testing.assert_array_equal(o1[0].view(np.uint32), out[b].view(np.uint32))
+    # and the oracle on the first and last shared rows
+    Kn, Vn = shared[0].cpu().numpy(), shared[1].cpu().numpy()
+    for b in (0, n - 1):
+        ref = ops.attention(q[b], Kn, Vn, t_kv[b])
+        assert_close_rows(out[b].reshape(1, -1), ref.reshape(1, -1), 2e-3, f"fa shared row {b}")
