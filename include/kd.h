@@ -194,9 +194,14 @@ typedef struct {
                                activation quantiser to its own output */
   kd_weight w_down;         /* [d, F] */
   const float* router;      /* MoE: fp32 [E][d] */
-  kd_weight e_gate, e_up;   /* MoE: experts stacked by rows, expert e = rows [e Fe, (e+1) Fe) of [E Fe, d] */
+  kd_weight e_gate, e_up;   /* MoE: experts stacked by rows, expert e = rows [e Fe, (e+1) Fe) of [E Fe, d];
+                               or e_gate alone holding [E 2Fe, d] with e_up.qs NULL: expert e =
+                               rows [e 2Fe, (e+1) 2Fe), its gate and up interleaved in blocks of
+                               32 rows as w_gate above (Fe % 32 == 0), so one grouped product
+                               per layer applies SwiGLU and quantises for e_down */
   kd_weight e_down;         /* MoE: expert e = rows [e d, (e+1) d) of [E d, Fe] */
-  kd_weight s_gate, s_up;   /* MoE shared expert [Fs, d] */
+  kd_weight s_gate, s_up;   /* MoE shared expert [Fs, d]; or s_gate alone holding [2Fs, d]
+                               interleaved as w_gate, with s_up.qs NULL */
   kd_weight s_down;         /* [d, Fs] */
 } kd_layer_desc;
 

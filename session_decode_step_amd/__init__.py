@@ -188,6 +188,22 @@ def interleave_gate_up(gate: Dict, up: Dict) -> Dict:
     return _take_rows(both, order.reshape(-1))
 
 
+def interleave_experts(gate: Dict, up: Dict, n_experts: int) -> Dict:
+    """Stacked expert gate and up [E*Fe, k] as [E*2Fe, k]: expert e's rows are its gate and up
+    interleaved in blocks of 32 rows (``interleave_gate_up`` per expert)."""
+    assert gate["fmt"] == up["fmt"] and gate["k"] == up["k"] and gate["n"] == up["n"]
+    EF = gate["n"]
+    Fe = EF // n_experts
+    assert Fe * n_experts == EF and Fe % 32 == 0
+    both = {"fmt": gate["fmt"], "n": 2 * EF, "k": gate["k"], "qs": np.concatenate([gate["qs"], up["qs"]]),
+            "d": np.concatenate([gate["d"], up["d"]])}
+    e = np.arange(n_experts)[:, None, None]
+    blk = np.arange(Fe // 32)[None, :, None]
+    i = np.arange(32)[None, None, :]
+    order = np.concatenate([e * Fe + blk * 32 + i, EF + e * Fe + blk * 32 + i], axis=2)   # [E][blocks][64]
+    return _take_rows(both, order.reshape(-1))
+
+
 def rope_pair_rows(wqkv: Dict, n_heads: int, hd: int) -> Dict:
     """wqkv with each head's rows in RoPE pair order: packed row 2i = row i, 2i+1 = row i + hd/2."""
     half = hd // 2
@@ -424,8 +440,13 @@ class KdModel:
                 D.w_gate, D.w_up, D.w_down = empty, empty, empty
             if "router" in L:
                 D.router = F(L["router"])
-                D.e_gate, D.e_up, D.e_down = W(L["e_gate"]), W(L["e_up"]), W(L["e_down"])
-                D.s_gate, D.s_up, D.s_down = W(L["s_gate"]), W(L["s_up"]), W(L["s_down"])
+                if fused:   # each expert's (and the shared expert's) gate/up interleaved: one product each
+                    D.e_gate, D.e_up = W(interleave_experts(L["e_gate"], L["e_up"], sp.n_experts)), empty
+                    D.s_gate, D.s_up = W(interleave_gate_up(L["s_gate"], L["s_up"])), empty
+                else:
+                    D.e_gate, D.e_up = W(L["e_gate"]), W(L["e_up"])
+                    D.s_gate, D.s_up = W(L["s_gate"]), W(L["s_up"])
+                D.e_down, D.s_down = W(L["e_down"]), W(L["s_down"])
             else:
                 D.router = None
                 D.e_gate = D.e_up = D.e_down = D.s_gate = D.s_up = D.s_down = empty

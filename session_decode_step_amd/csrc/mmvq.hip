@@ -519,13 +519,14 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
         }
         av[e2] = (gv / (1.0f + expf(-gv))) * uv;
       }
+      const int orow = out_row ? out_row[bq] : bq;  // grouped (experts): the row's (row, rank) pair
       quant4_lane8(make_float4(av[0], av[1], av[2], av[3]), sub, true,
-                   a.epi_qs + ((size_t)bq * NQo + (m >> 2)) * 128 + (m & 3) * 8, a.epi_qd + (size_t)bq * nbpo + m);
+                   a.epi_qs + ((size_t)orow * NQo + (m >> 2)) * 128 + (m & 3) * 8, a.epi_qd + (size_t)orow * nbpo + m);
       if (m == F / 32 - 1)  // zero blocks past F (only when F is not a multiple of 128)
         for (int blk = F / 32; blk < nbpo; ++blk)
           quant4_lane8(make_float4(0.0f, 0.0f, 0.0f, 0.0f), sub, true,
-                       a.epi_qs + ((size_t)bq * NQo + (blk >> 2)) * 128 + (blk & 3) * 8,
-                       a.epi_qd + (size_t)bq * nbpo + blk);
+                       a.epi_qs + ((size_t)orow * NQo + (blk >> 2)) * 128 + (blk & 3) * 8,
+                       a.epi_qd + (size_t)orow * nbpo + blk);
     } else if (EPI == EPI_RESNORM) {
       // the workgroup's 32 rows are block m of the residual row: x1 = res + y
       const int m = blockIdx.x, Dn = a.n_out, nblk = Dn / 32;
@@ -683,15 +684,15 @@ void launch_mmvq(const kd_weight& W, const int8_t* xq, const float* xd, int B, f
 }
 
 void launch_mmvq_swiglu(const kd_weight& W, const int8_t* xq, const float* xd, int B, int8_t* out_qs, float* out_d,
-                        hipStream_t st, const float* norm_ss, int norm_n, float norm_eps) {
-  MmvqArgs a = mmvq_args(W, xq, xd, B, nullptr, 0, nullptr, nullptr);
+                        hipStream_t st, const float* norm_ss, int norm_n, float norm_eps, const RowMap* map) {
+  MmvqArgs a = mmvq_args(W, xq, xd, B, nullptr, 0, map, nullptr);
   a.epi_qs = out_qs;
   a.epi_qd = out_d;
   a.norm_ss = norm_ss;
   a.norm_n = norm_n;
   a.norm_eps = norm_eps;
   a.QW = mmvq_qw(a.NQ, KD_MMVQ_QW_SWIGLU);
-  launch_mmvq_fmt<4, EPI_SWIGLU>(W, a, 1, st);
+  launch_mmvq_fmt<4, EPI_SWIGLU>(W, a, map ? map->n_groups : 1, st);
 }
 
 // Two row groups per workgroup (one 32-element block of the residual row); two quads per

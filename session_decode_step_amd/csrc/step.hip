@@ -124,12 +124,20 @@ extern "C" kd_status kd_model_create(const kd_model_desc* desc, kd_model** out) 
     }
     if (moe) {
       KD_REQUIRE(L.router, KD_ERR_INVALID, "kd_model_create: layer %d: null router", il);
-      KD_TRY(check_weight("e_gate", il, L.e_gate, m.n_experts * m.expert_ffn, d));
-      KD_TRY(check_weight("e_up", il, L.e_up, m.n_experts * m.expert_ffn, d));
+      if (L.e_up.qs) {
+        KD_TRY(check_weight("e_gate", il, L.e_gate, m.n_experts * m.expert_ffn, d));
+        KD_TRY(check_weight("e_up", il, L.e_up, m.n_experts * m.expert_ffn, d));
+      } else {  // each expert's gate and up interleaved in blocks of 32 rows
+        KD_TRY(check_weight("e_gate (interleaved expert gate+up)", il, L.e_gate, m.n_experts * 2 * m.expert_ffn, d));
+      }
       KD_TRY(check_weight("e_down", il, L.e_down, m.n_experts * d, m.expert_ffn));
       KD_REQUIRE(m.expert_ffn % 16 == 0, KD_ERR_UNSUPPORTED, "kd_model_create: expert_ffn %% 16");
-      KD_TRY(check_weight("s_gate", il, L.s_gate, m.shared_ffn, d));
-      KD_TRY(check_weight("s_up", il, L.s_up, m.shared_ffn, d));
+      if (L.s_up.qs) {
+        KD_TRY(check_weight("s_gate", il, L.s_gate, m.shared_ffn, d));
+        KD_TRY(check_weight("s_up", il, L.s_up, m.shared_ffn, d));
+      } else {
+        KD_TRY(check_weight("s_gate (interleaved shared gate+up)", il, L.s_gate, 2 * m.shared_ffn, d));
+      }
       KD_TRY(check_weight("s_down", il, L.s_down, d, m.shared_ffn));
     }
   }
@@ -175,7 +183,8 @@ struct StepBufs {
   float *act_d, *act2_d, *hq_d, *actn_d, *ss;
   void* fa_ws;
   int32_t *ids, *count, *rows, *pairs;
-  float *p, *gup, *yp, *rlog;
+  float *p, *gup, *yp, *rlog, *shq_d;
+  int8_t* shq_qs;
   int8_t* lm_qs;
   float* lm_d;
 };
@@ -216,6 +225,8 @@ size_t carve_step(const kd_model* m, int B, const FaPlan& plan, void* ws, StepBu
     s.yp = c.take<float>((size_t)B * K * D);
     s.sh = c.take<float>((size_t)B * D);
     s.sgu = c.take<float>((size_t)B * 2 * Fs);
+    s.shq_qs = c.take<int8_t>((size_t)B * n_quads(Fs) * 128);  // the shared expert's SwiGLU rows
+    s.shq_d = c.take<float>((size_t)B * n_quads(Fs) * 4);
   }
   return c.off + 256;
 }
@@ -366,21 +377,32 @@ extern "C" kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x
     } else {
       const int E = d.n_experts, K = d.n_expert_used, Fe = d.expert_ffn, Fs = d.shared_ffn;
       launch_router(s.z, Ly.router, B, D, E, K, s.ids, s.p, s.rlog, s.count, s.rows, s.pairs, st);
-      RowMap gu_map{s.count, s.rows, s.pairs, E, (long long)n_rowgroups(Fe) * n_quads(D), B};
       kd_weight eg = Ly.e_gate, eu = Ly.e_up, ed = Ly.e_down;
-      eg.n_out = Fe;
-      eu.n_out = Fe;
       ed.n_out = D;
-      launch_mmvq(eg, s.act_qs, s.act_d, 0, s.gup, 2 * Fe, st, &gu_map);
-      launch_mmvq(eu, s.act_qs, s.act_d, 0, s.gup + Fe, 2 * Fe, st, &gu_map);
-      // shared expert gate/up (reads the same Q(z) before it is overwritten)
-      launch_mmvq(Ly.s_gate, s.act_qs, s.act_d, B, s.sgu, 2 * Fs, st);
-      launch_mmvq(Ly.s_up, s.act_qs, s.act_d, B, s.sgu + Fs, 2 * Fs, st);
-      launch_swiglu_quant(s.gup, s.gup + Fe, B * K, Fe, 2 * Fe, nullptr, s.hq_qs, s.hq_d, st);
       RowMap dn_map{s.count, s.pairs, s.pairs, E, (long long)n_rowgroups(D) * n_quads(Fe), B * K};
-      launch_mmvq(ed, s.hq_qs, s.hq_d, 0, s.yp, D, st, &dn_map);
-      launch_swiglu_quant(s.sgu, s.sgu + Fs, B, Fs, 2 * Fs, nullptr, s.act_qs, s.act_d, st);
-      launch_mmvq(Ly.s_down, s.act_qs, s.act_d, B, s.sh, D, st);
+      if (!Ly.e_up.qs) {
+        // interleaved experts: one grouped product per layer applies SwiGLU and quantises the
+        // (row, rank) rows for the down product; the shared expert likewise
+        eg.n_out = 2 * Fe;
+        RowMap gu_map{s.count, s.rows, s.pairs, E, (long long)n_rowgroups(2 * Fe) * n_quads(D), B};
+        launch_mmvq_swiglu(eg, s.act_qs, s.act_d, 0, s.hq_qs, s.hq_d, st, nullptr, 0, 0.0f, &gu_map);
+        launch_mmvq_swiglu(Ly.s_gate, s.act_qs, s.act_d, B, s.shq_qs, s.shq_d, st);
+        launch_mmvq(ed, s.hq_qs, s.hq_d, 0, s.yp, D, st, &dn_map);
+        launch_mmvq(Ly.s_down, s.shq_qs, s.shq_d, B, s.sh, D, st);
+      } else {
+        RowMap gu_map{s.count, s.rows, s.pairs, E, (long long)n_rowgroups(Fe) * n_quads(D), B};
+        eg.n_out = Fe;
+        eu.n_out = Fe;
+        launch_mmvq(eg, s.act_qs, s.act_d, 0, s.gup, 2 * Fe, st, &gu_map);
+        launch_mmvq(eu, s.act_qs, s.act_d, 0, s.gup + Fe, 2 * Fe, st, &gu_map);
+        // shared expert gate/up (reads the same Q(z) before it is overwritten)
+        launch_mmvq(Ly.s_gate, s.act_qs, s.act_d, B, s.sgu, 2 * Fs, st);
+        launch_mmvq(Ly.s_up, s.act_qs, s.act_d, B, s.sgu + Fs, 2 * Fs, st);
+        launch_swiglu_quant(s.gup, s.gup + Fe, B * K, Fe, 2 * Fe, nullptr, s.hq_qs, s.hq_d, st);
+        launch_mmvq(ed, s.hq_qs, s.hq_d, 0, s.yp, D, st, &dn_map);
+        launch_swiglu_quant(s.sgu, s.sgu + Fs, B, Fs, 2 * Fs, nullptr, s.act_qs, s.act_d, st);
+        launch_mmvq(Ly.s_down, s.act_qs, s.act_d, B, s.sh, D, st);
+      }
       launch_moe_combine(s.yp, s.p, s.sh, B, K, D, s.f, st);
     }
     base = x1;

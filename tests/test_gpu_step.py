@@ -231,7 +231,7 @@ def test_c2_full_64_steps_bit_identity():
     # sampled oracle check on the final step's logits chain is covered by test_c2_dense_q8_lm_head
 
 
-@pytest.mark.parametrize("name,B,steps", [("c1", 2, 1), ("c2", 4, 3), ("c4", 8, 2)])
+@pytest.mark.parametrize("name,B,steps", [("c1", 2, 1), ("c2", 4, 3), ("c4", 8, 2), ("c5", 16, 1)])
 def test_fused_epilogues_against_separate_launches(name, B, steps):
     """The fused layouts against the canonical ones (separate launches).
 
@@ -239,7 +239,10 @@ def test_fused_epilogues_against_separate_launches(name, B, steps):
       bit: layer 0's K/V bytes, appended slots included, are identical.
     * The O product's epilogue that adds the residual and starts the FFN RMSNorm (the
       gate/up product applies 1/rms) rounds differently from the separate norm kernel, so
-      outputs agree within the oracle bars, not bit for bit."""
+      outputs agree within the oracle bars, not bit for bit.
+    * MoE: the interleaved expert and shared-expert gate/up products with the SwiGLU
+      epilogue against separate gate, up and SwiGLU launches (the same integers and the same
+      fp32 sequence per output: the outputs agree within the bars)."""
     say(f"fused vs separate {name} B={B}")
     wl = W.workload(name, B=B, steps=steps)
     fill = "device" if name == "c4" else "seeded"
