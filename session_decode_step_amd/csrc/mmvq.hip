@@ -417,14 +417,20 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
     }
     // tiles past the wave's quads have zero weight and activation scales: they add exact zeros
     const float4 dw = *reinterpret_cast<const float4*>(dww + ((r * QW + j) * 16 + n) * 16);
+    // the tile's four block products first (independent: their latencies overlap), then the
+    // fp32 epilogue in block order
+    v4i Sb[4];
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
+    for (int jb = 0; jb < 4; ++jb)
       // Q4_0 with several row groups: nibble dots accumulated onto the quad's cached offsets
       // (the same exact integers as block_dots)
-      const v4i S = (FMT == KD_FMT_Q4_0 && RG > 1)
-                        ? __builtin_amdgcn_mfma_i32_16x16x32_i8(act_op(A0, A1, jb), w_op<FMT>(cur.w0, cur.w1, jb),
-                                                                qoff[jb], 0, 0, 0)
-                        : block_dots<FMT>(act_op(A0, A1, jb), w_op<FMT>(cur.w0, cur.w1, jb));
+      Sb[jb] = (FMT == KD_FMT_Q4_0 && RG > 1)
+                   ? __builtin_amdgcn_mfma_i32_16x16x32_i8(act_op(A0, A1, jb), w_op<FMT>(cur.w0, cur.w1, jb),
+                                                           qoff[jb], 0, 0, 0)
+                   : block_dots<FMT>(act_op(A0, A1, jb), w_op<FMT>(cur.w0, cur.w1, jb));
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+      const v4i S = Sb[jb];
       if (DEBUG) {
         const int blk = 4 * q + jb;
         const int row = (rg0 + r) * 16 + n;
