@@ -107,6 +107,12 @@ def test_attention_and_append_validation_before_launch():
     assert st == kd.KD_ERR_CAPACITY                          # t_kv > capacity
     st = L.kd_fa_decode_ragged(0x100, 2, 8, 2, 128, kb, vb, t, 64, 0.1, 0x200, 0x300, 16, None)
     assert st == kd.KD_ERR_WORKSPACE
+    tmax = (C.c_int32 * 2)(131072 + 1, 20)                   # one key past the documented maximum
+    st = L.kd_fa_decode_ragged(0x100, 2, 8, 2, 128, kb, vb, tmax, 1 << 18, 0.1, 0x200, 0x300, 1 << 30, None)
+    assert st == kd.KD_ERR_UNSUPPORTED and b"131072" in L.kd_last_error()
+    t0 = (C.c_int32 * 2)(0, 20)                              # a row with no key
+    st = L.kd_fa_decode_ragged(0x100, 2, 8, 2, 128, kb, vb, t0, 64, 0.1, 0x200, 0x300, 1 << 20, None)
+    assert st == kd.KD_ERR_UNSUPPORTED
     pos = (C.c_int32 * 2)(63, 5)
     assert L.kd_kv_append(0x10, 0x20, 2, 2, 128, kb, vb, pos, 63, None) == kd.KD_ERR_CAPACITY
     pos2 = (C.c_int32 * 2)(5, 5)

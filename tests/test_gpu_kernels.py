@@ -387,3 +387,29 @@ def test_fa_rows_sharing_a_cache_match_their_solo_pass(H, G, hd, tails):
     for b in (0, n - 1):
         ref = ops.attention(q[b], Kn, Vn, t_kv[b])
         assert_close_rows(out[b].reshape(1, -1), ref.reshape(1, -1), 2e-3, f"fa shared row {b}")
+
+
+def test_fa_decode_at_the_key_limit():
+    """A row at the documented maximum of 131072 keys (multi-tile chunks of 1024 keys, 128
+    splits) beside a short row: oracle within the bar, and bit-identical to its 1-row call."""
+    H, G, hd = 8, 2, 128
+    t_kv = [131072, 300]
+    say(f"fa at the key limit t={t_kv}")
+    r = np.random.default_rng(77)
+    cap = 131072
+    caches = _caches(2, G, cap, hd)
+    gen = torch.Generator(device="cuda").manual_seed(77)
+    for c in caches:
+        c[0].normal_(generator=gen)
+        c[1].normal_(generator=gen)
+    q = (r.standard_normal((2, H, hd)) * 0.5).astype(np.float32)
+    kb = [c[0].data_ptr() for c in caches]
+    vb = [c[1].data_ptr() for c in caches]
+    scale = 1.0 / math.sqrt(hd)
+    out = kd.kd_fa_decode_ragged(dev(q), G, kb, vb, t_kv, cap, scale).cpu().numpy()
+    for b in range(2):
+        ref = ops.attention(q[b], caches[b][0].cpu().numpy(), caches[b][1].cpu().numpy(), t_kv[b])
+        assert_close_rows(out[b].reshape(1, -1), ref.reshape(1, -1), 2e-3, f"fa key limit row {b}")
+        o1 = kd.kd_fa_decode_ragged(dev(q[b:b + 1]), G, kb[b:b + 1], vb[b:b + 1], t_kv[b:b + 1], cap, scale)
+        np.testing.assert_array_equal(o1.cpu().numpy()[0].view(np.uint32), out[b].view(np.uint32))
+
