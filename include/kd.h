@@ -164,7 +164,9 @@ kd_status kd_kv_append(const float* k, const float* v, int32_t B, int32_t G, int
                        int32_t capacity, void* stream);
 /* Workspace bytes of kd_fa_decode_ragged for these per-row key counts (host t_kv[B]). */
 size_t kd_fa_decode_workspace(int32_t B, int32_t H, int32_t hd, const int32_t* t_kv);
-/* out[b][h][:] = sum_j softmax_j(q[b][h] . K_b[g][j] * scale) V_b[g][j], j < t_kv[b],
+/* A sliding window is a view: pass k_base[b] + off hd, v_base[b] + off hd (fp16 elements) and
+ * t_kv[b] = the window's key count, with the same capacity (the head stride).
+ * out[b][h][:] = sum_j softmax_j(q[b][h] . K_b[g][j] * scale) V_b[g][j], j < t_kv[b],
  * g = h / (H/G) (memra-engine decode_batch.rs phase B, ``fa_decode_batch_seqs_v4``: one
  * launch over all rows plus one combine).  Keys are split into chunks of
  * c_b = max(128, ceil(t_b / 128)) — a function of the row's own t_kv only — and the chunk
@@ -203,6 +205,11 @@ typedef struct {
   kd_weight s_gate, s_up;   /* MoE shared expert [Fs, d]; or s_gate alone holding [2Fs, d]
                                interleaved as w_gate, with s_up.qs NULL */
   kd_weight s_down;         /* [d, Fs] */
+  int32_t swa_window;       /* sliding-window attention (memra-engine decode_batch.rs, the SWA
+                               view of the Full-attention walk): 0 = every key; W > 0: a row
+                               whose cache holds len = pos + 1 > W keys after its append attends
+                               keys [len - W, len) only, as a view of its cache at that offset
+                               (keys keep their absolute rotation) */
 } kd_layer_desc;
 
 typedef struct {

@@ -118,6 +118,17 @@ def moe_ffn(spec, L: Dict, z: np.ndarray, zq, zd, dense: Optional[DenseWeights],
     return out + _mm(L["s_down"], hq, hd, dense, blocks)
 
 
+def _attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, length: int, win: int) -> np.ndarray:
+    """Attention of one row over the ``length`` keys its cache holds after its append; with a
+    sliding window ``win`` > 0 and ``length > win``, over the last ``win`` of them only
+    (memra-engine decode_batch.rs, the SWA view of the Full-attention walk: the view starts at
+    ``length - win`` and holds ``win`` keys, which keep their absolute rotation)."""
+    if win and length > win:
+        off = length - win
+        return ops.attention(q, K[:, off:length], V[:, off:length], win)
+    return ops.attention(q, K, V, length)
+
+
 def decode_step(model: Dict, caches: OracleCaches, x_in: np.ndarray, sessions: Sequence[int],
                 pos: Sequence[int], dense: Optional[DenseWeights] = None, blocks: bool = False,
                 route_override: Optional[Dict] = None, info: Optional[Dict] = None,
@@ -147,8 +158,9 @@ def decode_step(model: Dict, caches: OracleCaches, x_in: np.ndarray, sessions: S
             s = sessions[b]
             caches.K[s][il][:, pos[b]] = k[b].astype(np.float16)
             caches.V[s][il][:, pos[b]] = v[b].astype(np.float16)
-        attn = np.stack([ops.attention(q[b], caches.K[sessions[b]][il], caches.V[sessions[b]][il],
-                                       pos[b] + 1) for b in range(B)])   # phase B: attend
+        win = int(L.get("swa_window", 0))
+        attn = np.stack([_attend(q[b], caches.K[sessions[b]][il], caches.V[sessions[b]][il], pos[b] + 1, win)
+                         for b in range(B)])                  # phase B: attend
         aq, ad = _q(attn.reshape(B, H * hd))
         x1 = x + _mm(L["wo"], aq, ad, dense, blocks)
         if trace is not None:

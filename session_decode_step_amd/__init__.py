@@ -45,7 +45,7 @@ class KdLayerDesc(C.Structure):
                 ("ffn_norm", C.c_void_p),
                 ("w_gate", KdWeight), ("w_up", KdWeight), ("w_down", KdWeight), ("router", C.c_void_p),
                 ("e_gate", KdWeight), ("e_up", KdWeight), ("e_down", KdWeight),
-                ("s_gate", KdWeight), ("s_up", KdWeight), ("s_down", KdWeight)]
+                ("s_gate", KdWeight), ("s_up", KdWeight), ("s_down", KdWeight), ("swa_window", C.c_int32)]
 
 
 class KdModelDesc(C.Structure):
@@ -423,6 +423,7 @@ class KdModel:
             slot[0] = il
             D = self.layers[il]
             D.attn_norm = F(L["attn_norm"])
+            D.swa_window = int(L.get("swa_window", 0))
             if fused:
                 D.wqkv = W(rope_pair_rows(L["wqkv"], sp.n_head + 2 * sp.n_head_kv, sp.head_dim), "wqkv")
                 D.wqkv_pair_rows = 1

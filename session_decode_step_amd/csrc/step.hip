@@ -106,6 +106,7 @@ extern "C" kd_status kd_model_create(const kd_model_desc* desc, kd_model** out) 
   for (int il = 0; il < m.n_layers; ++il) {
     const kd_layer_desc& L = m.layers[il];
     KD_REQUIRE(L.attn_norm, KD_ERR_INVALID, "kd_model_create: layer %d: null attn_norm", il);
+    KD_REQUIRE(L.swa_window >= 0, KD_ERR_INVALID, "kd_model_create: layer %d: swa_window=%d < 0", il, L.swa_window);
     KD_TRY(check_weight("wqkv", il, L.wqkv, (H + 2 * G) * hd, d));
     KD_REQUIRE(L.wqkv_pair_rows == 0 || L.wqkv_pair_rows == 1, KD_ERR_INVALID,
                "kd_model_create: layer %d: wqkv_pair_rows=%d", il, L.wqkv_pair_rows);
@@ -331,7 +332,23 @@ extern "C" kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x
       launch_mmvq(Ly.wqkv, s.act_qs, s.act_d, B, s.qkv, ldqkv, st);
       launch_rope_append(s.qkv, ldqkv, B, H, G, hd, s.cs, rc, capacity, true, st, d.rope_base);
     }
-    launch_fa(plan, s.qkv, ldqkv, rc, capacity, scale, s.attn, s.act_qs, s.act_d, s.fa_ws, st);
+    if (Ly.swa_window > 0) {
+      // sliding window: rows holding more than W keys attend the last W through a view of
+      // their cache (the row's own key count decides its split, as for full attention)
+      int32_t tw[KD_MAX_B];
+      RowCaches rw = rc;
+      for (int b = 0; b < B; ++b) {
+        const int len = pos[b] + 1, off = len > Ly.swa_window ? len - Ly.swa_window : 0;
+        tw[b] = len - off;
+        rw.k[b] = static_cast<__half*>(rc.k[b]) + (size_t)off * hd;
+        rw.v[b] = static_cast<__half*>(rc.v[b]) + (size_t)off * hd;
+      }
+      FaPlan pw;
+      fa_make_plan(pw, B, H, G, hd, tw, 0);
+      launch_fa(pw, s.qkv, ldqkv, rw, capacity, scale, s.attn, s.act_qs, s.act_d, s.fa_ws, st);
+    } else {
+      launch_fa(plan, s.qkv, ldqkv, rc, capacity, scale, s.attn, s.act_qs, s.act_d, s.fa_ws, st);
+    }
     if (norm_fusable(il)) {
       // O product + residual add + the FFN RMSNorm's quantiser and sums of squares; the
       // gate/up product applies 1/rms, SwiGLU and the quantiser for down

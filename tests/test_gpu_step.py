@@ -98,6 +98,20 @@ def test_c2_dense_q8_lm_head(B):
     _bit_identity(gw, range(B), 3, outs[-1])
 
 
+def test_c2_sliding_window_layers():
+    """The 8-layer Q8_0 stack with a 512-key sliding window on layers 0, 2, 4, 6 (ctx 1238, so
+    those layers attend the last 512 keys through a view): oracle on two rows for two steps,
+    every row bit-identical to its B = 1 run."""
+    import dataclasses
+    say("c2 sliding window")
+    base = W.workload("c2", B=4, steps=2)
+    wl = dataclasses.replace(base, spec=dataclasses.replace(base.spec, swa_window=512, swa_layers=(0, 2, 4, 6)))
+    gw = GpuWorkload(wl)
+    assert [L["swa_window"] for L in gw.model["layers"]] == [512, 0] * 4
+    outs = _oracle_follow(gw, [0, 3], range(2), dense_budget=6 << 30)
+    _bit_identity(gw, range(4), 1, outs[-1])
+
+
 def test_c2_greedy_decode_feeds_tokens_back():
     """8-layer d=2048 Q8_0 with lm_head 32000, ctx 1238, B = 4, 6 steps of greedy decoding:
     each step's tokens (kd_argmax_rows on the logits) are embedded (kd_embed_rows) as the next

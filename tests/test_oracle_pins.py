@@ -245,6 +245,32 @@ def test_router_topk_ties_and_torch():
     assert ids2.tolist() == torch.topk(torch.tensor(rr), 8).indices.tolist()
 
 
+def test_sliding_window_is_a_positional_mask():
+    """The window view (the last W keys of the cache) against the plain definition: softmax
+    over every key with the keys before len - W masked out; a window at least len long is
+    full attention."""
+    from oracle.step import _attend
+    r = np.random.default_rng(21)
+    G, H, hd, cap = 2, 4, 64, 80
+    K = r.standard_normal((G, cap, hd)).astype(np.float16)
+    V = r.standard_normal((G, cap, hd)).astype(np.float16)
+    q = r.standard_normal((H, hd))
+    for length, win in ((50, 16), (50, 49), (17, 16), (16, 16), (10, 32)):
+        got = _attend(q, K, V, length, win)
+        lo = max(0, length - win)
+        ref = np.empty((H, hd))
+        for h in range(H):
+            g = h // (H // G)
+            sc = (K[g, :length].astype(np.float64) @ q[h]) / np.sqrt(hd)
+            sc[:lo] = -np.inf
+            p = np.exp(sc - sc.max())
+            p /= p.sum()
+            ref[h] = p @ V[g, :length].astype(np.float64)
+        np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+        if win >= length:
+            np.testing.assert_array_equal(got, ops.attention(q, K, V, length))
+
+
 # --------------------------------------------------------------------------- next token
 def test_greedy_token_hand_cases():
     # first maximum wins on ties; a lone entry; all-equal and all -inf rows give index 0

@@ -67,6 +67,8 @@ class ModelSpec:
     shared_ffn: int = 0
     rope_base: float = 10000.0
     rms_eps: float = 1e-5
+    swa_window: int = 0                  # sliding-window attention width (0: none)
+    swa_layers: Tuple[int, ...] = ()     # the layers that use it
 
     @property
     def qkv_rows(self) -> int:
@@ -183,6 +185,7 @@ def draw_gain(seed: int, code: int, tensor: int, layer: int, n: int) -> np.ndarr
 def make_layer(spec: ModelSpec, code: int, seed: int, il: int) -> Dict:
     d, fmt = spec.d, spec.fmt
     L: Dict = {
+        "swa_window": spec.swa_window if il in spec.swa_layers else 0,
         "attn_norm": draw_gain(seed, code, T_ATTN_NORM, il, d),
         "wqkv": draw_weight(fmt, seed, code, T_WQKV_Q, T_WQKV_D, il, spec.qkv_rows, d),
         "wo": draw_weight(fmt, seed, code, T_WO_Q, T_WO_D, il, d, spec.n_head * spec.head_dim),
