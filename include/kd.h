@@ -210,6 +210,11 @@ typedef struct {
                                whose cache holds len = pos + 1 > W keys after its append attends
                                keys [len - W, len) only, as a view of its cache at that offset
                                (keys keep their absolute rotation) */
+  const float* q_norm;      /* QK-norm (memra-engine decode_batch.rs, the QK-norm arm of the
+                               Full-attention walk): NULL, or per-head gains [hd] -- each query
+                               head is RMS-normalised over its hd values (with rms_eps) and
+                               scaled by the gains before RoPE; needs wqkv_pair_rows == 0 */
+  const float* k_norm;      /* the same for every key head (NULL when q_norm is NULL) */
 } kd_layer_desc;
 
 typedef struct {

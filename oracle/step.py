@@ -152,6 +152,9 @@ def decode_step(model: Dict, caches: OracleCaches, x_in: np.ndarray, sessions: S
         q = qkv[:, : H * hd].reshape(B, H, hd)
         k = qkv[:, H * hd: (H + G) * hd].reshape(B, G, hd)
         v = qkv[:, (H + G) * hd:].reshape(B, G, hd)
+        if "q_norm" in L:   # QK-norm: every head RMS-normalised over its hd values, before RoPE
+            q = ops.rmsnorm(q, L["q_norm"], eps)
+            k = ops.rmsnorm(k, L["k_norm"], eps)
         q = np.stack([ops.rope_neox(q[b], pos[b], sp.rope_base) for b in range(B)])
         k = np.stack([ops.rope_neox(k[b], pos[b], sp.rope_base) for b in range(B)])
         for b in range(B):                                   # phase A: append all rows

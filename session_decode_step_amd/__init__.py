@@ -45,7 +45,8 @@ class KdLayerDesc(C.Structure):
                 ("ffn_norm", C.c_void_p),
                 ("w_gate", KdWeight), ("w_up", KdWeight), ("w_down", KdWeight), ("router", C.c_void_p),
                 ("e_gate", KdWeight), ("e_up", KdWeight), ("e_down", KdWeight),
-                ("s_gate", KdWeight), ("s_up", KdWeight), ("s_down", KdWeight), ("swa_window", C.c_int32)]
+                ("s_gate", KdWeight), ("s_up", KdWeight), ("s_down", KdWeight), ("swa_window", C.c_int32),
+                ("q_norm", C.c_void_p), ("k_norm", C.c_void_p)]
 
 
 class KdModelDesc(C.Structure):
@@ -424,7 +425,10 @@ class KdModel:
             D = self.layers[il]
             D.attn_norm = F(L["attn_norm"])
             D.swa_window = int(L.get("swa_window", 0))
-            if fused:
+            qk_norm = "q_norm" in L
+            D.q_norm = F(L["q_norm"]) if qk_norm else None
+            D.k_norm = F(L["k_norm"]) if qk_norm else None
+            if fused and not qk_norm:   # QK-norm normalises whole heads: the canonical layout
                 D.wqkv = W(rope_pair_rows(L["wqkv"], sp.n_head + 2 * sp.n_head_kv, sp.head_dim), "wqkv")
                 D.wqkv_pair_rows = 1
             else:

@@ -194,11 +194,13 @@ void launch_mmvq_rope(const kd_weight& W, const int8_t* xq, const float* xd, int
 
 // cos/sin table [B][hd/2][2] fp32 from per-row positions (angles in fp64).
 void launch_rope_table(const RowCaches& rc, int B, int hd, float base, float* cs, hipStream_t st);
+// QK-norm first when q_norm / k_norm (per-head gains [hd]) are given.
 // Rotates q (in place, rows of qkv with stride ldqkv) and k, rounds k and v to fp16 and
 // stores them at each row's position (append) or only rotates (q and k heads).  cs is the
 // per-step table, or null to evaluate cos/sin inline with the same fp64 expression.
 void launch_rope_append(float* qkv, int ldqkv, int B, int H, int G, int hd, const float* cs,
-                        const RowCaches& rc, int capacity, bool append, hipStream_t st, float base);
+                        const RowCaches& rc, int capacity, bool append, hipStream_t st, float base,
+                        const float* q_norm = nullptr, const float* k_norm = nullptr, float eps = 0.0f);
 void launch_kv_append(const float* k, const float* v, int B, int G, int hd, const RowCaches& rc, int capacity,
                       hipStream_t st);
 

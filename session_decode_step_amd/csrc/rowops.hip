@@ -103,9 +103,13 @@ void launch_rope_table(const RowCaches& rc, int B, int hd, float base, float* cs
 // grid (H + 2G, B); block hd/2 threads.  Head index h < H: query (rotate in place);
 // H <= h < H+G: key (rotate, store fp16); h >= H+G: value (store fp16).  cs is the per-step
 // table, or null to evaluate the same fp64 expression inline.
+// QK-norm (qn / kn non-null: per-head gains [hd]): each q and k head is RMS-normalised over
+// its hd values before the rotation, y = x * (1 / sqrt(sum(x^2) / hd + eps)) * gain, with the
+// head's sum of squares added by a fixed butterfly over the block's single wave.
 __global__ void rope_append_kernel(float* __restrict__ qkv, int ldqkv, int H, int G, int hd,
                                    const float* __restrict__ cs, double base, RowCaches rc, int capacity,
-                                   int append) {
+                                   int append, const float* __restrict__ qn, const float* __restrict__ kn,
+                                   float eps) {
   const int h = blockIdx.x, b = blockIdx.y, i = threadIdx.x;
   const int half = hd / 2;
   float* row = qkv + (size_t)b * ldqkv + (size_t)h * hd;
@@ -113,7 +117,15 @@ __global__ void rope_append_kernel(float* __restrict__ qkv, int ldqkv, int H, in
   if (h < H + G) {
     const float2 t = cs ? make_float2(cs[2 * (b * half + i)], cs[2 * (b * half + i) + 1]) : rope_cs(pos, i, hd, base);
     const float c = t.x, s = t.y;
-    const float x0 = row[i], x1 = row[i + half];
+    float x0 = row[i], x1 = row[i + half];
+    const float* gn = h < H ? qn : kn;
+    if (gn) {  // uniform per block
+      float ss = fmaf(x1, x1, x0 * x0);
+      for (int m = half / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, half);
+      const float inv = 1.0f / sqrtf(ss / (float)hd + eps);
+      x0 = x0 * inv * gn[i];
+      x1 = x1 * inv * gn[i + half];
+    }
     const float y0 = fmaf(x0, c, -(x1 * s));
     const float y1 = fmaf(x0, s, x1 * c);
     row[i] = y0;
@@ -131,9 +143,11 @@ __global__ void rope_append_kernel(float* __restrict__ qkv, int ldqkv, int H, in
 }
 
 void launch_rope_append(float* qkv, int ldqkv, int B, int H, int G, int hd, const float* cs, const RowCaches& rc,
-                        int capacity, bool append, hipStream_t st, float base) {
+                        int capacity, bool append, hipStream_t st, float base, const float* q_norm,
+                        const float* k_norm, float eps) {
   dim3 grid(append ? H + 2 * G : H + G, B);
-  rope_append_kernel<<<grid, hd / 2, 0, st>>>(qkv, ldqkv, H, G, hd, cs, (double)base, rc, capacity, append ? 1 : 0);
+  rope_append_kernel<<<grid, hd / 2, 0, st>>>(qkv, ldqkv, H, G, hd, cs, (double)base, rc, capacity, append ? 1 : 0,
+                                              q_norm, k_norm, eps);
 }
 
 // Plain KV append (no rotation): k and v rows [B][G][hd] fp32 -> fp16 at pos.

@@ -107,6 +107,9 @@ extern "C" kd_status kd_model_create(const kd_model_desc* desc, kd_model** out) 
     const kd_layer_desc& L = m.layers[il];
     KD_REQUIRE(L.attn_norm, KD_ERR_INVALID, "kd_model_create: layer %d: null attn_norm", il);
     KD_REQUIRE(L.swa_window >= 0, KD_ERR_INVALID, "kd_model_create: layer %d: swa_window=%d < 0", il, L.swa_window);
+    KD_REQUIRE(!L.q_norm == !L.k_norm, KD_ERR_INVALID, "kd_model_create: layer %d: q_norm and k_norm go together", il);
+    KD_REQUIRE(!L.q_norm || L.wqkv_pair_rows == 0, KD_ERR_UNSUPPORTED,
+               "kd_model_create: layer %d: QK-norm needs the canonical wqkv layout (wqkv_pair_rows = 0)", il);
     KD_TRY(check_weight("wqkv", il, L.wqkv, (H + 2 * G) * hd, d));
     KD_REQUIRE(L.wqkv_pair_rows == 0 || L.wqkv_pair_rows == 1, KD_ERR_INVALID,
                "kd_model_create: layer %d: wqkv_pair_rows=%d", il, L.wqkv_pair_rows);
@@ -330,7 +333,8 @@ extern "C" kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x
                        prenormed ? s.ss : nullptr, D, d.rms_eps);
     } else {
       launch_mmvq(Ly.wqkv, s.act_qs, s.act_d, B, s.qkv, ldqkv, st);
-      launch_rope_append(s.qkv, ldqkv, B, H, G, hd, s.cs, rc, capacity, true, st, d.rope_base);
+      launch_rope_append(s.qkv, ldqkv, B, H, G, hd, s.cs, rc, capacity, true, st, d.rope_base, Ly.q_norm, Ly.k_norm,
+                         d.rms_eps);
     }
     if (Ly.swa_window > 0) {
       // sliding window: rows holding more than W keys attend the last W through a view of

@@ -112,6 +112,19 @@ def test_c2_sliding_window_layers():
     _bit_identity(gw, range(4), 1, outs[-1])
 
 
+def test_c2_qk_norm_layers():
+    """The 8-layer Q8_0 stack with QK-norm on every layer (per-head RMSNorm of q and k before
+    RoPE, in the unfused QKV path): oracle on two rows for two steps, rows bit-identical to
+    B = 1."""
+    import dataclasses
+    say("c2 qk-norm")
+    base = W.workload("c2", B=4, steps=2)
+    wl = dataclasses.replace(base, spec=dataclasses.replace(base.spec, qk_norm=True))
+    gw = GpuWorkload(wl)
+    outs = _oracle_follow(gw, [0, 3], range(2), dense_budget=6 << 30)
+    _bit_identity(gw, range(4), 1, outs[-1])
+
+
 def test_c2_greedy_decode_feeds_tokens_back():
     """8-layer d=2048 Q8_0 with lm_head 32000, ctx 1238, B = 4, 6 steps of greedy decoding:
     each step's tokens (kd_argmax_rows on the logits) are embedded (kd_embed_rows) as the next

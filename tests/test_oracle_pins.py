@@ -271,6 +271,28 @@ def test_sliding_window_is_a_positional_mask():
             np.testing.assert_array_equal(got, ops.attention(q, K, V, length))
 
 
+def test_qk_norm_heads_have_unit_rms_after_rope():
+    """QK-norm with unit gains: every query head that enters attention, and every key head
+    written to the cache, has RMS 1 (RoPE preserves each pair's norm), whatever the raw
+    projection's scale."""
+    import dataclasses
+    spec = dataclasses.replace(TINY, qk_norm=True, rms_eps=1e-12)
+    wl = _tiny_wl(spec, 91, [(0, 0), (1, 0)], [9, 20])
+    model = wlmod.make_model(spec, wl.code, wl.seed)
+    for L in model["layers"]:
+        L["q_norm"] = np.ones_like(L["q_norm"])
+        L["k_norm"] = np.ones_like(L["k_norm"])
+    oc = oracle.OracleCaches(wl)
+    trace = []
+    oracle.decode_step(model, oc, wlmod.step_inputs(wl, 0), [0, 1], wl.positions(0), trace=trace)
+    for t in trace:
+        np.testing.assert_allclose(np.sqrt(np.mean(t["q"] ** 2, axis=-1)), 1.0, rtol=1e-9)
+        np.testing.assert_allclose(np.sqrt(np.mean(t["k"].astype(np.float64) ** 2, axis=-1)), 1.0, rtol=1e-9)
+    for s, p in ((0, 9), (1, 20)):
+        kc = oc.K[s][0][:, p].astype(np.float64)                 # the appended key, fp16
+        np.testing.assert_allclose(np.sqrt(np.mean(kc ** 2, axis=-1)), 1.0, rtol=2e-3)
+
+
 # --------------------------------------------------------------------------- next token
 def test_greedy_token_hand_cases():
     # first maximum wins on ties; a lone entry; all-equal and all -inf rows give index 0

@@ -41,6 +41,7 @@ T_SGATE_Q, T_SGATE_D, T_SUP_Q, T_SUP_D, T_SDOWN_Q, T_SDOWN_D = 20, 21, 22, 23, 2
 T_FINAL_NORM, T_LM_Q, T_LM_D = 26, 27, 28
 T_X_IN, T_K_PRE, T_V_PRE, T_LENGTHS = 29, 30, 31, 32
 T_EMBED = 33
+T_Q_NORM, T_K_NORM = 34, 35
 
 
 def rng_for(seed: int, cfg_code: int, tensor: int, layer: int = 0, index: int = 0) -> np.random.Generator:
@@ -69,6 +70,7 @@ class ModelSpec:
     rms_eps: float = 1e-5
     swa_window: int = 0                  # sliding-window attention width (0: none)
     swa_layers: Tuple[int, ...] = ()     # the layers that use it
+    qk_norm: bool = False                # per-head RMSNorm of q and k before RoPE
 
     @property
     def qkv_rows(self) -> int:
@@ -190,6 +192,9 @@ def make_layer(spec: ModelSpec, code: int, seed: int, il: int) -> Dict:
         "wqkv": draw_weight(fmt, seed, code, T_WQKV_Q, T_WQKV_D, il, spec.qkv_rows, d),
         "wo": draw_weight(fmt, seed, code, T_WO_Q, T_WO_D, il, d, spec.n_head * spec.head_dim),
     }
+    if spec.qk_norm:
+        L["q_norm"] = draw_gain(seed, code, T_Q_NORM, il, spec.head_dim)
+        L["k_norm"] = draw_gain(seed, code, T_K_NORM, il, spec.head_dim)
     if spec.has_ffn:
         L["ffn_norm"] = draw_gain(seed, code, T_FFN_NORM, il, d)
     if spec.ffn:
