@@ -215,6 +215,11 @@ typedef struct {
                                head is RMS-normalised over its hd values (with rms_eps) and
                                scaled by the gains before RoPE; needs wqkv_pair_rows == 0 */
   const float* k_norm;      /* the same for every key head (NULL when q_norm is NULL) */
+  int32_t attn_gate;        /* attention output gate (memra-engine decode_batch.rs, the gated
+                               Full-attention arm): 1 = wqkv holds H hd more rows after v, the
+                               gate (in RoPE pair order too when wqkv_pair_rows = 1), and every
+                               attention output element is multiplied by sigmoid(gate) before
+                               wo; 0 = no gate */
 } kd_layer_desc;
 
 typedef struct {

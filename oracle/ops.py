@@ -160,6 +160,12 @@ def silu(g: np.ndarray) -> np.ndarray:
     return g / (1.0 + np.exp(-g))
 
 
+def sigmoid(g: np.ndarray) -> np.ndarray:
+    """``1 / (1 + e^-g)`` in fp64 (memra-engine decode_batch.rs, the attention output gate)."""
+    g = np.asarray(g, dtype=np.float64)
+    return 1.0 / (1.0 + np.exp(-g))
+
+
 def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
     """``silu(g) * u`` (memra-engine decode_batch.rs, ``silu_mul`` between gate/up and down)."""
     return silu(g) * np.asarray(u, dtype=np.float64)

@@ -151,7 +151,8 @@ def decode_step(model: Dict, caches: OracleCaches, x_in: np.ndarray, sessions: S
         qkv = _mm(L["wqkv"], xq, xd, dense, blocks)
         q = qkv[:, : H * hd].reshape(B, H, hd)
         k = qkv[:, H * hd: (H + G) * hd].reshape(B, G, hd)
-        v = qkv[:, (H + G) * hd:].reshape(B, G, hd)
+        v = qkv[:, (H + G) * hd: (H + 2 * G) * hd].reshape(B, G, hd)
+        gate = qkv[:, (H + 2 * G) * hd:].reshape(B, H, hd) if L.get("attn_gate") else None
         if "q_norm" in L:   # QK-norm: every head RMS-normalised over its hd values, before RoPE
             q = ops.rmsnorm(q, L["q_norm"], eps)
             k = ops.rmsnorm(k, L["k_norm"], eps)
@@ -164,6 +165,8 @@ def decode_step(model: Dict, caches: OracleCaches, x_in: np.ndarray, sessions: S
         win = int(L.get("swa_window", 0))
         attn = np.stack([_attend(q[b], caches.K[sessions[b]][il], caches.V[sessions[b]][il], pos[b] + 1, win)
                          for b in range(B)])                  # phase B: attend
+        if gate is not None:   # output gate: every attention output element times sigmoid(gate)
+            attn = attn * ops.sigmoid(gate)
         aq, ad = _q(attn.reshape(B, H * hd))
         x1 = x + _mm(L["wo"], aq, ad, dense, blocks)
         if trace is not None:

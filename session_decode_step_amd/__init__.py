@@ -46,7 +46,7 @@ class KdLayerDesc(C.Structure):
                 ("w_gate", KdWeight), ("w_up", KdWeight), ("w_down", KdWeight), ("router", C.c_void_p),
                 ("e_gate", KdWeight), ("e_up", KdWeight), ("e_down", KdWeight),
                 ("s_gate", KdWeight), ("s_up", KdWeight), ("s_down", KdWeight), ("swa_window", C.c_int32),
-                ("q_norm", C.c_void_p), ("k_norm", C.c_void_p)]
+                ("q_norm", C.c_void_p), ("k_norm", C.c_void_p), ("attn_gate", C.c_int32)]
 
 
 class KdModelDesc(C.Structure):
@@ -428,8 +428,10 @@ class KdModel:
             qk_norm = "q_norm" in L
             D.q_norm = F(L["q_norm"]) if qk_norm else None
             D.k_norm = F(L["k_norm"]) if qk_norm else None
+            D.attn_gate = 1 if L.get("attn_gate") else 0
+            n_heads_qkv = sp.n_head + 2 * sp.n_head_kv + (sp.n_head if D.attn_gate else 0)
             if fused and not qk_norm:   # QK-norm normalises whole heads: the canonical layout
-                D.wqkv = W(rope_pair_rows(L["wqkv"], sp.n_head + 2 * sp.n_head_kv, sp.head_dim), "wqkv")
+                D.wqkv = W(rope_pair_rows(L["wqkv"], n_heads_qkv, sp.head_dim), "wqkv")
                 D.wqkv_pair_rows = 1
             else:
                 D.wqkv = W(L["wqkv"], "wqkv")

@@ -358,10 +358,14 @@ __global__ __launch_bounds__(64 * kFaWaves) void fa_split_kernel(FaPlan p, const
 // costs one memory round trip; further chunks are merged in LDS-staged batches.
 constexpr int kCombineFast = 64;
 constexpr int kCombineStage = 1024;
-template <int HD>
+template <int HD, bool GATED>
 __global__ __launch_bounds__(HD) void fa_combine_kernel(FaPlan p, const float* __restrict__ ws, float* __restrict__ out,
-                                                        int8_t* __restrict__ oq, float* __restrict__ od) {
+                                                        int8_t* __restrict__ oq, float* __restrict__ od,
+                                                        const float* __restrict__ gate, int ldg) {
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  // output gate of this element (gated layers), fetched with the partials
+  float gv = 0.0f;
+  if (GATED) gv = gate[(size_t)b * ldg + (size_t)h * HD + d];
   const int H = p.H;
   const float* po = ws;
   const float* pm = ws + (size_t)p.n_items * H * HD;
@@ -428,7 +432,8 @@ __global__ __launch_bounds__(HD) void fa_combine_kernel(FaPlan p, const float* _
       den += wl[s];
     }
   }
-  const float v = num / den;
+  float v = num / den;
+  if (GATED) v = v * (1.0f / (1.0f + expf(-gv)));
   out[((size_t)b * H + h) * HD + d] = v;
   if (oq) {
     // 8 lanes per 32-element block: lane d holds dims (d/8)*32 + 4(d%8) .. +3 after a shuffle
@@ -468,12 +473,16 @@ static void launch_fa_c(const FaPlan& p, const float* q, int ldq, const RowCache
 
 template <int R, int HD>
 static void launch_fa_t(const FaPlan& p, const float* q, int ldq, const RowCaches& rc, int capacity, float scale,
-                        float* out, int8_t* oq, float* od, void* ws, hipStream_t st) {
+                        float* out, int8_t* oq, float* od, void* ws, hipStream_t st, const float* gate) {
   if (p.max_grp > 1)
     launch_fa_c<R, HD, kFaGroupCols>(p, q, ldq, rc, capacity, scale, ws, st);
   else
     launch_fa_c<R, HD, R>(p, q, ldq, rc, capacity, scale, ws, st);
-  fa_combine_kernel<HD><<<dim3(p.H, p.B), HD, 0, st>>>(p, static_cast<const float*>(ws), out, oq, od);
+  if (gate)
+    fa_combine_kernel<HD, true><<<dim3(p.H, p.B), HD, 0, st>>>(p, static_cast<const float*>(ws), out, oq, od, gate, ldq);
+  else
+    fa_combine_kernel<HD, false><<<dim3(p.H, p.B), HD, 0, st>>>(p, static_cast<const float*>(ws), out, oq, od, nullptr,
+                                                                0);
 }
 
 // Rows that can share one pass over their keys: consecutive rows of one cache (same K and V
@@ -509,12 +518,12 @@ static void fa_group_rows(FaPlan& p, const RowCaches& rc) {
 }
 
 void launch_fa(const FaPlan& plan, const float* q, int ldq, const RowCaches& rc, int capacity, float scale, float* out,
-               int8_t* out_qs, float* out_d, void* ws, hipStream_t st) {
+               int8_t* out_qs, float* out_d, void* ws, hipStream_t st, const float* gate) {
   FaPlan p = plan;
   fa_group_rows(p, rc);
   const int R = p.H / p.G;
 #define KD_FA_CASE(RR, HH) \
-  if (R == RR && p.hd == HH) return launch_fa_t<RR, HH>(p, q, ldq, rc, capacity, scale, out, out_qs, out_d, ws, st);
+  if (R == RR && p.hd == HH) return launch_fa_t<RR, HH>(p, q, ldq, rc, capacity, scale, out, out_qs, out_d, ws, st, gate);
   KD_FA_CASE(1, 64) KD_FA_CASE(2, 64) KD_FA_CASE(4, 64) KD_FA_CASE(8, 64)
   KD_FA_CASE(1, 128) KD_FA_CASE(2, 128) KD_FA_CASE(4, 128) KD_FA_CASE(8, 128)
 #undef KD_FA_CASE

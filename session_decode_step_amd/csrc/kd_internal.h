@@ -229,8 +229,10 @@ bool fa_make_plan(FaPlan& p, int B, int H, int G, int hd, const int32_t* t_kv, i
 size_t fa_workspace_bytes(const FaPlan& p);
 // q/out fp32 [B][H][hd] (row stride ldq / H*hd); if out_qs != nullptr the combine also
 // writes the quantised output rows.
+// gate (optional, row stride ldq like q): every output element is multiplied by
+// sigmoid(gate) before it is written and quantised.
 void launch_fa(const FaPlan& p, const float* q, int ldq, const RowCaches& rc, int capacity, float scale,
-               float* out, int8_t* out_qs, float* out_d, void* ws, hipStream_t st);
+               float* out, int8_t* out_qs, float* out_d, void* ws, hipStream_t st, const float* gate = nullptr);
 bool fa_shape_supported(int H, int G, int hd);
 int fa_max_keys();
 

@@ -582,10 +582,14 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
           K[i] = __float2half_rn(y0);
           K[i + half] = __float2half_rn(y1);
         }
-      } else {
+      } else if (hh < H + 2 * G) {
         __half* V = static_cast<__half*>(a.epi_rc.v[bq]) + ((size_t)(hh - H - G) * a.epi_capacity + pos) * hd;
         V[i] = __float2half_rn(x0);
         V[i + half] = __float2half_rn(x1);
+      } else {  // output-gate rows (gated layers): stored as they are, after v in the row
+        float* gr = a.epi_q + (size_t)bq * a.epi_ldq + (size_t)hh * hd;
+        gr[i] = x0;
+        gr[i + half] = x1;
       }
     }
   }

@@ -110,7 +110,9 @@ extern "C" kd_status kd_model_create(const kd_model_desc* desc, kd_model** out) 
     KD_REQUIRE(!L.q_norm == !L.k_norm, KD_ERR_INVALID, "kd_model_create: layer %d: q_norm and k_norm go together", il);
     KD_REQUIRE(!L.q_norm || L.wqkv_pair_rows == 0, KD_ERR_UNSUPPORTED,
                "kd_model_create: layer %d: QK-norm needs the canonical wqkv layout (wqkv_pair_rows = 0)", il);
-    KD_TRY(check_weight("wqkv", il, L.wqkv, (H + 2 * G) * hd, d));
+    KD_REQUIRE(L.attn_gate == 0 || L.attn_gate == 1, KD_ERR_INVALID, "kd_model_create: layer %d: attn_gate=%d", il,
+               L.attn_gate);
+    KD_TRY(check_weight("wqkv", il, L.wqkv, (H + 2 * G + (L.attn_gate ? H : 0)) * hd, d));
     KD_REQUIRE(L.wqkv_pair_rows == 0 || L.wqkv_pair_rows == 1, KD_ERR_INVALID,
                "kd_model_create: layer %d: wqkv_pair_rows=%d", il, L.wqkv_pair_rows);
     KD_TRY(check_weight("wo", il, L.wo, d, H * hd));
@@ -202,7 +204,7 @@ size_t carve_step(const kd_model* m, int B, const FaPlan& plan, void* ws, StepBu
   s.f = c.take<float>((size_t)B * D);
   s.o = c.take<float>((size_t)B * D);
   s.z = c.take<float>((size_t)B * D);
-  s.qkv = c.take<float>((size_t)B * (H + 2 * G) * hd);
+  s.qkv = c.take<float>((size_t)B * (2 * H + 2 * G) * hd);  // q, k, v and (gated layers) the gate
   s.attn = c.take<float>((size_t)B * H * hd);
   s.cs = c.take<float>((size_t)B * hd);
   s.act_qs = c.take<int8_t>((size_t)B * n_quads(m->max_k) * 128);
@@ -295,7 +297,7 @@ extern "C" kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x
   const bool moe = d.n_experts > 0;
   const bool has_ffn = d.ffn > 0 || moe;
   const float scale = 1.0f / sqrtf((float)hd);
-  const int ldqkv = (H + 2 * G) * hd;
+  const int ldqkv = (2 * H + 2 * G) * hd;  // room for the gate rows of gated layers
 
   RowCaches rc = {};
   for (int b = 0; b < B; ++b) rc.pos[b] = pos[b];
@@ -336,6 +338,8 @@ extern "C" kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x
       launch_rope_append(s.qkv, ldqkv, B, H, G, hd, s.cs, rc, capacity, true, st, d.rope_base, Ly.q_norm, Ly.k_norm,
                          d.rms_eps);
     }
+    // gated layers: the gate rows follow v in the projection's output row (same stride)
+    const float* gate = Ly.attn_gate ? s.qkv + (size_t)(H + 2 * G) * hd : nullptr;
     if (Ly.swa_window > 0) {
       // sliding window: rows holding more than W keys attend the last W through a view of
       // their cache (the row's own key count decides its split, as for full attention)
@@ -349,9 +353,9 @@ extern "C" kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x
       }
       FaPlan pw;
       fa_make_plan(pw, B, H, G, hd, tw, 0);
-      launch_fa(pw, s.qkv, ldqkv, rw, capacity, scale, s.attn, s.act_qs, s.act_d, s.fa_ws, st);
+      launch_fa(pw, s.qkv, ldqkv, rw, capacity, scale, s.attn, s.act_qs, s.act_d, s.fa_ws, st, gate);
     } else {
-      launch_fa(plan, s.qkv, ldqkv, rc, capacity, scale, s.attn, s.act_qs, s.act_d, s.fa_ws, st);
+      launch_fa(plan, s.qkv, ldqkv, rc, capacity, scale, s.attn, s.act_qs, s.act_d, s.fa_ws, st, gate);
     }
     if (norm_fusable(il)) {
       // O product + residual add + the FFN RMSNorm's quantiser and sums of squares; the

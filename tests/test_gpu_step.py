@@ -125,6 +125,25 @@ def test_c2_qk_norm_layers():
     _bit_identity(gw, range(4), 1, outs[-1])
 
 
+def test_c2_attention_output_gate():
+    """The 8-layer Q8_0 stack with the attention output gate on every layer (H hd more
+    projection rows; each attention output element times sigmoid(gate) before wo, applied in
+    the split merge): oracle on two rows for two steps, rows bit-identical to B = 1, and the
+    fused layout (gate rows stored by the RoPE epilogue) equal to the separate launches."""
+    import dataclasses
+    say("c2 output gate")
+    base = W.workload("c2", B=4, steps=2)
+    wl = dataclasses.replace(base, spec=dataclasses.replace(base.spec, attn_gate=True))
+    gw = GpuWorkload(wl)
+    outs = _oracle_follow(gw, [0, 3], range(2), dense_budget=6 << 30)
+    _bit_identity(gw, range(4), 1, outs[-1])
+    gs = GpuWorkload(wl, model=gw.model, fused=False)
+    for s in range(2):
+        ys = gs.step(s).cpu().numpy()
+        assert_close_rows(outs[s], ys.astype(np.float64), DEEP[0], f"gated step {s} fused vs separate",
+                          elem_rel=DEEP[1])
+
+
 def test_c2_greedy_decode_feeds_tokens_back():
     """8-layer d=2048 Q8_0 with lm_head 32000, ctx 1238, B = 4, 6 steps of greedy decoding:
     each step's tokens (kd_argmax_rows on the logits) are embedded (kd_embed_rows) as the next

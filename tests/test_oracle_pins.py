@@ -293,6 +293,15 @@ def test_qk_norm_heads_have_unit_rms_after_rope():
         np.testing.assert_allclose(np.sqrt(np.mean(kc ** 2, axis=-1)), 1.0, rtol=2e-3)
 
 
+def test_sigmoid_special_cases_and_silu():
+    x = np.linspace(-30, 30, 121)
+    s = ops.sigmoid(x)
+    assert ops.sigmoid(np.array([0.0]))[0] == 0.5
+    np.testing.assert_allclose(s + ops.sigmoid(-x), 1.0, rtol=0, atol=1e-15)   # odd symmetry about 1/2
+    np.testing.assert_allclose(x * s, ops.silu(x), rtol=1e-15, atol=1e-300)     # silu(x) = x sigmoid(x)
+    assert np.all(np.diff(s) > 0) and s[0] > 0 and s[-1] < 1
+
+
 # --------------------------------------------------------------------------- next token
 def test_greedy_token_hand_cases():
     # first maximum wins on ties; a lone entry; all-equal and all -inf rows give index 0

@@ -71,10 +71,11 @@ class ModelSpec:
     swa_window: int = 0                  # sliding-window attention width (0: none)
     swa_layers: Tuple[int, ...] = ()     # the layers that use it
     qk_norm: bool = False                # per-head RMSNorm of q and k before RoPE
+    attn_gate: bool = False              # attention output scaled by sigmoid of H hd more projection rows
 
     @property
     def qkv_rows(self) -> int:
-        return (self.n_head + 2 * self.n_head_kv) * self.head_dim
+        return (self.n_head + 2 * self.n_head_kv + (self.n_head if self.attn_gate else 0)) * self.head_dim
 
     @property
     def has_ffn(self) -> bool:
@@ -188,6 +189,7 @@ def make_layer(spec: ModelSpec, code: int, seed: int, il: int) -> Dict:
     d, fmt = spec.d, spec.fmt
     L: Dict = {
         "swa_window": spec.swa_window if il in spec.swa_layers else 0,
+        "attn_gate": bool(spec.attn_gate),
         "attn_norm": draw_gain(seed, code, T_ATTN_NORM, il, d),
         "wqkv": draw_weight(fmt, seed, code, T_WQKV_Q, T_WQKV_D, il, spec.qkv_rows, d),
         "wo": draw_weight(fmt, seed, code, T_WO_Q, T_WO_D, il, d, spec.n_head * spec.head_dim),
