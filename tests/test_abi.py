@@ -183,3 +183,39 @@ def test_model_create_validation_and_step_errors():
     layers[1].wo = _fake_weight(kd.KD_FMT_Q8_0, 255, 256, 0x900000)
     assert L.kd_model_create(C.byref(desc), C.byref(h)) == kd.KD_ERR_INVALID          # wrong shape
     assert b"wo" in L.kd_last_error()
+
+
+def test_layer_variant_fields_are_validated():
+    """Sliding window, QK-norm and output-gate fields of the layer descriptor are checked by
+    kd_model_create before anything is kept."""
+    L = kd.lib()
+    h = C.c_void_p()
+
+    def create(edit):
+        desc, layers = _fake_model()
+        edit(layers[1])
+        return L.kd_model_create(C.byref(desc), C.byref(h))
+
+    def ok(edit):
+        st = create(edit)
+        if st == kd.KD_OK:
+            L.kd_model_destroy(h)
+        return st
+
+    assert ok(lambda l: setattr(l, "swa_window", 512)) == kd.KD_OK
+    assert ok(lambda l: setattr(l, "swa_window", -1)) == kd.KD_ERR_INVALID
+    assert ok(lambda l: setattr(l, "q_norm", 0x7000)) == kd.KD_ERR_INVALID            # k_norm missing
+    assert b"q_norm" in L.kd_last_error()
+
+    def qk(l, pair):
+        l.q_norm, l.k_norm, l.wqkv_pair_rows = 0x7000, 0x7100, pair
+    assert ok(lambda l: qk(l, 0)) == kd.KD_OK
+    assert ok(lambda l: qk(l, 1)) == kd.KD_ERR_UNSUPPORTED                            # needs the canonical layout
+    assert ok(lambda l: setattr(l, "attn_gate", 2)) == kd.KD_ERR_INVALID
+    assert ok(lambda l: setattr(l, "attn_gate", 1)) == kd.KD_ERR_INVALID              # wqkv lacks the gate rows
+    assert b"wqkv" in L.kd_last_error()
+
+    def gated(l):
+        l.attn_gate = 1
+        l.wqkv = _fake_weight(kd.KD_FMT_Q8_0, (2 * 4 + 2 * 2) * 64, 256, 0xA00000)
+    assert ok(gated) == kd.KD_OK
