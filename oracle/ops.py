@@ -269,3 +269,56 @@ def accept_drafts(greedy: np.ndarray, fed: np.ndarray, k: int):
         nxt.append(int(g[s, a]))
     return np.array(n_acc, dtype=np.int64), np.array(nxt, dtype=np.int64)
 
+
+
+# ---------------------------------------------------------------------------------------
+# FP8 KV cache codec
+# ---------------------------------------------------------------------------------------
+def e4m3_values() -> np.ndarray:
+    """fp64 value of each of the 256 FP8 E4M3 codes (NaN for the two NaN codes).
+
+    memra-engine decode_batch.rs, phase A of ``decode_batch_layers``: the KV append stores
+    quantised rows and an engine switch turns the store to fp8 (``kv_fp8_on``); the format is
+    not spelled out there.  Reading: the OCP 8-bit E4M3 encoding -- bit 7 sign, bits 6..3 a
+    biased exponent e (bias 7), bits 2..0 a mantissa m; e > 0: 2^(e-7) (1 + m/8); e = 0:
+    2^-6 m/8; no infinities; e = 15 with m = 7 is NaN.  One value per element, no scale.
+    """
+    vals = np.empty(256, dtype=np.float64)
+    for c in range(256):
+        s = -1.0 if c & 0x80 else 1.0
+        e, m = (c >> 3) & 0xF, c & 0x7
+        if e == 15 and m == 7:
+            vals[c] = np.nan
+        elif e == 0:
+            vals[c] = s * (m / 8.0) * 2.0 ** -6
+        else:
+            vals[c] = s * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return vals
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """uint8 E4M3 codes of x: the nearest finite code, ties to the even code (even mantissa);
+    magnitudes past 448, the largest finite value, take 448 (saturation); the sign of x --
+    including -0 -- is kept; NaN gives 0x7F (0xFF if its sign bit is set).
+
+    Reading of the store's rounding (the pages fix none): round to nearest even, saturating,
+    the usual fp8 KV-cache conversion.  Done by brute force over the 127 non-negative finite
+    codes: the code minimising |value - |x||, the even one of two at equal distance.
+    """
+    xa = np.asarray(x, dtype=np.float64)
+    vals = e4m3_values()[:0x7F]                       # codes 0x00 .. 0x7E, ascending values
+    a = np.minimum(np.abs(xa), vals[-1]).reshape(-1)
+    dist = np.abs(a[:, None] - vals[None, :])
+    best = dist.min(axis=1, keepdims=True)
+    cand = dist == best                              # one code, or two at a tie
+    codes = np.arange(0x7F)
+    even = cand & (codes[None, :] % 2 == 0)
+    pick = np.where(even.any(axis=1), even.argmax(axis=1), cand.argmax(axis=1))
+    out = pick.astype(np.uint8).reshape(xa.shape)
+    out = np.where(np.isnan(xa), np.uint8(0x7F), out)
+    return np.where(np.signbit(xa), out | np.uint8(0x80), out).astype(np.uint8)
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """fp64 values of E4M3 codes (see ``e4m3_values``)."""
+    return e4m3_values()[np.asarray(codes, dtype=np.uint8).astype(np.int64)]

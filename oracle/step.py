@@ -44,7 +44,8 @@ class DenseWeights:
 
 
 class OracleCaches:
-    """fp16 K/V of the sessions the oracle follows: ``K[s][il]`` is ``[G, capacity, hd]``."""
+    """K/V of the sessions the oracle follows: ``K[s][il]`` is ``[G, capacity, hd]``, fp16, or
+    uint8 E4M3 codes for a model with FP8 caches (``spec.kv_fp8``)."""
 
     def __init__(self, wl, sessions: Optional[Sequence[int]] = None):
         from workload import kv_prefill_many  # seeded inputs only
@@ -58,7 +59,8 @@ class OracleCaches:
             self.K[s], self.V[s] = [], []
             for il in range(sp.n_layers):
                 k0, v0 = pre[(s, il)]
-                K = np.zeros((sp.n_head_kv, wl.capacity, sp.head_dim), dtype=np.float16)
+                dt = np.uint8 if getattr(sp, "kv_fp8", False) else np.float16
+                K = np.zeros((sp.n_head_kv, wl.capacity, sp.head_dim), dtype=dt)
                 V = np.zeros_like(K)
                 K[:, : k0.shape[1]] = k0
                 V[:, : v0.shape[1]] = v0
@@ -158,12 +160,21 @@ def decode_step(model: Dict, caches: OracleCaches, x_in: np.ndarray, sessions: S
             k = ops.rmsnorm(k, L["k_norm"], eps)
         q = np.stack([ops.rope_neox(q[b], pos[b], sp.rope_base) for b in range(B)])
         k = np.stack([ops.rope_neox(k[b], pos[b], sp.rope_base) for b in range(B)])
+        fp8 = getattr(sp, "kv_fp8", False)
         for b in range(B):                                   # phase A: append all rows
             s = sessions[b]
-            caches.K[s][il][:, pos[b]] = k[b].astype(np.float16)
-            caches.V[s][il][:, pos[b]] = v[b].astype(np.float16)
+            if fp8:   # FP8 caches: the nearest E4M3 code of each value
+                caches.K[s][il][:, pos[b]] = ops.e4m3_encode(k[b])
+                caches.V[s][il][:, pos[b]] = ops.e4m3_encode(v[b])
+            else:
+                caches.K[s][il][:, pos[b]] = k[b].astype(np.float16)
+                caches.V[s][il][:, pos[b]] = v[b].astype(np.float16)
         win = int(L.get("swa_window", 0))
-        attn = np.stack([_attend(q[b], caches.K[sessions[b]][il], caches.V[sessions[b]][il], pos[b] + 1, win)
+
+        def kv(s):   # the values a row attends (codes read as their E4M3 values)
+            K, V = caches.K[s][il], caches.V[s][il]
+            return (ops.e4m3_decode(K), ops.e4m3_decode(V)) if fp8 else (K, V)
+        attn = np.stack([_attend(q[b], *kv(sessions[b]), pos[b] + 1, win)
                          for b in range(B)])                  # phase B: attend
         if gate is not None:   # output gate: every attention output element times sigmoid(gate)
             attn = attn * ops.sigmoid(gate)

@@ -498,3 +498,73 @@ def test_deep_step_is_discontinuous_at_rounding_level():
     assert nw.max() > 1e-4          # some rows cascade far beyond the input perturbation
     assert np.median(nw) < 1e-5     # most rows see no flip at all
     assert nw.max() < 2e-2          # and the spread saturates at the quantisation-noise level
+
+
+# ---------------------------------------------------------------------------------------
+# FP8 E4M3 KV codec
+# ---------------------------------------------------------------------------------------
+def test_e4m3_values_hand_cases_and_order():
+    """Worked codes of the OCP E4M3 layout (sign, 4-bit exponent with bias 7, 3-bit mantissa)."""
+    v = oracle.e4m3_values()
+    hand = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0, 0x39: 1.125,
+            0x40: 2.0, 0x77: 240.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0}
+    for c, x in hand.items():
+        assert v[c] == x, hex(c)
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF])
+    assert np.all(np.diff(v[:0x7F]) > 0)                      # codes order like their values
+    np.testing.assert_array_equal(v[0x80:0xFF], -v[:0x7F])    # sign bit mirrors (0x80 is -0)
+    assert np.signbit(v[0x80])
+
+
+def test_e4m3_matches_torch_float8():
+    """Every code decodes as torch.float8_e4m3fn does; in-range values encode as torch rounds
+    them (nearest, ties to even)."""
+    torch = pytest.importorskip("torch")
+    c = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    t = c.view(torch.float8_e4m3fn).double().numpy()
+    v = oracle.e4m3_values()
+    np.testing.assert_array_equal(np.isnan(t), np.isnan(v))
+    np.testing.assert_array_equal(t[~np.isnan(t)], v[~np.isnan(v)])
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(50000) * np.exp2(rng.uniform(-12, 8, 50000))).astype(np.float32)
+    x = x[np.abs(x) < 448]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(oracle.e4m3_encode(x.astype(np.float64)), ref)
+
+
+def test_e4m3_encode_ties_saturation_and_round_trip():
+    enc = oracle.e4m3_encode
+    # ties go to the even mantissa: 1.0625 between 1.0 (m 0) and 1.125 (m 1) -> 1.0;
+    # 1.1875 between 1.125 and 1.25 -> 1.25; 2^-10 between 0 and 2^-9 -> 0; 3 2^-10 -> 2^-8
+    assert enc(np.array([1.0625, 1.1875, 2.0 ** -10, 3 * 2.0 ** -10])).tolist() == [0x38, 0x3A, 0x00, 0x02]
+    # past 448: saturate (464 is the midpoint to the NaN code's slot)
+    assert enc(np.array([448.0, 449.0, 464.0, 1e6, -1e6])).tolist() == [0x7E, 0x7E, 0x7E, 0x7E, 0xFE]
+    assert enc(np.array([-0.0, 0.0, np.nan])).tolist() == [0x80, 0x00, 0x7F]
+    finite = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    np.testing.assert_array_equal(enc(oracle.e4m3_decode(finite)), finite)
+
+
+def test_oracle_fp8_step_appends_nearest_codes_and_attends_their_values():
+    """With FP8 caches the oracle's append writes, at each row's position, the E4M3 code
+    nearest each traced k and v value, and nothing else; its attention output equals the
+    fp16-cache step's when that step's caches hold the same values (a one-layer model)."""
+    import dataclasses
+    base = wlmod.workload("c1")
+    wl = dataclasses.replace(base, spec=dataclasses.replace(base.spec, kv_fp8=True))
+    model = wlmod.make_model(wl.spec, wl.code, wl.seed)
+    oc = oracle.OracleCaches(wl)
+    before = [oc.K[s][0].copy() for s in range(2)]
+    trace = []
+    x = wlmod.step_inputs(wl, 0)
+    pos = wl.positions(0)
+    oracle.decode_step(model, oc, x, [0, 1], pos, trace=trace)
+    for b in range(2):
+        K = oc.K[b][0]
+        np.testing.assert_array_equal(K[:, pos[b]], oracle.e4m3_encode(trace[0]["k"][b]))
+        np.testing.assert_array_equal(oracle.e4m3_encode(trace[0]["v"][b]), oc.V[b][0][:, pos[b]])
+        mask = np.ones(K.shape[1], bool)
+        mask[pos[b]] = False
+        np.testing.assert_array_equal(K[:, mask], before[b][:, mask])
+        # attention over the decoded codes, from the traced q
+        ref = oracle.attention(trace[0]["q"][b], oracle.e4m3_decode(K), oracle.e4m3_decode(oc.V[b][0]), pos[b] + 1)
+        np.testing.assert_allclose(trace[0]["attn"][b], ref, rtol=0, atol=1e-12)

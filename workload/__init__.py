@@ -72,6 +72,7 @@ class ModelSpec:
     swa_layers: Tuple[int, ...] = ()     # the layers that use it
     qk_norm: bool = False                # per-head RMSNorm of q and k before RoPE
     attn_gate: bool = False              # attention output scaled by sigmoid of H hd more projection rows
+    kv_fp8: bool = False                 # KV caches hold FP8 E4M3 codes (uint8) instead of fp16
 
     @property
     def qkv_rows(self) -> int:
@@ -259,9 +260,21 @@ def kv_prefill(wl: Workload, session: int, layer: int) -> Tuple[np.ndarray, np.n
     shape = (sp.n_head_kv, wl.prefill[session], sp.head_dim)
     rk = rng_for(wl.seed, wl.code, T_K_PRE, layer, session)
     rv = rng_for(wl.seed, wl.code, T_V_PRE, layer, session)
+    if sp.kv_fp8:
+        return fp8_codes(rk, shape), fp8_codes(rv, shape)
     k = rk.standard_normal(shape, dtype=np.float32).astype(np.float16)
     v = rv.standard_normal(shape, dtype=np.float32).astype(np.float16)
     return k, v
+
+
+def fp8_codes(rng: np.random.Generator, shape) -> np.ndarray:
+    """Random E4M3 bytes drawn field by field: a random sign, an exponent field in 4 .. 8
+    (magnitudes 2^-3 .. 2^2, about the spread of unit-variance cache values) and a random
+    mantissa; never a NaN code.  No conversion: the bytes are the inputs."""
+    sign = rng.integers(0, 2, size=shape, dtype=np.uint8) << 7
+    expo = rng.integers(4, 9, size=shape, dtype=np.uint8) << 3
+    mant = rng.integers(0, 8, size=shape, dtype=np.uint8)
+    return (sign | expo | mant).astype(np.uint8)
 
 
 def kv_prefill_many(wl: Workload, pairs, threads: int = 8):
