@@ -69,6 +69,8 @@ typedef enum {
 } kd_status;
 
 typedef enum { KD_FMT_Q8_0 = 1, KD_FMT_Q4_0 = 2, KD_FMT_F32 = 3 } kd_format;
+/* KV cache element formats (kd_model_desc.kv_format). */
+typedef enum { KD_KV_F16 = 0, KD_KV_FP8_E4M3 = 1 } kd_kv_format;
 
 #define KD_MAX_B 16
 
@@ -177,6 +179,24 @@ kd_status kd_fa_decode_ragged(const float* q, int32_t B, int32_t H, int32_t G, i
                               const int32_t* t_kv, int32_t capacity, float scale, float* out,
                               void* ws, size_t ws_bytes, void* stream);
 
+/* FP8 KV caches (memra-engine decode_batch.rs phase A stores quantised K/V rows, with an fp8
+ * switch on the store and on ``fa_decode_kvmod``; the byte format is not given there).  Read
+ * here as OCP FP8 E4M3, one byte per element, no scale: bit 7 sign, bits 6..3 exponent with
+ * bias 7, bits 2..0 mantissa, no infinities, 0x7F / 0xFF NaN.  Caches are uint8
+ * [G][capacity][hd]; everything else as the fp16 calls.
+ * kd_kv_append_fp8 stores each fp32 value as its nearest E4M3 code (ties to the even code,
+ * magnitudes past 448 saturate to +-448, NaN -> 0x7F with its sign).
+ * kd_fa_decode_ragged_fp8 widens every code to its exact value (all E4M3 values are fp16
+ * numbers) and computes what kd_fa_decode_ragged computes on those values; the same
+ * workspace (kd_fa_decode_workspace).  NaN codes are outside its input domain. */
+kd_status kd_kv_append_fp8(const float* k, const float* v, int32_t B, int32_t G, int32_t hd,
+                           void* const* k_base, void* const* v_base, const int32_t* pos,
+                           int32_t capacity, void* stream);
+kd_status kd_fa_decode_ragged_fp8(const float* q, int32_t B, int32_t H, int32_t G, int32_t hd,
+                                  const void* const* k_base, const void* const* v_base,
+                                  const int32_t* t_kv, int32_t capacity, float scale, float* out,
+                                  void* ws, size_t ws_bytes, void* stream);
+
 /* ---- whole step ---------------------------------------------------------------------- */
 typedef struct {
   const float* attn_norm;   /* [d] */
@@ -232,6 +252,10 @@ typedef struct {
   const kd_layer_desc* layers;           /* host array [n_layers] (copied by kd_model_create) */
   const float* final_norm;               /* [d] or NULL */
   kd_weight lm_head;                     /* [vocab, d] or qs NULL */
+  int32_t kv_format;                     /* KD_KV_F16 (fp16 caches, k_base/v_base [G][capacity][hd]
+                                            fp16) or KD_KV_FP8_E4M3 (uint8 codes, stored and read as
+                                            kd_kv_append_fp8 / kd_fa_decode_ragged_fp8; needs
+                                            wqkv_pair_rows == 0 on every layer) */
 } kd_model_desc;
 
 typedef struct kd_model kd_model;

@@ -87,6 +87,27 @@ __device__ __forceinline__ void split_f16(float x, _Float16& hi, _Float16& lo) {
   lo = (_Float16)(x - (float)hi);
 }
 
+// FP8 E4M3 caches: two codes (bits 0..7 and 16..23 of c) to two fp16 values, exactly.  The
+// code's magnitude bits moved to fp16 bits 13..7 read as an fp16 number equal to the code's
+// value times 2^-8 (the exponent biases differ by 8; subnormal codes land on fp16 subnormals),
+// so one multiply by 256 gives the value; every E4M3 value is an fp16 number.  The NaN codes,
+// which the append never writes for finite inputs, read as 480.
+typedef _Float16 fa_v2h __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t c) {
+  const uint32_t h = ((c & 0x007F007Fu) << 7) | ((c & 0x00800080u) << 8);
+  const fa_v2h v = __builtin_bit_cast(fa_v2h, h) * (fa_v2h){(_Float16)256.0f, (_Float16)256.0f};
+  return __builtin_bit_cast(uint32_t, v);
+}
+// Eight codes (in memory order) to eight fp16 values (in the same order).
+__device__ __forceinline__ int4 e4m3x8_to_f16x8(uint2 c) {
+  int4 r;
+  r.x = (int)e4m3x2_to_f16x2((c.x & 0xFFu) | ((c.x & 0xFF00u) << 8));
+  r.y = (int)e4m3x2_to_f16x2(((c.x >> 16) & 0xFFu) | ((c.x >> 8) & 0xFF0000u));
+  r.z = (int)e4m3x2_to_f16x2((c.y & 0xFFu) | ((c.y & 0xFF00u) << 8));
+  r.w = (int)e4m3x2_to_f16x2(((c.y >> 16) & 0xFFu) | ((c.y >> 8) & 0xFF0000u));
+  return r;
+}
+
 // MULTI: chunks may span several 128-key tiles (rows longer than 128 x 128 keys).  Without
 // it the tile loop runs once, so the running output is not live across a tile's loads and
 // the kernel needs fewer registers (more workgroups per CU); the operations are the same.
@@ -94,7 +115,9 @@ __device__ __forceinline__ void split_f16(float x, _Float16& hi, _Float16& lo) {
 // MFMA's 16 columns.  Column h is head g R + h % R of the group's row h / R; each column
 // masks the keys at or past its own row's t_kv, so a row's partials are those of its own
 // pass (the keys it does not attend score -inf and weigh exactly 0).
-template <int R, int HD, bool MULTI, int C>
+// F8: the caches hold E4M3 codes; each lane loads 8 codes where it loads 8 fp16 values
+// otherwise and widens them exactly, so every product sees the same operands.
+template <int R, int HD, bool MULTI, int C, bool F8>
 __global__ __launch_bounds__(64 * kFaWaves) void fa_split_kernel(FaPlan p, const float* __restrict__ q,
                                                                           int ldq, RowCaches rc, int capacity,
                                                                           float scale, float* __restrict__ ws) {
@@ -161,11 +184,12 @@ __global__ __launch_bounds__(64 * kFaWaves) void fa_split_kernel(FaPlan p, const
   __shared__ float qun[16];
   __shared__ float alpha_s[2][16];
 
-  const __half* Kg = static_cast<const __half*>(kbase) + (size_t)g * capacity * HD;
-  const __half* Vg = static_cast<const __half*>(vbase) + (size_t)g * capacity * HD;
+  constexpr uint32_t ES = F8 ? 1 : 2;  // bytes per cache element
+  const char* Kg = static_cast<const char*>(kbase) + (size_t)g * capacity * HD * ES;
+  const char* Vg = static_cast<const char*>(vbase) + (size_t)g * capacity * HD * ES;
   // descriptors end at key k1: keys past the chunk read zeros, so offsets are base + constants
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg, (uint32_t)k1 * HD * 2);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg, (uint32_t)k1 * HD * 2);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg, (uint32_t)k1 * HD * ES);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg, (uint32_t)k1 * HD * ES);
 
   // q of the heads this wave stages (w, w + 8), fetched before any K/V load so that waiting
   // for it never waits for the tile's K/V bytes (loads complete in issue order)
@@ -193,16 +217,28 @@ __global__ __launch_bounds__(64 * kFaWaves) void fa_split_kernel(FaPlan p, const
 
   for (int t0 = 0, par = 0; t0 < (MULTI ? nk : 1); t0 += TK, par ^= 1) {
     const int wk = t0 + 16 * w;  // this wave's first key within the chunk
-    // K: slice j -> key wk + n, dims 32j + 8gq (16 bytes)
-    const uint32_t kb = ((uint32_t)(k0 + wk + n) * HD + 8 * gq) * 2;
+    // K: slice j -> key wk + n, dims 32j + 8gq (8 elements)
+    const uint32_t kb = ((uint32_t)(k0 + wk + n) * HD + 8 * gq) * ES;
     int4 kr[NC];
+    uint2 k8[NC];
 #pragma unroll
-    for (int j = 0; j < NC; ++j) kr[j] = buf16<KD_FA_AUX>(rk, kb + j * 64);
+    for (int j = 0; j < NC; ++j) {
+      if constexpr (F8)
+        k8[j] = buf8<KD_FA_AUX>(rk, kb + j * 32);
+      else
+        kr[j] = buf16<KD_FA_AUX>(rk, kb + j * 64);
+    }
     // V: key wk + 4gq + t, dims 8n .. 8n+7 (lanes with 8n >= HD read bytes whose outputs are dropped)
-    const uint32_t vb0 = ((uint32_t)(k0 + wk + 4 * gq) * HD + 8 * n) * 2;
+    const uint32_t vb0 = ((uint32_t)(k0 + wk + 4 * gq) * HD + 8 * n) * ES;
     int4 vr[4];
+    uint2 v8[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) vr[t] = buf16<KD_FA_AUX>(rv, vb0 + t * HD * 2);
+    for (int t = 0; t < 4; ++t) {
+      if constexpr (F8)
+        v8[t] = buf8<KD_FA_AUX>(rv, vb0 + t * HD);
+      else
+        vr[t] = buf16<KD_FA_AUX>(rv, vb0 + t * HD * 2);
+    }
     __builtin_amdgcn_sched_barrier(0);  // every K and V load of the tile ahead of the math
     if (t0 == 0) {
       // q' = q * scale * log2(e) * 2^e_h for the 16 head slots (zero past R), as fp16 hi + lo
@@ -237,7 +273,7 @@ __global__ __launch_bounds__(64 * kFaWaves) void fa_split_kernel(FaPlan p, const
     fa_v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
-      const fa_v8h kv = __builtin_bit_cast(fa_v8h, kr[j]);
+      const fa_v8h kv = __builtin_bit_cast(fa_v8h, F8 ? e4m3x8_to_f16x8(k8[j]) : kr[j]);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, *reinterpret_cast<const fa_v8h*>(&qlds[0][j][n][8 * gq]), acc,
                                                    0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, *reinterpret_cast<const fa_v8h*>(&qlds[1][j][n][8 * gq]), acc,
@@ -284,6 +320,10 @@ __global__ __launch_bounds__(64 * kFaWaves) void fa_split_kernel(FaPlan p, const
         for (int s = 0; s < 4; ++s) o[m][s] *= al[s];
     }
     // O += P V, one product per dim offset m of the lane's 8 dims
+    if constexpr (F8) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) vr[t] = e4m3x8_to_f16x8(v8[t]);
+    }
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       fa_v4h vb;
@@ -457,27 +497,34 @@ __global__ __launch_bounds__(HD) void fa_combine_kernel(FaPlan p, const float* _
   }
 }
 
-template <int R, int HD, int C>
+template <int R, int HD, int C, bool F8>
 static void launch_fa_c(const FaPlan& p, const float* q, int ldq, const RowCaches& rc, int capacity, float scale,
                         void* ws, hipStream_t st) {
   int cmax = 0;
   for (int b = 0; b < p.B; ++b) cmax = p.chunk[b] > cmax ? p.chunk[b] : cmax;
   const dim3 grid(C > R ? p.grp_off[p.n_grp] : p.n_items, p.G);
   if (cmax > 16 * kFaWaves)
-    fa_split_kernel<R, HD, true, C><<<grid, 64 * kFaWaves, 0, st>>>(p, q, ldq, rc, capacity, scale,
+    fa_split_kernel<R, HD, true, C, F8><<<grid, 64 * kFaWaves, 0, st>>>(p, q, ldq, rc, capacity, scale,
                                                                    static_cast<float*>(ws));
   else
-    fa_split_kernel<R, HD, false, C><<<grid, 64 * kFaWaves, 0, st>>>(p, q, ldq, rc, capacity, scale,
+    fa_split_kernel<R, HD, false, C, F8><<<grid, 64 * kFaWaves, 0, st>>>(p, q, ldq, rc, capacity, scale,
                                                                     static_cast<float*>(ws));
 }
 
 template <int R, int HD>
 static void launch_fa_t(const FaPlan& p, const float* q, int ldq, const RowCaches& rc, int capacity, float scale,
-                        float* out, int8_t* oq, float* od, void* ws, hipStream_t st, const float* gate) {
-  if (p.max_grp > 1)
-    launch_fa_c<R, HD, kFaGroupCols>(p, q, ldq, rc, capacity, scale, ws, st);
-  else
-    launch_fa_c<R, HD, R>(p, q, ldq, rc, capacity, scale, ws, st);
+                        float* out, int8_t* oq, float* od, void* ws, hipStream_t st, const float* gate, bool f8) {
+  if (f8) {
+    if (p.max_grp > 1)
+      launch_fa_c<R, HD, kFaGroupCols, true>(p, q, ldq, rc, capacity, scale, ws, st);
+    else
+      launch_fa_c<R, HD, R, true>(p, q, ldq, rc, capacity, scale, ws, st);
+  } else {
+    if (p.max_grp > 1)
+      launch_fa_c<R, HD, kFaGroupCols, false>(p, q, ldq, rc, capacity, scale, ws, st);
+    else
+      launch_fa_c<R, HD, R, false>(p, q, ldq, rc, capacity, scale, ws, st);
+  }
   if (gate)
     fa_combine_kernel<HD, true><<<dim3(p.H, p.B), HD, 0, st>>>(p, static_cast<const float*>(ws), out, oq, od, gate, ldq);
   else
@@ -518,12 +565,12 @@ static void fa_group_rows(FaPlan& p, const RowCaches& rc) {
 }
 
 void launch_fa(const FaPlan& plan, const float* q, int ldq, const RowCaches& rc, int capacity, float scale, float* out,
-               int8_t* out_qs, float* out_d, void* ws, hipStream_t st, const float* gate) {
+               int8_t* out_qs, float* out_d, void* ws, hipStream_t st, const float* gate, bool kv_fp8) {
   FaPlan p = plan;
   fa_group_rows(p, rc);
   const int R = p.H / p.G;
 #define KD_FA_CASE(RR, HH) \
-  if (R == RR && p.hd == HH) return launch_fa_t<RR, HH>(p, q, ldq, rc, capacity, scale, out, out_qs, out_d, ws, st, gate);
+  if (R == RR && p.hd == HH) return launch_fa_t<RR, HH>(p, q, ldq, rc, capacity, scale, out, out_qs, out_d, ws, st, gate, kv_fp8);
   KD_FA_CASE(1, 64) KD_FA_CASE(2, 64) KD_FA_CASE(4, 64) KD_FA_CASE(8, 64)
   KD_FA_CASE(1, 128) KD_FA_CASE(2, 128) KD_FA_CASE(4, 128) KD_FA_CASE(8, 128)
 #undef KD_FA_CASE
@@ -561,7 +608,8 @@ static kd_status fa_check(const char* who, const float* q, int32_t B, int32_t H,
 
 static kd_status fa_run(const char* who, const float* q, int32_t B, int32_t H, int32_t G, int32_t hd,
                         const void* const* k_base, const void* const* v_base, const int32_t* t_kv, int32_t capacity,
-                        float scale, float* out, int32_t chunk, void* ws, size_t ws_bytes, void* stream) {
+                        float scale, float* out, int32_t chunk, void* ws, size_t ws_bytes, void* stream,
+                        bool kv_fp8 = false) {
   kd_status s = fa_check(who, q, B, H, G, hd, k_base, v_base, t_kv, out);
   if (s != KD_OK) return s;
   for (int b = 0; b < B; ++b)
@@ -578,7 +626,7 @@ static kd_status fa_run(const char* who, const float* q, int32_t B, int32_t H, i
     rc.v[b] = const_cast<void*>(v_base[b]);
     rc.pos[b] = t_kv[b] - 1;
   }
-  launch_fa(p, q, H * hd, rc, capacity, scale, out, nullptr, nullptr, ws, as_stream(stream));
+  launch_fa(p, q, H * hd, rc, capacity, scale, out, nullptr, nullptr, ws, as_stream(stream), nullptr, kv_fp8);
   return check_launch(who);
 }
 
@@ -608,6 +656,14 @@ extern "C" kd_status kd_fa_decode_ragged(const float* q, int32_t B, int32_t H, i
                 stream);
 }
 
+extern "C" kd_status kd_fa_decode_ragged_fp8(const float* q, int32_t B, int32_t H, int32_t G, int32_t hd,
+                                             const void* const* k_base, const void* const* v_base,
+                                             const int32_t* t_kv, int32_t capacity, float scale, float* out, void* ws,
+                                             size_t ws_bytes, void* stream) {
+  return fa_run("kd_fa_decode_ragged_fp8", q, B, H, G, hd, k_base, v_base, t_kv, capacity, scale, out, 0, ws,
+                ws_bytes, stream, true);
+}
+
 extern "C" kd_status kd_debug_fa_decode_chunked(const float* q, int32_t B, int32_t H, int32_t G, int32_t hd,
                                                 const void* const* k_base, const void* const* v_base,
                                                 const int32_t* t_kv, int32_t capacity, float scale, float* out,
@@ -617,26 +673,38 @@ extern "C" kd_status kd_debug_fa_decode_chunked(const float* q, int32_t B, int32
                 ws_bytes, stream);
 }
 
-extern "C" kd_status kd_kv_append(const float* k, const float* v, int32_t B, int32_t G, int32_t hd,
-                                  void* const* k_base, void* const* v_base, const int32_t* pos, int32_t capacity,
-                                  void* stream) {
-  KD_REQUIRE(B >= 1 && B <= KD_MAX_B, KD_ERR_UNSUPPORTED, "kd_kv_append: B=%d outside [1,16]", B);
-  KD_REQUIRE(G > 0 && hd > 0, KD_ERR_INVALID, "kd_kv_append: G=%d hd=%d", G, hd);
-  KD_REQUIRE(hd == 64 || hd == 128, KD_ERR_UNSUPPORTED, "kd_kv_append: hd=%d not 64 or 128", hd);
-  KD_REQUIRE(k && v && k_base && v_base && pos, KD_ERR_INVALID, "kd_kv_append: null pointer");
+static kd_status kv_append_run(const char* who, const float* k, const float* v, int32_t B, int32_t G, int32_t hd,
+                               void* const* k_base, void* const* v_base, const int32_t* pos, int32_t capacity,
+                               void* stream, bool kv_fp8) {
+  KD_REQUIRE(B >= 1 && B <= KD_MAX_B, KD_ERR_UNSUPPORTED, "%s: B=%d outside [1,16]", who, B);
+  KD_REQUIRE(G > 0 && hd > 0, KD_ERR_INVALID, "%s: G=%d hd=%d", who, G, hd);
+  KD_REQUIRE(hd == 64 || hd == 128, KD_ERR_UNSUPPORTED, "%s: hd=%d not 64 or 128", who, hd);
+  KD_REQUIRE(k && v && k_base && v_base && pos, KD_ERR_INVALID, "%s: null pointer", who);
   RowCaches rc = {};
   for (int b = 0; b < B; ++b) {
-    KD_REQUIRE(k_base[b] && v_base[b], KD_ERR_INVALID, "kd_kv_append: null cache pointer for row %d", b);
-    KD_REQUIRE(pos[b] >= 0, KD_ERR_INVALID, "kd_kv_append: pos[%d]=%d < 0", b, pos[b]);
-    KD_REQUIRE(pos[b] + 1 <= capacity, KD_ERR_CAPACITY, "kd_kv_append: pos[%d]=%d does not fit capacity %d", b, pos[b],
+    KD_REQUIRE(k_base[b] && v_base[b], KD_ERR_INVALID, "%s: null cache pointer for row %d", who, b);
+    KD_REQUIRE(pos[b] >= 0, KD_ERR_INVALID, "%s: pos[%d]=%d < 0", who, b, pos[b]);
+    KD_REQUIRE(pos[b] + 1 <= capacity, KD_ERR_CAPACITY, "%s: pos[%d]=%d does not fit capacity %d", who, b, pos[b],
                capacity);
     for (int a = 0; a < b; ++a)
       KD_REQUIRE(!(k_base[a] == k_base[b] && pos[a] == pos[b]), KD_ERR_INVALID,
-                 "kd_kv_append: rows %d and %d write the same cache slot", a, b);
+                 "%s: rows %d and %d write the same cache slot", who, a, b);
     rc.k[b] = k_base[b];
     rc.v[b] = v_base[b];
     rc.pos[b] = pos[b];
   }
-  launch_kv_append(k, v, B, G, hd, rc, capacity, as_stream(stream));
-  return check_launch("kd_kv_append");
+  launch_kv_append(k, v, B, G, hd, rc, capacity, as_stream(stream), kv_fp8);
+  return check_launch(who);
+}
+
+extern "C" kd_status kd_kv_append(const float* k, const float* v, int32_t B, int32_t G, int32_t hd,
+                                  void* const* k_base, void* const* v_base, const int32_t* pos, int32_t capacity,
+                                  void* stream) {
+  return kv_append_run("kd_kv_append", k, v, B, G, hd, k_base, v_base, pos, capacity, stream, false);
+}
+
+extern "C" kd_status kd_kv_append_fp8(const float* k, const float* v, int32_t B, int32_t G, int32_t hd,
+                                      void* const* k_base, void* const* v_base, const int32_t* pos,
+                                      int32_t capacity, void* stream) {
+  return kv_append_run("kd_kv_append_fp8", k, v, B, G, hd, k_base, v_base, pos, capacity, stream, true);
 }

@@ -115,6 +115,33 @@ __device__ inline float2 rope_cs(int pos, int i, int hd, double base) {
   return make_float2((float)c, (float)s);
 }
 
+// fp32 -> FP8 E4M3 code (OCP layout: sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+// infinities, 0x7F / 0xFF NaN): nearest, ties to the even code; magnitudes past 448 (the
+// largest finite value) saturate to it; NaN -> 0x7F with its sign.  Integer rounding of the
+// fp32 mantissa for normal codes; subnormal codes (|x| < 2^-6) are |x| 2^9 rounded to even.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = fabsf(x);
+  uint32_t c;
+  if (a != a) {
+    c = 0x7Fu;
+  } else if (a >= 448.0f) {
+    c = 0x7Eu;
+  } else if (a < 0.015625f) {
+    c = (uint32_t)rintf(a * 512.0f);  // 0 .. 8; 8 is 2^-6, the first normal code
+  } else {
+    const uint32_t au = __float_as_uint(a);
+    const uint32_t e = (au >> 23) - 120u;  // biased E4M3 exponent, 1 .. 15
+    const uint32_t m = au & 0x7FFFFFu;
+    uint32_t r = m >> 20;
+    const uint32_t rem = m & 0xFFFFFu;
+    r += (rem > 0x80000u || (rem == 0x80000u && (r & 1u))) ? 1u : 0u;
+    c = (e << 3) + r;  // a mantissa carry moves to the next exponent
+  }
+  return sign | c;
+}
+
 // ---- buffer loads ----------------------------------------------------------------------
 // Raw (stride 0) buffer descriptors: an offset at or past num_records reads as zero without
 // touching memory, which masks out-of-range lanes without a branch.
@@ -198,11 +225,13 @@ void launch_rope_table(const RowCaches& rc, int B, int hd, float base, float* cs
 // Rotates q (in place, rows of qkv with stride ldqkv) and k, rounds k and v to fp16 and
 // stores them at each row's position (append) or only rotates (q and k heads).  cs is the
 // per-step table, or null to evaluate cos/sin inline with the same fp64 expression.
+// kv_fp8: the caches hold FP8 E4M3 codes (f32_to_e4m3) instead of fp16.
 void launch_rope_append(float* qkv, int ldqkv, int B, int H, int G, int hd, const float* cs,
                         const RowCaches& rc, int capacity, bool append, hipStream_t st, float base,
-                        const float* q_norm = nullptr, const float* k_norm = nullptr, float eps = 0.0f);
+                        const float* q_norm = nullptr, const float* k_norm = nullptr, float eps = 0.0f,
+                        bool kv_fp8 = false);
 void launch_kv_append(const float* k, const float* v, int B, int G, int hd, const RowCaches& rc, int capacity,
-                      hipStream_t st);
+                      hipStream_t st, bool kv_fp8 = false);
 
 struct FaPlan {
   int B, H, G, hd;
@@ -231,8 +260,10 @@ size_t fa_workspace_bytes(const FaPlan& p);
 // writes the quantised output rows.
 // gate (optional, row stride ldq like q): every output element is multiplied by
 // sigmoid(gate) before it is written and quantised.
+// kv_fp8: the caches hold FP8 E4M3 codes, widened to fp16 (exactly) as they are loaded.
 void launch_fa(const FaPlan& p, const float* q, int ldq, const RowCaches& rc, int capacity, float scale,
-               float* out, int8_t* out_qs, float* out_d, void* ws, hipStream_t st, const float* gate = nullptr);
+               float* out, int8_t* out_qs, float* out_d, void* ws, hipStream_t st, const float* gate = nullptr,
+               bool kv_fp8 = false);
 bool fa_shape_supported(int H, int G, int hd);
 int fa_max_keys();
 

@@ -131,41 +131,63 @@ __global__ void rope_append_kernel(float* __restrict__ qkv, int ldqkv, int H, in
     row[i] = y0;
     row[i + half] = y1;
     if (h >= H && append) {
-      __half* K = static_cast<__half*>(rc.k[b]) + ((size_t)(h - H) * capacity + pos) * hd;
-      K[i] = __float2half_rn(y0);
-      K[i + half] = __float2half_rn(y1);
+      const size_t o = ((size_t)(h - H) * capacity + pos) * hd;
+      if (append == 2) {
+        uint8_t* K = static_cast<uint8_t*>(rc.k[b]) + o;
+        K[i] = (uint8_t)f32_to_e4m3(y0);
+        K[i + half] = (uint8_t)f32_to_e4m3(y1);
+      } else {
+        __half* K = static_cast<__half*>(rc.k[b]) + o;
+        K[i] = __float2half_rn(y0);
+        K[i + half] = __float2half_rn(y1);
+      }
     }
   } else if (append) {
-    __half* V = static_cast<__half*>(rc.v[b]) + ((size_t)(h - H - G) * capacity + pos) * hd;
-    V[i] = __float2half_rn(row[i]);
-    V[i + half] = __float2half_rn(row[i + half]);
+    const size_t o = ((size_t)(h - H - G) * capacity + pos) * hd;
+    if (append == 2) {
+      uint8_t* V = static_cast<uint8_t*>(rc.v[b]) + o;
+      V[i] = (uint8_t)f32_to_e4m3(row[i]);
+      V[i + half] = (uint8_t)f32_to_e4m3(row[i + half]);
+    } else {
+      __half* V = static_cast<__half*>(rc.v[b]) + o;
+      V[i] = __float2half_rn(row[i]);
+      V[i + half] = __float2half_rn(row[i + half]);
+    }
   }
 }
 
 void launch_rope_append(float* qkv, int ldqkv, int B, int H, int G, int hd, const float* cs, const RowCaches& rc,
                         int capacity, bool append, hipStream_t st, float base, const float* q_norm,
-                        const float* k_norm, float eps) {
+                        const float* k_norm, float eps, bool kv_fp8) {
   dim3 grid(append ? H + 2 * G : H + G, B);
-  rope_append_kernel<<<grid, hd / 2, 0, st>>>(qkv, ldqkv, H, G, hd, cs, (double)base, rc, capacity, append ? 1 : 0,
-                                              q_norm, k_norm, eps);
+  rope_append_kernel<<<grid, hd / 2, 0, st>>>(qkv, ldqkv, H, G, hd, cs, (double)base, rc, capacity,
+                                              append ? (kv_fp8 ? 2 : 1) : 0, q_norm, k_norm, eps);
 }
 
-// Plain KV append (no rotation): k and v rows [B][G][hd] fp32 -> fp16 at pos.
+// Plain KV append (no rotation): k and v rows [B][G][hd] fp32 -> fp16 (or E4M3 codes) at pos.
+template <bool F8>
 __global__ void kv_append_kernel(const float* __restrict__ k, const float* __restrict__ v, int G, int hd,
                                  RowCaches rc, int capacity) {
   const int g = blockIdx.x, b = blockIdx.y;
   const size_t src = ((size_t)b * G + g) * hd;
-  __half* K = static_cast<__half*>(rc.k[b]) + ((size_t)g * capacity + rc.pos[b]) * hd;
-  __half* V = static_cast<__half*>(rc.v[b]) + ((size_t)g * capacity + rc.pos[b]) * hd;
+  const size_t o = ((size_t)g * capacity + rc.pos[b]) * hd;
   for (int i = threadIdx.x; i < hd; i += blockDim.x) {
-    K[i] = __float2half_rn(k[src + i]);
-    V[i] = __float2half_rn(v[src + i]);
+    if (F8) {
+      static_cast<uint8_t*>(rc.k[b])[o + i] = (uint8_t)f32_to_e4m3(k[src + i]);
+      static_cast<uint8_t*>(rc.v[b])[o + i] = (uint8_t)f32_to_e4m3(v[src + i]);
+    } else {
+      static_cast<__half*>(rc.k[b])[o + i] = __float2half_rn(k[src + i]);
+      static_cast<__half*>(rc.v[b])[o + i] = __float2half_rn(v[src + i]);
+    }
   }
 }
 
 void launch_kv_append(const float* k, const float* v, int B, int G, int hd, const RowCaches& rc, int capacity,
-                      hipStream_t st) {
-  kv_append_kernel<<<dim3(G, B), 64, 0, st>>>(k, v, G, hd, rc, capacity);
+                      hipStream_t st, bool kv_fp8) {
+  if (kv_fp8)
+    kv_append_kernel<true><<<dim3(G, B), 64, 0, st>>>(k, v, G, hd, rc, capacity);
+  else
+    kv_append_kernel<false><<<dim3(G, B), 64, 0, st>>>(k, v, G, hd, rc, capacity);
 }
 
 // ---------------------------------------------------------------------------------------

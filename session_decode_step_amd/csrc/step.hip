@@ -91,6 +91,8 @@ extern "C" kd_status kd_model_create(const kd_model_desc* desc, kd_model** out) 
              "kd_model_create: H=%d G=%d hd=%d unsupported (H/G in {1,2,4,8}, hd in {64,128})", m.n_head, m.n_head_kv,
              m.head_dim);
   KD_REQUIRE(m.rms_eps > 0 && m.rope_base > 0, KD_ERR_INVALID, "kd_model_create: eps / rope base");
+  KD_REQUIRE(m.kv_format == KD_KV_F16 || m.kv_format == KD_KV_FP8_E4M3, KD_ERR_INVALID,
+             "kd_model_create: kv_format=%d", m.kv_format);
   const int H = m.n_head, G = m.n_head_kv, hd = m.head_dim, d = m.d;
   const bool moe = m.n_experts > 0;
   if (moe) {
@@ -115,6 +117,8 @@ extern "C" kd_status kd_model_create(const kd_model_desc* desc, kd_model** out) 
     KD_TRY(check_weight("wqkv", il, L.wqkv, (H + 2 * G + (L.attn_gate ? H : 0)) * hd, d));
     KD_REQUIRE(L.wqkv_pair_rows == 0 || L.wqkv_pair_rows == 1, KD_ERR_INVALID,
                "kd_model_create: layer %d: wqkv_pair_rows=%d", il, L.wqkv_pair_rows);
+    KD_REQUIRE(L.wqkv_pair_rows == 0 || m.kv_format == KD_KV_F16, KD_ERR_UNSUPPORTED,
+               "kd_model_create: layer %d: FP8 caches need the canonical wqkv layout (wqkv_pair_rows = 0)", il);
     KD_TRY(check_weight("wo", il, L.wo, d, H * hd));
     if (m.ffn > 0 || moe) KD_REQUIRE(L.ffn_norm, KD_ERR_INVALID, "kd_model_create: layer %d: null ffn_norm", il);
     if (m.ffn > 0) {
@@ -297,6 +301,8 @@ extern "C" kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x
   const bool moe = d.n_experts > 0;
   const bool has_ffn = d.ffn > 0 || moe;
   const float scale = 1.0f / sqrtf((float)hd);
+  const bool kv8 = d.kv_format == KD_KV_FP8_E4M3;  // caches hold E4M3 codes
+  const size_t kv_es = kv8 ? 1 : 2;               // bytes per cache element
   const int ldqkv = (2 * H + 2 * G) * hd;  // room for the gate rows of gated layers
 
   RowCaches rc = {};
@@ -336,7 +342,7 @@ extern "C" kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x
     } else {
       launch_mmvq(Ly.wqkv, s.act_qs, s.act_d, B, s.qkv, ldqkv, st);
       launch_rope_append(s.qkv, ldqkv, B, H, G, hd, s.cs, rc, capacity, true, st, d.rope_base, Ly.q_norm, Ly.k_norm,
-                         d.rms_eps);
+                         d.rms_eps, kv8);
     }
     // gated layers: the gate rows follow v in the projection's output row (same stride)
     const float* gate = Ly.attn_gate ? s.qkv + (size_t)(H + 2 * G) * hd : nullptr;
@@ -348,14 +354,14 @@ extern "C" kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x
       for (int b = 0; b < B; ++b) {
         const int len = pos[b] + 1, off = len > Ly.swa_window ? len - Ly.swa_window : 0;
         tw[b] = len - off;
-        rw.k[b] = static_cast<__half*>(rc.k[b]) + (size_t)off * hd;
-        rw.v[b] = static_cast<__half*>(rc.v[b]) + (size_t)off * hd;
+        rw.k[b] = static_cast<char*>(rc.k[b]) + (size_t)off * hd * kv_es;
+        rw.v[b] = static_cast<char*>(rc.v[b]) + (size_t)off * hd * kv_es;
       }
       FaPlan pw;
       fa_make_plan(pw, B, H, G, hd, tw, 0);
-      launch_fa(pw, s.qkv, ldqkv, rw, capacity, scale, s.attn, s.act_qs, s.act_d, s.fa_ws, st, gate);
+      launch_fa(pw, s.qkv, ldqkv, rw, capacity, scale, s.attn, s.act_qs, s.act_d, s.fa_ws, st, gate, kv8);
     } else {
-      launch_fa(plan, s.qkv, ldqkv, rc, capacity, scale, s.attn, s.act_qs, s.act_d, s.fa_ws, st, gate);
+      launch_fa(plan, s.qkv, ldqkv, rc, capacity, scale, s.attn, s.act_qs, s.act_d, s.fa_ws, st, gate, kv8);
     }
     if (norm_fusable(il)) {
       // O product + residual add + the FFN RMSNorm's quantiser and sums of squares; the

@@ -26,7 +26,8 @@ class GpuWorkload:
         self.model = model if model is not None else W.make_model(sp, wl.code, wl.seed)
         self.km = KdModel(self.model, device, fused=fused)
         n_sess = len(wl.prefill)
-        self.caches = SessionCaches(n_sess, sp.n_layers, sp.n_head_kv, wl.capacity, sp.head_dim, device)
+        self.caches = SessionCaches(n_sess, sp.n_layers, sp.n_head_kv, wl.capacity, sp.head_dim, device,
+                                    fp8=sp.kv_fp8)
         fill_sessions = range(n_sess) if sessions is None else sessions
         if fill == "seeded":
             for s in fill_sessions:
@@ -39,7 +40,11 @@ class GpuWorkload:
                 gen.manual_seed(1000003 * (wl.seed + 1) + s)
                 L = wl.prefill[s]
                 t = self.caches.t[s]
-                t[:, :, :, :L].normal_(generator=gen)
+                if sp.kv_fp8:   # random E4M3 bytes: sign, exponent field 4 .. 8, mantissa
+                    c = torch.randint(0, 80, t[:, :, :, :L].shape, generator=gen, device=device)
+                    t[:, :, :, :L] = (((c & 1) << 7) | ((4 + (c >> 4)) << 3) | ((c >> 1) & 7)).to(torch.uint8)
+                else:
+                    t[:, :, :, :L].normal_(generator=gen)
         self.device = device
         last = max(0, wl.steps - 1)
         self.ws = torch.empty(self.km.workspace_bytes(wl.B, wl.positions(last)) + 4096, dtype=torch.uint8,

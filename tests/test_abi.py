@@ -219,3 +219,45 @@ def test_layer_variant_fields_are_validated():
         l.attn_gate = 1
         l.wqkv = _fake_weight(kd.KD_FMT_Q8_0, (2 * 4 + 2 * 2) * 64, 256, 0xA00000)
     assert ok(gated) == kd.KD_OK
+
+
+def test_kv_format_is_validated():
+    """kd_model_create accepts fp16 and E4M3 caches only, and E4M3 caches only with the
+    canonical wqkv layout (the appends are stored by the separate RoPE launch)."""
+    L = kd.lib()
+    h = C.c_void_p()
+
+    def create(fmt, pair):
+        desc, layers = _fake_model()
+        desc.kv_format = fmt
+        for il in range(desc.n_layers):
+            layers[il].wqkv_pair_rows = pair
+        st = L.kd_model_create(C.byref(desc), C.byref(h))
+        if st == kd.KD_OK:
+            L.kd_model_destroy(h)
+        return st
+
+    assert create(kd.KD_KV_F16, 1) == kd.KD_OK
+    assert create(kd.KD_KV_FP8_E4M3, 0) == kd.KD_OK
+    assert create(kd.KD_KV_FP8_E4M3, 1) == kd.KD_ERR_UNSUPPORTED
+    assert b"FP8" in L.kd_last_error()
+    assert create(2, 0) == kd.KD_ERR_INVALID
+
+
+def test_fp8_kv_entry_points_validate_before_launch():
+    L = kd.lib()
+    kb = (C.c_void_p * 2)(0x1000, 0x2000)
+    vb = (C.c_void_p * 2)(0x3000, 0x4000)
+    pos = (C.c_int32 * 2)(3, 3)
+    assert L.kd_kv_append_fp8(0x100, 0x200, 2, 2, 96, kb, vb, pos, 8, None) == kd.KD_ERR_UNSUPPORTED   # hd
+    assert L.kd_kv_append_fp8(0x100, 0x200, 2, 2, 64, kb, vb, pos, 3, None) == kd.KD_ERR_CAPACITY
+    kb_same = (C.c_void_p * 2)(0x1000, 0x1000)
+    assert L.kd_kv_append_fp8(0x100, 0x200, 2, 2, 64, kb_same, vb, pos, 8, None) == kd.KD_ERR_INVALID
+    t = (C.c_int32 * 2)(5, 9)
+    ws = L.kd_fa_decode_workspace(2, 4, 64, t)
+    assert L.kd_fa_decode_ragged_fp8(0x100, 2, 4, 2, 64, kb, vb, t, 8, 0.125, 0x200, 0x300, ws, None) == \
+        kd.KD_ERR_CAPACITY
+    assert L.kd_fa_decode_ragged_fp8(0x100, 2, 4, 2, 64, kb, vb, t, 16, 0.125, 0x200, 0x300, ws - 4, None) == \
+        kd.KD_ERR_WORKSPACE
+    assert L.kd_fa_decode_ragged_fp8(0x100, 2, 6, 2, 64, kb, vb, t, 16, 0.125, 0x200, 0x300, ws, None) == \
+        kd.KD_ERR_UNSUPPORTED                                                                          # H/G = 3
