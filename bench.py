@@ -11,7 +11,8 @@ Prints ONE JSON line: aggregate decode tok/s at B=8 (``value``), the B=1..16 swe
 GB/s, the roofline of the dominant kernel (fa_decode at B=8) and of the largest product (the
 gate/up mmvq, 28672 x 4096 Q4_0 at B=8), both timed with HIP events on the launch stream, the
 other workloads of the path (``other_workloads``: the 8-layer Q8_0 stack with lm_head at
-B=1..8, the ragged B=16 attention sublayer and its fa_decode, the MoE verify step), and the
+B=1..8, the ragged B=16 attention sublayer and its fa_decode, the MoE verify step, the
+headline stack with FP8 E4M3 caches and its fa_decode), and the
 CPU oracle timed on a bounded sample beside it.
 
 ``--summarize-trace CSV`` instead prints per-(kernel, grid) average durations from a
@@ -126,9 +127,10 @@ FA_B, FA_T, FA_CAP = 8, 4113, 4128          # fa_decode traffic case: B rows of 
 MM_N, MM_K, MM_B = 28672, 4096, 8           # gate/up product traffic case
 
 
-def fa_algorithmic_bytes(t_kv, G: int, H: int, hd: int) -> int:
-    """fa_decode: each row's K and V (fp16) once, q in and the output out (fp32)."""
-    return sum(t_kv) * G * hd * 2 * 2 + 2 * len(t_kv) * H * hd * 4
+def fa_algorithmic_bytes(t_kv, G: int, H: int, hd: int, kv_bytes: int = 2) -> int:
+    """fa_decode: each row's K and V (fp16, or 1-byte E4M3 codes) once, q in and the output
+    out (fp32)."""
+    return sum(t_kv) * G * hd * kv_bytes * 2 + 2 * len(t_kv) * H * hd * 4
 
 
 TRAFFIC = {
@@ -302,7 +304,7 @@ def other_workloads(stream, iters: int) -> dict:
     resident): the 8-layer Q8_0 stack with its 32000-row lm_head at B = 1, 2, 4, 8 (ctx 1238);
     the attention sublayer with B = 16 ragged rows (log-uniform lengths in [512, 32768]), its
     step and its fa_decode; the 8-layer MoE stack's verify step (4 streams x 4 draft rows,
-    ctx 8192)."""
+    ctx 8192); the headline stack with FP8 E4M3 caches and its fa_decode."""
     import torch
     import workload as W
     import session_decode_step_amd as kd
@@ -347,6 +349,30 @@ def other_workloads(stream, iters: int) -> dict:
     ms = _time_steps(gw, stream, iters, 3, repeat_first=True)
     res["8-layer MoE d=2816 128 experts top-8 + shared, Q4_0; 4 streams x 4 verify rows, ctx 8192"] = {
         "ms_per_step": round(ms, 4), "rows_s": round(wl.B / ms * 1e3, 1)}
+    del gw
+    # the headline stack with FP8 E4M3 caches, and its fa_decode
+    log("32-layer Q4_0 stack, FP8 E4M3 KV caches")
+    import dataclasses
+    base = W.workload("c4", B=8, steps=iters + 8)
+    wl = dataclasses.replace(base, spec=dataclasses.replace(base.spec, kv_fp8=True))
+    gw = GpuWorkload(wl, fill="device")
+    ms = _time_steps(gw, stream, iters, 3)
+    sp = wl.spec
+    t_kv = [p + 1 for p in wl.positions(0)]
+    q = torch.randn((wl.B, sp.n_head, sp.head_dim), device="cuda",
+                    generator=torch.Generator(device="cuda").manual_seed(3))
+    kb = [gw.caches.k_ptr(wl.rows[b][0], 0) for b in range(wl.B)]
+    vb = [gw.caches.v_ptr(wl.rows[b][0], 0) for b in range(wl.B)]
+    ws = torch.zeros(kd.kd_fa_decode_workspace(wl.B, sp.n_head, sp.head_dim, t_kv), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    us = time_rotating(lambda i: kd.kd_fa_decode_ragged_fp8(q, sp.n_head_kv, kb, vb, t_kv, wl.capacity,
+                                                           sp.head_dim ** -0.5, ws=ws, out=out, stream=stream),
+                       iters, stream)
+    fb = fa_algorithmic_bytes(t_kv, sp.n_head_kv, sp.n_head, sp.head_dim, kv_bytes=1)
+    res["32-layer d=4096 32Q/8KV Q4_0, FP8 E4M3 KV caches, B=8 ctx 4096 (canonical QKV layout)"] = {
+        "tok_s": round(wl.B / ms * 1e3, 1), "ms_per_step": round(ms, 4), "t_kv": t_kv,
+        "fa_us": round(us, 3), "fa_algorithmic_bytes": int(fb), "fa_GBs": round(fb / (us * 1e-6) / 1e9, 1),
+        "fa_frac": round(fb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     del gw
     torch.cuda.synchronize()
     return res
