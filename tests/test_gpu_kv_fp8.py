@@ -178,3 +178,41 @@ def test_c2_stack_with_fp8_caches():
         y1 = gw.step(s, rows=[b]).cpu().numpy()
         np.testing.assert_array_equal(y1[0].view(np.uint32), outs[-1][b].view(np.uint32))
         np.testing.assert_array_equal(gw.caches.t[sess_b][:, :, :, p].cpu().numpy(), before)
+
+
+def test_c4_stack_with_fp8_caches_b8():
+    """The bench's FP8 configuration: the 32-layer d=4096 Q4_0 stack at B = 8, ctx 4096, with
+    E4M3 caches; the oracle on one row, every row bit-identical to its B = 1 run."""
+    from session_decode_step_amd.runner import GpuWorkload
+    say("c4 fp8 kv B=8")
+    base = W.workload("c4", B=8, steps=1)
+    wl = dataclasses.replace(base, spec=dataclasses.replace(base.spec, kv_fp8=True))
+    gw = GpuWorkload(wl)
+    y = gw.step(0).cpu().numpy().copy()
+    b = 5
+    oc = oracle.OracleCaches(wl, sessions=[wl.rows[b][0]])
+    ref = oracle.decode_step(gw.model, oc, W.step_inputs(wl, 0)[[b]], [wl.rows[b][0]], [wl.positions(0)[b]])
+    assert_close_rows(y[[b]], ref, 2e-2, "c4 fp8 step 0", elem_rel=6e-2)
+    for r in range(8):
+        y1 = gw.step(0, rows=[r]).cpu().numpy()
+        np.testing.assert_array_equal(y1[0].view(np.uint32), y[r].view(np.uint32))
+
+
+def test_c2_fp8_caches_with_sliding_window_layers():
+    """FP8 caches under sliding-window layers (the window is a view one byte per element into
+    the code cache): oracle on two rows, rows bit-identical to B = 1."""
+    from session_decode_step_amd.runner import GpuWorkload
+    say("c2 fp8 kv + sliding window")
+    base = W.workload("c2", B=4, steps=1)
+    wl = dataclasses.replace(base, spec=dataclasses.replace(base.spec, kv_fp8=True, swa_window=512,
+                                                            swa_layers=(0, 2, 4, 6)))
+    gw = GpuWorkload(wl)
+    y = gw.step(0).cpu().numpy().copy()
+    rows = [0, 3]
+    oc = oracle.OracleCaches(wl, sessions=sorted({wl.rows[b][0] for b in rows}))
+    ref = oracle.decode_step(gw.model, oc, W.step_inputs(wl, 0)[rows], [wl.rows[b][0] for b in rows],
+                             [wl.positions(0)[b] for b in rows], dense=oracle.DenseWeights(6 << 30))
+    assert_close_rows(y[rows], ref, 2e-2, "c2 fp8 swa step 0", elem_rel=6e-2)
+    for r in range(4):
+        y1 = gw.step(0, rows=[r]).cpu().numpy()
+        np.testing.assert_array_equal(y1[0].view(np.uint32), y[r].view(np.uint32))
