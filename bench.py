@@ -369,7 +369,7 @@ def other_workloads(stream, iters: int) -> dict:
                                                            sp.head_dim ** -0.5, ws=ws, out=out, stream=stream),
                        iters, stream)
     fb = fa_algorithmic_bytes(t_kv, sp.n_head_kv, sp.n_head, sp.head_dim, kv_bytes=1)
-    res["32-layer d=4096 32Q/8KV Q4_0, FP8 E4M3 KV caches, B=8 ctx 4096 (canonical QKV layout)"] = {
+    res["32-layer d=4096 32Q/8KV Q4_0, FP8 E4M3 KV caches, B=8 ctx 4096"] = {
         "tok_s": round(wl.B / ms * 1e3, 1), "ms_per_step": round(ms, 4), "t_kv": t_kv,
         "fa_us": round(us, 3), "fa_algorithmic_bytes": int(fb), "fa_GBs": round(fb / (us * 1e-6) / 1e9, 1),
         "fa_frac": round(fb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}

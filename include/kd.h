@@ -254,8 +254,8 @@ typedef struct {
   kd_weight lm_head;                     /* [vocab, d] or qs NULL */
   int32_t kv_format;                     /* KD_KV_F16 (fp16 caches, k_base/v_base [G][capacity][hd]
                                             fp16) or KD_KV_FP8_E4M3 (uint8 codes, stored and read as
-                                            kd_kv_append_fp8 / kd_fa_decode_ragged_fp8; needs
-                                            wqkv_pair_rows == 0 on every layer) */
+                                            kd_kv_append_fp8 / kd_fa_decode_ragged_fp8, by either
+                                            wqkv layout) */
 } kd_model_desc;
 
 typedef struct kd_model kd_model;

@@ -445,7 +445,7 @@ class KdModel:
             self.keep.append(t)
             return t.data_ptr()
 
-        kv_fp8 = bool(getattr(sp, "kv_fp8", False))
+        kv_fp8 = bool(getattr(sp, "kv_fp8", False))   # E4M3 caches (kd_model_desc.kv_format)
         for il, L in enumerate(model["layers"]):
             slot[0] = il
             D = self.layers[il]
@@ -456,9 +456,7 @@ class KdModel:
             D.k_norm = F(L["k_norm"]) if qk_norm else None
             D.attn_gate = 1 if L.get("attn_gate") else 0
             n_heads_qkv = sp.n_head + 2 * sp.n_head_kv + (sp.n_head if D.attn_gate else 0)
-            # QK-norm normalises whole heads, and FP8 caches are stored by the RoPE launch: both
-            # take the canonical layout
-            if fused and not qk_norm and not kv_fp8:
+            if fused and not qk_norm:   # QK-norm normalises whole heads: the canonical layout
                 D.wqkv = W(rope_pair_rows(L["wqkv"], n_heads_qkv, sp.head_dim), "wqkv")
                 D.wqkv_pair_rows = 1
             else:

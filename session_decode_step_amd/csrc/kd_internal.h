@@ -212,12 +212,12 @@ constexpr int kNormFuseMax = 4096;  // longest row whose block sums the consumer
 void launch_mmvq_resnorm(const kd_weight& W, const int8_t* xq, const float* xd, int B, const float* res, int ld,
                          const float* gain, float* x1, int8_t* out_qs, float* out_d, float* ss, hipStream_t st);
 // RoPE: W is wqkv with each head's rows in pair order (i, i + hd/2 adjacent); writes the
-// rotated q rows to q (stride ldq) and the rotated k and the v rows (fp16) at each row's
-// position in its caches; cs is the step's cos/sin table.
+// rotated q rows to q (stride ldq) and the rotated k and the v rows (fp16, or E4M3 codes when
+// kv_fp8) at each row's position in its caches; cs is the step's cos/sin table.
 // cs == nullptr: the angles are evaluated in the epilogue (rope_base), same values.
 void launch_mmvq_rope(const kd_weight& W, const int8_t* xq, const float* xd, int B, float* q, int ldq, int H, int G,
                       int hd, const float* cs, float rope_base, const RowCaches& rc, int capacity, hipStream_t st,
-                      const float* norm_ss = nullptr, int norm_n = 0, float norm_eps = 0.0f);
+                      const float* norm_ss = nullptr, int norm_n = 0, float norm_eps = 0.0f, bool kv_fp8 = false);
 
 // cos/sin table [B][hd/2][2] fp32 from per-row positions (angles in fp64).
 void launch_rope_table(const RowCaches& rc, int B, int hd, float base, float* cs, hipStream_t st);

@@ -160,6 +160,7 @@ struct MmvqArgs {
   const float* norm_ss;
   int norm_n;
   float norm_eps;
+  int epi_kv8;  // RoPE: the caches hold FP8 E4M3 codes (else fp16)
 };
 
 // Epilogue of a product: write y (plain); apply SwiGLU to the interleaved gate/up rows and
@@ -578,14 +579,28 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
           qr[i] = y0;
           qr[i + half] = y1;
         } else {
-          __half* K = static_cast<__half*>(a.epi_rc.k[bq]) + ((size_t)(hh - H) * a.epi_capacity + pos) * hd;
-          K[i] = __float2half_rn(y0);
-          K[i + half] = __float2half_rn(y1);
+          const size_t o = ((size_t)(hh - H) * a.epi_capacity + pos) * hd;
+          if (a.epi_kv8) {
+            uint8_t* K = static_cast<uint8_t*>(a.epi_rc.k[bq]) + o;
+            K[i] = (uint8_t)f32_to_e4m3(y0);
+            K[i + half] = (uint8_t)f32_to_e4m3(y1);
+          } else {
+            __half* K = static_cast<__half*>(a.epi_rc.k[bq]) + o;
+            K[i] = __float2half_rn(y0);
+            K[i + half] = __float2half_rn(y1);
+          }
         }
       } else if (hh < H + 2 * G) {
-        __half* V = static_cast<__half*>(a.epi_rc.v[bq]) + ((size_t)(hh - H - G) * a.epi_capacity + pos) * hd;
-        V[i] = __float2half_rn(x0);
-        V[i + half] = __float2half_rn(x1);
+        const size_t o = ((size_t)(hh - H - G) * a.epi_capacity + pos) * hd;
+        if (a.epi_kv8) {
+          uint8_t* V = static_cast<uint8_t*>(a.epi_rc.v[bq]) + o;
+          V[i] = (uint8_t)f32_to_e4m3(x0);
+          V[i + half] = (uint8_t)f32_to_e4m3(x1);
+        } else {
+          __half* V = static_cast<__half*>(a.epi_rc.v[bq]) + o;
+          V[i] = __float2half_rn(x0);
+          V[i + half] = __float2half_rn(x1);
+        }
       } else {  // output-gate rows (gated layers): stored as they are, after v in the row
         float* gr = a.epi_q + (size_t)bq * a.epi_ldq + (size_t)hh * hd;
         gr[i] = x0;
@@ -723,11 +738,12 @@ void launch_mmvq_resnorm(const kd_weight& W, const int8_t* xq, const float* xd, 
 
 void launch_mmvq_rope(const kd_weight& W, const int8_t* xq, const float* xd, int B, float* q, int ldq, int H, int G,
                       int hd, const float* cs, float rope_base, const RowCaches& rc, int capacity, hipStream_t st,
-                      const float* norm_ss, int norm_n, float norm_eps) {
+                      const float* norm_ss, int norm_n, float norm_eps, bool kv_fp8) {
   MmvqArgs a = mmvq_args(W, xq, xd, B, nullptr, 0, nullptr, nullptr);
   a.norm_ss = norm_ss;
   a.norm_n = norm_n;
   a.norm_eps = norm_eps;
+  a.epi_kv8 = kv_fp8 ? 1 : 0;
   a.epi_base = (double)rope_base;
   a.epi_q = q;
   a.epi_ldq = ldq;

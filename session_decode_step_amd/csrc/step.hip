@@ -117,8 +117,6 @@ extern "C" kd_status kd_model_create(const kd_model_desc* desc, kd_model** out) 
     KD_TRY(check_weight("wqkv", il, L.wqkv, (H + 2 * G + (L.attn_gate ? H : 0)) * hd, d));
     KD_REQUIRE(L.wqkv_pair_rows == 0 || L.wqkv_pair_rows == 1, KD_ERR_INVALID,
                "kd_model_create: layer %d: wqkv_pair_rows=%d", il, L.wqkv_pair_rows);
-    KD_REQUIRE(L.wqkv_pair_rows == 0 || m.kv_format == KD_KV_F16, KD_ERR_UNSUPPORTED,
-               "kd_model_create: layer %d: FP8 caches need the canonical wqkv layout (wqkv_pair_rows = 0)", il);
     KD_TRY(check_weight("wo", il, L.wo, d, H * hd));
     if (m.ffn > 0 || moe) KD_REQUIRE(L.ffn_norm, KD_ERR_INVALID, "kd_model_create: layer %d: null ffn_norm", il);
     if (m.ffn > 0) {
@@ -338,7 +336,7 @@ extern "C" kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x
     }
     if (Ly.wqkv_pair_rows) {  // the product rotates q/k and appends k/v itself
       launch_mmvq_rope(Ly.wqkv, s.act_qs, s.act_d, B, s.qkv, ldqkv, H, G, hd, s.cs, d.rope_base, rc, capacity, st,
-                       prenormed ? s.ss : nullptr, D, d.rms_eps);
+                       prenormed ? s.ss : nullptr, D, d.rms_eps, kv8);
     } else {
       launch_mmvq(Ly.wqkv, s.act_qs, s.act_d, B, s.qkv, ldqkv, st);
       launch_rope_append(s.qkv, ldqkv, B, H, G, hd, s.cs, rc, capacity, true, st, d.rope_base, Ly.q_norm, Ly.k_norm,

@@ -222,8 +222,7 @@ def test_layer_variant_fields_are_validated():
 
 
 def test_kv_format_is_validated():
-    """kd_model_create accepts fp16 and E4M3 caches only, and E4M3 caches only with the
-    canonical wqkv layout (the appends are stored by the separate RoPE launch)."""
+    """kd_model_create accepts fp16 and E4M3 caches only, with either wqkv layout."""
     L = kd.lib()
     h = C.c_void_p()
 
@@ -239,9 +238,9 @@ def test_kv_format_is_validated():
 
     assert create(kd.KD_KV_F16, 1) == kd.KD_OK
     assert create(kd.KD_KV_FP8_E4M3, 0) == kd.KD_OK
-    assert create(kd.KD_KV_FP8_E4M3, 1) == kd.KD_ERR_UNSUPPORTED
-    assert b"FP8" in L.kd_last_error()
+    assert create(kd.KD_KV_FP8_E4M3, 1) == kd.KD_OK
     assert create(2, 0) == kd.KD_ERR_INVALID
+    assert b"kv_format" in L.kd_last_error()
 
 
 def test_fp8_kv_entry_points_validate_before_launch():

@@ -143,12 +143,14 @@ def _fp8_c2(B, steps):
 def test_c2_stack_with_fp8_caches():
     """The 8-layer Q8_0 stack with E4M3 caches: oracle on two rows for two steps, the appended
     codes equal to the oracle's where the oracle's k and v sit away from a rounding boundary,
-    every row bit-identical (outputs and the code bytes it wrote) to its B = 1 run."""
+    every row bit-identical (outputs and the code bytes it wrote) to its B = 1 run, and the
+    fused layout (codes stored by the QKV product's RoPE epilogue) equal to the separate
+    RoPE + append launch: the same layer-0 code bytes, outputs within the deep bar."""
     from session_decode_step_amd.runner import GpuWorkload
     say("c2 fp8 kv")
     wl = _fp8_c2(4, 2)
     gw = GpuWorkload(wl)
-    assert all(L.wqkv_pair_rows == 0 for L in gw.km.layers)
+    assert all(L.wqkv_pair_rows == 1 for L in gw.km.layers)   # the QKV product stores the codes
     rows = [0, 3]
     sess = sorted({wl.rows[b][0] for b in rows})
     oc = oracle.OracleCaches(wl, sessions=sess)
@@ -178,6 +180,14 @@ def test_c2_stack_with_fp8_caches():
         y1 = gw.step(s, rows=[b]).cpu().numpy()
         np.testing.assert_array_equal(y1[0].view(np.uint32), outs[-1][b].view(np.uint32))
         np.testing.assert_array_equal(gw.caches.t[sess_b][:, :, :, p].cpu().numpy(), before)
+    # the separate RoPE + append launch on the canonical layout
+    gs = GpuWorkload(wl, model=gw.model, fused=False)
+    assert all(L.wqkv_pair_rows == 0 for L in gs.km.layers)
+    for s2 in range(2):
+        ys = gs.step(s2).cpu().numpy()
+        assert_close_rows(outs[s2], ys.astype(np.float64), 2e-2, f"fp8 step {s2} fused vs separate", elem_rel=6e-2)
+    for sess_b in range(len(wl.prefill)):
+        np.testing.assert_array_equal(gw.caches.t[sess_b][0].cpu().numpy(), gs.caches.t[sess_b][0].cpu().numpy())
 
 
 def test_c4_stack_with_fp8_caches_b8():
