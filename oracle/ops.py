@@ -322,3 +322,30 @@ def e4m3_encode(x: np.ndarray) -> np.ndarray:
 def e4m3_decode(codes: np.ndarray) -> np.ndarray:
     """fp64 values of E4M3 codes (see ``e4m3_values``)."""
     return e4m3_values()[np.asarray(codes, dtype=np.uint8).astype(np.int64)]
+
+
+# ---------------------------------------------------------------------------------------
+# Gated delta-rule recurrent state (linear-attention layers)
+# ---------------------------------------------------------------------------------------
+def gdn_step(S: np.ndarray, q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.ndarray, beta: np.ndarray,
+             scale: float) -> Tuple[np.ndarray, np.ndarray]:
+    """One decode step of the gated delta rule for every value head of one row.
+
+    memra-engine decode_batch.rs, the Linear mixer of ``decode_batch_layers``: after the
+    batched projections and the prep launch (L2-normalised q and k, the gate beta and the
+    log-decay g per value head), one batched scan launch reads each sequence's state and
+    writes its other buffer, with the scale 1/sqrt(d_state); the update itself is not spelled
+    out there.  Reading (the published gated delta rule): per head, with state S [d_v, d_k],
+    decay a = exp(g), S' = a S, the delta-rule correction writes v at key k with strength beta:
+    S_new = S' + beta (v - S' k) k^T, and the output is o = scale S_new q.
+    S [H, d_v, d_k], q and k [H, d_k], v [H, d_v], g and beta [H]; returns (S_new, o), fp64.
+    """
+    S = np.asarray(S, dtype=np.float64)
+    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    a = np.exp(np.asarray(g, dtype=np.float64))[:, None, None]
+    Sd = a * S
+    u = np.einsum("hvk,hk->hv", Sd, k)                     # what the decayed state recalls at k
+    b = np.asarray(beta, dtype=np.float64)[:, None, None]
+    S_new = Sd + b * (v - u)[:, :, None] * k[:, None, :]
+    o = scale * np.einsum("hvk,hk->hv", S_new, q)
+    return S_new, o

@@ -568,3 +568,47 @@ def test_oracle_fp8_step_appends_nearest_codes_and_attends_their_values():
         # attention over the decoded codes, from the traced q
         ref = oracle.attention(trace[0]["q"][b], oracle.e4m3_decode(K), oracle.e4m3_decode(oc.V[b][0]), pos[b] + 1)
         np.testing.assert_allclose(trace[0]["attn"][b], ref, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------
+# Gated delta rule
+# ---------------------------------------------------------------------------------------
+def _gdn_inputs(seed, H=3, dk=8, dv=6):
+    r = np.random.default_rng(seed)
+    S = r.standard_normal((H, dv, dk))
+    q = r.standard_normal((H, dk))
+    k = r.standard_normal((H, dk))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    v = r.standard_normal((H, dv))
+    g = -r.uniform(0.01, 1.0, H)
+    beta = r.uniform(0.1, 0.9, H)
+    return S, q, k, v, g, beta
+
+
+def test_gdn_delta_rule_writes_v_at_k():
+    """No decay and beta = 1 with a unit key: afterwards the state recalls exactly v at k,
+    and leaves every direction orthogonal to k unchanged."""
+    S, q, k, v, g, beta = _gdn_inputs(1)
+    Sn, _ = oracle.gdn_step(S, q, k, v, np.zeros(3), np.ones(3), 1.0)
+    np.testing.assert_allclose(np.einsum("hvk,hk->hv", Sn, k), v, rtol=0, atol=1e-12)
+    r = np.random.default_rng(2).standard_normal((3, 8))
+    r -= np.sum(r * k, axis=1, keepdims=True) * k                # orthogonal to k
+    np.testing.assert_allclose(np.einsum("hvk,hk->hv", Sn, r), np.einsum("hvk,hk->hv", S, r), rtol=0, atol=1e-12)
+
+
+def test_gdn_special_cases_and_matrix_form():
+    S, q, k, v, g, beta = _gdn_inputs(3)
+    # beta = 0: pure decay
+    Sn, o = oracle.gdn_step(S, q, k, v, g, np.zeros(3), 0.5)
+    np.testing.assert_allclose(Sn, np.exp(g)[:, None, None] * S, rtol=1e-15)
+    np.testing.assert_allclose(o, 0.5 * np.einsum("hvk,hk->hv", Sn, q), rtol=1e-14)
+    # the closed matrix form a S (I - beta k k^T) + beta v k^T, written per head with numpy
+    Sn, o = oracle.gdn_step(S, q, k, v, g, beta, 0.25)
+    for h in range(3):
+        I = np.eye(8)
+        ref = np.exp(g[h]) * S[h] @ (I - beta[h] * np.outer(k[h], k[h])) + beta[h] * np.outer(v[h], k[h])
+        np.testing.assert_allclose(Sn[h], ref, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(o[h], 0.25 * ref @ q[h], rtol=0, atol=1e-13)
+    # zero state: the state becomes beta v k^T
+    Sn, _ = oracle.gdn_step(np.zeros_like(S), q, k, v, g, beta, 1.0)
+    np.testing.assert_allclose(Sn, beta[:, None, None] * v[:, :, None] * k[:, None, :], rtol=1e-15)
