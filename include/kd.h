@@ -197,6 +197,21 @@ kd_status kd_fa_decode_ragged_fp8(const float* q, int32_t B, int32_t H, int32_t 
                                   const int32_t* t_kv, int32_t capacity, float scale, float* out,
                                   void* ws, size_t ws_bytes, void* stream);
 
+/* ---- gated delta rule (linear-attention layers) -------------------------------------- */
+/* One decode step of the gated delta rule for B rows (memra-engine decode_batch.rs, the
+ * Linear mixer of decode_batch_layers: one batched scan launch over every sequence's state,
+ * through a per-row pointer table, with scale 1/sqrt(d_state); the update read as the
+ * published gated delta rule).  Per row b and value head h, with state S [d_v][d_k] fp32:
+ *   S' = exp(g) S;  S_new = S' + beta (v - S' k) k^T;  o = scale S_new q.
+ * q, k, v, o: fp32 [B][n_heads][d_state] (q and k as the prep step leaves them, e.g.
+ * L2-normalised); g (log decay) and beta: fp32 [B][n_heads].  state_in[b] / state_out[b]:
+ * host arrays of device pointers to fp32 [n_heads][d_state][d_state] (row-major [v][k]);
+ * state_out[b] may equal state_in[b] (in place) but no row may write a state another row
+ * reads or writes.  d_state must be 128; 1 <= B <= 16. */
+kd_status kd_gdn_step(const float* q, const float* k, const float* v, const float* g, const float* beta,
+                      int32_t B, int32_t n_heads, int32_t d_state, const void* const* state_in,
+                      void* const* state_out, float scale, float* o, void* stream);
+
 /* ---- whole step ---------------------------------------------------------------------- */
 typedef struct {
   const float* attn_norm;   /* [d] */

@@ -87,6 +87,7 @@ SIGNATURES = {
     "kd_verify_accept": (_I, [_P, _P, _I, _I, _P, _P, _P]),
     "kd_kv_append": (_I, [_P, _P, _I, _I, _I, _PP, _PP, _PI, _I, _P]),
     "kd_kv_append_fp8": (_I, [_P, _P, _I, _I, _I, _PP, _PP, _PI, _I, _P]),
+    "kd_gdn_step": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _PP, _PP, _F, _P, _P]),
     "kd_fa_decode_workspace": (_S, [_I, _I, _I, _PI]),
     "kd_fa_decode_ragged": (_I, [_P, _I, _I, _I, _I, _PP, _PP, _PI, _I, _F, _P, _P, _S, _P]),
     "kd_fa_decode_ragged_fp8": (_I, [_P, _I, _I, _I, _I, _PP, _PP, _PI, _I, _F, _P, _P, _S, _P]),
@@ -372,6 +373,17 @@ def kd_kv_append_fp8(k: torch.Tensor, v: torch.Tensor, k_base: Sequence[int], v_
     B, G, hd = k.shape
     _check(lib().kd_kv_append_fp8(k.data_ptr(), v.data_ptr(), B, G, hd, _ptrs(k_base), _ptrs(v_base), _i32(pos),
                                   capacity, _stream(stream)), "kd_kv_append_fp8")
+
+
+def kd_gdn_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+                state_in: Sequence[int], state_out: Sequence[int], scale: float,
+                o: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    B, H, d = q.shape
+    o = torch.empty_like(v) if o is None else o
+    _check(lib().kd_gdn_step(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(), B, H, d,
+                             _ptrs(state_in), _ptrs(state_out), scale, o.data_ptr(), _stream(stream)),
+           "kd_gdn_step")
+    return o
 
 
 def kd_fa_decode_workspace(B: int, H: int, hd: int, t_kv: Sequence[int]) -> int:

@@ -260,3 +260,17 @@ def test_fp8_kv_entry_points_validate_before_launch():
         kd.KD_ERR_WORKSPACE
     assert L.kd_fa_decode_ragged_fp8(0x100, 2, 6, 2, 64, kb, vb, t, 16, 0.125, 0x200, 0x300, ws, None) == \
         kd.KD_ERR_UNSUPPORTED                                                                          # H/G = 3
+
+
+def test_gdn_step_validates_before_launch():
+    L = kd.lib()
+    si = (C.c_void_p * 2)(0x1000, 0x2000)
+    so = (C.c_void_p * 2)(0x3000, 0x4000)
+    args = (0x100, 0x200, 0x300, 0x400, 0x500)
+    assert L.kd_gdn_step(*args, 2, 4, 64, si, so, 0.1, 0x600, None) == kd.KD_ERR_UNSUPPORTED       # d_state
+    assert L.kd_gdn_step(*args, 17, 4, 128, si, so, 0.1, 0x600, None) == kd.KD_ERR_UNSUPPORTED      # B
+    same = (C.c_void_p * 2)(0x3000, 0x3000)
+    assert L.kd_gdn_step(*args, 2, 4, 128, si, same, 0.1, 0x600, None) == kd.KD_ERR_INVALID
+    cross = (C.c_void_p * 2)(0x2000, 0x4000)                 # row 0 writes what row 1 reads
+    assert L.kd_gdn_step(*args, 2, 4, 128, si, cross, 0.1, 0x600, None) == kd.KD_ERR_INVALID
+    assert L.kd_gdn_step(0, *args[1:], 2, 4, 128, si, so, 0.1, 0x600, None) == kd.KD_ERR_INVALID
