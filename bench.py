@@ -12,7 +12,7 @@ GB/s, the roofline of the dominant kernel (fa_decode at B=8) and of the largest 
 gate/up mmvq, 28672 x 4096 Q4_0 at B=8), both timed with HIP events on the launch stream, the
 other workloads of the path (``other_workloads``: the 8-layer Q8_0 stack with lm_head at
 B=1..8, the ragged B=16 attention sublayer and its fa_decode, the MoE verify step, the
-headline stack with FP8 E4M3 caches and its fa_decode), and the
+headline stack with FP8 E4M3 caches and its fa_decode, the gated delta-rule state step), and the
 CPU oracle timed on a bounded sample beside it.
 
 ``--summarize-trace CSV`` instead prints per-(kernel, grid) average durations from a
@@ -35,8 +35,8 @@ HBM_PEAK_GBS = 8000.0
 
 def summarize_trace(path: str) -> None:
     """Per-(kernel, grid) call counts and average durations from a rocprofv3 kernel-trace
-    CSV, then the longest run of back-to-back dispatches of one (kernel, grid): the bench's
-    own timing loop of the dominant kernel, whose average the bench reports."""
+    CSV, then the longest run of back-to-back dispatches of one of this library's (kernel,
+    grid): the bench's own timing loop of a kernel, whose average the bench reports."""
     import csv
     from collections import defaultdict
     acc = defaultdict(lambda: [0, 0.0, 0])
@@ -62,7 +62,7 @@ def summarize_trace(path: str) -> None:
         j = i
         while j + 1 < len(seq) and seq[j + 1][1] == seq[i][1]:
             j += 1
-        if j - i + 1 > best[0]:
+        if j - i + 1 > best[0] and "kd::" in seq[i][1][0]:   # this library's kernels only
             best = (j - i + 1, i, j)
         i = j + 1
     n, i, j = best
@@ -304,7 +304,8 @@ def other_workloads(stream, iters: int) -> dict:
     resident): the 8-layer Q8_0 stack with its 32000-row lm_head at B = 1, 2, 4, 8 (ctx 1238);
     the attention sublayer with B = 16 ragged rows (log-uniform lengths in [512, 32768]), its
     step and its fa_decode; the 8-layer MoE stack's verify step (4 streams x 4 draft rows,
-    ctx 8192); the headline stack with FP8 E4M3 caches and its fa_decode."""
+    ctx 8192); the headline stack with FP8 E4M3 caches and its fa_decode; the gated
+    delta-rule state step at B = 8 x 32 heads."""
     import torch
     import workload as W
     import session_decode_step_amd as kd
@@ -374,6 +375,26 @@ def other_workloads(stream, iters: int) -> dict:
         "fa_us": round(us, 3), "fa_algorithmic_bytes": int(fb), "fa_GBs": round(fb / (us * 1e-6) / 1e9, 1),
         "fa_frac": round(fb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     del gw
+    # gated delta-rule state step of a linear-attention layer: B = 8 rows x 32 value heads
+    log("gated delta-rule state step, B=8 x 32 heads")
+    B, H, D, sets = 8, 32, 128, 8
+    gen = torch.Generator(device="cuda").manual_seed(4)
+    st_in = [[torch.randn((H, D, D), device="cuda", generator=gen) for _ in range(B)] for _ in range(sets)]
+    st_out = [[torch.empty((H, D, D), device="cuda") for _ in range(B)] for _ in range(sets)]
+    gq = torch.nn.functional.normalize(torch.randn((B, H, D), device="cuda", generator=gen), dim=2)
+    gk = torch.nn.functional.normalize(torch.randn((B, H, D), device="cuda", generator=gen), dim=2)
+    gv = torch.randn((B, H, D), device="cuda", generator=gen)
+    gg = -torch.rand((B, H), device="cuda", generator=gen)
+    gb = torch.rand((B, H), device="cuda", generator=gen)
+    go = torch.empty_like(gv)
+    us = time_rotating(lambda i: kd.kd_gdn_step(gq, gk, gv, gg, gb, [t.data_ptr() for t in st_in[i % sets]],
+                                                [t.data_ptr() for t in st_out[i % sets]], D ** -0.5, o=go,
+                                                stream=stream), iters, stream)
+    gbytes = B * H * D * D * 4 * 2 + B * H * D * 4 * 4 + B * H * 8
+    res["gated delta-rule state step (kd_gdn_step), B=8 rows x 32 value heads, d_state 128, fp32 state"] = {
+        "us": round(us, 3), "algorithmic_bytes": int(gbytes), "GBs": round(gbytes / (us * 1e-6) / 1e9, 1),
+        "frac": round(gbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    del st_in, st_out
     torch.cuda.synchronize()
     return res
 
