@@ -11,8 +11,7 @@
 // How: one workgroup of 4 waves per (head, row).  Wave w owns state rows v = 32w .. 32w+31
 // and lane l the columns 2l, 2l+1 of each, so every row is one coalesced 512-byte access.
 // All 32 rows are loaded before the first is used; u and o of each row are sums over the 64
-// lanes by a fixed xor butterfly (every lane ends with the same value), so a row's result
-// does not depend on B.  Each lane writes back only the elements it read: the step may run
+// lanes in a fixed order (row_sum), so a row's result does not depend on B.  Each lane writes back only the elements it read: the step may run
 // in place (state_in == state_out).
 #include "kd_internal.h"
 
@@ -20,6 +19,25 @@ namespace kd {
 
 constexpr int kGdnDim = 128;  // d_state: d_k = d_v = 128
 constexpr int kGdnRowsPerWave = 32;
+
+// Sum over the 64 lanes, the same value in every lane, without LDS: DPP adds within each
+// 16-lane row (partner lanes l^1, l^2, then the mirrored lane of the half row and of the row),
+// then the four row sums read from lanes 0, 16, 32, 48 and added in that order.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_sum(float x) {
+  x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+  x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+  x += dpp_f<0x141>(x);  // row_half_mirror: lane 7 - i of the half row (the other quad)
+  x += dpp_f<0x140>(x);  // row_mirror: lane 15 - i of the row (the other half row)
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return ((r0 + r1) + r2) + r3;
+}
 
 struct RowStates {
   const float* in[KD_MAX_B];
@@ -49,11 +67,11 @@ __global__ __launch_bounds__(256) void gdn_step_kernel(const float* __restrict__
 #pragma unroll
   for (int j = 0; j < kGdnRowsPerWave; ++j) {
     const float sx = a * s[j].x, sy = a * s[j].y;
-    const float u = wave_sum(fmaf(sx, k2.x, sy * k2.y));
+    const float u = row_sum(fmaf(sx, k2.x, sy * k2.y));
     const float c = bt * (__shfl(vl, j, 64) - u);
     const float nx = fmaf(c, k2.x, sx), ny = fmaf(c, k2.y, sy);
     *reinterpret_cast<float2*>(Sout + (size_t)(v0 + j) * kGdnDim + 2 * lane) = make_float2(nx, ny);
-    const float oj = wave_sum(fmaf(nx, q2.x, ny * q2.y));
+    const float oj = row_sum(fmaf(nx, q2.x, ny * q2.y));
     if (lane == j) ol = oj;
   }
   if (lane < kGdnRowsPerWave) o[hv * kGdnDim + v0 + lane] = scale * ol;
