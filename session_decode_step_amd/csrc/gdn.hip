@@ -23,20 +23,12 @@ constexpr int kGdnRowsPerWave = 32;
 // Sum over the 64 lanes, the same value in every lane, without LDS: DPP adds within each
 // 16-lane row (partner lanes l^1, l^2, then the mirrored lane of the half row and of the row),
 // then the four row sums read from lanes 0, 16, 32, 48 and added in that order.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
 __device__ __forceinline__ float row_sum(float x) {
   x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
   x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
   x += dpp_f<0x141>(x);  // row_half_mirror: lane 7 - i of the half row (the other quad)
   x += dpp_f<0x140>(x);  // row_mirror: lane 15 - i of the row (the other half row)
-  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
-  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
-  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
-  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
-  return ((r0 + r1) + r2) + r3;
+  return ((lane_f(x, 0) + lane_f(x, 16)) + lane_f(x, 32)) + lane_f(x, 48);
 }
 
 struct RowStates {

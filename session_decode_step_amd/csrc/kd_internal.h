@@ -101,10 +101,24 @@ __device__ inline float wave_sum(float v) {
   return v;
 }
 
+// DPP read of lane CTRL-permuted x within each 16-lane row (no LDS crossbar).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_f(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+// Maximum over the 64 lanes, the same value in every lane (exact in any order): DPP within
+// each 16-lane row (lane ^ 1, lane ^ 2, the mirrored lane of the half row, of the row), then
+// the four row maxima read from lanes 0, 16, 32, 48.  Call from uniform control flow.
 __device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-  return v;
+  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp_f<0x140>(v));  // row_mirror
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 
 // cos/sin of the NEOX RoPE angle pos * base^(-2i/hd), evaluated in fp64, rounded to fp32.
