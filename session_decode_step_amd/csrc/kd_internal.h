@@ -66,15 +66,40 @@ __device__ inline void quant32(const float* v, int8_t* dst_block, float* d_out) 
   *d_out = dd;
 }
 
+// DPP read of lane CTRL-permuted x within each 16-lane row (a VALU operand, where a shuffle
+// goes through the LDS crossbar).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_f(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+// Sum and maximum over each aligned group of 8 lanes, the same value in all 8 (every lane of
+// the group must be active): lane ^ 1, lane ^ 2, then the mirrored lane of the half row, which
+// holds the other quad's partial.  Each step combines the same two partials as the xor
+// butterfly over masks 1, 2, 4, so the results are equal bit for bit.
+__device__ __forceinline__ float group8_sum(float x) {
+  x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_f<0x141>(x);  // row_half_mirror
+  return x;
+}
+__device__ __forceinline__ float group8_max(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));
+  x = fmaxf(x, dpp_f<0x4E>(x));
+  x = fmaxf(x, dpp_f<0x141>(x));
+  return x;
+}
+
 // The same quantiser with a block spread over 8 consecutive lanes (lane sub = tid % 8 holds
 // elements [4 sub, 4 sub + 4) in v).  Every lane of the group must execute it (shuffles);
 // stores happen only if `store`.  Codes and scale equal quant32's for the same 32 values
 // (max is exact and order-free; each code is computed alone).
 __device__ inline void quant4_lane8(float4 v, int sub, bool store, int8_t* dst_block, float* d_out) {
   float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-  amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
+  amax = group8_max(amax);
   const float dd = amax / 127.0f;
   int c[4] = {0, 0, 0, 0};
   if (amax != 0.0f) {
@@ -99,15 +124,6 @@ __device__ inline float wave_sum(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
   return v;
-}
-
-// DPP read of lane CTRL-permuted x within each 16-lane row (no LDS crossbar).
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float lane_f(float x, int lane) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
 
 // Maximum over the 64 lanes, the same value in every lane (exact in any order): DPP within

@@ -175,7 +175,7 @@ enum { EPI_PLAIN = 0, EPI_SWIGLU = 1, EPI_ROPE = 2, EPI_RESNORM = 3 };
 // inv_b is the scale of the normalised block y = x1 * inv_b * gain, and the codes of z and y
 // are the same numbers.  The row's blocks are added by its 8 lanes: lane `sub` adds blocks
 // [sub * c, sub * c + c) in order (c = ceil(blocks / 8) <= kNormPerLane), then the 8 lanes by
-// xor butterfly (every lane ends with the same value).
+// DPP sum over the 8-lane group (group8_sum: every lane ends with the same value).
 constexpr int kNormPerLane = 16;  // block sums per lane: rows of up to 8 * 16 * 32 = 4096
 
 __device__ __forceinline__ void norm_ss_load(const MmvqArgs& a, int t, int nrows, float (&v)[kNormPerLane]) {
@@ -195,9 +195,7 @@ __device__ __forceinline__ float norm_inv(const MmvqArgs& a, const float (&v)[kN
   float s = v[0];
 #pragma unroll
   for (int i = 1; i < kNormPerLane; ++i) s += v[i];
-  s += __shfl_xor(s, 1, 64);
-  s += __shfl_xor(s, 2, 64);
-  s += __shfl_xor(s, 4, 64);
+  s = group8_sum(s);
   return 1.0f / sqrtf(s / (float)a.norm_n + a.norm_eps);
 }
 
@@ -548,9 +546,7 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
       ss = fmaf(v.y, v.y, ss);
       ss = fmaf(v.z, v.z, ss);
       ss = fmaf(v.w, v.w, ss);
-      ss += __shfl_xor(ss, 1, 64);
-      ss += __shfl_xor(ss, 2, 64);
-      ss += __shfl_xor(ss, 4, 64);
+      ss = group8_sum(ss);
       if (sub == 0) a.epi_ss[(size_t)bq * nblk + m] = ss;
       quant4_lane8(make_float4(v.x * gn.x, v.y * gn.y, v.z * gn.z, v.w * gn.w), sub, true,
                    a.epi_qs + ((size_t)bq * NQo + (m >> 2)) * 128 + (m & 3) * 8, a.epi_qd + (size_t)bq * nbpo + m);
