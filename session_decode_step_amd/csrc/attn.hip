@@ -13,6 +13,8 @@
 // of the group and writes (m, l, o): the chunk's score max, exp-sum and un-normalised
 // output.  The combine merges chunks in chunk order: M = max m_s, out = sum e^(m_s-M) o_s /
 // sum e^(m_s-M) l_s.  All reductions use fixed trees, so a row's bytes equal its 1-row call.
+#include <algorithm>
+
 #include "kd_internal.h"
 
 namespace kd {
@@ -393,12 +395,14 @@ __global__ __launch_bounds__(64 * kFaWaves) void fa_split_kernel(FaPlan p, const
 }
 
 // grid (H, B); HD threads.  Merge the row's chunks in chunk order; optionally quantise.
-// Every load of the first kCombineFast chunks -- their m and l, and this thread's dimension
-// of their partial outputs -- is issued at once, so a row with up to kCombineFast chunks
-// costs one memory round trip; further chunks are merged in LDS-staged batches.
+// Every load of the first FAST chunks -- their m and l, and this thread's dimension of their
+// partial outputs -- is issued at once, so a row with up to FAST chunks costs one memory
+// round trip; further chunks are merged in LDS-staged batches.  FAST (16, 32, 48 or 64: the
+// smallest covering the launch's longest row) only sets how many loads are issued up front:
+// the merge runs the same operations in the same order for any FAST.
 constexpr int kCombineFast = 64;
 constexpr int kCombineStage = 1024;
-template <int HD, bool GATED>
+template <int HD, bool GATED, int FAST>
 __global__ __launch_bounds__(HD) void fa_combine_kernel(FaPlan p, const float* __restrict__ ws, float* __restrict__ out,
                                                         int8_t* __restrict__ oq, float* __restrict__ od,
                                                         const float* __restrict__ gate, int ldg) {
@@ -417,9 +421,9 @@ __global__ __launch_bounds__(HD) void fa_combine_kernel(FaPlan p, const float* _
   const __amdgpu_buffer_rsrc_t rl = make_rsrc(pl + (size_t)s0 * H, (uint32_t)S * H * 4);
   const float mv = buf4f(rm, d < S ? (uint32_t)(d * H + h) * 4 : kOOB);  // thread d: chunk d
   const float lv = buf4f(rl, d < S ? (uint32_t)(d * H + h) * 4 : kOOB);
-  float ov[kCombineFast];
+  float ov[FAST];
 #pragma unroll
-  for (int i = 0; i < kCombineFast; ++i) ov[i] = buf4f(ro, (uint32_t)((i * H + h) * HD + d) * 4);
+  for (int i = 0; i < FAST; ++i) ov[i] = buf4f(ro, (uint32_t)((i * H + h) * HD + d) * 4);
   __builtin_amdgcn_sched_barrier(0);
 
   __shared__ float wm[kCombineStage];
@@ -432,21 +436,21 @@ __global__ __launch_bounds__(HD) void fa_combine_kernel(FaPlan p, const float* _
   __syncthreads();
   M = red[0];
   for (int i = 1; i < HD / 64; ++i) M = fmaxf(M, red[i]);
-  if (d < S && d < kCombineFast) {
+  if (d < S && d < FAST) {
     const float w = fast_exp2(mv - M);
     wm[d] = w;
     wl[d] = w * lv;
   }
   __syncthreads();
   float num = 0.0f, den = 0.0f;
-  const int nf = S < kCombineFast ? S : kCombineFast;
+  const int nf = S < FAST ? S : FAST;
 #pragma unroll
-  for (int i = 0; i < kCombineFast; ++i)
+  for (int i = 0; i < FAST; ++i)
     if (i < nf) {
       num = fmaf(wm[i], ov[i], num);
       den += wl[i];
     }
-  for (int base = kCombineFast; base < S; base += kCombineStage) {
+  for (int base = FAST; base < S; base += kCombineStage) {
     const int n = min(kCombineStage, S - base);
     __syncthreads();
     for (int s = d; s < n; s += HD) {
@@ -511,6 +515,15 @@ static void launch_fa_c(const FaPlan& p, const float* q, int ldq, const RowCache
                                                                     static_cast<float*>(ws));
 }
 
+template <int HD, int FAST>
+static void launch_combine(const FaPlan& p, const float* ws, float* out, int8_t* oq, float* od, const float* gate,
+                           int ldq, hipStream_t st) {
+  if (gate)
+    fa_combine_kernel<HD, true, FAST><<<dim3(p.H, p.B), HD, 0, st>>>(p, ws, out, oq, od, gate, ldq);
+  else
+    fa_combine_kernel<HD, false, FAST><<<dim3(p.H, p.B), HD, 0, st>>>(p, ws, out, oq, od, nullptr, 0);
+}
+
 template <int R, int HD>
 static void launch_fa_t(const FaPlan& p, const float* q, int ldq, const RowCaches& rc, int capacity, float scale,
                         float* out, int8_t* oq, float* od, void* ws, hipStream_t st, const float* gate, bool f8) {
@@ -525,11 +538,17 @@ static void launch_fa_t(const FaPlan& p, const float* q, int ldq, const RowCache
     else
       launch_fa_c<R, HD, R, false>(p, q, ldq, rc, capacity, scale, ws, st);
   }
-  if (gate)
-    fa_combine_kernel<HD, true><<<dim3(p.H, p.B), HD, 0, st>>>(p, static_cast<const float*>(ws), out, oq, od, gate, ldq);
+  int smax = 0;
+  for (int b = 0; b < p.B; ++b) smax = std::max(smax, (int)(p.split_off[b + 1] - p.split_off[b]));
+  const float* w = static_cast<const float*>(ws);
+  if (smax <= 16)
+    launch_combine<HD, 16>(p, w, out, oq, od, gate, ldq, st);
+  else if (smax <= 32)
+    launch_combine<HD, 32>(p, w, out, oq, od, gate, ldq, st);
+  else if (smax <= 48)
+    launch_combine<HD, 48>(p, w, out, oq, od, gate, ldq, st);
   else
-    fa_combine_kernel<HD, false><<<dim3(p.H, p.B), HD, 0, st>>>(p, static_cast<const float*>(ws), out, oq, od, nullptr,
-                                                                0);
+    launch_combine<HD, kCombineFast>(p, w, out, oq, od, gate, ldq, st);
 }
 
 // Rows that can share one pass over their keys: consecutive rows of one cache (same K and V
