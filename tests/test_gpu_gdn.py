@@ -96,3 +96,33 @@ def test_gdn_recurrence_over_steps():
     o = kd.kd_gdn_step(_dev(k), _dev(k), _dev(v), _dev(np.zeros_like(g)), _dev(np.ones_like(beta)),
                        [s.data_ptr() for s in st], [s.data_ptr() for s in st], 1.0).cpu().numpy()
     np.testing.assert_allclose(o, v, rtol=0, atol=2e-4 * np.abs(v).max())
+
+
+def test_gdn_degenerate_cases():
+    """No decay and beta = 0 leave the state unchanged bit for bit (exp(0) = 1 and a zero
+    correction are exact); beta = 0 alone is a pure decay; a zero state with a unit key and
+    beta = 1 becomes v k^T, whose readout at q = k is v."""
+    say("gdn degenerate cases")
+    B, H = 4, 8
+    r = np.random.default_rng(11)
+    q, k, v, g, beta = _inputs(r, B, H)
+    S0 = [r.standard_normal((H, D, D)).astype(np.float32) for _ in range(B)]
+    sin = [_dev(s) for s in S0]
+    sout = [torch.empty_like(s) for s in sin]
+    zeros = np.zeros((B, H), dtype=np.float32)
+    kd.kd_gdn_step(_dev(q), _dev(k), _dev(v), _dev(zeros), _dev(zeros), [s.data_ptr() for s in sin],
+                   [s.data_ptr() for s in sout], 1.0)
+    for b in range(B):
+        np.testing.assert_array_equal(sout[b].cpu().numpy().view(np.uint32), S0[b].view(np.uint32))
+    kd.kd_gdn_step(_dev(q), _dev(k), _dev(v), _dev(g), _dev(zeros), [s.data_ptr() for s in sin],
+                   [s.data_ptr() for s in sout], 1.0)
+    for b in range(B):
+        ref = np.exp(g[b].astype(np.float64))[:, None, None] * S0[b]
+        _close(sout[b].cpu().numpy(), ref, 1e-6, f"pure decay row {b}")
+    zs = [torch.zeros((H, D, D), dtype=torch.float32, device="cuda") for _ in range(B)]
+    o = kd.kd_gdn_step(_dev(k), _dev(k), _dev(v), _dev(zeros), _dev(np.ones_like(zeros)), [s.data_ptr() for s in zs],
+                       [s.data_ptr() for s in zs], 1.0).cpu().numpy()
+    for b in range(B):
+        ref = v[b].astype(np.float64)[:, :, None] * k[b].astype(np.float64)[:, None, :]
+        _close(zs[b].cpu().numpy(), ref, 1e-6, f"zero state row {b}")
+    np.testing.assert_allclose(o, v, rtol=0, atol=1e-5 * np.abs(v).max())
