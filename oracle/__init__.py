@@ -17,6 +17,6 @@ brute force and library routines; the end-to-end values of whole configurations
 have no external pin beyond that chain (parity unpinned beyond the op-level pins).
 """
 from .ops import (QK, accept_drafts, attention, block_dots, dequantize, dequantize_act, e4m3_decode,  # noqa: F401
-                  e4m3_encode, e4m3_values, embed_rows, gdn_step, greedy_token,
+                  e4m3_encode, e4m3_values, embed_rows, gdn_step, greedy_token, sigmoid,
                   mmvq, mmvq_blocks, quantize_act, rmsnorm, rope_neox, router_topk, silu, swiglu, weight_codes)
-from .step import DenseWeights, OracleCaches, decode_step, moe_ffn  # noqa: F401
+from .step import DenseWeights, OracleCaches, decode_layer, decode_step, moe_ffn, output_head  # noqa: F401

@@ -163,7 +163,8 @@ def silu(g: np.ndarray) -> np.ndarray:
 def sigmoid(g: np.ndarray) -> np.ndarray:
     """``1 / (1 + e^-g)`` in fp64 (memra-engine decode_batch.rs, the attention output gate)."""
     g = np.asarray(g, dtype=np.float64)
-    return 1.0 / (1.0 + np.exp(-g))
+    with np.errstate(over="ignore"):   # e^-g = inf for g << 0 gives the limit 0 exactly
+        return 1.0 / (1.0 + np.exp(-g))
 
 
 def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:

@@ -8,7 +8,9 @@ products at m = B -> RoPE with per-row positions -> phase A, append every row's 
 phase B, every row attends over its own cache -> o product -> residual add +
 post-attention norm -> quantise -> gate/up -> silu_mul -> quantise -> down -> residual
 add; then the output norm and lm_head (``decode_step_batch_lean_masked``).  The block
-variants that page also carries (QK-norm, output gate) are not part of this model.  The
+variants of the same walk are options of a layer: QK-norm (per-head RMSNorm of q and k
+before RoPE), the attention output gate (sigmoid of extra projection rows times the
+attention output, before the o product) and the sliding-window view.  The
 MoE FFN follows hf2q ADR-040 §0.7 F4 (per-token top-k routing, each active expert's
 matrices applied to the rows routed to it, weighted sum) and the shared expert of the
 Strata pull request #1524 ("What changes").
@@ -80,7 +82,7 @@ def _q(x: np.ndarray):
 
 
 def moe_ffn(spec, L: Dict, z: np.ndarray, zq, zd, dense: Optional[DenseWeights], blocks: bool,
-            route_override: Optional[Dict[int, np.ndarray]] = None, info: Optional[Dict] = None):
+            info: Optional[Dict] = None):
     """Routed experts + shared expert for rows ``z[B, d]`` (reading: rank-ordered sum, then + shared)."""
     B, d = z.shape
     E, k, Fe = spec.n_experts, spec.n_expert_used, spec.expert_ffn
@@ -88,15 +90,12 @@ def moe_ffn(spec, L: Dict, z: np.ndarray, zq, zd, dense: Optional[DenseWeights],
     out = np.zeros((B, d), dtype=np.float64)
     for b in range(B):
         ids, p = ops.router_topk(r[b], k)
-        if route_override is not None and b in route_override:
-            ids = np.asarray(route_override[b])
-            zz = r[b][ids] - np.max(r[b][ids])
-            p = np.exp(zz) / np.sum(np.exp(zz))
-        if info is not None:
+        if info is not None:   # the routing decision, and how close it came to another one
             srt = np.sort(r[b])[::-1]
-            info.setdefault("gap", []).append(float(srt[k - 1] - srt[k]))
+            info.setdefault("gap", []).append(float(srt[k - 1] - srt[k]) if k < E else np.inf)
             info.setdefault("kth", []).append(float(abs(srt[k - 1])))
             info.setdefault("ids", []).append(ids.copy())
+            info.setdefault("p", []).append(p.copy())
         acc = np.zeros(d, dtype=np.float64)
         for rank in range(k):
             e = int(ids[rank])
@@ -131,74 +130,95 @@ def _attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, length: int, win: int) 
     return ops.attention(q, K, V, length)
 
 
-def decode_step(model: Dict, caches: OracleCaches, x_in: np.ndarray, sessions: Sequence[int],
-                pos: Sequence[int], dense: Optional[DenseWeights] = None, blocks: bool = False,
-                route_override: Optional[Dict] = None, info: Optional[Dict] = None,
-                trace: Optional[List] = None) -> np.ndarray:
-    """One decode step for rows ``x_in[B, d]``; row b writes and reads cache ``sessions[b]``.
-
-    Row b appends its K/V at ``pos[b]`` and attends the first ``pos[b] + 1`` keys; every
-    append of the layer precedes every attention (phase A / phase B of the batched walk),
-    so rows sharing a cache at consecutive positions attend causally.  Returns logits
-    ``[B, vocab]`` if the model has an lm_head, the output-normed rows if it has an output
-    norm, else the residual stream.  Caches are updated in place.
-    """
+def decode_layer(model: Dict, il: int, caches: OracleCaches, x: np.ndarray, sessions: Sequence[int],
+                 pos: Sequence[int], dense: Optional[DenseWeights] = None, blocks: bool = False,
+                 info: Optional[Dict] = None, trace: Optional[List] = None) -> np.ndarray:
+    """Layer ``il`` of the stack on the residual rows ``x[B, d]`` (fp64): returns the residual
+    rows after the layer.  Row b appends its K/V at ``pos[b]`` of cache ``sessions[b]`` (layer
+    il) and attends the first ``pos[b] + 1`` keys; every append precedes every attention
+    (phase A / phase B of the batched walk), so rows sharing a cache at consecutive positions
+    attend causally.  ``info`` (MoE layers) receives the routing of each row."""
     sp = model["spec"]
+    L = model["layers"][il]
     H, G, hd, eps = sp.n_head, sp.n_head_kv, sp.head_dim, sp.rms_eps
-    x = np.asarray(x_in, dtype=np.float32).astype(np.float64)
+    x = np.asarray(x, dtype=np.float64)
     B = x.shape[0]
-    for il, L in enumerate(model["layers"]):
-        xn = ops.rmsnorm(x, L["attn_norm"], eps)
-        xq, xd = _q(xn)
-        qkv = _mm(L["wqkv"], xq, xd, dense, blocks)
-        q = qkv[:, : H * hd].reshape(B, H, hd)
-        k = qkv[:, H * hd: (H + G) * hd].reshape(B, G, hd)
-        v = qkv[:, (H + G) * hd: (H + 2 * G) * hd].reshape(B, G, hd)
-        gate = qkv[:, (H + 2 * G) * hd:].reshape(B, H, hd) if L.get("attn_gate") else None
-        if "q_norm" in L:   # QK-norm: every head RMS-normalised over its hd values, before RoPE
-            q = ops.rmsnorm(q, L["q_norm"], eps)
-            k = ops.rmsnorm(k, L["k_norm"], eps)
-        q = np.stack([ops.rope_neox(q[b], pos[b], sp.rope_base) for b in range(B)])
-        k = np.stack([ops.rope_neox(k[b], pos[b], sp.rope_base) for b in range(B)])
-        fp8 = getattr(sp, "kv_fp8", False)
-        for b in range(B):                                   # phase A: append all rows
-            s = sessions[b]
-            if fp8:   # FP8 caches: the nearest E4M3 code of each value
-                caches.K[s][il][:, pos[b]] = ops.e4m3_encode(k[b])
-                caches.V[s][il][:, pos[b]] = ops.e4m3_encode(v[b])
-            else:
-                caches.K[s][il][:, pos[b]] = k[b].astype(np.float16)
-                caches.V[s][il][:, pos[b]] = v[b].astype(np.float16)
-        win = int(L.get("swa_window", 0))
-
-        def kv(s):   # the values a row attends (codes read as their E4M3 values)
-            K, V = caches.K[s][il], caches.V[s][il]
-            return (ops.e4m3_decode(K), ops.e4m3_decode(V)) if fp8 else (K, V)
-        attn = np.stack([_attend(q[b], *kv(sessions[b]), pos[b] + 1, win)
-                         for b in range(B)])                  # phase B: attend
-        if gate is not None:   # output gate: every attention output element times sigmoid(gate)
-            attn = attn * ops.sigmoid(gate)
-        aq, ad = _q(attn.reshape(B, H * hd))
-        x1 = x + _mm(L["wo"], aq, ad, dense, blocks)
-        if trace is not None:
-            trace.append({"layer": il, "q": q, "k": k, "v": v, "attn": attn, "x1": x1})
-        if not sp.has_ffn:
-            x = x1
-            continue
-        z = ops.rmsnorm(x1, L["ffn_norm"], eps)
-        zq, zd = _q(z)
-        if sp.n_experts:
-            f = moe_ffn(sp, L, z, zq, zd, dense, blocks, route_override.get(il) if route_override else None,
-                        info.setdefault(il, {}) if info is not None else None)
+    xn = ops.rmsnorm(x, L["attn_norm"], eps)
+    xq, xd = _q(xn)
+    qkv = _mm(L["wqkv"], xq, xd, dense, blocks)
+    q = qkv[:, : H * hd].reshape(B, H, hd)
+    k = qkv[:, H * hd: (H + G) * hd].reshape(B, G, hd)
+    v = qkv[:, (H + G) * hd: (H + 2 * G) * hd].reshape(B, G, hd)
+    # output gate (gated layers): H hd more projection rows after v, one gate per attention
+    # output element
+    gate = qkv[:, (H + 2 * G) * hd:(2 * H + 2 * G) * hd].reshape(B, H, hd) if L.get("attn_gate") else None
+    if "q_norm" in L:   # QK-norm: every head RMS-normalised over its hd values, before RoPE
+        q = ops.rmsnorm(q, L["q_norm"], eps)
+        k = ops.rmsnorm(k, L["k_norm"], eps)
+    q = np.stack([ops.rope_neox(q[b], pos[b], sp.rope_base) for b in range(B)])
+    k = np.stack([ops.rope_neox(k[b], pos[b], sp.rope_base) for b in range(B)])
+    fp8 = getattr(sp, "kv_fp8", False)
+    for b in range(B):                                   # phase A: append all rows
+        s = sessions[b]
+        if fp8:   # FP8 caches: the nearest E4M3 code of each value
+            caches.K[s][il][:, pos[b]] = ops.e4m3_encode(k[b])
+            caches.V[s][il][:, pos[b]] = ops.e4m3_encode(v[b])
         else:
-            g = _mm(L["w_gate"], zq, zd, dense, blocks)
-            u = _mm(L["w_up"], zq, zd, dense, blocks)
-            hq, hdd = _q(ops.swiglu(g, u))
-            f = _mm(L["w_down"], hq, hdd, dense, blocks)
-        x = x1 + f
+            caches.K[s][il][:, pos[b]] = k[b].astype(np.float16)
+            caches.V[s][il][:, pos[b]] = v[b].astype(np.float16)
+    win = int(L.get("swa_window", 0))
+
+    def kv(s):   # the values a row attends (codes read as their E4M3 values)
+        K, V = caches.K[s][il], caches.V[s][il]
+        return (ops.e4m3_decode(K), ops.e4m3_decode(V)) if fp8 else (K, V)
+    attn = np.stack([_attend(q[b], *kv(sessions[b]), pos[b] + 1, win)
+                     for b in range(B)])                  # phase B: attend
+    if gate is not None:   # every attention output element times sigmoid of its gate, before W_o
+        attn = attn * ops.sigmoid(gate)
+    aq, ad = _q(attn.reshape(B, H * hd))
+    x1 = x + _mm(L["wo"], aq, ad, dense, blocks)
+    if trace is not None:
+        trace.append({"layer": il, "q": q, "k": k, "v": v, "attn": attn, "x1": x1})
+    if not sp.has_ffn:
+        return x1
+    z = ops.rmsnorm(x1, L["ffn_norm"], eps)
+    zq, zd = _q(z)
+    if sp.n_experts:
+        f = moe_ffn(sp, L, z, zq, zd, dense, blocks, info)
+    else:
+        g = _mm(L["w_gate"], zq, zd, dense, blocks)
+        u = _mm(L["w_up"], zq, zd, dense, blocks)
+        hq, hdd = _q(ops.swiglu(g, u))
+        f = _mm(L["w_down"], hq, hdd, dense, blocks)
+    return x1 + f
+
+
+def output_head(model: Dict, x: np.ndarray, dense: Optional[DenseWeights] = None, blocks: bool = False) -> np.ndarray:
+    """The stack's output from the residual rows after its last layer: logits ``[B, vocab]``
+    if the model has an lm_head (output norm, Q, lm_head), the output-normed rows if it has an
+    output norm, else the residual rows themselves."""
+    sp = model["spec"]
+    x = np.asarray(x, dtype=np.float64)
     if model["final_norm"] is not None:
-        x = ops.rmsnorm(x, model["final_norm"], eps)
+        x = ops.rmsnorm(x, model["final_norm"], sp.rms_eps)
     if model["lm_head"] is not None:
         oq, od = _q(x)
         x = _mm(model["lm_head"], oq, od, dense, blocks)
     return x
+
+
+def decode_step(model: Dict, caches: OracleCaches, x_in: np.ndarray, sessions: Sequence[int],
+                pos: Sequence[int], dense: Optional[DenseWeights] = None, blocks: bool = False,
+                info: Optional[Dict] = None, trace: Optional[List] = None) -> np.ndarray:
+    """One decode step for rows ``x_in[B, d]``; row b writes and reads cache ``sessions[b]``.
+
+    Every layer in order (:func:`decode_layer`), then :func:`output_head`.  Returns logits
+    ``[B, vocab]`` if the model has an lm_head, the output-normed rows if it has an output
+    norm, else the residual stream.  Caches are updated in place.  ``info[il]`` receives the
+    routing of MoE layer il.
+    """
+    x = np.asarray(x_in, dtype=np.float32).astype(np.float64)
+    for il in range(len(model["layers"])):
+        x = decode_layer(model, il, caches, x, sessions, pos, dense, blocks,
+                         info.setdefault(il, {}) if info is not None else None, trace)
+    return output_head(model, x, dense, blocks)

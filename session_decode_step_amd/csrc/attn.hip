@@ -19,9 +19,7 @@
 
 namespace kd {
 
-#ifndef KD_FA_AUX
-#define KD_FA_AUX 2       // cache policy of the K/V loads (2: non-temporal)
-#endif
+constexpr int kKvAux = 2;  // cache policy of the K/V loads: non-temporal (each key is read once)
 
 constexpr int kFaMinChunk = 128;
 constexpr int kFaMaxSplits = 128;
@@ -226,9 +224,9 @@ __global__ __launch_bounds__(64 * kFaWaves) void fa_split_kernel(FaPlan p, const
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
       if constexpr (F8)
-        k8[j] = buf8<KD_FA_AUX>(rk, kb + j * 32);
+        k8[j] = buf8<kKvAux>(rk, kb + j * 32);
       else
-        kr[j] = buf16<KD_FA_AUX>(rk, kb + j * 64);
+        kr[j] = buf16<kKvAux>(rk, kb + j * 64);
     }
     // V: key wk + 4gq + t, dims 8n .. 8n+7 (lanes with 8n >= HD read bytes whose outputs are dropped)
     const uint32_t vb0 = ((uint32_t)(k0 + wk + 4 * gq) * HD + 8 * n) * ES;
@@ -237,9 +235,9 @@ __global__ __launch_bounds__(64 * kFaWaves) void fa_split_kernel(FaPlan p, const
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       if constexpr (F8)
-        v8[t] = buf8<KD_FA_AUX>(rv, vb0 + t * HD);
+        v8[t] = buf8<kKvAux>(rv, vb0 + t * HD);
       else
-        vr[t] = buf16<KD_FA_AUX>(rv, vb0 + t * HD * 2);
+        vr[t] = buf16<kKvAux>(rv, vb0 + t * HD * 2);
     }
     __builtin_amdgcn_sched_barrier(0);  // every K and V load of the tile ahead of the math
     if (t0 == 0) {

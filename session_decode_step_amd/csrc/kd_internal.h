@@ -217,6 +217,9 @@ struct RowMap {
   int act_rows;             // rows of the activation buffer the act_row entries index
 };
 
+// Whether a Q8_0/Q4_0 matrix fits the product (k <= mmvq_max_k(), tiled arrays < 2 GiB).
+bool mmvq_weight_fits(int fmt, int n_out, int k);
+int mmvq_max_k();
 void launch_mmvq(const kd_weight& W, const int8_t* xq, const float* xd, int B, float* y, int ldy,
                  hipStream_t st, const RowMap* map = nullptr, int32_t* debug_S = nullptr);
 

@@ -22,40 +22,17 @@
 
 namespace kd {
 
-#ifndef KD_MMVQ_NT
-#define KD_MMVQ_NT 1
-#endif
-#ifndef KD_MMVQ_DEPTH_Q4
-#define KD_MMVQ_DEPTH_Q4 2
-#endif
-#ifndef KD_MMVQ_DEPTH_Q8
-#define KD_MMVQ_DEPTH_Q8 2
-#endif
-#ifndef KD_MMVQ_WAVE_QUADS
-#define KD_MMVQ_WAVE_QUADS 8
-#endif
-#ifndef KD_MMVQ_DEPTH_RG
-#define KD_MMVQ_DEPTH_RG 4  // ring depth when a workgroup streams several row groups
-#endif
-#ifndef KD_MMVQ_DEPTH_RN
-#define KD_MMVQ_DEPTH_RN 4  // ring depth of the add + RMSNorm products (two row groups)
-#endif
-#ifndef KD_MMVQ_TILE_FENCE
-#define KD_MMVQ_TILE_FENCE 1
-#endif
-#ifndef KD_MMVQ_RG
-#define KD_MMVQ_RG 1  // row groups per workgroup (they share the activation operands)
-#endif
-#ifndef KD_MMVQ_QW_SWIGLU
-#define KD_MMVQ_QW_SWIGLU KD_MMVQ_WAVE_QUADS  // quads per wave of the gate/up product
-#endif
-#ifndef KD_MMVQ_QW_ROPE
-#define KD_MMVQ_QW_ROPE KD_MMVQ_WAVE_QUADS  // quads per wave of the QKV product
-#endif
-#ifndef KD_MMVQ_QW_RN
-#define KD_MMVQ_QW_RN 2  // quads per wave of the add + RMSNorm products
-#endif
-
+// Launch shape constants (measured on MI355X; see the mmvq design notes).
+constexpr bool kWeightNT = true;  // weight tiles are streamed once: non-temporal loads
+constexpr int kDepthQ4 = 2;       // weight-ring depth, one row group per workgroup, Q4_0
+constexpr int kDepthQ8 = 2;       // the same for Q8_0
+constexpr int kDepthRG = 4;       // ring depth when a workgroup streams several row groups
+constexpr int kDepthRN = 4;       // ring depth of the add + RMSNorm products (two row groups)
+constexpr int kWaveQuads = 8;     // quads per wave of the plain, SwiGLU and RoPE products
+constexpr int kQuadsRN = 2;       // quads per wave of the add + RMSNorm products
+constexpr int kPlainRG = 1;       // row groups per workgroup of the plain product
+// the largest k a product takes: 16 waves of kWaveQuads quads of 128 elements
+constexpr int kMaxK = 16 * kWaveQuads * 128;
 
 constexpr int kTileQ8 = 2048;
 constexpr int kTileQ4 = 1024;
@@ -247,7 +224,7 @@ __device__ __forceinline__ float half_bits(uint32_t hw, int hi) {
   return __half2float(__ushort_as_half((unsigned short)(hi ? (hw >> 16) : (hw & 0xFFFF))));
 }
 
-constexpr int kWeightAux = KD_MMVQ_NT ? 2 : 0;
+constexpr int kWeightAux = kWeightNT ? 2 : 0;
 
 // One weight tile of a wave's stream: 16 bytes per lane (two for Q8_0).
 template <int FMT>
@@ -285,10 +262,7 @@ __host__ __device__ constexpr int mmvq_wave_lds(int QW, int RG) { return 16 * QW
 template <int FMT, int QW, int NS, int RG, int EPI, bool DEBUG>
 __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
   constexpr int NT = RG * QW;
-  constexpr int D0 = EPI == EPI_RESNORM ? KD_MMVQ_DEPTH_RN
-                     : RG > 1             ? KD_MMVQ_DEPTH_RG
-                     : FMT == KD_FMT_Q8_0 ? KD_MMVQ_DEPTH_Q8
-                                          : KD_MMVQ_DEPTH_Q4;
+  constexpr int D0 = EPI == EPI_RESNORM ? kDepthRN : RG > 1 ? kDepthRG : FMT == KD_FMT_Q8_0 ? kDepthQ8 : kDepthQ4;
   constexpr int D = D0 < NT ? D0 : NT;
   const int e = blockIdx.y;
   int nrows = a.B;
@@ -454,7 +428,7 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
       const int j2 = (t + D) / RG, r2 = (t + D) % RG;
       wstage_load<FMT>(cur, rw, gtile + (uint32_t)(rg0 + r2) * NQ + q0 + j2, q0 + j2 < q1 && rg0 + r2 < a.NR, lane);
     }
-    if (RG > 1 && KD_MMVQ_TILE_FENCE) __builtin_amdgcn_sched_barrier(0);  // tiles do not interleave (registers)
+    if (RG > 1) __builtin_amdgcn_sched_barrier(0);  // tiles do not interleave (registers)
   }
   if (DEBUG) return;
 
@@ -606,10 +580,10 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
   }
 }
 
-// Quads per wave: about NQ / 4 (four waves per workgroup), between 2 and KD_MMVQ_WAVE_QUADS,
+// Quads per wave: about NQ / 4 (four waves per workgroup), between 2 and kWaveQuads,
 // and enough that at most 16 waves cover NQ; then balanced (the smallest QW giving the same
 // wave count).  Waves per workgroup: ceil(NQ / QW).  Both depend on the matrix's k only.
-static int mmvq_qw(int NQ, int want_quads = KD_MMVQ_WAVE_QUADS) {
+static int mmvq_qw(int NQ, int want_quads = kWaveQuads) {
   int qw = ceil_div(NQ, 16);  // at most 16 waves; QW <= 8 covers k <= 16384
   want_quads = NQ / 4 < want_quads ? (NQ / 4 > 2 ? NQ / 4 : 2) : want_quads;
   const int want = NQ < want_quads ? NQ : want_quads;
@@ -701,7 +675,7 @@ static void launch_mmvq_fmt(const kd_weight& W, const MmvqArgs& a, int ng, hipSt
 void launch_mmvq(const kd_weight& W, const int8_t* xq, const float* xd, int B, float* y, int ldy,
                  hipStream_t st, const RowMap* map, int32_t* debug_S) {
   const MmvqArgs a = mmvq_args(W, xq, xd, B, y, ldy, map, debug_S);
-  launch_mmvq_fmt<KD_MMVQ_RG, EPI_PLAIN>(W, a, map ? map->n_groups : 1, st);
+  launch_mmvq_fmt<kPlainRG, EPI_PLAIN>(W, a, map ? map->n_groups : 1, st);
 }
 
 void launch_mmvq_swiglu(const kd_weight& W, const int8_t* xq, const float* xd, int B, int8_t* out_qs, float* out_d,
@@ -712,7 +686,7 @@ void launch_mmvq_swiglu(const kd_weight& W, const int8_t* xq, const float* xd, i
   a.norm_ss = norm_ss;
   a.norm_n = norm_n;
   a.norm_eps = norm_eps;
-  a.QW = mmvq_qw(a.NQ, KD_MMVQ_QW_SWIGLU);
+  a.QW = mmvq_qw(a.NQ, kWaveQuads);
   launch_mmvq_fmt<4, EPI_SWIGLU>(W, a, map ? map->n_groups : 1, st);
 }
 
@@ -721,7 +695,7 @@ void launch_mmvq_swiglu(const kd_weight& W, const int8_t* xq, const float* xd, i
 void launch_mmvq_resnorm(const kd_weight& W, const int8_t* xq, const float* xd, int B, const float* res, int ld,
                          const float* gain, float* x1, int8_t* out_qs, float* out_d, float* ss, hipStream_t st) {
   MmvqArgs a = mmvq_args(W, xq, xd, B, nullptr, 0, nullptr, nullptr);
-  a.QW = mmvq_qw(a.NQ, KD_MMVQ_QW_RN);
+  a.QW = mmvq_qw(a.NQ, kQuadsRN);
   a.epi_res = res;
   a.epi_ld = ld;
   a.epi_gain = gain;
@@ -749,9 +723,19 @@ void launch_mmvq_rope(const kd_weight& W, const int8_t* xq, const float* xd, int
   a.epi_cs = cs;
   a.epi_rc = rc;
   a.epi_capacity = capacity;
-  a.QW = mmvq_qw(a.NQ, KD_MMVQ_QW_ROPE);
+  a.QW = mmvq_qw(a.NQ, kWaveQuads);
   launch_mmvq_fmt<1, EPI_ROPE>(W, a, 1, st);
 }
+
+// A product's limits: k up to kMaxK (the widest wave partition), and the tiled codes and
+// scales addressable by 32-bit buffer offsets with kOOB past their end.
+bool mmvq_weight_fits(int fmt, int n_out, int k) {
+  if (n_out <= 0 || k <= 0 || k > kMaxK) return false;
+  const size_t tiles = (size_t)n_rowgroups(n_out) * n_quads(k);
+  const size_t qs = tiles * (fmt == KD_FMT_Q8_0 ? kTileQ8 : kTileQ4);
+  return qs < (size_t)kOOB && tiles * 128 < (size_t)kOOB;
+}
+int mmvq_max_k() { return kMaxK; }
 
 void launch_act_quant(const float* x, int B, int k, int ldx, int8_t* qs, float* d, hipStream_t st) {
   const int NQ = n_quads(k);
@@ -829,6 +813,9 @@ static kd_status check_mmvq_args(const char* who, const kd_weight* W, int32_t wa
   KD_REQUIRE(B >= 1 && B <= KD_MAX_B, KD_ERR_UNSUPPORTED, "%s: B=%d outside [1,16]", who, B);
   KD_REQUIRE(W->n_out > 0 && W->k > 0, KD_ERR_INVALID, "%s: bad shape %d x %d", who, W->n_out, W->k);
   KD_REQUIRE(W->k % 32 == 0, KD_ERR_UNSUPPORTED, "%s: k=%d is not a multiple of 32", who, W->k);
+  KD_REQUIRE(mmvq_weight_fits(W->fmt, W->n_out, W->k), KD_ERR_UNSUPPORTED,
+             "%s: %d x %d exceeds the product's limits (k <= %d, tiled codes under 2 GiB)", who, W->n_out, W->k,
+             kMaxK);
   KD_REQUIRE(W->qs && W->d && x.qs && x.d, KD_ERR_INVALID, "%s: null pointer", who);
   KD_REQUIRE(aligned16(W->qs) && aligned16(W->d) && aligned16(x.qs) && aligned16(x.d), KD_ERR_INVALID,
              "%s: buffers must be 16-byte aligned", who);

@@ -71,6 +71,9 @@ static kd_status check_weight(const char* name, int il, const kd_weight& w, int 
     KD_REQUIRE(w.d, KD_ERR_INVALID, "kd_model_create: layer %d %s: null scales", il, name);
     KD_REQUIRE(k % 32 == 0, KD_ERR_UNSUPPORTED, "kd_model_create: layer %d %s: k=%d not a multiple of 32", il, name, k);
     KD_REQUIRE(aligned16(w.qs) && aligned16(w.d), KD_ERR_INVALID, "kd_model_create: layer %d %s: unaligned", il, name);
+    KD_REQUIRE(mmvq_weight_fits(w.fmt, n_out, k), KD_ERR_UNSUPPORTED,
+               "kd_model_create: layer %d %s: %d x %d exceeds the product's limits (k <= %d, tiled codes under 2 GiB)",
+               il, name, n_out, k, mmvq_max_k());
   }
   return KD_OK;
 }

@@ -427,6 +427,84 @@ def test_moe_routed_sum_equals_dense_masked_sum():
     np.testing.assert_allclose(routed, dense, rtol=1e-10, atol=1e-12)
 
 
+def _gated_pair(seed):
+    """A one-layer gated stack and the same stack without the gate (its wqkv without the H hd
+    gate rows), one row, and that row's quantised attention-norm input."""
+    import dataclasses
+    spec_g = dataclasses.replace(TINY, n_layers=1, attn_gate=True, vocab=0, final_norm=False)
+    spec_u = dataclasses.replace(spec_g, attn_gate=False)
+    mg = wlmod.make_model(spec_g, seed)
+    Lg = mg["layers"][0]
+    n_qkv = spec_u.qkv_rows
+    Lu = {**Lg, "attn_gate": False,
+          "wqkv": {**Lg["wqkv"], "n": n_qkv, "qs": Lg["wqkv"]["qs"][:n_qkv].copy(), "d": Lg["wqkv"]["d"][:n_qkv].copy()}}
+    mu = {**mg, "spec": spec_u, "layers": [Lu]}
+    wl = _tiny_wl(spec_g, seed, [(0, 0)], [13])
+    x = wlmod.step_inputs(wl, 0)
+    xq, _ = ops.quantize_act(ops.rmsnorm(x.astype(np.float64), Lg["attn_norm"], spec_g.rms_eps).astype(np.float32))
+    return spec_g, mg, mu, wl, x, xq
+
+
+def _set_gate_rows(model, spec, xq, sign_per_head):
+    """Gate rows of head h = sign_per_head[h] * 127 * sign(codes of the row's input), scale 1:
+    the gate is then +-127 sum |x| (huge) for that input, or exactly 0 where the sign is 0."""
+    L = model["layers"][0]
+    H, G, hd = spec.n_head, spec.n_head_kv, spec.head_dim
+    qs, d = L["wqkv"]["qs"].copy(), L["wqkv"]["d"].copy()
+    base = (H + 2 * G) * hd
+    for h in range(H):
+        rows = slice(base + h * hd, base + (h + 1) * hd)
+        qs[rows] = (sign_per_head[h] * 127 * np.sign(xq[0].astype(np.int64)))[None, :].astype(np.int8)
+        d[rows] = np.float16(1.0)
+    L["wqkv"] = {**L["wqkv"], "qs": qs, "d": d}
+
+
+def test_output_gate_saturated_open_equals_ungated():
+    """Gate rows that make every gate huge and positive: sigmoid = 1, so the gated layer equals
+    the same layer without a gate (a wrong gate slice, or a gate through silu, fails)."""
+    spec, mg, mu, wl, x, xq = _gated_pair(201)
+    _set_gate_rows(mg, spec, xq, [1] * spec.n_head)
+    yg = oracle.decode_step(mg, oracle.OracleCaches(wl), x, [0], wl.positions(0), blocks=True)
+    yu = oracle.decode_step(mu, oracle.OracleCaches(wl), x, [0], wl.positions(0), blocks=True)
+    np.testing.assert_array_equal(yg, yu)
+
+
+def test_output_gate_zero_halves_the_attention_contribution():
+    """Gate rows of zeros: every gate is 0, sigmoid = 1/2 exactly; halving the attention output
+    halves its block scales and keeps its codes, so the o product's contribution to the
+    residual is exactly half the ungated one."""
+    spec, mg, mu, wl, x, xq = _gated_pair(202)
+    _set_gate_rows(mg, spec, xq, [0] * spec.n_head)
+    tg, tu = [], []
+    oracle.decode_step(mg, oracle.OracleCaches(wl), x, [0], wl.positions(0), blocks=True, trace=tg)
+    oracle.decode_step(mu, oracle.OracleCaches(wl), x, [0], wl.positions(0), blocks=True, trace=tu)
+    x0 = x.astype(np.float64)
+    og, ou = tg[0]["x1"] - x0, tu[0]["x1"] - x0
+    assert np.abs(ou).max() > 1e-3
+    np.testing.assert_allclose(og, 0.5 * ou, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(tg[0]["attn"], 0.5 * tu[0]["attn"], rtol=1e-15, atol=0)
+
+
+def test_output_gate_closed_head_removes_that_head():
+    """Head 0's gate huge and negative (sigmoid = 0), the others huge and positive: the gated
+    layer equals the ungated layer whose o matrix has head 0's input columns zeroed (a gate
+    applied to the wrong head, or after the o product, fails)."""
+    spec, mg, mu, wl, x, xq = _gated_pair(203)
+    _set_gate_rows(mg, spec, xq, [-1] + [1] * (spec.n_head - 1))
+    hd = spec.head_dim
+    wo = mu["layers"][0]["wo"]
+    qs = wo["qs"].copy()
+    qs[:, :hd] = 0
+    mu["layers"][0] = {**mu["layers"][0], "wo": {**wo, "qs": qs}}
+    yg = oracle.decode_step(mg, oracle.OracleCaches(wl), x, [0], wl.positions(0), blocks=True)
+    yu = oracle.decode_step(mu, oracle.OracleCaches(wl), x, [0], wl.positions(0), blocks=True)
+    np.testing.assert_allclose(yg, yu, rtol=1e-12, atol=1e-12 * np.abs(yu).max())
+    # and it differs from the fully open gate by head 0's contribution
+    _set_gate_rows(mg, spec, xq, [1] * spec.n_head)
+    yo = oracle.decode_step(mg, oracle.OracleCaches(wl), x, [0], wl.positions(0), blocks=True)
+    assert np.abs(yo - yg).max() > 1e-3
+
+
 def test_verify_rows_equal_sequential_steps():
     # A stream's 4 draft rows in one step (append all, then attend) equal 4 sequential
     # single-row steps at positions L..L+3 (Strata #1524 "Fresh validation": solo and batch
