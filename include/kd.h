@@ -119,7 +119,8 @@ kd_status kd_quantize_act_q8(const float* x, int32_t B, int32_t k, int32_t ldx, 
  * the codes, for n < W->n_out, b < B; y row stride ldy floats (>= n_out).  One pass over
  * the weights serves all B rows (memra-engine decode_batch.rs ``matmul_pre`` at m = B;
  * hf2q ADR-040 §0.7 F3).  The fp32 accumulation order of each output depends only on k.
- * W->fmt must match the entry point. */
+ * W->fmt must match the entry point.  Every product takes k <= 16384 and a matrix whose
+ * tiled codes stay under 2 GiB (KD_ERR_UNSUPPORTED otherwise). */
 kd_status kd_mmvq_q8_0(const kd_weight* W, kd_act_q8 x, int32_t B, float* y, int32_t ldy, void* stream);
 kd_status kd_mmvq_q4_0(const kd_weight* W, kd_act_q8 x, int32_t B, float* y, int32_t ldy, void* stream);
 
@@ -295,6 +296,38 @@ kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x_in, const 
                          void* const* k_base, void* const* v_base, int32_t capacity, float* out,
                          void* ws, size_t ws_bytes, void* stream);
 
+/* What one step leaves behind layer by layer (tests only: teacher-forced per-layer
+ * comparison, each layer checked against a reference fed this step's own layer input and,
+ * where the activation quantiser rounds, its own integer decisions).  Device pointers, each
+ * NULL or:
+ *   resid   fp32 [n_layers + 1][B][d]: the residual rows entering layer l (l < n_layers),
+ *           then the residual rows after the last layer (before the output norm);
+ *   moe_ids int32 [n_layers][B][n_expert_used]: the experts each row is routed to in an MoE
+ *           layer, by descending router logit (ties to the lower id);
+ *   moe_p   fp32 [n_layers][B][n_expert_used]: their softmax weights, in the same order;
+ *   the int8 codes of every activation quantisation, in the tiled activation layout (rows of
+ *   NQ(k) * 128 bytes, NQ(k) = ceil(k / 128)), per layer:
+ *   q_attn_in  [n_layers][B][NQ(d) 128]      the normed attention input (the q/k/v product's);
+ *   q_attn_out [n_layers][B][NQ(H hd) 128]   the attention output (the o product's input);
+ *   q_ffn_in   [n_layers][B][NQ(d) 128]      the normed FFN input;
+ *   q_ffn_mid  [n_layers][R][NQ(F) 128]      silu(gate) up, the down product's input: dense
+ *              layers R = B rows of F = ffn; MoE layers R = B n_expert_used (row, rank) rows of
+ *              F = expert_ffn, row b K + rank;
+ *   q_shared_mid [n_layers][B][NQ(shared_ffn) 128]  the shared expert's (MoE layers);
+ *   q_head_in  [B][NQ(d) 128]                the output-normed rows entering the lm_head.
+ * Entries of layers without experts are left untouched. */
+typedef struct {
+  float* resid;
+  int32_t* moe_ids;
+  float* moe_p;
+  int8_t* q_attn_in;
+  int8_t* q_attn_out;
+  int8_t* q_ffn_in;
+  int8_t* q_ffn_mid;
+  int8_t* q_shared_mid;
+  int8_t* q_head_in;
+} kd_step_trace;
+
 /* ---- next token: greedy argmax and embedding gather ----------------------------------- */
 /* Greedy token of each row (memra-engine decode_batch.rs, ``decode_step_batch_sampled``:
  * the device argmax of each greedy row's logits, equal to the host argmax).  x: device fp32
@@ -337,6 +370,43 @@ kd_status kd_debug_fa_decode_chunked(const float* q, int32_t B, int32_t H, int32
                                      const void* const* k_base, const void* const* v_base,
                                      const int32_t* t_kv, int32_t capacity, float scale, float* out,
                                      int32_t chunk, void* ws, size_t ws_bytes, void* stream);
+
+/* kd_decode_step, computing exactly the same (same launches, same outputs and cache bytes),
+ * that also copies the per-layer record above into *trace on the same stream (device-to-
+ * device copies, plus one residual add after the last layer).  memra-engine decode_batch.rs
+ * exactness contract: each layer of the batched walk must match its reference; this export
+ * lets a test compare every layer against the oracle given the GPU's own layer input. */
+kd_status kd_debug_decode_step_trace(const kd_model* m, int32_t B, const float* x_in, const int32_t* pos,
+                                     void* const* k_base, void* const* v_base, int32_t capacity, float* out,
+                                     void* ws, size_t ws_bytes, const kd_step_trace* trace, void* stream);
+
+/* The routing of one MoE layer for B rows (tests only; the kernels kd_decode_step runs for
+ * an MoE layer, hf2q ADR-040 §0.7 F4: per-token top-k routing; rows grouped by expert).
+ * Device pointers: z fp32 [B][d] (the FFN-normed rows), router fp32 [E][d].  Writes
+ * logits fp32 [B][E] = router z (fp32, a fixed order per d); ids int32 [B][K] = the K
+ * largest logits' experts by descending logit, ties to the lower id; p fp32 [B][K] =
+ * softmax over those K logits, in the same order; and the buckets: count int32 [E] = the
+ * (row, rank) pairs routed to expert e, rows / pairs int32 [E][16] = their row b and pair
+ * index b K + rank, in ascending row order (entries past count[e] untouched).
+ * 1 <= B <= 16, 1 <= K <= min(E, 16), E <= 256, d % 4 == 0. */
+kd_status kd_debug_moe_route(const float* z, const float* router, int32_t B, int32_t d, int32_t E, int32_t K,
+                             int32_t* ids, float* p, float* logits, int32_t* count, int32_t* rows, int32_t* pairs,
+                             void* stream);
+/* The grouped product kd_decode_step runs over those buckets (tests only; hf2q ADR-040 §0.7
+ * F4: each active expert's matrices read once and applied to every row routed to it).  W
+ * is group 0 of n_groups stacked groups of W->n_out rows each (W->n_out % 16 == 0, tiled
+ * as one [n_groups n_out, k] matrix).  For group e, its j-th row (j < count[e] <= 16)
+ * multiplies activation row act_row[e][j] of x (act_rows rows) and its result goes to
+ * output row out_row[e][j]; a group with count 0 reads nothing.  count [n_groups] and
+ * act_row / out_row [n_groups][16] are device int32 arrays whose entries the caller keeps in
+ * range (act_row < act_rows; out_row < the output's rows).  swiglu = 0: y fp32 rows (stride
+ * ldy >= n_out) as kd_mmvq_q8_0 / _q4_0 give them; swiglu = 1: each group is an interleaved
+ * gate/up block [2F, k] and out receives the quantised silu(gate) up rows as kd_mmvq_swiglu
+ * writes them.  Each output row equals, bit for bit, the plain product of its group's rows
+ * with its activation row alone. */
+kd_status kd_debug_mmvq_grouped(const kd_weight* W, int32_t n_groups, kd_act_q8 x, int32_t act_rows,
+                                const int32_t* count, const int32_t* act_row, const int32_t* out_row, int32_t swiglu,
+                                float* y, int32_t ldy, kd_act_q8 out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -49,17 +49,24 @@ class OracleCaches:
     """K/V of the sessions the oracle follows: ``K[s][il]`` is ``[G, capacity, hd]``, fp16, or
     uint8 E4M3 codes for a model with FP8 caches (``spec.kv_fp8``)."""
 
-    def __init__(self, wl, sessions: Optional[Sequence[int]] = None):
+    def __init__(self, wl, sessions: Optional[Sequence[int]] = None, layers: Optional[Sequence[int]] = None):
+        """``layers``: only these layers' caches are filled (the others stay None), for
+        following single layers of a deep stack."""
         from workload import kv_prefill_many  # seeded inputs only
         sp = wl.spec
         self.sessions = list(range(len(wl.prefill))) if sessions is None else list(sessions)
+        keep = set(range(sp.n_layers) if layers is None else layers)
         self.K: Dict[int, List[np.ndarray]] = {}
         self.V: Dict[int, List[np.ndarray]] = {}
-        pairs = [(s, il) for s in self.sessions for il in range(sp.n_layers)]
+        pairs = [(s, il) for s in self.sessions for il in range(sp.n_layers) if il in keep]
         pre = dict(zip(pairs, kv_prefill_many(wl, pairs)))
         for s in self.sessions:
             self.K[s], self.V[s] = [], []
             for il in range(sp.n_layers):
+                if il not in keep:
+                    self.K[s].append(None)
+                    self.V[s].append(None)
+                    continue
                 k0, v0 = pre[(s, il)]
                 dt = np.uint8 if getattr(sp, "kv_fp8", False) else np.float16
                 K = np.zeros((sp.n_head_kv, wl.capacity, sp.head_dim), dtype=dt)
@@ -81,13 +88,46 @@ def _q(x: np.ndarray):
     return ops.quantize_act(np.asarray(x, dtype=np.float64).astype(np.float32))
 
 
+# Teacher forcing of the quantiser's integer decisions.  An fp32 evaluation of the step and
+# this fp64 one reach each quantiser with values that differ by rounding, so a value lying
+# within that difference of a rounding boundary (x / d = k + 1/2) may take either neighbouring
+# code: both are correct results.  Given another evaluation's codes, ``_q_forced`` accepts
+# each code that is such a rounding of the oracle's own value -- |x / d - code| <= 1/2 + TOL,
+# the ratio computed as Q computes it -- records how many differ from the oracle's own choice
+# and how many are not valid roundings at all, and continues with the given codes, so that
+# what follows compares continuous arithmetic only.  The scales stay the oracle's own.
+FORCE_TOL = 1e-3
+
+
+def _q_forced(x: np.ndarray, codes: Optional[np.ndarray], record: Optional[List], what: str):
+    xq, xd = _q(x)
+    if codes is None:
+        return xq, xd
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    B, K = x32.shape
+    g = np.asarray(codes, dtype=np.int64).reshape(B, K)
+    safe = np.where(xd == 0, np.float32(1.0), xd).astype(np.float32)
+    ratio = (x32.reshape(B, K // ops.QK, ops.QK) / safe[:, :, None]).astype(np.float32).astype(np.float64)
+    ratio = np.where((xd == 0)[:, :, None], 0.0, ratio).reshape(B, K)
+    dist = np.abs(ratio - g)
+    invalid = int(np.sum((dist > 0.5 + FORCE_TOL) | (np.abs(g) > 127)))
+    differ = g != xq.astype(np.int64)
+    if record is not None:
+        record.append({"what": what, "codes": int(g.size), "flips": int(differ.sum()), "invalid": invalid,
+                       "flip_margin": float(np.max(np.abs(dist[differ] - 0.5))) if differ.any() else 0.0})
+    return g.astype(np.int8), xd
+
+
 def moe_ffn(spec, L: Dict, z: np.ndarray, zq, zd, dense: Optional[DenseWeights], blocks: bool,
-            info: Optional[Dict] = None):
+            info: Optional[Dict] = None, forced: Optional[Dict] = None, record: Optional[List] = None):
     """Routed experts + shared expert for rows ``z[B, d]`` (reading: rank-ordered sum, then + shared)."""
     B, d = z.shape
     E, k, Fe = spec.n_experts, spec.n_expert_used, spec.expert_ffn
     r = z @ L["router"].astype(np.float64).T            # fp32 router weights, unquantised input
     out = np.zeros((B, d), dtype=np.float64)
+
+    def fmid(b, rank):   # forced codes of row b's rank-th expert input to its down product
+        return None if forced is None or "ffn_mid" not in forced else forced["ffn_mid"][b * k + rank:b * k + rank + 1]
     for b in range(B):
         ids, p = ops.router_topk(r[b], k)
         if info is not None:   # the routing decision, and how close it came to another one
@@ -103,19 +143,19 @@ def moe_ffn(spec, L: Dict, z: np.ndarray, zq, zd, dense: Optional[DenseWeights],
                 sub = lambda w, r0, r1: {**w, "n": r1 - r0, "qs": w["qs"][r0:r1], "d": w["d"][r0:r1]}
                 g = ops.mmvq_blocks(sub(L["e_gate"], e * Fe, (e + 1) * Fe), zq[b:b + 1], zd[b:b + 1])
                 u = ops.mmvq_blocks(sub(L["e_up"], e * Fe, (e + 1) * Fe), zq[b:b + 1], zd[b:b + 1])
-                hq, hd = _q(ops.swiglu(g, u))
+                hq, hd = _q_forced(ops.swiglu(g, u), fmid(b, rank), record, "expert mid")
                 y = ops.mmvq_blocks(sub(L["e_down"], e * d, (e + 1) * d), hq, hd)
             else:
                 g = ops.mmvq(L["e_gate"], zq[b:b + 1], zd[b:b + 1], r0=e * Fe, r1=(e + 1) * Fe)
                 u = ops.mmvq(L["e_up"], zq[b:b + 1], zd[b:b + 1], r0=e * Fe, r1=(e + 1) * Fe)
-                hq, hd = _q(ops.swiglu(g, u))
+                hq, hd = _q_forced(ops.swiglu(g, u), fmid(b, rank), record, "expert mid")
                 y = ops.mmvq(L["e_down"], hq, hd, r0=e * d, r1=(e + 1) * d)
             acc += p[rank] * y[0]
         out[b] = acc
     # Shared expert: always on, weight 1, added after the routed sum.
     g = _mm(L["s_gate"], zq, zd, dense, blocks)
     u = _mm(L["s_up"], zq, zd, dense, blocks)
-    hq, hd = _q(ops.swiglu(g, u))
+    hq, hd = _q_forced(ops.swiglu(g, u), None if forced is None else forced.get("shared_mid"), record, "shared mid")
     return out + _mm(L["s_down"], hq, hd, dense, blocks)
 
 
@@ -132,19 +172,24 @@ def _attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, length: int, win: int) 
 
 def decode_layer(model: Dict, il: int, caches: OracleCaches, x: np.ndarray, sessions: Sequence[int],
                  pos: Sequence[int], dense: Optional[DenseWeights] = None, blocks: bool = False,
-                 info: Optional[Dict] = None, trace: Optional[List] = None) -> np.ndarray:
+                 info: Optional[Dict] = None, trace: Optional[List] = None, forced: Optional[Dict] = None,
+                 record: Optional[List] = None) -> np.ndarray:
     """Layer ``il`` of the stack on the residual rows ``x[B, d]`` (fp64): returns the residual
     rows after the layer.  Row b appends its K/V at ``pos[b]`` of cache ``sessions[b]`` (layer
     il) and attends the first ``pos[b] + 1`` keys; every append precedes every attention
     (phase A / phase B of the batched walk), so rows sharing a cache at consecutive positions
-    attend causally.  ``info`` (MoE layers) receives the routing of each row."""
+    attend causally.  ``info`` (MoE layers) receives the routing of each row.  ``forced``
+    (optional) holds another evaluation's codes for the layer's quantisations ("attn_in",
+    "attn_out", "ffn_in", "ffn_mid", "shared_mid"; int8 rows), taken as described at
+    ``_q_forced`` with ``record`` receiving the counts."""
+    fc = (lambda name: None) if forced is None else forced.get
     sp = model["spec"]
     L = model["layers"][il]
     H, G, hd, eps = sp.n_head, sp.n_head_kv, sp.head_dim, sp.rms_eps
     x = np.asarray(x, dtype=np.float64)
     B = x.shape[0]
     xn = ops.rmsnorm(x, L["attn_norm"], eps)
-    xq, xd = _q(xn)
+    xq, xd = _q_forced(xn, fc("attn_in"), record, "attn in")
     qkv = _mm(L["wqkv"], xq, xd, dense, blocks)
     q = qkv[:, : H * hd].reshape(B, H, hd)
     k = qkv[:, H * hd: (H + G) * hd].reshape(B, G, hd)
@@ -175,34 +220,36 @@ def decode_layer(model: Dict, il: int, caches: OracleCaches, x: np.ndarray, sess
                      for b in range(B)])                  # phase B: attend
     if gate is not None:   # every attention output element times sigmoid of its gate, before W_o
         attn = attn * ops.sigmoid(gate)
-    aq, ad = _q(attn.reshape(B, H * hd))
+    aq, ad = _q_forced(attn.reshape(B, H * hd), fc("attn_out"), record, "attn out")
     x1 = x + _mm(L["wo"], aq, ad, dense, blocks)
     if trace is not None:
         trace.append({"layer": il, "q": q, "k": k, "v": v, "attn": attn, "x1": x1})
     if not sp.has_ffn:
         return x1
     z = ops.rmsnorm(x1, L["ffn_norm"], eps)
-    zq, zd = _q(z)
+    zq, zd = _q_forced(z, fc("ffn_in"), record, "ffn in")
     if sp.n_experts:
-        f = moe_ffn(sp, L, z, zq, zd, dense, blocks, info)
+        f = moe_ffn(sp, L, z, zq, zd, dense, blocks, info, forced, record)
     else:
         g = _mm(L["w_gate"], zq, zd, dense, blocks)
         u = _mm(L["w_up"], zq, zd, dense, blocks)
-        hq, hdd = _q(ops.swiglu(g, u))
+        hq, hdd = _q_forced(ops.swiglu(g, u), fc("ffn_mid"), record, "ffn mid")
         f = _mm(L["w_down"], hq, hdd, dense, blocks)
     return x1 + f
 
 
-def output_head(model: Dict, x: np.ndarray, dense: Optional[DenseWeights] = None, blocks: bool = False) -> np.ndarray:
+def output_head(model: Dict, x: np.ndarray, dense: Optional[DenseWeights] = None, blocks: bool = False,
+                forced: Optional[np.ndarray] = None, record: Optional[List] = None) -> np.ndarray:
     """The stack's output from the residual rows after its last layer: logits ``[B, vocab]``
     if the model has an lm_head (output norm, Q, lm_head), the output-normed rows if it has an
-    output norm, else the residual rows themselves."""
+    output norm, else the residual rows themselves.  ``forced``: another evaluation's codes of
+    the lm_head input (see ``_q_forced``)."""
     sp = model["spec"]
     x = np.asarray(x, dtype=np.float64)
     if model["final_norm"] is not None:
         x = ops.rmsnorm(x, model["final_norm"], sp.rms_eps)
     if model["lm_head"] is not None:
-        oq, od = _q(x)
+        oq, od = _q_forced(x, forced, record, "head in")
         x = _mm(model["lm_head"], oq, od, dense, blocks)
     return x
 

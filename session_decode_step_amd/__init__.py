@@ -60,6 +60,12 @@ class KdModelDesc(C.Structure):
 KD_KV_F16, KD_KV_FP8_E4M3 = 0, 1
 
 
+class KdStepTrace(C.Structure):
+    _fields_ = [("resid", C.c_void_p), ("moe_ids", C.c_void_p), ("moe_p", C.c_void_p), ("q_attn_in", C.c_void_p),
+                ("q_attn_out", C.c_void_p), ("q_ffn_in", C.c_void_p), ("q_ffn_mid", C.c_void_p),
+                ("q_shared_mid", C.c_void_p), ("q_head_in", C.c_void_p)]
+
+
 _P, _I, _F, _S = C.c_void_p, C.c_int32, C.c_float, C.c_size_t
 _PW = C.POINTER(KdWeight)
 _PP = C.POINTER(C.c_void_p)
@@ -100,6 +106,9 @@ SIGNATURES = {
     "kd_debug_block_dots": (_I, [_PW, KdAct, _I, _P, _P]),
     "kd_debug_fa_workspace": (_S, [_I, _I, _I, _PI, _I]),
     "kd_debug_fa_decode_chunked": (_I, [_P, _I, _I, _I, _I, _PP, _PP, _PI, _I, _F, _P, _I, _P, _S, _P]),
+    "kd_debug_decode_step_trace": (_I, [_P, _I, _P, _PI, _PP, _PP, _I, _P, _P, _S, C.POINTER(KdStepTrace), _P]),
+    "kd_debug_moe_route": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
+    "kd_debug_mmvq_grouped": (_I, [_PW, _I, KdAct, _I, _P, _P, _P, _I, _P, _I, KdAct, _P]),
 }
 
 _lib: Optional[C.CDLL] = None
@@ -288,6 +297,60 @@ def kd_debug_block_dots(W: PackedWeight, x: Act, B: int, stream=None) -> torch.T
     wc = W.c()
     _check(lib().kd_debug_block_dots(C.byref(wc), x.c(), B, S.data_ptr(), _stream(stream)), "kd_debug_block_dots")
     return S
+
+
+def kd_debug_moe_route(z: torch.Tensor, router: torch.Tensor, K: int, stream=None) -> Dict[str, torch.Tensor]:
+    """Routing of rows z [B, d] by router [E, d] (fp32 device tensors): ids, p, logits and the
+    expert buckets (count [E], rows / pairs [E, 16]) as the MoE layer computes them."""
+    B, d = z.shape
+    E = router.shape[0]
+    dev = z.device
+    out = {"ids": torch.empty((B, K), dtype=torch.int32, device=dev), "p": torch.empty((B, K), device=dev),
+           "logits": torch.empty((B, E), device=dev), "count": torch.empty(E, dtype=torch.int32, device=dev),
+           "rows": torch.full((E, 16), -1, dtype=torch.int32, device=dev),
+           "pairs": torch.full((E, 16), -1, dtype=torch.int32, device=dev)}
+    _check(lib().kd_debug_moe_route(z.data_ptr(), router.data_ptr(), B, d, E, K, out["ids"].data_ptr(),
+                                    out["p"].data_ptr(), out["logits"].data_ptr(), out["count"].data_ptr(),
+                                    out["rows"].data_ptr(), out["pairs"].data_ptr(), _stream(stream)),
+           "kd_debug_moe_route")
+    return out
+
+
+def kd_debug_mmvq_grouped(W: PackedWeight, n_groups: int, x: Act, act_rows: int, count: torch.Tensor,
+                          act_row: torch.Tensor, out_row: torch.Tensor, out_rows: int, swiglu: bool = False,
+                          stream=None):
+    """Grouped product over row buckets: W is group 0 of n_groups stacked groups of W.n_out
+    rows.  Returns fp32 rows [out_rows, W.n_out] (plain) or the quantised SwiGLU rows
+    (an Act of out_rows rows of F = W.n_out / 2)."""
+    wc = W.c()
+    dev = x.qs.device
+    if swiglu:
+        out = alloc_act(out_rows, W.n_out // 2, dev)
+        y, ldy, oc = None, 0, out.c()
+    else:
+        out = torch.zeros((out_rows, W.n_out), dtype=torch.float32, device=dev)
+        y, ldy, oc = out.data_ptr(), W.n_out, KdAct(None, None)
+    _check(lib().kd_debug_mmvq_grouped(C.byref(wc), n_groups, x.c(), act_rows, count.data_ptr(), act_row.data_ptr(),
+                                       out_row.data_ptr(), 1 if swiglu else 0, y, ldy, oc, _stream(stream)),
+           "kd_debug_mmvq_grouped")
+    return out
+
+
+def weight_group(W: PackedWeight, group: int, rows: int) -> PackedWeight:
+    """Rows [group * rows, (group + 1) * rows) of a packed matrix as a matrix of its own (rows
+    a multiple of 16: the group's tiles are one contiguous range)."""
+    assert rows % 16 == 0
+    tiles = (rows // 16) * ((W.k + 127) // 128)
+    per_qs = W.qs.numel() * W.qs.element_size() // (W.n_out // 16 * ((W.k + 127) // 128))
+    qs = W.qs.view(torch.uint8)[group * tiles * per_qs:(group + 1) * tiles * per_qs]
+    d = W.d[group * tiles * 64:(group + 1) * tiles * 64]
+    return PackedWeight(W.fmt, rows, W.k, qs, d)
+
+
+def act_rows_view(x: Act, r0: int, n: int) -> Act:
+    """Rows [r0, r0 + n) of a quantised activation buffer (the layout is row-contiguous)."""
+    NQ = (x.k + 127) // 128
+    return Act(x.qs[r0 * NQ * 128:(r0 + n) * NQ * 128], x.d[r0 * NQ * 4:(r0 + n) * NQ * 4], n, x.k)
 
 
 # ------------------------------------------------------------------------------ row ops
@@ -524,6 +587,42 @@ class KdModel:
                                   out.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream))
         _check(st, "kd_decode_step")
         return out
+
+    def kd_debug_decode_step_trace(self, x_in: torch.Tensor, pos: Sequence[int], k_base: Sequence[int],
+                                   v_base: Sequence[int], capacity: int, out: torch.Tensor, ws: torch.Tensor,
+                                   stream=None) -> Dict[str, torch.Tensor]:
+        """kd_decode_step that also returns the residual rows entering every layer and after
+        the last ([n_layers + 1, B, d]), for MoE layers each row's experts and weights, and the
+        int8 codes of every activation quantisation (tiled layout, rows of NQ(k) * 128 bytes)."""
+        sp = self.spec
+        B = x_in.shape[0]
+        dev = x_in.device
+        nq = lambda k: (k + 127) // 128 * 128
+        Lyr = sp.n_layers
+        rec = {"resid": torch.empty((Lyr + 1, B, sp.d), dtype=torch.float32, device=dev),
+               "q_attn_in": torch.zeros((Lyr, B, nq(sp.d)), dtype=torch.int8, device=dev),
+               "q_attn_out": torch.zeros((Lyr, B, nq(sp.n_head * sp.head_dim)), dtype=torch.int8, device=dev)}
+        if sp.ffn or sp.n_experts:
+            rec["q_ffn_in"] = torch.zeros((Lyr, B, nq(sp.d)), dtype=torch.int8, device=dev)
+        if sp.ffn:
+            rec["q_ffn_mid"] = torch.zeros((Lyr, B, nq(sp.ffn)), dtype=torch.int8, device=dev)
+        if sp.n_experts:
+            K = sp.n_expert_used
+            rec["q_ffn_mid"] = torch.zeros((Lyr, B * K, nq(sp.expert_ffn)), dtype=torch.int8, device=dev)
+            rec["q_shared_mid"] = torch.zeros((Lyr, B, nq(sp.shared_ffn)), dtype=torch.int8, device=dev)
+        if sp.vocab:
+            rec["q_head_in"] = torch.zeros((B, nq(sp.d)), dtype=torch.int8, device=dev)
+        tr = KdStepTrace(*[rec[k].data_ptr() if k in rec else None for k, _ in KdStepTrace._fields_])
+        if sp.n_experts:
+            rec["moe_ids"] = torch.full((Lyr, B, sp.n_expert_used), -1, dtype=torch.int32, device=dev)
+            rec["moe_p"] = torch.zeros((Lyr, B, sp.n_expert_used), dtype=torch.float32, device=dev)
+            tr.moe_ids, tr.moe_p = rec["moe_ids"].data_ptr(), rec["moe_p"].data_ptr()
+        st = lib().kd_debug_decode_step_trace(self.handle, B, x_in.data_ptr(), _i32(pos), _ptrs(k_base),
+                                              _ptrs(v_base), capacity, out.data_ptr(), ws.data_ptr(), ws.numel(),
+                                              C.byref(tr), _stream(stream))
+        _check(st, "kd_debug_decode_step_trace")
+        rec["out"] = out
+        return rec
 
 
 class SessionCaches:

@@ -893,3 +893,31 @@ extern "C" kd_status kd_debug_block_dots(const kd_weight* W, kd_act_q8 x, int32_
   launch_mmvq(*W, x.qs, x.d, B, nullptr, 0, as_stream(stream), nullptr, S);
   return check_launch("kd_debug_block_dots");
 }
+
+extern "C" kd_status kd_debug_mmvq_grouped(const kd_weight* W, int32_t n_groups, kd_act_q8 x, int32_t act_rows,
+                                           const int32_t* count, const int32_t* act_row, const int32_t* out_row,
+                                           int32_t swiglu, float* y, int32_t ldy, kd_act_q8 out, void* stream) {
+  const char* who = "kd_debug_mmvq_grouped";
+  KD_REQUIRE(W, KD_ERR_INVALID, "%s: null weight", who);
+  kd_status s = check_mmvq_args(who, W, W->fmt, x, 1);
+  if (s != KD_OK) return s;
+  KD_REQUIRE(fmt_quant(W->fmt), KD_ERR_UNSUPPORTED, "%s: format %d", who, W->fmt);
+  KD_REQUIRE(n_groups >= 1 && W->n_out % 16 == 0, KD_ERR_UNSUPPORTED,
+             "%s: n_groups=%d, rows per group %d (a multiple of 16)", who, n_groups, W->n_out);
+  KD_REQUIRE(mmvq_weight_fits(W->fmt, W->n_out * n_groups, W->k), KD_ERR_UNSUPPORTED, "%s: stacked matrix too large",
+             who);
+  KD_REQUIRE(act_rows >= 1 && act_rows <= KD_MAX_B * 16, KD_ERR_UNSUPPORTED, "%s: act_rows=%d", who, act_rows);
+  KD_REQUIRE(count && act_row && out_row, KD_ERR_INVALID, "%s: null row map", who);
+  RowMap map{count, act_row, out_row, n_groups, (long long)n_rowgroups(W->n_out) * n_quads(W->k), act_rows};
+  if (swiglu) {
+    KD_REQUIRE(W->n_out % 64 == 0, KD_ERR_UNSUPPORTED, "%s: SwiGLU rows per group %d is not 2F, F %% 32 == 0", who,
+               W->n_out);
+    KD_REQUIRE(out.qs && out.d && aligned16(out.qs) && aligned16(out.d), KD_ERR_INVALID,
+               "%s: output buffers null or not 16-byte aligned", who);
+    launch_mmvq_swiglu(*W, x.qs, x.d, 0, out.qs, out.d, as_stream(stream), nullptr, 0, 0.0f, &map);
+  } else {
+    KD_REQUIRE(y && ldy >= W->n_out, KD_ERR_INVALID, "%s: null output or ldy=%d < rows per group", who, ldy);
+    launch_mmvq(*W, x.qs, x.d, 0, y, ldy, as_stream(stream), &map);
+  }
+  return check_launch(who);
+}

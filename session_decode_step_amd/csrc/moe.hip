@@ -153,3 +153,19 @@ int moe_max_experts() { return kMaxExperts; }
 int moe_max_topk() { return kMaxTopK; }
 
 }  // namespace kd
+
+using namespace kd;
+
+extern "C" kd_status kd_debug_moe_route(const float* z, const float* router, int32_t B, int32_t d, int32_t E,
+                                        int32_t K, int32_t* ids, float* p, float* logits, int32_t* count,
+                                        int32_t* rows, int32_t* pairs, void* stream) {
+  const char* who = "kd_debug_moe_route";
+  KD_REQUIRE(B >= 1 && B <= KD_MAX_B, KD_ERR_UNSUPPORTED, "%s: B=%d outside [1,16]", who, B);
+  KD_REQUIRE(E >= 1 && E <= kMaxExperts && K >= 1 && K <= kMaxTopK && K <= E, KD_ERR_UNSUPPORTED,
+             "%s: E=%d K=%d (E <= %d, K <= min(E, %d))", who, E, K, kMaxExperts, kMaxTopK);
+  KD_REQUIRE(d > 0 && d % 4 == 0, KD_ERR_UNSUPPORTED, "%s: d=%d is not a positive multiple of 4", who, d);
+  KD_REQUIRE(z && router && ids && p && logits && count && rows && pairs, KD_ERR_INVALID, "%s: null pointer", who);
+  KD_REQUIRE(aligned16(z) && aligned16(router), KD_ERR_INVALID, "%s: z and router must be 16-byte aligned", who);
+  launch_router(z, router, B, d, E, K, ids, p, logits, count, rows, pairs, as_stream(stream));
+  return check_launch(who);
+}

@@ -262,9 +262,27 @@ extern "C" size_t kd_decode_step_workspace(const kd_model* m, int32_t B, const i
 // ---------------------------------------------------------------------------------------
 // The step
 // ---------------------------------------------------------------------------------------
-extern "C" kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x_in, const int32_t* pos,
-                                    void* const* k_base, void* const* v_base, int32_t capacity, float* out, void* ws,
-                                    size_t ws_bytes, void* stream) {
+namespace {
+// Device-to-device copy of n floats (or int32s) for the step record; false on failure.
+bool trace_copy(void* dst, const void* src, size_t bytes, hipStream_t st) {
+  if (hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, st) != hipSuccess) {
+    set_error("kd_debug_decode_step_trace: copy failed");
+    return false;
+  }
+  return true;
+}
+// Copy the codes of `rows` activation rows of length k (tiled layout) into record slot `slot`
+// of a per-layer code array (nothing if the array is not requested).
+bool trace_codes(int8_t* dst, size_t slot, const int8_t* src, int rows, int k, hipStream_t st) {
+  if (!dst) return true;
+  const size_t bytes = (size_t)rows * n_quads(k) * 128;
+  return trace_copy(dst + slot * bytes, src, bytes, st);
+}
+}  // namespace
+
+static kd_status decode_step_impl(const kd_model* m, int32_t B, const float* x_in, const int32_t* pos,
+                                  void* const* k_base, void* const* v_base, int32_t capacity, float* out, void* ws,
+                                  size_t ws_bytes, const kd_step_trace* tr, void* stream) {
   KD_REQUIRE(m, KD_ERR_INVALID, "kd_decode_step: null model");
   KD_REQUIRE(B >= 1 && B <= KD_MAX_B, KD_ERR_UNSUPPORTED, "kd_decode_step: B=%d outside [1,16]", B);
   KD_REQUIRE(x_in && pos && k_base && v_base && out, KD_ERR_INVALID, "kd_decode_step: null pointer");
@@ -337,6 +355,11 @@ extern "C" kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x
     } else {
       launch_norm_quant(base, nullptr, Ly.attn_norm, B, D, d.rms_eps, nullptr, nullptr, s.act_qs, s.act_d, st);
     }
+    // res now holds the residual rows entering the layer (written by the previous layer's
+    // epilogue or by the norm launch above)
+    if (tr && tr->resid && !trace_copy(tr->resid + (size_t)il * B * D, res, sizeof(float) * B * D, st))
+      return KD_ERR_HIP;
+    if (tr && !trace_codes(tr->q_attn_in, il, s.act_qs, B, D, st)) return KD_ERR_HIP;
     if (Ly.wqkv_pair_rows) {  // the product rotates q/k and appends k/v itself
       launch_mmvq_rope(Ly.wqkv, s.act_qs, s.act_d, B, s.qkv, ldqkv, H, G, hd, s.cs, d.rope_base, rc, capacity, st,
                        prenormed ? s.ss : nullptr, D, d.rms_eps, kv8);
@@ -364,12 +387,15 @@ extern "C" kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x
     } else {
       launch_fa(plan, s.qkv, ldqkv, rc, capacity, scale, s.attn, s.act_qs, s.act_d, s.fa_ws, st, gate, kv8);
     }
+    if (tr && !trace_codes(tr->q_attn_out, il, s.act_qs, B, H * hd, st)) return KD_ERR_HIP;
     if (norm_fusable(il)) {
       // O product + residual add + the FFN RMSNorm's quantiser and sums of squares; the
       // gate/up product applies 1/rms, SwiGLU and the quantiser for down
       float* x1 = (res == s.xa) ? s.xb : s.xa;
       launch_mmvq_resnorm(Ly.wo, s.act_qs, s.act_d, B, res, D, Ly.ffn_norm, x1, s.actn_qs, s.actn_d, s.ss, st);
+      if (tr && !trace_codes(tr->q_ffn_in, il, s.actn_qs, B, D, st)) return KD_ERR_HIP;
       launch_mmvq_swiglu(Ly.w_gate, s.actn_qs, s.actn_d, B, s.act2_qs, s.act2_d, st, s.ss, D, d.rms_eps);
+      if (tr && !trace_codes(tr->q_ffn_mid, il, s.act2_qs, B, d.ffn, st)) return KD_ERR_HIP;
       if (il + 1 < L && norm_fusable(il + 1) && m->layers[il + 1].wqkv_pair_rows) {
         // down product + residual add + the next layer's attention RMSNorm (its QKV input
         // goes to act, free once the O product has run)
@@ -396,6 +422,7 @@ extern "C" kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x
     }
     float* x1 = (res == s.xa) ? s.xb : s.xa;
     launch_norm_quant(res, s.o, Ly.ffn_norm, B, D, d.rms_eps, x1, moe ? s.z : nullptr, s.act_qs, s.act_d, st);
+    if (tr && !trace_codes(tr->q_ffn_in, il, s.act_qs, B, D, st)) return KD_ERR_HIP;
     if (!moe) {
       const int F = d.ffn;
       if (Ly.w_up.qs) {
@@ -405,10 +432,15 @@ extern "C" kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x
       } else {  // interleaved gate/up: one product, SwiGLU and quantiser in its epilogue
         launch_mmvq_swiglu(Ly.w_gate, s.act_qs, s.act_d, B, s.act2_qs, s.act2_d, st);
       }
+      if (tr && !trace_codes(tr->q_ffn_mid, il, s.act2_qs, B, F, st)) return KD_ERR_HIP;
       launch_mmvq(Ly.w_down, s.act2_qs, s.act2_d, B, s.f, D, st);
     } else {
       const int E = d.n_experts, K = d.n_expert_used, Fe = d.expert_ffn, Fs = d.shared_ffn;
       launch_router(s.z, Ly.router, B, D, E, K, s.ids, s.p, s.rlog, s.count, s.rows, s.pairs, st);
+      if (tr && tr->moe_ids && !trace_copy(tr->moe_ids + (size_t)il * B * K, s.ids, sizeof(int32_t) * B * K, st))
+        return KD_ERR_HIP;
+      if (tr && tr->moe_p && !trace_copy(tr->moe_p + (size_t)il * B * K, s.p, sizeof(float) * B * K, st))
+        return KD_ERR_HIP;
       kd_weight eg = Ly.e_gate, eu = Ly.e_up, ed = Ly.e_down;
       ed.n_out = D;
       RowMap dn_map{s.count, s.pairs, s.pairs, E, (long long)n_rowgroups(D) * n_quads(Fe), B * K};
@@ -419,6 +451,8 @@ extern "C" kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x
         RowMap gu_map{s.count, s.rows, s.pairs, E, (long long)n_rowgroups(2 * Fe) * n_quads(D), B};
         launch_mmvq_swiglu(eg, s.act_qs, s.act_d, 0, s.hq_qs, s.hq_d, st, nullptr, 0, 0.0f, &gu_map);
         launch_mmvq_swiglu(Ly.s_gate, s.act_qs, s.act_d, B, s.shq_qs, s.shq_d, st);
+        if (tr && !trace_codes(tr->q_ffn_mid, il, s.hq_qs, B * K, Fe, st)) return KD_ERR_HIP;
+        if (tr && !trace_codes(tr->q_shared_mid, il, s.shq_qs, B, Fs, st)) return KD_ERR_HIP;
         launch_mmvq(ed, s.hq_qs, s.hq_d, 0, s.yp, D, st, &dn_map);
         launch_mmvq(Ly.s_down, s.shq_qs, s.shq_d, B, s.sh, D, st);
       } else {
@@ -431,8 +465,10 @@ extern "C" kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x
         launch_mmvq(Ly.s_gate, s.act_qs, s.act_d, B, s.sgu, 2 * Fs, st);
         launch_mmvq(Ly.s_up, s.act_qs, s.act_d, B, s.sgu + Fs, 2 * Fs, st);
         launch_swiglu_quant(s.gup, s.gup + Fe, B * K, Fe, 2 * Fe, nullptr, s.hq_qs, s.hq_d, st);
+        if (tr && !trace_codes(tr->q_ffn_mid, il, s.hq_qs, B * K, Fe, st)) return KD_ERR_HIP;
         launch_mmvq(ed, s.hq_qs, s.hq_d, 0, s.yp, D, st, &dn_map);
         launch_swiglu_quant(s.sgu, s.sgu + Fs, B, Fs, 2 * Fs, nullptr, s.act_qs, s.act_d, st);
+        if (tr && !trace_codes(tr->q_shared_mid, il, s.act_qs, B, Fs, st)) return KD_ERR_HIP;
         launch_mmvq(Ly.s_down, s.act_qs, s.act_d, B, s.sh, D, st);
       }
       launch_moe_combine(s.yp, s.p, s.sh, B, K, D, s.f, st);
@@ -440,9 +476,17 @@ extern "C" kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x
     base = x1;
     add = s.f;
   }
+  if (tr && tr->resid) {  // the residual rows after the last layer
+    float* last = tr->resid + (size_t)L * B * D;
+    if (add)
+      launch_add(base, add, last, (size_t)B * D, st);
+    else if (!trace_copy(last, base, sizeof(float) * B * D, st))
+      return KD_ERR_HIP;
+  }
   // output: [residual add +] final norm [+ quantise + lm_head]
   if (d.vocab > 0) {
     launch_norm_quant(base, add, d.final_norm, B, D, d.rms_eps, nullptr, nullptr, s.act_qs, s.act_d, st);
+    if (tr && !trace_codes(tr->q_head_in, 0, s.act_qs, B, D, st)) return KD_ERR_HIP;
     launch_mmvq(d.lm_head, s.act_qs, s.act_d, B, out, d.vocab, st);
   } else if (d.final_norm) {
     launch_norm_quant(base, add, d.final_norm, B, D, d.rms_eps, nullptr, out, nullptr, nullptr, st);
@@ -455,4 +499,18 @@ extern "C" kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x
     }
   }
   return check_launch("kd_decode_step");
+}
+
+extern "C" kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x_in, const int32_t* pos,
+                                    void* const* k_base, void* const* v_base, int32_t capacity, float* out, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  return decode_step_impl(m, B, x_in, pos, k_base, v_base, capacity, out, ws, ws_bytes, nullptr, stream);
+}
+
+extern "C" kd_status kd_debug_decode_step_trace(const kd_model* m, int32_t B, const float* x_in, const int32_t* pos,
+                                                void* const* k_base, void* const* v_base, int32_t capacity,
+                                                float* out, void* ws, size_t ws_bytes, const kd_step_trace* trace,
+                                                void* stream) {
+  KD_REQUIRE(trace, KD_ERR_INVALID, "kd_debug_decode_step_trace: null trace");
+  return decode_step_impl(m, B, x_in, pos, k_base, v_base, capacity, out, ws, ws_bytes, trace, stream);
 }

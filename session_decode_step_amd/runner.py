@@ -94,3 +94,16 @@ class GpuWorkload:
             out = self.out if len(rows) == wl.B else torch.empty((len(rows), wl.spec.out_dim), dtype=torch.float32,
                                                                  device=self.device)
         return self.km.kd_decode_step(x, pos, kb, vb, wl.capacity, out, self.ws, stream)
+
+    def step_trace(self, s: int, rows: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
+        """Decode step ``s`` through kd_debug_decode_step_trace: the output and the per-layer
+        record (residual rows entering each layer and after the last; MoE routing), on the host."""
+        wl = self.wl
+        rows = list(range(wl.B)) if rows is None else list(rows)
+        x = self._rows_input(s, rows)
+        pos_all = wl.positions(s)
+        pos = [pos_all[b] for b in rows]
+        kb, vb = self.caches.tables([wl.rows[b][0] for b in rows])
+        out = torch.empty((len(rows), wl.spec.out_dim), dtype=torch.float32, device=self.device)
+        rec = self.km.kd_debug_decode_step_trace(x, pos, kb, vb, wl.capacity, out, self.ws)
+        return {k: v.cpu().numpy() for k, v in rec.items()}

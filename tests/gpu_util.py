@@ -33,6 +33,18 @@ def untile_act(qs: torch.Tensor, d: torch.Tensor, B: int, k: int):
     return codes.reshape(B, NQ * 128)[:, :k], sc[:, : k // 32], codes[:, k // 32:], sc[:, k // 32:]
 
 
+def untile_codes(qs: np.ndarray, k: int) -> np.ndarray:
+    """int8 codes [R, k] of R activation rows in the tiled layout (rows of NQ * 128 bytes)."""
+    NQ = math.ceil(k / 128)
+    R = qs.shape[0]
+    a = np.asarray(qs).reshape(R, NQ, 4, 4, 8)                       # [r][q][g][j][e]
+    codes = np.zeros((R, NQ * 4, 32), dtype=np.int8)
+    for g in range(4):
+        for e in range(8):
+            codes[:, :, P[g, e]] = a[:, :, g, :, e].reshape(R, NQ * 4)
+    return codes.reshape(R, NQ * 128)[:, :k]
+
+
 def row_errors(gpu, ref):
     """(normwise, elementwise) relative errors per row: ||g - r||_2 / ||r||_2 and
     max_i |g_i - r_i| / max(|r_i|, rms(r))."""

@@ -274,3 +274,37 @@ def test_gdn_step_validates_before_launch():
     cross = (C.c_void_p * 2)(0x2000, 0x4000)                 # row 0 writes what row 1 reads
     assert L.kd_gdn_step(*args, 2, 4, 128, si, cross, 0.1, 0x600, None) == kd.KD_ERR_INVALID
     assert L.kd_gdn_step(0, *args[1:], 2, 4, 128, si, so, 0.1, 0x600, None) == kd.KD_ERR_INVALID
+
+
+def test_products_reject_shapes_past_their_limits():
+    """k beyond 16384 (the widest wave partition) and matrices whose tiled codes would reach
+    2 GiB (past the buffer offsets' masking value) are refused before any launch, by the
+    product entry points and by kd_model_create."""
+    L = kd.lib()
+    act = kd.KdAct(0x3000, 0x4000)
+    ok = kd.KdWeight(kd.KD_FMT_Q4_0, 64, 16384, 0x1000, 0x2000)
+    wide = kd.KdWeight(kd.KD_FMT_Q4_0, 64, 16384 + 32, 0x1000, 0x2000)
+    assert L.kd_mmvq_q4_0(C.byref(wide), act, 2, 0x5000, 64, None) == kd.KD_ERR_UNSUPPORTED
+    assert b"16384" in L.kd_last_error()
+    assert L.kd_mmvq_swiglu(C.byref(kd.KdWeight(kd.KD_FMT_Q4_0, 64, 28672, 0x1000, 0x2000)), act, 2,
+                            kd.KdAct(0x6000, 0x7000), None) == kd.KD_ERR_UNSUPPORTED
+    assert L.kd_debug_block_dots(C.byref(wide), act, 2, 0x5000, None) == kd.KD_ERR_UNSUPPORTED
+    # 2^31 bytes of Q8_0 tiles: 2^20 tiles of 2048 B, e.g. 131072 rows x 16384 columns (8192 x 128 tiles)
+    assert L.kd_weight_qs_bytes(kd.KD_FMT_Q8_0, 131072, 16384) == 1 << 31
+    big = kd.KdWeight(kd.KD_FMT_Q8_0, 131072, 16384, 0x1000, 0x2000)
+    assert L.kd_mmvq_q8_0(C.byref(big), act, 2, 0x5000, 131072, None) == kd.KD_ERR_UNSUPPORTED
+    assert b"2 GiB" in L.kd_last_error()
+    # one row group less fits (the call then proceeds to the output checks: ldy too small)
+    just = kd.KdWeight(kd.KD_FMT_Q8_0, 131072 - 16, 16384, 0x1000, 0x2000)
+    assert L.kd_weight_qs_bytes(kd.KD_FMT_Q8_0, 131072 - 16, 16384) < 1 << 31
+    assert L.kd_mmvq_q8_0(C.byref(just), act, 2, 0x5000, 16, None) == kd.KD_ERR_INVALID
+    assert b"ldy" in L.kd_last_error()
+    # ... and the same shapes inside a model: an FFN of 28672 (down product k = 28672)
+    desc, layers = _fake_model(F=28672)
+    h = C.c_void_p()
+    assert L.kd_model_create(C.byref(desc), C.byref(h)) == kd.KD_ERR_UNSUPPORTED
+    assert b"w_down" in L.kd_last_error() or b"w_gate" in L.kd_last_error()
+    desc, layers = _fake_model(F=16384)
+    assert L.kd_model_create(C.byref(desc), C.byref(h)) == kd.KD_OK
+    L.kd_model_destroy(h)
+    del ok, just

@@ -314,11 +314,12 @@ def test_c3_ragged_attention_b16():
 
 
 def test_c4_q4_32_layers_b8():
-    """32-layer d=4096 Q4_0 at B = 8, ctx 4096: oracle on one row, bit identity on all rows."""
+    """32-layer d=4096 Q4_0 at B = 8, ctx 4096: oracle on two rows end to end at the stated
+    2e-3 bar (the whole 32-layer chain; no code flip cascades here), bit identity on all rows."""
     say("c4 B=8")
     wl = W.workload("c4", B=8, steps=1)
     gw = GpuWorkload(wl)
-    y = _oracle_follow(gw, [5], [0])[0]
+    y = _oracle_follow(gw, [0, 5], [0], bars=SHALLOW)[0]
     _bit_identity(gw, range(8), 0, y)
 
 
@@ -334,31 +335,34 @@ def test_c4_every_width_is_row_identical():
 
 
 def test_c5_moe_verify_rows():
-    """MoE stack, 4 streams x 4 draft rows at ctx 8192: oracle on streams 0 and 1; rows equal
-    the stream alone (B = 4) and the drafts stepped one by one (B = 1)."""
+    """MoE stack, 4 streams x 4 draft rows at ctx 8192: the oracle follows all four streams end
+    to end (the cascade-level check; tests/test_gpu_layers.py holds every layer to 2e-3 with
+    exact routing), and rows equal the stream alone (B = 4) and the drafts stepped one by one
+    (B = 1)."""
     say("c5")
     wl = W.workload("c5")
     gw = GpuWorkload(wl)
     info = {}
     x = W.step_inputs(wl, 0)
-    y = gw.step(0).cpu().numpy().copy()
-    oc = oracle.OracleCaches(wl, sessions=[0, 1])
-    ref = oracle.decode_step(gw.model, oc, x[:8], [0] * 4 + [1] * 4, wl.positions(0)[:8], info=info)
-    # A row whose 8th and 9th router logits are within 1e-3 (relative) may take the other
-    # expert on the GPU (a swap changes the row by ~1/8 of an expert output): such rows are
-    # reported and held only to the bit-identity checks below.
-    near = set()
-    for il in info:
-        for b, (gap, kth) in enumerate(zip(info[il]["gap"], info[il]["kth"])):
-            if gap < 1e-3 * kth:
-                near.add(b)
-    keep = [b for b in range(8) if b not in near]
-    say(f"  near-tie rows {sorted(near)}; oracle-checked rows {keep}")
-    assert len(keep) >= 4, "too few rows without a near-tie router decision to check"
-    assert_close_rows(y[keep], ref[keep], DEEP[0], "c5 streams 0-1", elem_rel=DEEP[1])
+    rec = gw.step_trace(0)
+    y = rec["out"].copy()
+    oc = oracle.OracleCaches(wl)
+    ref = oracle.decode_step(gw.model, oc, x, [s for s, _ in wl.rows], wl.positions(0), info=info)
+    # End to end the oracle's fp64 routing can differ from the GPU's fp32 one where a row's
+    # 8th and 9th logits nearly tie after the layers below have drifted: such a row takes
+    # another expert (~1/8 of an expert output).  Rows routed alike in every layer are held to
+    # the deep bar; the others are reported (the per-layer test checks routing exactly).
+    same = [b for b in range(wl.B)
+            if all(np.array_equal(rec["moe_ids"][il][b], info[il]["ids"][b]) for il in range(wl.spec.n_layers))]
+    say(f"  rows routed alike in every layer: {same} of {wl.B}")
+    assert len(same) >= wl.B // 2
+    assert_close_rows(y[same], ref[same], DEEP[0], "c5 all streams", elem_rel=DEEP[1])
     # stream 2 alone (B = 4) and its drafts one by one (B = 1)
     y4 = gw.step(0, rows=[8, 9, 10, 11]).cpu().numpy()
     np.testing.assert_array_equal(y4.view(np.uint32), y[8:12].view(np.uint32))
     for j in range(4):
         y1 = gw.step(0, rows=[8 + j]).cpu().numpy()
         np.testing.assert_array_equal(y1[0].view(np.uint32), y[8 + j].view(np.uint32))
+    # the recorded step is the plain step
+    y_plain = gw.step(0).cpu().numpy()
+    np.testing.assert_array_equal(y_plain.view(np.uint32), y.view(np.uint32))

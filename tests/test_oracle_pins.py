@@ -505,6 +505,63 @@ def test_output_gate_closed_head_removes_that_head():
     assert np.abs(yo - yg).max() > 1e-3
 
 
+def test_forced_codes_accept_exactly_the_valid_roundings():
+    """Teacher forcing of the quantiser: the oracle's own codes change nothing (no flip, no
+    invalid code, the same step output); a code one step off where the value is far from a
+    rounding boundary is counted invalid; at a value within the tolerance of a boundary both
+    neighbouring codes are accepted, the other one counted as a flip."""
+    from oracle.step import _q_forced
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((2, 64))
+    q0, d0 = ops.quantize_act(x.astype(np.float32))
+    rec = []
+    q, d = _q_forced(x, q0, rec, "own")
+    assert np.array_equal(q, q0) and np.array_equal(d, d0)
+    assert rec[-1]["flips"] == 0 and rec[-1]["invalid"] == 0
+    # one code one step off, away from a boundary
+    ratio = x.astype(np.float32)[0, :32] / d0[0, 0]
+    i = int(np.argmin(np.abs(ratio - np.round(ratio))))          # closest to an integer: mid-cell
+    bad = q0.astype(np.int64).copy()
+    bad[0, i] += 1 if bad[0, i] < 127 else -1
+    _q_forced(x, bad, rec, "bad")
+    assert rec[-1]["invalid"] == 1
+    # a value on a boundary: block amax 127 d, and an element at (k + 1/2) d exactly
+    xb = np.zeros((1, 32))
+    xb[0, 0] = 127.0
+    xb[0, 1] = 10.5
+    qb, _ = ops.quantize_act(xb.astype(np.float32))
+    assert qb[0, 1] == 11                                        # half away from zero
+    alt = qb.astype(np.int64).copy()
+    alt[0, 1] = 10
+    _q_forced(xb, alt, rec, "tie")
+    assert rec[-1]["invalid"] == 0 and rec[-1]["flips"] == 1
+    alt[0, 1] = 12
+    _q_forced(xb, alt, rec, "two off")
+    assert rec[-1]["invalid"] == 1
+    # a whole layer forced with its own codes equals the unforced layer
+    wl = _tiny_wl(TINY, 97, [(0, 0), (1, 0)], [9, 30])
+    model = wlmod.make_model(TINY, 97)
+    xin = wlmod.step_inputs(wl, 0).astype(np.float64)
+    tr = []
+    y = oracle.decode_layer(model, 0, oracle.OracleCaches(wl), xin, [0, 1], wl.positions(0), trace=tr)
+    L = model["layers"][0]
+    xn = ops.rmsnorm(xin, L["attn_norm"], TINY.rms_eps)
+    attn = tr[0]["attn"].reshape(2, -1)
+    z = ops.rmsnorm(tr[0]["x1"], L["ffn_norm"], TINY.rms_eps)
+    zq, zd = ops.quantize_act(z.astype(np.float32))
+    g = ops.mmvq(L["w_gate"], zq, zd)
+    u = ops.mmvq(L["w_up"], zq, zd)
+    forced = {"attn_in": ops.quantize_act(xn.astype(np.float32))[0],
+              "attn_out": ops.quantize_act(attn.astype(np.float32))[0], "ffn_in": zq,
+              "ffn_mid": ops.quantize_act(ops.swiglu(g, u).astype(np.float32))[0]}
+    rec = []
+    yf = oracle.decode_layer(model, 0, oracle.OracleCaches(wl), xin, [0, 1], wl.positions(0), forced=forced,
+                             record=rec)
+    np.testing.assert_array_equal(yf, y)
+    assert [r["what"] for r in rec] == ["attn in", "attn out", "ffn in", "ffn mid"]
+    assert all(r["flips"] == 0 and r["invalid"] == 0 for r in rec)
+
+
 def test_verify_rows_equal_sequential_steps():
     # A stream's 4 draft rows in one step (append all, then attend) equal 4 sequential
     # single-row steps at positions L..L+3 (Strata #1524 "Fresh validation": solo and batch
