@@ -7,16 +7,26 @@ the metric "aggregate decode tok/s at B=1..16" is quoted.  A step is one kd_deco
 B rows (all 32 layers + final norm).  K timed steps run at positions 4096..4096+K-1 after W
 warm-up steps (the same positions are re-written, so caches hold the same bytes each pass).
 
-Prints ONE JSON line: aggregate decode tok/s at B=8 (``value``), the B=1..16 sweep, step HBM
-GB/s, the roofline of the dominant kernel (fa_decode at B=8) and of the largest product (the
-gate/up mmvq, 28672 x 4096 Q4_0 at B=8), both timed with HIP events on the launch stream, the
-other workloads of the path (``other_workloads``: the 8-layer Q8_0 stack with lm_head at
-B=1..8, the ragged B=16 attention sublayer and its fa_decode, the MoE verify step, the
-headline stack with FP8 E4M3 caches and its fa_decode, the gated delta-rule state step), and the
-CPU oracle timed on a bounded sample beside it.
+Prints ONE JSON line with:
+* ``value``: aggregate decode tok/s at B=8, and the B=1..16 sweep with step HBM GB/s;
+* ``roofline``: fa_decode (the dominant kernel: split + combine) at B=8 rows of 4113 keys,
+  timed with HIP events on the launch stream, its PMC traffic, and the plain read of the same
+  bytes (kd_debug_read_stream) as the practical ceiling;
+* ``products``: each product of the stack at B=8 with its fused epilogue (QKV + RoPE +
+  append, O + residual + norm codes, gate/up + SwiGLU, down + residual + norm codes) and the
+  8-layer Q8_0 stack's lm_head, each with algorithmic bytes, GB/s, PMC traffic and the plain
+  read of its weight bytes (``mmvq_roofline`` repeats gate/up, the largest);
+* ``other_workloads``: the 8-layer Q8_0 stack with lm_head at B=1..8, the ragged B=16
+  attention sublayer and its fa_decode, the MoE verify step (with its bytes counted over the
+  distinct experts its rows hit), the headline stack with FP8 E4M3 caches and its fa_decode,
+  the gated delta-rule state step;
+* ``cpu_baseline`` (the 32-layer stack at B=8) and ``cpu_baseline_configs`` (all five
+  workloads at their headline widths): the oracle on the host cores, bounded samples;
+* ``platform``: GPU name, ROCm and HIP versions.
 
-``--summarize-trace CSV`` instead prints per-(kernel, grid) average durations from a
-rocprofv3 kernel-trace CSV (the profiles/ summaries are made with it).
+``--summarize-trace CSV`` prints per-(kernel, grid) average durations from a rocprofv3
+kernel-trace CSV; ``--traffic-probe`` makes the launches of the two PMC passes and
+``--traffic-summarize FETCH WRITE`` turns them into the profiles/traffic_*.txt records.
 """
 from __future__ import annotations
 
@@ -97,14 +107,6 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def mmvq_algorithmic_bytes(n: int, k: int, B: int) -> int:
-    """The interleaved gate/up product with its SwiGLU epilogue: Q4_0 weights once (18 B per
-    32), B int8 activation rows of k with fp32 block scales in, B quantised rows of F = n/2
-    (int8 codes + fp32 block scales) out."""
-    F = n // 2
-    return n * k * 18 // 32 + B * k + B * (k // 32) * 4 + B * F + B * (F // 32) * 4
-
-
 def time_rotating(launch, iters: int, stream) -> float:
     """Average launch duration (us) of ``launch(i)`` over ``iters`` launches, HIP events on
     ``stream`` (the stream the launches go to), after a few untimed ones."""
@@ -121,10 +123,44 @@ def time_rotating(launch, iters: int, stream) -> float:
     return e0.elapsed_time(e1) * 1e3 / iters
 
 
-# ---------------------------------------------------------------------- HBM traffic (PMC)
-CALIB_BYTES = 512 << 20
-FA_B, FA_T, FA_CAP = 8, 4113, 4128          # fa_decode traffic case: B rows of t keys
-MM_N, MM_K, MM_B = 28672, 4096, 8           # gate/up product traffic case
+# ---------------------------------------------------------------------- algorithmic bytes
+# The 32-layer Q4_0 stack's products at the headline width, with their fused epilogues, and
+# the 8-layer Q8_0 stack's lm_head: what each launch must move (weights once, activations in,
+# the epilogue's reads and writes), per launch.
+FA_B, FA_T = 8, 4113      # fa_decode roofline case: B rows of t keys (ctx 4096 + 16 decode steps + 1)
+PB = 8                    # product roofline width
+D4, H4, G4, HD4, F4 = 4096, 32, 8, 128, 14336
+
+
+def act_bytes(B: int, k: int) -> int:
+    """B quantised activation rows of length k: int8 codes and fp32 block scales."""
+    return B * k + B * (k // 32) * 4
+
+
+def w_bytes(fmt: str, n: int, k: int) -> int:
+    return n * k * (34 if fmt == "q8_0" else 18) // 32
+
+
+PRODUCTS = {
+    # kind: (title, fmt, n, k, epilogue bytes beyond the weights and the activation rows in)
+    "qkv": ("QKV product + 1/rms + RoPE + fp16 K/V append (kd_mmvq_rope_normed), 6144x4096 Q4_0", "q4_0",
+            (H4 + 2 * G4) * HD4, D4,
+            lambda B: B * (D4 // 32) * 4 + B * H4 * HD4 * 4 + B * G4 * HD4 * 2 * 2),
+    "o": ("O product + residual + FFN-norm codes and block sums (kd_mmvq_resnorm), 4096x4096 Q4_0", "q4_0",
+          D4, H4 * HD4, lambda B: 3 * B * D4 * 4 + D4 * 4 + act_bytes(B, D4) + B * (D4 // 32) * 4),
+    "gateup": ("gate/up product + 1/rms + SwiGLU + quantiser (kd_mmvq_swiglu_normed), 28672x4096 Q4_0", "q4_0",
+               2 * F4, D4, lambda B: B * (D4 // 32) * 4 + act_bytes(B, F4)),
+    "down": ("down product + residual + next attention-norm codes and block sums (kd_mmvq_resnorm), "
+             "4096x14336 Q4_0", "q4_0", D4, F4,
+             lambda B: 3 * B * D4 * 4 + D4 * 4 + act_bytes(B, D4) + B * (D4 // 32) * 4),
+    "lm_head": ("lm_head product of the 8-layer stack (kd_mmvq_q8_0), 32000x2048 Q8_0", "q8_0", 32000, 2048,
+                lambda B: B * 32000 * 4),
+}
+
+
+def product_bytes(kind: str, B: int) -> int:
+    _, fmt, n, k, epi = PRODUCTS[kind]
+    return w_bytes(fmt, n, k) + act_bytes(B, k) + epi(B)
 
 
 def fa_algorithmic_bytes(t_kv, G: int, H: int, hd: int, kv_bytes: int = 2) -> int:
@@ -133,61 +169,139 @@ def fa_algorithmic_bytes(t_kv, G: int, H: int, hd: int, kv_bytes: int = 2) -> in
     return sum(t_kv) * G * hd * kv_bytes * 2 + 2 * len(t_kv) * H * hd * 4
 
 
-TRAFFIC = {
-    "fa": {"file": os.path.join(ROOT, "profiles", "traffic_fa_decode_b8_t4113.txt"),
-           "sources": ("session_decode_step_amd/csrc/attn.hip", "session_decode_step_amd/csrc/kd_internal.h"),
-           "kernels": ("fa_split_kernel", "fa_combine_kernel"),
-           "title": "fa_decode (fa_split_kernel + fa_combine_kernel), B=8 rows of t=4113 keys, H=32, G=8, hd=128",
-           "algorithmic": lambda: fa_algorithmic_bytes([FA_T] * FA_B, 8, 32, 128)},
-    "mmvq": {"file": os.path.join(ROOT, "profiles", "traffic_mmvq_q4_0_28672x4096_b8.txt"),
-             "sources": ("session_decode_step_amd/csrc/mmvq.hip", "session_decode_step_amd/csrc/kd_internal.h"),
-             "kernels": ("mmvq_kernel",),
-             "title": "mmvq_kernel<Q4_0> with the SwiGLU epilogue, gate/up 28672 x 4096, B=8",
-             "algorithmic": lambda: mmvq_algorithmic_bytes(MM_N, MM_K, MM_B)},
-}
+# ---------------------------------------------------------------------- HBM traffic (PMC)
+CALIB_BYTES = 512 << 20
+MM_SRC = ("session_decode_step_amd/csrc/mmvq.hip", "session_decode_step_amd/csrc/kd_internal.h")
+FA_SRC = ("session_decode_step_amd/csrc/attn.hip", "session_decode_step_amd/csrc/kd_internal.h")
+# in the order the probe launches them: (kind, profile file stem, sources, kernels per call)
+TRAFFIC_ORDER = [
+    ("fa", "traffic_fa_decode_b8_t4113", FA_SRC, ("fa_split_kernel", "fa_combine_kernel")),
+    ("qkv", "traffic_mmvq_qkv_rope_q4_0_6144x4096_b8", MM_SRC, ("mmvq_kernel",)),
+    ("o", "traffic_mmvq_o_resnorm_q4_0_4096x4096_b8", MM_SRC, ("mmvq_kernel",)),
+    ("gateup", "traffic_mmvq_gateup_swiglu_q4_0_28672x4096_b8", MM_SRC, ("mmvq_kernel",)),
+    ("down", "traffic_mmvq_down_resnorm_q4_0_4096x14336_b8", MM_SRC, ("mmvq_kernel",)),
+    ("lm_head", "traffic_mmvq_lm_head_q8_0_32000x2048_b8", MM_SRC, ("mmvq_kernel",)),
+]
+PROBE_CALLS = 8
+
+
+def _traffic_spec(kind):
+    for k, stem, src, kernels in TRAFFIC_ORDER:
+        if k == kind:
+            return stem, src, kernels
+    raise KeyError(kind)
+
+
+def _traffic_title_bytes(kind):
+    if kind == "fa":
+        return (f"fa_decode (fa_split_kernel + fa_combine_kernel), B={FA_B} rows of t={FA_T} keys, H=32, G=8, hd=128",
+                fa_algorithmic_bytes([FA_T] * FA_B, G4, H4, HD4))
+    return f"mmvq_kernel: {PRODUCTS[kind][0]}, B={PB}", product_bytes(kind, PB)
 
 
 def kernel_source_hash(kind: str) -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in TRAFFIC[kind]["sources"]:
+    for f in _traffic_spec(kind)[1]:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
+class ProductRig:
+    """Device inputs of the measured products at width B: each product's activation rows,
+    the split-RMSNorm sums, residual rows, gains and output buffers (everything a launch
+    reads or writes besides its matrix)."""
+
+    def __init__(self, B: int, caches_k, caches_v, pos: int, capacity: int):
+        import torch
+        import session_decode_step_amd as kd
+        g = torch.Generator(device="cuda").manual_seed(7)
+        self.B = B
+        self.x_d = kd.kd_quantize_act_q8(torch.randn((B, D4), device="cuda", generator=g))
+        self.x_f = kd.kd_quantize_act_q8(torch.randn((B, F4), device="cuda", generator=g))
+        self.x_lm = kd.kd_quantize_act_q8(torch.randn((B, 2048), device="cuda", generator=g))
+        self.res = torch.randn((B, D4), device="cuda", generator=g)
+        self.gain = 1 + 0.1 * torch.randn(D4, device="cuda", generator=g)
+        self.x1 = torch.empty_like(self.res)
+        self.out_d = kd.alloc_act(B, D4)
+        self.ss = (self.res * self.res).view(B, D4 // 32, 32).sum(2).contiguous()
+        self.h = kd.alloc_act(B, F4)
+        self.q = torch.empty((B, H4 * HD4), device="cuda")
+        self.y_lm = torch.empty((B, 32000), device="cuda")
+        self.kb, self.vb, self.pos, self.cap = caches_k, caches_v, [pos] * B, capacity
+
+    def launch(self, kind: str, W, stream=None):
+        import session_decode_step_amd as kd
+        B = self.B
+        if kind == "qkv":
+            kd.kd_mmvq_rope_normed(W, self.x_d, B, self.ss, 1e-5, H4, G4, HD4, self.q, self.kb, self.vb, self.pos,
+                                   self.cap, 10000.0, stream=stream)
+        elif kind == "o":
+            kd.kd_mmvq_resnorm(W, self.x_d, B, self.res, self.gain, self.x1, self.out_d, self.ss, stream=stream)
+        elif kind == "gateup":
+            kd.kd_mmvq_swiglu_normed(W, self.x_d, B, self.ss, 1e-5, self.h, stream=stream)
+        elif kind == "down":
+            kd.kd_mmvq_resnorm(W, self.x_f, B, self.res, self.gain, self.x1, self.out_d, self.ss, stream=stream)
+        else:
+            kd.kd_mmvq_q8_0(W, self.x_lm, B, self.y_lm, stream=stream)
+
+
+def lm_head_copies(n: int = 4):
+    """n independently drawn 32000x2048 Q8_0 matrices (more than the 256 MB Infinity Cache
+    holds together), packed: the lm_head launches rotate over them."""
+    import workload as W
+    import session_decode_step_amd as kd
+    return [kd.kd_pack_weight(W.draw_weight("q8_0", 0, 2, 27, 28, 100 + i, 32000, 2048)) for i in range(n)]
+
+
+def stack_products(gw):
+    """The 32-layer stack's own packed matrices per product kind (one per layer)."""
+    L = gw.wl.spec.n_layers
+    return {"qkv": [gw.km.packed[il]["wqkv"] for il in range(L)], "o": [gw.km.packed[il]["wo"] for il in range(L)],
+            "gateup": [gw.km.packed[il]["w_gateup"] for il in range(L)],
+            "down": [gw.km.packed[il]["w_down"] for il in range(L)]}
+
+
 def traffic_probe() -> None:
-    """Launches for the two ``rocprofv3 --pmc`` passes: a plain fp32 elementwise copy of
-    512 MiB (the calibration kernel: reads and writes 512 MiB), then 8 launches of the gate/up
-    mmvq with its SwiGLU epilogue at B=8 over four distinct matrices, then 8 fa_decode calls
-    at B=8 over two distinct sets of caches."""
+    """Launches for the two ``rocprofv3 --pmc`` passes: every input is prepared first; then a
+    plain fp32 elementwise copy of 512 MiB (the calibration kernel: reads and writes 512 MiB),
+    then, in TRAFFIC_ORDER, 8 fa_decode calls at B=8 (t=4113) over four layers' caches and 8
+    launches of each product at B=8 over four layers' matrices (the lm_head over four drawn
+    matrices)."""
+    import dataclasses
     import torch
     import workload as W
     import session_decode_step_amd as kd
+    from session_decode_step_amd.runner import GpuWorkload
     torch.cuda.set_device(0)
+    base = W.workload("c4", B=FA_B, steps=32)
+    wl = dataclasses.replace(base, spec=dataclasses.replace(base.spec, n_layers=4))
+    gw = GpuWorkload(wl, fill="device")
+    mats = stack_products(gw)
+    mats["lm_head"] = lm_head_copies(4)
+    rig = ProductRig(PB, [gw.caches.k_ptr(s, 0) for s in range(PB)], [gw.caches.v_ptr(s, 0) for s in range(PB)],
+                     wl.capacity - 1, wl.capacity)
+    t_kv = [FA_T] * FA_B
+    q = torch.randn((FA_B, H4, HD4), device="cuda")
+    ws = torch.empty(kd.kd_fa_decode_workspace(FA_B, H4, HD4, t_kv), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    kbl = [[gw.caches.k_ptr(s, il) for s in range(FA_B)] for il in range(4)]
+    vbl = [[gw.caches.v_ptr(s, il) for s in range(FA_B)] for il in range(4)]
     src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
+    torch.cuda.synchronize()
     for _ in range(2):
         torch.mul(src, 1.0, out=dst)
     torch.cuda.synchronize()
     del src, dst
-    mats = [kd.kd_pack_weight(W.draw_weight("q4_0", 0, 4, 90, 91, i, MM_N, MM_K)) for i in range(4)]
-    act = kd.kd_quantize_act_q8(torch.randn((MM_B, MM_K), device="cuda"))
-    h_act = kd.alloc_act(MM_B, MM_N // 2)
-    for i in range(8):
-        kd.kd_mmvq_swiglu(mats[i % 4], act, MM_B, h_act)
-    torch.cuda.synchronize()
-    H, G, hd = 32, 8, 128
-    sets = [torch.empty((FA_B, 2, G, FA_CAP, hd), dtype=torch.float16, device="cuda").fill_(0.01) for _ in range(2)]
-    t_kv = [FA_T] * FA_B
-    q = torch.randn((FA_B, H, hd), device="cuda")
-    ws = torch.empty(kd.kd_fa_decode_workspace(FA_B, H, hd, t_kv), dtype=torch.uint8, device="cuda")
-    out = torch.empty_like(q)
-    for i in range(8):
-        c = sets[i % 2]
-        kd.kd_fa_decode_ragged(q, G, [c[b, 0].data_ptr() for b in range(FA_B)], [c[b, 1].data_ptr() for b in range(FA_B)],
-                               t_kv, FA_CAP, hd ** -0.5, ws=ws, out=out)
-    torch.cuda.synchronize()
+    for kind, _, _, _ in TRAFFIC_ORDER:
+        for i in range(PROBE_CALLS):
+            if kind == "fa":
+                kd.kd_fa_decode_ragged(q, G4, kbl[i % 4], vbl[i % 4], t_kv, wl.capacity, HD4 ** -0.5, ws=ws, out=out)
+            else:
+                rig.launch(kind, mats[kind][i % 4])
+        torch.cuda.synchronize()
     log("traffic probe done")
 
 
@@ -198,9 +312,9 @@ def _read_counters(path: str):
     import glob
     if os.path.isdir(path):
         hits = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
-        if len(hits) != 1:
-            raise SystemExit(f"expected one counter_collection.csv under {path}, found {hits}")
-        path = hits[0]
+        if not hits:
+            raise SystemExit(f"no counter_collection.csv under {path}")
+        path = max(hits, key=os.path.getmtime)   # the latest pass written there
     out = {}
     with open(path) as f:
         for row in csv.DictReader(f):
@@ -213,33 +327,44 @@ def _read_counters(path: str):
 
 
 def traffic_summarize(fetch: str, write: str, fetch_cmd: str, write_cmd: str) -> None:
-    """HBM bytes per launch of the measured kernels from the FETCH_SIZE and WRITE_SIZE passes
+    """HBM bytes per launch of each measured kernel from the FETCH_SIZE and WRITE_SIZE passes
     (KiB per dispatch), each scaled by what the counter reads for the 512 MiB calibration
-    copy; writes one profile summary per kernel, which the bench reads back.  A call of
-    several kernels (fa_decode: split + combine) counts the mean of each kernel once."""
+    copy; writes one profile summary per kernel, which the bench reads back.  The dispatches
+    after the calibration are taken in the probe's order, PROBE_CALLS calls per kind (a call
+    of fa_decode is its split and its combine; each kernel's mean counts once)."""
     rows = {tag: _read_counters(path) for tag, path in (("fetch", fetch), ("write", write))}
-    factor, calib_kib = {}, {}
+    factor, calib_kib, seqs = {}, {}, {}
     for tag, rr in rows.items():
-        calib = max((v for _, nm, v in rr if "MulFunctor" in nm), default=0.0)
-        if not calib:
+        idx = [i for i, (_, nm, _) in enumerate(rr) if "MulFunctor" in nm]
+        if not idx:
             raise SystemExit(f"{tag}: calibration dispatch missing")
+        calib = max(rr[i][2] for i in idx)
         calib_kib[tag], factor[tag] = calib, CALIB_BYTES / (calib * 1024.0)
-    for kind, spec in TRAFFIC.items():
-        per = {}
-        for tag, rr in rows.items():
-            per[tag] = {kn: [v for _, nm, v in rr if kn in nm] for kn in spec["kernels"]}
-            if not all(per[tag].values()):
-                raise SystemExit(f"{tag}: {kind} dispatches missing")
-        byts = {tag: sum(sum(v) / len(v) for v in per[tag].values()) * 1024.0 * factor[tag] for tag in per}
-        alg = spec["algorithmic"]()
+        seqs[tag] = [(nm, v) for _, nm, v in rr[idx[-1] + 1:] if "kd::" in nm]
+    per = {tag: {} for tag in rows}
+    for tag, seq in seqs.items():
+        pos = 0
+        for kind, _, _, kernels in TRAFFIC_ORDER:
+            vals = {kn: [] for kn in kernels}
+            for _ in range(PROBE_CALLS):
+                for kn in kernels:
+                    nm, v = seq[pos]
+                    if kn not in nm:
+                        raise SystemExit(f"{tag}: dispatch {pos} is {nm[:60]}, expected {kn} ({kind})")
+                    vals[kn].append(v)
+                    pos += 1
+            per[tag][kind] = vals
+    for kind, stem, _, kernels in TRAFFIC_ORDER:
+        title, alg = _traffic_title_bytes(kind)
+        byts = {tag: sum(sum(v) / len(v) for v in per[tag][kind].values()) * 1024.0 * factor[tag] for tag in per}
         total = byts["fetch"] + byts["write"]
-        rec = {"kernel": spec["title"], "source_hash": kernel_source_hash(kind),
+        rec = {"kernel": title, "source_hash": kernel_source_hash(kind),
                "fetch_bytes": round(byts["fetch"]), "write_bytes": round(byts["write"]),
                "traffic_bytes": round(total), "algorithmic_bytes": alg,
                "traffic_over_algorithmic": round(total / alg, 4),
                "fetch_factor": round(factor["fetch"], 5), "write_factor": round(factor["write"], 5)}
         lines = [
-            f"HBM traffic of {spec['title']} (rocprofv3 PMC, MI355X)",
+            f"HBM traffic of {title} (rocprofv3 PMC, MI355X)",
             "",
             f"FETCH_SIZE pass: {fetch_cmd}",
             f"WRITE_SIZE pass: {write_cmd}",
@@ -250,7 +375,7 @@ def traffic_summarize(fetch: str, write: str, fetch_cmd: str, write_cmd: str) ->
             f"  WRITE_SIZE {calib_kib['write']:.0f} KiB -> factor {factor['write']:.5f}",
         ]
         for tag in ("fetch", "write"):
-            for kn, vals in per[tag].items():
+            for kn, vals in per[tag][kind].items():
                 lines.append(f"{kn} dispatches {tag.upper()}_SIZE KiB: {', '.join(f'{v:.0f}' for v in vals)}")
         lines += [
             f"per launch: fetch {rec['fetch_bytes']} B + write {rec['write_bytes']} B = {rec['traffic_bytes']} B; "
@@ -258,8 +383,9 @@ def traffic_summarize(fetch: str, write: str, fetch_cmd: str, write_cmd: str) ->
             "",
             "TRAFFIC_JSON " + json.dumps(rec),
         ]
-        os.makedirs(os.path.dirname(spec["file"]), exist_ok=True)
-        with open(spec["file"], "w") as f:
+        path = os.path.join(ROOT, "profiles", stem + ".txt")
+        os.makedirs(os.path.dirname(path), exist_ok=True)
+        with open(path, "w") as f:
             f.write("\n".join(lines) + "\n")
         print("\n".join(lines) + "\n")
 
@@ -267,7 +393,7 @@ def traffic_summarize(fetch: str, write: str, fetch_cmd: str, write_cmd: str) ->
 def load_traffic(kind: str):
     """Measured HBM bytes per launch of a kernel, or None when no measurement exists or the
     kernel source has changed since it was taken."""
-    path = TRAFFIC[kind]["file"]
+    path = os.path.join(ROOT, "profiles", _traffic_spec(kind)[0] + ".txt")
     if not os.path.exists(path):
         return None
     for line in open(path):
@@ -276,6 +402,42 @@ def load_traffic(kind: str):
             if rec.get("source_hash") == kernel_source_hash(kind):
                 return rec["traffic_bytes"]
     return None
+
+
+def read_ceiling_us(tensors, nbytes: int, stream, iters: int) -> float:
+    """The plain read of ``nbytes`` of each tensor in turn (rotating, as the measured kernel
+    rotates over its matrices): average us per read."""
+    import torch
+    import session_decode_step_amd as kd
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    return time_rotating(lambda i: kd.kd_debug_read_stream(tensors[i % len(tensors)], sink, nbytes, stream=stream),
+                         iters, stream)
+
+
+def measure_products(gw, stream, iters: int) -> dict:
+    """Each product of the 32-layer stack at B=8 with its fused epilogue (HIP events on the
+    launch stream, rotating over the 32 layers' matrices), the 8-layer stack's lm_head
+    (rotating over four drawn matrices), and the plain read of the same weight bytes."""
+    mats = stack_products(gw)
+    mats["lm_head"] = lm_head_copies(4)
+    wl = gw.wl
+    rig = ProductRig(PB, [gw.caches.k_ptr(s, 0) for s in range(PB)], [gw.caches.v_ptr(s, 0) for s in range(PB)],
+                     wl.capacity - 1, wl.capacity)
+    res = {}
+    for kind in PRODUCTS:
+        log(f"product {kind} at B={PB}")
+        Ms = mats[kind]
+        us = time_rotating(lambda i: rig.launch(kind, Ms[i % len(Ms)], stream=stream), iters, stream)
+        alg = product_bytes(kind, PB)
+        wb = w_bytes(PRODUCTS[kind][1], PRODUCTS[kind][2], PRODUCTS[kind][3])
+        rd = read_ceiling_us([m.qs for m in Ms], Ms[0].qs.numel(), stream, iters)
+        gbs = alg / (us * 1e-6) / 1e9
+        res[kind] = {"kernel": PRODUCTS[kind][0], "bound": "hbm", "avg_launch_us": round(us, 3),
+                     "algorithmic_bytes": int(alg), "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": load_traffic(kind),
+                     "read_ceiling_us": round(rd, 3), "read_ceiling_GBs": round(wb / (rd * 1e-6) / 1e9, 1),
+                     "frac_of_read_ceiling": round(rd / us, 4)}
+    return res
 
 
 def _time_steps(gw, stream, K: int, Wu: int, rows=None, repeat_first: bool = False) -> float:
@@ -306,6 +468,7 @@ def other_workloads(stream, iters: int) -> dict:
     step and its fa_decode; the 8-layer MoE stack's verify step (4 streams x 4 draft rows,
     ctx 8192); the headline stack with FP8 E4M3 caches and its fa_decode; the gated
     delta-rule state step at B = 8 x 32 heads."""
+    import numpy as np
     import torch
     import workload as W
     import session_decode_step_amd as kd
@@ -348,8 +511,28 @@ def other_workloads(stream, iters: int) -> dict:
     wl = W.workload("c5")
     gw = GpuWorkload(wl, fill="device")
     ms = _time_steps(gw, stream, iters, 3, repeat_first=True)
+    # algorithmic bytes of the step with experts merged across rows: each layer's attention
+    # weights, router and shared expert, the distinct experts its 16 rows are routed to (read
+    # once however many rows share one), and each stream's keys once (its 4 rows share a pass)
+    sp = wl.spec
+    ids = gw.step_trace(0)["moe_ids"]                      # [layers, rows, top-k]
+    distinct = [len(np.unique(ids[il])) for il in range(sp.n_layers)]
+    e_bytes = w_bytes("q4_0", 2 * sp.expert_ffn, sp.d) + w_bytes("q4_0", sp.d, sp.expert_ffn)
+    attn_w = w_bytes("q4_0", (2 * sp.n_head_kv + sp.n_head) * sp.head_dim, sp.d) + \
+        w_bytes("q4_0", sp.d, sp.n_head * sp.head_dim)
+    shared = w_bytes("q4_0", 2 * sp.shared_ffn, sp.d) + w_bytes("q4_0", sp.d, sp.shared_ffn)
+    router = sp.n_experts * sp.d * 4
+    t_stream = [max(p + 1 for (st, _), p in zip(wl.rows, wl.positions(0)) if st == s) for s in range(len(wl.prefill))]
+    kv_merged = sum(t_stream) * sp.n_head_kv * sp.head_dim * 2 * 2
+    kv_rows = sum(p + 1 for p in wl.positions(0)) * sp.n_head_kv * sp.head_dim * 2 * 2
+    merged = sum(attn_w + router + shared + n * e_bytes + kv_merged for n in distinct)
+    per_row = sp.n_layers * (attn_w + router + shared + wl.B * sp.n_expert_used * e_bytes + kv_rows)
     res["8-layer MoE d=2816 128 experts top-8 + shared, Q4_0; 4 streams x 4 verify rows, ctx 8192"] = {
-        "ms_per_step": round(ms, 4), "rows_s": round(wl.B / ms * 1e3, 1)}
+        "ms_per_step": round(ms, 4), "rows_s": round(wl.B / ms * 1e3, 1),
+        "distinct_experts_per_layer": distinct, "expert_bytes": int(e_bytes),
+        "step_algorithmic_bytes_merged": int(merged), "step_GBs_merged": round(merged / (ms * 1e-3) / 1e9, 1),
+        "step_frac_of_peak": round(merged / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "step_bytes_if_each_row_read_its_experts_and_keys": int(per_row)}
     del gw
     # the headline stack with FP8 E4M3 caches, and its fa_decode
     log("32-layer Q4_0 stack, FP8 E4M3 KV caches")
@@ -409,7 +592,8 @@ def main() -> None:
     ap.add_argument("--kernel-iters", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other", action="store_true", help="skip the other workloads (headline only)")
-    ap.add_argument("--cpu-layers", type=int, default=16, help="layers of one step the oracle is timed on")
+    ap.add_argument("--cpu-layers", type=int, default=8,
+                    help="layers of one step of the 32-layer stack the oracle is timed on")
     ap.add_argument("--summarize-trace", default=None)
     ap.add_argument("--traffic-probe", action="store_true", help="launches for the PMC traffic passes only")
     ap.add_argument("--traffic-summarize", nargs=2, metavar=("FETCH", "WRITE"), default=None)
@@ -487,70 +671,43 @@ def main() -> None:
     for B in widths:
         sweep[B]["step_GBs"] = step_bytes(B, mid) / (sweep[B]["ms_per_step"] / 1e3) / 1e9
 
-    # ---------------------------------------------------------------- the largest product
-    # the FFN's interleaved gate/up product (28672 x 4096 Q4_0) with its SwiGLU + quantiser
-    # epilogue, at the headline width: 54% of the step's weight bytes.  Launches rotate over
-    # the 32 layers' own matrices (2.1 GB, well above the 256 MB Infinity Cache), as inside
-    # a step.
-    B = Bh
-    log(f"gate/up mmvq with SwiGLU epilogue at B={B}")
-    mats = [gw.km.packed[il]["w_gateup"] for il in range(L)]
-    xin = torch.randn((B, sp.d), device="cuda", generator=torch.Generator(device="cuda").manual_seed(0))
-    act = kd.kd_quantize_act_q8(xin)
-    h_act = kd.alloc_act(B, mats[0].n_out // 2)
-    mm_us = time_rotating(lambda i: kd.kd_mmvq_swiglu(mats[i % L], act, B, h_act, stream=stream), args.kernel_iters,
-                          stream)
-    n, k = mats[0].n_out, mats[0].k
-    mm_bytes = mmvq_algorithmic_bytes(n, k, B)
-    mm_gbs = mm_bytes / (mm_us * 1e-6) / 1e9
-    mm_traffic = load_traffic("mmvq") if (n, k, B) == (MM_N, MM_K, MM_B) else None
+    # ---------------------------------------------------------------- the products
+    # each product of the stack with its fused epilogue at B=8, rotating over the 32 layers'
+    # own matrices (2.1 GB for gate/up, well above the 256 MB Infinity Cache), as inside a
+    # step; the lm_head of the 8-layer Q8_0 stack; and the plain read of the same bytes
+    products = measure_products(gw, stream, args.kernel_iters)
 
     # ---------------------------------------------------------------- dominant kernel: fa_decode
     # the split kernel and its combine: the largest share of the step's time (~40% at B = 8).
-    # Calls rotate over the 32 layers' caches (135 MB of KV per call), as inside a step.
-    log(f"fa_decode at B={B}")
-    t_kv = [p + 1 for p in wl.positions(mid)[:B]]
-    q = torch.randn((B, sp.n_head, hd), device="cuda", generator=torch.Generator(device="cuda").manual_seed(1))
-    kbl = [[gw.caches.k_ptr(s, il) for s in range(B)] for il in range(L)]
-    vbl = [[gw.caches.v_ptr(s, il) for s in range(B)] for il in range(L)]
-    fa_ws = torch.empty(kd.kd_fa_decode_workspace(B, sp.n_head, hd, t_kv), dtype=torch.uint8, device="cuda")
+    # B=8 rows of 4113 keys (ctx 4096 after 16 decode steps + this one), whatever --steps is;
+    # calls rotate over the 32 layers' caches (135 MB of KV per call), as inside a step.
+    log(f"fa_decode at B={FA_B}, t={FA_T}")
+    t_kv = [FA_T] * FA_B
+    q = torch.randn((FA_B, sp.n_head, hd), device="cuda", generator=torch.Generator(device="cuda").manual_seed(1))
+    kbl = [[gw.caches.k_ptr(s, il) for s in range(FA_B)] for il in range(L)]
+    vbl = [[gw.caches.v_ptr(s, il) for s in range(FA_B)] for il in range(L)]
+    fa_ws = torch.empty(kd.kd_fa_decode_workspace(FA_B, sp.n_head, hd, t_kv), dtype=torch.uint8, device="cuda")
     fa_out = torch.empty_like(q)
     fa_us = time_rotating(lambda i: kd.kd_fa_decode_ragged(q, G, kbl[i % L], vbl[i % L], t_kv, wl.capacity,
                                                            hd ** -0.5, ws=fa_ws, out=fa_out, stream=stream),
                           args.kernel_iters, stream)
     fa_bytes = fa_algorithmic_bytes(t_kv, G, sp.n_head, hd)
     fa_gbs = fa_bytes / (fa_us * 1e-6) / 1e9
-    fa_traffic = load_traffic("fa") if t_kv == [FA_T] * FA_B else None
-
+    # the plain read of as many bytes (one launch over a contiguous range of a session's cache
+    # tensor, rotating over sessions): the practical ceiling of this call
+    rd_bytes = sum(t_kv) * G * hd * 2 * 2
+    rd_us = read_ceiling_us([gw.caches.t[s] for s in range(FA_B)], rd_bytes, stream, args.kernel_iters)
     other = None if args.no_other else other_workloads(stream, 20)
 
-    # ---------------------------------------------------------------- CPU oracle baseline
-    cpu = None
+    # ---------------------------------------------------------------- CPU oracle baselines
+    cpu, cpu_configs = None, None
     if not args.no_cpu_baseline:
-        import dataclasses
-        import oracle
-        try:
-            from threadpoolctl import threadpool_info
-            info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
-            threads = max([i.get("num_threads", 1) for i in info] or [1])
-            blas = ",".join(sorted({i.get("internal_api", "?") for i in info}))
-        except Exception:
-            threads, blas = os.cpu_count(), "?"
-        nl = min(args.cpu_layers, sp.n_layers)
-        sub_spec = dataclasses.replace(sp, n_layers=nl)
-        sub_model = {"spec": sub_spec, "layers": gw.model["layers"][:nl], "final_norm": gw.model["final_norm"],
-                     "lm_head": None}
-        sub_wl = dataclasses.replace(wl, spec=sub_spec)
-        log(f"cpu baseline: oracle over {nl} layers")
-        oc = oracle.OracleCaches(sub_wl, sessions=list(range(Bh)))
-        t0 = time.perf_counter()
-        oracle.decode_step(sub_model, oc, W.step_inputs(wl, 0)[:Bh], list(range(Bh)), wl.positions(0)[:Bh])
-        cpu_s = (time.perf_counter() - t0) * sp.n_layers / nl
-        cpu = {"value": round(Bh / cpu_s, 3), "unit": "tok/s", "cores": int(threads), "kind": "oracle",
-               "sample": f"one decode step of B={Bh} rows through {nl} of the {sp.n_layers} layers (fp64 numpy, "
-                         f"{blas} BLAS, oracle's own seeded KV), time scaled by {sp.n_layers}/{nl}: "
-                         f"{cpu_s:.1f} s per full step"}
+        cpu, cpu_configs = cpu_baselines(gw, Bh, args.cpu_layers)
 
+    try:
+        rocm = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        rocm = "?"
     top = sweep[Bh]
     res = {
         "metric": "aggregate decode tok/s at B=1..16; achieved HBM GB/s vs MI355X peak",
@@ -568,22 +725,81 @@ def main() -> None:
         "config": {"workload": "32-layer dense decoder d=4096, 32Q/8KV hd=128, SwiGLU 14336, Q4_0 weights, "
                                f"final RMSNorm; B={Bh} sessions at ctx 4096, decode positions 4096..{4096 + K - 1}",
                    "B": Bh, "ctx": 4096, "layers": L, "parallelism": "single GPU"},
+        "platform": {"gpu": torch.cuda.get_device_name(0), "rocm": rocm, "hip": torch.version.hip,
+                     "torch": torch.__version__, "seed": 0},
         "sweep": {str(b): {kk: round(v, 3) for kk, v in sweep[b].items()} for b in widths},
         "step_GBs": round(top["step_GBs"], 1),
         "step_frac_of_peak": round(top["step_GBs"] / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(fa_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(fa_gbs / HBM_PEAK_GBS, 4), "traffic": fa_traffic,
-                     "kernel": "fa_decode: fa_split_kernel + fa_combine_kernel, B=%d, t_kv=%d" % (B, t_kv[0]),
-                     "avg_launch_us": round(fa_us, 3), "algorithmic_bytes": int(fa_bytes)},
-        "mmvq_roofline": {"bound": "hbm", "achieved": round(mm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                          "frac": round(mm_gbs / HBM_PEAK_GBS, 4), "traffic": mm_traffic,
-                          "kernel": "mmvq_kernel<Q4_0, SwiGLU epilogue> 28672x4096 (gate/up) at B=%d" % Bh,
-                          "avg_launch_us": round(mm_us, 3), "algorithmic_bytes": int(mm_bytes)},
+                     "frac": round(fa_gbs / HBM_PEAK_GBS, 4), "traffic": load_traffic("fa"),
+                     "kernel": "fa_decode: fa_split_kernel + fa_combine_kernel, B=%d, t_kv=%d" % (FA_B, FA_T),
+                     "avg_launch_us": round(fa_us, 3), "algorithmic_bytes": int(fa_bytes),
+                     "read_ceiling_us": round(rd_us, 3), "read_ceiling_GBs": round(rd_bytes / (rd_us * 1e-6) / 1e9, 1),
+                     "frac_of_read_ceiling": round(rd_us / fa_us, 4)},
+        "mmvq_roofline": products["gateup"],
+        "products": products,
         "cpu_baseline": cpu,
+        "cpu_baseline_configs": cpu_configs,
         "other_workloads": other,
         "setup_s": round(setup_s, 1),
     }
     print(json.dumps(res))
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        return (max([i.get("num_threads", 1) for i in info] or [1]),
+                ",".join(sorted({i.get("internal_api", "?") for i in info})))
+    except Exception:
+        return os.cpu_count(), "?"
+
+
+def oracle_sample(name: str, model, wl, B: int, nl: int) -> dict:
+    """The oracle on the host cores: the first ``nl`` layers and the output head of one step
+    of ``wl``'s first B rows (its own seeded KV), the layer time scaled to the whole stack."""
+    import numpy as np
+    import oracle
+    import workload as W
+    threads, blas = _blas_threads()
+    sp = wl.spec
+    nl = min(nl, sp.n_layers)
+    rows = list(range(B))
+    sess = [wl.rows[b][0] for b in rows]
+    oc = oracle.OracleCaches(wl, sessions=sorted(set(sess)), layers=range(nl))
+    x = W.step_inputs(wl, 0)[rows].astype(np.float64)
+    pos = wl.positions(0)[:B]
+    t0 = time.perf_counter()
+    for il in range(nl):
+        x = oracle.decode_layer(model, il, oc, x, sess, pos)
+    t1 = time.perf_counter()
+    oracle.output_head(model, x)
+    t2 = time.perf_counter()
+    step_s = (t1 - t0) * sp.n_layers / nl + (t2 - t1)
+    return {"value": round(B / step_s, 4), "unit": "rows/s" if name == "c5" else "tok/s", "cores": int(threads),
+            "kind": "oracle", "B": B,
+            "sample": f"{nl} of {sp.n_layers} layers + output head of one step (fp64 numpy, {blas} BLAS), "
+                      f"layer time scaled by {sp.n_layers}/{nl}: {step_s:.2f} s per full step"}
+
+
+def cpu_baselines(gw, Bh: int, c4_layers: int):
+    """The oracle timed on the host cores on a bounded sample of each workload at its
+    headline width: the 32-layer Q4_0 stack at B=8 (``cpu_baseline``, the bench's own
+    workload) and the five workloads (single layer B=2; 8-layer Q8_0 + lm_head B=8; ragged
+    attention sublayer B=16; 32-layer Q4_0 B=8; MoE verify rows B=16)."""
+    import workload as W
+    out = {}
+    c4 = oracle_sample("c4", gw.model, W.workload("c4", B=Bh, steps=1), Bh, c4_layers)
+    log("cpu baseline: c4 done")
+    for name, B, nl in (("c1", 2, 1), ("c2", 8, 2), ("c3", 16, 1), ("c5", 16, 1)):
+        wl = W.workload(name, B=B) if name != "c1" else W.workload("c1")
+        model = W.make_model(wl.spec, wl.code, wl.seed)
+        out[name] = oracle_sample(name, model, wl, B, nl)
+        del model
+        log(f"cpu baseline: {name} done")
+    out["c4"] = c4
+    return c4, {k: out[k] for k in ("c1", "c2", "c3", "c4", "c5")}
 
 
 if __name__ == "__main__":

@@ -157,6 +157,28 @@ kd_status kd_mmvq_rope(const kd_weight* W, kd_act_q8 x, int32_t B, int32_t H, in
                        float* q_out, int32_t ldq, void* const* k_base, void* const* v_base,
                        const int32_t* pos, int32_t capacity, float rope_base, void* stream);
 
+/* RMSNorm split across two products (the fused form of the O product + residual add +
+ * post-attention norm, and of the down product + residual + next attention norm; memra-engine
+ * decode_batch.rs ``decode_batch_layers``: o product, add_rms_norm, quantise before the next
+ * products).  A workgroup of the producing product owns 32 output rows, one quantisation
+ * block of the next product's input, but not the whole row, so it cannot know 1/rms:
+ * kd_mmvq_resnorm computes x1 = res + W x (fp32 [B][n_out], x1 may not alias res), quantises
+ * z = x1 * gain block by block with each block's own scale max|z|/127 into `out` (the
+ * activation layout for k = n_out), and writes ss[b][blk] = the block's sum of x1^2 (fp32
+ * [B][n_out / 32]).  The consumer (kd_mmvq_swiglu_normed, kd_mmvq_rope_normed, with the
+ * same rows as x and norm_ss = ss) multiplies each output of row b by
+ * 1 / sqrt(sum_blk ss[b][blk] / k + eps): y = x1 * that * gain has the same codes as z, and
+ * the block scale times it is y's scale, so the pair computes the product of Q(RMSNorm(x1))
+ * up to rounding.  n_out % 32 == 0 and n_out <= 4096; the consumers' k <= 4096. */
+kd_status kd_mmvq_resnorm(const kd_weight* W, kd_act_q8 x, int32_t B, const float* res, const float* gain, float* x1,
+                          kd_act_q8 out, float* ss, void* stream);
+kd_status kd_mmvq_swiglu_normed(const kd_weight* W, kd_act_q8 x, int32_t B, const float* norm_ss, float eps,
+                                kd_act_q8 out, void* stream);
+kd_status kd_mmvq_rope_normed(const kd_weight* W, kd_act_q8 x, int32_t B, const float* norm_ss, float eps, int32_t H,
+                              int32_t G, int32_t hd, float* q_out, int32_t ldq, void* const* k_base,
+                              void* const* v_base, const int32_t* pos, int32_t capacity, float rope_base,
+                              void* stream);
+
 /* ---- KV append and ragged split-K decode attention --------------------------------- */
 /* Store row b's k[b][G][hd] and v[b][G][hd] (fp32, rounded to fp16 nearest-even) at
  * position pos[b] of its own cache: K_b[g][pos[b]][:] (memra-engine decode_batch.rs phase A,
@@ -407,6 +429,13 @@ kd_status kd_debug_moe_route(const float* z, const float* router, int32_t B, int
 kd_status kd_debug_mmvq_grouped(const kd_weight* W, int32_t n_groups, kd_act_q8 x, int32_t act_rows,
                                 const int32_t* count, const int32_t* act_row, const int32_t* out_row, int32_t swiglu,
                                 float* y, int32_t ldy, kd_act_q8 out, void* stream);
+
+/* A plain read of `bytes` bytes at p (device, 16-byte aligned, bytes % 16 == 0) with wide
+ * non-temporal loads and no arithmetic (measurement only: the practical HBM read ceiling the
+ * products and the attention are compared with, as the survey's measurement plan asks).
+ * sink: a device uint32 that is written only in the rare case the loaded words fold to a
+ * fixed constant. */
+kd_status kd_debug_read_stream(const void* p, size_t bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -103,9 +103,13 @@ SIGNATURES = {
     "kd_decode_step": (_I, [_P, _I, _P, _PI, _PP, _PP, _I, _P, _P, _S, _P]),
     "kd_mmvq_swiglu": (_I, [_PW, KdAct, _I, KdAct, _P]),
     "kd_mmvq_rope": (_I, [_PW, KdAct, _I, _I, _I, _I, _P, _I, _PP, _PP, _PI, _I, _F, _P]),
+    "kd_mmvq_resnorm": (_I, [_PW, KdAct, _I, _P, _P, _P, KdAct, _P, _P]),
+    "kd_mmvq_swiglu_normed": (_I, [_PW, KdAct, _I, _P, _F, KdAct, _P]),
+    "kd_mmvq_rope_normed": (_I, [_PW, KdAct, _I, _P, _F, _I, _I, _I, _P, _I, _PP, _PP, _PI, _I, _F, _P]),
     "kd_debug_block_dots": (_I, [_PW, KdAct, _I, _P, _P]),
     "kd_debug_fa_workspace": (_S, [_I, _I, _I, _PI, _I]),
     "kd_debug_fa_decode_chunked": (_I, [_P, _I, _I, _I, _I, _PP, _PP, _PI, _I, _F, _P, _I, _P, _S, _P]),
+    "kd_debug_read_stream": (_I, [_P, _S, _P, _P]),
     "kd_debug_decode_step_trace": (_I, [_P, _I, _P, _PI, _PP, _PP, _I, _P, _P, _S, C.POINTER(KdStepTrace), _P]),
     "kd_debug_moe_route": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
     "kd_debug_mmvq_grouped": (_I, [_PW, _I, KdAct, _I, _P, _P, _P, _I, _P, _I, KdAct, _P]),
@@ -292,6 +296,43 @@ def kd_mmvq_rope(W: PackedWeight, x: Act, B: int, H: int, G: int, hd: int, q_out
     return q_out
 
 
+def kd_mmvq_resnorm(W: PackedWeight, x: Act, B: int, res: torch.Tensor, gain: torch.Tensor,
+                    x1: Optional[torch.Tensor] = None, out: Optional[Act] = None, ss: Optional[torch.Tensor] = None,
+                    stream=None):
+    """x1 = res + W x, the block codes of x1 * gain and the block sums of x1^2 (the producing
+    half of a split RMSNorm): returns (x1, out, ss)."""
+    n = W.n_out
+    dev = x.qs.device
+    x1 = torch.empty((B, n), dtype=torch.float32, device=dev) if x1 is None else x1
+    out = alloc_act(B, n, dev) if out is None else out
+    ss = torch.empty((B, n // 32), dtype=torch.float32, device=dev) if ss is None else ss
+    wc = W.c()
+    _check(lib().kd_mmvq_resnorm(C.byref(wc), x.c(), B, res.data_ptr(), gain.data_ptr(), x1.data_ptr(), out.c(),
+                                 ss.data_ptr(), _stream(stream)), "kd_mmvq_resnorm")
+    return x1, out, ss
+
+
+def kd_mmvq_swiglu_normed(W: PackedWeight, x: Act, B: int, norm_ss: torch.Tensor, eps: float,
+                          out: Optional[Act] = None, stream=None) -> Act:
+    """kd_mmvq_swiglu on a split-RMSNorm input (x and norm_ss from kd_mmvq_resnorm)."""
+    out = out or alloc_act(B, W.n_out // 2, x.qs.device)
+    wc = W.c()
+    _check(lib().kd_mmvq_swiglu_normed(C.byref(wc), x.c(), B, norm_ss.data_ptr(), eps, out.c(), _stream(stream)),
+           "kd_mmvq_swiglu_normed")
+    return out
+
+
+def kd_mmvq_rope_normed(W: PackedWeight, x: Act, B: int, norm_ss: torch.Tensor, eps: float, H: int, G: int, hd: int,
+                        q_out: torch.Tensor, k_base, v_base, pos: Sequence[int], capacity: int, rope_base: float,
+                        stream=None) -> torch.Tensor:
+    """kd_mmvq_rope on a split-RMSNorm input (x and norm_ss from kd_mmvq_resnorm)."""
+    wc = W.c()
+    _check(lib().kd_mmvq_rope_normed(C.byref(wc), x.c(), B, norm_ss.data_ptr(), eps, H, G, hd, q_out.data_ptr(),
+                                     q_out.stride(0), _ptrs(k_base), _ptrs(v_base), _i32(pos), capacity, rope_base,
+                                     _stream(stream)), "kd_mmvq_rope_normed")
+    return q_out
+
+
 def kd_debug_block_dots(W: PackedWeight, x: Act, B: int, stream=None) -> torch.Tensor:
     S = torch.empty((B, W.n_out, W.k // 32), dtype=torch.int32, device=x.qs.device)
     wc = W.c()
@@ -351,6 +392,12 @@ def act_rows_view(x: Act, r0: int, n: int) -> Act:
     """Rows [r0, r0 + n) of a quantised activation buffer (the layout is row-contiguous)."""
     NQ = (x.k + 127) // 128
     return Act(x.qs[r0 * NQ * 128:(r0 + n) * NQ * 128], x.d[r0 * NQ * 4:(r0 + n) * NQ * 4], n, x.k)
+
+
+def kd_debug_read_stream(t: torch.Tensor, sink: torch.Tensor, nbytes: Optional[int] = None, stream=None) -> None:
+    """A plain read of the tensor's bytes (the first nbytes of them): the HBM read ceiling."""
+    n = t.numel() * t.element_size() if nbytes is None else nbytes
+    _check(lib().kd_debug_read_stream(t.data_ptr(), n, sink.data_ptr(), _stream(stream)), "kd_debug_read_stream")
 
 
 # ------------------------------------------------------------------------------ row ops

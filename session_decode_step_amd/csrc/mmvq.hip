@@ -854,10 +854,10 @@ extern "C" kd_status kd_mmvq_swiglu(const kd_weight* W, kd_act_q8 x, int32_t B, 
   return check_launch(who);
 }
 
-extern "C" kd_status kd_mmvq_rope(const kd_weight* W, kd_act_q8 x, int32_t B, int32_t H, int32_t G, int32_t hd,
-                                  float* q_out, int32_t ldq, void* const* k_base, void* const* v_base,
-                                  const int32_t* pos, int32_t capacity, float rope_base, void* stream) {
-  const char* who = "kd_mmvq_rope";
+static kd_status rope_entry(const char* who, const kd_weight* W, kd_act_q8 x, int32_t B, int32_t H, int32_t G,
+                            int32_t hd, float* q_out, int32_t ldq, void* const* k_base, void* const* v_base,
+                            const int32_t* pos, int32_t capacity, float rope_base, const float* norm_ss, float eps,
+                            void* stream) {
   KD_REQUIRE(W, KD_ERR_INVALID, "%s: null weight", who);
   kd_status s = check_mmvq_args(who, W, W->fmt, x, B);
   if (s != KD_OK) return s;
@@ -880,8 +880,73 @@ extern "C" kd_status kd_mmvq_rope(const kd_weight* W, kd_act_q8 x, int32_t B, in
     rc.v[b] = v_base[b];
     rc.pos[b] = pos[b];
   }
-  launch_mmvq_rope(*W, x.qs, x.d, B, q_out, ldq, H, G, hd, nullptr, rope_base, rc, capacity, as_stream(stream));
+  launch_mmvq_rope(*W, x.qs, x.d, B, q_out, ldq, H, G, hd, nullptr, rope_base, rc, capacity, as_stream(stream), norm_ss,
+                   W->k, eps);
   return check_launch(who);
+}
+
+extern "C" kd_status kd_mmvq_rope(const kd_weight* W, kd_act_q8 x, int32_t B, int32_t H, int32_t G, int32_t hd,
+                                  float* q_out, int32_t ldq, void* const* k_base, void* const* v_base,
+                                  const int32_t* pos, int32_t capacity, float rope_base, void* stream) {
+  return rope_entry("kd_mmvq_rope", W, x, B, H, G, hd, q_out, ldq, k_base, v_base, pos, capacity, rope_base, nullptr,
+                    0.0f, stream);
+}
+
+static kd_status check_norm_ss(const char* who, const kd_weight* W, const float* norm_ss, float eps) {
+  if (!norm_ss) return KD_OK;
+  KD_REQUIRE(W->k <= kNormFuseMax, KD_ERR_UNSUPPORTED, "%s: a normalised input row of k=%d exceeds %d", who, W->k,
+             kNormFuseMax);
+  KD_REQUIRE(eps > 0.0f && aligned16(norm_ss), KD_ERR_INVALID, "%s: eps must be positive and norm_ss 16-byte aligned",
+             who);
+  return KD_OK;
+}
+
+extern "C" kd_status kd_mmvq_resnorm(const kd_weight* W, kd_act_q8 x, int32_t B, const float* res, const float* gain,
+                                     float* x1, kd_act_q8 out, float* ss, void* stream) {
+  const char* who = "kd_mmvq_resnorm";
+  KD_REQUIRE(W, KD_ERR_INVALID, "%s: null weight", who);
+  kd_status s = check_mmvq_args(who, W, W->fmt, x, B);
+  if (s != KD_OK) return s;
+  KD_REQUIRE(fmt_quant(W->fmt), KD_ERR_UNSUPPORTED, "%s: format %d", who, W->fmt);
+  KD_REQUIRE(W->n_out % 32 == 0 && W->n_out <= kNormFuseMax, KD_ERR_UNSUPPORTED,
+             "%s: n_out=%d must be a multiple of 32 and at most %d", who, W->n_out, kNormFuseMax);
+  KD_REQUIRE(res && gain && x1 && ss && out.qs && out.d, KD_ERR_INVALID, "%s: null pointer", who);
+  KD_REQUIRE(aligned16(res) && aligned16(gain) && aligned16(x1) && aligned16(out.qs) && aligned16(out.d),
+             KD_ERR_INVALID, "%s: res, gain, x1 and out must be 16-byte aligned", who);
+  KD_REQUIRE(res != x1, KD_ERR_INVALID, "%s: x1 may not alias res", who);
+  launch_mmvq_resnorm(*W, x.qs, x.d, B, res, W->n_out, gain, x1, out.qs, out.d, ss, as_stream(stream));
+  return check_launch(who);
+}
+
+extern "C" kd_status kd_mmvq_swiglu_normed(const kd_weight* W, kd_act_q8 x, int32_t B, const float* norm_ss,
+                                           float eps, kd_act_q8 out, void* stream) {
+  const char* who = "kd_mmvq_swiglu_normed";
+  KD_REQUIRE(norm_ss, KD_ERR_INVALID, "%s: null norm_ss", who);
+  KD_REQUIRE(W, KD_ERR_INVALID, "%s: null weight", who);
+  kd_status s = check_norm_ss(who, W, norm_ss, eps);
+  if (s != KD_OK) return s;
+  s = check_mmvq_args(who, W, W->fmt, x, B);
+  if (s != KD_OK) return s;
+  KD_REQUIRE(fmt_quant(W->fmt), KD_ERR_UNSUPPORTED, "%s: format %d", who, W->fmt);
+  KD_REQUIRE(W->n_out % 64 == 0, KD_ERR_UNSUPPORTED, "%s: n_out=%d is not 2F with F a multiple of 32", who,
+             W->n_out);
+  KD_REQUIRE(out.qs && out.d && aligned16(out.qs) && aligned16(out.d), KD_ERR_INVALID,
+             "%s: output buffers null or not 16-byte aligned", who);
+  launch_mmvq_swiglu(*W, x.qs, x.d, B, out.qs, out.d, as_stream(stream), norm_ss, W->k, eps);
+  return check_launch(who);
+}
+
+extern "C" kd_status kd_mmvq_rope_normed(const kd_weight* W, kd_act_q8 x, int32_t B, const float* norm_ss, float eps,
+                                         int32_t H, int32_t G, int32_t hd, float* q_out, int32_t ldq,
+                                         void* const* k_base, void* const* v_base, const int32_t* pos,
+                                         int32_t capacity, float rope_base, void* stream) {
+  const char* who = "kd_mmvq_rope_normed";
+  KD_REQUIRE(norm_ss, KD_ERR_INVALID, "%s: null norm_ss", who);
+  KD_REQUIRE(W, KD_ERR_INVALID, "%s: null weight", who);
+  kd_status s = check_norm_ss(who, W, norm_ss, eps);
+  if (s != KD_OK) return s;
+  return rope_entry(who, W, x, B, H, G, hd, q_out, ldq, k_base, v_base, pos, capacity, rope_base, norm_ss, eps,
+                    stream);
 }
 
 extern "C" kd_status kd_debug_block_dots(const kd_weight* W, kd_act_q8 x, int32_t B, int32_t* S, void* stream) {

@@ -47,7 +47,10 @@ def test_act_quant_codes_and_scales_exact(B, k):
 
 
 # ------------------------------------------------------------------ mmvq
-SHAPES = [("q8_0", 100, 704), ("q8_0", 512, 2048), ("q4_0", 100, 704), ("q4_0", 4096, 4096), ("q8_0", 48, 256)]
+# ragged shapes, the 32-layer stack's O (4096 x 4096) and down (4096 x 14336: 14 waves of 8
+# quads) products, the 8-layer stack's lm_head (32000 x 2048 Q8_0) and the largest k (16384)
+SHAPES = [("q8_0", 100, 704), ("q8_0", 512, 2048), ("q4_0", 100, 704), ("q4_0", 4096, 4096), ("q8_0", 48, 256),
+          ("q4_0", 4096, 14336), ("q8_0", 32000, 2048), ("q4_0", 272, 16384)]
 
 
 @pytest.mark.parametrize("fmt,n,k", SHAPES)
@@ -413,3 +416,62 @@ def test_fa_decode_at_the_key_limit():
         o1 = kd.kd_fa_decode_ragged(dev(q[b:b + 1]), G, kb[b:b + 1], vb[b:b + 1], t_kv[b:b + 1], cap, scale)
         np.testing.assert_array_equal(o1.cpu().numpy()[0].view(np.uint32), out[b].view(np.uint32))
 
+
+
+@pytest.mark.parametrize("fmt,n,k,B", [("q4_0", 4096, 4096, 8), ("q8_0", 2048, 2048, 3), ("q4_0", 4096, 14336, 16),
+                                       ("q4_0", 2816, 2048, 5)])
+def test_resnorm_pair_matches_oracle(fmt, n, k, B):
+    """The split RMSNorm: kd_mmvq_resnorm (x1 = res + W Q(a), the block codes of x1 * gain,
+    the block sums of x1^2) and its consumers kd_mmvq_swiglu_normed / kd_mmvq_rope_normed,
+    against the oracle's add + RMSNorm + Q and the products after it.  Every GPU code must
+    be a valid rounding of the oracle's value (|x/d - code| <= 1/2 + 1e-3); the consumers
+    are compared given the GPU's codes of their input (the oracle's own scales)."""
+    from oracle.step import _q_forced
+    say(f"resnorm pair {fmt} n={n} k={k} B={B}")
+    r = np.random.default_rng(n + k + B)
+    draw = W.draw_q8_0 if fmt == "q8_0" else W.draw_q4_0
+    w = draw(r, r, n, k)
+    a = r.standard_normal((B, k)).astype(np.float32)
+    res = r.standard_normal((B, n)).astype(np.float32)
+    gain = (1 + 0.1 * r.standard_normal(n)).astype(np.float32)
+    act = kd.kd_quantize_act_q8(dev(a))
+    x1, zq, ss = kd.kd_mmvq_resnorm(kd.kd_pack_weight(w), act, B, dev(res), dev(gain))
+    sync()
+    q, d = ops.quantize_act(a)
+    x1_ref = res.astype(np.float64) + ops.mmvq(w, q, d)
+    assert_close_rows(x1.cpu().numpy(), x1_ref, 1e-5, "resnorm x1")
+    ss_ref = (x1_ref.reshape(B, -1, 32) ** 2).sum(axis=2)
+    np.testing.assert_allclose(ss.cpu().numpy(), ss_ref, rtol=1e-5)
+    codes, _, pad_codes, _ = untile_act(zq.qs, zq.d, B, n)
+    z = ops.rmsnorm(x1_ref, gain, 1e-5)
+    rec = []
+    zc, zd = _q_forced(z, codes, rec, "z")
+    assert rec[0]["invalid"] == 0, rec
+    assert np.all(pad_codes == 0)
+    say(f"  {rec[0]['flips']} of {rec[0]['codes']} codes the other valid rounding")
+    # consumer 1: the interleaved gate/up product with SwiGLU on the normed input
+    F = 1024
+    gate, up = draw(r, r, F, n), draw(r, r, F, n)
+    h = kd.kd_mmvq_swiglu_normed(kd.kd_pack_weight(kd.interleave_gate_up(gate, up)), zq, B, ss, 1e-5)
+    sync()
+    hc, _, _, _ = untile_act(h.qs, h.d, B, F)
+    h_ref = ops.swiglu(ops.mmvq(gate, zc, zd), ops.mmvq(up, zc, zd))
+    rec = []
+    _q_forced(h_ref, hc, rec, "h")
+    assert rec[0]["invalid"] == 0, rec
+    # consumer 2: the pair-ordered QKV product with RoPE and the fp16 append on the normed input
+    H, G, hd, cap = 8, 4, 128, 32
+    wq = draw(r, r, (H + 2 * G) * hd, n)
+    pos = [int(p) for p in r.integers(0, cap, B)]
+    cs = _caches(B, G, cap, hd)
+    q_out = torch.zeros((B, H * hd), dtype=torch.float32, device="cuda")
+    kd.kd_mmvq_rope_normed(kd.kd_pack_weight(kd.rope_pair_rows(wq, H + 2 * G, hd)), zq, B, ss, 1e-5, H, G, hd,
+                           q_out, [c[0].data_ptr() for c in cs], [c[1].data_ptr() for c in cs], pos, cap, 10000.0)
+    sync()
+    y = ops.mmvq(wq, zc, zd)
+    qref = np.stack([ops.rope_neox(y[b, :H * hd].reshape(H, hd), pos[b], 10000.0) for b in range(B)])
+    assert_close_rows(q_out.cpu().numpy(), qref.reshape(B, -1), 1e-4, "rope normed q")
+    for b in range(B):
+        kref = ops.rope_neox(y[b, H * hd:(H + G) * hd].reshape(G, hd), pos[b], 10000.0)
+        kg = cs[b][0].cpu().numpy()[:, pos[b]].astype(np.float64)
+        assert np.max(np.abs(kg - kref)) <= np.max(np.abs(kref)) * 2 ** -10 + 1e-5 * np.sqrt(np.mean(kref ** 2))
