@@ -202,6 +202,18 @@ kd_status kd_fa_decode_ragged(const float* q, int32_t B, int32_t H, int32_t G, i
                               const int32_t* t_kv, int32_t capacity, float scale, float* out,
                               void* ws, size_t ws_bytes, void* stream);
 
+/* kd_fa_decode_ragged for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same computation and
+ * output bits, with the split partials kept in a scratch array the library holds on each GPU
+ * it runs on (16 MiB per GPU, until the process ends) instead of a caller's workspace.  The
+ * call allocates nothing.  A call whose partials need more than the array
+ * (kd_fa_decode_workspace > 16 MiB) returns KD_ERR_WORKSPACE before anything is enqueued.
+ * Every call on one GPU shares its array: calls that overlap on one GPU (on different streams,
+ * or from several threads) race and must be serialised by the caller. */
+kd_status kd_fa_decode_ragged_noalloc(const float* q, int32_t B, int32_t H, int32_t G, int32_t hd,
+                                      const void* const* k_base, const void* const* v_base, const int32_t* t_kv,
+                                      int32_t capacity, float scale, float* out, void* stream);
+
 /* FP8 KV caches (memra-engine decode_batch.rs phase A stores quantised K/V rows, with an fp8
  * switch on the store and on ``fa_decode_kvmod``; the byte format is not given there).  Read
  * here as OCP FP8 E4M3, one byte per element, no scale: bit 7 sign, bits 6..3 exponent with

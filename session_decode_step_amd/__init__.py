@@ -96,6 +96,7 @@ SIGNATURES = {
     "kd_gdn_step": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _PP, _PP, _F, _P, _P]),
     "kd_fa_decode_workspace": (_S, [_I, _I, _I, _PI]),
     "kd_fa_decode_ragged": (_I, [_P, _I, _I, _I, _I, _PP, _PP, _PI, _I, _F, _P, _P, _S, _P]),
+    "kd_fa_decode_ragged_noalloc": (_I, [_P, _I, _I, _I, _I, _PP, _PP, _PI, _I, _F, _P, _P]),
     "kd_fa_decode_ragged_fp8": (_I, [_P, _I, _I, _I, _I, _PP, _PP, _PI, _I, _F, _P, _P, _S, _P]),
     "kd_model_create": (_I, [C.POINTER(KdModelDesc), C.POINTER(_P)]),
     "kd_model_destroy": (None, [_P]),
@@ -510,6 +511,17 @@ def kd_fa_decode_ragged_fp8(q: torch.Tensor, G: int, k_base, v_base, t_kv, capac
     _check(lib().kd_fa_decode_ragged_fp8(q.data_ptr(), B, H, G, hd, _ptrs(k_base), _ptrs(v_base), _i32(t_kv),
                                          capacity, scale, out.data_ptr(), ws.data_ptr(), ws.numel(),
                                          _stream(stream)), "kd_fa_decode_ragged_fp8")
+    return out
+
+
+def kd_fa_decode_ragged_noalloc(q: torch.Tensor, G: int, k_base, v_base, t_kv, capacity: int, scale: float,
+                                out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """kd_fa_decode_ragged with the split partials in the library's per-GPU scratch array."""
+    B, H, hd = q.shape
+    out = torch.empty_like(q) if out is None else out
+    _check(lib().kd_fa_decode_ragged_noalloc(q.data_ptr(), B, H, G, hd, _ptrs(k_base), _ptrs(v_base), _i32(t_kv),
+                                             capacity, scale, out.data_ptr(), _stream(stream)),
+           "kd_fa_decode_ragged_noalloc")
     return out
 
 

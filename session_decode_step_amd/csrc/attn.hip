@@ -15,6 +15,8 @@
 // sum e^(m_s-M) l_s.  All reductions use fixed trees, so a row's bytes equal its 1-row call.
 #include <algorithm>
 
+#include <mutex>
+
 #include "kd_internal.h"
 
 namespace kd {
@@ -623,10 +625,36 @@ static kd_status fa_check(const char* who, const float* q, int32_t B, int32_t H,
   return KD_OK;
 }
 
+// Split-partial storage of kd_fa_decode_ragged_noalloc: one array per GPU the library runs
+// on, held until the process ends.  Host code never uses the array's name as an address: the
+// device address comes from hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kFaScratchBytes = 16u << 20;
+static __device__ __align__(256) char scratch[kFaScratchBytes];
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices] = {};
+
+static kd_status fa_scratch(const char* who, void** out) {
+  int dev = -1;
+  KD_REQUIRE(hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices, KD_ERR_HIP,
+             "%s: no current device (or more than %d)", who, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    KD_REQUIRE(e == hipSuccess && p, KD_ERR_HIP, "%s: hipGetSymbolAddress of the scratch array: %s", who,
+               hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KD_OK;
+}
+
+// ws == nullptr with use_scratch: the split partials go to this device's scratch array.
 static kd_status fa_run(const char* who, const float* q, int32_t B, int32_t H, int32_t G, int32_t hd,
                         const void* const* k_base, const void* const* v_base, const int32_t* t_kv, int32_t capacity,
                         float scale, float* out, int32_t chunk, void* ws, size_t ws_bytes, void* stream,
-                        bool kv_fp8 = false) {
+                        bool kv_fp8 = false, bool use_scratch = false) {
   kd_status s = fa_check(who, q, B, H, G, hd, k_base, v_base, t_kv, out);
   if (s != KD_OK) return s;
   for (int b = 0; b < B; ++b)
@@ -635,6 +663,14 @@ static kd_status fa_run(const char* who, const float* q, int32_t B, int32_t H, i
   fa_make_plan(p, B, H, G, hd, t_kv, chunk);
   for (int b = 0; b < B; ++b)
     KD_REQUIRE(p.chunk[b] <= 1024, KD_ERR_UNSUPPORTED, "%s: chunk of %d keys exceeds 1024", who, p.chunk[b]);
+  if (use_scratch) {
+    KD_REQUIRE(fa_workspace_bytes(p) <= kFaScratchBytes, KD_ERR_WORKSPACE,
+               "%s: the split partials need %zu bytes, more than the %zu-byte scratch array", who,
+               fa_workspace_bytes(p), kFaScratchBytes);
+    s = fa_scratch(who, &ws);
+    if (s != KD_OK) return s;
+    ws_bytes = kFaScratchBytes;
+  }
   KD_REQUIRE(ws && ws_bytes >= fa_workspace_bytes(p), KD_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", who, ws_bytes,
              fa_workspace_bytes(p));
   RowCaches rc = {};
@@ -663,6 +699,14 @@ extern "C" size_t kd_debug_fa_workspace(int32_t B, int32_t H, int32_t hd, const 
   FaPlan p;
   fa_make_plan(p, B, H, 1, hd, t_kv, chunk);
   return fa_workspace_bytes(p);
+}
+
+extern "C" kd_status kd_fa_decode_ragged_noalloc(const float* q, int32_t B, int32_t H, int32_t G, int32_t hd,
+                                                 const void* const* k_base, const void* const* v_base,
+                                                 const int32_t* t_kv, int32_t capacity, float scale, float* out,
+                                                 void* stream) {
+  return fa_run("kd_fa_decode_ragged_noalloc", q, B, H, G, hd, k_base, v_base, t_kv, capacity, scale, out, 0, nullptr,
+                0, stream, false, true);
 }
 
 extern "C" kd_status kd_fa_decode_ragged(const float* q, int32_t B, int32_t H, int32_t G, int32_t hd,

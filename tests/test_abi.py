@@ -308,3 +308,17 @@ def test_products_reject_shapes_past_their_limits():
     assert L.kd_model_create(C.byref(desc), C.byref(h)) == kd.KD_OK
     L.kd_model_destroy(h)
     del ok, just
+
+
+def test_noalloc_attention_rejects_partials_beyond_its_scratch():
+    """kd_fa_decode_ragged_noalloc refuses, before touching the device, a call whose split
+    partials exceed its 16 MiB scratch array (16 rows of 131072 keys, 64 query heads: 68 MB)."""
+    L = kd.lib()
+    B, H, G, hd, cap = 16, 64, 8, 128, 131072
+    t = (C.c_int32 * B)(*([cap] * B))
+    assert L.kd_fa_decode_workspace(B, H, hd, t) > 16 << 20
+    kb = (C.c_void_p * B)(*[0x100000 * (i + 1) for i in range(B)])
+    vb = (C.c_void_p * B)(*[0x8000000 + 0x100000 * i for i in range(B)])
+    assert L.kd_fa_decode_ragged_noalloc(0x1000, B, H, G, hd, kb, vb, t, cap, 0.088, 0x2000, None) \
+        == kd.KD_ERR_WORKSPACE
+    assert b"scratch" in L.kd_last_error()
