@@ -350,3 +350,52 @@ def gdn_step(S: np.ndarray, q: np.ndarray, k: np.ndarray, v: np.ndarray, g: np.n
     S_new = Sd + b * (v - u)[:, :, None] * k[:, None, :]
     o = scale * np.einsum("hvk,hk->hv", S_new, q)
     return S_new, o
+
+
+# ---------------------------------------------------------------------------------------
+# int8 (Q8_0-block) KV cache codec
+# ---------------------------------------------------------------------------------------
+def q8_kv_row_bytes(hd: int) -> int:
+    """Bytes of one cached (position, KV head) row: hd int8 codes, hd/32 fp16 block scales,
+    zero padding to a multiple of 16 bytes."""
+    return hd + 16
+
+
+def q8_kv_encode(x: np.ndarray) -> np.ndarray:
+    """Cache rows (uint8 ``[..., hd + 16]``) of fp32 values ``x[..., hd]``.
+
+    memra-engine decode_batch.rs, phase A of ``decode_batch_layers``: the append stores
+    quantised K/V rows (``append_kv_quantized_seqs``, with per-token row bytes); Strata PR #1524
+    "What changes" runs with resident int8 KV.  The byte format is not given.  Reading: Q8_0
+    blocks along the head row -- per 32 consecutive elements a = max |x_i|, the stored scale
+    d = fp16(a / 127) (fp32 division, then round to nearest even), and codes
+    q_i = clamp(round_half_away(x_i / d), -127, 127) with the stored scale as an fp32 number
+    (all zero when d is 0); the value of a code is d q_i.  A row is its hd codes, then its
+    hd/32 scales, then zeros up to hd + 16 bytes.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    hd = x.shape[-1]
+    assert hd % 32 == 0
+    lead = x.shape[:-1]
+    blk = x.reshape(-1, hd // 32, 32)
+    a = np.max(np.abs(blk), axis=2)
+    d16 = (a / np.float32(127.0)).astype(np.float32).astype(np.float16)      # RNE to fp16
+    df = d16.astype(np.float32)
+    safe = np.where(df == 0, np.float32(1.0), df)
+    r = (blk / safe[:, :, None]).astype(np.float32).astype(np.float64)       # IEEE fp32 division
+    q = np.clip(np.sign(r) * np.floor(np.abs(r) + 0.5), -127, 127)
+    q = np.where((df == 0)[:, :, None], 0, q).astype(np.int8)
+    out = np.zeros((blk.shape[0], q8_kv_row_bytes(hd)), dtype=np.uint8)
+    out[:, :hd] = q.reshape(-1, hd).view(np.uint8)
+    out[:, hd:hd + 2 * (hd // 32)] = d16.view(np.uint8).reshape(-1, 2 * (hd // 32))
+    return out.reshape(*lead, q8_kv_row_bytes(hd))
+
+
+def q8_kv_decode(rows: np.ndarray, hd: int) -> np.ndarray:
+    """fp64 values ``[..., hd]`` of cache rows written by :func:`q8_kv_encode` (d q_i)."""
+    rows = np.asarray(rows, dtype=np.uint8)
+    lead = rows.shape[:-1]
+    flat = rows.reshape(-1, rows.shape[-1])
+    q = flat[:, :hd].view(np.int8).astype(np.float64).reshape(-1, hd // 32, 32)
+    d = np.ascontiguousarray(flat[:, hd:hd + 2 * (hd // 32)]).view(np.float16).astype(np.float64)
+    return (q * d[:, :, None]).reshape(*lead, hd)

@@ -47,7 +47,8 @@ class DenseWeights:
 
 class OracleCaches:
     """K/V of the sessions the oracle follows: ``K[s][il]`` is ``[G, capacity, hd]``, fp16, or
-    uint8 E4M3 codes for a model with FP8 caches (``spec.kv_fp8``)."""
+    uint8 E4M3 codes for a model with FP8 caches (``spec.kv_fp8``), or uint8 rows
+    ``[G, capacity, hd + 16]`` for int8 caches (``spec.kv_q8``, see ``ops.q8_kv_encode``)."""
 
     def __init__(self, wl, sessions: Optional[Sequence[int]] = None, layers: Optional[Sequence[int]] = None):
         """``layers``: only these layers' caches are filled (the others stay None), for
@@ -68,8 +69,8 @@ class OracleCaches:
                     self.V[s].append(None)
                     continue
                 k0, v0 = pre[(s, il)]
-                dt = np.uint8 if getattr(sp, "kv_fp8", False) else np.float16
-                K = np.zeros((sp.n_head_kv, wl.capacity, sp.head_dim), dtype=dt)
+                dt = np.uint8 if getattr(sp, "kv_fp8", False) or getattr(sp, "kv_q8", False) else np.float16
+                K = np.zeros((sp.n_head_kv, wl.capacity, k0.shape[2]), dtype=dt)
                 V = np.zeros_like(K)
                 K[:, : k0.shape[1]] = k0
                 V[:, : v0.shape[1]] = v0
@@ -203,19 +204,27 @@ def decode_layer(model: Dict, il: int, caches: OracleCaches, x: np.ndarray, sess
     q = np.stack([ops.rope_neox(q[b], pos[b], sp.rope_base) for b in range(B)])
     k = np.stack([ops.rope_neox(k[b], pos[b], sp.rope_base) for b in range(B)])
     fp8 = getattr(sp, "kv_fp8", False)
+    q8 = getattr(sp, "kv_q8", False)
     for b in range(B):                                   # phase A: append all rows
         s = sessions[b]
         if fp8:   # FP8 caches: the nearest E4M3 code of each value
             caches.K[s][il][:, pos[b]] = ops.e4m3_encode(k[b])
             caches.V[s][il][:, pos[b]] = ops.e4m3_encode(v[b])
+        elif q8:  # int8 caches: Q8_0 blocks of the fp32 values
+            caches.K[s][il][:, pos[b]] = ops.q8_kv_encode(k[b].astype(np.float32))
+            caches.V[s][il][:, pos[b]] = ops.q8_kv_encode(v[b].astype(np.float32))
         else:
             caches.K[s][il][:, pos[b]] = k[b].astype(np.float16)
             caches.V[s][il][:, pos[b]] = v[b].astype(np.float16)
     win = int(L.get("swa_window", 0))
 
-    def kv(s):   # the values a row attends (codes read as their E4M3 values)
+    def kv(s):   # the values a row attends (codes read as their values)
         K, V = caches.K[s][il], caches.V[s][il]
-        return (ops.e4m3_decode(K), ops.e4m3_decode(V)) if fp8 else (K, V)
+        if fp8:
+            return ops.e4m3_decode(K), ops.e4m3_decode(V)
+        if q8:
+            return ops.q8_kv_decode(K, hd), ops.q8_kv_decode(V, hd)
+        return K, V
     attn = np.stack([_attend(q[b], *kv(sessions[b]), pos[b] + 1, win)
                      for b in range(B)])                  # phase B: attend
     if gate is not None:   # every attention output element times sigmoid of its gate, before W_o

@@ -747,3 +747,70 @@ def test_gdn_special_cases_and_matrix_form():
     # zero state: the state becomes beta v k^T
     Sn, _ = oracle.gdn_step(np.zeros_like(S), q, k, v, g, beta, 1.0)
     np.testing.assert_allclose(Sn, beta[:, None, None] * v[:, :, None] * k[:, None, :], rtol=1e-15)
+
+
+# ---------------------------------------------------------------------------------------
+# int8 (Q8_0-block) KV cache codec
+# ---------------------------------------------------------------------------------------
+def test_q8_kv_hand_worked_row():
+    """One 64-value row by hand: block 0 has max |x| = 63.5, so d = 0.5 exactly and the codes
+    are x / 0.5 with ties away from zero; block 1 is all zero (scale 0, codes 0); 16 bytes of
+    padding follow the two fp16 scales."""
+    x = np.zeros(64, dtype=np.float32)
+    x[:6] = [63.5, -63.5, 0.75, -1.25, 0.2, 10.0]      # x / d = 127, -127, 1.5, -2.5, 0.4, 20
+    row = ops.q8_kv_encode(x)
+    assert row.shape == (80,) and ops.q8_kv_row_bytes(64) == 80
+    codes = row[:64].view(np.int8)
+    assert codes[:6].tolist() == [127, -127, 2, -3, 0, 20] and not codes[6:].any()
+    d = row[64:68].view(np.float16)
+    assert d[0] == np.float16(0.5) and d[1] == 0
+    assert not row[68:].any()
+    np.testing.assert_array_equal(ops.q8_kv_decode(row, 64)[:6], [63.5, -63.5, 1.0, -1.5, 0.0, 10.0])
+
+
+def test_q8_kv_scale_is_rounded_to_fp16_before_coding():
+    """The stored scale is fp16(max/127) and the codes divide by that stored value: for a block
+    with max 1.0 the scale is fp16(1/127) = 0.0078735..., and 1.0 / it = 127.0078 -> 127."""
+    x = np.linspace(-1.0, 1.0, 32, dtype=np.float32)
+    row = ops.q8_kv_encode(x)
+    d = row[32:34].view(np.float16)[0]
+    assert d == np.float16(np.float32(1.0) / np.float32(127.0))
+    q = row[:32].view(np.int8)
+    assert q[0] == -127 and q[-1] == 127
+    ref = np.clip(np.sign(x / np.float32(d)) * np.floor(np.abs(x / np.float32(d)) + 0.5), -127, 127)
+    np.testing.assert_array_equal(q, ref.astype(np.int8))
+
+
+def test_q8_kv_round_trip_bound_and_row_independence():
+    """Decoded values are within half a step of the input (d/2 per block, plus the scale's
+    fp16 rounding for the clamped maximum); rows code independently of one another."""
+    rng = np.random.default_rng(8)
+    x = (rng.standard_normal((5, 3, 128)) * np.exp(rng.uniform(-3, 3, (5, 3, 1)))).astype(np.float32)
+    rows = ops.q8_kv_encode(x)
+    y = ops.q8_kv_decode(rows, 128)
+    d = rows[..., 128:136].copy().view(np.float16).astype(np.float64)           # [5, 3, 4]
+    err = np.abs(y - x).reshape(5, 3, 4, 32)
+    amax = np.abs(x).reshape(5, 3, 4, 32).max(axis=3)
+    bound = np.maximum(d / 2, np.abs(amax - 127 * d))[..., None] * (1 + 1e-6)
+    assert np.all(err <= bound)
+    np.testing.assert_array_equal(ops.q8_kv_encode(x[2, 1]), rows[2, 1])
+
+
+def test_oracle_q8_step_appends_encoded_rows():
+    """A step of a stack with int8 caches writes, at each row's position, exactly the Q8 rows of
+    the k and v it computed (the trace's fp32 values), and leaves every other slot as it was."""
+    import dataclasses
+    spec = dataclasses.replace(TINY, kv_q8=True)
+    wl = _tiny_wl(spec, 98, [(0, 0), (1, 0)], [9, 30])
+    model = wlmod.make_model(spec, 98)
+    c = oracle.OracleCaches(wl)
+    assert c.K[0][0].shape == (spec.n_head_kv, wl.capacity, spec.head_dim + 16) and c.K[0][0].dtype == np.uint8
+    before = [[k.copy() for k in c.K[s]] for s in (0, 1)]
+    tr = []
+    oracle.decode_step(model, c, wlmod.step_inputs(wl, 0), [0, 1], wl.positions(0), trace=tr)
+    for s, p in ((0, 9), (1, 30)):
+        for il in range(spec.n_layers):
+            diff = np.any(c.K[s][il] != before[s][il], axis=(0, 2))
+            assert diff.nonzero()[0].tolist() == [p]
+            np.testing.assert_array_equal(c.K[s][il][:, p], ops.q8_kv_encode(tr[il]["k"][s].astype(np.float32)))
+            np.testing.assert_array_equal(c.V[s][il][:, p], ops.q8_kv_encode(tr[il]["v"][s].astype(np.float32)))

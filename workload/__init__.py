@@ -22,7 +22,8 @@ Storage conventions of the arrays produced here (both sides read them):
 * Q8_0 ``qs``: int8 ``[n_out, k]`` row-major; ``d``: fp16 ``[n_out, k/32]``.
 * Q4_0 ``qs``: uint8 ``[n_out, k/2]`` (16 bytes per 32-element block, the
   block's bytes contiguous); ``d``: fp16 ``[n_out, k/32]``.
-* KV prefill for one (session, layer): fp16 ``[G, L, hd]`` for K and for V.
+* KV prefill for one (session, layer): fp16 ``[G, L, hd]`` for K and for V (uint8 E4M3
+  codes of the same shape for FP8 caches; uint8 rows ``[G, L, hd + 16]`` for int8 caches).
 """
 from __future__ import annotations
 
@@ -73,6 +74,7 @@ class ModelSpec:
     qk_norm: bool = False                # per-head RMSNorm of q and k before RoPE
     attn_gate: bool = False              # attention output scaled by sigmoid of H hd more projection rows
     kv_fp8: bool = False                 # KV caches hold FP8 E4M3 codes (uint8) instead of fp16
+    kv_q8: bool = False                  # KV caches hold int8 rows (Q8_0 blocks: codes + fp16 scales)
 
     @property
     def qkv_rows(self) -> int:
@@ -262,6 +264,8 @@ def kv_prefill(wl: Workload, session: int, layer: int) -> Tuple[np.ndarray, np.n
     rv = rng_for(wl.seed, wl.code, T_V_PRE, layer, session)
     if sp.kv_fp8:
         return fp8_codes(rk, shape), fp8_codes(rv, shape)
+    if sp.kv_q8:
+        return q8_rows(rk, shape), q8_rows(rv, shape)
     k = rk.standard_normal(shape, dtype=np.float32).astype(np.float16)
     v = rv.standard_normal(shape, dtype=np.float32).astype(np.float16)
     return k, v
@@ -275,6 +279,19 @@ def fp8_codes(rng: np.random.Generator, shape) -> np.ndarray:
     expo = rng.integers(4, 9, size=shape, dtype=np.uint8) << 3
     mant = rng.integers(0, 8, size=shape, dtype=np.uint8)
     return (sign | expo | mant).astype(np.uint8)
+
+
+def q8_rows(rng: np.random.Generator, shape) -> np.ndarray:
+    """Random int8 cache rows ``[G, L, hd + 16]`` drawn field by field: int8 codes uniform in
+    [-127, 127] and, per 32-element block, an fp16 scale 1.7 / 127 times U(0.5, 1.5) (values
+    of about unit spread), then zero padding.  No conversion: the bytes are the inputs."""
+    G, L, hd = shape
+    codes = rng.integers(-127, 128, size=(G, L, hd), dtype=np.int8)
+    d = (np.float32(1.7 / 127.0) * rng.uniform(0.5, 1.5, size=(G, L, hd // 32)).astype(np.float32)).astype(np.float16)
+    out = np.zeros((G, L, hd + 16), dtype=np.uint8)
+    out[:, :, :hd] = codes.view(np.uint8)
+    out[:, :, hd:hd + 2 * (hd // 32)] = d.view(np.uint8).reshape(G, L, 2 * (hd // 32))
+    return out
 
 
 def kv_prefill_many(wl: Workload, pairs, threads: int = 8):
