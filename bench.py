@@ -18,8 +18,8 @@ Prints ONE JSON line with:
   read of its weight bytes (``mmvq_roofline`` repeats gate/up, the largest);
 * ``other_workloads``: the 8-layer Q8_0 stack with lm_head at B=1..8, the ragged B=16
   attention sublayer and its fa_decode, the MoE verify step (with its bytes counted over the
-  distinct experts its rows hit), the headline stack with FP8 E4M3 caches and its fa_decode,
-  the gated delta-rule state step;
+  distinct experts its rows hit), the headline stack with FP8 E4M3 caches and with int8
+  (Q8_0-row) caches and their fa_decode, the gated delta-rule state step;
 * ``cpu_baseline`` (the 32-layer stack at B=8) and ``cpu_baseline_configs`` (all five
   workloads at their headline widths): the oracle on the host cores, bounded samples;
 * ``platform``: GPU name, ROCm and HIP versions.
@@ -554,6 +554,26 @@ def other_workloads(stream, iters: int) -> dict:
                        iters, stream)
     fb = fa_algorithmic_bytes(t_kv, sp.n_head_kv, sp.n_head, sp.head_dim, kv_bytes=1)
     res["32-layer d=4096 32Q/8KV Q4_0, FP8 E4M3 KV caches, B=8 ctx 4096"] = {
+        "tok_s": round(wl.B / ms * 1e3, 1), "ms_per_step": round(ms, 4), "t_kv": t_kv,
+        "fa_us": round(us, 3), "fa_algorithmic_bytes": int(fb), "fa_GBs": round(fb / (us * 1e-6) / 1e9, 1),
+        "fa_frac": round(fb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    del gw
+    # the headline stack with int8 caches (Q8_0 rows), and its fa_decode
+    log("32-layer Q4_0 stack, int8 KV caches")
+    wl = dataclasses.replace(base, spec=dataclasses.replace(base.spec, kv_q8=True))
+    gw = GpuWorkload(wl, fill="device")
+    ms = _time_steps(gw, stream, iters, 3)
+    sp = wl.spec
+    t_kv = [p + 1 for p in wl.positions(0)]
+    kb = [gw.caches.k_ptr(wl.rows[b][0], 0) for b in range(wl.B)]
+    vb = [gw.caches.v_ptr(wl.rows[b][0], 0) for b in range(wl.B)]
+    ws = torch.zeros(kd.kd_fa_decode_workspace(wl.B, sp.n_head, sp.head_dim, t_kv), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    us = time_rotating(lambda i: kd.kd_fa_decode_ragged_q8(q, sp.n_head_kv, kb, vb, t_kv, wl.capacity,
+                                                          sp.head_dim ** -0.5, ws=ws, out=out, stream=stream),
+                       iters, stream)
+    fb = sum(t_kv) * sp.n_head_kv * (sp.head_dim + 16) * 2 + 2 * wl.B * sp.n_head * sp.head_dim * 4
+    res["32-layer d=4096 32Q/8KV Q4_0, int8 (Q8_0-row) KV caches, B=8 ctx 4096"] = {
         "tok_s": round(wl.B / ms * 1e3, 1), "ms_per_step": round(ms, 4), "t_kv": t_kv,
         "fa_us": round(us, 3), "fa_algorithmic_bytes": int(fb), "fa_GBs": round(fb / (us * 1e-6) / 1e9, 1),
         "fa_frac": round(fb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}

@@ -70,7 +70,7 @@ typedef enum {
 
 typedef enum { KD_FMT_Q8_0 = 1, KD_FMT_Q4_0 = 2, KD_FMT_F32 = 3 } kd_format;
 /* KV cache element formats (kd_model_desc.kv_format). */
-typedef enum { KD_KV_F16 = 0, KD_KV_FP8_E4M3 = 1 } kd_kv_format;
+typedef enum { KD_KV_F16 = 0, KD_KV_FP8_E4M3 = 1, KD_KV_Q8_0 = 2 } kd_kv_format;
 
 #define KD_MAX_B 16
 
@@ -232,6 +232,26 @@ kd_status kd_fa_decode_ragged_fp8(const float* q, int32_t B, int32_t H, int32_t 
                                   const int32_t* t_kv, int32_t capacity, float scale, float* out,
                                   void* ws, size_t ws_bytes, void* stream);
 
+/* int8 KV caches (memra-engine decode_batch.rs, phase A: the append stores quantised K/V rows,
+ * ``append_kv_quantized_seqs`` with per-token row bytes; Strata PR #1524 "What changes": resident
+ * int8 KV; the byte format is not given there).  Read here as Q8_0 blocks along each cached
+ * head row: a cache is uint8 [G][capacity][hd + 16]; row (g, j) holds hd int8 codes, then hd/32
+ * fp16 scales (one per 32 consecutive elements), then zeros.  A block's value i is d * q_i.
+ * kd_kv_append_q8 codes each block of the fp32 k and v rows: a = max |x_i|, d = fp16(a / 127)
+ * (fp32 division, round to nearest even), q_i = round-half-away(x_i / d) clamped to
+ * [-127, 127] (all 0 when d is 0); it writes the codes and scales, never the padding (a cache
+ * starts zeroed).  kd_fa_decode_ragged_q8 computes what kd_fa_decode_ragged computes on those
+ * values: scores on the codes with one fp32 sum per block, scaled by the block scales; values
+ * d q_i formed exactly in fp32 and carried as fp16 hi + lo (values within the fp16 range, as
+ * for fp16 caches); the same workspace (kd_fa_decode_workspace).  A sliding window is a view at
+ * k_base[b] + off (hd + 16) bytes. */
+kd_status kd_kv_append_q8(const float* k, const float* v, int32_t B, int32_t G, int32_t hd, void* const* k_base,
+                          void* const* v_base, const int32_t* pos, int32_t capacity, void* stream);
+kd_status kd_fa_decode_ragged_q8(const float* q, int32_t B, int32_t H, int32_t G, int32_t hd,
+                                 const void* const* k_base, const void* const* v_base, const int32_t* t_kv,
+                                 int32_t capacity, float scale, float* out, void* ws, size_t ws_bytes,
+                                 void* stream);
+
 /* ---- gated delta rule (linear-attention layers) -------------------------------------- */
 /* One decode step of the gated delta rule for B rows (memra-engine decode_batch.rs, the
  * Linear mixer of decode_batch_layers: one batched scan launch over every sequence's state,
@@ -303,9 +323,12 @@ typedef struct {
   const float* final_norm;               /* [d] or NULL */
   kd_weight lm_head;                     /* [vocab, d] or qs NULL */
   int32_t kv_format;                     /* KD_KV_F16 (fp16 caches, k_base/v_base [G][capacity][hd]
-                                            fp16) or KD_KV_FP8_E4M3 (uint8 codes, stored and read as
+                                            fp16), KD_KV_FP8_E4M3 (uint8 codes, stored and read as
                                             kd_kv_append_fp8 / kd_fa_decode_ragged_fp8, by either
-                                            wqkv layout) */
+                                            wqkv layout) or KD_KV_Q8_0 (int8 rows [G][capacity][hd + 16],
+                                            as kd_kv_append_q8 / kd_fa_decode_ragged_q8; a block of
+                                            32 spans one head's rows across workgroups of the fused
+                                            RoPE epilogue, so these models need wqkv_pair_rows = 0) */
 } kd_model_desc;
 
 typedef struct kd_model kd_model;

@@ -57,7 +57,7 @@ class KdModelDesc(C.Structure):
                 ("final_norm", C.c_void_p), ("lm_head", KdWeight), ("kv_format", C.c_int32)]
 
 
-KD_KV_F16, KD_KV_FP8_E4M3 = 0, 1
+KD_KV_F16, KD_KV_FP8_E4M3, KD_KV_Q8_0 = 0, 1, 2
 
 
 class KdStepTrace(C.Structure):
@@ -93,11 +93,13 @@ SIGNATURES = {
     "kd_verify_accept": (_I, [_P, _P, _I, _I, _P, _P, _P]),
     "kd_kv_append": (_I, [_P, _P, _I, _I, _I, _PP, _PP, _PI, _I, _P]),
     "kd_kv_append_fp8": (_I, [_P, _P, _I, _I, _I, _PP, _PP, _PI, _I, _P]),
+    "kd_kv_append_q8": (_I, [_P, _P, _I, _I, _I, _PP, _PP, _PI, _I, _P]),
     "kd_gdn_step": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _PP, _PP, _F, _P, _P]),
     "kd_fa_decode_workspace": (_S, [_I, _I, _I, _PI]),
     "kd_fa_decode_ragged": (_I, [_P, _I, _I, _I, _I, _PP, _PP, _PI, _I, _F, _P, _P, _S, _P]),
     "kd_fa_decode_ragged_noalloc": (_I, [_P, _I, _I, _I, _I, _PP, _PP, _PI, _I, _F, _P, _P]),
     "kd_fa_decode_ragged_fp8": (_I, [_P, _I, _I, _I, _I, _PP, _PP, _PI, _I, _F, _P, _P, _S, _P]),
+    "kd_fa_decode_ragged_q8": (_I, [_P, _I, _I, _I, _I, _PP, _PP, _PI, _I, _F, _P, _P, _S, _P]),
     "kd_model_create": (_I, [C.POINTER(KdModelDesc), C.POINTER(_P)]),
     "kd_model_destroy": (None, [_P]),
     "kd_decode_step_workspace": (_S, [_P, _I, _PI]),
@@ -486,6 +488,26 @@ def kd_kv_append_fp8(k: torch.Tensor, v: torch.Tensor, k_base: Sequence[int], v_
                                   capacity, _stream(stream)), "kd_kv_append_fp8")
 
 
+def kd_kv_append_q8(k: torch.Tensor, v: torch.Tensor, k_base: Sequence[int], v_base: Sequence[int],
+                    pos: Sequence[int], capacity: int, stream=None) -> None:
+    B, G, hd = k.shape
+    _check(lib().kd_kv_append_q8(k.data_ptr(), v.data_ptr(), B, G, hd, _ptrs(k_base), _ptrs(v_base), _i32(pos),
+                                 capacity, _stream(stream)), "kd_kv_append_q8")
+
+
+def kd_fa_decode_ragged_q8(q: torch.Tensor, G: int, k_base, v_base, t_kv, capacity: int, scale: float,
+                           ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                           stream=None) -> torch.Tensor:
+    B, H, hd = q.shape
+    out = torch.empty_like(q) if out is None else out
+    if ws is None:
+        ws = torch.empty(max(kd_fa_decode_workspace(B, H, hd, t_kv), 16), dtype=torch.uint8, device=q.device)
+    _check(lib().kd_fa_decode_ragged_q8(q.data_ptr(), B, H, G, hd, _ptrs(k_base), _ptrs(v_base), _i32(t_kv),
+                                        capacity, scale, out.data_ptr(), ws.data_ptr(), ws.numel(),
+                                        _stream(stream)), "kd_fa_decode_ragged_q8")
+    return out
+
+
 def kd_gdn_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
                 state_in: Sequence[int], state_out: Sequence[int], scale: float,
                 o: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
@@ -580,6 +602,7 @@ class KdModel:
             return t.data_ptr()
 
         kv_fp8 = bool(getattr(sp, "kv_fp8", False))   # E4M3 caches (kd_model_desc.kv_format)
+        kv_q8 = bool(getattr(sp, "kv_q8", False))     # int8 rows: the canonical wqkv layout
         for il, L in enumerate(model["layers"]):
             slot[0] = il
             D = self.layers[il]
@@ -590,7 +613,7 @@ class KdModel:
             D.k_norm = F(L["k_norm"]) if qk_norm else None
             D.attn_gate = 1 if L.get("attn_gate") else 0
             n_heads_qkv = sp.n_head + 2 * sp.n_head_kv + (sp.n_head if D.attn_gate else 0)
-            if fused and not qk_norm:   # QK-norm normalises whole heads: the canonical layout
+            if fused and not qk_norm and not kv_q8:   # QK-norm and int8 caches need whole heads: canonical
                 D.wqkv = W(rope_pair_rows(L["wqkv"], n_heads_qkv, sp.head_dim), "wqkv")
                 D.wqkv_pair_rows = 1
             else:
@@ -620,7 +643,7 @@ class KdModel:
         self.desc = KdModelDesc(sp.n_layers, sp.d, sp.n_head, sp.n_head_kv, sp.head_dim, sp.ffn, sp.n_experts,
                                 sp.n_expert_used, sp.expert_ffn, sp.shared_ffn, sp.vocab, sp.rope_base, sp.rms_eps,
                                 self.layers, F(model["final_norm"]) if model["final_norm"] is not None else None,
-                                empty, KD_KV_FP8_E4M3 if kv_fp8 else KD_KV_F16)
+                                empty, KD_KV_FP8_E4M3 if kv_fp8 else KD_KV_Q8_0 if kv_q8 else KD_KV_F16)
         slot[0] = sp.n_layers   # packed[n_layers] holds the output head
         if model["lm_head"] is not None:
             self.desc.lm_head = W(model["lm_head"], "lm_head")
@@ -686,13 +709,15 @@ class KdModel:
 
 class SessionCaches:
     """K/V caches of several sessions: one tensor [n_layers, 2, G, capacity, hd] per session,
-    fp16, or uint8 E4M3 codes with ``fp8=True``."""
+    fp16, or uint8 E4M3 codes with ``fp8=True``, or uint8 int8 rows [..., hd + 16] with
+    ``q8=True``."""
 
     def __init__(self, n_sessions: int, n_layers: int, G: int, capacity: int, hd: int, device="cuda",
-                 fp8: bool = False):
+                 fp8: bool = False, q8: bool = False):
         self.n_layers, self.G, self.capacity, self.hd = n_layers, G, capacity, hd
-        dt = torch.uint8 if fp8 else torch.float16
-        self.t = [torch.zeros((n_layers, 2, G, capacity, hd), dtype=dt, device=device)
+        dt = torch.uint8 if (fp8 or q8) else torch.float16
+        row = hd + 16 if q8 else hd
+        self.t = [torch.zeros((n_layers, 2, G, capacity, row), dtype=dt, device=device)
                   for _ in range(n_sessions)]
 
     def k_ptr(self, s: int, il: int) -> int:

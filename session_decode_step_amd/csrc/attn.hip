@@ -110,6 +110,19 @@ __device__ __forceinline__ int4 e4m3x8_to_f16x8(uint2 c) {
   return r;
 }
 
+// Eight int8 codes (in memory order) to eight fp16 values, exactly (|code| <= 127).
+__device__ __forceinline__ fa_v8h i8x8_to_f16x8(uint2 c) {
+  fa_v8h r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (_Float16)(float)(int8_t)(((e < 4 ? c.x : c.y) >> (8 * (e & 3))) & 0xFF);
+  return r;
+}
+// fp16 number j (0..3) of four packed in a uint2, as fp32.
+__device__ __forceinline__ float half_at(uint2 v, int j) {
+  const uint32_t w = j < 2 ? v.x : v.y;
+  return __half2float(__ushort_as_half((unsigned short)((j & 1) ? (w >> 16) : (w & 0xFFFF))));
+}
+
 // MULTI: chunks may span several 128-key tiles (rows longer than 128 x 128 keys).  Without
 // it the tile loop runs once, so the running output is not live across a tile's loads and
 // the kernel needs fewer registers (more workgroups per CU); the operations are the same.
@@ -117,9 +130,15 @@ __device__ __forceinline__ int4 e4m3x8_to_f16x8(uint2 c) {
 // MFMA's 16 columns.  Column h is head g R + h % R of the group's row h / R; each column
 // masks the keys at or past its own row's t_kv, so a row's partials are those of its own
 // pass (the keys it does not attend score -inf and weigh exactly 0).
-// F8: the caches hold E4M3 codes; each lane loads 8 codes where it loads 8 fp16 values
-// otherwise and widens them exactly, so every product sees the same operands.
-template <int R, int HD, bool MULTI, int C, bool F8>
+// KF (kd_kv_format): KD_KV_F16 fp16 caches; KD_KV_FP8_E4M3: the caches hold E4M3 codes, each
+// lane loads 8 codes where it loads 8 fp16 values otherwise and widens them exactly, so every
+// product sees the same operands; KD_KV_Q8_0: int8 rows (Q8_0 blocks of 32 along the head row,
+// one fp16 scale each, rows of HD + 16 bytes).  For int8 rows the score product runs on the
+// codes (exact in fp16) with one accumulator per 32-dim slice -- one block -- and each key's
+// slice sums are scaled by its block scales in fp32, in slice order; the values are the codes
+// times their block scale (exact in fp32), split into fp16 hi + lo like p, and the output
+// product is issued for p_hi v_hi, p_lo v_hi and p_hi v_lo.
+template <int R, int HD, bool MULTI, int C, int KF>
 __global__ __launch_bounds__(64 * kFaWaves) void fa_split_kernel(FaPlan p, const float* __restrict__ q,
                                                                           int ldq, RowCaches rc, int capacity,
                                                                           float scale, float* __restrict__ ws) {
@@ -186,12 +205,15 @@ __global__ __launch_bounds__(64 * kFaWaves) void fa_split_kernel(FaPlan p, const
   __shared__ float qun[16];
   __shared__ float alpha_s[2][16];
 
-  constexpr uint32_t ES = F8 ? 1 : 2;  // bytes per cache element
-  const char* Kg = static_cast<const char*>(kbase) + (size_t)g * capacity * HD * ES;
-  const char* Vg = static_cast<const char*>(vbase) + (size_t)g * capacity * HD * ES;
+  constexpr bool F8 = KF == KD_KV_FP8_E4M3;
+  constexpr bool Q8 = KF == KD_KV_Q8_0;
+  constexpr uint32_t ES = KF == KD_KV_F16 ? 2 : 1;  // bytes per cache element
+  constexpr uint32_t RS = kv_row_bytes(KF, HD);      // bytes per cached key (one head)
+  const char* Kg = static_cast<const char*>(kbase) + (size_t)g * capacity * RS;
+  const char* Vg = static_cast<const char*>(vbase) + (size_t)g * capacity * RS;
   // descriptors end at key k1: keys past the chunk read zeros, so offsets are base + constants
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg, (uint32_t)k1 * HD * ES);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg, (uint32_t)k1 * HD * ES);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kg, (uint32_t)k1 * RS);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vg, (uint32_t)k1 * RS);
 
   // q of the heads this wave stages (w, w + 8), fetched before any K/V load so that waiting
   // for it never waits for the tile's K/V bytes (loads complete in issue order)
@@ -220,26 +242,36 @@ __global__ __launch_bounds__(64 * kFaWaves) void fa_split_kernel(FaPlan p, const
   for (int t0 = 0, par = 0; t0 < (MULTI ? nk : 1); t0 += TK, par ^= 1) {
     const int wk = t0 + 16 * w;  // this wave's first key within the chunk
     // K: slice j -> key wk + n, dims 32j + 8gq (8 elements)
-    const uint32_t kb = ((uint32_t)(k0 + wk + n) * HD + 8 * gq) * ES;
+    const uint32_t kb = (uint32_t)(k0 + wk + n) * RS + 8 * gq * ES;
     int4 kr[NC];
     uint2 k8[NC];
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
-      if constexpr (F8)
+      if constexpr (F8 || Q8)
         k8[j] = buf8<kKvAux>(rk, kb + j * 32);
       else
         kr[j] = buf16<kKvAux>(rk, kb + j * 64);
     }
+    // int8 rows: the block scales of the keys this lane's scores belong to (wk + 4gq + s)
+    uint2 ksc[4];
+    if constexpr (Q8) {
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) ksc[s2] = buf8<kKvAux>(rk, (uint32_t)(k0 + wk + 4 * gq + s2) * RS + HD);
+    }
     // V: key wk + 4gq + t, dims 8n .. 8n+7 (lanes with 8n >= HD read bytes whose outputs are dropped)
-    const uint32_t vb0 = ((uint32_t)(k0 + wk + 4 * gq) * HD + 8 * n) * ES;
+    const uint32_t vb0 = (uint32_t)(k0 + wk + 4 * gq) * RS + 8 * n * ES;
     int4 vr[4];
     uint2 v8[4];
+    uint32_t vsc[4];  // int8 rows: the scale pair holding block (8n)/32 of key wk + 4gq + t
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      if constexpr (F8)
-        v8[t] = buf8<kKvAux>(rv, vb0 + t * HD);
+      if constexpr (F8 || Q8)
+        v8[t] = buf8<kKvAux>(rv, vb0 + t * RS);
       else
-        vr[t] = buf16<kKvAux>(rv, vb0 + t * HD * 2);
+        vr[t] = buf16<kKvAux>(rv, vb0 + t * RS);
+      if constexpr (Q8)
+        vsc[t] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+            rv, (uint32_t)(k0 + wk + 4 * gq + t) * RS + HD + 4 * (n / 8), 0, kKvAux);
     }
     __builtin_amdgcn_sched_barrier(0);  // every K and V load of the tile ahead of the math
     if (t0 == 0) {
@@ -273,13 +305,33 @@ __global__ __launch_bounds__(64 * kFaWaves) void fa_split_kernel(FaPlan p, const
 
     // scores of keys wk + 4gq + s, head n (base 2)
     fa_v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (Q8) {
+      // one accumulator per slice (= block), then the keys' block scales in slice order
+      fa_v4f accj[NC];
 #pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      const fa_v8h kv = __builtin_bit_cast(fa_v8h, F8 ? e4m3x8_to_f16x8(k8[j]) : kr[j]);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, *reinterpret_cast<const fa_v8h*>(&qlds[0][j][n][8 * gq]), acc,
-                                                   0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, *reinterpret_cast<const fa_v8h*>(&qlds[1][j][n][8 * gq]), acc,
-                                                   0, 0, 0);
+      for (int j = 0; j < NC; ++j) {
+        const fa_v8h kv = i8x8_to_f16x8(k8[j]);
+        accj[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, *reinterpret_cast<const fa_v8h*>(&qlds[0][j][n][8 * gq]),
+                                                         fa_v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+        accj[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, *reinterpret_cast<const fa_v8h*>(&qlds[1][j][n][8 * gq]),
+                                                         accj[j], 0, 0, 0);
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) {
+        float v = half_at(ksc[s2], 0) * accj[0][s2];
+#pragma unroll
+        for (int j = 1; j < NC; ++j) v = fmaf(half_at(ksc[s2], j), accj[j][s2], v);
+        acc[s2] = v;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        const fa_v8h kv = __builtin_bit_cast(fa_v8h, F8 ? e4m3x8_to_f16x8(k8[j]) : kr[j]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, *reinterpret_cast<const fa_v8h*>(&qlds[0][j][n][8 * gq]), acc,
+                                                     0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv, *reinterpret_cast<const fa_v8h*>(&qlds[1][j][n][8 * gq]), acc,
+                                                     0, 0, 0);
+      }
     }
     const float qunscale = qun[n];
     float pv[4];
@@ -326,13 +378,35 @@ __global__ __launch_bounds__(64 * kFaWaves) void fa_split_kernel(FaPlan p, const
 #pragma unroll
       for (int t = 0; t < 4; ++t) vr[t] = e4m3x8_to_f16x8(v8[t]);
     }
+    if constexpr (Q8) {
+      // values = codes times their block scale (exact in fp32), as fp16 hi + lo
+      float dv[4];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      fa_v4h vb;
+      for (int t = 0; t < 4; ++t) dv[t] = __half2float(__ushort_as_half((unsigned short)(((n / 4) & 1) ? (vsc[t] >> 16) : (vsc[t] & 0xFFFF))));
 #pragma unroll
-      for (int t = 0; t < 4; ++t) vb[t] = __builtin_bit_cast(fa_v8h, vr[t])[m];
-      o[m] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, vb, o[m], 0, 0, 0);
-      o[m] = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, vb, o[m], 0, 0, 0);
+      for (int m = 0; m < 8; ++m) {
+        fa_v4h vh, vl;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float x = dv[t] * (float)(int8_t)((m < 4 ? (v8[t].x >> (8 * m)) : (v8[t].y >> (8 * (m - 4)))) & 0xFF);
+          _Float16 hi, lo;
+          split_f16(x, hi, lo);
+          vh[t] = hi;
+          vl[t] = lo;
+        }
+        o[m] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, vh, o[m], 0, 0, 0);
+        o[m] = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, vh, o[m], 0, 0, 0);
+        o[m] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, vl, o[m], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        fa_v4h vb;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) vb[t] = __builtin_bit_cast(fa_v8h, vr[t])[m];
+        o[m] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, vb, o[m], 0, 0, 0);
+        o[m] = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, vb, o[m], 0, 0, 0);
+      }
     }
   }
 
@@ -501,7 +575,7 @@ __global__ __launch_bounds__(HD) void fa_combine_kernel(FaPlan p, const float* _
   }
 }
 
-template <int R, int HD, int C, bool F8>
+template <int R, int HD, int C, int F8>
 static void launch_fa_c(const FaPlan& p, const float* q, int ldq, const RowCaches& rc, int capacity, float scale,
                         void* ws, hipStream_t st) {
   int cmax = 0;
@@ -526,17 +600,22 @@ static void launch_combine(const FaPlan& p, const float* ws, float* out, int8_t*
 
 template <int R, int HD>
 static void launch_fa_t(const FaPlan& p, const float* q, int ldq, const RowCaches& rc, int capacity, float scale,
-                        float* out, int8_t* oq, float* od, void* ws, hipStream_t st, const float* gate, bool f8) {
-  if (f8) {
+                        float* out, int8_t* oq, float* od, void* ws, hipStream_t st, const float* gate, int kvf) {
+  if (kvf == KD_KV_FP8_E4M3) {
     if (p.max_grp > 1)
-      launch_fa_c<R, HD, kFaGroupCols, true>(p, q, ldq, rc, capacity, scale, ws, st);
+      launch_fa_c<R, HD, kFaGroupCols, KD_KV_FP8_E4M3>(p, q, ldq, rc, capacity, scale, ws, st);
     else
-      launch_fa_c<R, HD, R, true>(p, q, ldq, rc, capacity, scale, ws, st);
+      launch_fa_c<R, HD, R, KD_KV_FP8_E4M3>(p, q, ldq, rc, capacity, scale, ws, st);
+  } else if (kvf == KD_KV_Q8_0) {
+    if (p.max_grp > 1)
+      launch_fa_c<R, HD, kFaGroupCols, KD_KV_Q8_0>(p, q, ldq, rc, capacity, scale, ws, st);
+    else
+      launch_fa_c<R, HD, R, KD_KV_Q8_0>(p, q, ldq, rc, capacity, scale, ws, st);
   } else {
     if (p.max_grp > 1)
-      launch_fa_c<R, HD, kFaGroupCols, false>(p, q, ldq, rc, capacity, scale, ws, st);
+      launch_fa_c<R, HD, kFaGroupCols, KD_KV_F16>(p, q, ldq, rc, capacity, scale, ws, st);
     else
-      launch_fa_c<R, HD, R, false>(p, q, ldq, rc, capacity, scale, ws, st);
+      launch_fa_c<R, HD, R, KD_KV_F16>(p, q, ldq, rc, capacity, scale, ws, st);
   }
   int smax = 0;
   for (int b = 0; b < p.B; ++b) smax = std::max(smax, (int)(p.split_off[b + 1] - p.split_off[b]));
@@ -584,12 +663,12 @@ static void fa_group_rows(FaPlan& p, const RowCaches& rc) {
 }
 
 void launch_fa(const FaPlan& plan, const float* q, int ldq, const RowCaches& rc, int capacity, float scale, float* out,
-               int8_t* out_qs, float* out_d, void* ws, hipStream_t st, const float* gate, bool kv_fp8) {
+               int8_t* out_qs, float* out_d, void* ws, hipStream_t st, const float* gate, int kv_fmt) {
   FaPlan p = plan;
   fa_group_rows(p, rc);
   const int R = p.H / p.G;
 #define KD_FA_CASE(RR, HH) \
-  if (R == RR && p.hd == HH) return launch_fa_t<RR, HH>(p, q, ldq, rc, capacity, scale, out, out_qs, out_d, ws, st, gate, kv_fp8);
+  if (R == RR && p.hd == HH) return launch_fa_t<RR, HH>(p, q, ldq, rc, capacity, scale, out, out_qs, out_d, ws, st, gate, kv_fmt);
   KD_FA_CASE(1, 64) KD_FA_CASE(2, 64) KD_FA_CASE(4, 64) KD_FA_CASE(8, 64)
   KD_FA_CASE(1, 128) KD_FA_CASE(2, 128) KD_FA_CASE(4, 128) KD_FA_CASE(8, 128)
 #undef KD_FA_CASE
@@ -654,7 +733,7 @@ static kd_status fa_scratch(const char* who, void** out) {
 static kd_status fa_run(const char* who, const float* q, int32_t B, int32_t H, int32_t G, int32_t hd,
                         const void* const* k_base, const void* const* v_base, const int32_t* t_kv, int32_t capacity,
                         float scale, float* out, int32_t chunk, void* ws, size_t ws_bytes, void* stream,
-                        bool kv_fp8 = false, bool use_scratch = false) {
+                        int kv_fmt = KD_KV_F16, bool use_scratch = false) {
   kd_status s = fa_check(who, q, B, H, G, hd, k_base, v_base, t_kv, out);
   if (s != KD_OK) return s;
   for (int b = 0; b < B; ++b)
@@ -679,7 +758,7 @@ static kd_status fa_run(const char* who, const float* q, int32_t B, int32_t H, i
     rc.v[b] = const_cast<void*>(v_base[b]);
     rc.pos[b] = t_kv[b] - 1;
   }
-  launch_fa(p, q, H * hd, rc, capacity, scale, out, nullptr, nullptr, ws, as_stream(stream), nullptr, kv_fp8);
+  launch_fa(p, q, H * hd, rc, capacity, scale, out, nullptr, nullptr, ws, as_stream(stream), nullptr, kv_fmt);
   return check_launch(who);
 }
 
@@ -706,7 +785,7 @@ extern "C" kd_status kd_fa_decode_ragged_noalloc(const float* q, int32_t B, int3
                                                  const int32_t* t_kv, int32_t capacity, float scale, float* out,
                                                  void* stream) {
   return fa_run("kd_fa_decode_ragged_noalloc", q, B, H, G, hd, k_base, v_base, t_kv, capacity, scale, out, 0, nullptr,
-                0, stream, false, true);
+                0, stream, KD_KV_F16, true);
 }
 
 extern "C" kd_status kd_fa_decode_ragged(const float* q, int32_t B, int32_t H, int32_t G, int32_t hd,
@@ -722,7 +801,15 @@ extern "C" kd_status kd_fa_decode_ragged_fp8(const float* q, int32_t B, int32_t 
                                              const int32_t* t_kv, int32_t capacity, float scale, float* out, void* ws,
                                              size_t ws_bytes, void* stream) {
   return fa_run("kd_fa_decode_ragged_fp8", q, B, H, G, hd, k_base, v_base, t_kv, capacity, scale, out, 0, ws,
-                ws_bytes, stream, true);
+                ws_bytes, stream, KD_KV_FP8_E4M3);
+}
+
+extern "C" kd_status kd_fa_decode_ragged_q8(const float* q, int32_t B, int32_t H, int32_t G, int32_t hd,
+                                            const void* const* k_base, const void* const* v_base, const int32_t* t_kv,
+                                            int32_t capacity, float scale, float* out, void* ws, size_t ws_bytes,
+                                            void* stream) {
+  return fa_run("kd_fa_decode_ragged_q8", q, B, H, G, hd, k_base, v_base, t_kv, capacity, scale, out, 0, ws,
+                ws_bytes, stream, KD_KV_Q8_0);
 }
 
 extern "C" kd_status kd_debug_fa_decode_chunked(const float* q, int32_t B, int32_t H, int32_t G, int32_t hd,
@@ -736,7 +823,7 @@ extern "C" kd_status kd_debug_fa_decode_chunked(const float* q, int32_t B, int32
 
 static kd_status kv_append_run(const char* who, const float* k, const float* v, int32_t B, int32_t G, int32_t hd,
                                void* const* k_base, void* const* v_base, const int32_t* pos, int32_t capacity,
-                               void* stream, bool kv_fp8) {
+                               void* stream, int kv_fmt) {
   KD_REQUIRE(B >= 1 && B <= KD_MAX_B, KD_ERR_UNSUPPORTED, "%s: B=%d outside [1,16]", who, B);
   KD_REQUIRE(G > 0 && hd > 0, KD_ERR_INVALID, "%s: G=%d hd=%d", who, G, hd);
   KD_REQUIRE(hd == 64 || hd == 128, KD_ERR_UNSUPPORTED, "%s: hd=%d not 64 or 128", who, hd);
@@ -754,18 +841,24 @@ static kd_status kv_append_run(const char* who, const float* k, const float* v, 
     rc.v[b] = v_base[b];
     rc.pos[b] = pos[b];
   }
-  launch_kv_append(k, v, B, G, hd, rc, capacity, as_stream(stream), kv_fp8);
+  launch_kv_append(k, v, B, G, hd, rc, capacity, as_stream(stream), kv_fmt);
   return check_launch(who);
 }
 
 extern "C" kd_status kd_kv_append(const float* k, const float* v, int32_t B, int32_t G, int32_t hd,
                                   void* const* k_base, void* const* v_base, const int32_t* pos, int32_t capacity,
                                   void* stream) {
-  return kv_append_run("kd_kv_append", k, v, B, G, hd, k_base, v_base, pos, capacity, stream, false);
+  return kv_append_run("kd_kv_append", k, v, B, G, hd, k_base, v_base, pos, capacity, stream, KD_KV_F16);
 }
 
 extern "C" kd_status kd_kv_append_fp8(const float* k, const float* v, int32_t B, int32_t G, int32_t hd,
                                       void* const* k_base, void* const* v_base, const int32_t* pos,
                                       int32_t capacity, void* stream) {
-  return kv_append_run("kd_kv_append_fp8", k, v, B, G, hd, k_base, v_base, pos, capacity, stream, true);
+  return kv_append_run("kd_kv_append_fp8", k, v, B, G, hd, k_base, v_base, pos, capacity, stream, KD_KV_FP8_E4M3);
+}
+
+extern "C" kd_status kd_kv_append_q8(const float* k, const float* v, int32_t B, int32_t G, int32_t hd,
+                                     void* const* k_base, void* const* v_base, const int32_t* pos, int32_t capacity,
+                                     void* stream) {
+  return kv_append_run("kd_kv_append_q8", k, v, B, G, hd, k_base, v_base, pos, capacity, stream, KD_KV_Q8_0);
 }

@@ -258,13 +258,21 @@ void launch_rope_table(const RowCaches& rc, int B, int hd, float base, float* cs
 // Rotates q (in place, rows of qkv with stride ldqkv) and k, rounds k and v to fp16 and
 // stores them at each row's position (append) or only rotates (q and k heads).  cs is the
 // per-step table, or null to evaluate cos/sin inline with the same fp64 expression.
-// kv_fp8: the caches hold FP8 E4M3 codes (f32_to_e4m3) instead of fp16.
+// kv_fmt (kd_kv_format): the caches hold fp16 values, FP8 E4M3 codes (f32_to_e4m3) or int8 rows
+// (kv_q8_row_bytes per (head, position): Q8_0 blocks, see q8_store_pair).
 void launch_rope_append(float* qkv, int ldqkv, int B, int H, int G, int hd, const float* cs,
                         const RowCaches& rc, int capacity, bool append, hipStream_t st, float base,
                         const float* q_norm = nullptr, const float* k_norm = nullptr, float eps = 0.0f,
-                        bool kv_fp8 = false);
+                        int kv_fmt = KD_KV_F16);
 void launch_kv_append(const float* k, const float* v, int B, int G, int hd, const RowCaches& rc, int capacity,
-                      hipStream_t st, bool kv_fp8 = false);
+                      hipStream_t st, int kv_fmt = KD_KV_F16);
+// Bytes of one cached (KV head, position) row of an int8 cache: hd codes, hd/32 fp16 scales,
+// zero padding to hd + 16.
+__host__ __device__ constexpr int kv_q8_row_bytes(int hd) { return hd + 16; }
+// Bytes between consecutive positions of one KV head's row stream, per cache format.
+__host__ __device__ constexpr int kv_row_bytes(int kv_fmt, int hd) {
+  return kv_fmt == KD_KV_Q8_0 ? kv_q8_row_bytes(hd) : kv_fmt == KD_KV_FP8_E4M3 ? hd : 2 * hd;
+}
 
 struct FaPlan {
   int B, H, G, hd;
@@ -293,10 +301,11 @@ size_t fa_workspace_bytes(const FaPlan& p);
 // writes the quantised output rows.
 // gate (optional, row stride ldq like q): every output element is multiplied by
 // sigmoid(gate) before it is written and quantised.
-// kv_fp8: the caches hold FP8 E4M3 codes, widened to fp16 (exactly) as they are loaded.
+// kv_fmt: fp16 caches; FP8 E4M3 codes, widened to fp16 (exactly) as they are loaded; or int8
+// rows (codes widened exactly, block scales applied in fp32).
 void launch_fa(const FaPlan& p, const float* q, int ldq, const RowCaches& rc, int capacity, float scale,
                float* out, int8_t* out_qs, float* out_d, void* ws, hipStream_t st, const float* gate = nullptr,
-               bool kv_fp8 = false);
+               int kv_fmt = KD_KV_F16);
 bool fa_shape_supported(int H, int G, int hd);
 int fa_max_keys();
 

@@ -100,6 +100,40 @@ void launch_rope_table(const RowCaches& rc, int B, int hd, float base, float* cs
   rope_table_kernel<<<ceil_div(total, 256), 256, 0, st>>>(rc, B, hd, (double)base, cs);
 }
 
+// int8 cache rows (Q8_0 blocks along the head row): thread i of a block of hd/2 threads holds
+// elements i and i + hd/2 of one (head, position) row, so the 32-element block of each lies in
+// its half of the threads (lanes 0..31 or 32..63 of the wave).  Per block a = max |x|, the
+// stored scale d = fp16(a / 127), codes round-half-away(x / d) clamped to [-127, 127] (0 when
+// d is 0); codes at bytes [0, hd) of the row, scales at [hd, hd + hd/16).  Every thread of the
+// block must call it (the maxima are 32-lane shuffles).
+__device__ __forceinline__ void q8_store_pair(uint8_t* row, int hd, int i, float x0, float x1) {
+  const int half = hd / 2;
+  float m0 = fabsf(x0), m1 = fabsf(x1);
+#pragma unroll
+  for (int mask = 16; mask >= 1; mask >>= 1) {
+    m0 = fmaxf(m0, __shfl_xor(m0, mask, 32));
+    m1 = fmaxf(m1, __shfl_xor(m1, mask, 32));
+  }
+  const __half d0 = __float2half_rn(m0 / 127.0f), d1 = __float2half_rn(m1 / 127.0f);
+  const float f0 = __half2float(d0), f1 = __half2float(d1);
+  int c0 = 0, c1 = 0;
+  if (f0 != 0.0f) {
+    c0 = (int)roundf(x0 / f0);
+    c0 = c0 > 127 ? 127 : (c0 < -127 ? -127 : c0);
+  }
+  if (f1 != 0.0f) {
+    c1 = (int)roundf(x1 / f1);
+    c1 = c1 > 127 ? 127 : (c1 < -127 ? -127 : c1);
+  }
+  row[i] = (uint8_t)(int8_t)c0;
+  row[i + half] = (uint8_t)(int8_t)c1;
+  __half* sc = reinterpret_cast<__half*>(row + hd);
+  if ((i & 31) == 0) {
+    sc[i / 32] = d0;
+    sc[(i + half) / 32] = d1;
+  }
+}
+
 // grid (H + 2G, B); block hd/2 threads.  Head index h < H: query (rotate in place);
 // H <= h < H+G: key (rotate, store fp16); h >= H+G: value (store fp16).  cs is the per-step
 // table, or null to evaluate the same fp64 expression inline.
@@ -130,7 +164,10 @@ __global__ void rope_append_kernel(float* __restrict__ qkv, int ldqkv, int H, in
     const float y1 = fmaf(x0, s, x1 * c);
     row[i] = y0;
     row[i + half] = y1;
-    if (h >= H && append) {
+    if (h >= H && append == 3) {
+      q8_store_pair(static_cast<uint8_t*>(rc.k[b]) + ((size_t)(h - H) * capacity + pos) * kv_q8_row_bytes(hd), hd, i,
+                    y0, y1);
+    } else if (h >= H && append) {
       const size_t o = ((size_t)(h - H) * capacity + pos) * hd;
       if (append == 2) {
         uint8_t* K = static_cast<uint8_t*>(rc.k[b]) + o;
@@ -142,6 +179,9 @@ __global__ void rope_append_kernel(float* __restrict__ qkv, int ldqkv, int H, in
         K[i + half] = __float2half_rn(y1);
       }
     }
+  } else if (append == 3) {
+    q8_store_pair(static_cast<uint8_t*>(rc.v[b]) + ((size_t)(h - H - G) * capacity + pos) * kv_q8_row_bytes(hd), hd,
+                  i, row[i], row[i + half]);
   } else if (append) {
     const size_t o = ((size_t)(h - H - G) * capacity + pos) * hd;
     if (append == 2) {
@@ -158,10 +198,11 @@ __global__ void rope_append_kernel(float* __restrict__ qkv, int ldqkv, int H, in
 
 void launch_rope_append(float* qkv, int ldqkv, int B, int H, int G, int hd, const float* cs, const RowCaches& rc,
                         int capacity, bool append, hipStream_t st, float base, const float* q_norm,
-                        const float* k_norm, float eps, bool kv_fp8) {
+                        const float* k_norm, float eps, int kv_fmt) {
   dim3 grid(append ? H + 2 * G : H + G, B);
-  rope_append_kernel<<<grid, hd / 2, 0, st>>>(qkv, ldqkv, H, G, hd, cs, (double)base, rc, capacity,
-                                              append ? (kv_fp8 ? 2 : 1) : 0, q_norm, k_norm, eps);
+  const int mode = !append ? 0 : kv_fmt == KD_KV_Q8_0 ? 3 : kv_fmt == KD_KV_FP8_E4M3 ? 2 : 1;
+  rope_append_kernel<<<grid, hd / 2, 0, st>>>(qkv, ldqkv, H, G, hd, cs, (double)base, rc, capacity, mode, q_norm,
+                                              k_norm, eps);
 }
 
 // Plain KV append (no rotation): k and v rows [B][G][hd] fp32 -> fp16 (or E4M3 codes) at pos.
@@ -182,8 +223,23 @@ __global__ void kv_append_kernel(const float* __restrict__ k, const float* __res
   }
 }
 
+// int8 rows: grid (G, B), hd/2 threads, thread i codes elements i and i + hd/2 of k and of v.
+__global__ void kv_append_q8_kernel(const float* __restrict__ k, const float* __restrict__ v, int G, int hd,
+                                    RowCaches rc, int capacity) {
+  const int g = blockIdx.x, b = blockIdx.y, i = threadIdx.x, half = hd / 2;
+  const size_t src = ((size_t)b * G + g) * hd;
+  const size_t o = ((size_t)g * capacity + rc.pos[b]) * kv_q8_row_bytes(hd);
+  q8_store_pair(static_cast<uint8_t*>(rc.k[b]) + o, hd, i, k[src + i], k[src + i + half]);
+  q8_store_pair(static_cast<uint8_t*>(rc.v[b]) + o, hd, i, v[src + i], v[src + i + half]);
+}
+
 void launch_kv_append(const float* k, const float* v, int B, int G, int hd, const RowCaches& rc, int capacity,
-                      hipStream_t st, bool kv_fp8) {
+                      hipStream_t st, int kv_fmt) {
+  if (kv_fmt == KD_KV_Q8_0) {
+    kv_append_q8_kernel<<<dim3(G, B), hd / 2, 0, st>>>(k, v, G, hd, rc, capacity);
+    return;
+  }
+  const bool kv_fp8 = kv_fmt == KD_KV_FP8_E4M3;
   if (kv_fp8)
     kv_append_kernel<true><<<dim3(G, B), 64, 0, st>>>(k, v, G, hd, rc, capacity);
   else

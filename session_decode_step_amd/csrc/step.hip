@@ -94,7 +94,7 @@ extern "C" kd_status kd_model_create(const kd_model_desc* desc, kd_model** out) 
              "kd_model_create: H=%d G=%d hd=%d unsupported (H/G in {1,2,4,8}, hd in {64,128})", m.n_head, m.n_head_kv,
              m.head_dim);
   KD_REQUIRE(m.rms_eps > 0 && m.rope_base > 0, KD_ERR_INVALID, "kd_model_create: eps / rope base");
-  KD_REQUIRE(m.kv_format == KD_KV_F16 || m.kv_format == KD_KV_FP8_E4M3, KD_ERR_INVALID,
+  KD_REQUIRE(m.kv_format == KD_KV_F16 || m.kv_format == KD_KV_FP8_E4M3 || m.kv_format == KD_KV_Q8_0, KD_ERR_INVALID,
              "kd_model_create: kv_format=%d", m.kv_format);
   const int H = m.n_head, G = m.n_head_kv, hd = m.head_dim, d = m.d;
   const bool moe = m.n_experts > 0;
@@ -115,6 +115,8 @@ extern "C" kd_status kd_model_create(const kd_model_desc* desc, kd_model** out) 
     KD_REQUIRE(!L.q_norm == !L.k_norm, KD_ERR_INVALID, "kd_model_create: layer %d: q_norm and k_norm go together", il);
     KD_REQUIRE(!L.q_norm || L.wqkv_pair_rows == 0, KD_ERR_UNSUPPORTED,
                "kd_model_create: layer %d: QK-norm needs the canonical wqkv layout (wqkv_pair_rows = 0)", il);
+    KD_REQUIRE(m.kv_format != KD_KV_Q8_0 || L.wqkv_pair_rows == 0, KD_ERR_UNSUPPORTED,
+               "kd_model_create: layer %d: int8 KV caches need the canonical wqkv layout (wqkv_pair_rows = 0)", il);
     KD_REQUIRE(L.attn_gate == 0 || L.attn_gate == 1, KD_ERR_INVALID, "kd_model_create: layer %d: attn_gate=%d", il,
                L.attn_gate);
     KD_TRY(check_weight("wqkv", il, L.wqkv, (H + 2 * G + (L.attn_gate ? H : 0)) * hd, d));
@@ -320,8 +322,9 @@ static kd_status decode_step_impl(const kd_model* m, int32_t B, const float* x_i
   const bool moe = d.n_experts > 0;
   const bool has_ffn = d.ffn > 0 || moe;
   const float scale = 1.0f / sqrtf((float)hd);
-  const bool kv8 = d.kv_format == KD_KV_FP8_E4M3;  // caches hold E4M3 codes
-  const size_t kv_es = kv8 ? 1 : 2;               // bytes per cache element
+  const int kvf = d.kv_format;
+  const bool kv8 = kvf == KD_KV_FP8_E4M3;                // caches hold E4M3 codes
+  const size_t kv_rs = (size_t)kv_row_bytes(kvf, hd);   // bytes per cached position of one head
   const int ldqkv = (2 * H + 2 * G) * hd;  // room for the gate rows of gated layers
 
   RowCaches rc = {};
@@ -366,7 +369,7 @@ static kd_status decode_step_impl(const kd_model* m, int32_t B, const float* x_i
     } else {
       launch_mmvq(Ly.wqkv, s.act_qs, s.act_d, B, s.qkv, ldqkv, st);
       launch_rope_append(s.qkv, ldqkv, B, H, G, hd, s.cs, rc, capacity, true, st, d.rope_base, Ly.q_norm, Ly.k_norm,
-                         d.rms_eps, kv8);
+                         d.rms_eps, kvf);
     }
     // gated layers: the gate rows follow v in the projection's output row (same stride)
     const float* gate = Ly.attn_gate ? s.qkv + (size_t)(H + 2 * G) * hd : nullptr;
@@ -378,14 +381,14 @@ static kd_status decode_step_impl(const kd_model* m, int32_t B, const float* x_i
       for (int b = 0; b < B; ++b) {
         const int len = pos[b] + 1, off = len > Ly.swa_window ? len - Ly.swa_window : 0;
         tw[b] = len - off;
-        rw.k[b] = static_cast<char*>(rc.k[b]) + (size_t)off * hd * kv_es;
-        rw.v[b] = static_cast<char*>(rc.v[b]) + (size_t)off * hd * kv_es;
+        rw.k[b] = static_cast<char*>(rc.k[b]) + (size_t)off * kv_rs;
+        rw.v[b] = static_cast<char*>(rc.v[b]) + (size_t)off * kv_rs;
       }
       FaPlan pw;
       fa_make_plan(pw, B, H, G, hd, tw, 0);
-      launch_fa(pw, s.qkv, ldqkv, rw, capacity, scale, s.attn, s.act_qs, s.act_d, s.fa_ws, st, gate, kv8);
+      launch_fa(pw, s.qkv, ldqkv, rw, capacity, scale, s.attn, s.act_qs, s.act_d, s.fa_ws, st, gate, kvf);
     } else {
-      launch_fa(plan, s.qkv, ldqkv, rc, capacity, scale, s.attn, s.act_qs, s.act_d, s.fa_ws, st, gate, kv8);
+      launch_fa(plan, s.qkv, ldqkv, rc, capacity, scale, s.attn, s.act_qs, s.act_d, s.fa_ws, st, gate, kvf);
     }
     if (tr && !trace_codes(tr->q_attn_out, il, s.act_qs, B, H * hd, st)) return KD_ERR_HIP;
     if (norm_fusable(il)) {

@@ -27,7 +27,7 @@ class GpuWorkload:
         self.km = KdModel(self.model, device, fused=fused)
         n_sess = len(wl.prefill)
         self.caches = SessionCaches(n_sess, sp.n_layers, sp.n_head_kv, wl.capacity, sp.head_dim, device,
-                                    fp8=sp.kv_fp8)
+                                    fp8=sp.kv_fp8, q8=sp.kv_q8)
         fill_sessions = range(n_sess) if sessions is None else sessions
         if fill == "seeded":
             for s in fill_sessions:
@@ -43,6 +43,12 @@ class GpuWorkload:
                 if sp.kv_fp8:   # random E4M3 bytes: sign, exponent field 4 .. 8, mantissa
                     c = torch.randint(0, 80, t[:, :, :, :L].shape, generator=gen, device=device)
                     t[:, :, :, :L] = (((c & 1) << 7) | ((4 + (c >> 4)) << 3) | ((c >> 1) & 7)).to(torch.uint8)
+                elif sp.kv_q8:  # random int8 rows: codes in [-127, 127], fp16 block scales ~1.7/127
+                    hd = sp.head_dim
+                    codes = torch.randint(-127, 128, t[:, :, :, :L, :hd].shape, generator=gen, device=device)
+                    t[:, :, :, :L, :hd] = codes.to(torch.int8).view(torch.uint8)
+                    sc = (1.7 / 127.0) * (0.5 + torch.rand(t[:, :, :, :L, :hd // 32].shape, generator=gen, device=device))
+                    t[:, :, :, :L, hd:hd + hd // 16] = sc.to(torch.float16).view(torch.uint8)
                 else:
                     t[:, :, :, :L].normal_(generator=gen)
         self.device = device

@@ -222,7 +222,8 @@ def test_layer_variant_fields_are_validated():
 
 
 def test_kv_format_is_validated():
-    """kd_model_create accepts fp16 and E4M3 caches only, with either wqkv layout."""
+    """kd_model_create accepts fp16 and E4M3 caches with either wqkv layout, int8 caches with
+    the canonical layout only, and no other format."""
     L = kd.lib()
     h = C.c_void_p()
 
@@ -239,7 +240,10 @@ def test_kv_format_is_validated():
     assert create(kd.KD_KV_F16, 1) == kd.KD_OK
     assert create(kd.KD_KV_FP8_E4M3, 0) == kd.KD_OK
     assert create(kd.KD_KV_FP8_E4M3, 1) == kd.KD_OK
-    assert create(2, 0) == kd.KD_ERR_INVALID
+    assert create(kd.KD_KV_Q8_0, 0) == kd.KD_OK
+    assert create(kd.KD_KV_Q8_0, 1) == kd.KD_ERR_UNSUPPORTED
+    assert b"int8 KV" in L.kd_last_error()
+    assert create(3, 0) == kd.KD_ERR_INVALID
     assert b"kv_format" in L.kd_last_error()
 
 

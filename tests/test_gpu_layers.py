@@ -64,8 +64,14 @@ def _gpu_slots_into(oc, gw, step, layers):
 def _slot_excess(g, r):
     """How far the GPU's appended values g exceed one rounding of the cache format from the
     oracle's r, beyond the fp32 evaluation error (1e-5 of each head's rms): <= 0 when g is r
-    rounded either way.  fp16: one unit <= 2^-10 |r|; E4M3 codes: <= 2^-3 |r|, 2^-9 below 2^-6."""
-    if g.dtype == np.uint8:
+    rounded either way.  fp16: one unit <= 2^-10 |r|; E4M3 codes: <= 2^-3 |r|, 2^-9 below 2^-6;
+    int8 rows: one code step d of the block plus one fp16 unit of its scale times the code."""
+    if g.dtype == np.uint8 and g.shape[-1] % 32 == 16:          # int8 rows: codes and block scales
+        hd = g.shape[-1] - 16
+        gv, rv = oracle.q8_kv_decode(g, hd), oracle.q8_kv_decode(r, hd)
+        d = np.repeat(r[..., hd:hd + hd // 16].copy().view(np.float16).astype(np.float64), 32, axis=-1)
+        unit = d * (1 + 2.0 ** -10) + 2.0 ** -10 * np.abs(rv)      # one code step, or the scale's fp16 unit
+    elif g.dtype == np.uint8:
         gv, rv = oracle.e4m3_decode(g), oracle.e4m3_decode(r)
         unit = np.maximum(np.abs(rv) * 2.0 ** -3, 2.0 ** -9)
     else:
@@ -160,7 +166,7 @@ def _check_layers(gw, steps, layers, rows=None, dense_budget=6 << 30, head=True,
     assert near == 0 or n_ids > 0
 
 
-@pytest.mark.parametrize("variant", ["plain", "swa", "qk_norm", "gate", "fp8"])
+@pytest.mark.parametrize("variant", ["plain", "swa", "qk_norm", "gate", "fp8", "q8"])
 def test_c2_every_layer_and_lm_head(variant):
     """8-layer d=2048 Q8_0 stack with lm_head 32000, ctx 1238, B = 4 (and its block variants:
     512-key windows on alternate layers, QK-norm, output gate, FP8 E4M3 caches): every layer
@@ -169,7 +175,7 @@ def test_c2_every_layer_and_lm_head(variant):
     base = W.workload("c2", B=4, steps=2)
     sp = base.spec
     extra = {"plain": {}, "swa": {"swa_window": 512, "swa_layers": (0, 2, 4, 6)}, "qk_norm": {"qk_norm": True},
-             "gate": {"attn_gate": True}, "fp8": {"kv_fp8": True}}[variant]
+             "gate": {"attn_gate": True}, "fp8": {"kv_fp8": True}, "q8": {"kv_q8": True}}[variant]
     wl = dataclasses.replace(base, spec=dataclasses.replace(sp, **extra))
     gw = GpuWorkload(wl)
     _check_layers(gw, [0, 1], list(range(sp.n_layers)))
