@@ -399,3 +399,66 @@ def q8_kv_decode(rows: np.ndarray, hd: int) -> np.ndarray:
     q = flat[:, :hd].view(np.int8).astype(np.float64).reshape(-1, hd // 32, 32)
     d = np.ascontiguousarray(flat[:, hd:hd + 2 * (hd // 32)]).view(np.float16).astype(np.float64)
     return (q * d[:, :, None]).reshape(*lead, hd)
+
+
+# ---------------------------------------------------------------------------------------
+# Linear-attention (gated delta rule) layer pieces around the state step
+# ---------------------------------------------------------------------------------------
+def softplus(x: np.ndarray) -> np.ndarray:
+    """log(1 + e^x) in fp64 (written as logaddexp(0, x), which does not overflow)."""
+    return np.logaddexp(0.0, np.asarray(x, dtype=np.float64))
+
+
+def l2_normalize(x: np.ndarray, eps: float) -> np.ndarray:
+    """x / sqrt(sum(x^2) + eps) over the last axis."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
+
+
+def ssm_conv_step(state: np.ndarray, x: np.ndarray, w: np.ndarray):
+    """One decode step of the causal depthwise convolution that feeds the linear mixer.
+
+    memra-engine decode_batch.rs, the Linear mixer of ``decode_batch_layers``: the mixed
+    projection passes through a fused conv ring per sequence (``ssm_conv1d_fused_decode_b``,
+    kernel width d_conv) before the prep.  Reading: channel c's output is
+    silu(sum_j w[c, j] window[j, c]) over the window of the last d_conv inputs, oldest first --
+    the d_conv - 1 held in the ring (``state [d_conv - 1, C]``) and this step's input ``x [C]``;
+    the ring then holds the newest d_conv - 1 of them.  Returns (y [C], new state), fp64.
+    """
+    state = np.asarray(state, dtype=np.float64)
+    window = np.concatenate([state, np.asarray(x, dtype=np.float64)[None, :]], axis=0)   # [d_conv, C]
+    pre = np.einsum("cj,jc->c", np.asarray(w, dtype=np.float64), window)
+    return silu(pre), window[1:].copy()
+
+
+def gdn_prep(conv_out: np.ndarray, beta_raw: np.ndarray, alpha: np.ndarray, dt_bias: np.ndarray, a: np.ndarray,
+             d_state: int, n_k: int, n_v: int, eps: float):
+    """The prep between the conv and the state step, for one row.
+
+    memra-engine decode_batch.rs (``gdn_prep_decode_b``): from the conv outputs and the beta /
+    alpha projections it leaves L2-normalised q and k, v, a gate beta and a log-decay g per
+    value head.  Reading: the conv output is q (n_k heads of d_state), then k (n_k heads), then
+    v (n_v heads); value head h uses key head h // (n_v / n_k) for q and k; q and k are
+    L2-normalised per head (``l2_normalize`` with the model's eps); beta = sigmoid(beta_raw);
+    g = a softplus(alpha + dt_bias), a being the layer's negative per-head decay rate.
+    Returns q, k, v [n_v, d_state] and g, beta [n_v], fp64.
+    """
+    c = np.asarray(conv_out, dtype=np.float64)
+    kd_ = d_state * n_k
+    qh = c[:kd_].reshape(n_k, d_state)
+    kh = c[kd_:2 * kd_].reshape(n_k, d_state)
+    v = c[2 * kd_:2 * kd_ + d_state * n_v].reshape(n_v, d_state)
+    rep = np.arange(n_v) // (n_v // n_k)
+    q = l2_normalize(qh, eps)[rep]
+    k = l2_normalize(kh, eps)[rep]
+    beta = sigmoid(beta_raw)
+    g = np.asarray(a, dtype=np.float64) * softplus(np.asarray(alpha, dtype=np.float64) +
+                                                   np.asarray(dt_bias, dtype=np.float64))
+    return q, k, v, g, beta
+
+
+def gated_rmsnorm(o: np.ndarray, w: np.ndarray, z: np.ndarray, eps: float) -> np.ndarray:
+    """The linear mixer's output norm (memra-engine decode_batch.rs ``gated_rmsnorm`` over
+    d_state per value head, with the z projection): y = rmsnorm(o_h) w * silu(z_h) for every
+    head's row of d_state values (``o``, ``z`` [..., d_state], ``w`` [d_state])."""
+    return rmsnorm(o, w, eps) * silu(z)

@@ -53,12 +53,18 @@ class OracleCaches:
     def __init__(self, wl, sessions: Optional[Sequence[int]] = None, layers: Optional[Sequence[int]] = None):
         """``layers``: only these layers' caches are filled (the others stay None), for
         following single layers of a deep stack."""
-        from workload import kv_prefill_many  # seeded inputs only
+        from workload import kv_prefill_many, recurrent_prefill  # seeded inputs only
         sp = wl.spec
         self.sessions = list(range(len(wl.prefill))) if sessions is None else list(sessions)
         keep = set(range(sp.n_layers) if layers is None else layers)
+        lin = set(getattr(sp, "linear_layers", ()))
         self.K: Dict[int, List[np.ndarray]] = {}
         self.V: Dict[int, List[np.ndarray]] = {}
+        # linear layers: the recurrent state {"conv": [d_conv - 1, conv_dim], "S": [n_v, d, d]}
+        self.R: Dict[int, Dict[int, Dict[str, np.ndarray]]] = {
+            s: {il: dict(zip(("conv", "S"), (a.astype(np.float64) for a in recurrent_prefill(wl, s, il))))
+                for il in sorted(keep & lin)} for s in self.sessions}
+        keep -= lin
         pairs = [(s, il) for s in self.sessions for il in range(sp.n_layers) if il in keep]
         pre = dict(zip(pairs, kv_prefill_many(wl, pairs)))
         for s in self.sessions:
@@ -191,6 +197,9 @@ def decode_layer(model: Dict, il: int, caches: OracleCaches, x: np.ndarray, sess
     B = x.shape[0]
     xn = ops.rmsnorm(x, L["attn_norm"], eps)
     xq, xd = _q_forced(xn, fc("attn_in"), record, "attn in")
+    if L.get("mixer") == "linear":
+        mixed = _linear_mixer(sp, L, caches, il, xq, xd, sessions, dense, blocks, fc, record, trace)
+        return _after_mixer(sp, L, x, mixed, dense, blocks, info, forced, record, fc, trace, il, None)
     qkv = _mm(L["wqkv"], xq, xd, dense, blocks)
     q = qkv[:, : H * hd].reshape(B, H, hd)
     k = qkv[:, H * hd: (H + G) * hd].reshape(B, G, hd)
@@ -230,9 +239,43 @@ def decode_layer(model: Dict, il: int, caches: OracleCaches, x: np.ndarray, sess
     if gate is not None:   # every attention output element times sigmoid of its gate, before W_o
         attn = attn * ops.sigmoid(gate)
     aq, ad = _q_forced(attn.reshape(B, H * hd), fc("attn_out"), record, "attn out")
+    return _after_mixer(sp, L, x, (aq, ad), dense, blocks, info, forced, record, fc, trace, il,
+                        {"q": q, "k": k, "v": v, "attn": attn})
+
+
+def _linear_mixer(sp, L: Dict, caches: OracleCaches, il: int, xq, xd, sessions, dense, blocks, fc, record, trace):
+    """The gated delta-rule mixer of a linear layer (memra-engine decode_batch.rs, the Linear
+    arm of ``decode_batch_layers``): one product of the normed input gives the conv channels,
+    z, beta and alpha; per row, the conv ring step, the prep, the state step (scale
+    1/sqrt(d_state)), the gated norm; returns Q() of the gated-norm rows (the out product's
+    input).  Each row's recurrent state in ``caches.R`` is updated in place."""
+    B = xq.shape[0]
+    nk, nv, ds = sp.ssm_n_k, sp.ssm_n_v, sp.ssm_d_state
+    C, Vd = sp.ssm_conv_dim, sp.ssm_value_dim
+    proj = _mm(L["wqkv"], xq, xd, dense, blocks)
+    y = np.empty((B, Vd), dtype=np.float64)
+    for b in range(B):
+        st = caches.R[sessions[b]][il]
+        conv_out, st["conv"] = ops.ssm_conv_step(st["conv"], proj[b, :C], L["ssm_conv"])
+        z = proj[b, C:C + Vd]
+        beta_raw = proj[b, C + Vd:C + Vd + nv]
+        alpha = proj[b, C + Vd + nv:C + Vd + 2 * nv]
+        q, k, v, g, beta = ops.gdn_prep(conv_out, beta_raw, alpha, L["ssm_dt"], L["ssm_a"], ds, nk, nv, sp.rms_eps)
+        st["S"], o = ops.gdn_step(st["S"], q, k, v, g, beta, 1.0 / np.sqrt(ds))
+        y[b] = ops.gated_rmsnorm(o, L["ssm_norm"], z.reshape(nv, ds), sp.rms_eps).reshape(Vd)
+        if trace is not None:
+            trace.append({"layer": il, "row": b, "conv_out": conv_out, "q": q, "k": k, "v": v, "g": g,
+                          "beta": beta, "o": o, "y": y[b].copy()})
+    return _q_forced(y, fc("attn_out"), record, "mixer out")
+
+
+def _after_mixer(sp, L: Dict, x, mixed, dense, blocks, info, forced, record, fc, trace, il, attn_trace):
+    """The o (out) product of the mixer's quantised output, the residual add, and the FFN."""
+    aq, ad = mixed
     x1 = x + _mm(L["wo"], aq, ad, dense, blocks)
-    if trace is not None:
-        trace.append({"layer": il, "q": q, "k": k, "v": v, "attn": attn, "x1": x1})
+    if trace is not None and attn_trace is not None:
+        trace.append({"layer": il, **attn_trace, "x1": x1})
+    eps = sp.rms_eps
     if not sp.has_ffn:
         return x1
     z = ops.rmsnorm(x1, L["ffn_norm"], eps)

@@ -28,6 +28,7 @@ Storage conventions of the arrays produced here (both sides read them):
 from __future__ import annotations
 
 import math
+import dataclasses
 from dataclasses import dataclass, field
 from typing import Dict, List, Optional, Tuple
 
@@ -43,6 +44,8 @@ T_FINAL_NORM, T_LM_Q, T_LM_D = 26, 27, 28
 T_X_IN, T_K_PRE, T_V_PRE, T_LENGTHS = 29, 30, 31, 32
 T_EMBED = 33
 T_Q_NORM, T_K_NORM = 34, 35
+T_SSM_IN_Q, T_SSM_IN_D, T_SSM_OUT_Q, T_SSM_OUT_D, T_SSM_CONV, T_SSM_DT, T_SSM_A, T_SSM_NORM = 36, 37, 38, 39, 40, 41, 42, 43
+T_REC_CONV, T_REC_S = 44, 45
 
 
 def rng_for(seed: int, cfg_code: int, tensor: int, layer: int = 0, index: int = 0) -> np.random.Generator:
@@ -75,10 +78,33 @@ class ModelSpec:
     attn_gate: bool = False              # attention output scaled by sigmoid of H hd more projection rows
     kv_fp8: bool = False                 # KV caches hold FP8 E4M3 codes (uint8) instead of fp16
     kv_q8: bool = False                  # KV caches hold int8 rows (Q8_0 blocks: codes + fp16 scales)
+    linear_layers: Tuple[int, ...] = ()  # gated delta-rule linear-attention layers (the others: attention)
+    ssm_d_state: int = 128               # linear layers: state size per head (d_k = d_v)
+    ssm_n_k: int = 0                     # key heads (q and k)
+    ssm_n_v: int = 0                     # value heads
+    ssm_d_conv: int = 4                  # conv kernel width
 
     @property
     def qkv_rows(self) -> int:
         return (self.n_head + 2 * self.n_head_kv + (self.n_head if self.attn_gate else 0)) * self.head_dim
+
+    @property
+    def ssm_key_dim(self) -> int:
+        return self.ssm_d_state * self.ssm_n_k
+
+    @property
+    def ssm_value_dim(self) -> int:
+        return self.ssm_d_state * self.ssm_n_v
+
+    @property
+    def ssm_conv_dim(self) -> int:
+        return 2 * self.ssm_key_dim + self.ssm_value_dim
+
+    @property
+    def ssm_in_rows(self) -> int:
+        """Rows of a linear layer's input projection: the conv's q, k, v channels, then z
+        (value_dim), then beta and alpha (one per value head each)."""
+        return self.ssm_conv_dim + self.ssm_value_dim + 2 * self.ssm_n_v
 
     @property
     def has_ffn(self) -> bool:
@@ -125,6 +151,10 @@ SPEC_C3 = ModelSpec("c3_attn_d4096_q8_0", 1, 4096, 32, 8, 128, 0, "q8_0")
 SPEC_C4 = ModelSpec("c4_32layer_d4096_q4_0", 32, 4096, 32, 8, 128, 14336, "q4_0", final_norm=True)
 SPEC_C5 = ModelSpec("c5_moe8layer_d2816_q4_0", 8, 2816, 16, 8, 128, 0, "q4_0", final_norm=True,
                     n_experts=128, n_expert_used=8, expert_ffn=704, shared_ffn=2816)
+# the 8-layer Q8_0 decoder with gated delta-rule layers in place of attention on three of every
+# four layers (attention on layers 3 and 7): 8 key heads and 16 value heads of 128, conv width 4
+SPEC_HYBRID = dataclasses.replace(SPEC_C2, name="hybrid_8layer_d2048_q8_0_gdn_lm32000",
+                                  linear_layers=(0, 1, 2, 4, 5, 6), ssm_n_k=8, ssm_n_v=16)
 
 
 def c3_lengths(seed: int = 0, B: int = 16) -> List[int]:
@@ -153,6 +183,9 @@ def workload(name: str, B: Optional[int] = None, seed: int = 0, steps: Optional[
         B = B or 8
         return Workload(4, SPEC_C4, [4096] * B, [(b, 0) for b in range(B)], steps or 32,
                         4096 + 32, seed)
+    if name == "hybrid":
+        B = B or 4
+        return Workload(6, SPEC_HYBRID, [1238] * B, [(b, 0) for b in range(B)], steps or 4, 1238 + 64, seed)
     if name == "c5":
         n_streams = (B or 16) // 4
         assert n_streams * 4 == (B or 16)
@@ -188,8 +221,50 @@ def draw_gain(seed: int, code: int, tensor: int, layer: int, n: int) -> np.ndarr
     return (np.float32(1.0) + np.float32(0.1) * r.standard_normal(n, dtype=np.float32)).astype(np.float32)
 
 
+def make_linear_layer(spec: ModelSpec, code: int, seed: int, il: int) -> Dict:
+    """A gated delta-rule layer: its input projection (quantised, rows as ``ssm_in_rows``), the
+    conv kernel fp32 [conv_dim, d_conv] ~ N(0, 0.5^2), dt bias fp32 [n_v] ~ N(0, 0.5^2), decay
+    rate a = -exp(U(-1, 1)) fp32 [n_v], the output-norm gain 1 + 0.1 N(0, 1) [d_state] and the
+    out projection [d, value_dim] (quantised)."""
+    d, fmt, nv = spec.d, spec.fmt, spec.ssm_n_v
+    r = lambda t: rng_for(seed, code, t, il)
+    return {
+        "mixer": "linear",
+        "attn_norm": draw_gain(seed, code, T_ATTN_NORM, il, d),
+        "wqkv": draw_weight(fmt, seed, code, T_SSM_IN_Q, T_SSM_IN_D, il, spec.ssm_in_rows, d),
+        "wo": draw_weight(fmt, seed, code, T_SSM_OUT_Q, T_SSM_OUT_D, il, d, spec.ssm_value_dim),
+        "ssm_conv": (np.float32(0.5) * r(T_SSM_CONV).standard_normal((spec.ssm_conv_dim, spec.ssm_d_conv),
+                                                                      dtype=np.float32)).astype(np.float32),
+        "ssm_dt": (np.float32(0.5) * r(T_SSM_DT).standard_normal(nv, dtype=np.float32)).astype(np.float32),
+        "ssm_a": (-np.exp(r(T_SSM_A).uniform(-1.0, 1.0, nv))).astype(np.float32),
+        "ssm_norm": draw_gain(seed, code, T_SSM_NORM, il, spec.ssm_d_state),
+    }
+
+
+def recurrent_prefill(wl: "Workload", session: int, layer: int) -> Tuple[np.ndarray, np.ndarray]:
+    """A linear layer's recurrent state before step 0: the conv ring [d_conv - 1, conv_dim]
+    ~ N(0, 1) (the last inputs of a prefix) and the state [n_v, d_state, d_state] ~ N(0, 0.05^2),
+    fp32."""
+    sp = wl.spec
+    conv = rng_for(wl.seed, wl.code, T_REC_CONV, layer, session).standard_normal(
+        (sp.ssm_d_conv - 1, sp.ssm_conv_dim), dtype=np.float32)
+    S = (np.float32(0.05) * rng_for(wl.seed, wl.code, T_REC_S, layer, session).standard_normal(
+        (sp.ssm_n_v, sp.ssm_d_state, sp.ssm_d_state), dtype=np.float32)).astype(np.float32)
+    return conv, S
+
+
 def make_layer(spec: ModelSpec, code: int, seed: int, il: int) -> Dict:
     d, fmt = spec.d, spec.fmt
+    if il in spec.linear_layers:
+        L = make_linear_layer(spec, code, seed, il)
+        if spec.has_ffn:
+            L["ffn_norm"] = draw_gain(seed, code, T_FFN_NORM, il, d)
+        if spec.ffn:
+            F = spec.ffn
+            L["w_gate"] = draw_weight(fmt, seed, code, T_GATE_Q, T_GATE_D, il, F, d)
+            L["w_up"] = draw_weight(fmt, seed, code, T_UP_Q, T_UP_D, il, F, d)
+            L["w_down"] = draw_weight(fmt, seed, code, T_DOWN_Q, T_DOWN_D, il, d, F)
+        return L
     L: Dict = {
         "swa_window": spec.swa_window if il in spec.swa_layers else 0,
         "attn_gate": bool(spec.attn_gate),
