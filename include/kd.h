@@ -310,6 +310,25 @@ typedef struct {
                                gate (in RoPE pair order too when wqkv_pair_rows = 1), and every
                                attention output element is multiplied by sigmoid(gate) before
                                wo; 0 = no gate */
+  /* Linear-attention layers (memra-engine decode_batch.rs, the Linear mixer of
+   * decode_batch_layers: batched projections, the fused conv ring, the prep, one batched scan
+   * of the gated delta rule over every row's state, the gated norm, the out projection).
+   * mixer = 1 replaces the attention of this layer: wqkv is the input projection
+   * [C + d_v + 2 n_v, d] (canonical layout, wqkv_pair_rows = 0) whose rows are the conv
+   * channels C = 2 d_state n_k + d_v (q of the n_k key heads, k of them, v of the n_v value
+   * heads), then z (d_v = d_state n_v), then beta_raw (n_v), then alpha (n_v); wo is the out
+   * projection [d, d_v].  Per row and value head h (key head h / (n_v / n_k)): each conv
+   * channel c becomes silu(sum_j ssm_conv[c][j] w_j) over the window w of the row's last
+   * d_conv inputs of that channel, oldest first; q and k are L2-normalised over the head
+   * (x / sqrt(sum x^2 + rms_eps)); beta = sigmoid(beta_raw); g = ssm_a[h] softplus(alpha +
+   * ssm_dt[h]); then the kd_gdn_step update with scale 1 / sqrt(d_state); the head's output o
+   * becomes o / sqrt(mean(o^2) + rms_eps) ssm_norm silu(z), quantised for wo.  The attention
+   * fields (q_norm, swa_window, attn_gate) must be 0 for such a layer. */
+  int32_t mixer;            /* 0 attention, 1 gated delta-rule linear attention */
+  const float* ssm_conv;    /* [C][d_conv] fp32 */
+  const float* ssm_dt;      /* [n_v] fp32 */
+  const float* ssm_a;       /* [n_v] fp32 (negative decay rates) */
+  const float* ssm_norm;    /* [d_state] fp32 */
 } kd_layer_desc;
 
 typedef struct {
@@ -322,6 +341,8 @@ typedef struct {
   const kd_layer_desc* layers;           /* host array [n_layers] (copied by kd_model_create) */
   const float* final_norm;               /* [d] or NULL */
   kd_weight lm_head;                     /* [vocab, d] or qs NULL */
+  int32_t ssm_d_state, ssm_n_k, ssm_n_v, ssm_d_conv;  /* linear layers: d_state (128), key and value
+                                            heads (n_v a multiple of n_k), conv width (2..8) */
   int32_t kv_format;                     /* KD_KV_F16 (fp16 caches, k_base/v_base [G][capacity][hd]
                                             fp16), KD_KV_FP8_E4M3 (uint8 codes, stored and read as
                                             kd_kv_append_fp8 / kd_fa_decode_ragged_fp8, by either
@@ -340,11 +361,20 @@ void kd_model_destroy(kd_model* m);
 
 /* Workspace bytes of kd_decode_step for B rows with these positions (host pos[B]). */
 size_t kd_decode_step_workspace(const kd_model* m, int32_t B, const int32_t* pos);
+/* Bytes of one row's recurrent state of one linear layer (0 if the model has none): fp32,
+ * 16-byte aligned, laid out as ring 0 [d_conv - 1][C], ring 1 (the same), state 0
+ * [n_v][d_state][d_state] (row-major [v][k], as kd_gdn_step), state 1 (the same).  A step at
+ * position pos reads ring and state pos % 2 and writes the other ones, so the state before the
+ * step stays readable (a step can be redone, or rolled back by one position).  The caller
+ * places a row's state after pos = p tokens in ring/state p % 2 before its first step. */
+size_t kd_recurrent_state_bytes(const kd_model* m);
 
 /* One decode step for B rows: x_in fp32 [B][d]; row b writes K/V at pos[b] of its caches
  * and attends pos[b] + 1 keys; all appends of a layer precede its attention, so rows that
  * share a cache at consecutive positions (speculative-verify rows) attend causally.
- * k_base / v_base: host arrays [n_layers][B] of cache base addresses.  out: fp32
+ * k_base / v_base: host arrays [n_layers][B] of cache base addresses; for a linear layer
+ * k_base[l][b] is row b's recurrent state (kd_recurrent_state_bytes; no two rows may share
+ * one) and v_base[l][b] is not read.  out: fp32
  * [B][vocab] logits if the model has an lm_head, else [B][d] (output-normed if final_norm).
  * x_in and out must be 16-byte aligned (rows are read and written four floats at a time);
  * KD_ERR_INVALID otherwise.  Positions are not advanced: the caller owns session state (memra-engine
@@ -365,7 +395,8 @@ kd_status kd_decode_step(const kd_model* m, int32_t B, const float* x_in, const 
  *   the int8 codes of every activation quantisation, in the tiled activation layout (rows of
  *   NQ(k) * 128 bytes, NQ(k) = ceil(k / 128)), per layer:
  *   q_attn_in  [n_layers][B][NQ(d) 128]      the normed attention input (the q/k/v product's);
- *   q_attn_out [n_layers][B][NQ(H hd) 128]   the attention output (the o product's input);
+ *   q_attn_out [n_layers][B][NQ(max(H hd, d_v)) 128]  the attention output, or a linear layer's
+ *              gated-norm output (the o / out product's input; its first NQ(k) 128 bytes);
  *   q_ffn_in   [n_layers][B][NQ(d) 128]      the normed FFN input;
  *   q_ffn_mid  [n_layers][R][NQ(F) 128]      silu(gate) up, the down product's input: dense
  *              layers R = B rows of F = ffn; MoE layers R = B n_expert_used (row, rank) rows of

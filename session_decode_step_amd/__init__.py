@@ -46,7 +46,9 @@ class KdLayerDesc(C.Structure):
                 ("w_gate", KdWeight), ("w_up", KdWeight), ("w_down", KdWeight), ("router", C.c_void_p),
                 ("e_gate", KdWeight), ("e_up", KdWeight), ("e_down", KdWeight),
                 ("s_gate", KdWeight), ("s_up", KdWeight), ("s_down", KdWeight), ("swa_window", C.c_int32),
-                ("q_norm", C.c_void_p), ("k_norm", C.c_void_p), ("attn_gate", C.c_int32)]
+                ("q_norm", C.c_void_p), ("k_norm", C.c_void_p), ("attn_gate", C.c_int32),
+                ("mixer", C.c_int32), ("ssm_conv", C.c_void_p), ("ssm_dt", C.c_void_p), ("ssm_a", C.c_void_p),
+                ("ssm_norm", C.c_void_p)]
 
 
 class KdModelDesc(C.Structure):
@@ -54,7 +56,8 @@ class KdModelDesc(C.Structure):
                 ("head_dim", C.c_int32), ("ffn", C.c_int32), ("n_experts", C.c_int32), ("n_expert_used", C.c_int32),
                 ("expert_ffn", C.c_int32), ("shared_ffn", C.c_int32), ("vocab", C.c_int32),
                 ("rope_base", C.c_float), ("rms_eps", C.c_float), ("layers", C.POINTER(KdLayerDesc)),
-                ("final_norm", C.c_void_p), ("lm_head", KdWeight), ("kv_format", C.c_int32)]
+                ("final_norm", C.c_void_p), ("lm_head", KdWeight), ("ssm_d_state", C.c_int32), ("ssm_n_k", C.c_int32),
+                ("ssm_n_v", C.c_int32), ("ssm_d_conv", C.c_int32), ("kv_format", C.c_int32)]
 
 
 KD_KV_F16, KD_KV_FP8_E4M3, KD_KV_Q8_0 = 0, 1, 2
@@ -103,6 +106,7 @@ SIGNATURES = {
     "kd_model_create": (_I, [C.POINTER(KdModelDesc), C.POINTER(_P)]),
     "kd_model_destroy": (None, [_P]),
     "kd_decode_step_workspace": (_S, [_P, _I, _PI]),
+    "kd_recurrent_state_bytes": (_S, [_P]),
     "kd_decode_step": (_I, [_P, _I, _P, _PI, _PP, _PP, _I, _P, _P, _S, _P]),
     "kd_mmvq_swiglu": (_I, [_PW, KdAct, _I, KdAct, _P]),
     "kd_mmvq_rope": (_I, [_PW, KdAct, _I, _I, _I, _I, _P, _I, _PP, _PP, _PI, _I, _F, _P]),
@@ -607,6 +611,22 @@ class KdModel:
             slot[0] = il
             D = self.layers[il]
             D.attn_norm = F(L["attn_norm"])
+            if L.get("mixer") == "linear":   # gated delta-rule layer: input and out projections, fp32 params
+                D.mixer = 1
+                D.wqkv, D.wqkv_pair_rows, D.wo = W(L["wqkv"], "wqkv"), 0, W(L["wo"], "wo")
+                D.ssm_conv, D.ssm_dt, D.ssm_a, D.ssm_norm = (F(L["ssm_conv"]), F(L["ssm_dt"]), F(L["ssm_a"]),
+                                                             F(L["ssm_norm"]))
+                D.ffn_norm = F(L["ffn_norm"]) if "ffn_norm" in L else None
+                if "w_gate" in L and fused:
+                    D.w_gate, D.w_up, D.w_down = (W(interleave_gate_up(L["w_gate"], L["w_up"]), "w_gateup"), empty,
+                                                  W(L["w_down"], "w_down"))
+                elif "w_gate" in L:
+                    D.w_gate, D.w_up, D.w_down = W(L["w_gate"], "w_gate"), W(L["w_up"], "w_up"), W(L["w_down"], "w_down")
+                else:
+                    D.w_gate = D.w_up = D.w_down = empty
+                D.router = None
+                D.e_gate = D.e_up = D.e_down = D.s_gate = D.s_up = D.s_down = empty
+                continue
             D.swa_window = int(L.get("swa_window", 0))
             qk_norm = "q_norm" in L
             D.q_norm = F(L["q_norm"]) if qk_norm else None
@@ -643,7 +663,9 @@ class KdModel:
         self.desc = KdModelDesc(sp.n_layers, sp.d, sp.n_head, sp.n_head_kv, sp.head_dim, sp.ffn, sp.n_experts,
                                 sp.n_expert_used, sp.expert_ffn, sp.shared_ffn, sp.vocab, sp.rope_base, sp.rms_eps,
                                 self.layers, F(model["final_norm"]) if model["final_norm"] is not None else None,
-                                empty, KD_KV_FP8_E4M3 if kv_fp8 else KD_KV_Q8_0 if kv_q8 else KD_KV_F16)
+                                empty, getattr(sp, "ssm_d_state", 0), getattr(sp, "ssm_n_k", 0),
+                                getattr(sp, "ssm_n_v", 0), getattr(sp, "ssm_d_conv", 0),
+                                KD_KV_FP8_E4M3 if kv_fp8 else KD_KV_Q8_0 if kv_q8 else KD_KV_F16)
         slot[0] = sp.n_layers   # packed[n_layers] holds the output head
         if model["lm_head"] is not None:
             self.desc.lm_head = W(model["lm_head"], "lm_head")
@@ -661,6 +683,9 @@ class KdModel:
 
     def workspace_bytes(self, B: int, pos: Sequence[int]) -> int:
         return lib().kd_decode_step_workspace(self.handle, B, _i32(pos))
+
+    def recurrent_state_bytes(self) -> int:
+        return lib().kd_recurrent_state_bytes(self.handle)
 
     def kd_decode_step(self, x_in: torch.Tensor, pos: Sequence[int], k_base: Sequence[int], v_base: Sequence[int],
                        capacity: int, out: torch.Tensor, ws: torch.Tensor, stream=None) -> torch.Tensor:
@@ -683,7 +708,8 @@ class KdModel:
         Lyr = sp.n_layers
         rec = {"resid": torch.empty((Lyr + 1, B, sp.d), dtype=torch.float32, device=dev),
                "q_attn_in": torch.zeros((Lyr, B, nq(sp.d)), dtype=torch.int8, device=dev),
-               "q_attn_out": torch.zeros((Lyr, B, nq(sp.n_head * sp.head_dim)), dtype=torch.int8, device=dev)}
+               "q_attn_out": torch.zeros((Lyr, B, nq(max(sp.n_head * sp.head_dim, sp.ssm_value_dim))),
+                                         dtype=torch.int8, device=dev)}
         if sp.ffn or sp.n_experts:
             rec["q_ffn_in"] = torch.zeros((Lyr, B, nq(sp.d)), dtype=torch.int8, device=dev)
         if sp.ffn:
@@ -713,17 +739,26 @@ class SessionCaches:
     ``q8=True``."""
 
     def __init__(self, n_sessions: int, n_layers: int, G: int, capacity: int, hd: int, device="cuda",
-                 fp8: bool = False, q8: bool = False):
+                 fp8: bool = False, q8: bool = False, linear_layers: Sequence[int] = (), rec_bytes: int = 0):
+        """``linear_layers``: layers holding a recurrent state of ``rec_bytes`` per session
+        instead of K/V (``rec[s][il]``, fp32; kd_recurrent_state_bytes)."""
         self.n_layers, self.G, self.capacity, self.hd = n_layers, G, capacity, hd
         dt = torch.uint8 if (fp8 or q8) else torch.float16
         row = hd + 16 if q8 else hd
         self.t = [torch.zeros((n_layers, 2, G, capacity, row), dtype=dt, device=device)
                   for _ in range(n_sessions)]
+        self.linear = set(linear_layers)
+        self.rec = [{il: torch.zeros(rec_bytes // 4, dtype=torch.float32, device=device) for il in sorted(self.linear)}
+                    for _ in range(n_sessions)]
 
     def k_ptr(self, s: int, il: int) -> int:
+        if il in self.linear:
+            return self.rec[s][il].data_ptr()
         return self.t[s][il, 0].data_ptr()
 
     def v_ptr(self, s: int, il: int) -> int:
+        if il in self.linear:
+            return self.rec[s][il].data_ptr()
         return self.t[s][il, 1].data_ptr()
 
     def tables(self, sessions: Sequence[int]):
@@ -731,6 +766,14 @@ class SessionCaches:
         kb = [self.k_ptr(s, il) for il in range(self.n_layers) for s in sessions]
         vb = [self.v_ptr(s, il) for il in range(self.n_layers) for s in sessions]
         return kb, vb
+
+    def recurrent_views(self, s: int, il: int, ring: int, state: int, d_conv: int, C: int):
+        """(ring[2] [d_conv - 1, C], state[2] [n_v, d, d]) views of a session's recurrent state
+        (the layout kd_recurrent_state_bytes describes; ring buffers padded to ``ring`` floats)."""
+        t = self.rec[s][il]
+        rings = [t[i * ring:i * ring + (d_conv - 1) * C].view(d_conv - 1, C) for i in range(2)]
+        states = [t[2 * ring + i * state:2 * ring + (i + 1) * state] for i in range(2)]
+        return rings, states
 
     def fill_prefill(self, s: int, il: int, k: np.ndarray, v: np.ndarray) -> None:
         L = k.shape[1]

@@ -309,6 +309,17 @@ void launch_fa(const FaPlan& p, const float* q, int ldq, const RowCaches& rc, in
 bool fa_shape_supported(int H, int G, int hd);
 int fa_max_keys();
 
+// Linear-attention (gated delta-rule) layers: the state step over per-row state pointers, the
+// conv ring + prep, and the gated norm + quantiser of the mixer output (see gdn.hip).
+int gdn_state_dim();
+void launch_gdn_step(const float* q, const float* k, const float* v, const float* g, const float* beta, int B, int H,
+                     const float* const* state_in, float* const* state_out, float scale, float* o, hipStream_t st);
+void launch_ssm_conv_prep(const float* proj, int ldp, const float* w, int dconv, const float* const* ring_in,
+                          float* const* ring_out, const float* dt, const float* a, int B, int nk, int nv, float eps,
+                          float* q, float* k, float* v, float* g, float* beta, hipStream_t st);
+void launch_gated_norm_quant(const float* o, const float* z, int ldz, const float* w, int B, int nv, float eps,
+                             int8_t* qs, float* qd, hipStream_t st);
+
 void launch_swiglu_quant(const float* g, const float* u, int rows, int n, int ld, float* a_out, int8_t* qs,
                          float* d, hipStream_t st);
 void launch_add(const float* x, const float* y, float* z, size_t n, hipStream_t st);

@@ -17,6 +17,7 @@
 // §0.12, the "N as a grid dimension, constant dispatch" plan).  Nothing here synchronises
 // the stream or copies host data to the device: per-row positions and cache addresses
 // travel as kernel arguments.
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -52,7 +53,12 @@ using namespace kd;
 struct kd_model {
   kd_model_desc desc;
   std::vector<kd_layer_desc> layers;
-  int max_k;  // longest activation row any product reads
+  int max_k;       // longest activation row any product reads
+  bool linear;     // some layer is a gated delta-rule linear-attention layer
+  int ssm_c;       // linear layers: conv channels C = 2 d_state n_k + d_state n_v
+  int ssm_vd;      // value dim d_state n_v
+  int ssm_nin;     // rows of the input projection: C + d_v + 2 n_v
+  size_t ring_floats, state_floats;  // one ring buffer, one state buffer
 };
 
 extern "C" const char* kd_last_error(void) { return g_err; }
@@ -108,9 +114,32 @@ extern "C" kd_status kd_model_create(const kd_model_desc* desc, kd_model** out) 
     KD_REQUIRE(m.ffn == 0, KD_ERR_INVALID, "kd_model_create: dense ffn and experts both set");
   }
   KD_REQUIRE(m.ffn >= 0 && m.ffn % 32 == 0, KD_ERR_UNSUPPORTED, "kd_model_create: ffn=%d", m.ffn);
+  bool any_linear = false;
+  for (int il = 0; il < m.n_layers; ++il) any_linear |= m.layers[il].mixer == 1;
+  const int ssm_ds = m.ssm_d_state, ssm_nk = m.ssm_n_k, ssm_nv = m.ssm_n_v, ssm_dc = m.ssm_d_conv;
+  if (any_linear) {
+    KD_REQUIRE(ssm_ds == gdn_state_dim(), KD_ERR_UNSUPPORTED, "kd_model_create: ssm_d_state=%d (only %d)", ssm_ds,
+               gdn_state_dim());
+    KD_REQUIRE(ssm_nk >= 1 && ssm_nv >= ssm_nk && ssm_nv % ssm_nk == 0 && ssm_nv <= 1024, KD_ERR_UNSUPPORTED,
+               "kd_model_create: ssm_n_k=%d ssm_n_v=%d (n_v a multiple of n_k)", ssm_nk, ssm_nv);
+    KD_REQUIRE(ssm_dc >= 2 && ssm_dc <= 8, KD_ERR_UNSUPPORTED, "kd_model_create: ssm_d_conv=%d outside [2, 8]", ssm_dc);
+  }
+  const int ssm_c = 2 * ssm_ds * ssm_nk + ssm_ds * ssm_nv, ssm_vd = ssm_ds * ssm_nv;
+  const int ssm_nin = ssm_c + ssm_vd + 2 * ssm_nv;
   for (int il = 0; il < m.n_layers; ++il) {
     const kd_layer_desc& L = m.layers[il];
     KD_REQUIRE(L.attn_norm, KD_ERR_INVALID, "kd_model_create: layer %d: null attn_norm", il);
+    KD_REQUIRE(L.mixer == 0 || L.mixer == 1, KD_ERR_INVALID, "kd_model_create: layer %d: mixer=%d", il, L.mixer);
+    if (L.mixer == 1) {
+      KD_REQUIRE(L.ssm_conv && L.ssm_dt && L.ssm_a && L.ssm_norm, KD_ERR_INVALID,
+                 "kd_model_create: layer %d: linear layer without its conv, dt, a or norm arrays", il);
+      KD_REQUIRE(aligned16(L.ssm_norm), KD_ERR_INVALID, "kd_model_create: layer %d: ssm_norm must be 16-byte aligned",
+                 il);
+      KD_REQUIRE(!L.q_norm && !L.k_norm && L.swa_window == 0 && L.attn_gate == 0 && L.wqkv_pair_rows == 0,
+                 KD_ERR_INVALID, "kd_model_create: layer %d: attention options set on a linear layer", il);
+      KD_TRY(check_weight("wqkv (linear input projection)", il, L.wqkv, ssm_nin, d));
+      KD_TRY(check_weight("wo (linear out projection)", il, L.wo, d, ssm_vd));
+    }
     KD_REQUIRE(L.swa_window >= 0, KD_ERR_INVALID, "kd_model_create: layer %d: swa_window=%d < 0", il, L.swa_window);
     KD_REQUIRE(!L.q_norm == !L.k_norm, KD_ERR_INVALID, "kd_model_create: layer %d: q_norm and k_norm go together", il);
     KD_REQUIRE(!L.q_norm || L.wqkv_pair_rows == 0, KD_ERR_UNSUPPORTED,
@@ -119,10 +148,12 @@ extern "C" kd_status kd_model_create(const kd_model_desc* desc, kd_model** out) 
                "kd_model_create: layer %d: int8 KV caches need the canonical wqkv layout (wqkv_pair_rows = 0)", il);
     KD_REQUIRE(L.attn_gate == 0 || L.attn_gate == 1, KD_ERR_INVALID, "kd_model_create: layer %d: attn_gate=%d", il,
                L.attn_gate);
-    KD_TRY(check_weight("wqkv", il, L.wqkv, (H + 2 * G + (L.attn_gate ? H : 0)) * hd, d));
-    KD_REQUIRE(L.wqkv_pair_rows == 0 || L.wqkv_pair_rows == 1, KD_ERR_INVALID,
-               "kd_model_create: layer %d: wqkv_pair_rows=%d", il, L.wqkv_pair_rows);
-    KD_TRY(check_weight("wo", il, L.wo, d, H * hd));
+    if (L.mixer == 0) {
+      KD_TRY(check_weight("wqkv", il, L.wqkv, (H + 2 * G + (L.attn_gate ? H : 0)) * hd, d));
+      KD_REQUIRE(L.wqkv_pair_rows == 0 || L.wqkv_pair_rows == 1, KD_ERR_INVALID,
+                 "kd_model_create: layer %d: wqkv_pair_rows=%d", il, L.wqkv_pair_rows);
+      KD_TRY(check_weight("wo", il, L.wo, d, H * hd));
+    }
     if (m.ffn > 0 || moe) KD_REQUIRE(L.ffn_norm, KD_ERR_INVALID, "kd_model_create: layer %d: null ffn_norm", il);
     if (m.ffn > 0) {
       if (L.w_up.qs) {
@@ -166,12 +197,25 @@ extern "C" kd_status kd_model_create(const kd_model_desc* desc, kd_model** out) 
   mk = H * hd > mk ? H * hd : mk;
   mk = m.ffn > mk ? m.ffn : mk;
   mk = m.shared_ffn > mk ? m.shared_ffn : mk;
+  if (any_linear) mk = ssm_vd > mk ? ssm_vd : mk;
   mm->max_k = mk;
+  mm->linear = any_linear;
+  mm->ssm_c = any_linear ? ssm_c : 0;
+  mm->ssm_vd = any_linear ? ssm_vd : 0;
+  mm->ssm_nin = any_linear ? ssm_nin : 0;
+  mm->ring_floats = any_linear ? (size_t)(ssm_dc - 1) * ssm_c : 0;
+  mm->ring_floats = (mm->ring_floats + 3) & ~(size_t)3;  // each buffer 16-byte aligned
+  mm->state_floats = any_linear ? (size_t)ssm_nv * ssm_ds * ssm_ds : 0;
   *out = mm;
   return KD_OK;
 }
 
 extern "C" void kd_model_destroy(kd_model* m) { delete m; }
+
+extern "C" size_t kd_recurrent_state_bytes(const kd_model* m) {
+  if (!m || !m->linear) return 0;
+  return sizeof(float) * 2 * (m->ring_floats + m->state_floats);
+}
 
 // ---------------------------------------------------------------------------------------
 // Workspace
@@ -192,6 +236,7 @@ struct Carve {
 
 struct StepBufs {
   float *xa, *xb, *f, *qkv, *attn, *o, *gu, *z, *cs, *sh, *sgu;
+  float *lq, *lk, *lv, *lg, *lb, *lo;  // linear layers: prep outputs and the state step's output
   int8_t *act_qs, *act2_qs, *hq_qs, *actn_qs;
   float *act_d, *act2_d, *hq_d, *actn_d, *ss;
   void* fa_ws;
@@ -211,7 +256,17 @@ size_t carve_step(const kd_model* m, int B, const FaPlan& plan, void* ws, StepBu
   s.f = c.take<float>((size_t)B * D);
   s.o = c.take<float>((size_t)B * D);
   s.z = c.take<float>((size_t)B * D);
-  s.qkv = c.take<float>((size_t)B * (2 * H + 2 * G) * hd);  // q, k, v and (gated layers) the gate
+  // q, k, v and (gated layers) the gate; linear layers: their input projection's rows
+  s.qkv = c.take<float>((size_t)B * std::max((2 * H + 2 * G) * hd, m->ssm_nin));
+  if (m->linear) {
+    const size_t hv = (size_t)B * d.ssm_n_v;
+    s.lq = c.take<float>(hv * d.ssm_d_state);
+    s.lk = c.take<float>(hv * d.ssm_d_state);
+    s.lv = c.take<float>(hv * d.ssm_d_state);
+    s.lo = c.take<float>(hv * d.ssm_d_state);
+    s.lg = c.take<float>(hv);
+    s.lb = c.take<float>(hv);
+  }
   s.attn = c.take<float>((size_t)B * H * hd);
   s.cs = c.take<float>((size_t)B * hd);
   s.act_qs = c.take<int8_t>((size_t)B * n_quads(m->max_k) * 128);
@@ -274,11 +329,18 @@ bool trace_copy(void* dst, const void* src, size_t bytes, hipStream_t st) {
   return true;
 }
 // Copy the codes of `rows` activation rows of length k (tiled layout) into record slot `slot`
-// of a per-layer code array (nothing if the array is not requested).
-bool trace_codes(int8_t* dst, size_t slot, const int8_t* src, int rows, int k, hipStream_t st) {
+// of a per-layer code array whose rows hold k_slot >= k columns (nothing if the array is not
+// requested).
+bool trace_codes(int8_t* dst, size_t slot, const int8_t* src, int rows, int k, hipStream_t st, int k_slot = 0) {
   if (!dst) return true;
-  const size_t bytes = (size_t)rows * n_quads(k) * 128;
-  return trace_copy(dst + slot * bytes, src, bytes, st);
+  k_slot = k_slot > k ? k_slot : k;
+  const size_t row = (size_t)n_quads(k) * 128, row_slot = (size_t)n_quads(k_slot) * 128;
+  if (hipMemcpy2DAsync(dst + slot * rows * row_slot, row_slot, src, row, row, rows, hipMemcpyDeviceToDevice, st) !=
+      hipSuccess) {
+    set_error("kd_debug_decode_step_trace: copy failed");
+    return false;
+  }
+  return true;
 }
 }  // namespace
 
@@ -301,6 +363,17 @@ static kd_status decode_step_impl(const kd_model* m, int32_t B, const float* x_i
   for (int il = 0; il < L; ++il)
     for (int b = 0; b < B; ++b) {
       void* kb = k_base[(size_t)il * B + b];
+      if (m->layers[il].mixer == 1) {  // a recurrent state per row, never shared
+        KD_REQUIRE(kb && aligned16(kb), KD_ERR_INVALID,
+                   "kd_decode_step: recurrent state of layer %d row %d null or unaligned", il, b);
+        const size_t rb = kd_recurrent_state_bytes(m);
+        for (int a = 0; a < b; ++a) {
+          const char *pa = static_cast<const char*>(k_base[(size_t)il * B + a]), *pb = static_cast<const char*>(kb);
+          KD_REQUIRE(pa + rb <= pb || pb + rb <= pa, KD_ERR_INVALID,
+                     "kd_decode_step: rows %d and %d share a recurrent state (layer %d)", a, b, il);
+        }
+        continue;
+      }
       void* vb = v_base[(size_t)il * B + b];
       KD_REQUIRE(kb && vb, KD_ERR_INVALID, "kd_decode_step: null cache pointer (layer %d row %d)", il, b);
       KD_REQUIRE(aligned16(kb) && aligned16(vb), KD_ERR_INVALID, "kd_decode_step: cache (layer %d row %d) unaligned", il,
@@ -363,6 +436,32 @@ static kd_status decode_step_impl(const kd_model* m, int32_t B, const float* x_i
     if (tr && tr->resid && !trace_copy(tr->resid + (size_t)il * B * D, res, sizeof(float) * B * D, st))
       return KD_ERR_HIP;
     if (tr && !trace_codes(tr->q_attn_in, il, s.act_qs, B, D, st)) return KD_ERR_HIP;
+    const int att_w = std::max(H * hd, m->ssm_vd);  // the trace's mixer-output record width
+    if (Ly.mixer == 1) {
+      // gated delta-rule mixer: input projection, conv ring + prep, state step (each row reads
+      // ring/state pos % 2 and writes the other), gated norm + quantiser for the out product
+      const int nk = d.ssm_n_k, nv = d.ssm_n_v;
+      launch_mmvq(Ly.wqkv, s.act_qs, s.act_d, B, s.qkv, m->ssm_nin, st);
+      const float* ring_in[KD_MAX_B];
+      float* ring_out[KD_MAX_B];
+      const float* st_in[KD_MAX_B];
+      float* st_out[KD_MAX_B];
+      for (int b = 0; b < B; ++b) {
+        float* blk = static_cast<float*>(k_base[(size_t)il * B + b]);
+        const int par = pos[b] & 1;
+        ring_in[b] = blk + par * m->ring_floats;
+        ring_out[b] = blk + (1 - par) * m->ring_floats;
+        st_in[b] = blk + 2 * m->ring_floats + par * m->state_floats;
+        st_out[b] = blk + 2 * m->ring_floats + (1 - par) * m->state_floats;
+      }
+      launch_ssm_conv_prep(s.qkv, m->ssm_nin, Ly.ssm_conv, d.ssm_d_conv, ring_in, ring_out, Ly.ssm_dt, Ly.ssm_a, B,
+                           nk, nv, d.rms_eps, s.lq, s.lk, s.lv, s.lg, s.lb, st);
+      launch_gdn_step(s.lq, s.lk, s.lv, s.lg, s.lb, B, nv, st_in, st_out, 1.0f / sqrtf((float)d.ssm_d_state), s.lo,
+                      st);
+      launch_gated_norm_quant(s.lo, s.qkv + m->ssm_c, m->ssm_nin, Ly.ssm_norm, B, nv, d.rms_eps, s.act_qs, s.act_d,
+                              st);
+      if (tr && !trace_codes(tr->q_attn_out, il, s.act_qs, B, m->ssm_vd, st, att_w)) return KD_ERR_HIP;
+    } else {
     if (Ly.wqkv_pair_rows) {  // the product rotates q/k and appends k/v itself
       launch_mmvq_rope(Ly.wqkv, s.act_qs, s.act_d, B, s.qkv, ldqkv, H, G, hd, s.cs, d.rope_base, rc, capacity, st,
                        prenormed ? s.ss : nullptr, D, d.rms_eps, kv8);
@@ -390,7 +489,8 @@ static kd_status decode_step_impl(const kd_model* m, int32_t B, const float* x_i
     } else {
       launch_fa(plan, s.qkv, ldqkv, rc, capacity, scale, s.attn, s.act_qs, s.act_d, s.fa_ws, st, gate, kvf);
     }
-    if (tr && !trace_codes(tr->q_attn_out, il, s.act_qs, B, H * hd, st)) return KD_ERR_HIP;
+    if (tr && !trace_codes(tr->q_attn_out, il, s.act_qs, B, H * hd, st, att_w)) return KD_ERR_HIP;
+    }  // attention
     if (norm_fusable(il)) {
       // O product + residual add + the FFN RMSNorm's quantiser and sums of squares; the
       // gate/up product applies 1/rms, SwiGLU and the quantiser for down

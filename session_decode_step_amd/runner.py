@@ -26,12 +26,27 @@ class GpuWorkload:
         self.model = model if model is not None else W.make_model(sp, wl.code, wl.seed)
         self.km = KdModel(self.model, device, fused=fused)
         n_sess = len(wl.prefill)
+        lin = tuple(sp.linear_layers)
         self.caches = SessionCaches(n_sess, sp.n_layers, sp.n_head_kv, wl.capacity, sp.head_dim, device,
-                                    fp8=sp.kv_fp8, q8=sp.kv_q8)
+                                    fp8=sp.kv_fp8, q8=sp.kv_q8, linear_layers=lin,
+                                    rec_bytes=self.km.recurrent_state_bytes() if lin else 0)
         fill_sessions = range(n_sess) if sessions is None else sessions
+        if lin:   # recurrent states before step 0, in the buffers the first step reads (pos % 2)
+            C, dc = sp.ssm_conv_dim, sp.ssm_d_conv
+            ring = ((dc - 1) * C + 3) // 4 * 4
+            state = sp.ssm_n_v * sp.ssm_d_state ** 2
+            assert 4 * 2 * (ring + state) == self.km.recurrent_state_bytes()
+            self.rec_layout = (ring, state, dc, C)
+            for s in fill_sessions:
+                par = wl.prefill[s] % 2
+                for il in lin:
+                    rings, states = self.caches.recurrent_views(s, il, *self.rec_layout)
+                    conv, S = W.recurrent_prefill(wl, s, il)
+                    rings[par].copy_(torch.from_numpy(conv))
+                    states[par].copy_(torch.from_numpy(S.reshape(-1)))
         if fill == "seeded":
             for s in fill_sessions:
-                pairs = [(s, il) for il in range(sp.n_layers)]
+                pairs = [(s, il) for il in range(sp.n_layers) if il not in lin]
                 for (ss, il), (k, v) in zip(pairs, W.kv_prefill_many(wl, pairs)):
                     self.caches.fill_prefill(ss, il, k, v)
         else:
@@ -39,7 +54,7 @@ class GpuWorkload:
             for s in fill_sessions:
                 gen.manual_seed(1000003 * (wl.seed + 1) + s)
                 L = wl.prefill[s]
-                t = self.caches.t[s]
+                t = self.caches.t[s]   # every layer's K/V (a linear layer's are never read)
                 if sp.kv_fp8:   # random E4M3 bytes: sign, exponent field 4 .. 8, mantissa
                     c = torch.randint(0, 80, t[:, :, :, :L].shape, generator=gen, device=device)
                     t[:, :, :, :L] = (((c & 1) << 7) | ((4 + (c >> 4)) << 3) | ((c >> 1) & 7)).to(torch.uint8)

@@ -326,3 +326,86 @@ def test_noalloc_attention_rejects_partials_beyond_its_scratch():
     assert L.kd_fa_decode_ragged_noalloc(0x1000, B, H, G, hd, kb, vb, t, cap, 0.088, 0x2000, None) \
         == kd.KD_ERR_WORKSPACE
     assert b"scratch" in L.kd_last_error()
+
+
+def _fake_hybrid(n_layers=2, d=256, nk=2, nv=4, dc=4):
+    """_fake_model with layer 0 a gated delta-rule layer (128-wide heads, nk key / nv value heads)."""
+    desc, layers = _fake_model(n_layers, d)
+    C_, vd = 2 * 128 * nk + 128 * nv, 128 * nv
+    D = layers[0]
+    D.mixer = 1
+    D.wqkv = _fake_weight(kd.KD_FMT_Q8_0, C_ + vd + 2 * nv, d, 0x30000000)
+    D.wo = _fake_weight(kd.KD_FMT_Q8_0, d, vd, 0x31000000)
+    D.ssm_conv, D.ssm_dt, D.ssm_a, D.ssm_norm = 0x32000000, 0x32100000, 0x32200000, 0x32300000
+    desc.ssm_d_state, desc.ssm_n_k, desc.ssm_n_v, desc.ssm_d_conv = 128, nk, nv, dc
+    return desc, layers
+
+
+def test_linear_layers_are_validated():
+    """A gated delta-rule layer needs its conv, dt, a and norm arrays, an input projection of
+    conv channels + z + beta + alpha rows, an out projection of n_v 128 columns, no attention
+    options, 128-wide heads with n_v a multiple of n_k; its recurrent state is two conv rings
+    [(d_conv - 1), C] (each padded to 4 floats) and two states [n_v, 128, 128], fp32."""
+    L = kd.lib()
+    h = C.c_void_p()
+
+    def create(edit=lambda desc, l: None):
+        desc, layers = _fake_hybrid()
+        edit(desc, layers[0])
+        st = L.kd_model_create(C.byref(desc), C.byref(h))
+        if st == kd.KD_OK:
+            L.kd_model_destroy(h)
+        return st
+
+    assert create() == kd.KD_OK
+    desc, layers = _fake_hybrid()
+    assert L.kd_model_create(C.byref(desc), C.byref(h)) == kd.KD_OK
+    try:
+        ring = (4 - 1) * (2 * 128 * 2 + 128 * 4)
+        assert L.kd_recurrent_state_bytes(h) == 4 * 2 * (ring + 4 * 128 * 128)
+    finally:
+        L.kd_model_destroy(h)
+    desc, layers = _fake_model()
+    assert L.kd_model_create(C.byref(desc), C.byref(h)) == kd.KD_OK
+    assert L.kd_recurrent_state_bytes(h) == 0           # no linear layer
+    L.kd_model_destroy(h)
+    assert create(lambda d, l: setattr(l, "ssm_norm", 0)) == kd.KD_ERR_INVALID
+    assert b"conv, dt, a or norm" in L.kd_last_error()
+    assert create(lambda d, l: setattr(l, "ssm_norm", 0x32300004)) == kd.KD_ERR_INVALID      # unaligned
+    assert create(lambda d, l: setattr(l, "mixer", 2)) == kd.KD_ERR_INVALID
+    assert create(lambda d, l: setattr(l, "swa_window", 64)) == kd.KD_ERR_INVALID
+    assert create(lambda d, l: setattr(d, "ssm_d_state", 64)) == kd.KD_ERR_UNSUPPORTED
+    assert create(lambda d, l: setattr(d, "ssm_n_v", 3)) == kd.KD_ERR_UNSUPPORTED             # not a multiple of n_k
+    assert create(lambda d, l: setattr(d, "ssm_d_conv", 1)) == kd.KD_ERR_UNSUPPORTED
+    assert create(lambda d, l: setattr(l, "wo", _fake_weight(kd.KD_FMT_Q8_0, 256, 4 * 64, 0x31000000))) \
+        == kd.KD_ERR_INVALID
+    assert b"out projection" in L.kd_last_error()
+    assert create(lambda d, l: setattr(l, "wqkv", _fake_weight(kd.KD_FMT_Q8_0, 1536, 256, 0x30000000))) \
+        == kd.KD_ERR_INVALID
+    assert b"input projection" in L.kd_last_error()
+
+
+def test_linear_layer_states_are_checked_per_step():
+    """kd_decode_step refuses a null or unaligned recurrent state and two rows whose states
+    overlap (each row owns its state for the step)."""
+    L = kd.lib()
+    desc, layers = _fake_hybrid()
+    h = C.c_void_p()
+    assert L.kd_model_create(C.byref(desc), C.byref(h)) == kd.KD_OK
+    try:
+        rb = L.kd_recurrent_state_bytes(h)
+        pos = (C.c_int32 * 2)(10, 20)
+        vb = (C.c_void_p * 4)(0x5000, 0x6000, 0x7000, 0x8000)
+        need = L.kd_decode_step_workspace(h, 2, pos)
+
+        def step(s0, s1):
+            kb = (C.c_void_p * 4)(s0, s1, 0x3000, 0x4000)    # layer 0: states; layer 1: K caches
+            return L.kd_decode_step(h, 2, 0x100, pos, kb, vb, 64, 0x200, 0x300, need - 1, None)
+
+        assert step(0x40000000, 0x40000000 + rb) == kd.KD_ERR_WORKSPACE   # the states pass
+        assert step(0x40000000, 0x40000000 + rb - 256) == kd.KD_ERR_INVALID
+        assert b"share a recurrent state" in L.kd_last_error()
+        assert step(0, 0x50000000) == kd.KD_ERR_INVALID
+        assert step(0x40000008, 0x50000000) == kd.KD_ERR_INVALID
+    finally:
+        L.kd_model_destroy(h)

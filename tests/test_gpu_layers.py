@@ -43,6 +43,7 @@ LAYER_BAR = 2e-3       # elementwise, scaled by max(|ref_i|, rms(row)): the stat
 DELTA_BAR = 2e-3       # normwise, on the layer's own contribution
 FREE_BAR = 1e-2        # free-running layer (quantiser flips included)
 P_BAR = 1e-6           # router weights
+STATE_BAR = 1e-4       # a linear layer's new recurrent state, relative to its rms
 TIE_REL = 1e-6         # router near-tie report threshold
 
 kd = pytest.importorskip("session_decode_step_amd")
@@ -52,11 +53,14 @@ from session_decode_step_amd.runner import GpuWorkload  # noqa: E402
 def _gpu_slots_into(oc, gw, step, layers):
     """Copy the K/V bytes the GPU wrote at ``step`` into the oracle's caches."""
     wl = gw.wl
+    lin = set(wl.spec.linear_layers)
     for b, (sess, _) in enumerate(wl.rows):
         if sess not in oc.K:
             continue
         p = wl.positions(step)[b]
         for il in layers:
+            if il in lin:
+                continue
             oc.K[sess][il][:, p] = gw.caches.t[sess][il, 0, :, p].cpu().numpy()
             oc.V[sess][il][:, p] = gw.caches.t[sess][il, 1, :, p].cpu().numpy()
 
@@ -84,8 +88,9 @@ def _slot_excess(g, r):
 def _forced_codes(rec, il, rows, sp):
     """The GPU's codes of layer il's quantisations, untiled, for the followed rows."""
     K = sp.n_expert_used
+    w_out = sp.ssm_value_dim if il in sp.linear_layers else sp.n_head * sp.head_dim
     f = {"attn_in": untile_codes(rec["q_attn_in"][il][rows], sp.d),
-         "attn_out": untile_codes(rec["q_attn_out"][il][rows], sp.n_head * sp.head_dim)}
+         "attn_out": untile_codes(rec["q_attn_out"][il][rows][:, :(w_out + 127) // 128 * 128], w_out)}
     if "q_ffn_in" in rec:
         f["ffn_in"] = untile_codes(rec["q_ffn_in"][il][rows], sp.d)
     if sp.ffn:
@@ -106,7 +111,8 @@ def _check_layers(gw, steps, layers, rows=None, dense_budget=6 << 30, head=True,
     sess = [wl.rows[b][0] for b in rows]
     oc = oracle.OracleCaches(wl, sessions=sorted(set(sess)), layers=layers)
     dense = oracle.DenseWeights(dense_budget)
-    worst, worst_delta, worst_free, n_ids, near, flips, codes = 0.0, 0.0, 0.0, 0, 0, 0, 0
+    worst, worst_delta, worst_free, n_ids, near, flips, codes, worst_state = 0.0, 0.0, 0.0, 0, 0, 0, 0, 0.0
+    lin = set(sp.linear_layers)
     for s in steps:
         say(f"  {sp.name} step {s}: gpu")
         rec = gw.step_trace(s)
@@ -115,10 +121,16 @@ def _check_layers(gw, steps, layers, rows=None, dense_budget=6 << 30, head=True,
         for il in layers:
             x_in = resid[il][rows]
             gpu = resid[il + 1][rows]
+            linear = il in lin
+            if linear:   # the recurrent state each evaluation starts from
+                snap = {ss: {k: v.copy() for k, v in oc.R[ss][il].items()} for ss in set(sess)}
             if free:
                 say(f"  step {s} layer {il}: oracle (free)")
                 ref = oracle.decode_layer(gw.model, il, oc, x_in, sess, pos, dense=dense)
                 worst_free = max(worst_free, assert_close_rows(gpu, ref, FREE_BAR, f"step {s} layer {il} (free)"))
+                if linear:
+                    for ss in snap:
+                        oc.R[ss][il] = {k: v.copy() for k, v in snap[ss].items()}
             info, qrec = {}, []
             say(f"  step {s} layer {il}: oracle (forced codes)")
             ref = oracle.decode_layer(gw.model, il, oc, x_in, sess, pos, dense=dense, info=info,
@@ -131,6 +143,20 @@ def _check_layers(gw, steps, layers, rows=None, dense_budget=6 << 30, head=True,
             dnorm, _ = row_errors(gpu - x_in, ref - x_in)
             worst_delta = max(worst_delta, float(dnorm.max()))
             assert dnorm.max() <= DELTA_BAR, f"step {s} layer {il}: contribution normwise error {dnorm.max():.3e}"
+            if linear:   # the new recurrent state; then the GPU's becomes the oracle's (teacher forcing)
+                for i, b in enumerate(rows):
+                    rings, states = gw.caches.recurrent_views(sess[i], il, *gw.rec_layout)
+                    new = (pos[i] + 1) % 2
+                    g_ring = rings[new].cpu().numpy().astype(np.float64)
+                    g_S = states[new].cpu().numpy().astype(np.float64).reshape(oc.R[sess[i]][il]["S"].shape)
+                    o_ring, o_S = oc.R[sess[i]][il]["conv"], oc.R[sess[i]][il]["S"]
+                    np.testing.assert_array_equal(g_ring[:-1], o_ring[:-1])      # shifted: copies
+                    assert_close_rows(g_ring[-1:], o_ring[-1:], 1e-5, f"step {s} layer {il} row {b} ring")
+                    srms = np.sqrt(np.mean(o_S ** 2))
+                    worst_state = max(worst_state, float(np.abs(g_S - o_S).max() / srms))
+                    assert np.abs(g_S - o_S).max() <= STATE_BAR * srms, (s, il, b)
+                    oc.R[sess[i]][il] = {"conv": g_ring, "S": g_S}
+                continue
             # the appended K/V: the oracle's values, each rounded either way to the cache format
             for i, b in enumerate(rows):
                 p = pos[i]
@@ -162,7 +188,8 @@ def _check_layers(gw, steps, layers, rows=None, dense_budget=6 << 30, head=True,
         _gpu_slots_into(oc, gw, s, layers)
     say(f"  worst forced layer error {worst:.3e}, contribution {worst_delta:.3e}; free-running {worst_free:.3e}; "
         f"{flips} of {codes} GPU codes are the other valid rounding"
-        + (f"; {n_ids} routings equal, {near} near ties" if sp.n_experts else ""))
+        + (f"; {n_ids} routings equal, {near} near ties" if sp.n_experts else "")
+        + (f"; recurrent states within {worst_state:.3e} of their rms" if lin else ""))
     assert near == 0 or n_ids > 0
 
 
@@ -198,3 +225,14 @@ def test_c5_every_moe_layer_with_exact_routing():
     wl = W.workload("c5")
     gw = GpuWorkload(wl)
     _check_layers(gw, [0], list(range(wl.spec.n_layers)), dense_budget=2 << 30, free=False)
+
+
+def test_hybrid_gdn_stack_every_layer_and_lm_head():
+    """The 8-layer Q8_0 stack with gated delta-rule layers in place of attention on layers 0-2
+    and 4-6 (8 key / 16 value heads of 128, conv width 4), B = 4, three steps: every layer and
+    the lm_head teacher-forced, each linear layer's new recurrent state (conv ring and state)
+    against the oracle's, then carried into the next step."""
+    say("hybrid per layer")
+    wl = W.workload("hybrid", B=4, steps=3)
+    gw = GpuWorkload(wl)
+    _check_layers(gw, [0, 1, 2], list(range(wl.spec.n_layers)))

@@ -366,3 +366,31 @@ def test_c5_moe_verify_rows():
     # the recorded step is the plain step
     y_plain = gw.step(0).cpu().numpy()
     np.testing.assert_array_equal(y_plain.view(np.uint32), y.view(np.uint32))
+
+
+def _state_bytes(gw, b, s):
+    """The recurrent states (conv ring and state, every linear layer) that row b's step s wrote."""
+    wl = gw.wl
+    sess, _ = wl.rows[b]
+    new = (wl.positions(s)[b] + 1) % 2
+    parts = []
+    for il in wl.spec.linear_layers:
+        rings, states = gw.caches.recurrent_views(sess, il, *gw.rec_layout)
+        parts += [rings[new].cpu().numpy().ravel(), states[new].cpu().numpy()]
+    return np.concatenate(parts).view(np.uint32).copy()
+
+
+def test_hybrid_gdn_stack_end_to_end():
+    """8 layers, six of them gated delta-rule layers, lm_head 32000, B = 4, four steps: the
+    oracle follows two rows end to end (its own recurrent states carried across the steps),
+    and every row of the last step, with the states it wrote, is bit-identical to that row
+    stepped alone (the step reads the states of parity pos % 2 and writes the other ones,
+    so stepping again is idempotent)."""
+    say("hybrid")
+    wl = W.workload("hybrid", B=4, steps=4)
+    gw = GpuWorkload(wl)
+    outs = _oracle_follow(gw, [0, 3], range(4), dense_budget=6 << 30)
+    before = {b: _state_bytes(gw, b, 3) for b in range(4)}
+    _bit_identity(gw, range(4), 3, outs[-1])
+    for b in range(4):
+        np.testing.assert_array_equal(_state_bytes(gw, b, 3), before[b])
