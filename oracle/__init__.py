@@ -16,7 +16,7 @@ Pins (tests marked ``not gpu``) check it against hand-worked blocks, closed form
 brute force and library routines; the end-to-end values of whole configurations
 have no external pin beyond that chain (parity unpinned beyond the op-level pins).
 """
-from .ops import (QK, accept_drafts, gated_rmsnorm, gdn_prep, l2_normalize, softplus, ssm_conv_step, attention, block_dots, dequantize, dequantize_act, e4m3_decode,  # noqa: F401
+from .ops import (QK, KQ_BYTES, kquant_dequantize, kquant_fields, kquant_scale_min, accept_drafts, gated_rmsnorm, gdn_prep, l2_normalize, softplus, ssm_conv_step, attention, block_dots, dequantize, dequantize_act, e4m3_decode,  # noqa: F401
                   e4m3_encode, e4m3_values, embed_rows, gdn_step, greedy_token, sigmoid,
                   mmvq, mmvq_blocks, q8_kv_decode, q8_kv_encode, q8_kv_row_bytes, quantize_act, rmsnorm, rope_neox, router_topk, silu, swiglu, weight_codes)
 from .step import DenseWeights, OracleCaches, decode_layer, decode_step, moe_ffn, output_head  # noqa: F401

@@ -46,9 +46,117 @@ def weight_codes(w: Dict, r0: int = 0, r1: Optional[int] = None) -> Tuple[np.nda
 
 
 def dequantize(w: Dict, r0: int = 0, r1: Optional[int] = None) -> np.ndarray:
-    """Dense fp64 values ``[r1 - r0, k]`` of a quantised matrix: ``w = d * q`` per block."""
+    """Dense fp64 values ``[r1 - r0, k]`` of a quantised matrix: ``w = d * q`` per block
+    (Q8_0, Q4_0), or the super-block formulas of :func:`kquant_fields` (Q4_K, Q5_K, Q6_K)."""
+    if w["fmt"] in KQ_BYTES:
+        return kquant_dequantize(w, r0, r1)
     q, d = weight_codes(w, r0, r1)
     return (q.astype(np.float64) * d[:, :, None]).reshape(q.shape[0], -1)
+
+
+# ---------------------------------------------------------------------------------------
+# K-quant weight codecs (super-blocks of 256 values)
+# ---------------------------------------------------------------------------------------
+# The pages name Q4_K, Q5_K and Q6_K among the weight types a batched decode must cover
+# (hf2q ADR-040, "Quant scope": the fused batch decode path covers every inference ftype,
+# Q4_K, Q5_K and Q6_K among them; memra-engine decode_batch.rs, the exact-16 admission list
+# admits QT_Q4_K, QT_Q5_K and QT_Q6_K) but do not spell out their bytes.  The reading used
+# here is the GGUF k-quant block format those names denote, one super-block of 256 values
+# per record, rows of k / 256 records:
+#   Q4_K, 144 bytes: fp16 d, fp16 dmin, 12 bytes of 6-bit sub-block scales and mins, 128
+#         bytes of 4-bit codes.  Value = d * sc_j * q - dmin * m_j in 32-value sub-block j.
+#   Q5_K, 176 bytes: as Q4_K, then 32 bytes of fifth bits before the 4-bit codes; q has 5 bits.
+#   Q6_K, 210 bytes: 128 bytes of low 4 bits, 64 bytes of upper 2 bits, 16 int8 scales (one
+#         per 16 values), fp16 d.  Value = d * sc_(e // 16) * (q - 32), q of 6 bits.
+KQ_BYTES = {"q4_k": 144, "q5_k": 176, "q6_k": 210}
+QK_K = 256
+
+
+def kquant_scale_min(sc12: np.ndarray, j: int) -> Tuple[np.ndarray, np.ndarray]:
+    """6-bit scale and min of sub-block j (0..7) from the 12 packed bytes (``[..., 12]``).
+
+    Sub-blocks 0..3 keep both in the low 6 bits of bytes j (scale) and j + 4 (min).
+    Sub-blocks 4..7 keep their low 4 bits in byte j + 4 (scale in the low nibble, min in the
+    high one) and their top 2 bits in the spare top bits of bytes j - 4 (scale) and j (min).
+    """
+    b = sc12.astype(np.int64)
+    if j < 4:
+        return b[..., j] & 63, b[..., j + 4] & 63
+    sc = (b[..., j + 4] & 15) | ((b[..., j - 4] >> 6) << 4)
+    mn = (b[..., j + 4] >> 4) | ((b[..., j] >> 6) << 4)
+    return sc, mn
+
+
+def _f16_at(blocks: np.ndarray, off: int) -> np.ndarray:
+    return np.ascontiguousarray(blocks[..., off:off + 2]).view(np.float16)[..., 0].astype(np.float64)
+
+
+def kquant_fields(w: Dict, r0: int = 0, r1: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """The fields of rows [r0, r1) of a K-quant matrix, per super-block s of each row:
+
+    * ``q``: the codes ``[n, nsb, 256]`` in value order (int64; Q4_K 0..15, Q5_K 0..31,
+      Q6_K 0..63 before its offset of 32);
+    * Q4_K / Q5_K: ``d``, ``dmin`` ``[n, nsb]`` and the sub-block ``sc``, ``m`` ``[n, nsb, 8]``;
+    * Q6_K: ``d`` ``[n, nsb]`` and the int8 ``sc`` ``[n, nsb, 16]``.
+
+    Value order within a super-block: Q4_K/Q5_K code bytes come in 4 runs of 32; byte l of
+    run c holds value 64c + l in its low nibble and value 64c + 32 + l in its high nibble;
+    the fifth bit of value 64c + l is bit 2c of fifth-bit byte l, of value 64c + 32 + l bit
+    2c + 1.  Q6_K: two halves of 128 values, half h with low bytes [64h, 64h + 64) and upper
+    bytes [32h, 32h + 32); for l < 32, low byte 64h + l gives values 128h + l (low nibble)
+    and 128h + 64 + l (high nibble), low byte 64h + 32 + l gives 128h + 32 + l and 128h + 96 + l,
+    and upper byte 32h + l gives those four values' top two bits in bit pairs 0-1, 2-3, 4-5, 6-7
+    (in the order 128h + l, 128h + 32 + l, 128h + 64 + l, 128h + 96 + l).
+    """
+    fmt, k = w["fmt"], w["k"]
+    r1 = w["n"] if r1 is None else r1
+    assert k % QK_K == 0
+    nsb, BS = k // QK_K, KQ_BYTES[fmt]
+    blk = np.ascontiguousarray(w["qs"][r0:r1]).view(np.uint8).reshape(r1 - r0, nsb, BS)
+    n = r1 - r0
+    if fmt in ("q4_k", "q5_k"):
+        out = {"d": _f16_at(blk, 0), "dmin": _f16_at(blk, 2)}
+        sc12 = blk[..., 4:16]
+        pairs = [kquant_scale_min(sc12, j) for j in range(8)]
+        out["sc"] = np.stack([p[0] for p in pairs], axis=-1)
+        out["m"] = np.stack([p[1] for p in pairs], axis=-1)
+        qs = blk[..., -128:].astype(np.int64).reshape(n, nsb, 4, 32)      # runs c, bytes l
+        q = np.empty((n, nsb, 4, 2, 32), dtype=np.int64)                  # value 64c + 32h + l
+        q[:, :, :, 0] = qs & 15
+        q[:, :, :, 1] = qs >> 4
+        if fmt == "q5_k":
+            qh = blk[..., 16:48].astype(np.int64)                          # byte l
+            for c in range(4):
+                for h in range(2):
+                    q[:, :, c, h] += 16 * ((qh >> (2 * c + h)) & 1)
+        out["q"] = q.reshape(n, nsb, QK_K)
+        return out
+    if fmt == "q6_k":
+        ql = blk[..., 0:128].astype(np.int64).reshape(n, nsb, 2, 2, 32)    # half h, run r, byte l
+        qh = blk[..., 128:192].astype(np.int64).reshape(n, nsb, 2, 32)     # half h, byte l
+        q = np.empty((n, nsb, 2, 4, 32), dtype=np.int64)                   # value 128h + 32i + l
+        q[:, :, :, 0] = (ql[:, :, :, 0] & 15) | (((qh >> 0) & 3) << 4)
+        q[:, :, :, 1] = (ql[:, :, :, 1] & 15) | (((qh >> 2) & 3) << 4)
+        q[:, :, :, 2] = (ql[:, :, :, 0] >> 4) | (((qh >> 4) & 3) << 4)
+        q[:, :, :, 3] = (ql[:, :, :, 1] >> 4) | (((qh >> 6) & 3) << 4)
+        return {"q": q.reshape(n, nsb, QK_K), "sc": blk[..., 192:208].view(np.int8).astype(np.int64),
+                "d": _f16_at(blk, 208)}
+    raise ValueError(fmt)
+
+
+def kquant_dequantize(w: Dict, r0: int = 0, r1: Optional[int] = None) -> np.ndarray:
+    """Dense fp64 values ``[r1 - r0, k]`` of a K-quant matrix (formulas of the block format)."""
+    f = kquant_fields(w, r0, r1)
+    q = f["q"].astype(np.float64)
+    n, nsb, _ = q.shape
+    if w["fmt"] == "q6_k":
+        scale = f["d"][:, :, None] * f["sc"].astype(np.float64)            # per 16 values
+        v = (q - 32.0).reshape(n, nsb, 16, 16) * scale[:, :, :, None]
+    else:
+        scale = f["d"][:, :, None] * f["sc"].astype(np.float64)            # per 32 values
+        mins = f["dmin"][:, :, None] * f["m"].astype(np.float64)
+        v = q.reshape(n, nsb, 8, 32) * scale[:, :, :, None] - mins[:, :, :, None]
+    return v.reshape(n, nsb * QK_K)
 
 
 # ---------------------------------------------------------------------------------------

@@ -53,6 +53,64 @@ def test_q4_0_codes_cover_range_and_rows():
     assert v[0, 32 + 5] == 2.0 * (5 - 8) and v[1, 32 + 16 + 2] == 4.0 * (((2 * 3) % 16) - 8)
 
 
+def _kq_record(fmt, hexs):
+    rec = np.frombuffer(bytes.fromhex(hexs), np.uint8)
+    assert rec.size == ops.KQ_BYTES[fmt]
+    return {"fmt": fmt, "n": 1, "k": 256, "qs": rec.reshape(1, -1), "d": np.zeros((1, 0), np.float16)}
+
+
+def test_kquant_packed_scales_and_mins_by_hand():
+    g = _gold("kquant_records.json")
+    b = np.frombuffer(bytes.fromhex(g["scales_hex"]), np.uint8)
+    got = [ops.kquant_scale_min(b, j) for j in range(8)]
+    assert [int(s) for s, _ in got] == g["scale_min_by_hand"]["sc"]
+    assert [int(m) for _, m in got] == g["scale_min_by_hand"]["m"]
+
+
+@pytest.mark.parametrize("fmt", ["q4_k", "q5_k", "q6_k"])
+def test_kquant_golden_records(fmt):
+    """Hand-worked values of one record per format (codes in both nibbles and every code run,
+    sub-block scales and mins of both packings, fifth and upper bits, signed Q6_K scales)."""
+    g = _gold("kquant_records.json")[fmt]
+    v = ops.dequantize(_kq_record(fmt, g["record_hex"]))[0]
+    for e, want in g["values"].items():
+        assert v[int(e)] == want, (fmt, e, v[int(e)], want)
+
+
+def test_kquant_structure():
+    """Rows and super-blocks keep their own fields; Q5_K with no fifth bits is Q4_K with the same
+    fields; a Q4_K record of zero codes holds -dmin m_j in sub-block j; a Q6_K record of codes
+    32 is zero."""
+    rng = np.random.default_rng(5)
+    rec4 = rng.integers(0, 256, size=(3, 2, 144), dtype=np.uint8)
+    rec4[:, :, 0:2] = np.array([0x00, 0x3C], np.uint8)      # d = 1
+    rec4[:, :, 2:4] = np.array([0x00, 0x40], np.uint8)      # dmin = 2
+    w4 = {"fmt": "q4_k", "n": 3, "k": 512, "qs": rec4.reshape(3, -1), "d": np.zeros((3, 0), np.float16)}
+    rec5 = np.zeros((3, 2, 176), np.uint8)
+    rec5[:, :, :16] = rec4[:, :, :16]
+    rec5[:, :, 48:] = rec4[:, :, 16:]
+    w5 = {"fmt": "q5_k", "n": 3, "k": 512, "qs": rec5.reshape(3, -1), "d": np.zeros((3, 0), np.float16)}
+    v4 = ops.dequantize(w4)
+    np.testing.assert_array_equal(v4, ops.dequantize(w5))
+    np.testing.assert_array_equal(ops.dequantize(w4, 1, 3), v4[1:3])
+    # second super-block of row 2 decoded alone
+    one = {"fmt": "q4_k", "n": 1, "k": 256, "qs": rec4[2, 1][None, :], "d": np.zeros((1, 0), np.float16)}
+    np.testing.assert_array_equal(ops.dequantize(one)[0], v4[2, 256:])
+    zero = rec4.copy()
+    zero[:, :, 16:] = 0
+    wz = {"fmt": "q4_k", "n": 3, "k": 512, "qs": zero.reshape(3, -1), "d": np.zeros((3, 0), np.float16)}
+    vz = ops.dequantize(wz).reshape(3, 2, 8, 32)
+    for j in range(8):
+        _, m = ops.kquant_scale_min(zero[:, :, 4:16], j)
+        np.testing.assert_array_equal(vz[:, :, j, :], np.broadcast_to(-2.0 * m[:, :, None], (3, 2, 32)))
+    rec6 = np.zeros((1, 210), np.uint8)
+    rec6[0, 128:192] = 0xAA                                  # upper bits 2 in every pair: q = 32
+    rec6[0, 192:208] = 7
+    rec6[0, 208:210] = [0x00, 0x3C]
+    np.testing.assert_array_equal(ops.dequantize({"fmt": "q6_k", "n": 1, "k": 256, "qs": rec6,
+                                                  "d": np.zeros((1, 0), np.float16)}), np.zeros((1, 256)))
+
+
 # --------------------------------------------------------------------------- quantiser (O3)
 def test_act_quant_golden_blocks():
     g = _gold("act_quant_blocks.json")

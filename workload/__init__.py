@@ -22,6 +22,9 @@ Storage conventions of the arrays produced here (both sides read them):
 * Q8_0 ``qs``: int8 ``[n_out, k]`` row-major; ``d``: fp16 ``[n_out, k/32]``.
 * Q4_0 ``qs``: uint8 ``[n_out, k/2]`` (16 bytes per 32-element block, the
   block's bytes contiguous); ``d``: fp16 ``[n_out, k/32]``.
+* Q4_K / Q5_K / Q6_K ``qs``: uint8 ``[n_out, (k/256) * record]``, each row's 256-value
+  records of 144 / 176 / 210 bytes back to back (their scales inside); ``d``: empty
+  ``[n_out, 0]``.
 * KV prefill for one (session, layer): fp16 ``[G, L, hd]`` for K and for V (uint8 E4M3
   codes of the same shape for FP8 caches; uint8 rows ``[G, L, hd + 16]`` for int8 caches).
 """
@@ -63,7 +66,7 @@ class ModelSpec:
     n_head_kv: int
     head_dim: int
     ffn: int                 # dense SwiGLU width; 0 = none (attention-only or MoE)
-    fmt: str                 # "q8_0" or "q4_0" for every quantised matrix
+    fmt: str                 # "q8_0", "q4_0", "q4_k", "q5_k" or "q6_k": every quantised matrix not in fmts
     vocab: int = 0           # lm_head rows; 0 = no lm_head
     final_norm: bool = False
     n_experts: int = 0       # 0 = dense FFN
@@ -83,6 +86,11 @@ class ModelSpec:
     ssm_n_k: int = 0                     # key heads (q and k)
     ssm_n_v: int = 0                     # value heads
     ssm_d_conv: int = 4                  # conv kernel width
+    fmts: Tuple[Tuple[str, str], ...] = ()  # per-matrix format overrides: (role, fmt), role in
+    #                                      wqkv, wo, w_gate, w_up, w_down, lm_head
+
+    def fmt_of(self, role: str) -> str:
+        return dict(self.fmts).get(role, self.fmt)
 
     @property
     def qkv_rows(self) -> int:
@@ -155,6 +163,10 @@ SPEC_C5 = ModelSpec("c5_moe8layer_d2816_q4_0", 8, 2816, 16, 8, 128, 0, "q4_0", f
 # four layers (attention on layers 3 and 7): 8 key heads and 16 value heads of 128, conv width 4
 SPEC_HYBRID = dataclasses.replace(SPEC_C2, name="hybrid_8layer_d2048_q8_0_gdn_lm32000",
                                   linear_layers=(0, 1, 2, 4, 5, 6), ssm_n_k=8, ssm_n_v=16)
+# the same 8-layer decoder with K-quant weights in a mix of the kind mixed k-quant files use:
+# Q4_K for O and gate/up, Q5_K for QKV, Q6_K for down and the lm_head
+SPEC_KQ = dataclasses.replace(SPEC_C2, name="kq_8layer_d2048_q4_k_q5_k_q6_k_lm32000", fmt="q4_k",
+                              fmts=(("wqkv", "q5_k"), ("w_down", "q6_k"), ("lm_head", "q6_k")))
 
 
 def c3_lengths(seed: int = 0, B: int = 16) -> List[int]:
@@ -183,6 +195,9 @@ def workload(name: str, B: Optional[int] = None, seed: int = 0, steps: Optional[
         B = B or 8
         return Workload(4, SPEC_C4, [4096] * B, [(b, 0) for b in range(B)], steps or 32,
                         4096 + 32, seed)
+    if name == "kq":
+        B = B or 8
+        return Workload(7, SPEC_KQ, [1238] * B, [(b, 0) for b in range(B)], steps or 4, 1238 + 64, seed)
     if name == "hybrid":
         B = B or 4
         return Workload(6, SPEC_HYBRID, [1238] * B, [(b, 0) for b in range(B)], steps or 4, 1238 + 64, seed)
@@ -211,8 +226,32 @@ def draw_q4_0(rq: np.random.Generator, rd: np.random.Generator, n: int, k: int) 
     return {"fmt": "q4_0", "n": n, "k": k, "qs": qs, "d": d}
 
 
+KQ_RECORD = {"q4_k": 144, "q5_k": 176, "q6_k": 210}   # bytes per 256-value super-block
+
+
+def draw_kquant(fmt: str, rq: np.random.Generator, rd: np.random.Generator, n: int, k: int) -> Dict:
+    """A K-quant matrix: every byte of each 256-value record uniformly random (codes, fifth
+    or upper bits, packed 6-bit scales and mins, int8 scales), then its fp16 scale fields set
+    to drawn values: Q4_K / Q5_K ``d = |N(0, 1)| 0.04 / (15 * 63)`` and
+    ``dmin = |N(0, 1)| 0.02 / 63`` at bytes 0 and 2; Q6_K ``d = |N(0, 1)| 0.02 / (32 * 127)`` at
+    byte 208 (weights of about the other formats' magnitude)."""
+    BS, nsb = KQ_RECORD[fmt], k // 256
+    rec = rq.integers(0, 256, size=(n, nsb, BS), dtype=np.uint8)
+    if fmt == "q6_k":
+        d = (np.abs(rd.standard_normal((n, nsb), dtype=np.float32)) * np.float32(0.02 / (32 * 127))).astype(np.float16)
+        rec[:, :, 208:210] = d.view(np.uint8).reshape(n, nsb, 2)
+    else:
+        d = (np.abs(rd.standard_normal((n, nsb), dtype=np.float32)) * np.float32(0.04 / (15 * 63))).astype(np.float16)
+        dm = (np.abs(rd.standard_normal((n, nsb), dtype=np.float32)) * np.float32(0.02 / 63)).astype(np.float16)
+        rec[:, :, 0:2] = d.view(np.uint8).reshape(n, nsb, 2)
+        rec[:, :, 2:4] = dm.view(np.uint8).reshape(n, nsb, 2)
+    return {"fmt": fmt, "n": n, "k": k, "qs": rec.reshape(n, nsb * BS), "d": np.zeros((n, 0), dtype=np.float16)}
+
+
 def draw_weight(fmt: str, seed: int, code: int, tq: int, td: int, layer: int, n: int, k: int) -> Dict:
     rq, rd = rng_for(seed, code, tq, layer), rng_for(seed, code, td, layer)
+    if fmt in KQ_RECORD:
+        return draw_kquant(fmt, rq, rd, n, k)
     return (draw_q8_0 if fmt == "q8_0" else draw_q4_0)(rq, rd, n, k)
 
 
@@ -269,8 +308,8 @@ def make_layer(spec: ModelSpec, code: int, seed: int, il: int) -> Dict:
         "swa_window": spec.swa_window if il in spec.swa_layers else 0,
         "attn_gate": bool(spec.attn_gate),
         "attn_norm": draw_gain(seed, code, T_ATTN_NORM, il, d),
-        "wqkv": draw_weight(fmt, seed, code, T_WQKV_Q, T_WQKV_D, il, spec.qkv_rows, d),
-        "wo": draw_weight(fmt, seed, code, T_WO_Q, T_WO_D, il, d, spec.n_head * spec.head_dim),
+        "wqkv": draw_weight(spec.fmt_of("wqkv"), seed, code, T_WQKV_Q, T_WQKV_D, il, spec.qkv_rows, d),
+        "wo": draw_weight(spec.fmt_of("wo"), seed, code, T_WO_Q, T_WO_D, il, d, spec.n_head * spec.head_dim),
     }
     if spec.qk_norm:
         L["q_norm"] = draw_gain(seed, code, T_Q_NORM, il, spec.head_dim)
@@ -279,9 +318,9 @@ def make_layer(spec: ModelSpec, code: int, seed: int, il: int) -> Dict:
         L["ffn_norm"] = draw_gain(seed, code, T_FFN_NORM, il, d)
     if spec.ffn:
         F = spec.ffn
-        L["w_gate"] = draw_weight(fmt, seed, code, T_GATE_Q, T_GATE_D, il, F, d)
-        L["w_up"] = draw_weight(fmt, seed, code, T_UP_Q, T_UP_D, il, F, d)
-        L["w_down"] = draw_weight(fmt, seed, code, T_DOWN_Q, T_DOWN_D, il, d, F)
+        L["w_gate"] = draw_weight(spec.fmt_of("w_gate"), seed, code, T_GATE_Q, T_GATE_D, il, F, d)
+        L["w_up"] = draw_weight(spec.fmt_of("w_up"), seed, code, T_UP_Q, T_UP_D, il, F, d)
+        L["w_down"] = draw_weight(spec.fmt_of("w_down"), seed, code, T_DOWN_Q, T_DOWN_D, il, d, F)
     if spec.n_experts:
         E, Fe, Fs = spec.n_experts, spec.expert_ffn, spec.shared_ffn
         r = rng_for(seed, code, T_ROUTER, il)
@@ -307,7 +346,7 @@ def make_model(spec: ModelSpec, code: int, seed: int = 0, threads: int = 8) -> D
         layers = list(ex.map(lambda il: make_layer(spec, code, seed, il), range(spec.n_layers)))
     m: Dict = {"spec": spec, "layers": layers}
     m["final_norm"] = draw_gain(seed, code, T_FINAL_NORM, 0, spec.d) if spec.final_norm else None
-    m["lm_head"] = (draw_weight(spec.fmt, seed, code, T_LM_Q, T_LM_D, 0, spec.vocab, spec.d)
+    m["lm_head"] = (draw_weight(spec.fmt_of("lm_head"), seed, code, T_LM_Q, T_LM_D, 0, spec.vocab, spec.d)
                     if spec.vocab else None)
     return m
 
@@ -378,19 +417,20 @@ def kv_prefill_many(wl: Workload, pairs, threads: int = 8):
 
 def algorithmic_bytes_weights(spec: ModelSpec) -> int:
     """Bytes of every quantised matrix and fp32 router the step streams once (dense view)."""
-    bpw = 34 if spec.fmt == "q8_0" else 18     # bytes per 32-element block
-
-    def mat(n, k):
-        return n * (k // 32) * bpw
+    def mat(n, k, role=""):
+        fmt = spec.fmt_of(role)
+        if fmt in KQ_RECORD:
+            return n * (k // 256) * KQ_RECORD[fmt]
+        return n * (k // 32) * (34 if fmt == "q8_0" else 18)    # bytes per 32-element block
 
     tot = 0
     for _ in range(spec.n_layers):
-        tot += mat(spec.qkv_rows, spec.d) + mat(spec.d, spec.n_head * spec.head_dim)
+        tot += mat(spec.qkv_rows, spec.d, "wqkv") + mat(spec.d, spec.n_head * spec.head_dim, "wo")
         if spec.ffn:
-            tot += 2 * mat(spec.ffn, spec.d) + mat(spec.d, spec.ffn)
+            tot += mat(spec.ffn, spec.d, "w_gate") + mat(spec.ffn, spec.d, "w_up") + mat(spec.d, spec.ffn, "w_down")
         if spec.n_experts:
             tot += spec.n_experts * spec.d * 4
             tot += 2 * mat(spec.shared_ffn, spec.d) + mat(spec.d, spec.shared_ffn)
     if spec.vocab:
-        tot += mat(spec.vocab, spec.d)
+        tot += mat(spec.vocab, spec.d, "lm_head")
     return tot
