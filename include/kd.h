@@ -43,6 +43,24 @@
  *     value = nibble - 8).
  *   - d (both formats): fp16, 64 per tile: d[t * 64 + 4 n + j] = scale of row 16r+n,
  *     block 4q+j.
+ *   - K-quant formats (KD_FMT_Q4_K, KD_FMT_Q5_K, KD_FMT_Q6_K; k % 256 == 0): the GGUF
+ *     k-quant weight types the pages list among the formats a batched decode must cover
+ *     (hf2q ADR-040 "Quant scope"; memra-engine decode_batch.rs exact-16 admission list).
+ *     Source rows are k / 256 records of 256 values (Q4_K 144 bytes: fp16 d, fp16 dmin,
+ *     12 bytes of packed 6-bit sub-block scales and mins, 128 bytes of 4-bit codes, value
+ *     d sc_j q - dmin m_j in 32-value sub-block j; Q5_K 176 bytes: the same with 32 bytes
+ *     of fifth bits before the codes; Q6_K 210 bytes: 128 bytes of low 4 bits, 64 bytes of
+ *     upper 2 bits, 16 int8 scales, fp16 d, value d sc_(e/16) (q - 32)).  Tiles: qs bytes
+ *     [16 l + 4 j, +4) = the low 4 bits of the codes P_g of block 4q+j, byte i holding
+ *     element 4g+i in its low nibble and 4g+16+i in its high nibble; then (Q5_K, 1280
+ *     bytes per tile) byte 1024 + 4 l + j = the fifth bits (bit i: element 4g+i, bit 4+i:
+ *     4g+16+i), or (Q6_K, 1536 bytes per tile) bytes [1024 + 8 l + 2 j, +2) = the upper
+ *     two bits (pair i of the first byte: element 4g+i; of the second: 4g+16+i); Q4_K tiles
+ *     are 1024 bytes.  d: 192 bytes per tile: bytes [8 n + 2 j, +2) = sub-block scale and
+ *     min of block 4q+j of row 16r+n (Q6_K: the int8 scales of its two 16-value halves),
+ *     bytes [128 + 4 n, +4) = the row's fp16 d and dmin of that super-block (Q6_K: d, 0).
+ *     A tiled K-quant matrix is 2.8-5.6 % larger than its records (d and dmin once per
+ *     half record, the 12-byte scale packing unpacked to 8 bytes per quad).
  *  Quantised activations (kd_act_q8) for B rows of length k: int8 codes
  *  qs[(b * NQ + q) * 128 + 32 g + 8 j + e] = code of element P_g[e] of block 4q+j of row b,
  *  and fp32 scales d[b * 4 NQ + blk]; padded blocks have code 0 and scale 0.
@@ -68,7 +86,14 @@ typedef enum {
   KD_ERR_HIP = -5           /* a HIP launch failed */
 } kd_status;
 
-typedef enum { KD_FMT_Q8_0 = 1, KD_FMT_Q4_0 = 2, KD_FMT_F32 = 3 } kd_format;
+typedef enum {
+  KD_FMT_Q8_0 = 1,
+  KD_FMT_Q4_0 = 2,
+  KD_FMT_F32 = 3,
+  KD_FMT_Q4_K = 4,
+  KD_FMT_Q5_K = 5,
+  KD_FMT_Q6_K = 6
+} kd_format;
 /* KV cache element formats (kd_model_desc.kv_format). */
 typedef enum { KD_KV_F16 = 0, KD_KV_FP8_E4M3 = 1, KD_KV_Q8_0 = 2 } kd_kv_format;
 
@@ -102,8 +127,10 @@ size_t kd_act_qs_bytes(int32_t B, int32_t k);
 size_t kd_act_d_bytes(int32_t B, int32_t k);
 
 /* Repack a matrix from the row-major block layout (Q8_0: int8 [n_out][k]; Q4_0: uint8
- * [n_out][k/2], 16 bytes per block; d: fp16 [n_out][k/32]; device pointers) into the tiled
- * layout above (dst_qs / dst_d sized by kd_weight_*_bytes).  Once per matrix, at load. */
+ * [n_out][k/2], 16 bytes per block; d: fp16 [n_out][k/32]; K-quants: uint8 records
+ * [n_out][k/256][144 | 176 | 210] with src_d unused and may be NULL; device pointers) into
+ * the tiled layout above (dst_qs / dst_d sized by kd_weight_*_bytes).  Once per matrix, at
+ * load. */
 kd_status kd_pack_weight(int32_t fmt, int32_t n_out, int32_t k, const void* src_qs, const void* src_d,
                          void* dst_qs, void* dst_d, void* stream);
 
@@ -123,6 +150,13 @@ kd_status kd_quantize_act_q8(const float* x, int32_t B, int32_t k, int32_t ldx, 
  * tiled codes stay under 2 GiB (KD_ERR_UNSUPPORTED otherwise). */
 kd_status kd_mmvq_q8_0(const kd_weight* W, kd_act_q8 x, int32_t B, float* y, int32_t ldy, void* stream);
 kd_status kd_mmvq_q4_0(const kd_weight* W, kd_act_q8 x, int32_t B, float* y, int32_t ldy, void* stream);
+/* The same product for any quantised format (Q8_0, Q4_0, Q4_K, Q5_K, Q6_K).  K-quants:
+ * y[b][n] = sum_blk d_x[b][blk] (d sc_j S[b][n][blk] - dmin m_j X[b][blk]) for Q4_K / Q5_K,
+ * X the sum of the activation codes of the block, and sum_blk d_x d (sc' S' + sc'' S'') for
+ * Q6_K over the block's two 16-value halves; every S and X an exact integer, the fp32 terms
+ * in block order (a function of k only: rows are B-invariant, as for the other formats).
+ * The fused products below (SwiGLU, add + RMSNorm, RoPE) take every format as well. */
+kd_status kd_mmvq(const kd_weight* W, kd_act_q8 x, int32_t B, float* y, int32_t ldy, void* stream);
 
 /* ---- row operations (fp32, rows of length n, row stride n) ------------------------- */
 /* y = x / sqrt(mean(x^2) + eps) * g  (memra-engine decode_batch.rs attn_norm / output norm). */
@@ -449,7 +483,8 @@ kd_status kd_verify_accept(const int32_t* greedy, const int32_t* fed, int32_t n_
 
 /* ---- test exports ---------------------------------------------------------------------- */
 /* The exact int32 block dot products S[b][n][blk] (b < B, n < n_out, blk < k/32) that the
- * mmvq kernel computes for this matrix and activation (same kernel, epilogue replaced). */
+ * mmvq kernel computes for this matrix and activation (same kernel, epilogue replaced).
+ * Q8_0 and Q4_0 only (KD_ERR_UNSUPPORTED for the K-quant formats). */
 kd_status kd_debug_block_dots(const kd_weight* W, kd_act_q8 x, int32_t B, int32_t* S, void* stream);
 /* kd_fa_decode_ragged with a forced chunk size (keys per split, >= 1) for split-invariance
  * tests; the workspace must hold ceil(t_b / chunk) splits per row. */

@@ -21,8 +21,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkd.so")
 
 KD_OK, KD_ERR_INVALID, KD_ERR_UNSUPPORTED, KD_ERR_CAPACITY, KD_ERR_WORKSPACE, KD_ERR_HIP = 0, -1, -2, -3, -4, -5
-KD_FMT_Q8_0, KD_FMT_Q4_0, KD_FMT_F32 = 1, 2, 3
-FMT_CODE = {"q8_0": KD_FMT_Q8_0, "q4_0": KD_FMT_Q4_0}
+KD_FMT_Q8_0, KD_FMT_Q4_0, KD_FMT_F32, KD_FMT_Q4_K, KD_FMT_Q5_K, KD_FMT_Q6_K = 1, 2, 3, 4, 5, 6
+FMT_CODE = {"q8_0": KD_FMT_Q8_0, "q4_0": KD_FMT_Q4_0, "q4_k": KD_FMT_Q4_K, "q5_k": KD_FMT_Q5_K, "q6_k": KD_FMT_Q6_K}
+KQ_FORMATS = (KD_FMT_Q4_K, KD_FMT_Q5_K, KD_FMT_Q6_K)
 KD_MAX_B = 16
 
 
@@ -86,6 +87,7 @@ SIGNATURES = {
     "kd_quantize_act_q8": (_I, [_P, _I, _I, _I, KdAct, _P]),
     "kd_mmvq_q8_0": (_I, [_PW, KdAct, _I, _P, _I, _P]),
     "kd_mmvq_q4_0": (_I, [_PW, KdAct, _I, _P, _I, _P]),
+    "kd_mmvq": (_I, [_PW, KdAct, _I, _P, _I, _P]),
     "kd_rmsnorm_rows": (_I, [_P, _P, _P, _I, _I, _F, _P]),
     "kd_add_rmsnorm_rows": (_I, [_P, _P, _P, _P, _P, _I, _I, _F, _P]),
     "kd_rope_neox_rows": (_I, [_P, _I, _I, _I, _PI, _F, _P]),
@@ -189,11 +191,12 @@ def kd_pack_weight(w: Dict, device="cuda", stream=None) -> PackedWeight:
     """Upload a row-major block matrix (``{"fmt","n","k","qs","d"}`` numpy) and repack it on the GPU."""
     fmt, n, k = FMT_CODE[w["fmt"]], int(w["n"]), int(w["k"])
     src_qs = torch.from_numpy(np.ascontiguousarray(w["qs"]).view(np.uint8)).to(device)
-    src_d = torch.from_numpy(np.ascontiguousarray(w["d"]).view(np.int16)).to(device)
+    # K-quant records carry their own scales (no separate d)
+    src_d = None if fmt in KQ_FORMATS else torch.from_numpy(np.ascontiguousarray(w["d"]).view(np.int16)).to(device)
     qs = torch.empty(lib().kd_weight_qs_bytes(fmt, n, k), dtype=torch.uint8, device=device)
     dd = torch.empty(lib().kd_weight_d_bytes(fmt, n, k) // 2, dtype=torch.int16, device=device)
-    _check(lib().kd_pack_weight(fmt, n, k, src_qs.data_ptr(), src_d.data_ptr(), qs.data_ptr(), dd.data_ptr(),
-                                _stream(stream)), "kd_pack_weight")
+    _check(lib().kd_pack_weight(fmt, n, k, src_qs.data_ptr(), None if src_d is None else src_d.data_ptr(),
+                                qs.data_ptr(), dd.data_ptr(), _stream(stream)), "kd_pack_weight")
     torch.cuda.current_stream().synchronize()   # the sources are freed on return
     return PackedWeight(fmt, n, k, qs, dd)
 
@@ -283,6 +286,11 @@ def kd_mmvq_q8_0(W: PackedWeight, x: Act, B: int, y: Optional[torch.Tensor] = No
 
 def kd_mmvq_q4_0(W: PackedWeight, x: Act, B: int, y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     return _mmvq("kd_mmvq_q4_0", W, x, B, y, stream)
+
+
+def kd_mmvq(W: PackedWeight, x: Act, B: int, y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The product for any quantised format (Q8_0, Q4_0, Q4_K, Q5_K, Q6_K)."""
+    return _mmvq("kd_mmvq", W, x, B, y, stream)
 
 
 def kd_mmvq_swiglu(W: PackedWeight, x: Act, B: int, out: Optional[Act] = None, stream=None) -> Act:
@@ -389,9 +397,11 @@ def weight_group(W: PackedWeight, group: int, rows: int) -> PackedWeight:
     a multiple of 16: the group's tiles are one contiguous range)."""
     assert rows % 16 == 0
     tiles = (rows // 16) * ((W.k + 127) // 128)
-    per_qs = W.qs.numel() * W.qs.element_size() // (W.n_out // 16 * ((W.k + 127) // 128))
+    all_tiles = W.n_out // 16 * ((W.k + 127) // 128)
+    per_qs = W.qs.numel() * W.qs.element_size() // all_tiles
+    per_d = W.d.numel() // all_tiles                        # int16 entries per tile
     qs = W.qs.view(torch.uint8)[group * tiles * per_qs:(group + 1) * tiles * per_qs]
-    d = W.d[group * tiles * 64:(group + 1) * tiles * 64]
+    d = W.d[group * tiles * per_d:(group + 1) * tiles * per_d]
     return PackedWeight(W.fmt, rows, W.k, qs, d)
 
 

@@ -193,6 +193,10 @@ __device__ __forceinline__ uint2 buf8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   const v2i v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX);
   return make_uint2((uint32_t)v.x, (uint32_t)v.y);
 }
+template <int AUX>
+__device__ __forceinline__ uint32_t buf4u(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX);
+}
 __device__ __forceinline__ float buf4f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __int_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
@@ -219,6 +223,8 @@ struct RowMap {
 
 // Whether a Q8_0/Q4_0 matrix fits the product (k <= mmvq_max_k(), tiled arrays < 2 GiB).
 bool mmvq_weight_fits(int fmt, int n_out, int k);
+bool mmvq_fmt_ok(int fmt, int k);     // a quantised weight format, k a multiple of its block
+bool mmvq_swiglu_fits(int k);         // the SwiGLU product's LDS at this k fits a CU
 int mmvq_max_k();
 void launch_mmvq(const kd_weight& W, const int8_t* xq, const float* xd, int B, float* y, int ldy,
                  hipStream_t st, const RowMap* map = nullptr, int32_t* debug_S = nullptr);

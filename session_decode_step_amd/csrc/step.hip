@@ -72,10 +72,13 @@ static kd_status check_weight(const char* name, int il, const kd_weight& w, int 
   KD_REQUIRE(w.n_out == n_out && w.k == k, KD_ERR_INVALID, "kd_model_create: layer %d %s: shape %d x %d, expected %d x %d",
              il, name, w.n_out, w.k, n_out, k);
   if (quant_only) {
-    KD_REQUIRE(w.fmt == KD_FMT_Q8_0 || w.fmt == KD_FMT_Q4_0, KD_ERR_UNSUPPORTED,
-               "kd_model_create: layer %d %s: format %d is not Q8_0/Q4_0", il, name, w.fmt);
+    KD_REQUIRE(w.fmt == KD_FMT_Q8_0 || w.fmt == KD_FMT_Q4_0 || w.fmt == KD_FMT_Q4_K || w.fmt == KD_FMT_Q5_K ||
+                   w.fmt == KD_FMT_Q6_K,
+               KD_ERR_UNSUPPORTED, "kd_model_create: layer %d %s: format %d is not a quantised weight format", il, name,
+               w.fmt);
     KD_REQUIRE(w.d, KD_ERR_INVALID, "kd_model_create: layer %d %s: null scales", il, name);
-    KD_REQUIRE(k % 32 == 0, KD_ERR_UNSUPPORTED, "kd_model_create: layer %d %s: k=%d not a multiple of 32", il, name, k);
+    KD_REQUIRE(mmvq_fmt_ok(w.fmt, k), KD_ERR_UNSUPPORTED,
+               "kd_model_create: layer %d %s: k=%d not a multiple of the format's block (32; K-quants 256)", il, name, k);
     KD_REQUIRE(aligned16(w.qs) && aligned16(w.d), KD_ERR_INVALID, "kd_model_create: layer %d %s: unaligned", il, name);
     KD_REQUIRE(mmvq_weight_fits(w.fmt, n_out, k), KD_ERR_UNSUPPORTED,
                "kd_model_create: layer %d %s: %d x %d exceeds the product's limits (k <= %d, tiled codes under 2 GiB)",
@@ -160,6 +163,8 @@ extern "C" kd_status kd_model_create(const kd_model_desc* desc, kd_model** out) 
         KD_TRY(check_weight("w_gate", il, L.w_gate, m.ffn, d));
         KD_TRY(check_weight("w_up", il, L.w_up, m.ffn, d));
       } else {
+        KD_REQUIRE(mmvq_swiglu_fits(d), KD_ERR_UNSUPPORTED,
+                   "kd_model_create: layer %d: d=%d exceeds the fused SwiGLU product's LDS", il, d);
         KD_TRY(check_weight("w_gate (interleaved gate+up)", il, L.w_gate, 2 * m.ffn, d));
         KD_REQUIRE(m.ffn % 32 == 0, KD_ERR_UNSUPPORTED,
                    "kd_model_create: interleaved gate/up needs ffn %% 32 == 0 (ffn=%d)", m.ffn);
@@ -172,6 +177,8 @@ extern "C" kd_status kd_model_create(const kd_model_desc* desc, kd_model** out) 
         KD_TRY(check_weight("e_gate", il, L.e_gate, m.n_experts * m.expert_ffn, d));
         KD_TRY(check_weight("e_up", il, L.e_up, m.n_experts * m.expert_ffn, d));
       } else {  // each expert's gate and up interleaved in blocks of 32 rows
+        KD_REQUIRE(mmvq_swiglu_fits(d), KD_ERR_UNSUPPORTED,
+                   "kd_model_create: layer %d: d=%d exceeds the fused SwiGLU product's LDS", il, d);
         KD_TRY(check_weight("e_gate (interleaved expert gate+up)", il, L.e_gate, m.n_experts * 2 * m.expert_ffn, d));
       }
       KD_TRY(check_weight("e_down", il, L.e_down, m.n_experts * d, m.expert_ffn));
@@ -180,6 +187,8 @@ extern "C" kd_status kd_model_create(const kd_model_desc* desc, kd_model** out) 
         KD_TRY(check_weight("s_gate", il, L.s_gate, m.shared_ffn, d));
         KD_TRY(check_weight("s_up", il, L.s_up, m.shared_ffn, d));
       } else {
+        KD_REQUIRE(mmvq_swiglu_fits(d), KD_ERR_UNSUPPORTED,
+                   "kd_model_create: layer %d: d=%d exceeds the fused SwiGLU product's LDS", il, d);
         KD_TRY(check_weight("s_gate (interleaved shared gate+up)", il, L.s_gate, 2 * m.shared_ffn, d));
       }
       KD_TRY(check_weight("s_down", il, L.s_down, d, m.shared_ffn));

@@ -409,3 +409,36 @@ def test_linear_layer_states_are_checked_per_step():
         assert step(0x40000008, 0x50000000) == kd.KD_ERR_INVALID
     finally:
         L.kd_model_destroy(h)
+
+
+def test_kquant_layouts_and_validation():
+    """K-quant tiles: 1024 / 1280 / 1536 code bytes and 192 scale bytes per tile; k must be a
+    multiple of 256 (one record) for the pack, the products and kd_model_create; the block-dot
+    test export takes Q8_0 / Q4_0 only; kd_mmvq refuses the fp32 router format."""
+    L = kd.lib()
+    for fmt, tile in ((kd.KD_FMT_Q4_K, 1024), (kd.KD_FMT_Q5_K, 1280), (kd.KD_FMT_Q6_K, 1536)):
+        assert L.kd_weight_qs_bytes(fmt, 20, 512) == 2 * 4 * tile       # 2 row groups x 4 quads
+        assert L.kd_weight_d_bytes(fmt, 20, 512) == 2 * 4 * 192
+        assert L.kd_weight_qs_bytes(fmt, 20, 384) == 0                  # not a whole record
+        assert L.kd_pack_weight(fmt, 20, 384, 0x1000, None, 0x2000, 0x3000, None) == kd.KD_ERR_UNSUPPORTED
+        act = kd.KdAct(0x3000, 0x4000)
+        bad = kd.KdWeight(fmt, 64, 384, 0x1000, 0x2000)
+        assert L.kd_mmvq(C.byref(bad), act, 2, 0x5000, 64, None) == kd.KD_ERR_UNSUPPORTED
+        ok = kd.KdWeight(fmt, 64, 512, 0x1000, 0x2000)
+        assert L.kd_mmvq(C.byref(ok), act, 2, None, 64, None) == kd.KD_ERR_INVALID      # gets to the output check
+        assert L.kd_mmvq_q4_0(C.byref(ok), act, 2, 0x5000, 64, None) == kd.KD_ERR_UNSUPPORTED   # format mismatch
+        assert L.kd_debug_block_dots(C.byref(ok), act, 2, 0x5000, None) == kd.KD_ERR_UNSUPPORTED
+    f32 = kd.KdWeight(kd.KD_FMT_F32, 64, 512, 0x1000, None)
+    assert L.kd_mmvq(C.byref(f32), kd.KdAct(0x3000, 0x4000), 2, 0x5000, 64, None) == kd.KD_ERR_UNSUPPORTED
+    # a model with K-quant matrices: accepted at d = 256, refused where a k is not a whole record
+    h = C.c_void_p()
+    desc, layers = _fake_model()
+    for il in range(desc.n_layers):
+        layers[il].wqkv = _fake_weight(kd.KD_FMT_Q5_K, (4 + 2 * 2) * 64, 256, 0x10000000 * (il + 1) + 0x100000)
+        layers[il].w_down = _fake_weight(kd.KD_FMT_Q6_K, 256, 512, 0x10000000 * (il + 1) + 0x600000)
+    assert L.kd_model_create(C.byref(desc), C.byref(h)) == kd.KD_OK
+    L.kd_model_destroy(h)
+    desc, layers = _fake_model(F=640)
+    layers[0].w_down = _fake_weight(kd.KD_FMT_Q4_K, 256, 640, 0x10600000)
+    assert L.kd_model_create(C.byref(desc), C.byref(h)) == kd.KD_ERR_UNSUPPORTED
+    assert b"w_down" in L.kd_last_error()

@@ -28,6 +28,18 @@ def sync():
     torch.cuda.synchronize()
 
 
+def _drawer(fmt):
+    """The seeded matrix draw of a weight format, as f(rq, rd, n, k)."""
+    if fmt in W.KQ_RECORD:
+        return lambda rq, rd, n, k: W.draw_kquant(fmt, rq, rd, n, k)
+    return W.draw_q8_0 if fmt == "q8_0" else W.draw_q4_0
+
+
+def product_fn(fmt):
+    """The plain product entry point of a format (the K-quants go through kd_mmvq)."""
+    return {"q8_0": kd.kd_mmvq_q8_0, "q4_0": kd.kd_mmvq_q4_0}.get(fmt, kd.kd_mmvq)
+
+
 # ------------------------------------------------------------------ activation quantiser
 @pytest.mark.parametrize("B,k", [(1, 256), (5, 704), (16, 2048), (3, 14336)])
 def test_act_quant_codes_and_scales_exact(B, k):
@@ -51,13 +63,17 @@ def test_act_quant_codes_and_scales_exact(B, k):
 # quads) products, the 8-layer stack's lm_head (32000 x 2048 Q8_0) and the largest k (16384)
 SHAPES = [("q8_0", 100, 704), ("q8_0", 512, 2048), ("q4_0", 100, 704), ("q4_0", 4096, 4096), ("q8_0", 48, 256),
           ("q4_0", 4096, 14336), ("q8_0", 32000, 2048), ("q4_0", 272, 16384)]
+# K-quants (k a multiple of 256): ragged rows, one record per row, an odd number of records
+# (a quad pair split across waves), the 8-layer mixed stack's shapes and the largest k
+SHAPES_KQ = [("q4_k", 100, 768), ("q5_k", 48, 256), ("q6_k", 100, 768), ("q4_k", 4096, 4096), ("q5_k", 3072, 2048),
+             ("q6_k", 2048, 5632), ("q6_k", 32000, 2048), ("q4_k", 272, 16384), ("q5_k", 2816, 2816)]
 
 
 @pytest.mark.parametrize("fmt,n,k", SHAPES)
 def test_block_dots_exact(fmt, n, k):
     say(f"block_dots {fmt} n={n} k={k}")
     r = np.random.default_rng(7 + n)
-    w = (W.draw_q8_0 if fmt == "q8_0" else W.draw_q4_0)(r, r, n, k)
+    w = _drawer(fmt)(r, r, n, k)
     x = r.standard_normal((16, k)).astype(np.float32)
     pw = kd.kd_pack_weight(w)
     act = kd.kd_quantize_act_q8(dev(x))
@@ -67,15 +83,15 @@ def test_block_dots_exact(fmt, n, k):
     np.testing.assert_array_equal(S.cpu().numpy(), ops.block_dots(w, xq))
 
 
-@pytest.mark.parametrize("fmt,n,k", SHAPES)
+@pytest.mark.parametrize("fmt,n,k", SHAPES + SHAPES_KQ)
 def test_mmvq_matches_oracle_and_rows_are_b_invariant(fmt, n, k):
     say(f"mmvq {fmt} n={n} k={k}")
     r = np.random.default_rng(11 + n + k)
-    w = (W.draw_q8_0 if fmt == "q8_0" else W.draw_q4_0)(r, r, n, k)
+    w = _drawer(fmt)(r, r, n, k)
     x = r.standard_normal((16, k)).astype(np.float32)
     pw = kd.kd_pack_weight(w)
     act = kd.kd_quantize_act_q8(dev(x))
-    fn = kd.kd_mmvq_q8_0 if fmt == "q8_0" else kd.kd_mmvq_q4_0
+    fn = product_fn(fmt)
     y16 = fn(pw, act, 16)
     sync()
     xq, xd = ops.quantize_act(x)
@@ -92,6 +108,62 @@ def test_mmvq_matches_oracle_and_rows_are_b_invariant(fmt, n, k):
         act1 = kd.kd_quantize_act_q8(dev(x[b:b + 1]))
         y1 = fn(pw, act1, 1).cpu().numpy()
         np.testing.assert_array_equal(y1[0], y16h[b])
+
+
+@pytest.mark.parametrize("fmt", ["q4_k", "q5_k", "q6_k"])
+def test_kquant_tiles_hold_the_records(fmt):
+    """Packed K-quant tiles against the layout kd.h states, byte by byte, decoded from the
+    oracle's fields of the same records: low code nibbles, fifth / upper bits, per-block
+    scale bytes and the super-block's fp16 scales (rows past n_out zero)."""
+    say(f"kquant tiles {fmt}")
+    r = np.random.default_rng(91)
+    n, k = 20, 512
+    w = W.draw_kquant(fmt, r, r, n, k)
+    pw = kd.kd_pack_weight(w)
+    sync()
+    qs = pw.qs.cpu().numpy().view(np.uint8)
+    dd = pw.d.cpu().numpy().view(np.uint8)
+    f = ops.kquant_fields(w)
+    TQ = {"q4_k": 1024, "q5_k": 1280, "q6_k": 1536}[fmt]
+    NQ, NR = k // 128, 2
+    assert qs.size == NR * NQ * TQ and dd.size == NR * NQ * 192
+    codes = f["q"].reshape(n, k // 32, 32)                     # [row, block, element]
+    raw = np.ascontiguousarray(w["qs"]).reshape(n, k // 256, -1)
+    for row in range(NR * 16):
+        rr, nn = row // 16, row % 16
+        for q in range(NQ):
+            t = rr * NQ + q
+            for j in range(4):
+                blk = 4 * q + j
+                c = codes[row, blk] if row < n else np.zeros(32, np.int64)
+                for g in range(4):
+                    lane = 16 * g + nn
+                    lo, hi = c[4 * g:4 * g + 4], c[4 * g + 16:4 * g + 20]
+                    np.testing.assert_array_equal(qs[t * TQ + lane * 16 + 4 * j:t * TQ + lane * 16 + 4 * j + 4],
+                                                  (lo & 15) | ((hi & 15) << 4))
+                    if fmt == "q5_k":
+                        want = sum(int((lo[i] >> 4) & 1) << i for i in range(4)) + \
+                            sum(int((hi[i] >> 4) & 1) << (4 + i) for i in range(4))
+                        assert qs[t * TQ + 1024 + lane * 4 + j] == want
+                    if fmt == "q6_k":
+                        assert qs[t * TQ + 1024 + lane * 8 + 2 * j] == sum(int((lo[i] >> 4) & 3) << (2 * i) for i in range(4))
+                        assert qs[t * TQ + 1024 + lane * 8 + 2 * j + 1] == sum(int((hi[i] >> 4) & 3) << (2 * i)
+                                                                               for i in range(4))
+                sb, sub = blk // 8, blk % 8
+                pair = dd[t * 192 + 8 * nn + 2 * j:t * 192 + 8 * nn + 2 * j + 2]
+                if row >= n:
+                    assert pair.tolist() == [0, 0]
+                elif fmt == "q6_k":
+                    assert pair.view(np.int8).tolist() == [int(f["sc"][row, sb, 2 * sub]), int(f["sc"][row, sb, 2 * sub + 1])]
+                else:
+                    assert pair.tolist() == [int(f["sc"][row, sb, sub]), int(f["m"][row, sb, sub])]
+            sup = dd[t * 192 + 128 + 4 * nn:t * 192 + 128 + 4 * nn + 4]
+            if row >= n:
+                assert sup.tolist() == [0, 0, 0, 0]
+            elif fmt == "q6_k":
+                assert sup.tolist() == raw[row, q // 2, 208:210].tolist() + [0, 0]
+            else:
+                assert sup.tolist() == raw[row, q // 2, 0:4].tolist()
 
 
 def test_mmvq_rejects_wrong_format():
@@ -231,18 +303,19 @@ def test_fa_row_bits_independent_of_the_split_kernel_variant():
 
 # ------------------------------------------------------------------ products with fused epilogues
 @pytest.mark.parametrize("fmt,F,k,B", [("q4_0", 1024, 512, 8), ("q8_0", 704, 256, 5), ("q4_0", 2048, 4096, 16),
-                                       ("q4_0", 352, 704, 1)])
+                                       ("q4_0", 352, 704, 1), ("q4_k", 1024, 512, 8), ("q6_k", 704, 2816, 3),
+                                       ("q5_k", 512, 4096, 16)])
 def test_mmvq_swiglu_equals_unfused_path(fmt, F, k, B):
     """The SwiGLU epilogue gives the bytes of product -> kd_swiglu_rows -> quantiser, and the
     dequantised rows match the oracle's silu(gate) * up."""
     say(f"mmvq_swiglu {fmt} F={F} k={k} B={B}")
     r = np.random.default_rng(F + k + B)
-    draw = W.draw_q8_0 if fmt == "q8_0" else W.draw_q4_0
+    draw = _drawer(fmt)
     gate, up = draw(r, r, F, k), draw(r, r, F, k)
     x = r.standard_normal((B, k)).astype(np.float32)
     act = kd.kd_quantize_act_q8(dev(x))
     fused = kd.kd_mmvq_swiglu(kd.kd_pack_weight(kd.interleave_gate_up(gate, up)), act, B)
-    fn = kd.kd_mmvq_q8_0 if fmt == "q8_0" else kd.kd_mmvq_q4_0
+    fn = product_fn(fmt)
     g = fn(kd.kd_pack_weight(gate), act, B)
     u = fn(kd.kd_pack_weight(up), act, B)
     ref_act = kd.kd_quantize_act_q8(kd.kd_swiglu_rows(g, u))
@@ -260,7 +333,8 @@ def test_mmvq_swiglu_equals_unfused_path(fmt, F, k, B):
     assert np.all(np.abs(deq - a_ref) <= 0.5 * np.repeat(s1.reshape(B, -1), 32, axis=1) + 2e-3 * np.abs(a_ref) + 1e-6)
 
 
-@pytest.mark.parametrize("fmt,H,G,hd,B", [("q8_0", 4, 2, 64, 2), ("q4_0", 32, 8, 128, 8), ("q4_0", 16, 8, 128, 16)])
+@pytest.mark.parametrize("fmt,H,G,hd,B", [("q8_0", 4, 2, 64, 2), ("q4_0", 32, 8, 128, 8), ("q4_0", 16, 8, 128, 16),
+                                          ("q5_k", 32, 8, 128, 8), ("q6_k", 4, 2, 64, 2)])
 def test_mmvq_rope_equals_unfused_path(fmt, H, G, hd, B):
     """The RoPE/append epilogue writes the q bits and the fp16 K/V bytes of product ->
     kd_rope_neox_rows -> kd_kv_append; rows are B-invariant."""
@@ -268,7 +342,7 @@ def test_mmvq_rope_equals_unfused_path(fmt, H, G, hd, B):
     r = np.random.default_rng(H * hd + B)
     k = 512
     n = (H + 2 * G) * hd
-    w = (W.draw_q8_0 if fmt == "q8_0" else W.draw_q4_0)(r, r, n, k)
+    w = _drawer(fmt)(r, r, n, k)
     x = r.standard_normal((B, k)).astype(np.float32)
     act = kd.kd_quantize_act_q8(dev(x))
     cap = 64
@@ -278,7 +352,7 @@ def test_mmvq_rope_equals_unfused_path(fmt, H, G, hd, B):
     q_f = torch.zeros((B, H * hd), dtype=torch.float32, device="cuda")
     kd.kd_mmvq_rope(kd.kd_pack_weight(kd.rope_pair_rows(w, H + 2 * G, hd)), act, B, H, G, hd, q_f,
                     [c[0].data_ptr() for c in fused_c], [c[1].data_ptr() for c in fused_c], pos, cap, 10000.0)
-    fn = kd.kd_mmvq_q8_0 if fmt == "q8_0" else kd.kd_mmvq_q4_0
+    fn = product_fn(fmt)
     y = fn(kd.kd_pack_weight(w), act, B)
     qk = y[:, :(H + G) * hd].contiguous().view(B, H + G, hd)
     kd.kd_rope_neox_rows(qk, pos, 10000.0)
@@ -419,7 +493,8 @@ def test_fa_decode_at_the_key_limit():
 
 
 @pytest.mark.parametrize("fmt,n,k,B", [("q4_0", 4096, 4096, 8), ("q8_0", 2048, 2048, 3), ("q4_0", 4096, 14336, 16),
-                                       ("q4_0", 2816, 2048, 5)])
+                                       ("q4_0", 2816, 2048, 5), ("q4_k", 4096, 4096, 8), ("q6_k", 2048, 5632, 5),
+                                       ("q5_k", 2816, 2048, 3)])
 def test_resnorm_pair_matches_oracle(fmt, n, k, B):
     """The split RMSNorm: kd_mmvq_resnorm (x1 = res + W Q(a), the block codes of x1 * gain,
     the block sums of x1^2) and its consumers kd_mmvq_swiglu_normed / kd_mmvq_rope_normed,
@@ -429,7 +504,7 @@ def test_resnorm_pair_matches_oracle(fmt, n, k, B):
     from oracle.step import _q_forced
     say(f"resnorm pair {fmt} n={n} k={k} B={B}")
     r = np.random.default_rng(n + k + B)
-    draw = W.draw_q8_0 if fmt == "q8_0" else W.draw_q4_0
+    draw = _drawer(fmt)
     w = draw(r, r, n, k)
     a = r.standard_normal((B, k)).astype(np.float32)
     res = r.standard_normal((B, n)).astype(np.float32)

@@ -236,3 +236,13 @@ def test_hybrid_gdn_stack_every_layer_and_lm_head():
     wl = W.workload("hybrid", B=4, steps=3)
     gw = GpuWorkload(wl)
     _check_layers(gw, [0, 1, 2], list(range(wl.spec.n_layers)))
+
+
+def test_kquant_stack_every_layer_and_lm_head():
+    """The 8-layer d=2048 stack with K-quant weights (Q5_K QKV, Q4_K O and gate/up, Q6_K down
+    and lm_head), B = 8, two steps: every layer and the lm_head teacher-forced at the stated
+    bar, on rows 0 and 7."""
+    say("kquant per layer")
+    wl = W.workload("kq", B=8, steps=2)
+    gw = GpuWorkload(wl)
+    _check_layers(gw, [0, 1], list(range(wl.spec.n_layers)), rows=[0, 7])

@@ -394,3 +394,18 @@ def test_hybrid_gdn_stack_end_to_end():
     _bit_identity(gw, range(4), 3, outs[-1])
     for b in range(4):
         np.testing.assert_array_equal(_state_bytes(gw, b, 3), before[b])
+
+
+def test_kquant_stack_end_to_end():
+    """The 8-layer d=2048 stack with Q4_K / Q5_K / Q6_K weights, B = 8, three steps: the oracle
+    follows rows 0 and 7 through the first step end to end (deep bar; later steps also read
+    K/V rows appended from diverged states, and tests/test_gpu_layers.py holds every layer
+    of two steps to the stated bar teacher-forced), and every row of the last step is
+    bit-identical to that row stepped alone (outputs and the K/V bytes it wrote)."""
+    say("kquant stack")
+    wl = W.workload("kq", B=8, steps=3)
+    gw = GpuWorkload(wl)
+    _oracle_follow(gw, [0, 7], range(1), dense_budget=6 << 30)
+    gw.step(1)
+    y = gw.step(2).cpu().numpy().copy()
+    _bit_identity(gw, range(8), 2, y)
