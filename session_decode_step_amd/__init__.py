@@ -413,7 +413,11 @@ def act_rows_view(x: Act, r0: int, n: int) -> Act:
 
 def kd_debug_read_stream(t: torch.Tensor, sink: torch.Tensor, nbytes: Optional[int] = None, stream=None) -> None:
     """A plain read of the tensor's bytes (the first nbytes of them): the HBM read ceiling."""
-    n = t.numel() * t.element_size() if nbytes is None else nbytes
+    size = t.numel() * t.element_size()
+    n = size if nbytes is None else nbytes
+    if not t.is_contiguous() or n < 0 or n > size:
+        raise ValueError(f"kd_debug_read_stream: {n} bytes from a tensor of {size} bytes (contiguous: "
+                         f"{t.is_contiguous()})")
     _check(lib().kd_debug_read_stream(t.data_ptr(), n, sink.data_ptr(), _stream(stream)), "kd_debug_read_stream")
 
 

@@ -133,7 +133,7 @@ void launch_mmvq_swiglu(const kd_weight& W, const int8_t* xq, const float* xd, i
   a.norm_ss = norm_ss;
   a.norm_n = norm_n;
   a.norm_eps = norm_eps;
-  a.QW = mmvq_qw(a.NQ, kWaveQuads);
+  a.QW = mmvq_qw(a.NQ, kQuadsSW);
   launch_mmvq_fmt<4, EPI_SWIGLU>(W, a, map ? map->n_groups : 1, st);
 }
 
@@ -170,7 +170,7 @@ void launch_mmvq_rope(const kd_weight& W, const int8_t* xq, const float* xd, int
   a.epi_cs = cs;
   a.epi_rc = rc;
   a.epi_capacity = capacity;
-  a.QW = mmvq_qw(a.NQ, kWaveQuads);
+  a.QW = mmvq_qw(a.NQ, kQuadsRope);
   launch_mmvq_fmt<1, EPI_ROPE>(W, a, 1, st);
 }
 
@@ -193,7 +193,7 @@ bool mmvq_fmt_ok(int fmt, int k) {
 // LDS of the SwiGLU product (four row groups per workgroup: the largest of the products),
 // which bounds its k below kMaxK on a 160 KiB-LDS CU.
 static size_t swiglu_lds_bytes(int k) {
-  const int NQ = n_quads(k), QW = mmvq_qw(NQ, kWaveQuads), nw = ceil_div(NQ, QW);
+  const int NQ = n_quads(k), QW = mmvq_qw(NQ, kQuadsSW), nw = ceil_div(NQ, QW);
   return (size_t)nw * mmvq_wave_lds(QW, 4) + (size_t)nw * 4 * 256 * sizeof(float) + 4 * 256 * sizeof(float);
 }
 bool mmvq_swiglu_fits(int k) { return swiglu_lds_bytes(k) <= 160u * 1024u; }

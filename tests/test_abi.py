@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import session_decode_step_amd as kd
 
@@ -442,3 +443,14 @@ def test_kquant_layouts_and_validation():
     layers[0].w_down = _fake_weight(kd.KD_FMT_Q4_K, 256, 640, 0x10600000)
     assert L.kd_model_create(C.byref(desc), C.byref(h)) == kd.KD_ERR_UNSUPPORTED
     assert b"w_down" in L.kd_last_error()
+
+
+def test_read_stream_binding_bounds_the_bytes():
+    """The read-ceiling export reads raw bytes from a pointer: its binding refuses a byte count
+    past the tensor (nothing is launched)."""
+    t = torch.zeros(64, dtype=torch.float16)
+    sink = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        kd.kd_debug_read_stream(t, sink, 129)
+    with pytest.raises(ValueError):
+        kd.kd_debug_read_stream(t[::2], sink, 16)
