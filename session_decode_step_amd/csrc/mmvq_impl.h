@@ -325,16 +325,6 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
     ax0[j] = buf16<0>(rx, ao);
     ax1[j] = buf16<0>(rx, ao == kOOB ? kOOB : ao + 16);
   }
-  // add + RMSNorm: the residual and gain this thread's epilogue item reads (row t / 8, four
-  // elements of block blockIdx.x), issued with the prologue so they arrive during the stream
-  float4 xr_pre = make_float4(0.0f, 0.0f, 0.0f, 0.0f), gn_pre = xr_pre;
-  if constexpr (EPI == EPI_RESNORM) {
-    const int bq = threadIdx.x >> 3, sub = threadIdx.x & 7;
-    if (bq < nrows) {
-      xr_pre = *reinterpret_cast<const float4*>(a.epi_res + (size_t)bq * a.epi_ld + 32 * blockIdx.x + 4 * sub);
-      gn_pre = *reinterpret_cast<const float4*>(a.epi_gain + 32 * blockIdx.x + 4 * sub);
-    }
-  }
   __builtin_amdgcn_sched_barrier(0);  // every prologue load is issued before anything waits
 
   // ---- the shared fetches into this wave's LDS slice (each waits on its own loads only)
@@ -558,9 +548,8 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
       const int m = blockIdx.x, Dn = a.n_out, nblk = Dn / 32;
       const int NQo = n_quads(Dn), nbpo = NQo * 4;
       const size_t o = (size_t)bq * a.epi_ld + 32 * m + 4 * sub;
-      const bool pre = t == (int)threadIdx.x;  // this thread's first item: fetched up front
-      const float4 xr = pre ? xr_pre : *reinterpret_cast<const float4*>(a.epi_res + o);
-      const float4 gn = pre ? gn_pre : *reinterpret_cast<const float4*>(a.epi_gain + 32 * m + 4 * sub);
+      const float4 xr = *reinterpret_cast<const float4*>(a.epi_res + o);
+      const float4 gn = *reinterpret_cast<const float4*>(a.epi_gain + 32 * m + 4 * sub);
       const float* ov = outv + (4 * sub) * 16 + bq;
       const float4 v = make_float4(xr.x + ov[0], xr.y + ov[16], xr.z + ov[32], xr.w + ov[48]);
       *reinterpret_cast<float4*>(a.epi_x1 + o) = v;
