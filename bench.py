@@ -171,7 +171,8 @@ def fa_algorithmic_bytes(t_kv, G: int, H: int, hd: int, kv_bytes: int = 2) -> in
 
 # ---------------------------------------------------------------------- HBM traffic (PMC)
 CALIB_BYTES = 512 << 20
-MM_SRC = ("session_decode_step_amd/csrc/mmvq.hip", "session_decode_step_amd/csrc/kd_internal.h")
+MM_SRC = ("session_decode_step_amd/csrc/mmvq.hip", "session_decode_step_amd/csrc/mmvq_impl.h",
+          "session_decode_step_amd/csrc/kd_internal.h")
 FA_SRC = ("session_decode_step_amd/csrc/attn.hip", "session_decode_step_amd/csrc/kd_internal.h")
 # in the order the probe launches them: (kind, profile file stem, sources, kernels per call)
 TRAFFIC_ORDER = [
