@@ -467,8 +467,10 @@ def other_workloads(stream, iters: int) -> dict:
     resident): the 8-layer Q8_0 stack with its 32000-row lm_head at B = 1, 2, 4, 8 (ctx 1238);
     the attention sublayer with B = 16 ragged rows (log-uniform lengths in [512, 32768]), its
     step and its fa_decode; the 8-layer MoE stack's verify step (4 streams x 4 draft rows,
-    ctx 8192); the headline stack with FP8 E4M3 caches and its fa_decode; the gated
-    delta-rule state step at B = 8 x 32 heads."""
+    ctx 8192); the headline stack with FP8 E4M3 caches and its fa_decode, and with int8
+    caches; the gated delta-rule state step at B = 8 x 32 heads; the 8-layer stack with
+    K-quant weights and plain K-quant products; the 8-layer stack with gated delta-rule
+    layers."""
     import numpy as np
     import torch
     import workload as W
@@ -599,6 +601,49 @@ def other_workloads(stream, iters: int) -> dict:
         "us": round(us, 3), "algorithmic_bytes": int(gbytes), "GBs": round(gbytes / (us * 1e-6) / 1e9, 1),
         "frac": round(gbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     del st_in, st_out
+    torch.cuda.synchronize()
+    # the 8-layer stack with K-quant weights (Q5_K QKV, Q4_K O and gate/up, Q6_K down and
+    # lm_head) at ctx 1238, and plain K-quant products at the 32-layer stack's shapes, B = 8
+    log("8-layer K-quant stack with lm_head")
+    wl = W.workload("kq", B=8, steps=64)
+    gw = GpuWorkload(wl, fill="device")
+    wb = W.algorithmic_bytes_weights(wl.spec)
+    kq = {}
+    for B in (1, 8):
+        ms = _time_steps(gw, stream, 16, 3, rows=list(range(B)))
+        kvb = B * (1238 + 8) * wl.spec.n_layers * wl.spec.n_head_kv * wl.spec.head_dim * 2 * 2
+        kq[str(B)] = {"tok_s": round(B / ms * 1e3, 1), "ms_per_step": round(ms, 4),
+                      "step_GBs": round((wb + kvb) / (ms * 1e-3) / 1e9, 1)}
+    res["8-layer d=2048 decoder with Q4_K / Q5_K / Q6_K weights + lm_head 32000 (Q6_K), ctx 1238"] = kq
+    del gw
+    x8 = kd.kd_quantize_act_q8(torch.randn((8, 14336), device="cuda", generator=torch.Generator(device="cuda").manual_seed(5)))
+    x4 = kd.kd_quantize_act_q8(torch.randn((8, 4096), device="cuda", generator=torch.Generator(device="cuda").manual_seed(6)))
+    prods = {}
+    for fmt, n, k, x in (("q4_k", 28672, 4096, x4), ("q5_k", 6144, 4096, x4), ("q6_k", 4096, 14336, x8),
+                         ("q4_0", 28672, 4096, x4)):
+        copies = 8 if n * k < 64 << 20 else 4
+        Ms = [kd.kd_pack_weight(W.draw_weight(fmt, 0, 7, 50, 51, 200 + i, n, k)) for i in range(copies)]
+        y = torch.empty((8, n), device="cuda")
+        us = time_rotating(lambda i: kd.kd_mmvq(Ms[i % copies], x, 8, y, stream=stream), iters, stream)
+        rec = W.KQ_RECORD.get(fmt)
+        wbytes = n * (k // 256) * rec if rec else w_bytes(fmt, n, k)
+        alg = wbytes + act_bytes(8, k) + 8 * n * 4
+        prods[f"{fmt} {n}x{k}"] = {"us": round(us, 3), "algorithmic_bytes": int(alg),
+                                   "GBs": round(alg / (us * 1e-6) / 1e9, 1),
+                                   "frac": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        del Ms
+    res["plain mmvq (kd_mmvq) at B=8, K-quant records against Q4_0, rotating over drawn matrices"] = prods
+    # the 8-layer Q8_0 stack with gated delta-rule layers on layers 0-2 and 4-6, ctx 1238
+    log("8-layer hybrid stack (gated delta-rule layers)")
+    wl = W.workload("hybrid", B=8, steps=64)
+    gw = GpuWorkload(wl, fill="device")
+    hy = {}
+    for B in (1, 8):
+        ms = _time_steps(gw, stream, 16, 3, rows=list(range(B)))
+        hy[str(B)] = {"tok_s": round(B / ms * 1e3, 1), "ms_per_step": round(ms, 4)}
+    res["8-layer d=2048 Q8_0 decoder, gated delta-rule layers 0-2 and 4-6 (16 value heads of 128), "
+        "attention layers 3 and 7, lm_head 32000, ctx 1238"] = hy
+    del gw
     torch.cuda.synchronize()
     return res
 
