@@ -482,9 +482,13 @@ def other_workloads(stream, iters: int) -> dict:
     wl = W.workload("c2", B=8, steps=64)
     gw = GpuWorkload(wl, fill="device")
     dense = {}
+    wb2 = W.algorithmic_bytes_weights(wl.spec)
     for B in (1, 2, 4, 8):
         ms = _time_steps(gw, stream, 16, 3, rows=list(range(B)))
-        dense[str(B)] = {"tok_s": round(B / ms * 1e3, 1), "ms_per_step": round(ms, 4)}
+        # weights once, each row's keys (ctx 1238 + the 16 timed steps' mean position) once
+        kvb = B * (1238 + 8 + 1) * wl.spec.n_layers * wl.spec.n_head_kv * wl.spec.head_dim * 2 * 2
+        dense[str(B)] = {"tok_s": round(B / ms * 1e3, 1), "ms_per_step": round(ms, 4),
+                         "step_GBs": round((wb2 + kvb) / (ms * 1e-3) / 1e9, 1)}
     res["8-layer d=2048 Q8_0 decoder + lm_head 32000, ctx 1238"] = dense
     del gw
     # attention sublayer, ragged B = 16
@@ -504,8 +508,10 @@ def other_workloads(stream, iters: int) -> dict:
                                                        sp.head_dim ** -0.5, ws=ws, out=out, stream=stream),
                        iters, stream)
     fb = fa_algorithmic_bytes(t_kv, sp.n_head_kv, sp.n_head, sp.head_dim)
+    sb = W.algorithmic_bytes_weights(sp) + fb
     res["attention sublayer d=4096 32Q/8KV hd=128 Q8_0, B=16 ragged ctx 512..32768"] = {
         "ms_per_step": round(ms, 4), "rows_s": round(wl.B / ms * 1e3, 1), "t_kv": t_kv,
+        "step_GBs": round(sb / (ms * 1e-3) / 1e9, 1),
         "fa_us": round(us, 3), "fa_algorithmic_bytes": int(fb), "fa_GBs": round(fb / (us * 1e-6) / 1e9, 1),
         "fa_frac": round(fb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     del gw
@@ -791,7 +797,9 @@ def main() -> None:
         "config": {"workload": "32-layer dense decoder d=4096, 32Q/8KV hd=128, SwiGLU 14336, Q4_0 weights, "
                                f"final RMSNorm; B={Bh} sessions at ctx 4096, decode positions 4096..{4096 + K - 1}",
                    "B": Bh, "ctx": 4096, "layers": L, "parallelism": "single GPU"},
-        "platform": {"gpu": torch.cuda.get_device_name(0), "rocm": rocm, "hip": torch.version.hip,
+        "platform": {"gpu": torch.cuda.get_device_name(0),
+                     "arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", "?"),
+                     "cus": torch.cuda.get_device_properties(0).multi_processor_count, "rocm": rocm, "hip": torch.version.hip,
                      "torch": torch.__version__, "seed": 0},
         "sweep": {str(b): {kk: round(v, 3) for kk, v in sweep[b].items()} for b in widths},
         "step_GBs": round(top["step_GBs"], 1),

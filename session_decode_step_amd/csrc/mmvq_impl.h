@@ -649,9 +649,12 @@ template <int FMT, int QW, int RG, int EPI>
 static void launch_mmvq_q(const MmvqArgs& a, int n_groups, hipStream_t st) {
   // epilogue slots: ceil(B / 4), a function of B (rows past B are never written, so
   // dropping their slots leaves every live output's operation sequence unchanged)
-  // (K-quant formats: always 4 slots, one instantiation)
+  // (K-quant formats: 2 slots up to B = 8, else 4 -- two instantiations)
   if constexpr (fmt_is_kq(FMT)) {
-    launch_mmvq_qn<FMT, QW, 4, RG, EPI>(a, n_groups, st);
+    if (!a.count && a.B <= 8)
+      launch_mmvq_qn<FMT, QW, 2, RG, EPI>(a, n_groups, st);
+    else
+      launch_mmvq_qn<FMT, QW, 4, RG, EPI>(a, n_groups, st);
   } else {
     const int ns = a.count ? 4 : (a.B + 3) / 4;
     switch (ns) {
