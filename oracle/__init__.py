@@ -13,8 +13,10 @@ fp32 only at the rounding points the method defines: the activation quantiser an
 the fp16 KV store.  Each function cites the passage it follows.
 
 Pins (tests marked ``not gpu``) check it against hand-worked blocks, closed forms,
-brute force and library routines; the end-to-end values of whole configurations
-have no external pin beyond that chain (parity unpinned beyond the op-level pins).
+brute force and library routines; the composition of a whole dense step (two layers and
+the lm_head) is pinned against the same step built from torch's own routines, the MoE
+routed sum against a dense masked sum over every expert, and the block variants and the
+linear layer by their closed forms and special cases.
 """
 from .ops import (QK, KQ_BYTES, kquant_dequantize, kquant_fields, kquant_scale_min, accept_drafts, gated_rmsnorm, gdn_prep, l2_normalize, softplus, ssm_conv_step, attention, block_dots, dequantize, dequantize_act, e4m3_decode,  # noqa: F401
                   e4m3_encode, e4m3_values, embed_rows, gdn_step, greedy_token, sigmoid,

@@ -968,3 +968,74 @@ def test_hybrid_block_formula_equals_dense_formulation():
     ys = [oracle.decode_step(model, oracle.OracleCaches(wl), x, [0, 1], wl.positions(0), blocks=blk)
           for blk in (True, False)]
     np.testing.assert_allclose(ys[0], ys[1], rtol=1e-10, atol=1e-10 * np.abs(ys[1]).max())
+
+
+def test_dense_step_against_a_torch_composition():
+    """The whole two-layer step (with lm_head) against the same step composed from torch's own
+    routines in fp64: F.rms_norm, matmul with the dequantised weights, the rotate-half form of
+    NEOX RoPE, scaled_dot_product_attention with GQA over each row's cache (every append of
+    the layer first), F.silu.  Only the block codecs (pinned above) are shared.  Three rows,
+    two of them on one cache at consecutive positions (causal verify rows).  A slip in the
+    step's wiring -- a residual in the wrong place, RoPE on v, a wrong head map, the wrong key
+    count, an append after the attention -- fails it."""
+    import torch.nn.functional as F
+    spec = TINY
+    wl = _tiny_wl(spec, 93, [(0, 0), (1, 0), (1, 1)], [5, 20])
+    model = wlmod.make_model(spec, 93)
+    x_np = wlmod.step_inputs(wl, 0)
+    sess, pos = [0, 1, 1], wl.positions(0)
+    ref = oracle.decode_step(model, oracle.OracleCaches(wl), x_np, sess, pos)
+
+    H, G, hd, d, eps = spec.n_head, spec.n_head_kv, spec.head_dim, spec.d, spec.rms_eps
+    T = torch.float64
+    caches = {}
+    for s in (0, 1):
+        for il in range(spec.n_layers):
+            k, v = wlmod.kv_prefill(wl, s, il)
+            Kc = torch.zeros((G, wl.capacity, hd), dtype=T)
+            Vc = torch.zeros((G, wl.capacity, hd), dtype=T)
+            Kc[:, :k.shape[1]] = torch.from_numpy(k.astype(np.float64))
+            Vc[:, :v.shape[1]] = torch.from_numpy(v.astype(np.float64))
+            caches[s, il] = (Kc, Vc)
+
+    def q8(t):   # the step's activation codec (pinned by the golden blocks): fp32 in, values out
+        q, dd = ops.quantize_act(t.numpy().astype(np.float32))
+        return torch.from_numpy(ops.dequantize_act(q, dd))
+
+    def W(w):
+        return torch.from_numpy(ops.dequantize(w))
+
+    def rope(t, p):   # t [n, hd] at position p: rotate-half form
+        inv = torch.pow(torch.tensor(10000.0, dtype=T), -torch.arange(0, hd, 2, dtype=T) / hd)
+        ang = p * inv
+        c, s_ = torch.cat([torch.cos(ang)] * 2), torch.cat([torch.sin(ang)] * 2)
+        rot = torch.cat([-t[:, hd // 2:], t[:, :hd // 2]], dim=1)
+        return t * c + rot * s_
+
+    x = torch.from_numpy(x_np.astype(np.float32).astype(np.float64))
+    for il, L in enumerate(model["layers"]):
+        g = lambda name: torch.from_numpy(L[name].astype(np.float64))
+        xv = q8(F.rms_norm(x, (d,), weight=g("attn_norm"), eps=eps))
+        qkv = xv @ W(L["wqkv"]).T
+        q = qkv[:, :H * hd].reshape(-1, H, hd)
+        k = qkv[:, H * hd:(H + G) * hd].reshape(-1, G, hd)
+        v = qkv[:, (H + G) * hd:(H + 2 * G) * hd].reshape(-1, G, hd)
+        qs = [rope(q[b], pos[b]) for b in range(3)]
+        for b in range(3):   # every row's append before any attention, fp16 cache values
+            Kc, Vc = caches[sess[b], il]
+            Kc[:, pos[b]] = rope(k[b], pos[b]).to(torch.float16).to(T)
+            Vc[:, pos[b]] = v[b].to(torch.float16).to(T)
+        att = []
+        for b in range(3):
+            Kc, Vc = caches[sess[b], il]
+            t = pos[b] + 1
+            o = F.scaled_dot_product_attention(qs[b][None, :, None, :], Kc[None, :, :t], Vc[None, :, :t],
+                                               scale=hd ** -0.5, enable_gqa=True)
+            att.append(o[0, :, 0].reshape(H * hd))
+        x1 = x + q8(torch.stack(att)) @ W(L["wo"]).T
+        zv = q8(F.rms_norm(x1, (d,), weight=g("ffn_norm"), eps=eps))
+        h = F.silu(zv @ W(L["w_gate"]).T) * (zv @ W(L["w_up"]).T)
+        x = x1 + q8(h) @ W(L["w_down"]).T
+    fn = torch.from_numpy(model["final_norm"].astype(np.float64))
+    logits = q8(F.rms_norm(x, (d,), weight=fn, eps=eps)) @ W(model["lm_head"]).T
+    np.testing.assert_allclose(logits.numpy(), ref, rtol=1e-9, atol=1e-9 * np.abs(ref).max())
