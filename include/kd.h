@@ -533,7 +533,7 @@ kd_status kd_debug_mmvq_grouped(const kd_weight* W, int32_t n_groups, kd_act_q8 
 
 /* A plain read of `bytes` bytes at p (device, 16-byte aligned, bytes % 16 == 0) with wide
  * non-temporal loads and no arithmetic (measurement only: the practical HBM read ceiling the
- * products and the attention are compared with, as the survey's measurement plan asks).
+ * products and the attention are compared with).
  * sink: a device uint32 that is written only in the rare case the loaded words fold to a
  * fixed constant. */
 kd_status kd_debug_read_stream(const void* p, size_t bytes, uint32_t* sink, void* stream);
