@@ -104,6 +104,18 @@ __device__ __forceinline__ void norm_ss_load(const MmvqArgs& a, int t, int nrows
   // no sums (plain SwiGLU): an empty range, every load reads zero without touching memory
   const __amdgpu_buffer_rsrc_t r =
       a.norm_ss ? make_rsrc(a.norm_ss, (uint32_t)(nrows * nblk * 4)) : make_rsrc(a.xd, 0u);
+  if (nblk == 8 * c && (c & 3) == 0) {  // whole 16-byte quads of sums: c / 4 wide loads
+#pragma unroll
+    for (int i4 = 0; i4 < kNormPerLane / 4; ++i4) {
+      const int blk = sub * c + 4 * i4;
+      const int4 q4 = buf16<0>(r, (bq < nrows && 4 * i4 < c) ? (uint32_t)(bq * nblk + blk) * 4u : kOOB);
+      v[4 * i4] = __int_as_float(q4.x);
+      v[4 * i4 + 1] = __int_as_float(q4.y);
+      v[4 * i4 + 2] = __int_as_float(q4.z);
+      v[4 * i4 + 3] = __int_as_float(q4.w);
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < kNormPerLane; ++i) {
     const int blk = sub * c + i;
@@ -117,6 +129,20 @@ __device__ __forceinline__ float norm_inv(const MmvqArgs& a, const float (&v)[kN
   for (int i = 1; i < kNormPerLane; ++i) s += v[i];
   s = group8_sum(s);
   return 1.0f / sqrtf(s / (float)a.norm_n + a.norm_eps);
+}
+
+// Sum over the waves of the workgroup, in wave order, of output (r, s, l) of the partials
+// red[wave][r][s][64]: every read is issued before the adds (nw <= 16).
+template <int RG>
+__device__ __forceinline__ float sum_waves(const float* red, int nw, int r, int s, int l) {
+  float v = red[(r * 4 + s) * 64 + l];
+  float x[15];
+#pragma unroll
+  for (int ww = 1; ww < 16; ++ww) x[ww - 1] = ww < nw ? red[((ww * RG + r) * 4 + s) * 64 + l] : 0.0f;
+#pragma unroll
+  for (int ww = 1; ww < 16; ++ww)
+    if (ww < nw) v += x[ww - 1];
+  return v;
 }
 
 // Batch rows on the MFMA operand: operand row i (accumulator slot s = i % 4 of lane group
@@ -480,10 +506,9 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
     for (int s = 0; s < 4; ++s) red[((w * RG + r) * 4 + s) * 64 + lane] = acc[r][s];
   __syncthreads();
   if (EPI == EPI_PLAIN) {
-    for (int t = threadIdx.x; t < RG * 256; t += blockDim.x) {
-      const int r = t >> 8, s = (t >> 6) & 3, l = t & 63;
-      float v = red[(r * 4 + s) * 64 + l];
-      for (int ww = 1; ww < nw; ++ww) v += red[((ww * RG + r) * 4 + s) * 64 + l];  // fixed wave order
+    for (int t = threadIdx.x; t < RG * NS * 64; t += blockDim.x) {
+      const int r = t / (NS * 64), s = (t >> 6) % NS, l = t & 63;
+      const float v = sum_waves<RG>(red, nw, r, s, l);
       const int b = (l >> 4) + 4 * s;
       const int row = (rg0 + r) * 16 + (l & 15);
       if (b < nrows && row < a.n_out) {
@@ -499,10 +524,9 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
   if (kNormEpi) norm_ss_load(a, threadIdx.x, nrows, ssv);
   // fused epilogues: the workgroup's outputs outv[row in workgroup][activation row]
   float* outv = red + nw * RG * 256;
-  for (int t = threadIdx.x; t < RG * 256; t += blockDim.x) {
-    const int r = t >> 8, s = (t >> 6) & 3, l = t & 63;
-    float v = red[(r * 4 + s) * 64 + l];
-    for (int ww = 1; ww < nw; ++ww) v += red[((ww * RG + r) * 4 + s) * 64 + l];  // fixed wave order
+  for (int t = threadIdx.x; t < RG * NS * 64; t += blockDim.x) {
+    const int r = t / (NS * 64), s = (t >> 6) % NS, l = t & 63;
+    const float v = sum_waves<RG>(red, nw, r, s, l);
     outv[(r * 16 + (l & 15)) * 16 + (l >> 4) + 4 * s] = v;
   }
   __syncthreads();
