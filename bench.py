@@ -201,11 +201,17 @@ def _traffic_title_bytes(kind):
 
 
 def kernel_source_hash(kind: str) -> str:
+    """Hash of the code (comments and whitespace removed) of the files a kernel is built from:
+    a measurement stays attached to its kernel until the code changes."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in _traffic_spec(kind)[1]:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

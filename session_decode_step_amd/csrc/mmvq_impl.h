@@ -95,7 +95,9 @@ enum { EPI_PLAIN = 0, EPI_SWIGLU = 1, EPI_ROPE = 2, EPI_RESNORM = 3 };
 // inv_b is the scale of the normalised block y = x1 * inv_b * gain, and the codes of z and y
 // are the same numbers.  The row's blocks are added by its 8 lanes: lane `sub` adds blocks
 // [sub * c, sub * c + c) in order (c = ceil(blocks / 8) <= kNormPerLane), then the 8 lanes by
-// DPP sum over the 8-lane group (group8_sum: every lane ends with the same value).
+// DPP sum over the 8-lane group (group8_sum: every lane ends with the same value).  A lane
+// fetches its sums in 16-byte loads when they come in whole quads (c a multiple of 4 and 8c
+// blocks per row), else one by one; the sums and their order are the same.
 constexpr int kNormPerLane = 16;  // block sums per lane: rows of up to 8 * 16 * 32 = 4096
 
 __device__ __forceinline__ void norm_ss_load(const MmvqArgs& a, int t, int nrows, float (&v)[kNormPerLane]) {
