@@ -737,6 +737,36 @@ def main() -> None:
         ms = e0.elapsed_time(e1)
         sweep[B] = {"tok_s": B * K / (ms / 1e3), "ms_per_step": ms / K, "host_ms_per_step": 1e3 * host_s / K}
 
+    # ---------------------------------------------------------------- the step as a HIP graph
+    # one step (positions of step 0, so every replay rewrites the same cache slots) captured
+    # whole and replayed K times, against the same step enqueued K times
+    log(f"step captured in a HIP graph at B={Bh}")
+    rows = list(range(Bh))
+    gw.prefetch([0], rows)
+    out_g = torch.empty((Bh, sp.out_dim), dtype=torch.float32, device="cuda")
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        gw.step(0, rows=rows, out=out_g)
+    torch.cuda.synchronize()
+
+    def _timed(fn):
+        for _ in range(Wu):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(K):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K
+
+    graph_ms = _timed(graph.replay)
+    eager_ms = _timed(lambda: gw.step(0, rows=rows, out=out_g, stream=stream))
+    graph_rec = {"B": Bh, "ms_per_step_graph": round(graph_ms, 4), "ms_per_step_enqueued": round(eager_ms, 4)}
+    del graph
+
     # algorithmic bytes of one step at width B (weights once + KV read + KV write + acts)
     wbytes = W.algorithmic_bytes_weights(sp)
     G, hd, L = sp.n_head_kv, sp.head_dim, sp.n_layers
@@ -821,6 +851,7 @@ def main() -> None:
         "cpu_baseline": cpu,
         "cpu_baseline_configs": cpu_configs,
         "other_workloads": other,
+        "graph_replay": graph_rec,
         "setup_s": round(setup_s, 1),
     }
     print(json.dumps(res))

@@ -409,3 +409,42 @@ def test_kquant_stack_end_to_end():
     gw.step(1)
     y = gw.step(2).cpu().numpy().copy()
     _bit_identity(gw, range(8), 2, y)
+
+
+@pytest.mark.parametrize("name,B", [("c2", 4), ("c4", 8)])
+def test_step_replays_from_a_hip_graph(name, B):
+    """kd_decode_step captured whole in a HIP graph (torch.cuda.CUDAGraph records the library's
+    launches on its capture stream) replays to the eager call's bytes.  Between replays the
+    program zeroes the step's output and the cache slots it appends and synchronises; every
+    replay must write the same output rows and slots again.  (The step enqueues kernels only:
+    no memset node, whose replays have given wrong results on these GPUs.)"""
+    say(f"graph replay {name} B={B}")
+    wl = W.workload(name, B=B, steps=1)
+    gw = GpuWorkload(wl, fill="device" if name == "c4" else "seeded")
+    gw.prefetch([0])
+    sess = [wl.rows[b][0] for b in range(B)]
+    pos = wl.positions(0)
+
+    def slots():
+        return [gw.caches.t[sess[b]][:, :, :, pos[b]].clone() for b in range(B)]
+
+    eager = gw.step(0).clone()
+    eager_slots = slots()
+    out = torch.empty_like(eager)
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        gw.step(0, out=out)
+    torch.cuda.synchronize()
+    for r in range(3):
+        out.zero_()
+        for b in range(B):
+            gw.caches.t[sess[b]][:, :, :, pos[b]].zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        say(f"  replay {r}")
+        assert torch.equal(out.view(torch.int32), eager.view(torch.int32)), f"replay {r}: output rows differ"
+        for b, (a, e) in enumerate(zip(slots(), eager_slots)):
+            assert torch.equal(a.view(torch.uint8), e.view(torch.uint8)), f"replay {r}: row {b}'s appended slot differs"
+    del g
