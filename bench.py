@@ -421,6 +421,73 @@ def read_ceiling_us(tensors, nbytes: int, stream, iters: int) -> float:
                          iters, stream)
 
 
+def tp8_shard(gw, stream, iters: int) -> dict:
+    """One GPU's share of a C4 layer under 8-way tensor parallelism, at B=8 (what one GPU can
+    show of that layout; the two [B, d] all-reduces per layer are not run): QKV rows of 4 query
+    heads and 1 KV head (768 x 4096, RoPE + append epilogue), 1792 gate/up outputs (3584 x 4096,
+    SwiGLU epilogue), O over 512 input columns (4096 x 512) and down over 1792 (4096 x 1792) as
+    plain products (their partial sums go to the all-reduce), and fa_decode over 1 KV head
+    (H = 4, G = 1, t = 4113).  Row shards are views of each layer's packed matrix (its leading
+    tiles); column shards are the leading quads of every row group, copied once."""
+    import torch
+    import session_decode_step_amd as kd
+    from session_decode_step_amd import PackedWeight
+    wl = gw.wl
+    L = wl.spec.n_layers
+    mats = stack_products(gw)
+
+    def tiles(W):
+        nr, nq = W.n_out // 16, W.k // 128
+        return nr, nq, W.qs.numel() // (nr * nq), W.d.numel() // (nr * nq)
+
+    def rows(W, n):
+        _, nq, tq, td = tiles(W)
+        return PackedWeight(W.fmt, n, W.k, W.qs[: (n // 16) * nq * tq], W.d[: (n // 16) * nq * td])
+
+    def cols(W, k):
+        nr, nq, tq, td = tiles(W)
+        nqs = k // 128
+        return PackedWeight(W.fmt, W.n_out, k, W.qs.view(nr, nq, tq)[:, :nqs].contiguous().view(-1),
+                            W.d.view(nr, nq, td)[:, :nqs].contiguous().view(-1))
+
+    qkv = [rows(m, 768) for m in mats["qkv"]]
+    gu = [rows(m, 3584) for m in mats["gateup"]]
+    o = [cols(m, 512) for m in mats["o"]]
+    down = [cols(m, 1792) for m in mats["down"]]
+    g = torch.Generator(device="cuda").manual_seed(11)
+    B = PB
+    x_d = kd.kd_quantize_act_q8(torch.randn((B, D4), device="cuda", generator=g))
+    x_o = kd.kd_quantize_act_q8(torch.randn((B, 512), device="cuda", generator=g))
+    x_dn = kd.kd_quantize_act_q8(torch.randn((B, 1792), device="cuda", generator=g))
+    res = torch.randn((B, D4), device="cuda", generator=g)
+    ss = (res * res).view(B, D4 // 32, 32).sum(2).contiguous()
+    qo = torch.empty((B, 4 * HD4), device="cuda")
+    h = kd.alloc_act(B, 1792)
+    y = torch.empty((B, D4), device="cuda")
+    pos = [wl.capacity - 1] * B
+    kb = [[gw.caches.k_ptr(s, il) for s in range(B)] for il in range(L)]
+    vb = [[gw.caches.v_ptr(s, il) for s in range(B)] for il in range(L)]
+    t_kv = [FA_T] * B
+    q = torch.randn((B, 4, HD4), device="cuda", generator=g)
+    fa_out = torch.empty_like(q)
+    fa_ws = torch.empty(kd.kd_fa_decode_workspace(B, 4, HD4, t_kv), dtype=torch.uint8, device="cuda")
+    launches = {
+        "qkv 768x4096 + RoPE + append": lambda i: kd.kd_mmvq_rope_normed(
+            qkv[i % L], x_d, B, ss, 1e-5, 4, 1, HD4, qo, kb[i % L], vb[i % L], pos, wl.capacity, 10000.0, stream=stream),
+        "fa_decode H=4 G=1 t=4113": lambda i: kd.kd_fa_decode_ragged(
+            q, 1, kb[i % L], vb[i % L], t_kv, wl.capacity, HD4 ** -0.5, ws=fa_ws, out=fa_out, stream=stream),
+        "o 4096x512": lambda i: kd.kd_mmvq_q4_0(o[i % L], x_o, B, y, stream=stream),
+        "gate/up 3584x4096 + SwiGLU": lambda i: kd.kd_mmvq_swiglu_normed(gu[i % L], x_d, B, ss, 1e-5, h, stream=stream),
+        "down 4096x1792": lambda i: kd.kd_mmvq_q4_0(down[i % L], x_dn, B, y, stream=stream),
+    }
+    out = {}
+    for name, fn in launches.items():
+        out[name] = round(time_rotating(fn, iters, stream), 3)
+    out["sum_us"] = round(sum(v for v in out.values()), 3)
+    out["note"] = "per-layer kernels of one TP8 shard at B=8 (us; the two all-reduces per layer not run)"
+    return out
+
+
 def measure_products(gw, stream, iters: int) -> dict:
     """Each product of the 32-layer stack at B=8 with its fused epilogue (HIP events on the
     launch stream, rotating over the 32 layers' matrices), the 8-layer stack's lm_head
@@ -784,6 +851,8 @@ def main() -> None:
     # own matrices (2.1 GB for gate/up, well above the 256 MB Infinity Cache), as inside a
     # step; the lm_head of the 8-layer Q8_0 stack; and the plain read of the same bytes
     products = measure_products(gw, stream, args.kernel_iters)
+    log("one TP8 shard of a layer at B=8")
+    shard = tp8_shard(gw, stream, args.kernel_iters)
 
     # ---------------------------------------------------------------- dominant kernel: fa_decode
     # the split kernel and its combine: the largest share of the step's time (~40% at B = 8).
@@ -852,6 +921,7 @@ def main() -> None:
         "cpu_baseline_configs": cpu_configs,
         "other_workloads": other,
         "graph_replay": graph_rec,
+        "tp8_shard": shard,
         "setup_s": round(setup_s, 1),
     }
     print(json.dumps(res))
