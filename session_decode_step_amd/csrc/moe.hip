@@ -56,14 +56,41 @@ __global__ __launch_bounds__(64) void router_logits_kernel(const float* __restri
 
 // Top-K of every row and the expert buckets, in one workgroup of 16 waves.  Wave b takes row b:
 // its lanes hold experts l, l + 64, l + 128, l + 192, and each of K rounds takes the largest
-// untaken logit with ties to the lower id (a total order, so the butterfly's shape does not
-// matter); then the softmax over the K selected logits in rank order.  Then thread e lists the
-// (row, rank) pairs routed to expert e in ascending row order.
+// untaken logit with ties to the lower id (a total order, so the reduction's shape does not
+// matter: DPP within 16-lane rows, then the rows' winners); then the softmax over the K
+// selected logits in rank order.  Then each wave lists, for its experts, the (row, rank)
+// pairs routed there in ascending row order (ballots over the pairs).
 __device__ __forceinline__ void topk_merge(float& v, int& i, float v2, int i2) {
   if (i2 != INT_MAX && (i == INT_MAX || v2 > v || (v2 == v && i2 < i))) {
     v = v2;
     i = i2;
   }
+}
+
+// The largest (value, index) pair of the wave (ties to the lower index) in every lane: DPP
+// steps within each 16-lane row, then the four rows' pairs read from lanes 0, 16, 32 and 48.
+// The merge is a total order, so any combining order gives the same pair.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ void topk_step(float& v, int& i) {
+  const float v2 = dpp_f<CTRL>(v);
+  const int i2 = dpp_i<CTRL>(i);
+  topk_merge(v, i, v2, i2);
+}
+__device__ __forceinline__ void topk_wave(float& v, int& i) {
+  topk_step<0xB1>(v, i);   // quad_perm [1,0,3,2]
+  topk_step<0x4E>(v, i);   // quad_perm [2,3,0,1]
+  topk_step<0x141>(v, i);  // row_half_mirror
+  topk_step<0x140>(v, i);  // row_mirror
+  float bv = lane_f(v, 0);
+  int bi = __builtin_amdgcn_readlane(i, 0);
+#pragma unroll
+  for (int r = 16; r < 64; r += 16) topk_merge(bv, bi, lane_f(v, r), __builtin_amdgcn_readlane(i, r));
+  v = bv;
+  i = bi;
 }
 
 __global__ __launch_bounds__(1024) void route_bucket_kernel(const float* __restrict__ logits, int B, int E, int K,
@@ -88,12 +115,7 @@ __global__ __launch_bounds__(1024) void route_bucket_kernel(const float* __restr
       int bi = INT_MAX;
 #pragma unroll
       for (int i = 0; i < kMaxExperts / 64; ++i) topk_merge(bv, bi, v[i], live[i] ? lane + 64 * i : INT_MAX);
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) {
-        const float v2 = __shfl_xor(bv, m, 64);
-        const int i2 = __shfl_xor(bi, m, 64);
-        topk_merge(bv, bi, v2, i2);
-      }
+      topk_wave(bv, bi);
       sel[k] = bi;
       val[k] = bv;
 #pragma unroll
@@ -116,15 +138,26 @@ __global__ __launch_bounds__(1024) void route_bucket_kernel(const float* __restr
     }
   }
   __syncthreads();
-  for (int e = tid; e < E; e += blockDim.x) {
-    int c = 0;
-    for (int j = 0; j < B * K; ++j)
-      if (sids[j] == e) {
+  // one wave per expert: lane l looks at pairs l + 64 q (B K <= 256); a pair's place in its
+  // expert's list is the number of matching pairs before it (ascending pair order)
+  constexpr int kPairChunks = KD_MAX_B * kMaxTopK / 64;
+  const int n = B * K, nwv = blockDim.x >> 6;
+  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+  for (int e = w; e < E; e += nwv) {
+    int c0 = 0;
+#pragma unroll
+    for (int q = 0; q < kPairChunks; ++q) {
+      const int j = lane + 64 * q;
+      const bool m = j < n && sids[j] == e;
+      const uint64_t bq = __ballot(m);
+      if (m) {
+        const int c = c0 + __popcll(bq & below);
         rows[e * 16 + c] = j / K;
         pairs[e * 16 + c] = j;
-        ++c;
       }
-    count[e] = c;
+      c0 += __popcll(bq);
+    }
+    if (lane == 0) count[e] = c0;
   }
 }
 
