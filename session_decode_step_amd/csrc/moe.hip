@@ -13,8 +13,6 @@
 // and treats its rows as the MFMA's activation rows, whose results never depend on which
 // other rows share the expert; the combine adds the k expert outputs of a row in rank
 // order.  So a row's result is the same at any B.
-#include <climits>
-
 #include "kd_internal.h"
 
 namespace kd {
@@ -55,44 +53,13 @@ __global__ __launch_bounds__(64) void router_logits_kernel(const float* __restri
 }
 
 // Top-K of every row and the expert buckets, in one workgroup of 16 waves.  Wave b takes row b:
-// its lanes hold experts l, l + 64, l + 128, l + 192, and each of K rounds takes the largest
-// untaken logit with ties to the lower id (a total order, so the reduction's shape does not
-// matter: DPP within 16-lane rows, then the rows' winners); then the softmax over the K
-// selected logits in rank order.  Then each wave lists, for its experts, the (row, rank)
-// pairs routed there in ascending row order (ballots over the pairs).
-__device__ __forceinline__ void topk_merge(float& v, int& i, float v2, int i2) {
-  if (i2 != INT_MAX && (i == INT_MAX || v2 > v || (v2 == v && i2 < i))) {
-    v = v2;
-    i = i2;
-  }
-}
-
-// The largest (value, index) pair of the wave (ties to the lower index) in every lane: DPP
-// steps within each 16-lane row, then the four rows' pairs read from lanes 0, 16, 32 and 48.
-// The merge is a total order, so any combining order gives the same pair.
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int x) {
-  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
-}
-template <int CTRL>
-__device__ __forceinline__ void topk_step(float& v, int& i) {
-  const float v2 = dpp_f<CTRL>(v);
-  const int i2 = dpp_i<CTRL>(i);
-  topk_merge(v, i, v2, i2);
-}
-__device__ __forceinline__ void topk_wave(float& v, int& i) {
-  topk_step<0xB1>(v, i);   // quad_perm [1,0,3,2]
-  topk_step<0x4E>(v, i);   // quad_perm [2,3,0,1]
-  topk_step<0x141>(v, i);  // row_half_mirror
-  topk_step<0x140>(v, i);  // row_mirror
-  float bv = lane_f(v, 0);
-  int bi = __builtin_amdgcn_readlane(i, 0);
-#pragma unroll
-  for (int r = 16; r < 64; r += 16) topk_merge(bv, bi, lane_f(v, r), __builtin_amdgcn_readlane(i, r));
-  v = bv;
-  i = bi;
-}
-
+// its lanes hold experts l + 64 i (NS slots), and each of K rounds takes the largest live logit
+// (a float maximum, exact in any order: DPP within 16-lane rows, then the rows' maxima), then
+// the lowest live expert id holding it (slot by slot, the first set bit of the first non-empty
+// ballot), so ties go to the lower id.  Lane k keeps round k's logit and id; the softmax over
+// the K selected logits adds their exponentials in rank order.  Then each wave lists, for its
+// experts, the (row, rank) pairs routed there in ascending row order (ballots over the pairs).
+template <int NS>
 __global__ __launch_bounds__(1024) void route_bucket_kernel(const float* __restrict__ logits, int B, int E, int K,
                                                             int32_t* __restrict__ ids, float* __restrict__ p,
                                                             int32_t* __restrict__ count, int32_t* __restrict__ rows,
@@ -100,41 +67,54 @@ __global__ __launch_bounds__(1024) void route_bucket_kernel(const float* __restr
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   __shared__ int32_t sids[KD_MAX_B * kMaxTopK];
   if (w < B) {
-    float v[kMaxExperts / 64];
-    bool live[kMaxExperts / 64];
+    float v[NS];
+    bool live[NS];
 #pragma unroll
-    for (int i = 0; i < kMaxExperts / 64; ++i) {
+    for (int i = 0; i < NS; ++i) {
       const int e = lane + 64 * i;
       live[i] = e < E;
       v[i] = live[i] ? logits[(size_t)w * E + e] : 0.0f;
     }
-    int sel[kMaxTopK];
-    float val[kMaxTopK];
+    float myv = 0.0f;  // lane k < K: the logit and expert of rank k
+    int mye = 0;
     for (int k = 0; k < K; ++k) {
-      float bv = 0.0f;
-      int bi = INT_MAX;
+      float m = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < kMaxExperts / 64; ++i) topk_merge(bv, bi, v[i], live[i] ? lane + 64 * i : INT_MAX);
-      topk_wave(bv, bi);
-      sel[k] = bi;
-      val[k] = bv;
+      for (int i = 0; i < NS; ++i) m = live[i] ? fmaxf(m, v[i]) : m;
+      const float M = wave_max(m);
+      int sel = -1;
 #pragma unroll
-      for (int i = 0; i < kMaxExperts / 64; ++i)
-        if (lane + 64 * i == bi) live[i] = false;
+      for (int i = 0; i < NS; ++i) {
+        const uint64_t bq = __ballot(live[i] && v[i] == M);
+        if (sel < 0 && bq) sel = 64 * i + __builtin_ctzll(bq);
+      }
+      if (sel < 0) {  // no live logit equals the maximum (NaN logits only): the lowest live id
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+          const uint64_t bq = __ballot(live[i]);
+          if (sel < 0 && bq) sel = 64 * i + __builtin_ctzll(bq);
+        }
+      }
+      float vs = v[0];
+#pragma unroll
+      for (int i = 1; i < NS; ++i) vs = (sel >> 6) == i ? v[i] : vs;
+      vs = lane_f(vs, sel & 63);
+#pragma unroll
+      for (int i = 0; i < NS; ++i) live[i] = live[i] && lane + 64 * i != sel;
+      if (lane == k) {
+        myv = vs;
+        mye = sel;
+      }
     }
-    if (lane == 0) {
-      const float mx = val[0];
-      float ex[kMaxTopK];
-      float sum = 0.0f;
-      for (int k = 0; k < K; ++k) {
-        ex[k] = expf(val[k] - mx);
-        sum += ex[k];
-      }
-      for (int k = 0; k < K; ++k) {
-        ids[w * K + k] = sel[k];
-        p[w * K + k] = ex[k] / sum;
-        sids[w * K + k] = sel[k];
-      }
+    // p = softmax over the selected logits: exponentials per lane, their sum in rank order
+    const float mx = lane_f(myv, 0);
+    const float ex = lane < K ? expf(myv - mx) : 0.0f;
+    float sum = 0.0f;
+    for (int k = 0; k < K; ++k) sum += lane_f(ex, k);
+    if (lane < K) {
+      ids[w * K + lane] = mye;
+      p[w * K + lane] = ex / sum;
+      sids[w * K + lane] = mye;
     }
   }
   __syncthreads();
@@ -175,7 +155,12 @@ __global__ void moe_combine_kernel(const float* __restrict__ y, const float* __r
 void launch_router(const float* z, const float* Wr, int B, int d, int E, int K, int32_t* ids, float* p, float* logits,
                    int32_t* count, int32_t* rows, int32_t* pairs, hipStream_t st) {
   router_logits_kernel<<<dim3(E, B), 64, 0, st>>>(z, Wr, d, E, logits);
-  route_bucket_kernel<<<1, 1024, 0, st>>>(logits, B, E, K, ids, p, count, rows, pairs);
+  switch (ceil_div(E, 64)) {
+    case 1: route_bucket_kernel<1><<<1, 1024, 0, st>>>(logits, B, E, K, ids, p, count, rows, pairs); break;
+    case 2: route_bucket_kernel<2><<<1, 1024, 0, st>>>(logits, B, E, K, ids, p, count, rows, pairs); break;
+    case 3: route_bucket_kernel<3><<<1, 1024, 0, st>>>(logits, B, E, K, ids, p, count, rows, pairs); break;
+    default: route_bucket_kernel<4><<<1, 1024, 0, st>>>(logits, B, E, K, ids, p, count, rows, pairs); break;
+  }
 }
 
 void launch_moe_combine(const float* y, const float* p, const float* sh, int B, int K, int d, float* f, hipStream_t st) {
