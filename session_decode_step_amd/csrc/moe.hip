@@ -121,18 +121,25 @@ __global__ __launch_bounds__(1024) void route_bucket_kernel(const float* __restr
   // one wave per expert: lane l looks at pairs l + 64 q (B K <= 256); a pair's place in its
   // expert's list is the number of matching pairs before it (ascending pair order)
   constexpr int kPairChunks = KD_MAX_B * kMaxTopK / 64;
-  const int n = B * K, nwv = blockDim.x >> 6;
+  const int n = B * K, nq = (n + 63) / 64, nwv = blockDim.x >> 6;
   const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+  int sj[kPairChunks], rj[kPairChunks];  // expert (-1 past the n pairs) and row of pair lane + 64 q
+#pragma unroll
+  for (int q = 0; q < kPairChunks; ++q) {
+    sj[q] = q < nq && lane + 64 * q < n ? sids[lane + 64 * q] : -1;
+    rj[q] = (lane + 64 * q) / K;
+  }
   for (int e = w; e < E; e += nwv) {
     int c0 = 0;
 #pragma unroll
     for (int q = 0; q < kPairChunks; ++q) {
+      if (q >= nq) break;
       const int j = lane + 64 * q;
-      const bool m = j < n && sids[j] == e;
+      const bool m = sj[q] == e;
       const uint64_t bq = __ballot(m);
       if (m) {
         const int c = c0 + __popcll(bq & below);
-        rows[e * 16 + c] = j / K;
+        rows[e * 16 + c] = rj[q];
         pairs[e * 16 + c] = j;
       }
       c0 += __popcll(bq);
