@@ -265,7 +265,7 @@ __host__ __device__ constexpr int mmvq_wave_lds(int QW, int RG) { return 16 * QW
 // Dynamic LDS: nw wave slices, then [nw][RG][4][64] floats, then (fused epilogues) the
 // workgroup's outputs [RG * 16][16].
 template <int FMT, int QW, int NS, int RG, int EPI, bool DEBUG>
-__global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
+__device__ __forceinline__ void mmvq_body(const MmvqArgs& a) {
   constexpr int NT = RG * QW;
   constexpr int D0 = EPI == EPI_RESNORM ? kDepthRN : RG > 1 ? kDepthRG : FMT == KD_FMT_Q8_0 ? kDepthQ8 : kDepthQ4;
   constexpr int D = D0 < NT ? D0 : NT;
@@ -643,6 +643,27 @@ __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
   }
 }
 
+// The product kernel.  GRP (grouped launches, 4 accumulator slots): each workgroup runs the
+// copy of the body with as many slots as its group's rows need (slot s holds rows 4s .. 4s+3),
+// so a group of few rows does only its own rows' epilogue work; every live output takes the
+// same operations in every copy.
+template <int FMT, int QW, int NS, int RG, int EPI, bool DEBUG, bool GRP = false>
+__global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
+  if constexpr (GRP) {
+    const int rows = a.count[blockIdx.y];
+    if (rows <= 4)
+      mmvq_body<FMT, QW, 1, RG, EPI, DEBUG>(a);
+    else if (rows <= 8)
+      mmvq_body<FMT, QW, 2, RG, EPI, DEBUG>(a);
+    else if (rows <= 12)
+      mmvq_body<FMT, QW, 3, RG, EPI, DEBUG>(a);
+    else
+      mmvq_body<FMT, QW, 4, RG, EPI, DEBUG>(a);
+  } else {
+    mmvq_body<FMT, QW, NS, RG, EPI, DEBUG>(a);
+  }
+}
+
 // Quads per wave: about NQ / 4 (four waves per workgroup), between 2 and kWaveQuads,
 // and enough that at most 16 waves cover NQ; then balanced (the smallest QW giving the same
 // wave count).  Waves per workgroup: ceil(NQ / QW).  Both depend on the matrix's k only.
@@ -665,6 +686,12 @@ static void launch_mmvq_qn(const MmvqArgs& a, int n_groups, hipStream_t st) {
   if constexpr (EPI == EPI_PLAIN && !fmt_is_kq(FMT)) {
     if (a.debug_S) {
       mmvq_kernel<FMT, QW, 4, RG, EPI_PLAIN, true><<<grid, 64 * nw, slices, st>>>(a);
+      return;
+    }
+  }
+  if constexpr (NS == 4 && (EPI == EPI_PLAIN || EPI == EPI_SWIGLU) && (FMT == KD_FMT_Q4_0 || FMT == KD_FMT_Q8_0)) {
+    if (a.count) {
+      mmvq_kernel<FMT, QW, NS, RG, EPI, false, true><<<grid, 64 * nw, slices + red_shm + out_shm, st>>>(a);
       return;
     }
   }

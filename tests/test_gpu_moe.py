@@ -131,6 +131,20 @@ def test_fanout_all_rows_on_the_same_experts(layer):
     _grouped_equals_per_row(layer, z, g, "same experts")
 
 
+def test_fanout_two_clusters_of_rows(layer):
+    """Rows 0..5 near one vector and rows 6..15 near another: buckets of 6 and 10 rows (the
+    grouped product's two- and three-slot workgroups), each output bit-identical to its row's
+    plain product."""
+    rng = np.random.default_rng(74)
+    a, c = rng.standard_normal(D), rng.standard_normal(D)
+    z = np.concatenate([a[None, :] + 1e-4 * rng.standard_normal((6, D)),
+                        c[None, :] + 1e-4 * rng.standard_normal((10, D))])
+    g = _route_and_check(z, layer["router"], layer["L"]["router"], "two clusters")
+    counts = sorted(int(x) for x in g["count"] if x)
+    assert 6 in counts and 10 in counts, counts
+    _grouped_equals_per_row(layer, z, g, "two clusters")
+
+
 def test_fanout_every_row_on_its_own_experts(layer):
     """A router whose experts 8b .. 8b+7 respond to direction u_b only, and rows along u_b:
     the 16 rows take 128 distinct experts, every bucket holds one row."""
