@@ -689,7 +689,8 @@ static void launch_mmvq_qn(const MmvqArgs& a, int n_groups, hipStream_t st) {
       return;
     }
   }
-  if constexpr (NS == 4 && (EPI == EPI_PLAIN || EPI == EPI_SWIGLU) && (FMT == KD_FMT_Q4_0 || FMT == KD_FMT_Q8_0)) {
+  // (the grouped down product, k = expert_ffn, keeps the one body: its epilogue is small)
+  if constexpr (NS == 4 && EPI == EPI_SWIGLU && (FMT == KD_FMT_Q4_0 || FMT == KD_FMT_Q8_0)) {
     if (a.count) {
       mmvq_kernel<FMT, QW, NS, RG, EPI, false, true><<<grid, 64 * nw, slices + red_shm + out_shm, st>>>(a);
       return;
