@@ -122,7 +122,12 @@ static void launch_mmvq_fmt(const kd_weight& W, const MmvqArgs& a, int ng, hipSt
 void launch_mmvq(const kd_weight& W, const int8_t* xq, const float* xd, int B, float* y, int ldy,
                  hipStream_t st, const RowMap* map, int32_t* debug_S) {
   const MmvqArgs a = mmvq_args(W, xq, xd, B, y, ldy, map, debug_S);
-  launch_mmvq_fmt<kPlainRG, EPI_PLAIN>(W, a, map ? map->n_groups : 1, st);
+  // grouped Q4_0 products (the experts' down product: small k, so a workgroup of one row
+  // group has little to stream) take four row groups per workgroup
+  if (map && W.fmt == KD_FMT_Q4_0)
+    launch_mmvq_fmt<4, EPI_PLAIN>(W, a, map->n_groups, st);
+  else
+    launch_mmvq_fmt<kPlainRG, EPI_PLAIN>(W, a, map ? map->n_groups : 1, st);
 }
 
 void launch_mmvq_swiglu(const kd_weight& W, const int8_t* xq, const float* xd, int B, int8_t* out_qs, float* out_d,
