@@ -241,9 +241,15 @@ struct RowCaches {
 // (gate rows 32m.., then up rows 32m..); writes the quantised silu(gate) * up rows [B][F].
 // With a row map (grouped experts): W holds each group's interleaved [2F, d] block, and
 // output row j of group e goes to row out_row[e*16 + j] of (out_qs, out_d).
+// Grouped (map): X, when given, is an extra matrix of whole groups' rows (the shared
+// expert's interleaved gate/up, its n_out a multiple of W.n_out, same format and k) applied to
+// all B rows in the same launch, its SwiGLU rows going to x_qs / x_qd (X.n_out / 2 columns);
+// only when mmvq_swiglu_merges(W, X).
 void launch_mmvq_swiglu(const kd_weight& W, const int8_t* xq, const float* xd, int B, int8_t* out_qs, float* out_d,
                         hipStream_t st, const float* norm_ss = nullptr, int norm_n = 0, float norm_eps = 0.0f,
-                        const RowMap* map = nullptr);
+                        const RowMap* map = nullptr, const kd_weight* X = nullptr, int8_t* x_qs = nullptr,
+                        float* x_qd = nullptr);
+bool mmvq_swiglu_merges(const kd_weight& W, const kd_weight& X);
 // O-style product whose epilogue adds the residual and starts the next RMSNorm: x1 = res + W x
 // (x1 may not alias res), Q8 codes of x1 * gain with per-block scales, and the per-block sums
 // of squares ss [B][n_out / 32] that launch_mmvq_swiglu's norm_ss turns into 1/rms.

@@ -99,6 +99,7 @@ static MmvqArgs mmvq_args(const kd_weight& W, const int8_t* xq, const float* xd,
   a.act_row = map ? map->act_row : nullptr;
   a.out_row = map ? map->out_row : nullptr;
   a.w_group_tiles = map ? map->w_group_tiles : 0;
+  a.n_groups = map ? map->n_groups : 1;
   a.debug_S = debug_S;
   const size_t tiles = (size_t)(map ? map->n_groups : 1) * (map ? (size_t)map->w_group_tiles : (size_t)a.NR * a.NQ);
   a.w_bytes = (uint32_t)(tiles * tile_qs_bytes(W.fmt));
@@ -130,16 +131,32 @@ void launch_mmvq(const kd_weight& W, const int8_t* xq, const float* xd, int B, f
     launch_mmvq_fmt<kPlainRG, EPI_PLAIN>(W, a, map ? map->n_groups : 1, st);
 }
 
+bool mmvq_swiglu_merges(const kd_weight& W, const kd_weight& X) {
+  return (W.fmt == KD_FMT_Q4_0 || W.fmt == KD_FMT_Q8_0) && X.fmt == W.fmt && X.k == W.k && W.n_out % 64 == 0 &&
+         X.n_out % W.n_out == 0 && X.n_out / W.n_out <= 8 && X.qs && X.d;
+}
+
 void launch_mmvq_swiglu(const kd_weight& W, const int8_t* xq, const float* xd, int B, int8_t* out_qs, float* out_d,
-                        hipStream_t st, const float* norm_ss, int norm_n, float norm_eps, const RowMap* map) {
+                        hipStream_t st, const float* norm_ss, int norm_n, float norm_eps, const RowMap* map,
+                        const kd_weight* X, int8_t* x_qs, float* x_qd) {
   MmvqArgs a = mmvq_args(W, xq, xd, B, nullptr, 0, map, nullptr);
+  if (map && X) {  // the extra matrix's slices as groups after the row map's
+    a.x_groups = X->n_out / W.n_out;
+    a.x_wq = static_cast<const uint8_t*>(X->qs);
+    a.x_wd = static_cast<const __half*>(X->d);
+    const size_t xt = (size_t)n_rowgroups(X->n_out) * a.NQ;
+    a.x_w_bytes = (uint32_t)(xt * tile_qs_bytes(X->fmt));
+    a.x_d_bytes = (uint32_t)(xt * tile_d_bytes(X->fmt));
+    a.x_qs = x_qs;
+    a.x_qd = x_qd;
+  }
   a.epi_qs = out_qs;
   a.epi_qd = out_d;
   a.norm_ss = norm_ss;
   a.norm_n = norm_n;
   a.norm_eps = norm_eps;
   a.QW = mmvq_qw(a.NQ, kQuadsSW);
-  launch_mmvq_fmt<4, EPI_SWIGLU>(W, a, map ? map->n_groups : 1, st);
+  launch_mmvq_fmt<4, EPI_SWIGLU>(W, a, map ? map->n_groups + a.x_groups : 1, st);
 }
 
 // Two row groups per workgroup (one 32-element block of the residual row); two quads per

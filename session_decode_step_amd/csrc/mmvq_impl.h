@@ -81,6 +81,16 @@ struct MmvqArgs {
   int norm_n;
   float norm_eps;
   int epi_kv8;  // RoPE: the caches hold FP8 E4M3 codes (else fp16)
+  // grouped SwiGLU launches: n_groups groups from the row map, then x_groups more that cut an
+  // extra matrix (x_wq / x_wd: the shared expert's, x_groups times a group's rows) into
+  // slices of w_group_tiles tiles and apply each to all B rows; slice c writes output columns
+  // [c F, (c + 1) F) of the x_qs / x_qd rows (F = n_out / 2 per slice)
+  int n_groups, x_groups;
+  const uint8_t* x_wq;
+  const __half* x_wd;
+  uint32_t x_w_bytes, x_d_bytes;
+  int8_t* x_qs;
+  float* x_qd;
 };
 
 // Epilogue of a product: write y (plain); apply SwiGLU to the interleaved gate/up rows and
@@ -264,16 +274,17 @@ __host__ __device__ constexpr int mmvq_wave_lds(int QW, int RG) { return 16 * QW
 // ascending order -- a function of k alone.
 // Dynamic LDS: nw wave slices, then [nw][RG][4][64] floats, then (fused epilogues) the
 // workgroup's outputs [RG * 16][16].
-template <int FMT, int QW, int NS, int RG, int EPI, bool DEBUG>
+template <int FMT, int QW, int NS, int RG, int EPI, bool DEBUG, bool XG = false>
 __device__ __forceinline__ void mmvq_body(const MmvqArgs& a) {
   constexpr int NT = RG * QW;
   constexpr int D0 = EPI == EPI_RESNORM ? kDepthRN : RG > 1 ? kDepthRG : FMT == KD_FMT_Q8_0 ? kDepthQ8 : kDepthQ4;
   constexpr int D = D0 < NT ? D0 : NT;
   const int e = blockIdx.y;
+  const bool xg = XG && e >= a.n_groups;  // a slice of the extra matrix, on all B rows
   int nrows = a.B;
   const int32_t* act_row = nullptr;
   const int32_t* out_row = nullptr;
-  if (a.count) {
+  if (a.count && !xg) {
     nrows = a.count[e];
     if (nrows <= 0) return;
     act_row = a.act_row + e * 16;
@@ -289,11 +300,11 @@ __device__ __forceinline__ void mmvq_body(const MmvqArgs& a) {
   const int q1 = min(NQ, q0 + QW);
   const int rg0 = blockIdx.x * RG;
 
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.wq, a.w_bytes);
-  const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.wd, a.d_bytes);
+  const __amdgpu_buffer_rsrc_t rw = xg ? make_rsrc(a.x_wq, a.x_w_bytes) : make_rsrc(a.wq, a.w_bytes);
+  const __amdgpu_buffer_rsrc_t rd = xg ? make_rsrc(a.x_wd, a.x_d_bytes) : make_rsrc(a.wd, a.d_bytes);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.xq, a.x_bytes);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.xd, a.xd_bytes);
-  const uint32_t gtile = (uint32_t)((size_t)e * (size_t)a.w_group_tiles);
+  const uint32_t gtile = (uint32_t)((size_t)(xg ? e - a.n_groups : e) * (size_t)a.w_group_tiles);
   // A operand of lane n: operand row n = activation row mfma_row_b(n) (rows past the live
   // rows read zeros)
   const int bn = mfma_row_b(n);
@@ -549,7 +560,12 @@ __device__ __forceinline__ void mmvq_body(const MmvqArgs& a) {
     if (EPI == EPI_SWIGLU) {
       // rows 0..31 of the workgroup: gate rows 32m..32m+31; rows 32..63: the same up rows
       const int m = blockIdx.x, F = a.n_out / 2;
-      const int NQo = n_quads(F), nbpo = NQo * 4;
+      // the output rows, their width and this workgroup's output block (extra-matrix slice c:
+      // block c F / 32 + m of rows F x_groups wide)
+      int8_t* const oq = xg ? a.x_qs : a.epi_qs;
+      float* const od = xg ? a.x_qd : a.epi_qd;
+      const int Fo = xg ? F * a.x_groups : F, mo = xg ? (e - a.n_groups) * (F / 32) + m : m;
+      const int NQo = n_quads(Fo), nbpo = NQo * 4;
       float av[4];
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
@@ -563,12 +579,11 @@ __device__ __forceinline__ void mmvq_body(const MmvqArgs& a) {
       }
       const int orow = out_row ? out_row[bq] : bq;  // grouped (experts): the row's (row, rank) pair
       quant4_lane8(make_float4(av[0], av[1], av[2], av[3]), sub, true,
-                   a.epi_qs + ((size_t)orow * NQo + (m >> 2)) * 128 + (m & 3) * 8, a.epi_qd + (size_t)orow * nbpo + m);
-      if (m == F / 32 - 1)  // zero blocks past F (only when F is not a multiple of 128)
-        for (int blk = F / 32; blk < nbpo; ++blk)
+                   oq + ((size_t)orow * NQo + (mo >> 2)) * 128 + (mo & 3) * 8, od + (size_t)orow * nbpo + mo);
+      if (mo == Fo / 32 - 1)  // zero blocks past Fo (only when Fo is not a multiple of 128)
+        for (int blk = Fo / 32; blk < nbpo; ++blk)
           quant4_lane8(make_float4(0.0f, 0.0f, 0.0f, 0.0f), sub, true,
-                       a.epi_qs + ((size_t)orow * NQo + (blk >> 2)) * 128 + (blk & 3) * 8,
-                       a.epi_qd + (size_t)orow * nbpo + blk);
+                       oq + ((size_t)orow * NQo + (blk >> 2)) * 128 + (blk & 3) * 8, od + (size_t)orow * nbpo + blk);
     } else if (EPI == EPI_RESNORM) {
       // the workgroup's 32 rows are block m of the residual row: x1 = res + y
       const int m = blockIdx.x, Dn = a.n_out, nblk = Dn / 32;
@@ -650,15 +665,15 @@ __device__ __forceinline__ void mmvq_body(const MmvqArgs& a) {
 template <int FMT, int QW, int NS, int RG, int EPI, bool DEBUG, bool GRP = false>
 __global__ __launch_bounds__(1024) void mmvq_kernel(MmvqArgs a) {
   if constexpr (GRP) {
-    const int rows = a.count[blockIdx.y];
+    const int rows = (int)blockIdx.y >= a.n_groups ? a.B : a.count[blockIdx.y];
     if (rows <= 4)
-      mmvq_body<FMT, QW, 1, RG, EPI, DEBUG>(a);
+      mmvq_body<FMT, QW, 1, RG, EPI, DEBUG, true>(a);
     else if (rows <= 8)
-      mmvq_body<FMT, QW, 2, RG, EPI, DEBUG>(a);
+      mmvq_body<FMT, QW, 2, RG, EPI, DEBUG, true>(a);
     else if (rows <= 12)
-      mmvq_body<FMT, QW, 3, RG, EPI, DEBUG>(a);
+      mmvq_body<FMT, QW, 3, RG, EPI, DEBUG, true>(a);
     else
-      mmvq_body<FMT, QW, 4, RG, EPI, DEBUG>(a);
+      mmvq_body<FMT, QW, 4, RG, EPI, DEBUG, true>(a);
   } else {
     mmvq_body<FMT, QW, NS, RG, EPI, DEBUG>(a);
   }

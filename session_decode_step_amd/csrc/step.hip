@@ -561,8 +561,14 @@ static kd_status decode_step_impl(const kd_model* m, int32_t B, const float* x_i
         // (row, rank) rows for the down product; the shared expert likewise
         eg.n_out = 2 * Fe;
         RowMap gu_map{s.count, s.rows, s.pairs, E, (long long)n_rowgroups(2 * Fe) * n_quads(D), B};
-        launch_mmvq_swiglu(eg, s.act_qs, s.act_d, 0, s.hq_qs, s.hq_d, st, nullptr, 0, 0.0f, &gu_map);
-        launch_mmvq_swiglu(Ly.s_gate, s.act_qs, s.act_d, B, s.shq_qs, s.shq_d, st);
+        // the shared expert's gate/up rides in the same launch when its matrix is whole groups
+        if (mmvq_swiglu_merges(eg, Ly.s_gate)) {
+          launch_mmvq_swiglu(eg, s.act_qs, s.act_d, B, s.hq_qs, s.hq_d, st, nullptr, 0, 0.0f, &gu_map, &Ly.s_gate,
+                             s.shq_qs, s.shq_d);
+        } else {
+          launch_mmvq_swiglu(eg, s.act_qs, s.act_d, 0, s.hq_qs, s.hq_d, st, nullptr, 0, 0.0f, &gu_map);
+          launch_mmvq_swiglu(Ly.s_gate, s.act_qs, s.act_d, B, s.shq_qs, s.shq_d, st);
+        }
         if (tr && !trace_codes(tr->q_ffn_mid, il, s.hq_qs, B * K, Fe, st)) return KD_ERR_HIP;
         if (tr && !trace_codes(tr->q_shared_mid, il, s.shq_qs, B, Fs, st)) return KD_ERR_HIP;
         launch_mmvq(ed, s.hq_qs, s.hq_d, 0, s.yp, D, st, &dn_map);
