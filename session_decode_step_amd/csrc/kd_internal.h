@@ -226,8 +226,12 @@ bool mmvq_weight_fits(int fmt, int n_out, int k);
 bool mmvq_fmt_ok(int fmt, int k);     // a quantised weight format, k a multiple of its block
 bool mmvq_swiglu_fits(int k);         // the SwiGLU product's LDS at this k fits a CU
 int mmvq_max_k();
+// mo_y / mo_p / mo_K (plain products only): y is a MoE layer's output, the rank-order sum
+// of the experts' rows mo_y [B K][n_out] weighted by mo_p [B][K], plus W x (the shared
+// expert's down product): per element, an fma chain over k from 0, then + (W x).
 void launch_mmvq(const kd_weight& W, const int8_t* xq, const float* xd, int B, float* y, int ldy,
-                 hipStream_t st, const RowMap* map = nullptr, int32_t* debug_S = nullptr);
+                 hipStream_t st, const RowMap* map = nullptr, int32_t* debug_S = nullptr,
+                 const float* mo_y = nullptr, const float* mo_p = nullptr, int mo_K = 0);
 
 // Per-row cache addresses and positions of one layer, passed by value as a kernel argument
 // (B <= 16 rows: no host-to-device copy and no synchronisation per step).
@@ -341,7 +345,6 @@ void launch_add(const float* x, const float* y, float* z, size_t n, hipStream_t 
 // rows/pairs [E][16], ascending row order).
 void launch_router(const float* z, const float* Wr, int B, int d, int E, int K, int32_t* ids, float* p, float* logits,
                    int32_t* count, int32_t* rows, int32_t* pairs, hipStream_t st);
-void launch_moe_combine(const float* y, const float* p, const float* sh, int B, int K, int d, float* f, hipStream_t st);
 int moe_max_experts();
 int moe_max_topk();
 

@@ -121,8 +121,11 @@ static void launch_mmvq_fmt(const kd_weight& W, const MmvqArgs& a, int ng, hipSt
 }
 
 void launch_mmvq(const kd_weight& W, const int8_t* xq, const float* xd, int B, float* y, int ldy,
-                 hipStream_t st, const RowMap* map, int32_t* debug_S) {
-  const MmvqArgs a = mmvq_args(W, xq, xd, B, y, ldy, map, debug_S);
+                 hipStream_t st, const RowMap* map, int32_t* debug_S, const float* mo_y, const float* mo_p, int mo_K) {
+  MmvqArgs a = mmvq_args(W, xq, xd, B, y, ldy, map, debug_S);
+  a.mo_y = mo_y;
+  a.mo_p = mo_p;
+  a.mo_K = mo_K;
   // grouped Q4_0 products (the experts' down product: small k, so a workgroup of one row
   // group has little to stream) take four row groups per workgroup
   if (map && W.fmt == KD_FMT_Q4_0)

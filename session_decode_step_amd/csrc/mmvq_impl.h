@@ -91,6 +91,12 @@ struct MmvqArgs {
   uint32_t x_w_bytes, x_d_bytes;
   int8_t* x_qs;
   float* x_qd;
+  // plain product writing a MoE layer's output (mo_y != nullptr): y[b][row] = sum_k
+  // mo_p[b][k] mo_y[b K + k][row] (rank order, fma from 0) + (W x)[b][row] -- the experts' rows
+  // and this product (the shared expert's down), as the separate combine adds them
+  const float* mo_y;
+  const float* mo_p;
+  int mo_K;
 };
 
 // Epilogue of a product: write y (plain); apply SwiGLU to the interleaved gate/up rows and
@@ -526,7 +532,14 @@ __device__ __forceinline__ void mmvq_body(const MmvqArgs& a) {
       const int row = (rg0 + r) * 16 + (l & 15);
       if (b < nrows && row < a.n_out) {
         const int orow = out_row ? out_row[b] : b;
-        a.y[(size_t)orow * a.ldy + row] = v;
+        float o = v;
+        if (a.mo_y) {
+          float acc = 0.0f;
+          for (int k = 0; k < a.mo_K; ++k)
+            acc = fmaf(a.mo_p[b * a.mo_K + k], a.mo_y[(size_t)(b * a.mo_K + k) * a.n_out + row], acc);
+          o = acc + v;
+        }
+        a.y[(size_t)orow * a.ldy + row] = o;
       }
     }
     return;

@@ -11,8 +11,8 @@
 // also lists, for each expert, the (row, rank) pairs routed to it in ascending row order; the
 // grouped mmvq reads each active expert's tiles once (empty experts exit before reading)
 // and treats its rows as the MFMA's activation rows, whose results never depend on which
-// other rows share the expert; the combine adds the k expert outputs of a row in rank
-// order.  So a row's result is the same at any B.
+// other rows share the expert; the shared expert's down product adds the k expert outputs of
+// a row in rank order to its own (its epilogue).  So a row's result is the same at any B.
 #include "kd_internal.h"
 
 namespace kd {
@@ -148,17 +148,6 @@ __global__ __launch_bounds__(1024) void route_bucket_kernel(const float* __restr
   }
 }
 
-// f[b][i] = sum_k p[b][k] y[b*K + k][i] (rank order) + sh[b][i].
-__global__ void moe_combine_kernel(const float* __restrict__ y, const float* __restrict__ p, const float* __restrict__ sh,
-                                   int B, int K, int d, float* __restrict__ f) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= B * d) return;
-  const int b = idx / d, i = idx % d;
-  float acc = 0.0f;
-  for (int k = 0; k < K; ++k) acc = fmaf(p[b * K + k], y[(size_t)(b * K + k) * d + i], acc);
-  f[idx] = acc + sh[idx];
-}
-
 void launch_router(const float* z, const float* Wr, int B, int d, int E, int K, int32_t* ids, float* p, float* logits,
                    int32_t* count, int32_t* rows, int32_t* pairs, hipStream_t st) {
   router_logits_kernel<<<dim3(E, B), 64, 0, st>>>(z, Wr, d, E, logits);
@@ -168,10 +157,6 @@ void launch_router(const float* z, const float* Wr, int B, int d, int E, int K, 
     case 3: route_bucket_kernel<3><<<1, 1024, 0, st>>>(logits, B, E, K, ids, p, count, rows, pairs); break;
     default: route_bucket_kernel<4><<<1, 1024, 0, st>>>(logits, B, E, K, ids, p, count, rows, pairs); break;
   }
-}
-
-void launch_moe_combine(const float* y, const float* p, const float* sh, int B, int K, int d, float* f, hipStream_t st) {
-  moe_combine_kernel<<<ceil_div(B * d, 256), 256, 0, st>>>(y, p, sh, B, K, d, f);
 }
 
 int moe_max_experts() { return kMaxExperts; }

@@ -244,7 +244,7 @@ struct Carve {
 };
 
 struct StepBufs {
-  float *xa, *xb, *f, *qkv, *attn, *o, *gu, *z, *cs, *sh, *sgu;
+  float *xa, *xb, *f, *qkv, *attn, *o, *gu, *z, *cs, *sgu;
   float *lq, *lk, *lv, *lg, *lb, *lo;  // linear layers: prep outputs and the state step's output
   int8_t *act_qs, *act2_qs, *hq_qs, *actn_qs;
   float *act_d, *act2_d, *hq_d, *actn_d, *ss;
@@ -300,7 +300,6 @@ size_t carve_step(const kd_model* m, int B, const FaPlan& plan, void* ws, StepBu
     s.hq_qs = c.take<int8_t>((size_t)B * K * n_quads(Fe) * 128);
     s.hq_d = c.take<float>((size_t)B * K * n_quads(Fe) * 4);
     s.yp = c.take<float>((size_t)B * K * D);
-    s.sh = c.take<float>((size_t)B * D);
     s.sgu = c.take<float>((size_t)B * 2 * Fs);
     s.shq_qs = c.take<int8_t>((size_t)B * n_quads(Fs) * 128);  // the shared expert's SwiGLU rows
     s.shq_d = c.take<float>((size_t)B * n_quads(Fs) * 4);
@@ -572,7 +571,8 @@ static kd_status decode_step_impl(const kd_model* m, int32_t B, const float* x_i
         if (tr && !trace_codes(tr->q_ffn_mid, il, s.hq_qs, B * K, Fe, st)) return KD_ERR_HIP;
         if (tr && !trace_codes(tr->q_shared_mid, il, s.shq_qs, B, Fs, st)) return KD_ERR_HIP;
         launch_mmvq(ed, s.hq_qs, s.hq_d, 0, s.yp, D, st, &dn_map);
-        launch_mmvq(Ly.s_down, s.shq_qs, s.shq_d, B, s.sh, D, st);
+        // the shared expert's down product writes the layer's output f (experts' rows added)
+        launch_mmvq(Ly.s_down, s.shq_qs, s.shq_d, B, s.f, D, st, nullptr, nullptr, s.yp, s.p, K);
       } else {
         RowMap gu_map{s.count, s.rows, s.pairs, E, (long long)n_rowgroups(Fe) * n_quads(D), B};
         eg.n_out = Fe;
@@ -587,9 +587,8 @@ static kd_status decode_step_impl(const kd_model* m, int32_t B, const float* x_i
         launch_mmvq(ed, s.hq_qs, s.hq_d, 0, s.yp, D, st, &dn_map);
         launch_swiglu_quant(s.sgu, s.sgu + Fs, B, Fs, 2 * Fs, nullptr, s.act_qs, s.act_d, st);
         if (tr && !trace_codes(tr->q_shared_mid, il, s.act_qs, B, Fs, st)) return KD_ERR_HIP;
-        launch_mmvq(Ly.s_down, s.act_qs, s.act_d, B, s.sh, D, st);
+        launch_mmvq(Ly.s_down, s.act_qs, s.act_d, B, s.f, D, st, nullptr, nullptr, s.yp, s.p, K);
       }
-      launch_moe_combine(s.yp, s.p, s.sh, B, K, D, s.f, st);
     }
     base = x1;
     add = s.f;
