@@ -228,7 +228,7 @@ size_t kd_fa_decode_workspace(int32_t B, int32_t H, int32_t hd, const int32_t* t
  * out[b][h][:] = sum_j softmax_j(q[b][h] . K_b[g][j] * scale) V_b[g][j], j < t_kv[b],
  * g = h / (H/G) (memra-engine decode_batch.rs phase B, ``fa_decode_batch_seqs_v4``: one
  * launch over all rows plus one combine).  Keys are split into chunks of
- * c_b = max(128, ceil(t_b / 128)) — a function of the row's own t_kv only — and the chunk
+ * c_b = max(128, ceil(t_b / 256)) — a function of the row's own t_kv only — and the chunk
  * partials are merged in chunk order.  q, out: fp32 [B][H][hd]; caches fp16 [G][capacity][hd];
  * H/G must be 1, 2, 4 or 8, hd 64 or 128, 1 <= t_kv[b] <= min(capacity, 131072). */
 kd_status kd_fa_decode_ragged(const float* q, int32_t B, int32_t H, int32_t G, int32_t hd,

@@ -6,7 +6,7 @@
 // per-query base pointer and kv length): for row b and query head h with KV head
 // g = h / (H/G), out = softmax(q . K[0:t_b] * scale) V[0:t_b].
 //
-// How: keys of row b are cut into S_b chunks of c_b = max(128, ceil(t_b / 128)) keys — a
+// How: keys of row b are cut into S_b chunks of c_b = max(128, ceil(t_b / 256)) keys — a
 // function of the row's own t_b only, never of B or of the other rows (the reading of the
 // page's rule that every row must run the program of its isolated run).  One workgroup per
 // (row, chunk, KV head) reads that head's contiguous K/V stream once for all H/G query heads
@@ -24,7 +24,7 @@ namespace kd {
 constexpr int kKvAux = 2;  // cache policy of the K/V loads: non-temporal (each key is read once)
 
 constexpr int kFaMinChunk = 128;
-constexpr int kFaMaxSplits = 128;
+constexpr int kFaMaxSplits = 256;
 constexpr int kFaMaxKeys = 128 * 1024;  // t_kv limit: chunk <= 1024 keys
 
 int fa_chunk_for(int t) {

@@ -50,8 +50,8 @@ def test_layout_sizes():
     assert L.kd_act_qs_bytes(3, 704) == 3 * 6 * 128
     assert L.kd_act_d_bytes(3, 704) == 3 * 24 * 4
     t = (C.c_int32 * 3)(1, 129, 40000)
-    # splits: 1 -> 1 (chunk 128), 129 -> 2, 40000 -> chunk 313, 128 splits
-    assert L.kd_fa_decode_workspace(3, 8, 128, t) == (1 + 2 + 128) * 8 * (128 + 2) * 4
+    # splits: 1 -> 1 (chunk 128), 129 -> 2, 40000 -> chunk 157, 255 splits
+    assert L.kd_fa_decode_workspace(3, 8, 128, t) == (1 + 2 + 255) * 8 * (128 + 2) * 4
 
 
 def _status(fn, *args):
@@ -317,7 +317,7 @@ def test_products_reject_shapes_past_their_limits():
 
 def test_noalloc_attention_rejects_partials_beyond_its_scratch():
     """kd_fa_decode_ragged_noalloc refuses, before touching the device, a call whose split
-    partials exceed its 16 MiB scratch array (16 rows of 131072 keys, 64 query heads: 68 MB)."""
+    partials exceed its 16 MiB scratch array (16 rows of 131072 keys, 64 query heads: 136 MB)."""
     L = kd.lib()
     B, H, G, hd, cap = 16, 64, 8, 128, 131072
     t = (C.c_int32 * B)(*([cap] * B))
