@@ -148,7 +148,8 @@ __global__ __launch_bounds__(64 * kFaWaves) void fa_split_kernel(FaPlan p, const
   constexpr float kPScale = 16384.0f, kPInv = 1.0f / 16384.0f;
   static_assert(R <= C && C <= 16, "query columns");
   constexpr bool GROUPED = C > R;  // rows sharing a cache pass; otherwise one row per workgroup
-  const int item = blockIdx.x, g = blockIdx.y;
+  int item = blockIdx.x;
+  const int g = blockIdx.y;
   const int H = p.H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = lane & 15, gq = lane >> 4;
@@ -168,6 +169,17 @@ __global__ __launch_bounds__(64 * kFaWaves) void fa_split_kernel(FaPlan p, const
     k1 = min(k0 + p.grp_chunk[gi], p.grp_t[gi]);
     kbase = p.grp_k[gi];
     vbase = p.grp_v[gi];
+  } else if (gridDim.z > 1) {
+    // (chunk, KV head, row) grid: the row is known without reading the plan, so every value
+    // the chunk needs comes in one round of loads; chunks past the row's last exit
+    b = blockIdx.z;
+    sc = blockIdx.x;
+    if (sc >= p.split_off[b + 1] - p.split_off[b]) return;
+    item = p.split_off[b] + sc;
+    k0 = sc * p.chunk[b];
+    k1 = min(k0 + p.chunk[b], p.t_kv[b]);
+    kbase = rc.k[b];
+    vbase = rc.v[b];
   } else {
 #pragma unroll
     for (int i = 1; i < KD_MAX_B; ++i)
@@ -580,7 +592,12 @@ static void launch_fa_c(const FaPlan& p, const float* q, int ldq, const RowCache
                         void* ws, hipStream_t st) {
   int cmax = 0;
   for (int b = 0; b < p.B; ++b) cmax = p.chunk[b] > cmax ? p.chunk[b] : cmax;
-  const dim3 grid(C > R ? p.grp_off[p.n_grp] : p.n_items, p.G);
+  // rows not sharing a cache: a (chunk, KV head, row) grid when it wastes at most an eighth of
+  // its workgroups on chunks past short rows' ends, else one workgroup per (item, KV head)
+  int smax = 0;
+  for (int b = 0; b < p.B; ++b) smax = std::max(smax, p.split_off[b + 1] - p.split_off[b]);
+  const bool rows3d = C == R && smax * p.B <= p.n_items + p.n_items / 8;
+  const dim3 grid(C > R ? p.grp_off[p.n_grp] : rows3d ? smax : p.n_items, p.G, rows3d ? p.B : 1);
   if (cmax > 16 * kFaWaves)
     fa_split_kernel<R, HD, true, C, F8><<<grid, 64 * kFaWaves, 0, st>>>(p, q, ldq, rc, capacity, scale,
                                                                    static_cast<float*>(ws));
