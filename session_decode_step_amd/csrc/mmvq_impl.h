@@ -290,7 +290,14 @@ __device__ __forceinline__ void mmvq_body(const MmvqArgs& a) {
   int nrows = a.B;
   const int32_t* act_row = nullptr;
   const int32_t* out_row = nullptr;
+  // grouped: the row map's entries for this lane's operand rows are read together with the
+  // group's count (the map holds 16 entries per group, so the reads stay in bounds; entries
+  // past the count are masked below)
+  const int lane0 = threadIdx.x & 63;
+  int32_t ar_a = 0, ar_s = 0;
   if (a.count && !xg) {
+    ar_a = a.act_row[e * 16 + mfma_row_b(lane0 & 15)];
+    ar_s = a.act_row[e * 16 + mfma_row_b(lane0 >> 2)];
     nrows = a.count[e];
     if (nrows <= 0) return;
     act_row = a.act_row + e * 16;
@@ -314,7 +321,7 @@ __device__ __forceinline__ void mmvq_body(const MmvqArgs& a) {
   // A operand of lane n: operand row n = activation row mfma_row_b(n) (rows past the live
   // rows read zeros)
   const int bn = mfma_row_b(n);
-  const uint32_t a_off = (bn < nrows) ? (uint32_t)(act_row ? act_row[bn] : bn) * (uint32_t)NQ * 128u + g * 32 : kOOB;
+  const uint32_t a_off = (bn < nrows) ? (uint32_t)(act_row ? ar_a : bn) * (uint32_t)NQ * 128u + g * 32 : kOOB;
 
   char* slice = reinterpret_cast<char*>(smem) + (size_t)w * mmvq_wave_lds(QW, RG);
   float* dxw = reinterpret_cast<float*>(slice);  // [16][QW] float4
@@ -328,7 +335,7 @@ __device__ __forceinline__ void mmvq_body(const MmvqArgs& a) {
   int4 dxv[NDX];
   if (!DEBUG) {
     const int r = lane >> 2, p = lane & 3, br = mfma_row_b(r);
-    const uint32_t row_base = (br < nrows) ? (uint32_t)(act_row ? act_row[br] : br) * (uint32_t)NQ * 16u : kOOB;
+    const uint32_t row_base = (br < nrows) ? (uint32_t)(act_row ? ar_s : br) * (uint32_t)NQ * 16u : kOOB;
 #pragma unroll
     for (int i = 0; i < NDX; ++i) {
       const int q = q0 + 4 * i + p;
