@@ -81,6 +81,9 @@ struct MmvqArgs {
   int norm_n;
   float norm_eps;
   int epi_kv8;  // RoPE: the caches hold FP8 E4M3 codes (else fp16)
+  // add + RMSNorm launches: activation rows per grid z slice (slice z takes rows
+  // [z row_split, min(B, (z + 1) row_split))); 0: one slice of all B rows
+  int row_split;
   // grouped SwiGLU launches: n_groups groups from the row map, then x_groups more that cut an
   // extra matrix (x_wq / x_wd: the shared expert's, x_groups times a group's rows) into
   // slices of w_group_tiles tiles and apply each to all B rows; slice c writes output columns
@@ -288,6 +291,12 @@ __device__ __forceinline__ void mmvq_body(const MmvqArgs& a) {
   const int e = blockIdx.y;
   const bool xg = XG && e >= a.n_groups;  // a slice of the extra matrix, on all B rows
   int nrows = a.B;
+  // row split (add + RMSNorm products): this workgroup's rows start at activation row b0
+  int b0 = 0;
+  if (EPI == EPI_RESNORM && a.row_split) {
+    b0 = (int)blockIdx.z * a.row_split;
+    nrows = min(a.row_split, a.B - b0);
+  }
   const int32_t* act_row = nullptr;
   const int32_t* out_row = nullptr;
   // grouped: the row map's entries for this lane's operand rows are read together with the
@@ -321,7 +330,7 @@ __device__ __forceinline__ void mmvq_body(const MmvqArgs& a) {
   // A operand of lane n: operand row n = activation row mfma_row_b(n) (rows past the live
   // rows read zeros)
   const int bn = mfma_row_b(n);
-  const uint32_t a_off = (bn < nrows) ? (uint32_t)(act_row ? ar_a : bn) * (uint32_t)NQ * 128u + g * 32 : kOOB;
+  const uint32_t a_off = (bn < nrows) ? (uint32_t)(act_row ? ar_a : b0 + bn) * (uint32_t)NQ * 128u + g * 32 : kOOB;
 
   char* slice = reinterpret_cast<char*>(smem) + (size_t)w * mmvq_wave_lds(QW, RG);
   float* dxw = reinterpret_cast<float*>(slice);  // [16][QW] float4
@@ -335,7 +344,7 @@ __device__ __forceinline__ void mmvq_body(const MmvqArgs& a) {
   int4 dxv[NDX];
   if (!DEBUG) {
     const int r = lane >> 2, p = lane & 3, br = mfma_row_b(r);
-    const uint32_t row_base = (br < nrows) ? (uint32_t)(act_row ? ar_s : br) * (uint32_t)NQ * 16u : kOOB;
+    const uint32_t row_base = (br < nrows) ? (uint32_t)(act_row ? ar_s : b0 + br) * (uint32_t)NQ * 16u : kOOB;
 #pragma unroll
     for (int i = 0; i < NDX; ++i) {
       const int q = q0 + 4 * i + p;
@@ -605,10 +614,11 @@ __device__ __forceinline__ void mmvq_body(const MmvqArgs& a) {
           quant4_lane8(make_float4(0.0f, 0.0f, 0.0f, 0.0f), sub, true,
                        oq + ((size_t)orow * NQo + (blk >> 2)) * 128 + (blk & 3) * 8, od + (size_t)orow * nbpo + blk);
     } else if (EPI == EPI_RESNORM) {
-      // the workgroup's 32 rows are block m of the residual row: x1 = res + y
-      const int m = blockIdx.x, Dn = a.n_out, nblk = Dn / 32;
+      // the workgroup's 32 rows are block m of the residual row: x1 = res + y (activation
+      // row bg = b0 + bq)
+      const int m = blockIdx.x, Dn = a.n_out, nblk = Dn / 32, bg = b0 + bq;
       const int NQo = n_quads(Dn), nbpo = NQo * 4;
-      const size_t o = (size_t)bq * a.epi_ld + 32 * m + 4 * sub;
+      const size_t o = (size_t)bg * a.epi_ld + 32 * m + 4 * sub;
       const float4 xr = *reinterpret_cast<const float4*>(a.epi_res + o);
       const float4 gn = *reinterpret_cast<const float4*>(a.epi_gain + 32 * m + 4 * sub);
       const float* ov = outv + (4 * sub) * 16 + bq;
@@ -619,14 +629,14 @@ __device__ __forceinline__ void mmvq_body(const MmvqArgs& a) {
       ss = fmaf(v.z, v.z, ss);
       ss = fmaf(v.w, v.w, ss);
       ss = group8_sum(ss);
-      if (sub == 0) a.epi_ss[(size_t)bq * nblk + m] = ss;
+      if (sub == 0) a.epi_ss[(size_t)bg * nblk + m] = ss;
       quant4_lane8(make_float4(v.x * gn.x, v.y * gn.y, v.z * gn.z, v.w * gn.w), sub, true,
-                   a.epi_qs + ((size_t)bq * NQo + (m >> 2)) * 128 + (m & 3) * 8, a.epi_qd + (size_t)bq * nbpo + m);
+                   a.epi_qs + ((size_t)bg * NQo + (m >> 2)) * 128 + (m & 3) * 8, a.epi_qd + (size_t)bg * nbpo + m);
       if (m == nblk - 1)  // zero blocks past the row (only when it is not a multiple of 128)
         for (int blk = nblk; blk < nbpo; ++blk)
           quant4_lane8(make_float4(0.0f, 0.0f, 0.0f, 0.0f), sub, true,
-                       a.epi_qs + ((size_t)bq * NQo + (blk >> 2)) * 128 + (blk & 3) * 8,
-                       a.epi_qd + (size_t)bq * nbpo + blk);
+                       a.epi_qs + ((size_t)bg * NQo + (blk >> 2)) * 128 + (blk & 3) * 8,
+                       a.epi_qd + (size_t)bg * nbpo + blk);
     } else {
       // 16 rows = 8 RoPE pairs (i, i + hd/2) of one head, packed adjacently
       const int hd = a.epi_hd, half = hd / 2, H = a.epi_H, G = a.epi_G;
@@ -714,7 +724,7 @@ static int mmvq_qw(int NQ, int want_quads = kWaveQuads) {
 template <int FMT, int QW, int NS, int RG, int EPI>
 static void launch_mmvq_qn(const MmvqArgs& a, int n_groups, hipStream_t st) {
   const int nw = ceil_div(a.NQ, QW);
-  dim3 grid(ceil_div(a.NR, RG), n_groups);
+  dim3 grid(ceil_div(a.NR, RG), n_groups, a.row_split ? ceil_div(a.B, a.row_split) : 1);
   const size_t slices = (size_t)nw * mmvq_wave_lds(QW, RG);
   const size_t red_shm = (size_t)nw * RG * 256 * sizeof(float);
   const size_t out_shm = EPI == EPI_PLAIN ? 0 : (size_t)RG * 256 * sizeof(float);
@@ -736,16 +746,18 @@ static void launch_mmvq_qn(const MmvqArgs& a, int n_groups, hipStream_t st) {
 
 template <int FMT, int QW, int RG, int EPI>
 static void launch_mmvq_q(const MmvqArgs& a, int n_groups, hipStream_t st) {
-  // epilogue slots: ceil(B / 4), a function of B (rows past B are never written, so
-  // dropping their slots leaves every live output's operation sequence unchanged)
+  // epilogue slots: ceil(rows / 4) for the rows a workgroup takes (B, or a row split's slice;
+  // rows past them are never written, so dropping their slots leaves every live output's
+  // operation sequence unchanged)
   // (K-quant formats: 2 slots up to B = 8, else 4 -- two instantiations)
+  const int rows = a.row_split ? a.row_split : a.B;  // rows per workgroup
   if constexpr (fmt_is_kq(FMT)) {
-    if (!a.count && a.B <= 8)
+    if (!a.count && rows <= 8)
       launch_mmvq_qn<FMT, QW, 2, RG, EPI>(a, n_groups, st);
     else
       launch_mmvq_qn<FMT, QW, 4, RG, EPI>(a, n_groups, st);
   } else {
-    const int ns = a.count ? 4 : (a.B + 3) / 4;
+    const int ns = a.count ? 4 : (rows + 3) / 4;
     switch (ns) {
       case 1: return launch_mmvq_qn<FMT, QW, 1, RG, EPI>(a, n_groups, st);
       case 2: return launch_mmvq_qn<FMT, QW, 2, RG, EPI>(a, n_groups, st);
