@@ -163,16 +163,20 @@ void launch_mmvq_swiglu(const kd_weight& W, const int8_t* xq, const float* xd, i
 }
 
 // Two row groups per workgroup (one 32-element block of the residual row); two quads per
-// wave, so the workgroup count halves but the wave count does not.  More than four rows are
-// split over two grid slices (each workgroup streams its 32 weight rows for half the rows,
-// with half the epilogue slots per tile), so the launch fills twice the CUs.  The two slices
+// wave, so the workgroup count halves but the wave count does not.  Two or more rows are
+// split over two grid slices (each workgroup streams its 32 weight rows for half the rows;
+// above four rows, with half the epilogue slots per tile), so the launch fills twice the
+// CUs.  The two slices
 // of a block are gridDim.x workgroups apart in dispatch order: on one XCD, and its L2, when
 // gridDim.x is a multiple of 8.
 void launch_mmvq_resnorm(const kd_weight& W, const int8_t* xq, const float* xd, int B, const float* res, int ld,
                          const float* gain, float* x1, int8_t* out_qs, float* out_d, float* ss, hipStream_t st) {
   MmvqArgs a = mmvq_args(W, xq, xd, B, nullptr, 0, nullptr, nullptr);
   a.QW = mmvq_qw(a.NQ, kQuadsRN);
-  if (B > 4) a.row_split = 4 * ceil_div(ceil_div(B, 4), 2);
+  if (B > 4)
+    a.row_split = 4 * ceil_div(ceil_div(B, 4), 2);
+  else if (B > 1)
+    a.row_split = ceil_div(B, 2);
   a.epi_res = res;
   a.epi_ld = ld;
   a.epi_gain = gain;
