@@ -492,6 +492,33 @@ def test_fa_decode_at_the_key_limit():
 
 
 
+@pytest.mark.parametrize("fmt,n,k,B", [("q4_0", 4096, 4096, 2), ("q4_0", 4096, 14336, 4), ("q8_0", 2048, 2048, 9),
+                                       ("q4_0", 4096, 4096, 16), ("q6_k", 2048, 5632, 7)])
+def test_resnorm_rows_bit_identical_to_their_one_row_call(fmt, n, k, B):
+    """kd_mmvq_resnorm splits two or more rows over grid slices (ceil(B/2) rows each up to
+    B = 4, then 4 or 8 rows); every row's x1, block codes, block scales and block sums must
+    equal that row's own B = 1 call bit for bit (B = 9: a last slice of one row)."""
+    say(f"resnorm rows vs 1-row calls {fmt} n={n} k={k} B={B}")
+    r = np.random.default_rng(7 * n + k + B)
+    w = kd.kd_pack_weight(_drawer(fmt)(r, r, n, k))
+    a = r.standard_normal((B, k)).astype(np.float32)
+    res = r.standard_normal((B, n)).astype(np.float32)
+    gain = dev((1 + 0.1 * r.standard_normal(n)).astype(np.float32))
+    act = kd.kd_quantize_act_q8(dev(a))
+    x1, zq, ss = kd.kd_mmvq_resnorm(w, act, B, dev(res), gain)
+    sync()
+    x1, qs, qd, ss = (t.cpu().numpy() for t in (x1, zq.qs, zq.d, ss))
+    nq, nbp = qs.size // B, qd.size // B   # per-row extents of the tiled codes and scales
+    for b in range(B):
+        x1b, zb, ssb = kd.kd_mmvq_resnorm(w, kd.act_rows_view(act, b, 1), 1, dev(res[b:b + 1]), gain)
+        sync()
+        np.testing.assert_array_equal(x1b.cpu().numpy()[0].view(np.uint32), x1[b].view(np.uint32), err_msg=f"x1 row {b}")
+        np.testing.assert_array_equal(zb.qs.cpu().numpy(), qs[b * nq:(b + 1) * nq], err_msg=f"codes row {b}")
+        np.testing.assert_array_equal(zb.d.cpu().numpy().view(np.uint32), qd[b * nbp:(b + 1) * nbp].view(np.uint32))
+        np.testing.assert_array_equal(ssb.cpu().numpy()[0].view(np.uint32), ss[b].view(np.uint32))
+    say(f"  {B} rows equal their 1-row calls")
+
+
 @pytest.mark.parametrize("fmt,n,k,B", [("q4_0", 4096, 4096, 8), ("q8_0", 2048, 2048, 3), ("q4_0", 4096, 14336, 16),
                                        ("q4_0", 2816, 2048, 5), ("q4_k", 4096, 4096, 8), ("q6_k", 2048, 5632, 5),
                                        ("q5_k", 2816, 2048, 3)])
